@@ -1,0 +1,285 @@
+"""CPU oracle for the TTQ (activation-aware test-time quantization) linear
+projection.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check in ``__graft_entry__``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
+the HIP implementation; the only thing both sides consume is the seeded
+bfloat16 input bytes from the ``workloads`` package.
+
+Sources (pages as titled; sections as headed on each page):
+
+* [ZH]  "TTQ: Activation-Aware Test-Time Quantization to Accelerate LLM
+  Inference On The Fly", gist.science zh summary of arXiv:2603.19296.
+  Sec. 2.1 (online activation-aware quantization): the diagonal
+  D_ii = (||X_{i,:}||_p + lambda)^alpha and W_hat = Q[W D^{1/2}] D^{-1/2};
+  Sec. 2.2 (low-rank integration): W ~ W_q + BA with static B, A;
+  Sec. 2.3 (complexity): overhead O[dT + 3d'd] against O[d'dT].
+* [NL], [IT]  the nl and it summaries of the same paper, Sec. 2
+  (methodology), which restate the same formulas.
+* [BLOG-EN] "Test-time quantization: quantising on the fly with no
+  calibration dataset", section "The maths that matter": the affine
+  quantizer (integer code, scale s, zero point) with |x - x_hat| <= s/2, the
+  symmetric scale M / (2^{b-1} - 1), and the INT4 outlier example.
+
+Notation: X has d input channels and T tokens.  Arrays here store it
+token-major, ``X[t, j]`` = channel j of token t, as a linear layer receives
+it.  W is ``[d_out, d]``; Y = W_hat X is stored ``[T, d_out]``.
+
+Readings taken where the pages leave a step open (all listed in the design doc):
+
+1. Quantizer Q: asymmetric b-bit, groups of ``group`` consecutive input
+   channels of one output row, min-anchored with a real zero point:
+   s = (max - min) / (2^b - 1), q = clamp(round((u - min) / s), 0, 2^b - 1),
+   u_hat = min + s q.  A group with max == min gets s = 0 and q = 0.
+2. round = round half to even.
+3. ||X_{i,:}||_p is the plain (unnormalised) L_p norm over the T tokens.
+4. lambda is added to the norm before the power: (n + lambda)^alpha.
+5. D^{1/2}, D^{-1/2} are the elementwise powers +-alpha/2 of the diagonal;
+   D^{-1/2} is evaluated as 1 / D^{1/2}.  A channel with n + lambda = 0 gets
+   D^{1/2} = D^{-1/2} = 1 (it multiplies zero activations only).
+6. Low rank: the W passed in is already the residual W_q; Y = Q_D[W] X +
+   B (A X), with B, A unquantized and untouched by D.
+7. Decision precision: the pages fix none, so the integer codes are decided
+   in IEEE float32 by this fixed sequence (no fused multiply-add):
+     dh32 = float32(D^{1/2});  u = fl(w * dh32);  m, M = min, max of u;
+     s = fl(fl(M - m) / N);    inv = fl(1 / s) (0 if s == 0);
+     t = fl(fl(u - m) * inv);  q = clamp(rint(t), 0, N).
+   Statistics (norms, powers) and the dequantized contraction are float64.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64",
+    "bf16_to_f32",
+    "channel_norms",
+    "diag_scales",
+    "encode_groups_fp32",
+    "pre_rounding_fp64",
+    "dequantize",
+    "ttq_linear",
+    "ttq_linear_batched",
+    "band_excused",
+    "symmetric_quantize",
+]
+
+
+# --------------------------------------------------------------------------
+# input decoding (the oracle's own; bfloat16 is the top half of a float32)
+# --------------------------------------------------------------------------
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# statistics: [ZH] Sec. 2.1, [NL]/[IT] Sec. 2
+# --------------------------------------------------------------------------
+def channel_norms(X: np.ndarray, p: float) -> np.ndarray:
+    """n_j = ||X_{j,:}||_p, the L_p norm of channel j over all T tokens.
+
+    ``X`` is ``[T, d]`` float64.  Reading 3: no 1/T normalisation.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    if X.shape[0] == 0:
+        return np.zeros(X.shape[1], dtype=np.float64)
+    if p == 2.0:
+        return np.sqrt(np.sum(X * X, axis=0))
+    if p == 1.0:
+        return np.sum(np.abs(X), axis=0)
+    return np.sum(np.abs(X) ** p, axis=0) ** (1.0 / p)
+
+
+def diag_scales(n: np.ndarray, lam: float, alpha: float):
+    """D^{1/2} and D^{-1/2} for D_ii = (n_i + lambda)^alpha ([ZH] Sec. 2.1).
+
+    Returns float64 ``(dh, dhi)``; readings 4 and 5.
+    """
+    base = np.asarray(n, dtype=np.float64) + float(lam)
+    dh = np.ones_like(base)
+    ok = base > 0.0
+    dh[ok] = base[ok] ** (0.5 * float(alpha))
+    dhi = 1.0 / dh
+    return dh, dhi
+
+
+# --------------------------------------------------------------------------
+# quantizer Q[W D^{1/2}]: [ZH] Sec. 2.1; affine form from [BLOG-EN] maths
+# --------------------------------------------------------------------------
+def encode_groups_fp32(W32: np.ndarray, dh32: np.ndarray, bits: int,
+                       group: int):
+    """Integer codes of W D^{1/2}, decided in float32 (reading 7).
+
+    ``W32`` is ``[rows, d]`` float32 (exact bf16 values), ``dh32`` is ``[d]``
+    float32.  Returns ``(q uint8 [rows, d], s f32 [rows, G], m f32 [rows, G])``
+    with G = d / group.
+    """
+    W32 = np.asarray(W32, dtype=np.float32)
+    dh32 = np.asarray(dh32, dtype=np.float32)
+    rows, d = W32.shape
+    G = d // group
+    N = np.float32(2 ** bits - 1)
+    u = (W32 * dh32[None, :]).reshape(rows, G, group)       # fl(w * dh)
+    m = u.min(axis=2)
+    M = u.max(axis=2)
+    s = (M - m) / N                                          # fl(fl(M-m)/N)
+    pos = s > np.float32(0)
+    inv = np.zeros_like(s)
+    inv[pos] = np.float32(1.0) / s[pos]                      # fl(1/s)
+    t = (u - m[:, :, None]) * inv[:, :, None]                # fl(fl(u-m)*inv)
+    q = np.clip(np.rint(t), np.float32(0), N)
+    q = np.where(pos[:, :, None], q, np.float32(0))
+    return q.astype(np.uint8).reshape(rows, d), s, m
+
+
+def pre_rounding_fp64(W64: np.ndarray, dh64: np.ndarray, bits: int,
+                      group: int):
+    """The real-valued pre-rounding code t* = (u - min) / s in float64.
+
+    Used only to decide whether a code mismatch sits on a rounding boundary.
+    Returns ``(t, u, m, s)`` with t, u ``[rows, d]`` and m, s ``[rows, G]``.
+    """
+    W64 = np.asarray(W64, dtype=np.float64)
+    rows, d = W64.shape
+    G = d // group
+    N = float(2 ** bits - 1)
+    u = (W64 * dh64[None, :]).reshape(rows, G, group)
+    m = u.min(axis=2)
+    s = (u.max(axis=2) - m) / N
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s[:, :, None] > 0, (u - m[:, :, None]) / s[:, :, None], 0.0)
+    return t.reshape(rows, d), u.reshape(rows, d), m, s
+
+
+def dequantize(q: np.ndarray, s: np.ndarray, m: np.ndarray, dhi: np.ndarray,
+               group: int) -> np.ndarray:
+    """W_hat = (min + s q) D^{-1/2}, float64 ([ZH] Sec. 2.1)."""
+    rows, d = q.shape
+    G = d // group
+    u_hat = (m.astype(np.float64)[:, :, None]
+             + s.astype(np.float64)[:, :, None]
+             * q.reshape(rows, G, group).astype(np.float64))
+    return u_hat.reshape(rows, d) * np.asarray(dhi, dtype=np.float64)[None, :]
+
+
+# --------------------------------------------------------------------------
+# the whole projection
+# --------------------------------------------------------------------------
+def ttq_linear(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
+               group: int, p: float, lam: float, alpha: float,
+               B_bits: Optional[np.ndarray] = None,
+               A_bits: Optional[np.ndarray] = None,
+               rows: Optional[np.ndarray] = None,
+               dh32_override: Optional[np.ndarray] = None,
+               want_t: bool = False) -> dict:
+    """One TTQ linear call for one request.
+
+    ``W_bits`` uint16 ``[d_out, d]``, ``X_bits`` uint16 ``[T, d]``, optional
+    ``B_bits`` ``[d_out, r]`` and ``A_bits`` ``[r, d]``.  ``rows`` restricts
+    the quantization and the output to a subset of output channels (rows of
+    W are independent once D is fixed; D always uses the full X).
+    ``dh32_override`` replaces the float32 D^{1/2} fed to the code decision
+    (used to check a kernel's codes against its own exported statistics).
+
+    Returns a dict with ``n, dh, dhi`` (float64 [d]), ``dh32`` (float32
+    [d]), ``q`` (uint8 [rows, d]), ``s, m`` (float32 [rows, G]), ``Y``
+    (float64 [T, rows]) and, if ``want_t``, the float64 pre-rounding values.
+    """
+    X = bf16_to_f64(X_bits)
+    T, d = X.shape
+    d_out = W_bits.shape[0]
+    if d % group != 0:
+        raise ValueError("group must divide d")
+    sel = np.arange(d_out) if rows is None else np.asarray(rows)
+    Wsel = np.asarray(W_bits)[sel]
+
+    n = channel_norms(X, p)
+    dh, dhi = diag_scales(n, lam, alpha)
+    dh32 = dh.astype(np.float32) if dh32_override is None else \
+        np.asarray(dh32_override, dtype=np.float32)
+
+    q, s, m = encode_groups_fp32(bf16_to_f32(Wsel), dh32, bits, group)
+    W_hat = dequantize(q, s, m, dhi, group)
+    Y = X @ W_hat.T
+    if B_bits is not None and A_bits is not None and np.asarray(A_bits).size:
+        A = bf16_to_f64(A_bits)
+        Bm = bf16_to_f64(np.asarray(B_bits)[sel])
+        Z = X @ A.T                       # (A X) stored token-major [T, r]
+        Y = Y + Z @ Bm.T                  # + B (A X)   ([ZH] Sec. 2.2)
+    out = dict(n=n, dh=dh, dhi=dhi, dh32=dh32, q=q, s=s, m=m, Y=Y, rows=sel)
+    if want_t:
+        t, u, mm, ss = pre_rounding_fp64(bf16_to_f64(Wsel), dh, bits, group)
+        out.update(t64=t, u64=u, m64=mm, s64=ss)
+    return out
+
+
+def ttq_linear_batched(W_bits, X_bits, **kw) -> list:
+    """R independent requests on a shared W (and B, A): one D per request."""
+    return [ttq_linear(W_bits, X_bits[r], **kw) for r in range(X_bits.shape[0])]
+
+
+# --------------------------------------------------------------------------
+# code-parity band
+# --------------------------------------------------------------------------
+def band_excused(q_gpu: np.ndarray, q_ref: np.ndarray, t64: np.ndarray,
+                 u64: np.ndarray, m64: np.ndarray, s64: np.ndarray,
+                 group: int, rel: float = 1e-6):
+    """Classify code mismatches.
+
+    A mismatch is excused iff the two codes are adjacent (k, k+1) and the
+    float64 pre-rounding value t* lies within ``rel`` of the boundary k + 1/2,
+    relative to max(|t*|, (|u| + |min|)/s), the size of the operands that
+    enter the subtraction.  Returns ``(n_mismatch, n_excused, n_literal)``,
+    where ``n_literal`` counts mismatches inside the literal band
+    ``rel * (k + 1/2)``.
+    """
+    q_gpu = np.asarray(q_gpu).astype(np.int64)
+    q_ref = np.asarray(q_ref).astype(np.int64)
+    bad = q_gpu != q_ref
+    nb = int(bad.sum())
+    if nb == 0:
+        return 0, 0, 0
+    rows, d = q_ref.shape
+    G = d // group
+    mm = np.repeat(m64, group, axis=1)
+    ss = np.repeat(s64, group, axis=1)
+    k = np.minimum(q_gpu, q_ref)
+    adjacent = np.abs(q_gpu - q_ref) == 1
+    dist = np.abs(t64 - (k + 0.5))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = np.maximum(np.abs(t64), (np.abs(u64) + np.abs(mm)) / ss)
+    exc = bad & adjacent & (dist <= rel * scale)
+    lit = bad & adjacent & (dist <= rel * (k + 0.5))
+    return nb, int(exc.sum()), int(lit.sum())
+
+
+# --------------------------------------------------------------------------
+# [BLOG-EN] maths: the symmetric b-bit quantizer of the worked example
+# --------------------------------------------------------------------------
+def symmetric_quantize(x: np.ndarray, bits: int):
+    """Symmetric round-to-nearest with s = max|x| / (2^{b-1} - 1).
+
+    Returns ``(q, s, x_hat)``; q in [-(2^{b-1}-1), 2^{b-1}-1], x_hat = s q.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    L = 2 ** (bits - 1) - 1
+    s = float(np.max(np.abs(x))) / L
+    if s == 0.0:
+        return np.zeros_like(x, dtype=np.int64), 0.0, np.zeros_like(x)
+    q = np.clip(np.rint(x / s), -L, L).astype(np.int64)
+    return q, s, s * q
+
+
+def overhead_ratio(d_out: int, T: int) -> float:
+    """The pages' relative overhead of the online statistics, 1/d' + 3/T
+    ([ZH] Sec. 2.3)."""
+    return 1.0 / d_out + 3.0 / T if T > 0 else math.inf
