@@ -1,0 +1,162 @@
+/*
+ * ttq.h -- C ABI of the TTQ linear projection on AMD Instinct MI355X (gfx950).
+ *
+ * TTQ (activation-aware test-time quantization, arXiv:2603.19296) quantizes
+ * the weights of a linear layer on the fly from the activations of the
+ * current call, with no calibration data and no state kept between calls.
+ * For activations X (d input channels x T tokens) and weights W (d' x d)
+ * one call computes
+ *
+ *   n_i      = ||X_{i,:}||_p                        L_p norm of channel i
+ *   D_ii     = (n_i + lambda)^alpha                 damped diagonal
+ *   W_hat    = Q[W D^{1/2}] D^{-1/2}                group quantize-dequantize
+ *   Y        = W_hat X + B (A X)                    plus the static low rank
+ *
+ * as defined in "TTQ: Activation-Aware Test-Time Quantization to Accelerate
+ * LLM Inference On The Fly" (gist.science zh summary, Sec. 2.1 for D and
+ * W_hat, Sec. 2.2 for the low-rank term; the nl and it summaries, Sec. 2,
+ * restate both).  Q is the asymmetric b-bit affine quantizer of the blog
+ * "Test-time quantization: quantising on the fly with no calibration
+ * dataset", section "The maths that matter", applied to groups of `group`
+ * consecutive input channels of each output row, with a min-anchored real
+ * zero point: s = (max - min)/(2^b - 1), q = clamp(rint((u - min)/s)),
+ * u_hat = min + s q.  Codes are decided in IEEE float32:
+ *   dh = float32(D^{1/2}); u = w*dh; s = (max-min)/N; inv = 1/s (0 if s=0);
+ *   t = (u - min)*inv; q = clamp(rint_half_even(t), 0, N)
+ * with every operation correctly rounded and no fused multiply-add.  The
+ * statistics (norms and powers) are evaluated in float64.
+ *
+ * Memory layout (all row-major, bfloat16 = raw 16-bit patterns):
+ *   W  [d_out][d]      bf16    (nn.Linear weight layout)
+ *   X  [T][d]          bf16    (token-major; batched: [R][T][d])
+ *   B  [d_out][rank]   bf16    A [rank][d] bf16   (both NULL if rank == 0)
+ *   Y  [T][d_out]      float32 (batched: [R][T][d_out])
+ *
+ * Ownership and ordering: every pointer is caller-owned device memory (or
+ * NULL where optional).  The library never allocates, frees or synchronizes
+ * on the calling path: it validates arguments on the host, enqueues kernels
+ * on `stream` (a hipStream_t; NULL is the null stream) and returns.  Device
+ * faults surface at the caller's next synchronization.  Results are
+ * deterministic: identical inputs give bit-identical outputs.
+ *
+ * Errors: validation happens before anything is enqueued, so a negative
+ * status means nothing was launched -- except TTQ_EHIP, which reports a
+ * failed launch (some earlier kernels of the same call may have been
+ * enqueued); the raw hipError_t is then available from ttq_last_hip_error().
+ */
+#ifndef TTQ_H_
+#define TTQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  TTQ_OK = 0,
+  TTQ_EINVAL = -1,       /* a size or scalar argument is out of range          */
+  TTQ_ENULL = -2,        /* a required pointer is NULL                          */
+  TTQ_EALIGN = -3,       /* a pointer is not aligned as required                */
+  TTQ_EWORKSPACE = -4,   /* workspace smaller than ttq_workspace_bytes()        */
+  TTQ_EUNSUPPORTED = -5, /* valid by the method, not supported by this library  */
+  TTQ_EHIP = -100        /* a HIP runtime call failed; see ttq_last_hip_error() */
+};
+
+/* flags */
+#define TTQ_FLAG_FORCE_FUSED 1u    /* use the single-pass fused path (T <= 128) */
+#define TTQ_FLAG_FORCE_TWO_PHASE 2u /* quantize pass + GEMM, at any T            */
+
+/* One projection's shape and the method's constants.
+ *   d      input channels; >= 1 and a multiple of `group`
+ *   d_out  output channels; >= 0
+ *   T      tokens per request; >= 0 (T = 0: Y is empty, codes/scales are
+ *          still produced from zero statistics)
+ *   rank   low-rank r; 0 = no low-rank term; otherwise a multiple of 8, <= 1024
+ *   bits   code width b in 1..8
+ *   group  group size along d: 32, 64, 128 or 256
+ *   p      norm order, finite and > 0 (1 and 2 are exact; others use pow)
+ *   lambda damping, finite and >= 0
+ *   alpha  exponent, finite and >= 0 (0 gives D = I, i.e. plain RTN)
+ *   flags  0, or one TTQ_FLAG_* path override                                */
+typedef struct ttq_params {
+  int64_t d;
+  int64_t d_out;
+  int64_t T;
+  int64_t rank;
+  int32_t bits;
+  int32_t group;
+  double p;
+  double lambda;
+  double alpha;
+  uint32_t flags;
+  uint32_t reserved;
+} ttq_params;
+
+/* Device workspace, in bytes, that ttq_linear (n_requests = 1) or
+ * ttq_linear_batched needs for these parameters.  Writes *bytes; returns a
+ * status (the same validation as the compute calls, minus pointers). */
+int ttq_workspace_bytes(const ttq_params* prm, int64_t n_requests,
+                        size_t* bytes);
+
+/* One TTQ linear call (one request).
+ *   W, X             required (X may be NULL when T == 0); 16-byte aligned
+ *   B, A             required iff rank > 0; 16-byte aligned
+ *   Y                [T][d_out] float32; required iff T*d_out > 0; 4-byte aligned
+ *   codes_out        optional [d_out][d] uint8 codes q
+ *   scales_out       optional [d_out][d/group] float32 scales s
+ *   mins_out         optional [d_out][d/group] float32 group minima (zero points)
+ *   dhalf_out        optional [d] float32 D^{1/2} as fed to the code decision
+ *   workspace        device scratch of at least ttq_workspace_bytes(prm, 1);
+ *                    256-byte aligned; contents need not be initialized and
+ *                    are clobbered; must not be shared by concurrent calls
+ *   stream           hipStream_t to enqueue on
+ * Returns TTQ_OK or a negative status. */
+int ttq_linear(const ttq_params* prm, const void* W, const void* X,
+               const void* B, const void* A, float* Y, uint8_t* codes_out,
+               float* scales_out, float* mins_out, float* dhalf_out,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* R independent requests on one shared W (and B, A): each request has its
+ * own statistics D computed from its own X (multitenant traffic).  X is
+ * [R][T][d], Y [R][T][d_out]; the optional outputs gain a leading [R]
+ * dimension.  n_requests = 0 is a valid no-op. */
+int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
+                       const void* W, const void* X, const void* B,
+                       const void* A, float* Y, uint8_t* codes_out,
+                       float* scales_out, float* mins_out, float* dhalf_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Which path a call with these parameters takes: 0 = fused single pass over
+ * W (statistics kernel + one fused quantize/MFMA kernel), 1 = two phase
+ * (statistics, quantize pass writing W_hat, MFMA GEMM).  Negative = status. */
+int ttq_path(const ttq_params* prm, int64_t n_requests);
+
+/* Human-readable text of a status code (static storage). */
+const char* ttq_status_string(int status);
+
+/* The hipError_t of the last failed HIP call on this thread (0 if none). */
+int ttq_last_hip_error(void);
+
+/* Library version string (static storage). */
+const char* ttq_version(void);
+
+/* ---- measurement ------------------------------------------------------
+ * When enabled, every kernel the library launches is bracketed by a pair of
+ * hipEvents recorded on the launch stream, and ttq_timing_query() sums
+ * their elapsed times per kernel kind.  For measurement only: the timing
+ * state is process-global and not thread-safe; query synchronizes on the
+ * recorded events. */
+int ttq_timing_enable(int on);
+int ttq_timing_reset(void);
+int ttq_kernel_count(void);
+const char* ttq_kernel_name(int kernel);
+int ttq_timing_query(int kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTQ_H_ */

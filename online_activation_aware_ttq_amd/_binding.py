@@ -1,0 +1,244 @@
+"""ctypes binding of ``libttq.so`` (the C ABI in ``include/ttq.h``).
+
+Argument marshalling only: every step of the projection runs in the gfx950
+kernels of the library.  Torch is used for device memory and streams.  If the
+library has not been built, importing the compute functions raises -- there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libttq.so")
+
+TTQ_OK = 0
+TTQ_EINVAL = -1
+TTQ_ENULL = -2
+TTQ_EALIGN = -3
+TTQ_EWORKSPACE = -4
+TTQ_EUNSUPPORTED = -5
+TTQ_EHIP = -100
+
+TTQ_FLAG_FORCE_FUSED = 1
+TTQ_FLAG_FORCE_TWO_PHASE = 2
+
+# Every entry point include/ttq.h declares, with its ctypes signature.
+_c = ctypes
+_vp = _c.c_void_p
+EXPORTS = {
+    "ttq_workspace_bytes": (_c.c_int, [_vp, _c.c_int64, _c.POINTER(_c.c_size_t)]),
+    "ttq_linear": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _vp, _c.c_size_t, _vp]),
+    "ttq_linear_batched": (_c.c_int, [_vp, _c.c_int64, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
+                                      _vp]),
+    "ttq_path": (_c.c_int, [_vp, _c.c_int64]),
+    "ttq_status_string": (_c.c_char_p, [_c.c_int]),
+    "ttq_last_hip_error": (_c.c_int, []),
+    "ttq_version": (_c.c_char_p, []),
+    "ttq_timing_enable": (_c.c_int, [_c.c_int]),
+    "ttq_timing_reset": (_c.c_int, []),
+    "ttq_kernel_count": (_c.c_int, []),
+    "ttq_kernel_name": (_c.c_char_p, [_c.c_int]),
+    "ttq_timing_query": (_c.c_int, [_c.c_int, _c.POINTER(_c.c_double),
+                                    _c.POINTER(_c.c_int64)]),
+}
+
+
+class ttq_params(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int64),
+        ("d_out", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("rank", ctypes.c_int64),
+        ("bits", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("p", ctypes.c_double),
+        ("lambda_", ctypes.c_double),
+        ("alpha", ctypes.c_double),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class TTQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = ttq_status_string(status)
+        if status == TTQ_EHIP:
+            msg += f" (hipError {load_library().ttq_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree ``libttq.so``; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m online_activation_aware_ttq_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def make_params(*, d: int, d_out: int, T: int, rank: int = 0, bits: int,
+                group: int, p: float, lam: float, alpha: float,
+                flags: int = 0) -> ttq_params:
+    return ttq_params(int(d), int(d_out), int(T), int(rank), int(bits),
+                      int(group), float(p), float(lam), float(alpha),
+                      int(flags), 0)
+
+
+def ttq_status_string(status: int) -> str:
+    return load_library().ttq_status_string(int(status)).decode()
+
+
+def ttq_version() -> str:
+    return load_library().ttq_version().decode()
+
+
+def ttq_workspace_bytes(prm: ttq_params, n_requests: int = 1) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().ttq_workspace_bytes(ctypes.byref(prm), int(n_requests),
+                                            ctypes.byref(out))
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_workspace_bytes")
+    return int(out.value)
+
+
+def ttq_path(prm: ttq_params, n_requests: int = 1) -> int:
+    st = load_library().ttq_path(ctypes.byref(prm), int(n_requests))
+    if st < 0:
+        raise TTQError(st, "ttq_path")
+    return st
+
+
+# ------------------------------------------------------------------ torch side
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype, shape, device):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
+          codes_out, scales_out, mins_out, dhalf_out, workspace, stream,
+          flags):
+    import torch
+    lib = load_library()
+    if batched:
+        R, T, d = X.shape
+    else:
+        (T, d), R = X.shape, 1
+    d_out = W.shape[0]
+    rank = 0 if A is None else A.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("W must be a GPU tensor")
+    lead = (R,) if batched else ()
+    G = d // group if group > 0 and d % group == 0 else 0
+    _check(W, "W", torch.bfloat16, (d_out, d), dev)
+    _check(X, "X", torch.bfloat16, lead + (T, d), dev)
+    _check(B, "B", torch.bfloat16, (d_out, rank), dev)
+    _check(A, "A", torch.bfloat16, (rank, d), dev)
+    if (A is None) != (B is None):
+        raise ValueError("pass both B and A or neither")
+    prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
+                      group=group, p=p, lam=lam, alpha=alpha, flags=flags)
+    need = ttq_workspace_bytes(prm, R)
+    if Y is None:
+        Y = torch.empty(lead + (T, d_out), dtype=torch.float32, device=dev)
+    _check(Y, "Y", torch.float32, lead + (T, d_out), dev)
+    _check(codes_out, "codes_out", torch.uint8, lead + (d_out, d), dev)
+    _check(scales_out, "scales_out", torch.float32, lead + (d_out, G), dev)
+    _check(mins_out, "mins_out", torch.float32, lead + (d_out, G), dev)
+    _check(dhalf_out, "dhalf_out", torch.float32, lead + (d,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    args = [_ptr(W), _ptr(X), _ptr(B), _ptr(A), _ptr(Y), _ptr(codes_out),
+            _ptr(scales_out), _ptr(mins_out), _ptr(dhalf_out),
+            _ptr(workspace), workspace.numel(), stream]
+    if batched:
+        st = lib.ttq_linear_batched(ctypes.byref(prm), R, *args)
+    else:
+        st = lib.ttq_linear(ctypes.byref(prm), *args)
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_linear_batched" if batched else "ttq_linear")
+    return Y
+
+
+def ttq_linear(W, X, B=None, A=None, *, p: float, lam: float, alpha: float,
+               bits: int, group: int, Y=None, codes_out=None, scales_out=None,
+               mins_out=None, dhalf_out=None, workspace=None, stream=None,
+               flags: int = 0):
+    """Y[T, d_out] = Q_D[W] X + B (A X) for one request (see include/ttq.h).
+
+    W [d_out, d], X [T, d], B [d_out, r], A [r, d] are bfloat16 GPU tensors;
+    Y is float32.  Enqueued on ``stream`` (default: torch's current stream).
+    """
+    return _call(False, W, X, B, A, p=p, lam=lam, alpha=alpha, bits=bits,
+                 group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
+                 mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
+                 stream=stream, flags=flags)
+
+
+def ttq_linear_batched(W, X, B=None, A=None, *, p: float, lam: float,
+                       alpha: float, bits: int, group: int, Y=None,
+                       codes_out=None, scales_out=None, mins_out=None,
+                       dhalf_out=None, workspace=None, stream=None,
+                       flags: int = 0):
+    """R requests with their own statistics on a shared W: X [R, T, d]."""
+    return _call(True, W, X, B, A, p=p, lam=lam, alpha=alpha, bits=bits,
+                 group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
+                 mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
+                 stream=stream, flags=flags)
+
+
+# ------------------------------------------------------------------ timing
+def timing_enable(on: bool = True) -> None:
+    load_library().ttq_timing_enable(1 if on else 0)
+
+
+def timing_reset() -> None:
+    load_library().ttq_timing_reset()
+
+
+def timing_query() -> dict:
+    """{kernel name: (total milliseconds, launches)} for recorded launches."""
+    lib = load_library()
+    out = {}
+    for k in range(lib.ttq_kernel_count()):
+        ms = ctypes.c_double(0.0)
+        n = ctypes.c_int64(0)
+        st = lib.ttq_timing_query(k, ctypes.byref(ms), ctypes.byref(n))
+        if st != TTQ_OK:
+            raise TTQError(st, "ttq_timing_query")
+        out[lib.ttq_kernel_name(k).decode()] = (ms.value, n.value)
+    return out

@@ -1,0 +1,91 @@
+"""Build the gfx950 TTQ library (``libttq.so``) in-tree with hipcc.
+
+Usage: ``python -m online_activation_aware_ttq_amd.build [-v]``.
+
+Every HIP translation unit is compiled with
+  * ``--offload-arch=gfx950`` (MI355X, CDNA4),
+  * ``-ffp-contract=off``: the code decision is a fixed float32 sequence and
+    must not be fused into multiply-adds (the kernels write ``fmaf`` where a
+    fused multiply-add is wanted),
+  * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed fp32
+    VALU instructions are generated.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "libttq.so")
+
+SOURCES = [
+    "k_stats.hip",
+    "k_fused.hip",
+    "k_quant.hip",
+    "k_gemm.hip",
+    "k_lowrank.hip",
+    "ttq_api.cpp",
+]
+
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-variable",
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libttq.so)")
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or res.returncode != 0:
+        out = (res.stdout + res.stderr).strip()
+        # the host pass does not know the gfx feature flag; that note is noise
+        out = "\n".join(x for x in out.splitlines()
+                        if "packed-fp32-ops" not in x)
+        if out:
+            print(out, file=sys.stderr)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
+def build(verbose: bool = False, jobs: int = 6) -> str:
+    """Compile all sources and link ``libttq.so``; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+           *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        print(res.stdout + res.stderr, file=sys.stderr)
+        raise RuntimeError("linking libttq.so failed")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,348 @@
+// Fused single-pass TTQ projection for small token counts (T <= 128).
+//
+// Each bf16 weight element is read from HBM exactly once.  In registers it
+// is scaled by D^{1/2}, the group min/max are reduced, the b-bit code is
+// decided in float32 and the contraction with the activations runs on the
+// gfx950 matrix cores:
+//
+//   Y[t,i] = sum_k  s_ik * sum_{j in k} q_ij x'_tj  +  m_ik * sum_{j in k} x'_tj
+//
+// where x' = x D^{-1/2} and (s_ik, m_ik) are the group scale and minimum.
+// This is the dequantized product (m + s q) D^{-1/2} X of "TTQ:
+// Activation-Aware Test-Time Quantization ..." (gist.science zh summary,
+// Sec. 2.1) regrouped so that the integer codes -- exact in bf16 -- are the
+// MFMA operand and the per-group affine terms are applied once per group to
+// the fp32 accumulators.  The static low-rank term B (A X) (same page, Sec.
+// 2.2) is one more MFMA chain on Z = A X.
+//
+// Activation operand: for T <= 16 one outlier channel can dominate every
+// output of a token, so a single bf16 rounding of its x' would be shared by
+// all of them; there x' is carried as a bf16 pair hi + lo (~16 significant
+// bits) and both halves are contracted.  For T > 16 x' is rounded once to
+// bf16 and the rounding errors average over the tokens.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16 with A = x' (16 tokens x 32 channels) and
+// B = codes (32 channels x 16 weight rows).  Lane l holds weight row l & 15
+// and channels 8*(l >> 4) .. +8 of each 32-channel step -- exactly one 16-byte
+// load of W -- so the group statistics of a row live in the 4 lanes
+// {l, l^16, l^32, l^48}, and the accumulators of row l & 15 land in the same
+// lane that owns its scale and minimum.
+//
+// Work split: a workgroup of 8 waves owns 16 weight rows and all of K; waves
+// stride over the groups and meet once in LDS at the end (fixed order, no
+// inter-workgroup traffic, deterministic).  D^{1/2} of the request is staged
+// in LDS once per workgroup (when it fits).  Workgroup indices are laid out so that
+// the R requests of one weight tile run back to back on the same XCD and
+// share the tile through its L2.
+#include "ttq_internal.h"
+
+namespace ttq {
+
+constexpr int FW = 8;  // waves per workgroup
+
+template <int NTB, int GS, bool DH_LDS>
+__global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
+  constexpr int NKS = GS / 32;
+  constexpr bool HILO = (NTB == 1);
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+
+  const int64_t b = blockIdx.x;
+  const int xcd = (int)(b & 7);
+  const int64_t jb = b >> 3;
+  const int64_t rb = (jb / a.R) * 8 + xcd;
+  const int req = (int)(jb % a.R);
+  if (rb >= a.rowblocks) return;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int lr = l & 15, qd = l >> 4;
+  const int64_t row = rb * 16 + lr;
+  const bool row_ok = row < a.d_out;
+  const int64_t T = a.T, d = a.d;
+  const int G = a.G;
+  const int Tp = NTB * 16;
+
+  const float* dhg = a.dh + (int64_t)req * d;
+  const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 : 1) * T * d;
+  const bf16_t* xs_lo = xs + T * d;
+  const float* sx = a.sx + (int64_t)req * G * Tp;
+  // rows past d_out read row 0 (valid memory); their results are discarded
+  const bf16_t* Wq = a.W + (row_ok ? row : 0) * d + qd * 8;
+  const float Nf = a.Nf;
+
+  f32x4 acc[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // T <= 16: lane l holds token l & 15 of the activation operand
+  u32x4 xh[NKS], xl[NKS];
+  f32x4 sxv0;
+
+  auto load_w = [&](u32x4 (&wv)[NKS], int g) {
+#pragma unroll
+    for (int k = 0; k < NKS; ++k)
+      wv[k] = *(const u32x4*)(Wq + (int64_t)g * GS + k * 32);
+  };
+  // lanes whose token is past T read a small zero buffer instead of
+  // branching (no divergent load paths for the wait-count logic)
+  const bool tok_ok = lr < T;
+  auto load_x = [&](int g) {
+    if (NTB == 1) {
+      const int64_t colg = (int64_t)g * GS + qd * 8;
+      const bf16_t* ph = tok_ok ? xs + lr * d + colg : a.zeros + qd * 8;
+      const bf16_t* pl = tok_ok ? xs_lo + lr * d + colg : a.zeros + qd * 8;
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        xh[k] = *(const u32x4*)(ph + k * 32);
+        xl[k] = *(const u32x4*)(pl + k * 32);
+      }
+      sxv0 = *(const f32x4*)(sx + (int64_t)g * Tp + qd * 4);
+    }
+  };
+
+  auto process = [&](const u32x4 (&wv)[NKS], int g) {
+    const int64_t colg = (int64_t)g * GS + qd * 8;
+    // u = fl(w * dh), group min / max
+    float u[NKS][8];
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+      f32x4 d0, d1;
+      if (DH_LDS) {
+        d0 = *(const f32x4*)(lds + colg + k * 32);
+        d1 = *(const f32x4*)(lds + colg + k * 32 + 4);
+      } else {
+        d0 = *(const f32x4*)(dhg + colg + k * 32);
+        d1 = *(const f32x4*)(dhg + colg + k * 32 + 4);
+      }
+      u[k][0] = bf16lo(wv[k].x) * d0.x;
+      u[k][1] = bf16hi(wv[k].x) * d0.y;
+      u[k][2] = bf16lo(wv[k].y) * d0.z;
+      u[k][3] = bf16hi(wv[k].y) * d0.w;
+      u[k][4] = bf16lo(wv[k].z) * d1.x;
+      u[k][5] = bf16hi(wv[k].z) * d1.y;
+      u[k][6] = bf16lo(wv[k].w) * d1.z;
+      u[k][7] = bf16hi(wv[k].w) * d1.w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mn = fminf(mn, u[k][j]);
+        mx = fmaxf(mx, u[k][j]);
+      }
+    }
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    // s = fl(fl(M - m) / N), inv = fl(1 / s); IEEE division, no contraction
+    const float s = (mx - mn) / Nf;
+    const float inv = s > 0.f ? 1.0f / s : 0.f;
+
+    // codes q = rint(fl(fl(u - m) * inv)), packed as bf16 pairs.  The clamp to
+    // [0, N] of the definition is a no-op here: 0 <= u - m <= M - m, and the
+    // largest t is N (1 + e) with |e| < 4e-7 for the three roundings, so
+    // rint(t) stays in [0, N] for every finite input (NaN propagates to Y).
+    u32x4 qv[NKS];
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+      float q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        q[j] = __builtin_rintf((u[k][j] - mn) * inv);
+      qv[k].x = __builtin_amdgcn_perm(__float_as_uint(q[1]),
+                                      __float_as_uint(q[0]), 0x07060302u);
+      qv[k].y = __builtin_amdgcn_perm(__float_as_uint(q[3]),
+                                      __float_as_uint(q[2]), 0x07060302u);
+      qv[k].z = __builtin_amdgcn_perm(__float_as_uint(q[5]),
+                                      __float_as_uint(q[4]), 0x07060302u);
+      qv[k].w = __builtin_amdgcn_perm(__float_as_uint(q[7]),
+                                      __float_as_uint(q[6]), 0x07060302u);
+      if (a.codes_out && row_ok) {
+        u32x2 c;
+        c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
+              ((unsigned)q[3] << 24);
+        c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
+              ((unsigned)q[7] << 24);
+        *(u32x2*)(a.codes_out + ((int64_t)req * a.d_out + row) * d + colg +
+                  k * 32) = c;
+      }
+    }
+    if (a.s_out && row_ok && qd == 0) {
+      const int64_t o = ((int64_t)req * a.d_out + row) * G + g;
+      a.s_out[o] = s;
+      a.m_out[o] = mn;
+    }
+
+    // contraction on the matrix cores + per-group affine epilogue
+    if (NTB == 1) {
+      f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, xh[k]), __builtin_bit_cast(bf16x8, qv[k]),
+            P, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, xl[k]), __builtin_bit_cast(bf16x8, qv[k]),
+            P, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[0][i] = fmaf(s, P[i], fmaf(mn, sxv0[i], acc[0][i]));
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const int64_t tok = tb * 16 + lr;
+        u32x4 xv[NKS];
+#pragma unroll
+        for (int k = 0; k < NKS; ++k)
+          xv[k] = tok < T ? *(const u32x4*)(xs + tok * d + colg + k * 32)
+                          : u32x4{0u, 0u, 0u, 0u};
+        const f32x4 sxv = *(const f32x4*)(sx + (int64_t)g * Tp + tb * 16 + qd * 4);
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NKS; ++k)
+          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, xv[k]),
+              __builtin_bit_cast(bf16x8, qv[k]), P, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[tb][i] = fmaf(s, P[i], fmaf(mn, sxv[i], acc[tb][i]));
+      }
+    }
+  };
+
+  // two weight register sets in ping-pong: the loads of the next group are
+  // issued after this group's activation loads, so waiting for the latter
+  // does not wait for the former, and no register copies are needed
+  // (the last prefetch re-reads the final group instead of branching)
+  u32x4 wa[NKS], wb[NKS];
+  int g = w;
+  if (DH_LDS) {
+    // D^{1/2} of this request into LDS; the first weight loads are issued
+    // behind the staging loads so that their latencies overlap
+    constexpr int kStage = 4;  // float4 per thread: up to 8192 channels
+    f32x4 st[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int64_t c = ((int64_t)i * FW * 64 + tid) * 4;
+      if (c < d) st[i] = *(const f32x4*)(dhg + c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, min(g, G - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int64_t c = ((int64_t)i * FW * 64 + tid) * 4;
+      if (c < d) *(f32x4*)(lds + c) = st[i];
+    }
+    for (int64_t c = ((int64_t)kStage * FW * 64 + tid) * 4; c < d;
+         c += FW * 64 * 4)
+      *(f32x4*)(lds + c) = *(const f32x4*)(dhg + c);
+    __syncthreads();
+  } else if (g < G) {
+    load_w(wa, g);
+  }
+  // (scheduling barriers keep that issue order: the compiler would otherwise
+  // hoist loads across the prefetch)
+  while (g < G) {
+    load_x(g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wb, min(g + FW, G - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    process(wa, g);
+    g += FW;
+    if (g >= G) break;
+    load_x(g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, min(g + FW, G - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    process(wb, g);
+    g += FW;
+  }
+
+  // static low-rank term B (A X): one more MFMA chain on Z = A X
+  if (a.rank > 0) {
+    const int nk = a.rp / 32;
+    for (int kk = w; kk < nk; kk += FW) {
+      const int c8 = kk * 32 + qd * 8;
+      const u32x4 bv = (row_ok && c8 < a.rank)
+                           ? *(const u32x4*)(a.Blr + row * a.rank + c8)
+                           : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const int64_t tok = tb * 16 + lr;
+        const u32x4 zv =
+            tok < T ? *(const u32x4*)(a.Z + ((int64_t)req * T + tok) * a.rp + c8)
+                    : u32x4{0u, 0u, 0u, 0u};
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, bv),
+            acc[tb], 0, 0, 0);
+      }
+    }
+  }
+
+  // combine the 8 waves in a fixed order (LDS reused after the main loop)
+  if (DH_LDS) __syncthreads();
+  float* red = lds;  // [FW][NTB * 4][64]
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(w * NTB * 4 + tb * 4 + i) * 64 + l] = acc[tb][i];
+  __syncthreads();
+  float* Y = a.Y + (int64_t)req * T * a.d_out;
+  for (int e = tid; e < NTB * 256; e += FW * 64) {
+    const int ti = e >> 6, ll = e & 63;
+    const int64_t tok = (ti >> 2) * 16 + (ll >> 4) * 4 + (ti & 3);
+    const int64_t rowx = rb * 16 + (ll & 15);
+    if (tok < T && rowx < a.d_out) {
+      float v = red[ti * 64 + ll];
+#pragma unroll
+      for (int ww = 1; ww < FW; ++ww) v += red[(ww * NTB * 4 + ti) * 64 + ll];
+      Y[tok * a.d_out + rowx] = v;
+    }
+  }
+}
+
+template <int NTB, bool DHL>
+static hipError_t launch_fused_ntb(const FusedArgs& a, int group, dim3 grid,
+                                   uint32_t lds, const Launch& L) {
+  const dim3 blk(FW * 64);
+  switch (group) {
+    case 32: return ext_launch(k_fused<NTB, 32, DHL>, grid, blk, lds, L, a);
+    case 64: return ext_launch(k_fused<NTB, 64, DHL>, grid, blk, lds, L, a);
+    case 128: return ext_launch(k_fused<NTB, 128, DHL>, grid, blk, lds, L, a);
+    case 256: return ext_launch(k_fused<NTB, 256, DHL>, grid, blk, lds, L, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool DHL>
+static hipError_t launch_fused_dhl(const FusedArgs& a, int ntb, int group,
+                                   dim3 grid, uint32_t lds, const Launch& L) {
+  switch (ntb) {
+    case 1: return launch_fused_ntb<1, DHL>(a, group, grid, lds, L);
+    case 2: return launch_fused_ntb<2, DHL>(a, group, grid, lds, L);
+    case 4: return launch_fused_ntb<4, DHL>(a, group, grid, lds, L);
+    case 8: return launch_fused_ntb<8, DHL>(a, group, grid, lds, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t fused_lds_bytes(int64_t d, int ntb, bool* dh_in_lds) {
+  const size_t red = (size_t)FW * ntb * 4 * 64 * sizeof(float);
+  const size_t dhb = (size_t)d * sizeof(float);
+  *dh_in_lds = dhb <= kFusedDhLdsMax;
+  return *dh_in_lds ? (dhb > red ? dhb : red) : red;
+}
+
+hipError_t launch_fused(const FusedArgs& a, int ntb, int group,
+                        const Launch& L) {
+  const int64_t nblk = ((a.rowblocks + 7) / 8) * 8 * a.R;
+  if (nblk == 0) return hipSuccess;
+  bool dh_in = false;
+  const uint32_t lds = (uint32_t)fused_lds_bytes(a.d, ntb, &dh_in);
+  dim3 grid((unsigned)nblk);
+  return dh_in ? launch_fused_dhl<true>(a, ntb, group, grid, lds, L)
+               : launch_fused_dhl<false>(a, ntb, group, grid, lds, L);
+}
+
+}  // namespace ttq

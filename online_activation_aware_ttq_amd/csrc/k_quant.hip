@@ -1,0 +1,115 @@
+// Quantize pass of the two-phase (large T) TTQ path on gfx950.
+//
+// Reads W once and writes the dequantized operand
+//   W_hat = (m + s q) D^{-1/2}     rounded once to bf16
+// ("TTQ: Activation-Aware Test-Time Quantization ...", gist.science zh
+// summary, Sec. 2.1), which the MFMA GEMM then contracts with the raw bf16
+// activations.  The codes are decided by the same float32 sequence as the
+// fused path.  A wave covers 512 consecutive channels of 8 weight rows: each
+// lane loads 16 bytes per row, a group of g channels lives in g/8 adjacent
+// lanes and is reduced with xor-shuffles inside that lane group.
+#include "ttq_internal.h"
+
+namespace ttq {
+
+constexpr int QROWS = 8;  // weight rows per wave (D^{+-1/2} reused across them)
+
+template <int GS>
+__global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
+  constexpr int LPG = GS / 8;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t nchunk = (a.d + 511) / 512;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + w;
+  const int64_t rgrp = wid / nchunk;
+  const int64_t chunk = wid % nchunk;
+  const int64_t row0 = rgrp * QROWS;
+  if (row0 >= a.d_out) return;  // uniform over the wave
+  const int64_t c0 = chunk * 512 + l * 8;
+  const bool live = c0 < a.d;
+  const float Nf = a.Nf;
+
+  float dh[8], dhi[8];
+  if (live) {
+    const f32x4 h0 = *(const f32x4*)(a.dh + c0);
+    const f32x4 h1 = *(const f32x4*)(a.dh + c0 + 4);
+    const f32x4 i0 = *(const f32x4*)(a.dhi + c0);
+    const f32x4 i1 = *(const f32x4*)(a.dhi + c0 + 4);
+    dh[0] = h0.x; dh[1] = h0.y; dh[2] = h0.z; dh[3] = h0.w;
+    dh[4] = h1.x; dh[5] = h1.y; dh[6] = h1.z; dh[7] = h1.w;
+    dhi[0] = i0.x; dhi[1] = i0.y; dhi[2] = i0.z; dhi[3] = i0.w;
+    dhi[4] = i1.x; dhi[5] = i1.y; dhi[6] = i1.z; dhi[7] = i1.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { dh[j] = 0.f; dhi[j] = 0.f; }
+  }
+
+  u32x4 wv[QROWS];
+#pragma unroll
+  for (int rr = 0; rr < QROWS; ++rr) {
+    const int64_t row = row0 + rr;
+    wv[rr] = (live && row < a.d_out) ? *(const u32x4*)(a.W + row * a.d + c0)
+                                     : u32x4{0u, 0u, 0u, 0u};
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < QROWS; ++rr) {
+    const int64_t row = row0 + rr;
+    float u[8] = {bf16lo(wv[rr].x) * dh[0], bf16hi(wv[rr].x) * dh[1],
+                  bf16lo(wv[rr].y) * dh[2], bf16hi(wv[rr].y) * dh[3],
+                  bf16lo(wv[rr].z) * dh[4], bf16hi(wv[rr].z) * dh[5],
+                  bf16lo(wv[rr].w) * dh[6], bf16hi(wv[rr].w) * dh[7]};
+    float mn = u[0], mx = u[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      mn = fminf(mn, u[j]);
+      mx = fmaxf(mx, u[j]);
+    }
+#pragma unroll
+    for (int off = LPG / 2; off > 0; off >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off));
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    const float s = (mx - mn) / Nf;
+    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      q[j] = __builtin_amdgcn_fmed3f(__builtin_rintf((u[j] - mn) * inv), 0.f,
+                                     Nf);
+    if (!live || row >= a.d_out) continue;
+    u32x4 o;
+    o.x = pack_bf16(fmaf(s, q[0], mn) * dhi[0], fmaf(s, q[1], mn) * dhi[1]);
+    o.y = pack_bf16(fmaf(s, q[2], mn) * dhi[2], fmaf(s, q[3], mn) * dhi[3]);
+    o.z = pack_bf16(fmaf(s, q[4], mn) * dhi[4], fmaf(s, q[5], mn) * dhi[5]);
+    o.w = pack_bf16(fmaf(s, q[6], mn) * dhi[6], fmaf(s, q[7], mn) * dhi[7]);
+    *(u32x4*)(a.What + row * a.d + c0) = o;
+    if (a.codes_out) {
+      u32x2 c;
+      c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
+            ((unsigned)q[3] << 24);
+      c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
+            ((unsigned)q[7] << 24);
+      *(u32x2*)(a.codes_out + row * a.d + c0) = c;
+    }
+    if (a.s_out && (l % LPG) == 0) {
+      const int64_t o2 = row * a.G + c0 / GS;
+      a.s_out[o2] = s;
+      a.m_out[o2] = mn;
+    }
+  }
+}
+
+hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L) {
+  const int64_t nchunk = (a.d + 511) / 512;
+  const int64_t waves = ((a.d_out + QROWS - 1) / QROWS) * nchunk;
+  const dim3 grid((unsigned)((waves + 3) / 4)), blk(256);
+  switch (group) {
+    case 32: return ext_launch(k_quant<32>, grid, blk, 0, L, a);
+    case 64: return ext_launch(k_quant<64>, grid, blk, 0, L, a);
+    case 128: return ext_launch(k_quant<128>, grid, blk, 0, L, a);
+    case 256: return ext_launch(k_quant<256>, grid, blk, 0, L, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ttq

@@ -1,0 +1,237 @@
+// Activation statistics of the TTQ linear projection on gfx950.
+//
+// Per input channel i: n_i = ||X_{i,:}||_p over the tokens, then
+// D^{1/2}_ii = (n_i + lambda)^{alpha/2} and D^{-1/2}_ii = 1 / D^{1/2}_ii
+// ("TTQ: Activation-Aware Test-Time Quantization ...", gist.science zh
+// summary, Sec. 2.1; the norm is not normalised by T, lambda is added to the
+// norm before the power).  Sums and powers are evaluated in float64 -- the
+// CDNA vector unit runs fp64 at the fp32 rate and this reduction is bound by
+// the X read, so the extra precision is free -- and rounded once to fp32.
+//
+// X is token-major [T][d]; a lane owns 8 consecutive channels (one 16-byte
+// load per token), so every load of a wave is a contiguous 1 KiB row piece.
+#include "ttq_internal.h"
+
+namespace ttq {
+
+__device__ __forceinline__ double pow_term(float x, int pmode, double p) {
+  double a = fabs((double)x);
+  if (pmode == 2) return a * a;
+  if (pmode == 1) return a;
+  return a == 0.0 ? 0.0 : pow(a, p);
+}
+
+__device__ __forceinline__ double finish_norm(double S, int pmode, double p) {
+  if (pmode == 2) return sqrt(S);
+  if (pmode == 1) return S;
+  return pow(S, 1.0 / p);
+}
+
+// (n + lambda)^{alpha/2} and its reciprocal; a channel with n + lambda == 0
+// multiplies only zero activations and gets the neutral scale 1.
+__device__ __forceinline__ void diag_half(double n, double lam, double alpha,
+                                          float& dh, float& dhi) {
+  double base = n + lam;
+  double h = 1.0;
+  if (base > 0.0) {
+    // correctly rounded square roots for the common exponents, pow otherwise;
+    // either is within ~1 ulp of float64 before the single fp32 rounding
+    if (alpha == 0.5) h = sqrt(sqrt(base));
+    else if (alpha == 1.0) h = sqrt(base);
+    else if (alpha == 2.0) h = base;
+    else if (alpha != 0.0) h = pow(base, 0.5 * alpha);
+  }
+  dh = (float)h;
+  dhi = (float)(1.0 / h);
+}
+
+__device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
+                                       double p) {
+  acc[0] += pow_term(bf16lo(v.x), pmode, p);
+  acc[1] += pow_term(bf16hi(v.x), pmode, p);
+  acc[2] += pow_term(bf16lo(v.y), pmode, p);
+  acc[3] += pow_term(bf16hi(v.y), pmode, p);
+  acc[4] += pow_term(bf16lo(v.z), pmode, p);
+  acc[5] += pow_term(bf16hi(v.z), pmode, p);
+  acc[6] += pow_term(bf16lo(v.w), pmode, p);
+  acc[7] += pow_term(bf16hi(v.w), pmode, p);
+}
+
+// ---------------------------------------------------------------------------
+// Small T (fused path): a workgroup of 256 threads owns 256 channels and one
+// chunk of 16 tokens.  It reduces the norm of its channels over all T tokens
+// (8 token lanes x 32 channel lanes of 8 channels, float64 partials meeting
+// in LDS), finishes D^{+-1/2} with one thread per channel, then writes, for
+// its 16 tokens only, x' = x * D^{-1/2} and the per-group sums of x'.  The
+// token chunks of a channel block recompute the same norms (T <= 128 rows of
+// 512 bytes, from L2) and the same powers; chunk 0 stores D^{+-1/2}.
+//
+// x' is the MFMA operand of the fused kernel.  For T <= 16 it is carried as an
+// unevaluated pair of bf16 numbers hi + lo (hi = bf16(x'), lo = bf16(x' -
+// hi)), about 16 significant bits: with few tokens one outlier channel can
+// dominate every output and a single bf16 rounding of it would be shared by
+// all of them.  For larger T a single bf16 plane is written.  The group sums
+// are of exactly the values written, padded with zeros to the chunk end.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_stats_small(StatsSmallArgs a) {
+  __shared__ double red[8][256];
+  __shared__ float dhi_l[256];
+  const int tid = threadIdx.x;
+  const int tg = tid >> 5, cl = tid & 31;
+  const int r = blockIdx.z;
+  const int64_t c_base = (int64_t)blockIdx.x * 256;
+  const int64_t c0 = c_base + cl * 8;
+  const int64_t t0 = (int64_t)blockIdx.y * 16;
+  const bool live = c0 < a.d;
+  const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
+
+  if (a.zeros && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 &&
+      tid < (int)(kZeroBytes / 4))
+    ((unsigned*)a.zeros)[tid] = 0u;
+
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (live) {
+    int64_t t = tg;
+    for (; t + 8 < a.T; t += 16) {
+      const u32x4 v0 = *(const u32x4*)(X + t * a.d + c0);
+      const u32x4 v1 = *(const u32x4*)(X + (t + 8) * a.d + c0);
+      accum8(acc, v0, a.pmode, a.p);
+      accum8(acc, v1, a.pmode, a.p);
+    }
+    if (t < a.T) accum8(acc, *(const u32x4*)(X + t * a.d + c0), a.pmode, a.p);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[tg][cl * 8 + j] = acc[j];
+  __syncthreads();
+  {
+    const int64_t c = c_base + tid;
+    double S = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) S += red[k][tid];
+    float dh = 1.f, dhi = 1.f;
+    if (c < a.d) {
+      diag_half(finish_norm(S, a.pmode, a.p), a.lam, a.alpha, dh, dhi);
+      if (blockIdx.y == 0) {
+        a.dh[(int64_t)r * a.d + c] = dh;
+        a.dhi[(int64_t)r * a.d + c] = dhi;
+        if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
+      }
+    }
+    dhi_l[tid] = dhi;
+  }
+  if (!a.xs) return;
+  __syncthreads();
+
+  const int lpg = a.group >> 3;  // lanes per quantization group
+  const int G = (int)(a.d / a.group);
+  bf16_t* xs = a.xs + (int64_t)r * a.planes * a.T * a.d;
+  bf16_t* xs_lo = xs + a.T * a.d;
+  float* sx = a.sx + (int64_t)r * G * a.Tp;
+  float sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sc[j] = dhi_l[cl * 8 + j];
+  for (int64_t t = t0 + tg; t < t0 + 16; t += 8) {
+    float ps = 0.f;
+    if (live && t < a.T) {
+      const u32x4 v = *(const u32x4*)(X + t * a.d + c0);
+      const float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                          bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      unsigned bh[8], bl[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float xp = x[j] * sc[j];
+        bh[j] = f2bf(xp);
+        const float hi = __uint_as_float(bh[j] << 16);
+        bl[j] = f2bf(xp - hi);
+        ps += a.planes == 2 ? hi + __uint_as_float(bl[j] << 16) : hi;
+      }
+      u32x4 o;
+      o.x = bh[0] | (bh[1] << 16);
+      o.y = bh[2] | (bh[3] << 16);
+      o.z = bh[4] | (bh[5] << 16);
+      o.w = bh[6] | (bh[7] << 16);
+      *(u32x4*)(xs + t * a.d + c0) = o;
+      if (a.planes == 2) {
+        u32x4 ol;
+        ol.x = bl[0] | (bl[1] << 16);
+        ol.y = bl[2] | (bl[3] << 16);
+        ol.z = bl[4] | (bl[5] << 16);
+        ol.w = bl[6] | (bl[7] << 16);
+        *(u32x4*)(xs_lo + t * a.d + c0) = ol;
+      }
+    }
+    // lanes of one group are adjacent inside a 32-lane half wave
+    for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    if (live && (cl % lpg) == 0 && t < a.Tp)
+      sx[(int64_t)(c0 / a.group) * a.Tp + t] = ps;
+  }
+}
+
+hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
+  const unsigned chunks = a.xs ? (unsigned)(a.Tp / 16) : 1u;
+  dim3 grid((unsigned)((a.d + 255) / 256), chunks, (unsigned)R);
+  return ext_launch(k_stats_small, grid, dim3(256), 0, L, a);
+}
+
+// ---------------------------------------------------------------------------
+// Large T: token slices reduced by separate waves into float64 partials,
+// then a finalize pass sums the partials in slice order (deterministic).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_stats_partial(StatsSplitArgs a) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int split = blockIdx.y * 4 + w;
+  const int r = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.x * 512 + l * 8;
+  if (split >= a.nsplit || c0 >= a.d) return;
+  const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
+  const int64_t t0 = (int64_t)split * a.tchunk;
+  const int64_t t1 = min(a.T, t0 + a.tchunk);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t t = t0;
+  for (; t + 4 <= t1; t += 4) {
+    u32x4 v0 = *(const u32x4*)(X + (t + 0) * a.d + c0);
+    u32x4 v1 = *(const u32x4*)(X + (t + 1) * a.d + c0);
+    u32x4 v2 = *(const u32x4*)(X + (t + 2) * a.d + c0);
+    u32x4 v3 = *(const u32x4*)(X + (t + 3) * a.d + c0);
+    accum8(acc, v0, a.pmode, a.p);
+    accum8(acc, v1, a.pmode, a.p);
+    accum8(acc, v2, a.pmode, a.p);
+    accum8(acc, v3, a.pmode, a.p);
+  }
+  for (; t < t1; ++t) {
+    u32x4 v = *(const u32x4*)(X + t * a.d + c0);
+    accum8(acc, v, a.pmode, a.p);
+  }
+  double* out = a.partial + ((int64_t)r * a.nsplit + split) * a.d + c0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = acc[j];
+}
+
+__global__ __launch_bounds__(512) void k_stats_final(StatsSplitArgs a) {
+  const int r = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * 512 + threadIdx.x;
+  if (c >= a.d) return;
+  const double* P = a.partial + (int64_t)r * a.nsplit * a.d + c;
+  double S = 0.0;
+  for (int k = 0; k < a.nsplit; ++k) S += P[(int64_t)k * a.d];
+  float dh, dhi;
+  diag_half(finish_norm(S, a.pmode, a.p), a.lam, a.alpha, dh, dhi);
+  a.dh[(int64_t)r * a.d + c] = dh;
+  a.dhi[(int64_t)r * a.d + c] = dhi;
+  if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
+}
+
+hipError_t launch_stats_partial(const StatsSplitArgs& a, int R,
+                                const Launch& L) {
+  if (a.nsplit == 0) return hipSuccess;
+  dim3 grid((unsigned)((a.d + 511) / 512), (unsigned)((a.nsplit + 3) / 4),
+            (unsigned)R);
+  return ext_launch(k_stats_partial, grid, dim3(256), 0, L, a);
+}
+
+hipError_t launch_stats_final(const StatsSplitArgs& a, int R, const Launch& L) {
+  dim3 grid((unsigned)((a.d + 511) / 512), (unsigned)R);
+  return ext_launch(k_stats_final, grid, dim3(512), 0, L, a);
+}
+
+}  // namespace ttq

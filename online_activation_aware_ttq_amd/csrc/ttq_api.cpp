@@ -1,0 +1,384 @@
+// Host side of the TTQ linear projection library: argument validation,
+// path selection, workspace layout and kernel dispatch.  Everything here is
+// plain host code; the arithmetic of the method runs in the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/ttq.h"
+#include "ttq_internal.h"
+
+using namespace ttq;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxD = int64_t(1) << 20;
+constexpr int64_t kMaxDout = int64_t(1) << 22;
+constexpr int64_t kMaxT = int64_t(1) << 22;
+constexpr int64_t kMaxR = 4096;
+constexpr int64_t kMaxElems = int64_t(1) << 34;
+constexpr int kFusedMaxT = 128;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int path = 0;          // 0 fused, 1 two-phase
+  int ntb = 1;           // fused: 16-token blocks (power of two)
+  int G = 0;             // groups per row
+  int planes = 1;        // fused: activation planes (2 = bf16 hi + lo)
+  int64_t rowblocks = 0;
+  int tchunk = 0, nsplit = 0;
+  int64_t rp = 0;        // rank padded to a multiple of 32
+  size_t off_dh = 0, off_dhi = 0, off_xs = 0, off_sx = 0, off_z = 0,
+         off_statp = 0, off_what = 0, off_zeros = 0;
+  size_t total = 0;
+};
+
+bool finite_nonneg(double v) { return std::isfinite(v) && v >= 0.0; }
+
+int validate_params(const ttq_params* prm, int64_t R) {
+  if (!prm) return TTQ_ENULL;
+  if (R < 0 || R > kMaxR) return TTQ_EINVAL;
+  if (prm->d < 1 || prm->d > kMaxD) return TTQ_EINVAL;
+  if (prm->d_out < 0 || prm->d_out > kMaxDout) return TTQ_EINVAL;
+  if (prm->T < 0 || prm->T > kMaxT) return TTQ_EINVAL;
+  if (prm->rank < 0) return TTQ_EINVAL;
+  if (prm->bits < 1 || prm->bits > 8) return TTQ_EINVAL;
+  if (prm->group <= 0 || prm->d % prm->group != 0) return TTQ_EINVAL;
+  if (!(std::isfinite(prm->p) && prm->p > 0.0)) return TTQ_EINVAL;
+  if (!finite_nonneg(prm->lambda) || !finite_nonneg(prm->alpha))
+    return TTQ_EINVAL;
+  const uint32_t known = TTQ_FLAG_FORCE_FUSED | TTQ_FLAG_FORCE_TWO_PHASE;
+  if (prm->flags & ~known) return TTQ_EINVAL;
+  if ((prm->flags & known) == known) return TTQ_EINVAL;
+  if (prm->d * prm->d_out > kMaxElems) return TTQ_EINVAL;
+  if (R * prm->T * prm->d > kMaxElems) return TTQ_EINVAL;
+  if (R * prm->T * prm->d_out > kMaxElems) return TTQ_EINVAL;
+  if (prm->group != 32 && prm->group != 64 && prm->group != 128 &&
+      prm->group != 256)
+    return TTQ_EUNSUPPORTED;
+  if (prm->rank > 0 && (prm->rank % 8 != 0 || prm->rank > 1024))
+    return TTQ_EUNSUPPORTED;
+  if ((prm->flags & TTQ_FLAG_FORCE_FUSED) && prm->T > kFusedMaxT)
+    return TTQ_EUNSUPPORTED;
+  return TTQ_OK;
+}
+
+Plan make_plan(const ttq_params* prm, int64_t R) {
+  Plan P;
+  const int64_t d = prm->d, dout = prm->d_out, T = prm->T;
+  P.G = (int)(d / prm->group);
+  P.rp = prm->rank > 0 ? (prm->rank + 31) / 32 * 32 : 0;
+  bool fused = T <= kFusedMaxT;
+  if (prm->flags & TTQ_FLAG_FORCE_FUSED) fused = true;
+  if (prm->flags & TTQ_FLAG_FORCE_TWO_PHASE) fused = false;
+  P.path = fused ? 0 : 1;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  P.off_dh = take(sizeof(float) * R * d);
+  P.off_dhi = take(sizeof(float) * R * d);
+  if (P.rp > 0) P.off_z = take(sizeof(uint16_t) * R * T * P.rp);
+
+  if (fused) {
+    P.ntb = 1;
+    while (P.ntb * 16 < T) P.ntb *= 2;
+    P.rowblocks = (dout + 15) / 16;
+    P.planes = T <= 16 ? 2 : 1;
+    P.off_xs = take(sizeof(uint16_t) * P.planes * R * T * d);
+    P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
+    P.off_zeros = take(kZeroBytes);
+  } else {
+    P.tchunk = (int)((T + 63) / 64);
+    if (P.tchunk < 32) P.tchunk = 32;
+    P.nsplit = (int)((T + P.tchunk - 1) / P.tchunk);
+    P.off_statp = take(sizeof(double) * R * P.nsplit * d);
+    P.off_what = take(sizeof(uint16_t) * dout * d);
+  }
+  P.total = off;
+  return P;
+}
+
+bool misaligned(const void* p, size_t a) {
+  return p && (reinterpret_cast<uintptr_t>(p) % a) != 0;
+}
+
+// ---------------------------------------------------------------- timing
+struct TimingState {
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[K_NUM_KINDS];
+  std::vector<hipEvent_t> pool;
+  double total_ms[K_NUM_KINDS] = {};
+  int64_t launches[K_NUM_KINDS] = {};
+};
+TimingState g_timing;
+
+const char* kKernelNames[K_NUM_KINDS] = {
+    "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
+    "quant_what", "gemm_mfma", "lowrank_z"};
+
+hipEvent_t take_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch one kernel through `launch(L)`; with timing enabled the runtime
+// stamps the kernel's own start and end into a pair of events.
+template <class F>
+int run(KernelKind kind, hipStream_t s, F&& launch) {
+  Launch L{s, nullptr, nullptr};
+  if (g_timing.enabled) {
+    L.e0 = take_event();
+    L.e1 = take_event();
+    if (!L.e0 || !L.e1) {
+      if (L.e0) g_timing.pool.push_back(L.e0);
+      if (L.e1) g_timing.pool.push_back(L.e1);
+      L.e0 = L.e1 = nullptr;
+    }
+  }
+  const hipError_t err = launch(L);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    if (L.e0) g_timing.pool.push_back(L.e0);
+    if (L.e1) g_timing.pool.push_back(L.e1);
+    return TTQ_EHIP;
+  }
+  if (L.e0) g_timing.pending[kind].push_back({L.e0, L.e1});
+  return TTQ_OK;
+}
+
+int linear_impl(const ttq_params* prm, int64_t R, const void* W,
+                const void* X, const void* B, const void* A, float* Y,
+                uint8_t* codes_out, float* scales_out, float* mins_out,
+                float* dhalf_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int st = validate_params(prm, R);
+  if (st != TTQ_OK) return st;
+  const int64_t d = prm->d, dout = prm->d_out, T = prm->T, rank = prm->rank;
+  if (R == 0) return TTQ_OK;
+  if (dout > 0 && !W) return TTQ_ENULL;
+  if (T > 0 && !X) return TTQ_ENULL;
+  if (T > 0 && dout > 0 && !Y) return TTQ_ENULL;
+  if (rank > 0 && (!B || !A)) return TTQ_ENULL;
+  if ((scales_out == nullptr) != (mins_out == nullptr)) return TTQ_EINVAL;
+  if (misaligned(W, 16) || misaligned(X, 16) || misaligned(B, 16) ||
+      misaligned(A, 16) || misaligned(Y, 4) || misaligned(codes_out, 8) ||
+      misaligned(scales_out, 4) || misaligned(mins_out, 4) ||
+      misaligned(dhalf_out, 4) || misaligned(workspace, 256))
+    return TTQ_EALIGN;
+  const Plan P = make_plan(prm, R);
+  if (P.total > 0 && !workspace) return TTQ_ENULL;
+  if (workspace_bytes < P.total) return TTQ_EWORKSPACE;
+  {
+    const char* inj = std::getenv("TTQ_INJECT_HIP_ERROR");
+    if (inj && inj[0] == '1') {
+      g_last_hip_error = (int)hipErrorLaunchFailure;
+      return TTQ_EHIP;
+    }
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* dh = reinterpret_cast<float*>(ws + P.off_dh);
+  float* dhi = reinterpret_cast<float*>(ws + P.off_dhi);
+  bf16_t* Zb = P.rp > 0 ? reinterpret_cast<bf16_t*>(ws + P.off_z) : nullptr;
+  const bf16_t* Wb = static_cast<const bf16_t*>(W);
+  const bf16_t* Xb = static_cast<const bf16_t*>(X);
+  const bf16_t* Bb = static_cast<const bf16_t*>(B);
+  const bf16_t* Ab = static_cast<const bf16_t*>(A);
+  const int pmode = prm->p == 2.0 ? 2 : (prm->p == 1.0 ? 1 : 0);
+  const float Nf = (float)((1 << prm->bits) - 1);
+  const bool need_quant = dout > 0;
+
+  if (P.path == 0) {
+    StatsSmallArgs sa{};
+    sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = pmode;
+    sa.p = prm->p; sa.lam = prm->lambda; sa.alpha = prm->alpha;
+    sa.dh = dh; sa.dhi = dhi; sa.dh_export = dhalf_out;
+    sa.xs = need_quant ? reinterpret_cast<bf16_t*>(ws + P.off_xs) : nullptr;
+    sa.sx = need_quant ? reinterpret_cast<float*>(ws + P.off_sx) : nullptr;
+    sa.group = prm->group;
+    sa.planes = P.planes;
+    sa.Tp = 16 * P.ntb;
+    sa.zeros = need_quant ? reinterpret_cast<bf16_t*>(ws + P.off_zeros) : nullptr;
+    st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, (int)R, L); });
+    if (st != TTQ_OK) return st;
+    if (!need_quant) return TTQ_OK;
+    if (P.rp > 0 && T > 0) {
+      LowRankZArgs za{Xb, Ab, R * T, d, (int)rank, (int)P.rp, Zb};
+      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      if (st != TTQ_OK) return st;
+    }
+    FusedArgs fa{};
+    fa.W = Wb; fa.d = d; fa.d_out = dout; fa.T = T; fa.G = P.G; fa.Nf = Nf;
+    fa.dh = dh; fa.xs = sa.xs; fa.sx = sa.sx;
+    fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
+    fa.zeros = sa.zeros;
+    fa.Y = Y;
+    fa.rowblocks = P.rowblocks;
+    fa.R = (int)R;
+    fa.codes_out = codes_out; fa.s_out = scales_out; fa.m_out = mins_out;
+    return run(K_FUSED, s, [&](const Launch& L) { return launch_fused(fa, P.ntb, prm->group, L); });
+  }
+
+  // two-phase path
+  StatsSplitArgs ta{};
+  ta.X = Xb; ta.T = T; ta.d = d; ta.pmode = pmode;
+  ta.p = prm->p; ta.lam = prm->lambda; ta.alpha = prm->alpha;
+  ta.tchunk = P.tchunk; ta.nsplit = P.nsplit;
+  ta.partial = reinterpret_cast<double*>(ws + P.off_statp);
+  ta.dh = dh; ta.dhi = dhi; ta.dh_export = dhalf_out;
+  st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_partial(ta, (int)R, L); });
+  if (st != TTQ_OK) return st;
+  st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(ta, (int)R, L); });
+  if (st != TTQ_OK) return st;
+  if (!need_quant) return TTQ_OK;
+  if (P.rp > 0) {
+    GemmArgs za{};
+    za.A1 = Xb; za.lda1 = d; za.B1 = Ab; za.ldb1 = d; za.K1 = d;
+    za.M = R * T; za.N = rank; za.N_store = P.rp;
+    za.Cb = Zb; za.ldc = P.rp;
+    st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_gemm(za, L); });
+    if (st != TTQ_OK) return st;
+  }
+  bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
+  for (int64_t r = 0; r < R; ++r) {
+    QuantArgs qa{};
+    qa.W = Wb; qa.d = d; qa.d_out = dout; qa.G = P.G; qa.Nf = Nf;
+    qa.dh = dh + r * d; qa.dhi = dhi + r * d; qa.What = What;
+    qa.codes_out = codes_out ? codes_out + r * dout * d : nullptr;
+    qa.s_out = scales_out ? scales_out + r * dout * P.G : nullptr;
+    qa.m_out = mins_out ? mins_out + r * dout * P.G : nullptr;
+    st = run(K_QUANT, s, [&](const Launch& L) { return launch_quant(qa, prm->group, L); });
+    if (st != TTQ_OK) return st;
+    GemmArgs ga{};
+    ga.A1 = Xb + r * T * d; ga.lda1 = d; ga.B1 = What; ga.ldb1 = d; ga.K1 = d;
+    if (P.rp > 0) {
+      ga.A2 = Zb + r * T * P.rp; ga.lda2 = P.rp;
+      ga.B2 = Bb; ga.ldb2 = rank; ga.K2 = rank;
+    }
+    ga.M = T; ga.N = dout; ga.N_store = dout;
+    ga.C = Y + r * T * dout; ga.ldc = dout;
+    st = run(K_GEMM, s, [&](const Launch& L) { return launch_gemm(ga, L); });
+    if (st != TTQ_OK) return st;
+  }
+  return TTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttq_workspace_bytes(const ttq_params* prm, int64_t n_requests,
+                        size_t* bytes) {
+  if (!bytes) return TTQ_ENULL;
+  const int st = validate_params(prm, n_requests);
+  if (st != TTQ_OK) return st;
+  *bytes = n_requests == 0 ? 0 : make_plan(prm, n_requests).total;
+  return TTQ_OK;
+}
+
+int ttq_linear(const ttq_params* prm, const void* W, const void* X,
+               const void* B, const void* A, float* Y, uint8_t* codes_out,
+               float* scales_out, float* mins_out, float* dhalf_out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl(prm, 1, W, X, B, A, Y, codes_out, scales_out, mins_out,
+                     dhalf_out, workspace, workspace_bytes, stream);
+}
+
+int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
+                       const void* W, const void* X, const void* B,
+                       const void* A, float* Y, uint8_t* codes_out,
+                       float* scales_out, float* mins_out, float* dhalf_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl(prm, n_requests, W, X, B, A, Y, codes_out, scales_out,
+                     mins_out, dhalf_out, workspace, workspace_bytes, stream);
+}
+
+int ttq_path(const ttq_params* prm, int64_t n_requests) {
+  const int st = validate_params(prm, n_requests);
+  if (st != TTQ_OK) return st;
+  return make_plan(prm, n_requests < 1 ? 1 : n_requests).path;
+}
+
+const char* ttq_status_string(int status) {
+  switch (status) {
+    case TTQ_OK: return "ok";
+    case TTQ_EINVAL: return "invalid argument (size or scalar out of range)";
+    case TTQ_ENULL: return "required pointer is NULL";
+    case TTQ_EALIGN: return "pointer not aligned as required";
+    case TTQ_EWORKSPACE: return "workspace too small";
+    case TTQ_EUNSUPPORTED: return "valid but unsupported configuration";
+    case TTQ_EHIP: return "HIP runtime error (see ttq_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int ttq_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ttq_version(void) { return "ttq-gfx950 0.1.0"; }
+
+int ttq_timing_enable(int on) {
+  g_timing.enabled = on != 0;
+  return TTQ_OK;
+}
+
+int ttq_timing_reset(void) {
+  for (int k = 0; k < K_NUM_KINDS; ++k) {
+    for (auto& pr : g_timing.pending[k]) {
+      (void)hipEventSynchronize(pr.second);
+      g_timing.pool.push_back(pr.first);
+      g_timing.pool.push_back(pr.second);
+    }
+    g_timing.pending[k].clear();
+    g_timing.total_ms[k] = 0.0;
+    g_timing.launches[k] = 0;
+  }
+  return TTQ_OK;
+}
+
+int ttq_kernel_count(void) { return K_NUM_KINDS; }
+
+const char* ttq_kernel_name(int kernel) {
+  if (kernel < 0 || kernel >= K_NUM_KINDS) return nullptr;
+  return kKernelNames[kernel];
+}
+
+int ttq_timing_query(int kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= K_NUM_KINDS) return TTQ_EINVAL;
+  if (!total_ms || !launches) return TTQ_ENULL;
+  for (auto& pr : g_timing.pending[kernel]) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return TTQ_EHIP;
+    }
+    g_timing.total_ms[kernel] += ms;
+    g_timing.launches[kernel] += 1;
+    g_timing.pool.push_back(pr.first);
+    g_timing.pool.push_back(pr.second);
+  }
+  g_timing.pending[kernel].clear();
+  *total_ms = g_timing.total_ms[kernel];
+  *launches = g_timing.launches[kernel];
+  return TTQ_OK;
+}
+
+}  // extern "C"

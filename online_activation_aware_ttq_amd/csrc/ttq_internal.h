@@ -1,0 +1,159 @@
+// Internal declarations shared by the gfx950 kernels and the host layer of
+// the TTQ linear projection.  Not part of the public ABI (include/ttq.h).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttq {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bit pattern
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// Kernel kinds, for the optional event timing.
+enum KernelKind {
+  K_STATS_SMALL = 0,   // norms + diag + scaled activations (T <= 128)
+  K_STATS_PARTIAL,     // norms, partial sums over a token slice
+  K_STATS_FINAL,       // norms finalize + diag
+  K_FUSED,             // fused quantize + MFMA contraction (single W pass)
+  K_QUANT,             // quantize pass writing W_hat (two-phase path)
+  K_GEMM,              // MFMA GEMM Y = X W_hat^T + Z B^T (two-phase path)
+  K_LOWRANK_Z,         // Z = X A^T (low-rank first factor)
+  K_NUM_KINDS
+};
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf16lo(unsigned v) {
+  return __uint_as_float(v << 16);
+}
+__device__ __forceinline__ float bf16hi(unsigned v) {
+  return __uint_as_float(v & 0xffff0000u);
+}
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned f2bf(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// ---------------------------------------------------------------- launchers
+// Where and how to launch: the stream, plus optional events that the runtime
+// stamps with the kernel's own start and end (measurement only).
+struct Launch {
+  hipStream_t s;
+  hipEvent_t e0, e1;
+};
+
+template <typename A>
+inline hipError_t ext_launch(void (*kernel)(A), dim3 grid, dim3 block,
+                             uint32_t lds, const Launch& L, const A& args) {
+  void* argv[] = {const_cast<A*>(&args)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                            argv, lds, L.s, L.e0, L.e1, 0);
+}
+
+struct StatsSmallArgs {
+  const bf16_t* X;      // [R][T][d]
+  int64_t T, d;
+  int pmode;            // 1: p == 1, 2: p == 2, 0: general p
+  double p, lam, alpha;
+  float* dh;            // [R][d]
+  float* dhi;           // [R][d]
+  float* dh_export;     // optional [R][d]
+  bf16_t* xs;           // optional [R][planes][T][d] x * D^{-1/2} (bf16 hi[, lo])
+  float* sx;            // optional [R][G][Tp] group sums of xs, zero past T
+  int group;
+  int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16
+  int Tp;               // padded token count of sx
+  bf16_t* zeros;        // optional kZeroBytes to clear
+};
+hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
+                              const Launch& L);
+
+struct StatsSplitArgs {
+  const bf16_t* X;      // [R][T][d]
+  int64_t T, d;
+  int pmode;
+  double p, lam, alpha;
+  int tchunk, nsplit;
+  double* partial;      // [R][nsplit][d]
+  float* dh;
+  float* dhi;
+  float* dh_export;
+};
+hipError_t launch_stats_partial(const StatsSplitArgs& a, int R,
+                                const Launch& L);
+hipError_t launch_stats_final(const StatsSplitArgs& a, int R, const Launch& L);
+
+struct FusedArgs {
+  const bf16_t* W;      // [d_out][d]
+  int64_t d, d_out, T;
+  int G;                // groups per row
+  float Nf;             // 2^bits - 1
+  const float* dh;      // [R][d]
+  const bf16_t* xs;     // [R][planes][T][d]; planes = 2 (hi, lo) iff T <= 16
+  const float* sx;      // [R][G][Tp], Tp = 16 * ntb, zero past T
+  const bf16_t* Z;      // [R][T][rp] or null
+  const bf16_t* Blr;    // [d_out][rank] or null
+  int rank, rp;
+  const bf16_t* zeros;  // kZeroBytes of zeros (cleared by the stats kernel)
+  float* Y;             // [R][T][d_out]
+  int64_t rowblocks;    // ceil(d_out / 16)
+  int R;
+  uint8_t* codes_out;   // [R][d_out][d]
+  float* s_out;         // [R][d_out][G]
+  float* m_out;         // [R][d_out][G]
+};
+constexpr size_t kZeroBytes = 1024;
+// D^{1/2} is staged in LDS when it fits in this many bytes.
+constexpr size_t kFusedDhLdsMax = 64 * 1024;
+hipError_t launch_fused(const FusedArgs& a, int ntb, int group,
+                        const Launch& L);
+
+struct QuantArgs {
+  const bf16_t* W;      // [d_out][d]
+  int64_t d, d_out;
+  int G;
+  float Nf;
+  const float* dh;      // [d]
+  const float* dhi;     // [d]
+  bf16_t* What;         // [d_out][d]
+  uint8_t* codes_out;   // [d_out][d]
+  float* s_out;
+  float* m_out;
+};
+hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L);
+
+// C[M][N] (+)= A1[M][K1] B1[N][K1]^T + A2[M][K2] B2[N][K2]^T, fp32 accumulate.
+struct GemmArgs {
+  const bf16_t* A1; int64_t lda1;
+  const bf16_t* B1; int64_t ldb1;
+  int64_t K1;
+  const bf16_t* A2; int64_t lda2;   // optional second segment (low rank)
+  const bf16_t* B2; int64_t ldb2;
+  int64_t K2;
+  int64_t M, N;
+  int64_t N_store;                  // columns actually stored (<= ldc)
+  float* C; int64_t ldc;            // fp32 output, or
+  bf16_t* Cb;                       // bf16 output (one of the two)
+};
+hipError_t launch_gemm(const GemmArgs& a, const Launch& L);
+
+struct LowRankZArgs {
+  const bf16_t* X;      // [M][d]
+  const bf16_t* A;      // [rank][d]
+  int64_t M, d;
+  int rank, rp;
+  bf16_t* Z;            // [M][rp]
+};
+hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L);
+
+}  // namespace ttq

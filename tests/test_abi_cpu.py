@@ -1,0 +1,203 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+The library is loaded, every entry point include/ttq.h declares must be
+exported, and every validation error is forced from the host: all of these
+calls return before the library makes any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_activation_aware_ttq_amd as ttq
+from online_activation_aware_ttq_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttq.h")
+
+FAKE = 0x7f0000000000  # 256-byte aligned, never dereferenced by validation
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttq_[a-z_]+)\s*\(", src)))
+
+
+def lib():
+    return ttq.load_library()
+
+
+def prm(**kw):
+    base = dict(d=256, d_out=64, T=16, rank=0, bits=4, group=128, p=2.0,
+                lam=1e-3, alpha=0.5, flags=0)
+    base.update(kw)
+    return ttq.make_params(**base)
+
+
+def call_linear(p, W=FAKE, X=FAKE, Bm=None, A=None, Y=FAKE, codes=None,
+                scales=None, mins=None, dh=None, ws=FAKE, ws_bytes=1 << 40,
+                R=None):
+    L = lib()
+    args = [W, X, Bm, A, Y, codes, scales, mins, dh, ws, ws_bytes, None]
+    if R is None:
+        return L.ttq_linear(ctypes.byref(p) if p is not None else None, *args)
+    return L.ttq_linear_batched(ctypes.byref(p) if p is not None else None, R,
+                                *args)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in B.EXPORTS, f"binding lacks a signature for {n}"
+    assert set(B.EXPORTS) == set(names)
+
+
+def test_params_struct_matches_header_layout():
+    assert ctypes.sizeof(ttq.ttq_params) == 8 * 4 + 4 * 2 + 8 * 3 + 4 * 2
+    assert ttq.ttq_params.p.offset == 40 and ttq.ttq_params.flags.offset == 64
+
+
+def test_status_strings_and_version():
+    for st in (0, -1, -2, -3, -4, -5, -100, 12345):
+        s = ttq.ttq_status_string(st)
+        assert isinstance(s, str) and s
+    assert ttq.ttq_status_string(-4).startswith("workspace")
+    assert "gfx950" in ttq.ttq_version()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=0), ttq.TTQ_EINVAL),
+    (dict(bits=9), ttq.TTQ_EINVAL),
+    (dict(d=0), ttq.TTQ_EINVAL),
+    (dict(d=-1), ttq.TTQ_EINVAL),
+    (dict(d_out=-1), ttq.TTQ_EINVAL),
+    (dict(T=-1), ttq.TTQ_EINVAL),
+    (dict(rank=-1), ttq.TTQ_EINVAL),
+    (dict(group=0), ttq.TTQ_EINVAL),
+    (dict(d=256, group=96), ttq.TTQ_EINVAL),        # does not divide d
+    (dict(d=256, group=16), ttq.TTQ_EUNSUPPORTED),  # divides, not supported
+    (dict(p=0.0), ttq.TTQ_EINVAL),
+    (dict(p=-2.0), ttq.TTQ_EINVAL),
+    (dict(p=float("nan")), ttq.TTQ_EINVAL),
+    (dict(p=float("inf")), ttq.TTQ_EINVAL),
+    (dict(lam=-1e-3), ttq.TTQ_EINVAL),
+    (dict(lam=float("inf")), ttq.TTQ_EINVAL),
+    (dict(alpha=-0.5), ttq.TTQ_EINVAL),
+    (dict(alpha=float("nan")), ttq.TTQ_EINVAL),
+    (dict(rank=12), ttq.TTQ_EUNSUPPORTED),
+    (dict(rank=2048), ttq.TTQ_EUNSUPPORTED),
+    (dict(flags=3), ttq.TTQ_EINVAL),
+    (dict(flags=4), ttq.TTQ_EINVAL),
+    (dict(T=129, flags=1), ttq.TTQ_EUNSUPPORTED),
+])
+def test_invalid_params_rejected_everywhere(kw, status):
+    p = prm(**kw)
+    out = ctypes.c_size_t(7)
+    assert lib().ttq_workspace_bytes(ctypes.byref(p), 1, ctypes.byref(out)) == status
+    assert out.value == 7
+    assert lib().ttq_path(ctypes.byref(p), 1) == status
+    assert call_linear(p) == status
+    assert call_linear(p, R=2) == status
+
+
+def test_valid_edge_params_accepted():
+    for kw in (dict(bits=1), dict(bits=8), dict(group=32, d=32), dict(d_out=0),
+               dict(T=0), dict(rank=8), dict(rank=1024), dict(alpha=0.0),
+               dict(lam=0.0), dict(p=0.37), dict(group=256, d=512),
+               dict(T=128, flags=1), dict(T=1, flags=2)):
+        assert ttq.ttq_workspace_bytes(prm(**kw)) >= 0, kw
+
+
+def test_null_pointers():
+    p = prm()
+    assert lib().ttq_workspace_bytes(None, 1, ctypes.byref(ctypes.c_size_t())) == ttq.TTQ_ENULL
+    assert lib().ttq_workspace_bytes(ctypes.byref(p), 1, None) == ttq.TTQ_ENULL
+    assert call_linear(None) == ttq.TTQ_ENULL
+    assert call_linear(p, W=None) == ttq.TTQ_ENULL
+    assert call_linear(p, X=None) == ttq.TTQ_ENULL
+    assert call_linear(p, Y=None) == ttq.TTQ_ENULL
+    assert call_linear(p, ws=None) == ttq.TTQ_ENULL
+    pr = prm(rank=8)
+    assert call_linear(pr, Bm=FAKE, A=None) == ttq.TTQ_ENULL
+    assert call_linear(pr, Bm=None, A=FAKE) == ttq.TTQ_ENULL
+    # scales without mins (or the reverse) is a usage error
+    assert call_linear(p, scales=FAKE) == ttq.TTQ_EINVAL
+    assert call_linear(p, mins=FAKE) == ttq.TTQ_EINVAL
+
+
+def test_alignment_rules():
+    p = prm()
+    assert call_linear(p, W=FAKE + 8) == ttq.TTQ_EALIGN
+    assert call_linear(p, X=FAKE + 2) == ttq.TTQ_EALIGN
+    assert call_linear(p, Y=FAKE + 2) == ttq.TTQ_EALIGN
+    assert call_linear(p, codes=FAKE + 4) == ttq.TTQ_EALIGN
+    assert call_linear(p, dh=FAKE + 1) == ttq.TTQ_EALIGN
+    assert call_linear(p, ws=FAKE + 128) == ttq.TTQ_EALIGN
+    pr = prm(rank=8)
+    assert call_linear(pr, Bm=FAKE + 8, A=FAKE) == ttq.TTQ_EALIGN
+
+
+def test_workspace_too_small():
+    p = prm()
+    need = ttq.ttq_workspace_bytes(p)
+    assert need > 0
+    assert call_linear(p, ws_bytes=need - 1) == ttq.TTQ_EWORKSPACE
+    assert call_linear(p, ws_bytes=0) == ttq.TTQ_EWORKSPACE
+    need2 = ttq.ttq_workspace_bytes(p, 3)
+    assert need2 > need
+    assert call_linear(p, ws_bytes=need2 - 1, R=3) == ttq.TTQ_EWORKSPACE
+
+
+def test_zero_requests_is_a_no_op():
+    p = prm()
+    assert ttq.ttq_workspace_bytes(p, 0) == 0
+    assert call_linear(p, W=None, X=None, Y=None, ws=None, ws_bytes=0, R=0) == ttq.TTQ_OK
+    assert call_linear(p, R=-1) == ttq.TTQ_EINVAL
+
+
+def test_injected_hip_error_is_reported(monkeypatch):
+    monkeypatch.setenv("TTQ_INJECT_HIP_ERROR", "1")
+    p = prm()
+    assert call_linear(p) == ttq.TTQ_EHIP
+    assert lib().ttq_last_hip_error() != 0
+    with pytest.raises(ttq.TTQError) as ei:
+        raise ttq.TTQError(ttq.TTQ_EHIP, "x")
+    assert "hipError" in str(ei.value)
+
+
+def test_path_selection():
+    assert ttq.ttq_path(prm(T=1)) == 0
+    assert ttq.ttq_path(prm(T=128)) == 0
+    assert ttq.ttq_path(prm(T=129)) == 1
+    assert ttq.ttq_path(prm(T=2048)) == 1
+    assert ttq.ttq_path(prm(T=2048, flags=ttq.TTQ_FLAG_FORCE_FUSED & 0)) == 1
+    assert ttq.ttq_path(prm(T=64, flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE)) == 1
+    assert ttq.ttq_path(prm(T=100, flags=ttq.TTQ_FLAG_FORCE_FUSED)) == 0
+
+
+def test_workspace_grows_with_shape():
+    small = ttq.ttq_workspace_bytes(prm(T=1))
+    big = ttq.ttq_workspace_bytes(prm(T=2048, d_out=11008, rank=64))
+    assert big > small
+    # the two-phase path holds the dequantized bf16 weights
+    assert big >= 11008 * 256 * 2
+
+
+def test_timing_api_without_launches():
+    L = lib()
+    n = L.ttq_kernel_count()
+    assert n >= 5
+    names = [L.ttq_kernel_name(k).decode() for k in range(n)]
+    assert "fused_qdq_mfma" in names and "gemm_mfma" in names
+    assert L.ttq_kernel_name(n) is None
+    ttq.timing_reset()
+    q = ttq.timing_query()
+    assert all(v == (0.0, 0) for v in q.values())
+    ms = ctypes.c_double()
+    cnt = ctypes.c_int64()
+    assert L.ttq_timing_query(-1, ctypes.byref(ms), ctypes.byref(cnt)) == ttq.TTQ_EINVAL

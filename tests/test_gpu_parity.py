@@ -1,0 +1,175 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Reduced shapes span several tiles and ragged tails on both paths (fused
+single pass for T <= 128 and the two-phase quantize + GEMM path), every
+code path of the kernels (group sizes, bit widths, norm orders, low rank,
+batched requests) and the degenerate cases of the method.  The bars are
+written in ``parity_util``.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from parity_util import check_problem, run_gpu
+from workloads import make_c1, make_problem
+
+pytestmark = pytest.mark.gpu
+
+FUSED, TWO = 1, 2
+
+
+def _say(name, rep):
+    print(f"[parity] {name}: " + " ".join(
+        f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}"
+        for k, v in rep.items()), flush=True)
+    log = os.environ.get("TTQ_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps(dict(case=name, **rep)) + "\n")
+
+
+def _run_and_check(prob, flags=0, name=None):
+    print(f"[case] {name or prob.name} d={prob.d} d_out={prob.d_out} T={prob.T} "
+          f"R={prob.R} b={prob.bits} g={prob.group} r={prob.rank} p={prob.p} "
+          f"flags={flags}", flush=True)
+    gpu = run_gpu(prob, flags=flags)
+    rep = check_problem(prob, gpu)
+    _say(name or prob.name, rep)
+    return gpu, rep
+
+
+@pytest.mark.parametrize("flags", [FUSED, TWO])
+def test_c1_both_paths(flags):
+    _run_and_check(make_c1(), flags)
+
+
+CASES = [
+    # name, kwargs (reduced shapes of the standard workloads + edge shapes)
+    ("c2s_T1", dict(d=1024, d_out=1040, T=1, bits=4, group=128,
+                    x_kind="logu10_100", n_outliers=10, seed=1)),
+    ("c2s_T128", dict(d=1024, d_out=1040, T=128, bits=4, group=128,
+                      x_kind="logu10_100", n_outliers=10, seed=1)),
+    ("c3s_gateup", dict(d=512, d_out=1376, T=300, bits=3, group=128, rank=64,
+                        seed=2)),
+    ("c3s_down", dict(d=1376 // 32 * 32, d_out=512, T=200, bits=3, group=32,
+                      rank=64, seed=12)),
+    ("c4s_p1", dict(d=1024, d_out=896, T=512, bits=2, group=64, rank=128,
+                    p=1.0, lam=1e-2, x_kind="t3_logu30_100", n_outliers=5,
+                    seed=3)),
+    ("c4s_p2", dict(d=1024, d_out=896, T=512, bits=2, group=64, rank=128,
+                    p=2.0, lam=1e-2, x_kind="t3_logu30_100", n_outliers=5,
+                    seed=3)),
+    ("ragged_T17_g256", dict(d=768, d_out=40, T=17, bits=5, group=256, seed=21)),
+    ("ragged_T33_g32", dict(d=96, d_out=33, T=33, bits=3, group=32, rank=8,
+                            seed=22)),
+    ("T65_b8", dict(d=256, d_out=100, T=65, bits=8, group=64, seed=23)),
+    ("b1", dict(d=256, d_out=48, T=16, bits=1, group=32, seed=24)),
+    ("p_general", dict(d=256, d_out=64, T=16, bits=4, group=128, p=0.5,
+                       seed=25)),
+    ("p3", dict(d=256, d_out=64, T=129, bits=4, group=64, p=3.0, seed=26)),
+    ("alpha0_rtn", dict(d=256, d_out=64, T=16, bits=3, group=128, alpha=0.0,
+                        seed=27)),
+    ("alpha2_lam0", dict(d=512, d_out=64, T=8, bits=4, group=128, alpha=2.0,
+                         lam=0.0, seed=28)),
+]
+
+
+@pytest.mark.parametrize("flags", [0, FUSED, TWO])
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_reduced_cases(name, kw, flags):
+    prob = make_problem(name, **kw)
+    if flags == FUSED and prob.T > 128:
+        pytest.skip("fused path covers T <= 128")
+    _run_and_check(prob, flags, name)
+
+
+@pytest.mark.parametrize("T", [1, 16, 100, 256])
+@pytest.mark.parametrize("flags", [0, TWO])
+def test_batched_requests(T, flags):
+    prob = make_problem("c5s", d=512, d_out=272, T=T, R=8, bits=4, group=128,
+                        rank=32, x_kind="logu10_100", n_outliers=5, seed=4)
+    gpu, rep = _run_and_check(prob, flags, f"c5s_T{T}")
+    # each request has its own statistics: D differs between requests
+    assert not np.array_equal(gpu["dh"][0], gpu["dh"][1])
+
+
+def test_batched_matches_single_calls():
+    prob = make_problem("bs", d=512, d_out=160, T=4, R=3, bits=4, group=128,
+                        rank=16, seed=31)
+    gb = run_gpu(prob)
+    for r in range(prob.R):
+        single = make_problem("bs", d=512, d_out=160, T=4, R=1, bits=4,
+                              group=128, rank=16, seed=31)
+        single.X = prob.X[r:r + 1]
+        gs = run_gpu(single)
+        np.testing.assert_array_equal(gs["q"][0], gb["q"][r])
+        np.testing.assert_array_equal(gs["dh"][0], gb["dh"][r])
+        np.testing.assert_array_equal(gs["Y"][0], gb["Y"][r])
+
+
+def test_degenerate_groups_and_zero_channels():
+    # constant weight rows (max == min) and all-zero activation channels with
+    # lambda = 0 (n + lambda = 0 -> neutral scale 1)
+    prob = make_problem("deg", d=256, d_out=48, T=8, bits=4, group=64, lam=0.0,
+                        seed=41)
+    prob.W[:5] = prob.W[0, 0]
+    prob.X[0][:, :64] = 0
+    for flags in (FUSED, TWO):
+        gpu, rep = _run_and_check(prob, flags, f"degenerate_f{flags}")
+        # group 0: constant weights times the neutral scale -> max == min
+        assert np.all(gpu["s"][0][:5, 0] == 0)
+        assert np.all(gpu["q"][0][:5, :64] == 0)
+        assert np.all(gpu["s"][0][5:, 0] > 0)
+        assert np.all(gpu["dh"][0][:64] == 1.0)
+
+
+def test_empty_shapes():
+    import torch
+    import online_activation_aware_ttq_amd as ttq
+    from parity_util import to_dev
+    prob = make_problem("e", d=256, d_out=32, T=0, bits=4, group=128, seed=5)
+    gpu, _ = _run_and_check(prob, 0, "T0")
+    ref = oracle.ttq_linear(prob.W, prob.X[0], bits=4, group=128, p=2.0,
+                            lam=1e-3, alpha=0.5)
+    np.testing.assert_array_equal(gpu["q"][0], ref["q"])
+    gpu2, _ = _run_and_check(prob, TWO, "T0_two_phase")
+    np.testing.assert_array_equal(gpu2["q"][0], ref["q"])
+    # d_out = 0: only the statistics are produced
+    p2 = make_problem("e2", d=256, d_out=1, T=5, bits=4, group=128, seed=6)
+    W = to_dev(p2.W)[:0]
+    X = to_dev(p2.X[0])
+    dh = torch.empty(256, dtype=torch.float32, device="cuda")
+    Y = ttq.ttq_linear(W, X, p=2.0, lam=1e-3, alpha=0.5, bits=4, group=128,
+                       dhalf_out=dh)
+    torch.cuda.synchronize()
+    assert Y.shape == (5, 0)
+    ref2 = oracle.ttq_linear(p2.W, p2.X[0], bits=4, group=128, p=2.0,
+                             lam=1e-3, alpha=0.5)
+    np.testing.assert_array_equal(dh.cpu().numpy(), ref2["dh32"])
+    # zero requests
+    Xb = to_dev(p2.X)[:0]
+    Yb = ttq.ttq_linear_batched(to_dev(p2.W), Xb, p=2.0, lam=1e-3, alpha=0.5,
+                                bits=4, group=128)
+    assert Yb.shape == (0, 5, 1)
+
+
+def test_deterministic_and_stateless():
+    prob = make_problem("det", d=1024, d_out=528, T=16, bits=4, group=128,
+                        rank=32, x_kind="logu10_100", n_outliers=10, seed=51)
+    for flags in (FUSED, TWO):
+        a = run_gpu(prob, flags)
+        b = run_gpu(prob, flags)
+        for k in ("Y", "q", "s", "m", "dh"):
+            np.testing.assert_array_equal(a[k], b[k])
+    # a new X (new outlier set) must give new statistics and new codes:
+    # nothing is cached between calls
+    p2 = make_problem("det", d=1024, d_out=528, T=16, bits=4, group=128,
+                      rank=32, x_kind="logu10_100", n_outliers=10, seed=51,
+                      call=1)
+    c = run_gpu(p2)
+    assert not np.array_equal(a["dh"], c["dh"])
+    assert not np.array_equal(a["q"], c["q"])
+    check_problem(p2, c)
