@@ -34,7 +34,9 @@ METRIC = ("TTQ-linear tokens/s per projection + % HBM/MFMA roofline; "
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 640 * 2 ** 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_c2_T1.json")
+KERNEL_SOURCES = {"gemv_t1": "k_gemv.hip", "fused_qdq_mfma": "k_fused.hip",
+                  "stats_small": "k_stats.hip", "gemm_mfma": "k_gemm.hip",
+                  "quant_what": "k_quant.hip"}
 
 
 def parse():
@@ -48,13 +50,25 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only-ttq", action="store_true",
                     help="time only the TTQ step (for profiler runs)")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="after the timed work, run 5 device-to-device copies "
+                         "of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
+                    help="write profiles/ summaries from rocprofv3 output "
+                         "directories (kernel trace, FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--profile-cmd", default="",
+                    help="command lines recorded in the summary")
     return ap.parse_args()
 
 
-def kernel_src_sha() -> str:
+def kernel_src_sha(kernel: str) -> str:
     p = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
-                     "k_fused.hip")
+                     KERNEL_SOURCES.get(kernel, "k_fused.hip"))
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_file(kernel: str, T: int) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_q_proj4096_T{T}.json")
 
 
 def dev_bf16(bits, torch):
@@ -136,7 +150,8 @@ def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
     def step_hot(i):
         ttq.ttq_linear(Ws[0], Xs[i % n_x], Y=Ys[i % n_y], workspace=ws,
                        stream=stream, **kw)
-    out["ms_per_step_hot_w"] = timed(step_hot, max(50, steps // 4), warmup)
+    if want_graph:
+        out["ms_per_step_hot_w"] = timed(step_hot, max(50, steps // 4), warmup)
 
     if want_graph:
         # one graph holding n_w calls (one per W copy), replayed
@@ -196,18 +211,112 @@ def cpu_baseline(T: int, seconds: float):
                       f"host cpu_count={os.cpu_count()}"}
 
 
-def traffic_entry(launch_ms: float):
+def _read_csv(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize(a):
+    """profiles/: kernel-trace summary of the dominant kernel and the HBM
+    traffic per launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
+    same counter reads for a device-to-device copy of known size."""
+    trace, fetch, write = a.summarize
+    stats = _read_csv(trace, "kernel_stats.csv")
+    T = a.T
+    key = {1: "gemv", 128: "k_fused"}.get(T, "k_fused")
+    kname = {1: "gemv_t1"}.get(T, "fused_qdq_mfma")
+    calib_bytes = a.copy_calib_mb * 2 ** 20
+
+    def per_dispatch(rows, counter, match):
+        vals = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+        return vals
+
+    fr = _read_csv(fetch, "counter_collection.csv")
+    wr = _read_csv(write, "counter_collection.csv")
+    k_f = per_dispatch(fr, "FETCH_SIZE", lambda n: key in n)
+    k_w = per_dispatch(wr, "WRITE_SIZE", lambda n: key in n)
+
+    def calib(rows, counter):
+        cp = [r for r in rows if r["Counter_Name"] == counter
+              and "copyBuffer" in r["Kernel_Name"]]
+        cp.sort(key=lambda r: int(r["Dispatch_Id"]))
+        vals = [float(r["Counter_Value"]) for r in cp[-5:]]
+        return sum(vals) / len(vals) if vals else float("nan")
+
+    c_f, c_w = calib(fr, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
+    sf = calib_bytes / (c_f * 1024) if c_f == c_f and c_f > 0 else float("nan")
+    sw = calib_bytes / (c_w * 1024) if c_w == c_w and c_w > 0 else float("nan")
+    f_kib = sum(k_f) / len(k_f)
+    w_kib = sum(k_w) / len(k_w)
+    traffic = f_kib * 1024 * sf + w_kib * 1024 * sw
+    d = d_out = 4096
+    ab = alg_bytes(d, d_out, T)
+    rec = {"kernel": kname, "workload": f"q_proj 4096x4096 T={T}",
+           "kernel_src_sha": kernel_src_sha(kname),
+           "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+           "copy_calib_bytes": calib_bytes,
+           "copy_fetch_kib": c_f, "copy_write_kib": c_w,
+           "fetch_scale": sf, "write_scale": sw,
+           "bytes_per_launch": traffic, "alg_bytes_per_launch": ab,
+           "traffic_over_alg": traffic / ab,
+           "launches_counted": [len(k_f), len(k_w)]}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    json.dump(rec, open(traffic_file(kname, T), "w"), indent=1)
+    lines = [f"# {kname}: 4096x4096 q_proj, T={T} (4-bit g128, p=2)", "",
+             "Commands (from the repository root):", "", "```"]
+    lines += [c for c in a.profile_cmd.split(";;") if c] + ["```", "",
+              "## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
+              "| kernel | calls | avg ns | min ns | max ns |",
+              "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:70]} | {r['Calls']} | "
+                     f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              f"- kernel FETCH_SIZE {f_kib:.0f} KiB/launch, WRITE_SIZE {w_kib:.1f} KiB/launch"
+              f" (averaged over {len(k_f)} / {len(k_w)} launches)",
+              f"- calibration: device-to-device copy of {calib_bytes} bytes reads "
+              f"FETCH_SIZE {c_f:.0f} KiB and WRITE_SIZE {c_w:.0f} KiB; scale "
+              f"factors {sf:.4f} (fetch) and {sw:.4f} (write)",
+              f"- traffic = {traffic / 1e6:.3f} MB/launch against "
+              f"{ab / 1e6:.3f} MB algorithmic (ratio {traffic / ab:.3f})", ""]
+    md = os.path.join(ROOT, "profiles", f"{kname}_q_proj4096_T{T}.md")
+    open(md, "w").write("\n".join(lines))
+    print(json.dumps(rec))
+
+
+def traffic_entry(kernel: str, T: int):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source has changed since it was taken."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(kernel, T)))
     except Exception:
         return None
-    if rec.get("kernel_src_sha") != kernel_src_sha():
+    if rec.get("kernel_src_sha") != kernel_src_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
 
 
+def copy_calibration(mb: int, torch):
+    n = mb * 2 ** 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     a = parse()
+    if a.summarize:
+        summarize(a)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the TTQ projection is built and "
@@ -219,6 +328,8 @@ def main():
     torch.cuda.init()
     main_m = measure(a.T, a.steps, a.warmup, torch, ttq,
                      want_graph=not a.only_ttq, want_gemm=not a.only_ttq)
+    if a.copy_calib_mb:
+        copy_calibration(a.copy_calib_mb, torch)
     sec = None
     if not a.only_ttq and a.T != 128:
         sec = measure(128, max(100, a.steps // 4), a.warmup, torch, ttq,
@@ -228,8 +339,11 @@ def main():
     T = a.T
     ms = main_m["ms_per_step"]
     value = T / (ms * 1e-3)
-    kname = "fused_qdq_mfma" if T <= 128 else "gemm_mfma"
-    k_ms = main_m["kernels_ms_avg"].get(kname, float("nan"))
+    # dominant kernel: the largest share of the step's kernel time
+    kt = main_m["kernels_ms_avg"]
+    launches = main_m["kernels_launches"]
+    kname = max(kt, key=lambda k: kt[k] * launches[k])
+    k_ms = kt[kname]
     ab = alg_bytes(d, d_out, T)
     af = alg_flops(d, d_out, T)
     hbm_bound = ab / HBM_PEAK_GBS > af / (BF16_PEAK_TFLOPS * 1e3)
@@ -242,7 +356,7 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved,
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["traffic"] = traffic_entry(k_ms)
+    roof["traffic"] = traffic_entry(kname, T)
     roof.update(kernel=kname, kernel_ms=k_ms, alg_bytes=ab, alg_flops=af)
 
     line = {
@@ -283,7 +397,7 @@ def main():
         line["rho_pages"] = 1.0 / d_out + 3.0 / T
     if sec is not None:
         s_ms = sec["ms_per_step"]
-        k2 = sec["kernels_ms_avg"].get("fused_qdq_mfma", float("nan"))
+        k2 = max(sec["kernels_ms_avg"].values())
         line["secondary_T128"] = {
             "tokens_per_s": 128 / (s_ms * 1e-3), "ms_per_step": s_ms,
             "fused_kernel_ms": k2,

@@ -29,6 +29,7 @@ SOURCES = [
     "k_quant.hip",
     "k_gemm.hip",
     "k_lowrank.hip",
+    "k_gemv.hip",
     "ttq_api.cpp",
 ]
 

@@ -40,7 +40,7 @@ namespace ttq {
 
 constexpr int FW = 8;  // waves per workgroup
 
-template <int NTB, int GS, bool DH_LDS>
+template <int NTB, int GS, bool DH_LDS, bool EXPORT>
 __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   constexpr int NKS = GS / 32;
   constexpr bool HILO = (NTB == 1);
@@ -53,7 +53,10 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const int req = (int)(jb % a.R);
   if (rb >= a.rowblocks) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63;
+  // wave index as a scalar: the group loop below is then wave-uniform control
+  // flow (a per-lane counter would make every loop exit a divergent branch)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = l & 15, qd = l >> 4;
   const int64_t row = rb * 16 + lr;
   const bool row_ok = row < a.d_out;
@@ -65,8 +68,12 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 : 1) * T * d;
   const bf16_t* xs_lo = xs + T * d;
   const float* sx = a.sx + (int64_t)req * G * Tp;
-  // rows past d_out read row 0 (valid memory); their results are discarded
-  const bf16_t* Wq = a.W + (row_ok ? row : 0) * d + qd * 8;
+  // the workgroup's weight rows as one bounded buffer: rows past d_out and
+  // groups past the end read as zeros without memory traffic
+  const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(a.W + rb * 16 * d, (uint32_t)(rows_here * d * 2));
+  const uint32_t lane_off = (uint32_t)((lr * d + qd * 8) * 2);
   const float Nf = a.Nf;
 
   f32x4 acc[NTB];
@@ -78,9 +85,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   f32x4 sxv0;
 
   auto load_w = [&](u32x4 (&wv)[NKS], int g) {
+    const uint32_t soff = g < G ? (uint32_t)g * GS * 2 : kOutOfRange;
 #pragma unroll
-    for (int k = 0; k < NKS; ++k)
-      wv[k] = *(const u32x4*)(Wq + (int64_t)g * GS + k * 32);
+    for (int k = 0; k < NKS; ++k) wv[k] = buf_load16(wr, lane_off + k * 64, soff);
   };
   // lanes whose token is past T read a small zero buffer instead of
   // branching (no divergent load paths for the wait-count logic)
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
                                       __float_as_uint(q[4]), 0x07060302u);
       qv[k].w = __builtin_amdgcn_perm(__float_as_uint(q[7]),
                                       __float_as_uint(q[6]), 0x07060302u);
-      if (a.codes_out && row_ok) {
+      if (EXPORT && a.codes_out && row_ok) {
         u32x2 c;
         c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
               ((unsigned)q[3] << 24);
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
                   k * 32) = c;
       }
     }
-    if (a.s_out && row_ok && qd == 0) {
+    if (EXPORT && a.s_out && row_ok && qd == 0) {
       const int64_t o = ((int64_t)req * a.d_out + row) * G + g;
       a.s_out[o] = s;
       a.m_out[o] = mn;
@@ -213,32 +220,21 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   // two weight register sets in ping-pong: the loads of the next group are
   // issued after this group's activation loads, so waiting for the latter
   // does not wait for the former, and no register copies are needed
-  // (the last prefetch re-reads the final group instead of branching)
+  // (a prefetch past the last group is out of range: zeros, no traffic)
   u32x4 wa[NKS], wb[NKS];
   int g = w;
   if (DH_LDS) {
-    // D^{1/2} of this request into LDS; the first weight loads are issued
-    // behind the staging loads so that their latencies overlap
-    constexpr int kStage = 4;  // float4 per thread: up to 8192 channels
-    f32x4 st[kStage];
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int64_t c = ((int64_t)i * FW * 64 + tid) * 4;
-      if (c < d) st[i] = *(const f32x4*)(dhg + c);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(wa, min(g, G - 1));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int64_t c = ((int64_t)i * FW * 64 + tid) * 4;
-      if (c < d) *(f32x4*)(lds + c) = st[i];
-    }
-    for (int64_t c = ((int64_t)kStage * FW * 64 + tid) * 4; c < d;
-         c += FW * 64 * 4)
+    // D^{1/2} of this request into LDS before the first weight loads: once
+    // every CU's weight requests are queued, these small reads would sit
+    // behind them
+    for (int64_t c = (int64_t)tid * 4; c < d; c += FW * 64 * 4)
       *(f32x4*)(lds + c) = *(const f32x4*)(dhg + c);
+    wait_vmem_all();
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, g);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-  } else if (g < G) {
+  } else {
     load_w(wa, g);
   }
   // (scheduling barriers keep that issue order: the compiler would otherwise
@@ -246,14 +242,14 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   while (g < G) {
     load_x(g);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(wb, min(g + FW, G - 1));
+    load_w(wb, g + FW);
     __builtin_amdgcn_sched_barrier(0);
     process(wa, g);
     g += FW;
     if (g >= G) break;
     load_x(g);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(wa, min(g + FW, G - 1));
+    load_w(wa, g + FW);
     __builtin_amdgcn_sched_barrier(0);
     process(wb, g);
     g += FW;
@@ -306,13 +302,21 @@ template <int NTB, bool DHL>
 static hipError_t launch_fused_ntb(const FusedArgs& a, int group, dim3 grid,
                                    uint32_t lds, const Launch& L) {
   const dim3 blk(FW * 64);
+  // the exports are a separate instantiation: conditional stores in the loop
+  // would make the compiler's memory wait counts conservative
+  const bool exp = a.codes_out || a.s_out;
+#define TTQ_FUSED_CASE(GSV)                                                  \
+  case GSV:                                                                  \
+    return exp ? ext_launch(k_fused<NTB, GSV, DHL, true>, grid, blk, lds, L, a) \
+               : ext_launch(k_fused<NTB, GSV, DHL, false>, grid, blk, lds, L, a);
   switch (group) {
-    case 32: return ext_launch(k_fused<NTB, 32, DHL>, grid, blk, lds, L, a);
-    case 64: return ext_launch(k_fused<NTB, 64, DHL>, grid, blk, lds, L, a);
-    case 128: return ext_launch(k_fused<NTB, 128, DHL>, grid, blk, lds, L, a);
-    case 256: return ext_launch(k_fused<NTB, 256, DHL>, grid, blk, lds, L, a);
+    TTQ_FUSED_CASE(32)
+    TTQ_FUSED_CASE(64)
+    TTQ_FUSED_CASE(128)
+    TTQ_FUSED_CASE(256)
     default: return hipErrorInvalidValue;
   }
+#undef TTQ_FUSED_CASE
 }
 
 template <bool DHL>

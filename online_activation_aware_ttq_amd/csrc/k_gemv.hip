@@ -1,0 +1,309 @@
+// Single-launch TTQ projection for one token (T = 1, decode).
+//
+// With one token the whole call is one pass over W, so everything runs in
+// one kernel: every workgroup derives the statistics of the token itself
+// (for T = 1 the channel norm is |x_j| for every p), keeps D^{1/2} and
+// x' = x D^{-1/2} in LDS, and streams its 16 weight rows exactly once:
+//
+//   y_i = sum_k  s_ik * sum_{j in k} q_ij x'_j  +  m_ik * sum_{j in k} x'_j
+//
+// the dequantized product (m + s q) D^{-1/2} x of "TTQ: Activation-Aware
+// Test-Time Quantization ..." (gist.science zh summary, Sec. 2.1), with the
+// per-group affine terms applied once per group.  x' stays in float32 and
+// the dot products run on the VALU (a 16x16 MFMA tile would be 1/16 used),
+// so the activation operand is never rounded to bf16.
+//
+// D^{1/2} is evaluated exactly as in the statistics kernels (float64 norm
+// and power, one rounding to float32), so the codes are decided from the
+// same float32 values as on the other paths.
+//
+// Lane layout as in the fused kernel: lane l holds weight row l & 15 and
+// channels 8*(l >> 4) .. +8 of each 32-channel step (one 16-byte load of W);
+// a group's statistics live in lanes {l, l^16, l^32, l^48}.  16 waves stride
+// over the groups with two weight register sets (one group in flight while
+// the other is processed); the token's loads are issued ahead of the ring so
+// the statistics overlap the first weight fetches.  Weights are read with
+// bounded buffer loads: prefetches past the last group return zeros without
+// memory traffic, so the ring needs no branches.
+#include "ttq_internal.h"
+
+namespace ttq {
+
+
+// D^{1/2} for one channel of one token, float64.  For T = 1 the norm is |x|
+// for p in {1, 2}; the general route mirrors the reduction kernels.  FAST
+// (p in {1, 2} and alpha in {0, 1/2, 1, 2}) uses correctly rounded square
+// roots instead of pow; both are within about one float64 ulp of the exact
+// value before the single rounding to float32.
+template <bool FAST>
+__device__ __forceinline__ double gemv_diag(double ax, int pmode, double p,
+                                            double lam, double alpha) {
+  double n = ax;
+  if (!FAST && pmode == 0 && ax != 0.0) n = pow(pow(ax, p), 1.0 / p);
+  const double base = n + lam;
+  if (!(base > 0.0) || alpha == 0.0) return 1.0;
+  if (!FAST) return pow(base, 0.5 * alpha);
+  if (alpha == 0.5) return sqrt(sqrt(base));
+  if (alpha == 1.0) return sqrt(base);
+  return base;  // alpha == 2
+}
+
+// Waves per workgroup: 16 where the registers fit in the 128 VGPRs of a
+// 1024-thread workgroup (the timed variants up to g = 128), else 8.
+template <int GS, bool EXPORT>
+constexpr int gemv_waves() {
+  return (GS <= 128 && !EXPORT) ? 16 : 8;
+}
+
+template <int GS, bool FAST, bool EXPORT>
+__global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
+    GemvArgs a) {
+  constexpr int VW = gemv_waves<GS, EXPORT>();
+  constexpr int NKS = GS / 32;
+  // weight register sets in the ring: one group in flight while one is
+  // processed (measured on MI355X: deeper rings only add register pressure)
+  constexpr int NR = 2;
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  // LDS: dh[d] | xp[d] | sxp[G] | red[VW][16]
+  const int64_t d = a.d;
+  const int G = a.G;
+  float* dh_s = lds;
+  float* xp_s = lds + d;
+  float* sx_s = lds + 2 * d;
+  float* red = sx_s + G;
+
+  const int64_t b = blockIdx.x;
+  const int xcd = (int)(b & 7);
+  const int64_t jb = b >> 3;
+  const int64_t rb = (jb / a.R) * 8 + xcd;
+  const int req = (int)(jb % a.R);
+  if (rb >= a.rowblocks) return;
+
+  const int tid = threadIdx.x, l = tid & 63;
+  // wave index as a scalar: the group loop below is then wave-uniform control
+  // flow (a per-lane counter would make every loop exit a divergent branch)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = l & 15, qd = l >> 4;
+  const int64_t row = rb * 16 + lr;
+  const bool row_ok = row < a.d_out;
+  const bf16_t* x = a.X + (int64_t)req * d;
+  const float Nf = a.Nf;
+
+  // the workgroup's weight rows as one bounded buffer: rows past d_out and
+  // groups past the end read as zeros without memory traffic
+  const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(a.W + rb * 16 * d, (uint32_t)(rows_here * d * 2));
+  const uint32_t lane_off = (uint32_t)((lr * d + qd * 8) * 2);
+  auto load_w = [&](u32x4 (&wv)[NKS], int g) {
+    const uint32_t soff = g < G ? (uint32_t)g * GS * 2 : kOutOfRange;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) wv[k] = buf_load16(wr, lane_off + k * 64, soff);
+  };
+
+  // ---- prologue.  The token's loads are issued and waited for first: once
+  // every CU's weight requests are queued, a later 8 KB read of x would sit
+  // behind them, and the statistics (and the barrier all waves wait at)
+  // would start only after most of W had arrived.  So x first, then the
+  // weight ring, then the statistics while the weights stream in.
+  // (d <= kGemvMaxD = VW * 64 * 4 * XPT: all of x is loaded here.)
+  constexpr int XPT = kGemvMaxD / (VW * 64 * 4);
+  float xf[XPT][4];
+  {
+    u32x2 xv[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int64_t c = ((int64_t)i * VW * 64 + tid) * 4;
+      xv[i] = *(const u32x2*)(x + (c < d ? c : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      xf[i][0] = bf16lo(xv[i].x);
+      xf[i][1] = bf16hi(xv[i].x);
+      xf[i][2] = bf16lo(xv[i].y);
+      xf[i][3] = bf16hi(xv[i].y);
+    }
+  }
+  wait_vmem_all();
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 ring[NR][NKS];
+  int g = w;
+#pragma unroll
+  for (int r = 0; r + 1 < NR; ++r) load_w(ring[r], g + r * VW);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // statistics of the token: D^{1/2} (float64, rounded once: it decides the
+  // codes), x' = x D^{-1/2} (float32; it only enters the contraction) and
+  // the group sums of x'.  4 channels per thread.
+  const int lpg = GS / 4;  // threads per group in this layout
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int64_t c = ((int64_t)i * VW * 64 + tid) * 4;
+    float ps = 0.f;
+    if (c < d) {
+      float hv[4], xpv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double h = gemv_diag<FAST>(fabs((double)xf[i][j]), a.pmode, a.p,
+                                         a.lam, a.alpha);
+        hv[j] = (float)h;
+        xpv[j] = xf[i][j] * __builtin_amdgcn_rcpf(hv[j]);
+        ps += xpv[j];
+      }
+      *(f32x4*)(dh_s + c) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+      *(f32x4*)(xp_s + c) = f32x4{xpv[0], xpv[1], xpv[2], xpv[3]};
+      if (EXPORT && a.dh_export && rb == 0)
+        *(f32x4*)(a.dh_export + (int64_t)req * d + c) =
+            f32x4{hv[0], hv[1], hv[2], hv[3]};
+    }
+    for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    if (c < d && (tid % lpg) == 0) sx_s[c / GS] = ps;
+  }
+  __syncthreads();
+
+  // ---- main loop: quantize-dequantize + dot, one group per step
+  float acc = 0.f;
+  auto process = [&](const u32x4 (&wv)[NKS], int gg) {
+    const int64_t colg = (int64_t)gg * GS + qd * 8;
+    float u[NKS][8];
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+      const f32x4 d0 = *(const f32x4*)(dh_s + colg + k * 32);
+      const f32x4 d1 = *(const f32x4*)(dh_s + colg + k * 32 + 4);
+      u[k][0] = bf16lo(wv[k].x) * d0.x;
+      u[k][1] = bf16hi(wv[k].x) * d0.y;
+      u[k][2] = bf16lo(wv[k].y) * d0.z;
+      u[k][3] = bf16hi(wv[k].y) * d0.w;
+      u[k][4] = bf16lo(wv[k].z) * d1.x;
+      u[k][5] = bf16hi(wv[k].z) * d1.y;
+      u[k][6] = bf16lo(wv[k].w) * d1.z;
+      u[k][7] = bf16hi(wv[k].w) * d1.w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mn = fminf(mn, u[k][j]);
+        mx = fmaxf(mx, u[k][j]);
+      }
+    }
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // s = fl(fl(M - m) / N), inv = fl(1 / s); IEEE division, no contraction
+    const float s = (mx - mn) / Nf;
+    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    // q = rint(fl(fl(u - m) * inv)) (the clamp to [0, N] is a no-op, see the
+    // fused kernel); P = sum q x' over this lane's 32 channels
+    float P = 0.f;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+      const f32x4 x0 = *(const f32x4*)(xp_s + colg + k * 32);
+      const f32x4 x1 = *(const f32x4*)(xp_s + colg + k * 32 + 4);
+      const float xq[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        q[j] = __builtin_rintf((u[k][j] - mn) * inv);
+        P = fmaf(q[j], xq[j], P);
+      }
+      if (EXPORT && a.codes_out && row_ok) {
+        u32x2 c;
+        c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
+              ((unsigned)q[3] << 24);
+        c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
+              ((unsigned)q[7] << 24);
+        *(u32x2*)(a.codes_out + ((int64_t)req * a.d_out + row) * d + colg +
+                  k * 32) = c;
+      }
+    }
+    if (EXPORT && a.s_out && row_ok && qd == 0) {
+      const int64_t o = ((int64_t)req * a.d_out + row) * G + gg;
+      a.s_out[o] = s;
+      a.m_out[o] = mn;
+    }
+    acc = fmaf(s, P, acc);
+    if (qd == 0) acc = fmaf(mn, sx_s[gg], acc);
+  };
+
+  // ring of NR weight register sets: NR - 1 groups in flight while one is
+  // processed (indices are compile-time after unrolling)
+  while (g < G) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      load_w(ring[(r + NR - 1) % NR], g + (NR - 1) * VW);
+      __builtin_amdgcn_sched_barrier(0);
+      process(ring[r], g);
+      g += VW;
+      if (g >= G) break;
+    }
+  }
+
+  // static low-rank term: + B[row, :] . z, z = A x precomputed
+  if (a.rank > 0 && w == 0 && qd == 0 && row_ok) {
+    const bf16_t* Br = a.Blr + row * a.rank;
+    const bf16_t* z = a.Z + (int64_t)req * a.rp;
+    for (int k = 0; k < a.rank; k += 8) {
+      const u32x4 bv = *(const u32x4*)(Br + k);
+      const u32x4 zv = *(const u32x4*)(z + k);
+      acc = fmaf(bf16lo(bv.x), bf16lo(zv.x), acc);
+      acc = fmaf(bf16hi(bv.x), bf16hi(zv.x), acc);
+      acc = fmaf(bf16lo(bv.y), bf16lo(zv.y), acc);
+      acc = fmaf(bf16hi(bv.y), bf16hi(zv.y), acc);
+      acc = fmaf(bf16lo(bv.z), bf16lo(zv.z), acc);
+      acc = fmaf(bf16hi(bv.z), bf16hi(zv.z), acc);
+      acc = fmaf(bf16lo(bv.w), bf16lo(zv.w), acc);
+      acc = fmaf(bf16hi(bv.w), bf16hi(zv.w), acc);
+    }
+  }
+
+  // reduce: the 4 lanes of a row (fixed xor order), then the 8 waves
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (qd == 0) red[w * 16 + lr] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float v = red[tid];
+#pragma unroll
+    for (int ww = 1; ww < VW; ++ww) v += red[ww * 16 + tid];
+    const int64_t rowx = rb * 16 + tid;
+    if (rowx < a.d_out) a.Y[(int64_t)req * a.d_out + rowx] = v;
+  }
+}
+
+size_t gemv_lds_bytes(int64_t d, int G) {
+  return (size_t)(2 * d + G + 16 * 16) * sizeof(float);
+}
+
+hipError_t launch_gemv(const GemvArgs& a, int group, const Launch& L) {
+  const int64_t nblk = ((a.rowblocks + 7) / 8) * 8 * a.R;
+  if (nblk == 0) return hipSuccess;
+  if (a.d > kGemvMaxD) return hipErrorInvalidValue;
+  const uint32_t lds = (uint32_t)gemv_lds_bytes(a.d, a.G);
+  const dim3 grid((unsigned)nblk);
+  const bool fast = a.pmode != 0 && (a.alpha == 0.0 || a.alpha == 0.5 ||
+                                     a.alpha == 1.0 || a.alpha == 2.0);
+  // optional exports (codes, scales, minima, D^{1/2}) are a separate
+  // instantiation: conditional stores in the loop would make the compiler's
+  // memory wait counts conservative on the timed path
+  const bool exp = a.codes_out || a.s_out || a.dh_export;
+#define TTQ_GEMV_LAUNCH(GSV, F, E) \
+  ext_launch(k_gemv<GSV, F, E>, grid, dim3(gemv_waves<GSV, E>() * 64), lds, L, a)
+#define TTQ_GEMV_CASE(GSV)                                               \
+  case GSV:                                                              \
+    if (exp)                                                             \
+      return fast ? TTQ_GEMV_LAUNCH(GSV, true, true)                     \
+                  : TTQ_GEMV_LAUNCH(GSV, false, true);                   \
+    return fast ? TTQ_GEMV_LAUNCH(GSV, true, false)                      \
+                : TTQ_GEMV_LAUNCH(GSV, false, false);
+  switch (group) {
+    TTQ_GEMV_CASE(32)
+    TTQ_GEMV_CASE(64)
+    TTQ_GEMV_CASE(128)
+    TTQ_GEMV_CASE(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef TTQ_GEMV_CASE
+#undef TTQ_GEMV_LAUNCH
+}
+
+}  // namespace ttq

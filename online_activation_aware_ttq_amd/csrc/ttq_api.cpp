@@ -24,10 +24,16 @@ constexpr int64_t kMaxR = 4096;
 constexpr int64_t kMaxElems = int64_t(1) << 34;
 constexpr int kFusedMaxT = 128;
 
+constexpr size_t kGemvLdsMax = 128 * 1024;
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+constexpr uint32_t known_flags() {
+  return TTQ_FLAG_FORCE_FUSED | TTQ_FLAG_FORCE_TWO_PHASE;
+}
+
 struct Plan {
-  int path = 0;          // 0 fused, 1 two-phase
+  int path = 0;          // 0 fused, 1 two-phase, 2 single launch (T = 1)
   int ntb = 1;           // fused: 16-token blocks (power of two)
   int G = 0;             // groups per row
   int planes = 1;        // fused: activation planes (2 = bf16 hi + lo)
@@ -78,6 +84,8 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
   if (prm->flags & TTQ_FLAG_FORCE_FUSED) fused = true;
   if (prm->flags & TTQ_FLAG_FORCE_TWO_PHASE) fused = false;
   P.path = fused ? 0 : 1;
+  const bool gemv_fits = d <= kGemvMaxD && gemv_lds_bytes(d, P.G) <= kGemvLdsMax;
+  if (T == 1 && gemv_fits && !(prm->flags & known_flags())) P.path = 2;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -89,7 +97,9 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
   P.off_dhi = take(sizeof(float) * R * d);
   if (P.rp > 0) P.off_z = take(sizeof(uint16_t) * R * T * P.rp);
 
-  if (fused) {
+  if (P.path == 2) {
+    P.rowblocks = (dout + 15) / 16;
+  } else if (fused) {
     P.ntb = 1;
     while (P.ntb * 16 < T) P.ntb *= 2;
     P.rowblocks = (dout + 15) / 16;
@@ -124,7 +134,7 @@ TimingState g_timing;
 
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
-    "quant_what", "gemm_mfma", "lowrank_z"};
+    "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -205,6 +215,28 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
   const float Nf = (float)((1 << prm->bits) - 1);
   const bool need_quant = dout > 0;
 
+  if (P.path == 2) {
+    if (P.rp > 0) {
+      LowRankZArgs za{Xb, Ab, R, d, (int)rank, (int)P.rp, Zb};
+      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      if (st != TTQ_OK) return st;
+    }
+    GemvArgs va{};
+    va.W = Wb; va.X = Xb; va.d = d; va.d_out = dout; va.G = P.G; va.Nf = Nf;
+    va.pmode = pmode; va.p = prm->p; va.lam = prm->lambda; va.alpha = prm->alpha;
+    va.Z = Zb; va.Blr = Bb; va.rank = (int)rank; va.rp = (int)P.rp;
+    va.Y = Y; va.rowblocks = P.rowblocks; va.R = (int)R;
+    va.codes_out = codes_out; va.s_out = scales_out; va.m_out = mins_out;
+    va.dh_export = dhalf_out;
+    if (dout == 0) {  // statistics only: the gemv kernel needs a row block
+      StatsSmallArgs sa{};
+      sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = pmode;
+      sa.p = prm->p; sa.lam = prm->lambda; sa.alpha = prm->alpha;
+      sa.dh = dh; sa.dhi = dhi; sa.dh_export = dhalf_out; sa.group = prm->group;
+      return run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, (int)R, L); });
+    }
+    return run(K_GEMV, s, [&](const Launch& L) { return launch_gemv(va, prm->group, L); });
+  }
   if (P.path == 0) {
     StatsSmallArgs sa{};
     sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = pmode;

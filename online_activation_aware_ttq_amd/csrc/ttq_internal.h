@@ -24,6 +24,7 @@ enum KernelKind {
   K_QUANT,             // quantize pass writing W_hat (two-phase path)
   K_GEMM,              // MFMA GEMM Y = X W_hat^T + Z B^T (two-phase path)
   K_LOWRANK_Z,         // Z = X A^T (low-rank first factor)
+  K_GEMV,              // single-launch path for one token (T = 1)
   K_NUM_KINDS
 };
 
@@ -43,6 +44,31 @@ __device__ __forceinline__ unsigned f2bf(float f) {
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);
 }
+
+// Raw buffer loads: a resource descriptor bounds the addressable range, and a
+// 16-byte load whose offset falls outside it returns zeros without touching
+// memory.  Used to stream weight tiles with no branches for ragged edges.
+// (Descriptor word 3 for the gfx9 family, which includes gfx950.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r,
+                                            uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// Wait until every vector memory access of this wave has completed (gfx9
+// s_waitcnt encoding: vmcnt[3:0] = 0, expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
+// Used to order a small dependent read ahead of a large batch of loads.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// scalar offset that puts a load out of range (no wrap-around: the lane
+// offsets of a weight tile stay far below 2^30)
+constexpr uint32_t kOutOfRange = 0x40000000u;
 
 // ---------------------------------------------------------------- launchers
 // Where and how to launch: the stream, plus optional events that the runtime
@@ -117,6 +143,30 @@ constexpr size_t kZeroBytes = 1024;
 constexpr size_t kFusedDhLdsMax = 64 * 1024;
 hipError_t launch_fused(const FusedArgs& a, int ntb, int group,
                         const Launch& L);
+
+struct GemvArgs {
+  const bf16_t* W;      // [d_out][d]
+  const bf16_t* X;      // [R][d]   (one token per request)
+  int64_t d, d_out;
+  int G;
+  float Nf;
+  int pmode;
+  double p, lam, alpha;
+  const bf16_t* Z;      // [R][rp] or null
+  const bf16_t* Blr;    // [d_out][rank] or null
+  int rank, rp;
+  float* Y;             // [R][d_out]
+  int64_t rowblocks;
+  int R;
+  uint8_t* codes_out;   // [R][d_out][d]
+  float* s_out;         // [R][d_out][G]
+  float* m_out;
+  float* dh_export;     // [R][d]
+};
+// the single-launch T = 1 kernel holds all of D^{1/2} and x' in LDS
+constexpr int64_t kGemvMaxD = 12288;
+size_t gemv_lds_bytes(int64_t d, int G);
+hipError_t launch_gemv(const GemvArgs& a, int group, const Launch& L);
 
 struct QuantArgs {
   const bf16_t* W;      // [d_out][d]

@@ -171,7 +171,10 @@ def test_injected_hip_error_is_reported(monkeypatch):
 
 
 def test_path_selection():
-    assert ttq.ttq_path(prm(T=1)) == 0
+    assert ttq.ttq_path(prm(T=1)) == 2
+    assert ttq.ttq_path(prm(T=1, d=12288 + 128)) == 0
+    assert ttq.ttq_path(prm(T=1, flags=ttq.TTQ_FLAG_FORCE_FUSED)) == 0
+    assert ttq.ttq_path(prm(T=2)) == 0
     assert ttq.ttq_path(prm(T=128)) == 0
     assert ttq.ttq_path(prm(T=129)) == 1
     assert ttq.ttq_path(prm(T=2048)) == 1

@@ -74,6 +74,16 @@ CASES = [
                         seed=27)),
     ("alpha2_lam0", dict(d=512, d_out=64, T=8, bits=4, group=128, alpha=2.0,
                          lam=0.0, seed=28)),
+    # one token: the single-launch kernel, its general-p / general-alpha
+    # instantiation and the group sizes
+    ("T1_p_general", dict(d=512, d_out=80, T=1, bits=4, group=64, p=0.5,
+                          seed=29)),
+    ("T1_alpha_general", dict(d=512, d_out=80, T=1, bits=3, group=32,
+                              alpha=0.7, seed=30)),
+    ("T1_g256_r16", dict(d=1024, d_out=72, T=1, bits=4, group=256, rank=16,
+                         seed=32)),
+    ("T1_alpha1_p1", dict(d=384, d_out=50, T=1, bits=2, group=128, p=1.0,
+                          alpha=1.0, lam=0.0, seed=33)),
 ]
 
 
@@ -146,6 +156,15 @@ def test_empty_shapes():
                        dhalf_out=dh)
     torch.cuda.synchronize()
     assert Y.shape == (5, 0)
+    # d_out = 0 at T = 1 (the single-launch path): statistics only
+    dh1 = torch.empty(256, dtype=torch.float32, device="cuda")
+    Y1 = ttq.ttq_linear(W, X[:1], p=2.0, lam=1e-3, alpha=0.5, bits=4,
+                        group=128, dhalf_out=dh1)
+    torch.cuda.synchronize()
+    assert Y1.shape == (1, 0)
+    ref1 = oracle.ttq_linear(p2.W, p2.X[0][:1], bits=4, group=128, p=2.0,
+                             lam=1e-3, alpha=0.5)
+    np.testing.assert_array_equal(dh1.cpu().numpy(), ref1["dh32"])
     ref2 = oracle.ttq_linear(p2.W, p2.X[0], bits=4, group=128, p=2.0,
                              lam=1e-3, alpha=0.5)
     np.testing.assert_array_equal(dh.cpu().numpy(), ref2["dh32"])
@@ -154,6 +173,17 @@ def test_empty_shapes():
     Yb = ttq.ttq_linear_batched(to_dev(p2.W), Xb, p=2.0, lam=1e-3, alpha=0.5,
                                 bits=4, group=128)
     assert Yb.shape == (0, 5, 1)
+
+
+@pytest.mark.parametrize("T", [1, 16, 200])
+def test_outputs_without_exports_match(T):
+    # the timed path runs a separate kernel instantiation without the
+    # optional exports: same Y bit for bit
+    prob = make_problem("noexp", d=1024, d_out=272, T=T, bits=4, group=128,
+                        rank=32, x_kind="logu10_100", n_outliers=10, seed=61)
+    a = run_gpu(prob, exports=True)
+    b = run_gpu(prob, exports=False)
+    np.testing.assert_array_equal(a["Y"], b["Y"])
 
 
 def test_deterministic_and_stateless():
