@@ -28,6 +28,7 @@ SOURCES = [
     "k_fused.hip",
     "k_quant.hip",
     "k_gemm.hip",
+    "k_gemm_lds.hip",
     "k_lowrank.hip",
     "k_gemv.hip",
     "ttq_api.cpp",

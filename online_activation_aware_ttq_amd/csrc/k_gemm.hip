@@ -7,14 +7,17 @@
 // channels), and the optional second segment is the static low-rank term
 // Z B^T with Z = X A^T ("TTQ: Activation-Aware Test-Time Quantization ...",
 // gist.science zh summary, Sec. 2.2); the same kernel with one segment
-// computes Z itself.  Both operands are K-contiguous, which matches the
+// computes Z itself (split over K when the token count leaves too few output
+// tiles to fill the chip; the fp32 partials are then summed in split order by
+// a second small kernel).  Both operands are K-contiguous, which matches the
 // v_mfma_f32_32x32x16_bf16 register layout (8 consecutive K values per lane).
 //
 // Tiling: 128 x 128 output tile per workgroup of 4 waves (2 x 2, each wave
 // 64 x 64 = 2 x 2 MFMA tiles of 32 x 32), K step 64, both operand tiles
 // double-buffered in LDS with a 16-byte row pad (conflict-free 16-byte
-// reads).  Workgroups are ordered so that the M tiles of one weight tile run
-// back to back on the same XCD and share it through that XCD's L2.
+// reads).  With 8 or more weight tiles, workgroups are ordered so that the M
+// tiles of one weight tile run back to back on the same XCD and share it
+// through that XCD's L2; narrower outputs are spread over all XCDs.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -22,17 +25,30 @@ namespace ttq {
 constexpr int GBM = 128, GBN = 128, GBK = 64, GLDK = GBK + 8;
 
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
+  if (a.nsplit > 1) {
+    const int64_t kb = (int64_t)blockIdx.y * a.ksplit;
+    a.A1 += kb;
+    a.B1 += kb;
+    a.K1 = min(a.ksplit, a.K1 - kb);
+    a.C += (int64_t)blockIdx.y * a.split_stride;
+  }
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][GBM * GLDK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][GBN * GLDK];
 
   const int64_t mtiles = (a.M + GBM - 1) / GBM;
   const int64_t ntiles = ((a.N > a.N_store ? a.N : a.N_store) + GBN - 1) / GBN;
   const int64_t id = blockIdx.x;
-  const int xcd = (int)(id & 7);
-  const int64_t j = id >> 3;
-  const int64_t ntile = (j / mtiles) * 8 + xcd;
-  const int64_t mtile = j % mtiles;
-  if (ntile >= ntiles) return;
+  int64_t ntile, mtile;
+  if (ntiles >= 8) {
+    const int xcd = (int)(id & 7);
+    const int64_t j = id >> 3;
+    ntile = (j / mtiles) * 8 + xcd;
+    mtile = j % mtiles;
+  } else {
+    ntile = id % ntiles;
+    mtile = id / ntiles;
+  }
+  if (ntile >= ntiles || mtile >= mtiles) return;
   const int64_t m0 = mtile * GBM, n0 = ntile * GBN;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -135,9 +151,35 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
 hipError_t launch_gemm(const GemmArgs& a, const Launch& L) {
   const int64_t mtiles = (a.M + GBM - 1) / GBM;
   const int64_t ntiles = ((a.N > a.N_store ? a.N : a.N_store) + GBN - 1) / GBN;
-  const int64_t nblk = ((ntiles + 7) / 8) * 8 * mtiles;
+  const int64_t nblk =
+      ntiles >= 8 ? ((ntiles + 7) / 8) * 8 * mtiles : ntiles * mtiles;
   if (nblk == 0) return hipSuccess;
-  return ext_launch(k_gemm, dim3((unsigned)nblk), dim3(256), 0, L, a);
+  const unsigned ns = a.nsplit > 1 ? (unsigned)a.nsplit : 1u;
+  return ext_launch(k_gemm, dim3((unsigned)nblk, ns), dim3(256), 0, L, a);
+}
+
+__global__ __launch_bounds__(256) void k_splitk_reduce(SplitReduceArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= a.n) return;
+  f32x4 acc = *(const f32x4*)(a.part + i);
+  for (int z = 1; z < a.nsplit; ++z) {
+    const f32x4 v = *(const f32x4*)(a.part + (int64_t)z * a.n + i);
+    acc[0] += v[0];
+    acc[1] += v[1];
+    acc[2] += v[2];
+    acc[3] += v[3];
+  }
+  u32x2 o;
+  o.x = pack_bf16(acc[0], acc[1]);
+  o.y = pack_bf16(acc[2], acc[3]);
+  *(u32x2*)(a.out + i) = o;
+}
+
+hipError_t launch_splitk_reduce(const SplitReduceArgs& a, const Launch& L) {
+  if (a.n == 0) return hipSuccess;
+  const int64_t nthr = (a.n + 3) / 4;
+  return ext_launch(k_splitk_reduce, dim3((unsigned)((nthr + 255) / 256)),
+                    dim3(256), 0, L, a);
 }
 
 }  // namespace ttq

@@ -174,46 +174,69 @@ hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
 }
 
 // ---------------------------------------------------------------------------
-// Large T: token slices reduced by separate waves into float64 partials,
-// then a finalize pass sums the partials in slice order (deterministic).
+// Large T: each wave reduces one slice of tokens for 512 channels; the four
+// waves of a block add their slices in LDS in slice order and write one
+// float64 partial per block; a finalize pass sums the block partials in
+// order (deterministic).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_stats_partial(StatsSplitArgs a) {
+  __shared__ double red[4][512];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int split = blockIdx.y * 4 + w;
   const int r = blockIdx.z;
   const int64_t c0 = (int64_t)blockIdx.x * 512 + l * 8;
-  if (split >= a.nsplit || c0 >= a.d) return;
-  const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
-  const int64_t t0 = (int64_t)split * a.tchunk;
-  const int64_t t1 = min(a.T, t0 + a.tchunk);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int64_t t = t0;
-  for (; t + 4 <= t1; t += 4) {
-    u32x4 v0 = *(const u32x4*)(X + (t + 0) * a.d + c0);
-    u32x4 v1 = *(const u32x4*)(X + (t + 1) * a.d + c0);
-    u32x4 v2 = *(const u32x4*)(X + (t + 2) * a.d + c0);
-    u32x4 v3 = *(const u32x4*)(X + (t + 3) * a.d + c0);
-    accum8(acc, v0, a.pmode, a.p);
-    accum8(acc, v1, a.pmode, a.p);
-    accum8(acc, v2, a.pmode, a.p);
-    accum8(acc, v3, a.pmode, a.p);
+  if (split < a.nsplit && c0 < a.d) {
+    const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
+    const int64_t t0 = (int64_t)split * a.tchunk;
+    const int64_t t1 = min(a.T, t0 + a.tchunk);
+    int64_t t = t0;
+    for (; t + 4 <= t1; t += 4) {
+      u32x4 v0 = *(const u32x4*)(X + (t + 0) * a.d + c0);
+      u32x4 v1 = *(const u32x4*)(X + (t + 1) * a.d + c0);
+      u32x4 v2 = *(const u32x4*)(X + (t + 2) * a.d + c0);
+      u32x4 v3 = *(const u32x4*)(X + (t + 3) * a.d + c0);
+      accum8(acc, v0, a.pmode, a.p);
+      accum8(acc, v1, a.pmode, a.p);
+      accum8(acc, v2, a.pmode, a.p);
+      accum8(acc, v3, a.pmode, a.p);
+    }
+    for (; t < t1; ++t) {
+      u32x4 v = *(const u32x4*)(X + t * a.d + c0);
+      accum8(acc, v, a.pmode, a.p);
+    }
   }
-  for (; t < t1; ++t) {
-    u32x4 v = *(const u32x4*)(X + t * a.d + c0);
-    accum8(acc, v, a.pmode, a.p);
-  }
-  double* out = a.partial + ((int64_t)r * a.nsplit + split) * a.d + c0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) out[j] = acc[j];
+  for (int j = 0; j < 8; ++j) red[w][l * 8 + j] = acc[j];
+  __syncthreads();
+  const int64_t nb = (a.nsplit + 3) / 4;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int64_t c = (int64_t)blockIdx.x * 512 + i;
+    if (c < a.d) {
+      const double v = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+      a.partial[((int64_t)r * nb + blockIdx.y) * a.d + c] = v;
+    }
+  }
 }
 
-__global__ __launch_bounds__(512) void k_stats_final(StatsSplitArgs a) {
+// One thread per channel; the block partials are read 8 at a time (independent
+// loads in flight) and added in slice order.
+__global__ __launch_bounds__(64) void k_stats_final(StatsSplitArgs a) {
   const int r = blockIdx.y;
-  const int64_t c = (int64_t)blockIdx.x * 512 + threadIdx.x;
+  const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (c >= a.d) return;
-  const double* P = a.partial + (int64_t)r * a.nsplit * a.d + c;
+  const int nb = (a.nsplit + 3) / 4;
+  const double* P = a.partial + (int64_t)r * nb * a.d + c;
   double S = 0.0;
-  for (int k = 0; k < a.nsplit; ++k) S += P[(int64_t)k * a.d];
+  int k = 0;
+  for (; k + 8 <= nb; k += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = P[(int64_t)(k + j) * a.d];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) S += v[j];
+  }
+  for (; k < nb; ++k) S += P[(int64_t)k * a.d];
   float dh, dhi;
   diag_half(finish_norm(S, a.pmode, a.p), a.lam, a.alpha, dh, dhi);
   a.dh[(int64_t)r * a.d + c] = dh;
@@ -230,8 +253,8 @@ hipError_t launch_stats_partial(const StatsSplitArgs& a, int R,
 }
 
 hipError_t launch_stats_final(const StatsSplitArgs& a, int R, const Launch& L) {
-  dim3 grid((unsigned)((a.d + 511) / 512), (unsigned)R);
-  return ext_launch(k_stats_final, grid, dim3(512), 0, L, a);
+  dim3 grid((unsigned)((a.d + 63) / 64), (unsigned)R);
+  return ext_launch(k_stats_final, grid, dim3(64), 0, L, a);
 }
 
 }  // namespace ttq

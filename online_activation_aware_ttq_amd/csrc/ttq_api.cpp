@@ -40,8 +40,10 @@ struct Plan {
   int64_t rowblocks = 0;
   int tchunk = 0, nsplit = 0;
   int64_t rp = 0;        // rank padded to a multiple of 32
+  int zsplit = 1;        // two-phase: K splits of Z = X A^T
+  int64_t zksplit = 0;   // channels per split
   size_t off_dh = 0, off_dhi = 0, off_xs = 0, off_sx = 0, off_z = 0,
-         off_statp = 0, off_what = 0, off_zeros = 0;
+         off_statp = 0, off_what = 0, off_zeros = 0, off_zpart = 0;
   size_t total = 0;
 };
 
@@ -108,11 +110,30 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
     P.off_zeros = take(kZeroBytes);
   } else {
-    P.tchunk = (int)((T + 63) / 64);
-    if (P.tchunk < 32) P.tchunk = 32;
+    // token slices for the norm partials: enough workgroups to fill the chip
+    // (about 2048 waves), at least 8 tokens per slice
+    const int64_t cchunks = (d + 511) / 512;
+    int64_t target = 2048 / (cchunks * R);
+    if (target < 1) target = 1;
+    int64_t tch = (T + target - 1) / target;
+    if (tch < 8) tch = 8;
+    P.tchunk = (int)tch;
     P.nsplit = (int)((T + P.tchunk - 1) / P.tchunk);
-    P.off_statp = take(sizeof(double) * R * P.nsplit * d);
+    P.off_statp = take(sizeof(double) * R * ((P.nsplit + 3) / 4) * d);
     P.off_what = take(sizeof(uint16_t) * dout * d);
+    if (P.rp > 0 && T > 0) {
+      // Z has few output tiles (rank columns): split the channels so that
+      // about 512 workgroups run, each over at least 256 channels
+      const int64_t tiles = ((R * T + 127) / 128) * ((P.rp + 127) / 128);
+      const int64_t nk = (d + 63) / 64;
+      int64_t S = (512 + tiles - 1) / tiles;
+      if (S > nk / 4) S = nk / 4;
+      if (S < 1) S = 1;
+      P.zksplit = (nk + S - 1) / S * 64;
+      P.zsplit = (int)((d + P.zksplit - 1) / P.zksplit);
+      if (P.zsplit > 1)
+        P.off_zpart = take(sizeof(float) * P.zsplit * R * T * P.rp);
+    }
   }
   P.total = off;
   return P;
@@ -134,7 +155,7 @@ TimingState g_timing;
 
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
-    "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1"};
+    "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -284,9 +305,22 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     GemmArgs za{};
     za.A1 = Xb; za.lda1 = d; za.B1 = Ab; za.ldb1 = d; za.K1 = d;
     za.M = R * T; za.N = rank; za.N_store = P.rp;
-    za.Cb = Zb; za.ldc = P.rp;
+    za.ldc = P.rp;
+    if (P.zsplit > 1) {
+      za.C = reinterpret_cast<float*>(ws + P.off_zpart);
+      za.ksplit = P.zksplit;
+      za.nsplit = P.zsplit;
+      za.split_stride = R * T * P.rp;
+    } else {
+      za.Cb = Zb;
+    }
     st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_gemm(za, L); });
     if (st != TTQ_OK) return st;
+    if (P.zsplit > 1) {
+      SplitReduceArgs ra{za.C, P.zsplit, R * T * P.rp, Zb};
+      st = run(K_SPLITK_REDUCE, s, [&](const Launch& L) { return launch_splitk_reduce(ra, L); });
+      if (st != TTQ_OK) return st;
+    }
   }
   bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
   for (int64_t r = 0; r < R; ++r) {
@@ -306,7 +340,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     }
     ga.M = T; ga.N = dout; ga.N_store = dout;
     ga.C = Y + r * T * dout; ga.ldc = dout;
-    st = run(K_GEMM, s, [&](const Launch& L) { return launch_gemm(ga, L); });
+    st = run(K_GEMM, s, [&](const Launch& L) { return launch_gemm_lds(ga, L); });
     if (st != TTQ_OK) return st;
   }
   return TTQ_OK;

@@ -25,6 +25,7 @@ enum KernelKind {
   K_GEMM,              // MFMA GEMM Y = X W_hat^T + Z B^T (two-phase path)
   K_LOWRANK_Z,         // Z = X A^T (low-rank first factor)
   K_GEMV,              // single-launch path for one token (T = 1)
+  K_SPLITK_REDUCE,     // split-K partial sums of Z -> bf16
   K_NUM_KINDS
 };
 
@@ -110,7 +111,7 @@ struct StatsSplitArgs {
   int pmode;
   double p, lam, alpha;
   int tchunk, nsplit;
-  double* partial;      // [R][nsplit][d]
+  double* partial;      // [R][ceil(nsplit/4)][d], one row per block of 4 slices
   float* dh;
   float* dhi;
   float* dh_export;
@@ -194,8 +195,27 @@ struct GemmArgs {
   int64_t N_store;                  // columns actually stored (<= ldc)
   float* C; int64_t ldc;            // fp32 output, or
   bf16_t* Cb;                       // bf16 output (one of the two)
+  // split-K (first segment only, fp32 output): split z covers channels
+  // [z*ksplit, (z+1)*ksplit) and writes C + z*split_stride
+  int64_t ksplit;                   // multiple of 64; 0 = no split
+  int nsplit;
+  int64_t split_stride;
 };
 hipError_t launch_gemm(const GemmArgs& a, const Launch& L);
+// Large-tile variant for the projection GEMM (fp32 C, no split): operands
+// streamed into LDS by direct loads.  gemm_lds_config: 0 = 256 x 256 tiles,
+// 1 = 256 x 128 tiles.
+hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L);
+int gemm_lds_config(int64_t M, int64_t N);
+
+// out[i] = bf16(sum_{z<nsplit} part[z*n + i]) in split order, n % 4 == 0
+struct SplitReduceArgs {
+  const float* part;
+  int nsplit;
+  int64_t n;
+  bf16_t* out;
+};
+hipError_t launch_splitk_reduce(const SplitReduceArgs& a, const Launch& L);
 
 struct LowRankZArgs {
   const bf16_t* X;      // [M][d]
