@@ -95,9 +95,8 @@ def check_problem(prob, gpu: dict, rows=None, report: dict = None,
     rep.update(dh_mismatch=0, strict_mismatch=0, contract_mismatch=0,
                contract_excused=0, literal_band=0, y_max=0.0, y_mean=0.0,
                y_normwise=0.0)
-    W32_all = oracle.bf16_to_f32(prob.W)
     sel = np.arange(prob.d_out) if rows is None else np.asarray(rows)
-    W32 = W32_all[sel]
+    W32 = oracle.bf16_to_f32(np.asarray(prob.W)[sel])
     for r in range(prob.R):
         ref = oracle.ttq_linear(
             prob.W, prob.X[r], bits=prob.bits, group=prob.group, p=prob.p,
