@@ -19,12 +19,13 @@
 //
 // Lane layout as in the fused kernel: lane l holds weight row l & 15 and
 // channels 8*(l >> 4) .. +8 of each 32-channel step (one 16-byte load of W);
-// a group's statistics live in lanes {l, l^16, l^32, l^48}.  16 waves stride
-// over the groups with two weight register sets (one group in flight while
-// the other is processed); the token's loads are issued ahead of the ring so
-// the statistics overlap the first weight fetches.  Weights are read with
-// bounded buffer loads: prefetches past the last group return zeros without
-// memory traffic, so the ring needs no branches.
+// a group's statistics live in lanes {l, l^16, l^32, l^48}.  Each of the 16
+// waves owns a contiguous run of groups (contiguous weight bytes per row),
+// derives the statistics of its own channels while its first weights are in
+// flight, and walks its groups with two weight register sets (one group in
+// flight while the other is processed).  Weights are read with bounded
+// buffer loads: prefetches past the last group return zeros without memory
+// traffic, so the ring needs no branches.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -61,7 +62,8 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
   constexpr int VW = gemv_waves<GS, EXPORT>();
   constexpr int NKS = GS / 32;
   // weight register sets in the ring: one group in flight while one is
-  // processed (measured on MI355X: deeper rings only add register pressure)
+  // processed (measured on MI355X: requesting a wave's next groups up front,
+  // all at once, is slower than issuing each when the previous one starts)
   constexpr int NR = 2;
   extern __shared__ __attribute__((aligned(16))) float lds[];
   // LDS: dh[d] | xp[d] | sxp[G] | red[VW][16]
@@ -101,65 +103,68 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     for (int k = 0; k < NKS; ++k) wv[k] = buf_load16(wr, lane_off + k * 64, soff);
   };
 
-  // ---- prologue.  The token's loads are issued and waited for first: once
-  // every CU's weight requests are queued, a later 8 KB read of x would sit
-  // behind them, and the statistics (and the barrier all waves wait at)
-  // would start only after most of W had arrived.  So x first, then the
-  // weight ring, then the statistics while the weights stream in.
-  // (d <= kGemvMaxD = VW * 64 * 4 * XPT: all of x is loaded here.)
-  constexpr int XPT = kGemvMaxD / (VW * 64 * 4);
-  float xf[XPT][4];
-  {
-    u32x2 xv[XPT];
+  // ---- prologue, per wave (no workgroup barrier).  Wave w owns the
+  // contiguous groups [w*NGW, (w+1)*NGW) and derives the statistics of
+  // exactly those channels:
+  //   D^{1/2}  float64, rounded once (it decides the codes)
+  //   x' = x D^{-1/2} (float32; it only enters the contraction)
+  //   group sums of x'
+  // Loads complete in issue order within a wave, so the token's channels are
+  // requested first and the weight ring right after: waiting for the token
+  // then leaves the weight loads in flight, and the float64 work overlaps
+  // them.  Token layout: piece p holds channels p*256 + 4*l .. +4 of the
+  // wave's run; a group spans GS / 4 adjacent lanes of one piece.
+  const int NGW = (G + VW - 1) / VW;
+  const int g_begin = w * NGW;
+  const int g_end = min(G, g_begin + NGW);
+  constexpr int NP = (int)(kGemvMaxD / (VW * 256));   // token pieces per lane
+  static_assert(NP * VW * 256 == kGemvMaxD, "token pieces");
+  const int64_t c_begin = (int64_t)g_begin * GS;
+  const int64_t c_end = (int64_t)g_end * GS;
+  u32x2 xv[NP];
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int64_t c = ((int64_t)i * VW * 64 + tid) * 4;
-      xv[i] = *(const u32x2*)(x + (c < d ? c : 0));
-    }
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      xf[i][0] = bf16lo(xv[i].x);
-      xf[i][1] = bf16hi(xv[i].x);
-      xf[i][2] = bf16lo(xv[i].y);
-      xf[i][3] = bf16hi(xv[i].y);
-    }
+  for (int p = 0; p < NP; ++p) {
+    const int64_t c = c_begin + p * 256 + l * 4;
+    xv[p] = *(const u32x2*)(x + (c < c_end ? c : 0));
   }
-  wait_vmem_all();
   __builtin_amdgcn_sched_barrier(0);
   u32x4 ring[NR][NKS];
-  int g = w;
+  int g = g_begin;
 #pragma unroll
-  for (int r = 0; r + 1 < NR; ++r) load_w(ring[r], g + r * VW);
+  for (int r = 0; r + 1 < NR; ++r) load_w(ring[r], g + r < g_end ? g + r : G);
   __builtin_amdgcn_sched_barrier(0);
-
-  // statistics of the token: D^{1/2} (float64, rounded once: it decides the
-  // codes), x' = x D^{-1/2} (float32; it only enters the contraction) and
-  // the group sums of x'.  4 channels per thread.
-  const int lpg = GS / 4;  // threads per group in this layout
+  constexpr int lpg4 = GS / 4;  // lanes per group
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int64_t c = ((int64_t)i * VW * 64 + tid) * 4;
+  for (int p = 0; p < NP; ++p) {
+    if (c_begin + p * 256 >= c_end) break;  // wave-uniform
+    const int64_t c = c_begin + p * 256 + l * 4;
+    const float xf[4] = {bf16lo(xv[p].x), bf16hi(xv[p].x), bf16lo(xv[p].y),
+                         bf16hi(xv[p].y)};
+    float hv[4], xpv[4];
     float ps = 0.f;
-    if (c < d) {
-      float hv[4], xpv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const double h = gemv_diag<FAST>(fabs((double)xf[i][j]), a.pmode, a.p,
-                                         a.lam, a.alpha);
-        hv[j] = (float)h;
-        xpv[j] = xf[i][j] * __builtin_amdgcn_rcpf(hv[j]);
-        ps += xpv[j];
-      }
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = (float)gemv_diag<FAST>(fabs((double)xf[j]), a.pmode, a.p, a.lam,
+                                     a.alpha);
+      xpv[j] = xf[j] * __builtin_amdgcn_rcpf(hv[j]);
+      ps += xpv[j];
+    }
+    if (c < c_end) {
       *(f32x4*)(dh_s + c) = f32x4{hv[0], hv[1], hv[2], hv[3]};
       *(f32x4*)(xp_s + c) = f32x4{xpv[0], xpv[1], xpv[2], xpv[3]};
       if (EXPORT && a.dh_export && rb == 0)
         *(f32x4*)(a.dh_export + (int64_t)req * d + c) =
             f32x4{hv[0], hv[1], hv[2], hv[3]};
     }
-    for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
-    if (c < d && (tid % lpg) == 0) sx_s[c / GS] = ps;
+#pragma unroll
+    for (int off = lpg4 >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    if (c < c_end && (l % lpg4) == 0) sx_s[c / GS] = ps;
   }
-  __syncthreads();
+  // the wave reads back only what it wrote: LDS operations of one wave
+  // complete in order, so a wave-level fence suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // ---- main loop: quantize-dequantize + dot, one group per step
   float acc = 0.f;
@@ -227,14 +232,15 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
 
   // ring of NR weight register sets: NR - 1 groups in flight while one is
   // processed (indices are compile-time after unrolling)
-  while (g < G) {
+  while (g < g_end) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      load_w(ring[(r + NR - 1) % NR], g + (NR - 1) * VW);
+      const int gn = g + NR - 1;
+      load_w(ring[(r + NR - 1) % NR], gn < g_end ? gn : G);
       __builtin_amdgcn_sched_barrier(0);
       process(ring[r], g);
-      g += VW;
-      if (g >= G) break;
+      g += 1;
+      if (g >= g_end) break;
     }
   }
 
