@@ -19,7 +19,10 @@
 // output of a token, so a single bf16 rounding of its x' would be shared by
 // all of them; there x' is carried as a bf16 pair hi + lo (~16 significant
 // bits) and both halves are contracted.  For T > 16 x' is rounded once to
-// bf16 and the rounding errors average over the tokens.
+// bf16 and the rounding errors average over the tokens; it is stored in MFMA
+// fragment order so that every activation load is a contiguous 1 KiB per
+// wave, and the weights are streamed with non-temporal loads so that they do
+// not evict x' (re-read by every workgroup) from L2.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 with A = x' (16 tokens x 32 channels) and
 // B = codes (32 channels x 16 weight rows).  Lane l holds weight row l & 15
@@ -31,8 +34,8 @@
 // Work split: a workgroup of 8 waves owns 16 weight rows and all of K; waves
 // stride over the groups and meet once in LDS at the end (fixed order, no
 // inter-workgroup traffic, deterministic).  D^{1/2} of the request is staged
-// in LDS once per workgroup (when it fits).  Workgroup indices are laid out so that
-// the R requests of one weight tile run back to back on the same XCD and
+// in LDS once per workgroup (when it fits).  Workgroup indices are laid out so
+// that the R requests of one weight tile run back to back on the same XCD and
 // share the tile through its L2.
 #include "ttq_internal.h"
 
@@ -65,9 +68,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const int Tp = NTB * 16;
 
   const float* dhg = a.dh + (int64_t)req * d;
-  const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 : 1) * T * d;
-  const bf16_t* xs_lo = xs + T * d;
+  const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 * T : Tp) * d;
   const float* sx = a.sx + (int64_t)req * G * Tp;
+  const bf16_t* xs_lo = xs + T * d;
   // the workgroup's weight rows as one bounded buffer: rows past d_out and
   // groups past the end read as zeros without memory traffic
   const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
@@ -87,7 +90,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   auto load_w = [&](u32x4 (&wv)[NKS], int g) {
     const uint32_t soff = g < G ? (uint32_t)g * GS * 2 : kOutOfRange;
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) wv[k] = buf_load16(wr, lane_off + k * 64, soff);
+    for (int k = 0; k < NKS; ++k)
+      wv[k] = HILO ? buf_load16(wr, lane_off + k * 64, soff)
+                   : buf_load16_nt(wr, lane_off + k * 64, soff);
   };
   // lanes whose token is past T read a small zero buffer instead of
   // branching (no divergent load paths for the wait-count logic)
@@ -184,12 +189,11 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
       f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
+        const bf16x8 q = __builtin_bit_cast(bf16x8, qv[k]);
         P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xh[k]), __builtin_bit_cast(bf16x8, qv[k]),
-            P, 0, 0, 0);
+            __builtin_bit_cast(bf16x8, xh[k]), q, P, 0, 0, 0);
         P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xl[k]), __builtin_bit_cast(bf16x8, qv[k]),
-            P, 0, 0, 0);
+            __builtin_bit_cast(bf16x8, xl[k]), q, P, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -197,12 +201,11 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     } else {
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        const int64_t tok = tb * 16 + lr;
+        // fragment-ordered x' (zero past T): each load is 1 KiB per wave
         u32x4 xv[NKS];
 #pragma unroll
         for (int k = 0; k < NKS; ++k)
-          xv[k] = tok < T ? *(const u32x4*)(xs + tok * d + colg + k * 32)
-                          : u32x4{0u, 0u, 0u, 0u};
+          xv[k] = *(const u32x4*)(xs + 8 * xs_frag_index(g, tb, k, l, NTB, GS));
         const f32x4 sxv = *(const f32x4*)(sx + (int64_t)g * Tp + tb * 16 + qd * 4);
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -58,84 +58,104 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 }
 
 // ---------------------------------------------------------------------------
-// Small T (fused path): a workgroup of 256 threads owns 256 channels and one
-// chunk of 16 tokens.  It reduces the norm of its channels over all T tokens
-// (8 token lanes x 32 channel lanes of 8 channels, float64 partials meeting
-// in LDS), finishes D^{+-1/2} with one thread per channel, then writes, for
-// its 16 tokens only, x' = x * D^{-1/2} and the per-group sums of x'.  The
-// token chunks of a channel block recompute the same norms (T <= 128 rows of
-// 512 bytes, from L2) and the same powers; chunk 0 stores D^{+-1/2}.
+// Small T (T <= 128, fused path and statistics-only calls): a workgroup of
+// 1024 threads owns BC channels (128, or 256 for groups of 256: always whole
+// quantization groups) and every token.  Thread (token lane tl, channel chunk
+// cq) loads the tokens tl + i * TLN of 8 consecutive channels; the float64
+// partial powers are summed over the token lanes of a wave (fixed butterfly),
+// then over the waves in LDS in order, one thread per channel finishes
+// D^{+-1/2} and publishes it.  Then every thread writes x' = x * D^{-1/2} for
+// its tokens (the fused kernel's MFMA operand) and the group sums of x' per
+// token.  X is read once.
 //
-// x' is the MFMA operand of the fused kernel.  For T <= 16 it is carried as an
-// unevaluated pair of bf16 numbers hi + lo (hi = bf16(x'), lo = bf16(x' -
-// hi)), about 16 significant bits: with few tokens one outlier channel can
-// dominate every output and a single bf16 rounding of it would be shared by
-// all of them.  For larger T a single bf16 plane is written.  The group sums
-// are of exactly the values written, padded with zeros to the chunk end.
+// For T <= 16 x' is carried as an unevaluated pair of bf16 numbers hi + lo
+// (hi = bf16(x'), lo = bf16(x' - hi)), about 16 significant bits: with few
+// tokens one outlier channel can dominate every output and a single bf16
+// rounding of it would be shared by all of them.  For larger T a single bf16
+// plane is written, in MFMA fragment order (xs_frag_index) and zero-padded to
+// whole 16-token blocks.  The group sums are of exactly the values written,
+// zero past T up to the padded token count.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_stats_small(StatsSmallArgs a) {
-  __shared__ double red[8][256];
-  __shared__ float dhi_l[256];
+template <int PM, int BC>
+__global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
+  constexpr int NCH = BC / 8;          // channel chunks
+  constexpr int TLN = 1024 / NCH;      // token lanes
+  constexpr int TPW = 64 / NCH;        // token lanes per wave
+  constexpr int NTK = 128 / TLN;       // tokens per thread (T <= 128)
+  __shared__ double red[16][BC];
+  __shared__ float dhi_l[BC];
   const int tid = threadIdx.x;
-  const int tg = tid >> 5, cl = tid & 31;
+  const int cq = tid % NCH, tl = tid / NCH;
+  const int wv = tid >> 6;
   const int r = blockIdx.z;
-  const int64_t c_base = (int64_t)blockIdx.x * 256;
-  const int64_t c0 = c_base + cl * 8;
-  const int64_t t0 = (int64_t)blockIdx.y * 16;
+  const int64_t c0 = (int64_t)blockIdx.x * BC + cq * 8;
   const bool live = c0 < a.d;
   const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
 
-  if (a.zeros && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 &&
+  if (a.zeros && blockIdx.x == 0 && blockIdx.z == 0 &&
       tid < (int)(kZeroBytes / 4))
     ((unsigned*)a.zeros)[tid] = 0u;
 
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) {
-    int64_t t = tg;
-    for (; t + 8 < a.T; t += 16) {
-      const u32x4 v0 = *(const u32x4*)(X + t * a.d + c0);
-      const u32x4 v1 = *(const u32x4*)(X + (t + 8) * a.d + c0);
-      accum8(acc, v0, a.pmode, a.p);
-      accum8(acc, v1, a.pmode, a.p);
-    }
-    if (t < a.T) accum8(acc, *(const u32x4*)(X + t * a.d + c0), a.pmode, a.p);
-  }
+  u32x4 v[NTK];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[tg][cl * 8 + j] = acc[j];
-  __syncthreads();
+  for (int i = 0; i < NTK; ++i) {
+    const int64_t t = tl + i * TLN;
+    v[i] = (live && t < a.T) ? *(const u32x4*)(X + t * a.d + c0)
+                             : u32x4{0u, 0u, 0u, 0u};
+  }
   {
-    const int64_t c = c_base + tid;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NTK; ++i)
+      if (live && tl + i * TLN < a.T) accum8(acc, v[i], PM, a.p);
+    // token lanes of this wave (lanes cq, cq + NCH, ...): fixed butterfly
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int off = NCH; off < 64; off <<= 1) acc[j] += __shfl_xor(acc[j], off);
+      if (tl % TPW == 0) red[wv][cq * 8 + j] = acc[j];
+    }
+  }
+  __syncthreads();
+  if (tid < BC) {
+    const int64_t c = (int64_t)blockIdx.x * BC + tid;
     double S = 0.0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) S += red[k][tid];
+    for (int k = 0; k < 16; ++k) S += red[k][tid];
     float dh = 1.f, dhi = 1.f;
     if (c < a.d) {
-      diag_half(finish_norm(S, a.pmode, a.p), a.lam, a.alpha, dh, dhi);
-      if (blockIdx.y == 0) {
-        a.dh[(int64_t)r * a.d + c] = dh;
-        a.dhi[(int64_t)r * a.d + c] = dhi;
-        if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
-      }
+      diag_half(finish_norm(S, PM, a.p), a.lam, a.alpha, dh, dhi);
+      a.dh[(int64_t)r * a.d + c] = dh;
+      a.dhi[(int64_t)r * a.d + c] = dhi;
+      if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
     }
     dhi_l[tid] = dhi;
   }
   if (!a.xs) return;
   __syncthreads();
 
-  const int lpg = a.group >> 3;  // lanes per quantization group
+  const bool tiled = a.planes == 1;
+  const int ntb = a.Tp / 16;
   const int G = (int)(a.d / a.group);
-  bf16_t* xs = a.xs + (int64_t)r * a.planes * a.T * a.d;
+  const int lpg = a.group >> 3;  // chunk lanes per quantization group
+  bf16_t* xs = a.xs + (int64_t)r * (tiled ? (int64_t)a.Tp : 2 * a.T) * a.d;
   bf16_t* xs_lo = xs + a.T * a.d;
   float* sx = a.sx + (int64_t)r * G * a.Tp;
   float sc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sc[j] = dhi_l[cl * 8 + j];
-  for (int64_t t = t0 + tg; t < t0 + 16; t += 8) {
+  for (int j = 0; j < 8; ++j) sc[j] = dhi_l[cq * 8 + j];
+  const int64_t g = c0 / a.group, k = (c0 % a.group) / 32;
+  const int lane_q = (int)((c0 % 32) / 8) * 16;
+#pragma unroll
+  for (int i = 0; i < NTK; ++i) {
+    const int64_t t = tl + i * TLN;
+    if (t >= a.Tp) break;  // uniform across the chunk lanes of a token
     float ps = 0.f;
+    u32x4 o = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
     if (live && t < a.T) {
-      const u32x4 v = *(const u32x4*)(X + t * a.d + c0);
-      const float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                          bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      const float x[8] = {bf16lo(v[i].x), bf16hi(v[i].x), bf16lo(v[i].y),
+                          bf16hi(v[i].y), bf16lo(v[i].z), bf16hi(v[i].z),
+                          bf16lo(v[i].w), bf16hi(v[i].w)};
       unsigned bh[8], bl[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -143,34 +163,41 @@ __global__ __launch_bounds__(256) void k_stats_small(StatsSmallArgs a) {
         bh[j] = f2bf(xp);
         const float hi = __uint_as_float(bh[j] << 16);
         bl[j] = f2bf(xp - hi);
-        ps += a.planes == 2 ? hi + __uint_as_float(bl[j] << 16) : hi;
+        ps += tiled ? hi : hi + __uint_as_float(bl[j] << 16);
       }
-      u32x4 o;
-      o.x = bh[0] | (bh[1] << 16);
-      o.y = bh[2] | (bh[3] << 16);
-      o.z = bh[4] | (bh[5] << 16);
-      o.w = bh[6] | (bh[7] << 16);
-      *(u32x4*)(xs + t * a.d + c0) = o;
-      if (a.planes == 2) {
-        u32x4 ol;
-        ol.x = bl[0] | (bl[1] << 16);
-        ol.y = bl[2] | (bl[3] << 16);
-        ol.z = bl[4] | (bl[5] << 16);
-        ol.w = bl[6] | (bl[7] << 16);
+      o = u32x4{bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16),
+                bh[4] | (bh[5] << 16), bh[6] | (bh[7] << 16)};
+      ol = u32x4{bl[0] | (bl[1] << 16), bl[2] | (bl[3] << 16),
+                 bl[4] | (bl[5] << 16), bl[6] | (bl[7] << 16)};
+    }
+    if (live) {
+      if (tiled) {
+        const int lane = lane_q + (int)(t & 15);
+        *(u32x4*)(xs + 8 * xs_frag_index(g, t >> 4, k, lane, ntb, a.group)) = o;
+      } else if (t < a.T) {
+        *(u32x4*)(xs + t * a.d + c0) = o;
         *(u32x4*)(xs_lo + t * a.d + c0) = ol;
       }
     }
-    // lanes of one group are adjacent inside a 32-lane half wave
+    // the chunk lanes of one group are adjacent within a token row
     for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
-    if (live && (cl % lpg) == 0 && t < a.Tp)
-      sx[(int64_t)(c0 / a.group) * a.Tp + t] = ps;
+    if (live && (cq % lpg) == 0) sx[g * a.Tp + t] = ps;
   }
 }
 
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
-  const unsigned chunks = a.xs ? (unsigned)(a.Tp / 16) : 1u;
-  dim3 grid((unsigned)((a.d + 255) / 256), chunks, (unsigned)R);
-  return ext_launch(k_stats_small, grid, dim3(256), 0, L, a);
+  if (a.T > 128) return hipErrorInvalidValue;
+  const dim3 blk(1024);
+  if (a.group == 256) {
+    const dim3 grid((unsigned)((a.d + 255) / 256), 1u, (unsigned)R);
+    if (a.pmode == 2) return ext_launch(k_stats_small<2, 256>, grid, blk, 0, L, a);
+    if (a.pmode == 1) return ext_launch(k_stats_small<1, 256>, grid, blk, 0, L, a);
+    return ext_launch(k_stats_small<0, 256>, grid, blk, 0, L, a);
+  }
+  const dim3 grid((unsigned)((a.d + 127) / 128), 1u, (unsigned)R);
+  if (a.pmode == 2) return ext_launch(k_stats_small<2, 128>, grid, blk, 0, L, a);
+  if (a.pmode == 1) return ext_launch(k_stats_small<1, 128>, grid, blk, 0, L, a);
+  return ext_launch(k_stats_small<0, 128>, grid, blk, 0, L, a);
 }
 
 // ---------------------------------------------------------------------------

@@ -106,7 +106,8 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     while (P.ntb * 16 < T) P.ntb *= 2;
     P.rowblocks = (dout + 15) / 16;
     P.planes = T <= 16 ? 2 : 1;
-    P.off_xs = take(sizeof(uint16_t) * P.planes * R * T * d);
+    P.off_xs = take(sizeof(uint16_t) * P.planes * R *
+                    (P.planes == 2 ? T : 16 * P.ntb) * d);
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
     P.off_zeros = take(kZeroBytes);
   } else {

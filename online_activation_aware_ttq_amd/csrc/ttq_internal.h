@@ -60,6 +60,13 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r,
   return __builtin_bit_cast(u32x4,
                             __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// Same, non-temporal (streamed data that should not displace reused lines
+// from the caches; cache-policy bit NT of the gfx94x/gfx950 encoding).
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r,
+                                               uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
 // Wait until every vector memory access of this wave has completed (gfx9
 // s_waitcnt encoding: vmcnt[3:0] = 0, expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
 // Used to order a small dependent read ahead of a large batch of loads.
@@ -70,6 +77,20 @@ __device__ __forceinline__ void wait_vmem_all() {
 // scalar offset that puts a load out of range (no wrap-around: the lane
 // offsets of a weight tile stay far below 2^30)
 constexpr uint32_t kOutOfRange = 0x40000000u;
+
+// Scaled activations x' = x D^{-1/2} as the fused kernel's MFMA operand.
+//   T <= 16: two planes (bf16 hi, lo), each token-major [T][d].
+//   T  > 16: one plane in MFMA fragment order, Tp = 16 * ceil(T / 16) tokens
+//     (zeros past T): the 16-byte fragment of lane l for group g, 16-token
+//     block tb and 32-channel step k holds tokens tb*16 + (l & 15), channels
+//     g*GS + k*32 + 8*(l >> 4) .. +8, at fragment index
+//     ((g * NTB + tb) * (GS / 32) + k) * 64 + l, so that one wave load of a
+//     fragment is 1 KiB contiguous.
+__host__ __device__ inline int64_t xs_frag_index(int64_t g, int64_t tb,
+                                                 int64_t k, int l, int ntb,
+                                                 int gs) {
+  return ((g * ntb + tb) * (gs / 32) + k) * 64 + l;
+}
 
 // ---------------------------------------------------------------- launchers
 // Where and how to launch: the stream, plus optional events that the runtime
@@ -95,11 +116,11 @@ struct StatsSmallArgs {
   float* dh;            // [R][d]
   float* dhi;           // [R][d]
   float* dh_export;     // optional [R][d]
-  bf16_t* xs;           // optional [R][planes][T][d] x * D^{-1/2} (bf16 hi[, lo])
-  float* sx;            // optional [R][G][Tp] group sums of xs, zero past T
+  bf16_t* xs;           // optional x * D^{-1/2} in bf16, see xs_frag_index
+  float* sx;            // with xs: [R][G][Tp] group sums of xs, zero past T
   int group;
   int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16
-  int Tp;               // padded token count of sx
+  int Tp;               // 16 * ceil(T / 16): tokens of the fragment layout
   bf16_t* zeros;        // optional kZeroBytes to clear
 };
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
@@ -126,8 +147,9 @@ struct FusedArgs {
   int G;                // groups per row
   float Nf;             // 2^bits - 1
   const float* dh;      // [R][d]
-  const bf16_t* xs;     // [R][planes][T][d]; planes = 2 (hi, lo) iff T <= 16
-  const float* sx;      // [R][G][Tp], Tp = 16 * ntb, zero past T
+  const bf16_t* xs;     // x * D^{-1/2}, layout as written by the stats kernel
+  const float* sx;      // [R][G][Tp] group sums of xs, Tp = 16 * ntb,
+                        // zero past T
   const bf16_t* Z;      // [R][T][rp] or null
   const bf16_t* Blr;    // [d_out][rank] or null
   int rank, rp;
