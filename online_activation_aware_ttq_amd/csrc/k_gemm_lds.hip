@@ -25,7 +25,8 @@
 //    MFMAs of the current one (register double buffer).
 // Workgroups are ordered so that the M tiles of one weight tile run back to
 // back on the same XCD (shared through that XCD's L2); narrower outputs are
-// spread over all XCDs.
+// spread over all XCDs.  A batch of independent products (one per request,
+// each with its own W_hat) is the second grid dimension.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -45,6 +46,14 @@ __device__ __forceinline__ void wait_vm() {
 // TM x TN MFMA tiles of 32 x 32 per wave, WGM x WGN waves, NS LDS stages.
 template <int TM, int TN, int WGM, int WGN, int NS>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
+  if (blockIdx.y > 0) {  // product z of a batch
+    const int64_t z = blockIdx.y;
+    a.A1 += z * a.sA1;
+    a.B1 += z * a.sB1;
+    if (a.A2) a.A2 += z * a.sA2;
+    if (a.B2) a.B2 += z * a.sB2;
+    a.C += z * a.sC;
+  }
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32, BK = 64;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
@@ -228,24 +237,25 @@ hipError_t launch_t(const GemmArgs& a, const Launch& L) {
       reinterpret_cast<const void*>(k_gemm_lds<TM, TN, WGM, WGN, NS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  return ext_launch(k_gemm_lds<TM, TN, WGM, WGN, NS>, dim3((unsigned)nblk),
+  const unsigned nb = a.batch > 1 ? (unsigned)a.batch : 1u;
+  return ext_launch(k_gemm_lds<TM, TN, WGM, WGN, NS>, dim3((unsigned)nblk, nb),
                     dim3(WGM * WGN * 64), lds, L, a);
 }
 
 }  // namespace
 
-int gemm_lds_config(int64_t M, int64_t N) {
+int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
   // 256 x 256 tiles keep the most MFMA work per LDS byte; when they would
   // leave a quarter of the 256 CUs idle in a single round, 256 x 128 tiles
   // give twice as many workgroups
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256) * batch;
   return big >= 192 ? 0 : 1;
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L) {
   if (a.M <= 0 || a.N_store <= 0) return hipSuccess;
   if (a.K1 <= 0 || !a.C || a.nsplit > 1) return hipErrorInvalidValue;
-  if (gemm_lds_config(a.M, a.N_store) == 0)
+  if (gemm_lds_config(a.M, a.N_store, a.batch > 1 ? a.batch : 1) == 0)
     return launch_t<4, 2, 2, 4, 2>(a, L);   // 256 x 256, 8 waves, 2 stages
   return launch_t<2, 2, 4, 2, 3>(a, L);     // 256 x 128, 8 waves, 3 stages
 }

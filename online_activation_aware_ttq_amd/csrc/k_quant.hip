@@ -5,7 +5,8 @@
 // ("TTQ: Activation-Aware Test-Time Quantization ...", gist.science zh
 // summary, Sec. 2.1), which the MFMA GEMM then contracts with the raw bf16
 // activations.  The codes are decided by the same float32 sequence as the
-// fused path.  A wave covers 512 consecutive channels of 8 weight rows: each
+// fused path (for R requests at once, each with its own statistics and its
+// own W_hat).  A wave covers 512 consecutive channels of 8 weight rows: each
 // lane loads 16 bytes per row, a group of g channels lives in g/8 adjacent
 // lanes and is reduced with xor-shuffles inside that lane group.
 #include "ttq_internal.h"
@@ -19,7 +20,16 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   constexpr int LPG = GS / 8;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int64_t nchunk = (a.d + 511) / 512;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + w;
+  const int64_t nblk1 = (((a.d_out + QROWS - 1) / QROWS) * nchunk + 3) / 4;
+  // the R requests of one weight tile run back to back on the same XCD and
+  // share it through that XCD's L2
+  const int64_t b = blockIdx.x;
+  const int xcd = (int)(b & 7);
+  const int64_t jb = b >> 3;
+  const int64_t bq = (jb / a.R) * 8 + xcd;
+  const int r = (int)(jb % a.R);
+  if (bq >= nblk1) return;
+  const int64_t wid = bq * 4 + w;
   const int64_t rgrp = wid / nchunk;
   const int64_t chunk = wid % nchunk;
   const int64_t row0 = rgrp * QROWS;
@@ -27,13 +37,19 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   const int64_t c0 = chunk * 512 + l * 8;
   const bool live = c0 < a.d;
   const float Nf = a.Nf;
+  const float* dhr = a.dh + (int64_t)r * a.d;
+  const float* dhir = a.dhi + (int64_t)r * a.d;
+  bf16_t* What = a.What + (int64_t)r * a.d_out * a.d;
+  uint8_t* codes_out = a.codes_out ? a.codes_out + (int64_t)r * a.d_out * a.d : nullptr;
+  float* s_out = a.s_out ? a.s_out + (int64_t)r * a.d_out * a.G : nullptr;
+  float* m_out = a.m_out ? a.m_out + (int64_t)r * a.d_out * a.G : nullptr;
 
   float dh[8], dhi[8];
   if (live) {
-    const f32x4 h0 = *(const f32x4*)(a.dh + c0);
-    const f32x4 h1 = *(const f32x4*)(a.dh + c0 + 4);
-    const f32x4 i0 = *(const f32x4*)(a.dhi + c0);
-    const f32x4 i1 = *(const f32x4*)(a.dhi + c0 + 4);
+    const f32x4 h0 = *(const f32x4*)(dhr + c0);
+    const f32x4 h1 = *(const f32x4*)(dhr + c0 + 4);
+    const f32x4 i0 = *(const f32x4*)(dhir + c0);
+    const f32x4 i1 = *(const f32x4*)(dhir + c0 + 4);
     dh[0] = h0.x; dh[1] = h0.y; dh[2] = h0.z; dh[3] = h0.w;
     dh[4] = h1.x; dh[5] = h1.y; dh[6] = h1.z; dh[7] = h1.w;
     dhi[0] = i0.x; dhi[1] = i0.y; dhi[2] = i0.z; dhi[3] = i0.w;
@@ -82,19 +98,19 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     o.y = pack_bf16(fmaf(s, q[2], mn) * dhi[2], fmaf(s, q[3], mn) * dhi[3]);
     o.z = pack_bf16(fmaf(s, q[4], mn) * dhi[4], fmaf(s, q[5], mn) * dhi[5]);
     o.w = pack_bf16(fmaf(s, q[6], mn) * dhi[6], fmaf(s, q[7], mn) * dhi[7]);
-    *(u32x4*)(a.What + row * a.d + c0) = o;
-    if (a.codes_out) {
+    *(u32x4*)(What + row * a.d + c0) = o;
+    if (codes_out) {
       u32x2 c;
       c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
             ((unsigned)q[3] << 24);
       c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
             ((unsigned)q[7] << 24);
-      *(u32x2*)(a.codes_out + row * a.d + c0) = c;
+      *(u32x2*)(codes_out + row * a.d + c0) = c;
     }
-    if (a.s_out && (l % LPG) == 0) {
+    if (s_out && (l % LPG) == 0) {
       const int64_t o2 = row * a.G + c0 / GS;
-      a.s_out[o2] = s;
-      a.m_out[o2] = mn;
+      s_out[o2] = s;
+      m_out[o2] = mn;
     }
   }
 }
@@ -102,7 +118,9 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
 hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L) {
   const int64_t nchunk = (a.d + 511) / 512;
   const int64_t waves = ((a.d_out + QROWS - 1) / QROWS) * nchunk;
-  const dim3 grid((unsigned)((waves + 3) / 4)), blk(256);
+  const int64_t nblk1 = (waves + 3) / 4;
+  if (nblk1 == 0 || a.R == 0) return hipSuccess;
+  const dim3 grid((unsigned)(((nblk1 + 7) / 8) * 8 * a.R)), blk(256);
   switch (group) {
     case 32: return ext_launch(k_quant<32>, grid, blk, 0, L, a);
     case 64: return ext_launch(k_quant<64>, grid, blk, 0, L, a);

@@ -22,6 +22,8 @@ constexpr int64_t kMaxDout = int64_t(1) << 22;
 constexpr int64_t kMaxT = int64_t(1) << 22;
 constexpr int64_t kMaxR = 4096;
 constexpr int64_t kMaxElems = int64_t(1) << 34;
+// two-phase path: workspace for the dequantized weights of several requests
+constexpr int64_t kMaxWhatBytes = int64_t(4) << 30;
 constexpr int kFusedMaxT = 128;
 
 constexpr size_t kGemvLdsMax = 128 * 1024;
@@ -40,6 +42,7 @@ struct Plan {
   int64_t rowblocks = 0;
   int tchunk = 0, nsplit = 0;
   int64_t rp = 0;        // rank padded to a multiple of 32
+  int64_t rchunk = 1;    // two-phase: requests quantized per pass
   int zsplit = 1;        // two-phase: K splits of Z = X A^T
   int64_t zksplit = 0;   // channels per split
   size_t off_dh = 0, off_dhi = 0, off_xs = 0, off_sx = 0, off_z = 0,
@@ -121,7 +124,12 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.tchunk = (int)tch;
     P.nsplit = (int)((T + P.tchunk - 1) / P.tchunk);
     P.off_statp = take(sizeof(double) * R * ((P.nsplit + 3) / 4) * d);
-    P.off_what = take(sizeof(uint16_t) * dout * d);
+    // W_hat of up to rchunk requests at a time (at most kMaxWhatBytes)
+    const int64_t per = (int64_t)sizeof(uint16_t) * dout * d;
+    P.rchunk = per > 0 ? kMaxWhatBytes / per : R;
+    if (P.rchunk < 1) P.rchunk = 1;
+    if (P.rchunk > R) P.rchunk = R;
+    P.off_what = take((size_t)(per * P.rchunk));
     if (P.rp > 0 && T > 0) {
       // Z has few output tiles (rank columns): split the channels so that
       // about 512 workgroups run, each over at least 256 channels
@@ -323,24 +331,30 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
       if (st != TTQ_OK) return st;
     }
   }
+  // requests in chunks of P.rchunk: one quantize pass (each request its own
+  // W_hat), then one batched GEMM launch per chunk
   bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
-  for (int64_t r = 0; r < R; ++r) {
+  for (int64_t r0 = 0; r0 < R; r0 += P.rchunk) {
+    const int64_t rc = R - r0 < P.rchunk ? R - r0 : P.rchunk;
     QuantArgs qa{};
-    qa.W = Wb; qa.d = d; qa.d_out = dout; qa.G = P.G; qa.Nf = Nf;
-    qa.dh = dh + r * d; qa.dhi = dhi + r * d; qa.What = What;
-    qa.codes_out = codes_out ? codes_out + r * dout * d : nullptr;
-    qa.s_out = scales_out ? scales_out + r * dout * P.G : nullptr;
-    qa.m_out = mins_out ? mins_out + r * dout * P.G : nullptr;
+    qa.W = Wb; qa.d = d; qa.d_out = dout; qa.G = P.G; qa.R = (int)rc; qa.Nf = Nf;
+    qa.dh = dh + r0 * d; qa.dhi = dhi + r0 * d; qa.What = What;
+    qa.codes_out = codes_out ? codes_out + r0 * dout * d : nullptr;
+    qa.s_out = scales_out ? scales_out + r0 * dout * P.G : nullptr;
+    qa.m_out = mins_out ? mins_out + r0 * dout * P.G : nullptr;
     st = run(K_QUANT, s, [&](const Launch& L) { return launch_quant(qa, prm->group, L); });
     if (st != TTQ_OK) return st;
     GemmArgs ga{};
-    ga.A1 = Xb + r * T * d; ga.lda1 = d; ga.B1 = What; ga.ldb1 = d; ga.K1 = d;
+    ga.A1 = Xb + r0 * T * d; ga.lda1 = d; ga.B1 = What; ga.ldb1 = d; ga.K1 = d;
     if (P.rp > 0) {
-      ga.A2 = Zb + r * T * P.rp; ga.lda2 = P.rp;
+      ga.A2 = Zb + r0 * T * P.rp; ga.lda2 = P.rp;
       ga.B2 = Bb; ga.ldb2 = rank; ga.K2 = rank;
     }
     ga.M = T; ga.N = dout; ga.N_store = dout;
-    ga.C = Y + r * T * dout; ga.ldc = dout;
+    ga.C = Y + r0 * T * dout; ga.ldc = dout;
+    ga.batch = (int)rc;
+    ga.sA1 = T * d; ga.sB1 = dout * d; ga.sA2 = T * P.rp; ga.sB2 = 0;
+    ga.sC = T * dout;
     st = run(K_GEMM, s, [&](const Launch& L) { return launch_gemm_lds(ga, L); });
     if (st != TTQ_OK) return st;
   }

@@ -192,16 +192,17 @@ size_t gemv_lds_bytes(int64_t d, int G);
 hipError_t launch_gemv(const GemvArgs& a, int group, const Launch& L);
 
 struct QuantArgs {
-  const bf16_t* W;      // [d_out][d]
+  const bf16_t* W;      // [d_out][d], shared by the requests
   int64_t d, d_out;
   int G;
+  int R;                // requests, each with its own statistics
   float Nf;
-  const float* dh;      // [d]
-  const float* dhi;     // [d]
-  bf16_t* What;         // [d_out][d]
-  uint8_t* codes_out;   // [d_out][d]
-  float* s_out;
-  float* m_out;
+  const float* dh;      // [R][d]
+  const float* dhi;     // [R][d]
+  bf16_t* What;         // [R][d_out][d]
+  uint8_t* codes_out;   // [R][d_out][d]
+  float* s_out;         // [R][d_out][G]
+  float* m_out;         // [R][d_out][G]
 };
 hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L);
 
@@ -222,13 +223,17 @@ struct GemmArgs {
   int64_t ksplit;                   // multiple of 64; 0 = no split
   int nsplit;
   int64_t split_stride;
+  // batch of independent products (large-tile kernel): product z uses
+  // A1 + z*sA1, B1 + z*sB1, A2 + z*sA2, B2 + z*sB2 and writes C + z*sC
+  int batch;                        // 0 or 1 = a single product
+  int64_t sA1, sB1, sA2, sB2, sC;
 };
 hipError_t launch_gemm(const GemmArgs& a, const Launch& L);
 // Large-tile variant for the projection GEMM (fp32 C, no split): operands
 // streamed into LDS by direct loads.  gemm_lds_config: 0 = 256 x 256 tiles,
 // 1 = 256 x 128 tiles.
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L);
-int gemm_lds_config(int64_t M, int64_t N);
+int gemm_lds_config(int64_t M, int64_t N, int64_t batch);
 
 // out[i] = bf16(sum_{z<nsplit} part[z*n + i]) in split order, n % 4 == 0
 struct SplitReduceArgs {
