@@ -66,6 +66,11 @@ __all__ = [
     "ttq_linear_batched",
     "band_excused",
     "symmetric_quantize",
+    "code_container_bits",
+    "pack_codes",
+    "unpack_codes",
+    "ttq_quantize",
+    "ttq_qmatmul",
 ]
 
 
@@ -225,6 +230,99 @@ def ttq_linear(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
 def ttq_linear_batched(W_bits, X_bits, **kw) -> list:
     """R independent requests on a shared W (and B, A): one D per request."""
     return [ttq_linear(W_bits, X_bits[r], **kw) for r in range(X_bits.shape[0])]
+
+
+# --------------------------------------------------------------------------
+# quantize once per prompt, then contract later tokens with stored codes
+# --------------------------------------------------------------------------
+# The statistics are computed per input prompt ([NL] Sec. 2, methodology),
+# and the speed-up of the deployed model comes from integer-matmul kernels
+# over stored low-bit weights ([NL] Sec. 3, efficiency; [ZH] Sec. 3) because
+# moving the weights is the bottleneck at scale ([ZH] Sec. 4).  Reading
+# (listed in DESIGN.md): the deployed form keeps the codes, the per-group
+# (s, min) and D^{-1/2} of the prompt, and every later step computes
+# Y = ((min + s q) D^{-1/2}) X + B (A X) with those stored values.
+#
+# Storage of the codes: each code takes the smallest of 1, 2, 4, 8 bits that
+# holds b bits ("container"), channel j of a row at bit (j * cb) % 8 of byte
+# (j * cb) // 8 (least significant bits first).
+
+def code_container_bits(bits: int) -> int:
+    """Storage width in bits of one b-bit code."""
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be in 1..8")
+    for cb in (1, 2, 4, 8):
+        if bits <= cb:
+            return cb
+    raise AssertionError
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """uint8 codes [rows, d] -> packed bytes [rows, d * cb / 8]."""
+    cb = code_container_bits(bits)
+    q = np.asarray(q, dtype=np.uint8)
+    rows, d = q.shape
+    if (d * cb) % 8:
+        raise ValueError("d * container bits must be a whole number of bytes")
+    if q.size and int(q.max()) >= (1 << bits):
+        raise ValueError("code out of range")
+    per = 8 // cb                         # codes per byte
+    qq = q.reshape(rows, d // per, per).astype(np.uint16)
+    out = np.zeros((rows, d // per), dtype=np.uint16)
+    for k in range(per):
+        out |= qq[:, :, k] << (k * cb)
+    return out.astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, d: int) -> np.ndarray:
+    """Inverse of ``pack_codes``."""
+    cb = code_container_bits(bits)
+    per = 8 // cb
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    mask = (1 << cb) - 1
+    parts = [(packed >> (k * cb)) & mask for k in range(per)]
+    return np.stack(parts, axis=-1).reshape(rows, d).astype(np.uint8)
+
+
+def ttq_quantize(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
+                 group: int, p: float, lam: float, alpha: float,
+                 rows: Optional[np.ndarray] = None,
+                 dh32_override: Optional[np.ndarray] = None) -> dict:
+    """Statistics of one prompt X and the quantized weights to keep.
+
+    Same steps as ``ttq_linear`` up to the codes; returns ``q`` (uint8),
+    ``packed`` (``pack_codes``), ``s, m`` (float32 [rows, G]), ``dh32`` and
+    ``dhi32`` = float32(1 / D^{1/2}) (the stored D^{-1/2}), and the float64
+    ``dh, dhi``.
+    """
+    X = bf16_to_f64(X_bits)
+    d_out = W_bits.shape[0]
+    sel = np.arange(d_out) if rows is None else np.asarray(rows)
+    Wsel = np.asarray(W_bits)[sel]
+    n = channel_norms(X, p)
+    dh, dhi = diag_scales(n, lam, alpha)
+    dh32 = dh.astype(np.float32) if dh32_override is None else \
+        np.asarray(dh32_override, dtype=np.float32)
+    q, s, m = encode_groups_fp32(bf16_to_f32(Wsel), dh32, bits, group)
+    return dict(q=q, packed=pack_codes(q, bits), s=s, m=m, dh=dh, dhi=dhi,
+                dh32=dh32, dhi32=dhi.astype(np.float32), rows=sel)
+
+
+def ttq_qmatmul(packed: np.ndarray, s: np.ndarray, m: np.ndarray,
+                dhi32: np.ndarray, X_bits: np.ndarray, *, bits: int,
+                group: int, B_bits: Optional[np.ndarray] = None,
+                A_bits: Optional[np.ndarray] = None) -> np.ndarray:
+    """Y [T, rows] = X ((min + s q) D^{-1/2})^T + (X A^T) B^T, float64, from
+    the stored codes, (s, min) and D^{-1/2} of an earlier prompt."""
+    X = bf16_to_f64(X_bits)
+    d = X.shape[1]
+    q = unpack_codes(packed, bits, d)
+    W_hat = dequantize(q, s, m, np.asarray(dhi32, dtype=np.float64), group)
+    Y = X @ W_hat.T
+    if B_bits is not None and A_bits is not None and np.asarray(A_bits).size:
+        Y = Y + (X @ bf16_to_f64(A_bits).T) @ bf16_to_f64(B_bits).T
+    return Y
 
 
 # --------------------------------------------------------------------------
