@@ -131,8 +131,60 @@ int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
 
 /* Which path a call with these parameters takes: 0 = fused single pass over
  * W (statistics kernel + one fused quantize/MFMA kernel), 1 = two phase
- * (statistics, quantize pass writing W_hat, MFMA GEMM).  Negative = status. */
+ * (statistics, quantize pass writing W_hat, MFMA GEMM), 2 = single launch
+ * for one token (T = 1, d <= 12288, no path flag).  Negative = status. */
 int ttq_path(const ttq_params* prm, int64_t n_requests);
+
+/* ---- quantize once per prompt, decode from the stored codes -------------
+ * The statistics can be taken once per input prompt ("TTQ: Activation-Aware
+ * Test-Time Quantization ...", nl summary, Sec. 2; zh summary, Sec. 3-4:
+ * the speed-up comes from contracting stored low-bit weights, because
+ * moving weights is the bottleneck).  ttq_quantize computes D from the
+ * prompt's X and stores the codes, the per-group (s, min) and D^{-1/2};
+ * ttq_qmatmul then computes, for the activations X of a later step,
+ *   Y = X ((min + s q) D^{-1/2})^T + (X A^T) B^T
+ * with those stored values (nothing is recomputed from the step's X).
+ *
+ * Code storage: each b-bit code takes the smallest container c of 1, 2, 4
+ * or 8 bits that holds it; channel j of a row sits at bit (j*c) % 8 of byte
+ * (j*c) / 8 of that row (least significant bits first).  A row takes
+ * ttq_packed_row_bytes = d*c/8 bytes; d*c must be a multiple of 128 bits
+ * (always true for the supported group sizes when c >= 4; checked). */
+
+/* Bytes of one row of packed codes for these parameters (writes *bytes). */
+int ttq_packed_row_bytes(const ttq_params* prm, int64_t* bytes);
+
+/* Device workspace for ttq_quantize / ttq_qmatmul (writes *bytes). */
+int ttq_quantize_workspace_bytes(const ttq_params* prm, size_t* bytes);
+int ttq_qmatmul_workspace_bytes(const ttq_params* prm, size_t* bytes);
+
+/* Quantize W for the prompt X ([T][d] bf16, T = prm->T >= 0; T = 0 gives
+ * D from zero statistics, as in ttq_linear).
+ *   codes       [d_out][row_bytes] packed codes, 16-byte aligned, required
+ *   scales      [d_out][d/group] float32 s, required
+ *   mins        [d_out][d/group] float32 group minima, required
+ *   dhalf_inv   [d] float32 D^{-1/2} = float32(1 / D^{1/2}), required
+ *   dhalf_out   optional [d] float32 D^{1/2} as fed to the code decision
+ * rank and the path flags are not read (the low-rank factors are used as
+ * given by ttq_qmatmul); unknown flag bits are still TTQ_EINVAL.  Same
+ * validation, alignment and error rules as ttq_linear otherwise. */
+int ttq_quantize(const ttq_params* prm, const void* W, const void* X,
+                 uint8_t* codes, float* scales, float* mins, float* dhalf_inv,
+                 float* dhalf_out, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Y [T][d_out] float32 for the step activations X ([T][d] bf16, T =
+ * prm->T) from the stored codes, scales, mins and dhalf_inv of ttq_quantize
+ * (same d, d_out, bits, group).  B, A as in ttq_linear (rank = prm->rank).
+ * codes 16-byte aligned, dhalf_inv 16-byte aligned, the rest as in
+ * ttq_linear.  p, lambda, alpha and TTQ_FLAG_FORCE_FUSED are not used;
+ * TTQ_FLAG_FORCE_TWO_PHASE takes the dequantize + GEMM route also for
+ * T = 1 (otherwise taken for T > 1, or where x D^{-1/2} of one token does
+ * not fit 128 KiB of LDS: d above about 30000). */
+int ttq_qmatmul(const ttq_params* prm, const uint8_t* codes,
+                const float* scales, const float* mins, const float* dhalf_inv,
+                const void* X, const void* B, const void* A, float* Y,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* ttq_status_string(int status);

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     TTQ_FLAG_FORCE_TWO_PHASE,
     TTQ_OK,
     TTQError,
+    container_bits,
     load_library,
     make_params,
     timing_enable,
@@ -26,7 +27,12 @@ from ._binding import (  # noqa: F401
     ttq_linear,
     ttq_linear_batched,
     ttq_params,
+    ttq_packed_row_bytes,
     ttq_path,
+    ttq_qmatmul,
+    ttq_qmatmul_workspace_bytes,
+    ttq_quantize,
+    ttq_quantize_workspace_bytes,
     ttq_status_string,
     ttq_version,
     ttq_workspace_bytes,

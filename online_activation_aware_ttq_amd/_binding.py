@@ -36,6 +36,13 @@ EXPORTS = {
                                       _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
                                       _vp]),
     "ttq_path": (_c.c_int, [_vp, _c.c_int64]),
+    "ttq_packed_row_bytes": (_c.c_int, [_vp, _c.POINTER(_c.c_int64)]),
+    "ttq_quantize_workspace_bytes": (_c.c_int, [_vp, _c.POINTER(_c.c_size_t)]),
+    "ttq_qmatmul_workspace_bytes": (_c.c_int, [_vp, _c.POINTER(_c.c_size_t)]),
+    "ttq_quantize": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _c.c_size_t, _vp]),
+    "ttq_qmatmul": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _c.c_size_t, _vp]),
     "ttq_status_string": (_c.c_char_p, [_c.c_int]),
     "ttq_last_hip_error": (_c.c_int, []),
     "ttq_version": (_c.c_char_p, []),
@@ -219,6 +226,128 @@ def ttq_linear_batched(W, X, B=None, A=None, *, p: float, lam: float,
                  group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
                  mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
                  stream=stream, flags=flags)
+
+
+# ------------------------------------------- quantize once, decode from codes
+def container_bits(bits: int) -> int:
+    """Bits each stored code takes (1, 2, 4 or 8)."""
+    return 1 if bits <= 1 else 2 if bits <= 2 else 4 if bits <= 4 else 8
+
+
+def ttq_packed_row_bytes(prm: ttq_params) -> int:
+    out = ctypes.c_int64(0)
+    st = load_library().ttq_packed_row_bytes(ctypes.byref(prm), ctypes.byref(out))
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_packed_row_bytes")
+    return int(out.value)
+
+
+def ttq_quantize_workspace_bytes(prm: ttq_params) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().ttq_quantize_workspace_bytes(ctypes.byref(prm),
+                                                     ctypes.byref(out))
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_quantize_workspace_bytes")
+    return int(out.value)
+
+
+def ttq_qmatmul_workspace_bytes(prm: ttq_params) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().ttq_qmatmul_workspace_bytes(ctypes.byref(prm),
+                                                    ctypes.byref(out))
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_qmatmul_workspace_bytes")
+    return int(out.value)
+
+
+def ttq_quantize(W, X, *, p: float, lam: float, alpha: float, bits: int,
+                 group: int, codes=None, scales=None, mins=None,
+                 dhalf_inv=None, dhalf_out=None, workspace=None, stream=None):
+    """Quantize W once for the prompt X (see include/ttq.h).
+
+    Returns (codes [d_out, row_bytes] uint8, scales [d_out, G] float32,
+    mins [d_out, G] float32, dhalf_inv [d] float32).
+    """
+    import torch
+    lib = load_library()
+    T, d = X.shape
+    d_out = W.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("W must be a GPU tensor")
+    prm = make_params(d=d, d_out=d_out, T=T, bits=bits, group=group, p=p,
+                      lam=lam, alpha=alpha)
+    rb = ttq_packed_row_bytes(prm)
+    need = ttq_quantize_workspace_bytes(prm)
+    G = d // group
+    _check(W, "W", torch.bfloat16, (d_out, d), dev)
+    _check(X, "X", torch.bfloat16, (T, d), dev)
+    if codes is None:
+        codes = torch.empty((d_out, rb), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((d_out, G), dtype=torch.float32, device=dev)
+    if mins is None:
+        mins = torch.empty((d_out, G), dtype=torch.float32, device=dev)
+    if dhalf_inv is None:
+        dhalf_inv = torch.empty((d,), dtype=torch.float32, device=dev)
+    _check(codes, "codes", torch.uint8, (d_out, rb), dev)
+    _check(scales, "scales", torch.float32, (d_out, G), dev)
+    _check(mins, "mins", torch.float32, (d_out, G), dev)
+    _check(dhalf_inv, "dhalf_inv", torch.float32, (d,), dev)
+    _check(dhalf_out, "dhalf_out", torch.float32, (d,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.ttq_quantize(ctypes.byref(prm), _ptr(W), _ptr(X), _ptr(codes),
+                          _ptr(scales), _ptr(mins), _ptr(dhalf_inv),
+                          _ptr(dhalf_out), _ptr(workspace), workspace.numel(),
+                          stream)
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_quantize")
+    return codes, scales, mins, dhalf_inv
+
+
+def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
+                bits: int, group: int, Y=None, workspace=None, stream=None,
+                flags: int = 0):
+    """Y[T, d_out] = X ((min + s q) D^{-1/2})^T + (X A^T) B^T from the codes
+    stored by ttq_quantize (see include/ttq.h)."""
+    import torch
+    lib = load_library()
+    T, d = X.shape
+    d_out = codes.shape[0]
+    rank = 0 if A is None else A.shape[0]
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("X must be a GPU tensor")
+    if (A is None) != (B is None):
+        raise ValueError("pass both B and A or neither")
+    prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
+                      group=group, p=1.0, lam=0.0, alpha=0.0, flags=flags)
+    rb = ttq_packed_row_bytes(prm)
+    need = ttq_qmatmul_workspace_bytes(prm)
+    G = d // group
+    _check(codes, "codes", torch.uint8, (d_out, rb), dev)
+    _check(scales, "scales", torch.float32, (d_out, G), dev)
+    _check(mins, "mins", torch.float32, (d_out, G), dev)
+    _check(dhalf_inv, "dhalf_inv", torch.float32, (d,), dev)
+    _check(X, "X", torch.bfloat16, (T, d), dev)
+    _check(B, "B", torch.bfloat16, (d_out, rank), dev)
+    _check(A, "A", torch.bfloat16, (rank, d), dev)
+    if Y is None:
+        Y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
+    _check(Y, "Y", torch.float32, (T, d_out), dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.ttq_qmatmul(ctypes.byref(prm), _ptr(codes), _ptr(scales),
+                         _ptr(mins), _ptr(dhalf_inv), _ptr(X), _ptr(B), _ptr(A),
+                         _ptr(Y), _ptr(workspace), workspace.numel(), stream)
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_qmatmul")
+    return Y
 
 
 # ------------------------------------------------------------------ timing

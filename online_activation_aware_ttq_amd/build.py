@@ -31,6 +31,7 @@ SOURCES = [
     "k_gemm_lds.hip",
     "k_lowrank.hip",
     "k_gemv.hip",
+    "k_qgemv.hip",
     "ttq_api.cpp",
 ]
 

@@ -6,8 +6,9 @@
 // summary, Sec. 2.1), which the MFMA GEMM then contracts with the raw bf16
 // activations.  The codes are decided by the same float32 sequence as the
 // fused path (for R requests at once, each with its own statistics and its
-// own W_hat).  A wave covers 512 consecutive channels of 8 weight rows: each
-// lane loads 16 bytes per row, a group of g channels lives in g/8 adjacent
+// own W_hat).  For quantize-once use it writes the packed codes instead of
+// W_hat.  A wave covers 512 consecutive channels of 8 weight rows: each lane
+// loads 16 bytes per row, a group of g channels lives in g/8 adjacent
 // lanes and is reduced with xor-shuffles inside that lane group.
 #include "ttq_internal.h"
 
@@ -15,7 +16,10 @@ namespace ttq {
 
 constexpr int QROWS = 8;  // weight rows per wave (D^{+-1/2} reused across them)
 
-template <int GS>
+// CB = 0: write W_hat (and optional byte codes, scales, minima);
+// CB = 1, 2, 4, 8: write the codes packed in CB-bit containers instead of
+// W_hat (channel j of a row at bit (j*CB) % 8 of byte (j*CB) / 8).
+template <int GS, int CB>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   constexpr int LPG = GS / 8;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -93,6 +97,32 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
       q[j] = __builtin_amdgcn_fmed3f(__builtin_rintf((u[j] - mn) * inv), 0.f,
                                      Nf);
     if (!live || row >= a.d_out) continue;
+    if (CB > 0) {
+      // 8 codes of this lane -> 8*CB bits, one aligned store
+      uint8_t* dst = a.packed + (int64_t)r * a.d_out * a.row_bytes +
+                     row * a.row_bytes + c0 * CB / 8;
+      if (CB == 8) {
+        u32x2 c;
+        c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
+              ((unsigned)q[3] << 24);
+        c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
+              ((unsigned)q[7] << 24);
+        *(u32x2*)dst = c;
+      } else {
+        unsigned c = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c |= (unsigned)q[j] << (j * CB);
+        if (CB == 4) *(unsigned*)dst = c;
+        else if (CB == 2) *(uint16_t*)dst = (uint16_t)c;
+        else *dst = (uint8_t)c;
+      }
+      if (s_out && (l % LPG) == 0) {
+        const int64_t o2 = row * a.G + c0 / GS;
+        s_out[o2] = s;
+        m_out[o2] = mn;
+      }
+      continue;
+    }
     u32x4 o;
     o.x = pack_bf16(fmaf(s, q[0], mn) * dhi[0], fmaf(s, q[1], mn) * dhi[1]);
     o.y = pack_bf16(fmaf(s, q[2], mn) * dhi[2], fmaf(s, q[3], mn) * dhi[3]);
@@ -121,13 +151,24 @@ hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L) {
   const int64_t nblk1 = (waves + 3) / 4;
   if (nblk1 == 0 || a.R == 0) return hipSuccess;
   const dim3 grid((unsigned)(((nblk1 + 7) / 8) * 8 * a.R)), blk(256);
+#define TTQ_QUANT_CB(GSV)                                                   \
+  case GSV:                                                                 \
+    switch (a.packed ? a.cb : 0) {                                          \
+      case 0: return ext_launch(k_quant<GSV, 0>, grid, blk, 0, L, a);       \
+      case 1: return ext_launch(k_quant<GSV, 1>, grid, blk, 0, L, a);       \
+      case 2: return ext_launch(k_quant<GSV, 2>, grid, blk, 0, L, a);       \
+      case 4: return ext_launch(k_quant<GSV, 4>, grid, blk, 0, L, a);       \
+      case 8: return ext_launch(k_quant<GSV, 8>, grid, blk, 0, L, a);       \
+      default: return hipErrorInvalidValue;                                 \
+    }
   switch (group) {
-    case 32: return ext_launch(k_quant<32>, grid, blk, 0, L, a);
-    case 64: return ext_launch(k_quant<64>, grid, blk, 0, L, a);
-    case 128: return ext_launch(k_quant<128>, grid, blk, 0, L, a);
-    case 256: return ext_launch(k_quant<256>, grid, blk, 0, L, a);
+    TTQ_QUANT_CB(32)
+    TTQ_QUANT_CB(64)
+    TTQ_QUANT_CB(128)
+    TTQ_QUANT_CB(256)
     default: return hipErrorInvalidValue;
   }
+#undef TTQ_QUANT_CB
 }
 
 }  // namespace ttq

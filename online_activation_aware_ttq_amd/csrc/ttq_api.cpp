@@ -80,6 +80,34 @@ int validate_params(const ttq_params* prm, int64_t R) {
   return TTQ_OK;
 }
 
+// Token slices for the norm partials of the large-T statistics: enough
+// workgroups to fill the chip (about 2048 waves), at least 8 tokens a slice.
+template <class Take>
+void plan_stats_split(Plan& P, int64_t R, int64_t T, int64_t d, Take& take) {
+  const int64_t cchunks = (d + 511) / 512;
+  int64_t target = 2048 / (cchunks * R);
+  if (target < 1) target = 1;
+  int64_t tch = (T + target - 1) / target;
+  if (tch < 8) tch = 8;
+  P.tchunk = (int)tch;
+  P.nsplit = (int)((T + P.tchunk - 1) / P.tchunk);
+  P.off_statp = take(sizeof(double) * R * ((P.nsplit + 3) / 4) * d);
+}
+
+// Z = X A^T has few output tiles (rank columns): split the channels so that
+// about 512 workgroups run, each over at least 256 channels.
+template <class Take>
+void plan_z_split(Plan& P, int64_t M, int64_t d, Take& take) {
+  const int64_t tiles = ((M + 127) / 128) * ((P.rp + 127) / 128);
+  const int64_t nk = (d + 63) / 64;
+  int64_t S = (512 + tiles - 1) / tiles;
+  if (S > nk / 4) S = nk / 4;
+  if (S < 1) S = 1;
+  P.zksplit = (nk + S - 1) / S * 64;
+  P.zsplit = (int)((d + P.zksplit - 1) / P.zksplit);
+  if (P.zsplit > 1) P.off_zpart = take(sizeof(float) * P.zsplit * M * P.rp);
+}
+
 Plan make_plan(const ttq_params* prm, int64_t R) {
   Plan P;
   const int64_t d = prm->d, dout = prm->d_out, T = prm->T;
@@ -114,35 +142,14 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
     P.off_zeros = take(kZeroBytes);
   } else {
-    // token slices for the norm partials: enough workgroups to fill the chip
-    // (about 2048 waves), at least 8 tokens per slice
-    const int64_t cchunks = (d + 511) / 512;
-    int64_t target = 2048 / (cchunks * R);
-    if (target < 1) target = 1;
-    int64_t tch = (T + target - 1) / target;
-    if (tch < 8) tch = 8;
-    P.tchunk = (int)tch;
-    P.nsplit = (int)((T + P.tchunk - 1) / P.tchunk);
-    P.off_statp = take(sizeof(double) * R * ((P.nsplit + 3) / 4) * d);
+    plan_stats_split(P, R, T, d, take);
     // W_hat of up to rchunk requests at a time (at most kMaxWhatBytes)
     const int64_t per = (int64_t)sizeof(uint16_t) * dout * d;
     P.rchunk = per > 0 ? kMaxWhatBytes / per : R;
     if (P.rchunk < 1) P.rchunk = 1;
     if (P.rchunk > R) P.rchunk = R;
     P.off_what = take((size_t)(per * P.rchunk));
-    if (P.rp > 0 && T > 0) {
-      // Z has few output tiles (rank columns): split the channels so that
-      // about 512 workgroups run, each over at least 256 channels
-      const int64_t tiles = ((R * T + 127) / 128) * ((P.rp + 127) / 128);
-      const int64_t nk = (d + 63) / 64;
-      int64_t S = (512 + tiles - 1) / tiles;
-      if (S > nk / 4) S = nk / 4;
-      if (S < 1) S = 1;
-      P.zksplit = (nk + S - 1) / S * 64;
-      P.zsplit = (int)((d + P.zksplit - 1) / P.zksplit);
-      if (P.zsplit > 1)
-        P.off_zpart = take(sizeof(float) * P.zsplit * R * T * P.rp);
-    }
+    if (P.rp > 0 && T > 0) plan_z_split(P, R * T, d, take);
   }
   P.total = off;
   return P;
@@ -164,7 +171,8 @@ TimingState g_timing;
 
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
-    "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce"};
+    "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
+    "qgemv", "dequant"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -202,6 +210,40 @@ int run(KernelKind kind, hipStream_t s, F&& launch) {
   return TTQ_OK;
 }
 
+// Failure injection for the error-path tests: with TTQ_INJECT_HIP_ERROR=1 a
+// call that passed validation reports a failed launch and enqueues nothing.
+bool inject_hip_error() {
+  const char* inj = std::getenv("TTQ_INJECT_HIP_ERROR");
+  if (inj && inj[0] == '1') {
+    g_last_hip_error = (int)hipErrorLaunchFailure;
+    return true;
+  }
+  return false;
+}
+
+// Z = X A^T (M rows) with the MFMA GEMM, split over the channels as planned
+// (fp32 partials summed in split order, then rounded to bf16).
+int enqueue_z_gemm(const Plan& P, char* ws, const bf16_t* Xb,
+                   const bf16_t* Ab, int64_t M, int64_t d, int64_t rank,
+                   bf16_t* Zb, hipStream_t s) {
+  GemmArgs za{};
+  za.A1 = Xb; za.lda1 = d; za.B1 = Ab; za.ldb1 = d; za.K1 = d;
+  za.M = M; za.N = rank; za.N_store = P.rp;
+  za.ldc = P.rp;
+  if (P.zsplit > 1) {
+    za.C = reinterpret_cast<float*>(ws + P.off_zpart);
+    za.ksplit = P.zksplit;
+    za.nsplit = P.zsplit;
+    za.split_stride = M * P.rp;
+  } else {
+    za.Cb = Zb;
+  }
+  int st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_gemm(za, L); });
+  if (st != TTQ_OK || P.zsplit <= 1) return st;
+  SplitReduceArgs ra{za.C, P.zsplit, M * P.rp, Zb};
+  return run(K_SPLITK_REDUCE, s, [&](const Launch& L) { return launch_splitk_reduce(ra, L); });
+}
+
 int linear_impl(const ttq_params* prm, int64_t R, const void* W,
                 const void* X, const void* B, const void* A, float* Y,
                 uint8_t* codes_out, float* scales_out, float* mins_out,
@@ -224,13 +266,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
   const Plan P = make_plan(prm, R);
   if (P.total > 0 && !workspace) return TTQ_ENULL;
   if (workspace_bytes < P.total) return TTQ_EWORKSPACE;
-  {
-    const char* inj = std::getenv("TTQ_INJECT_HIP_ERROR");
-    if (inj && inj[0] == '1') {
-      g_last_hip_error = (int)hipErrorLaunchFailure;
-      return TTQ_EHIP;
-    }
-  }
+  if (inject_hip_error()) return TTQ_EHIP;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -311,25 +347,8 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
   if (st != TTQ_OK) return st;
   if (!need_quant) return TTQ_OK;
   if (P.rp > 0) {
-    GemmArgs za{};
-    za.A1 = Xb; za.lda1 = d; za.B1 = Ab; za.ldb1 = d; za.K1 = d;
-    za.M = R * T; za.N = rank; za.N_store = P.rp;
-    za.ldc = P.rp;
-    if (P.zsplit > 1) {
-      za.C = reinterpret_cast<float*>(ws + P.off_zpart);
-      za.ksplit = P.zksplit;
-      za.nsplit = P.zsplit;
-      za.split_stride = R * T * P.rp;
-    } else {
-      za.Cb = Zb;
-    }
-    st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_gemm(za, L); });
+    st = enqueue_z_gemm(P, ws, Xb, Ab, R * T, d, rank, Zb, s);
     if (st != TTQ_OK) return st;
-    if (P.zsplit > 1) {
-      SplitReduceArgs ra{za.C, P.zsplit, R * T * P.rp, Zb};
-      st = run(K_SPLITK_REDUCE, s, [&](const Launch& L) { return launch_splitk_reduce(ra, L); });
-      if (st != TTQ_OK) return st;
-    }
   }
   // requests in chunks of P.rchunk: one quantize pass (each request its own
   // W_hat), then one batched GEMM launch per chunk
@@ -359,6 +378,207 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     if (st != TTQ_OK) return st;
   }
   return TTQ_OK;
+}
+
+
+// ------------------------------------------------- quantize once, decode
+int container_bits(int bits) {
+  return bits <= 1 ? 1 : (bits <= 2 ? 2 : (bits <= 4 ? 4 : 8));
+}
+
+int packed_row_bytes(const ttq_params* prm, int64_t* rb) {
+  const int64_t rbits = prm->d * container_bits(prm->bits);
+  if (rbits % 128 != 0) return TTQ_EUNSUPPORTED;
+  *rb = rbits / 8;
+  return TTQ_OK;
+}
+
+// ttq_quantize reads neither rank nor the path flags
+ttq_params quantize_view(const ttq_params* prm) {
+  ttq_params q = *prm;
+  q.rank = 0;
+  q.flags = 0;
+  return q;
+}
+
+// ttq_qmatmul reads neither the statistics constants nor FORCE_FUSED
+ttq_params qmatmul_view(const ttq_params* prm) {
+  ttq_params q = *prm;
+  q.p = 1.0;
+  q.lambda = 0.0;
+  q.alpha = 0.0;
+  q.flags &= TTQ_FLAG_FORCE_TWO_PHASE;
+  return q;
+}
+
+int validate_packed(const ttq_params* prm, const ttq_params& q, int64_t* rb) {
+  if (!prm) return TTQ_ENULL;
+  if (prm->flags & ~known_flags()) return TTQ_EINVAL;
+  const int st = validate_params(&q, 1);
+  if (st != TTQ_OK) return st;
+  return packed_row_bytes(&q, rb);
+}
+
+// path 0: one statistics kernel (T <= 128); 1: partials + final
+Plan make_quantize_plan(const ttq_params& q) {
+  Plan P;
+  P.G = (int)(q.d / q.group);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  P.off_dh = take(sizeof(float) * q.d);
+  P.path = q.T <= kFusedMaxT ? 0 : 1;
+  if (P.path == 1) plan_stats_split(P, 1, q.T, q.d, take);
+  P.total = off;
+  return P;
+}
+
+// path 2: one-token contraction of the codes; 1: dequantize + MFMA GEMM
+Plan make_qmatmul_plan(const ttq_params& q, int cb) {
+  Plan P;
+  const int64_t d = q.d, T = q.T;
+  P.G = (int)(d / q.group);
+  P.rp = q.rank > 0 ? (q.rank + 31) / 32 * 32 : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  if (P.rp > 0) P.off_z = take(sizeof(uint16_t) * T * P.rp);
+  const bool fits = qgemv_lds_bytes(d, cb, q.group) <= kGemvLdsMax;
+  P.path = (T == 1 && fits && !(q.flags & TTQ_FLAG_FORCE_TWO_PHASE)) ? 2 : 1;
+  if (P.path == 1 && T > 0 && q.d_out > 0) {
+    P.off_what = take(sizeof(uint16_t) * q.d_out * d);
+    if (P.rp > 0) plan_z_split(P, T, d, take);
+  }
+  P.total = off;
+  return P;
+}
+
+int quantize_impl(const ttq_params* prm, const void* W, const void* X,
+                  uint8_t* codes, float* scales, float* mins, float* dhalf_inv,
+                  float* dhalf_out, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!prm) return TTQ_ENULL;
+  const ttq_params q = quantize_view(prm);
+  int64_t rb = 0;
+  int st = validate_packed(prm, q, &rb);
+  if (st != TTQ_OK) return st;
+  const int64_t d = q.d, dout = q.d_out, T = q.T;
+  if (dout > 0 && (!W || !codes || !scales || !mins)) return TTQ_ENULL;
+  if (T > 0 && !X) return TTQ_ENULL;
+  if (!dhalf_inv) return TTQ_ENULL;
+  if (misaligned(W, 16) || misaligned(X, 16) || misaligned(codes, 16) ||
+      misaligned(scales, 4) || misaligned(mins, 4) ||
+      misaligned(dhalf_inv, 16) || misaligned(dhalf_out, 4) ||
+      misaligned(workspace, 256))
+    return TTQ_EALIGN;
+  const Plan P = make_quantize_plan(q);
+  if (P.total > 0 && !workspace) return TTQ_ENULL;
+  if (workspace_bytes < P.total) return TTQ_EWORKSPACE;
+  if (inject_hip_error()) return TTQ_EHIP;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* dh = reinterpret_cast<float*>(ws + P.off_dh);
+  const bf16_t* Xb = static_cast<const bf16_t*>(X);
+  const int pmode = q.p == 2.0 ? 2 : (q.p == 1.0 ? 1 : 0);
+  if (P.path == 0) {
+    StatsSmallArgs sa{};
+    sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = pmode;
+    sa.p = q.p; sa.lam = q.lambda; sa.alpha = q.alpha;
+    sa.dh = dh; sa.dhi = dhalf_inv; sa.dh_export = dhalf_out; sa.group = q.group;
+    st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
+  } else {
+    StatsSplitArgs ta{};
+    ta.X = Xb; ta.T = T; ta.d = d; ta.pmode = pmode;
+    ta.p = q.p; ta.lam = q.lambda; ta.alpha = q.alpha;
+    ta.tchunk = P.tchunk; ta.nsplit = P.nsplit;
+    ta.partial = reinterpret_cast<double*>(ws + P.off_statp);
+    ta.dh = dh; ta.dhi = dhalf_inv; ta.dh_export = dhalf_out;
+    st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_partial(ta, 1, L); });
+    if (st == TTQ_OK)
+      st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(ta, 1, L); });
+  }
+  if (st != TTQ_OK || dout == 0) return st;
+  QuantArgs qa{};
+  qa.W = static_cast<const bf16_t*>(W); qa.d = d; qa.d_out = dout; qa.G = P.G;
+  qa.R = 1; qa.Nf = (float)((1 << q.bits) - 1);
+  qa.dh = dh; qa.dhi = dhalf_inv;
+  qa.s_out = scales; qa.m_out = mins;
+  qa.packed = codes; qa.cb = container_bits(q.bits); qa.row_bytes = rb;
+  return run(K_QUANT, s, [&](const Launch& L) { return launch_quant(qa, q.group, L); });
+}
+
+int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
+                 const float* scales, const float* mins,
+                 const float* dhalf_inv, const void* X, const void* B,
+                 const void* A, float* Y, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!prm) return TTQ_ENULL;
+  const ttq_params q = qmatmul_view(prm);
+  int64_t rb = 0;
+  int st = validate_packed(prm, q, &rb);
+  if (st != TTQ_OK) return st;
+  const int64_t d = q.d, dout = q.d_out, T = q.T, rank = q.rank;
+  const int cb = container_bits(q.bits);
+  if (dout > 0 && (!codes || !scales || !mins)) return TTQ_ENULL;
+  if (!dhalf_inv) return TTQ_ENULL;
+  if (T > 0 && !X) return TTQ_ENULL;
+  if (T > 0 && dout > 0 && !Y) return TTQ_ENULL;
+  if (rank > 0 && (!B || !A)) return TTQ_ENULL;
+  if (misaligned(codes, 16) || misaligned(scales, 4) || misaligned(mins, 4) ||
+      misaligned(dhalf_inv, 16) || misaligned(X, 16) || misaligned(B, 16) ||
+      misaligned(A, 16) || misaligned(Y, 4) || misaligned(workspace, 256))
+    return TTQ_EALIGN;
+  const Plan P = make_qmatmul_plan(q, cb);
+  if (P.total > 0 && !workspace) return TTQ_ENULL;
+  if (workspace_bytes < P.total) return TTQ_EWORKSPACE;
+  if (inject_hip_error()) return TTQ_EHIP;
+  if (T == 0 || dout == 0) return TTQ_OK;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  bf16_t* Zb = P.rp > 0 ? reinterpret_cast<bf16_t*>(ws + P.off_z) : nullptr;
+  const bf16_t* Xb = static_cast<const bf16_t*>(X);
+  const bf16_t* Bb = static_cast<const bf16_t*>(B);
+  const bf16_t* Ab = static_cast<const bf16_t*>(A);
+  if (P.path == 2) {
+    if (P.rp > 0) {
+      LowRankZArgs za{Xb, Ab, 1, d, (int)rank, (int)P.rp, Zb};
+      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      if (st != TTQ_OK) return st;
+    }
+    QGemvArgs ga{};
+    ga.packed = codes; ga.row_bytes = rb; ga.s = scales; ga.m = mins;
+    ga.dhi = dhalf_inv; ga.X = Xb; ga.d = d; ga.d_out = dout; ga.G = P.G;
+    ga.Z = Zb; ga.Blr = Bb; ga.rank = (int)rank; ga.Y = Y;
+    return run(K_QGEMV, s, [&](const Launch& L) { return launch_qgemv(ga, q.group, cb, L); });
+  }
+  bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
+  DequantArgs da{};
+  da.packed = codes; da.row_bytes = rb; da.s = scales; da.m = mins;
+  da.dhi = dhalf_inv; da.d = d; da.d_out = dout; da.G = P.G; da.What = What;
+  st = run(K_DEQUANT, s, [&](const Launch& L) { return launch_dequant(da, q.group, cb, L); });
+  if (st != TTQ_OK) return st;
+  if (P.rp > 0) {
+    st = enqueue_z_gemm(P, ws, Xb, Ab, T, d, rank, Zb, s);
+    if (st != TTQ_OK) return st;
+  }
+  GemmArgs ga{};
+  ga.A1 = Xb; ga.lda1 = d; ga.B1 = What; ga.ldb1 = d; ga.K1 = d;
+  if (P.rp > 0) {
+    ga.A2 = Zb; ga.lda2 = P.rp;
+    ga.B2 = Bb; ga.ldb2 = rank; ga.K2 = rank;
+  }
+  ga.M = T; ga.N = dout; ga.N_store = dout;
+  ga.C = Y; ga.ldc = dout;
+  ga.batch = 1;
+  return run(K_GEMM, s, [&](const Launch& L) { return launch_gemm_lds(ga, L); });
 }
 
 }  // namespace
@@ -395,6 +615,48 @@ int ttq_path(const ttq_params* prm, int64_t n_requests) {
   const int st = validate_params(prm, n_requests);
   if (st != TTQ_OK) return st;
   return make_plan(prm, n_requests < 1 ? 1 : n_requests).path;
+}
+
+int ttq_packed_row_bytes(const ttq_params* prm, int64_t* bytes) {
+  if (!bytes || !prm) return TTQ_ENULL;
+  const ttq_params q = quantize_view(prm);
+  return validate_packed(prm, q, bytes);
+}
+
+int ttq_quantize_workspace_bytes(const ttq_params* prm, size_t* bytes) {
+  if (!bytes || !prm) return TTQ_ENULL;
+  const ttq_params q = quantize_view(prm);
+  int64_t rb = 0;
+  const int st = validate_packed(prm, q, &rb);
+  if (st != TTQ_OK) return st;
+  *bytes = make_quantize_plan(q).total;
+  return TTQ_OK;
+}
+
+int ttq_qmatmul_workspace_bytes(const ttq_params* prm, size_t* bytes) {
+  if (!bytes || !prm) return TTQ_ENULL;
+  const ttq_params q = qmatmul_view(prm);
+  int64_t rb = 0;
+  const int st = validate_packed(prm, q, &rb);
+  if (st != TTQ_OK) return st;
+  *bytes = make_qmatmul_plan(q, container_bits(q.bits)).total;
+  return TTQ_OK;
+}
+
+int ttq_quantize(const ttq_params* prm, const void* W, const void* X,
+                 uint8_t* codes, float* scales, float* mins, float* dhalf_inv,
+                 float* dhalf_out, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return quantize_impl(prm, W, X, codes, scales, mins, dhalf_inv, dhalf_out,
+                       workspace, workspace_bytes, stream);
+}
+
+int ttq_qmatmul(const ttq_params* prm, const uint8_t* codes,
+                const float* scales, const float* mins, const float* dhalf_inv,
+                const void* X, const void* B, const void* A, float* Y,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return qmatmul_impl(prm, codes, scales, mins, dhalf_inv, X, B, A, Y,
+                      workspace, workspace_bytes, stream);
 }
 
 const char* ttq_status_string(int status) {

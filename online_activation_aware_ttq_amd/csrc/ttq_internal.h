@@ -26,6 +26,8 @@ enum KernelKind {
   K_LOWRANK_Z,         // Z = X A^T (low-rank first factor)
   K_GEMV,              // single-launch path for one token (T = 1)
   K_SPLITK_REDUCE,     // split-K partial sums of Z -> bf16
+  K_QGEMV,             // stored packed codes x one token
+  K_DEQUANT,           // stored packed codes -> W_hat
   K_NUM_KINDS
 };
 
@@ -203,8 +205,46 @@ struct QuantArgs {
   uint8_t* codes_out;   // [R][d_out][d]
   float* s_out;         // [R][d_out][G]
   float* m_out;         // [R][d_out][G]
+  // packed-code output instead of W_hat (What unused when set)
+  uint8_t* packed;      // [R][d_out][row_bytes]
+  int cb;               // container bits 1, 2, 4, 8
+  int64_t row_bytes;    // d * cb / 8
 };
 hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L);
+
+// Contraction of later tokens with stored packed codes (one token):
+// y_i = sum_g s_ig * sum_{j in g} q_ij x'_j + m_ig * sum_{j in g} x'_j
+// + B_i . z, with x' = x D^{-1/2} from the stored D^{-1/2}.
+struct QGemvArgs {
+  const uint8_t* packed;  // [d_out][row_bytes]
+  int64_t row_bytes;
+  const float* s;         // [d_out][G]
+  const float* m;         // [d_out][G]
+  const float* dhi;       // [d]
+  const bf16_t* X;        // [d] (one token)
+  int64_t d, d_out;
+  int G;
+  const bf16_t* Z;        // [rp] or null
+  const bf16_t* Blr;      // [d_out][rank] or null
+  int rank;
+  float* Y;               // [d_out]
+};
+hipError_t launch_qgemv(const QGemvArgs& a, int group, int cb, const Launch& L);
+size_t qgemv_lds_bytes(int64_t d, int cb, int group);
+
+// Dequantize stored packed codes to W_hat = bf16((m + s q) D^{-1/2}).
+struct DequantArgs {
+  const uint8_t* packed;  // [d_out][row_bytes]
+  int64_t row_bytes;
+  const float* s;
+  const float* m;
+  const float* dhi;
+  int64_t d, d_out;
+  int G;
+  bf16_t* What;           // [d_out][d]
+};
+hipError_t launch_dequant(const DequantArgs& a, int group, int cb,
+                          const Launch& L);
 
 // C[M][N] (+)= A1[M][K1] B1[N][K1]^T + A2[M][K2] B2[N][K2]^T, fp32 accumulate.
 struct GemmArgs {

@@ -204,3 +204,111 @@ def test_timing_api_without_launches():
     ms = ctypes.c_double()
     cnt = ctypes.c_int64()
     assert L.ttq_timing_query(-1, ctypes.byref(ms), ctypes.byref(cnt)) == ttq.TTQ_EINVAL
+
+
+# ---------------------------------------------- quantize once / decode calls
+def call_quantize(p, W=FAKE, X=FAKE, codes=FAKE, scales=FAKE, mins=FAKE,
+                  dhi=FAKE, dh=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib().ttq_quantize(ctypes.byref(p) if p is not None else None, W, X,
+                              codes, scales, mins, dhi, dh, ws, ws_bytes, None)
+
+
+def call_qmatmul(p, codes=FAKE, scales=FAKE, mins=FAKE, dhi=FAKE, X=FAKE,
+                 Bm=None, A=None, Y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib().ttq_qmatmul(ctypes.byref(p) if p is not None else None,
+                             codes, scales, mins, dhi, X, Bm, A, Y, ws,
+                             ws_bytes, None)
+
+
+@pytest.mark.parametrize("bits,d,row_bytes", [
+    (4, 256, 128), (3, 256, 128), (8, 256, 256), (5, 4096, 4096),
+    (2, 256, 64), (1, 256, 32), (4, 4096, 2048), (2, 4096, 1024),
+])
+def test_packed_row_bytes(bits, d, row_bytes):
+    assert B.container_bits(bits) * d // 8 == row_bytes
+    assert ttq.ttq_packed_row_bytes(prm(bits=bits, d=d)) == row_bytes
+
+
+def test_packed_rows_must_fill_16_bytes():
+    # 1-bit codes of 64 channels are 8 bytes a row: not supported
+    p = prm(bits=1, d=64, group=32)
+    out = ctypes.c_int64(-7)
+    assert lib().ttq_packed_row_bytes(ctypes.byref(p), ctypes.byref(out)) == ttq.TTQ_EUNSUPPORTED
+    assert out.value == -7
+    assert call_quantize(p) == ttq.TTQ_EUNSUPPORTED
+    assert call_qmatmul(p) == ttq.TTQ_EUNSUPPORTED
+    # 2-bit codes of 64 channels are 16 bytes: fine
+    assert ttq.ttq_packed_row_bytes(prm(bits=2, d=64, group=32)) == 16
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=0), ttq.TTQ_EINVAL),
+    (dict(bits=9), ttq.TTQ_EINVAL),
+    (dict(d=0), ttq.TTQ_EINVAL),
+    (dict(d_out=-1), ttq.TTQ_EINVAL),
+    (dict(T=-1), ttq.TTQ_EINVAL),
+    (dict(d=256, group=96), ttq.TTQ_EINVAL),
+    (dict(d=256, group=16), ttq.TTQ_EUNSUPPORTED),
+])
+def test_packed_calls_validate_shapes(kw, status):
+    p = prm(**kw)
+    out = ctypes.c_size_t(7)
+    assert lib().ttq_quantize_workspace_bytes(ctypes.byref(p), ctypes.byref(out)) == status
+    assert lib().ttq_qmatmul_workspace_bytes(ctypes.byref(p), ctypes.byref(out)) == status
+    assert out.value == 7
+    assert call_quantize(p) == status
+    assert call_qmatmul(p) == status
+
+
+def test_quantize_checks_statistics_constants_only():
+    # statistics constants are validated by ttq_quantize ...
+    assert call_quantize(prm(p=0.0)) == ttq.TTQ_EINVAL
+    assert call_quantize(prm(alpha=-1.0)) == ttq.TTQ_EINVAL
+    # ... but rank and the path flags are not read (unknown flags still are)
+    assert ttq.ttq_quantize_workspace_bytes(prm(rank=12, flags=3)) > 0
+    assert call_quantize(prm(flags=4)) == ttq.TTQ_EINVAL
+    # ttq_qmatmul does not read the statistics constants or FORCE_FUSED
+    assert ttq.ttq_qmatmul_workspace_bytes(prm(p=0.0, alpha=-1.0, flags=1)) >= 0
+    assert call_qmatmul(prm(rank=12)) == ttq.TTQ_EUNSUPPORTED
+    assert call_qmatmul(prm(flags=4)) == ttq.TTQ_EINVAL
+
+
+def test_packed_calls_null_and_alignment():
+    p = prm()
+    assert call_quantize(None) == ttq.TTQ_ENULL
+    for k in ("W", "X", "codes", "scales", "mins", "dhi", "ws"):
+        assert call_quantize(p, **{k: None}) == ttq.TTQ_ENULL, k
+    for k, off in (("W", 8), ("X", 2), ("codes", 8), ("scales", 2),
+                   ("mins", 2), ("dhi", 4), ("dh", 2), ("ws", 128)):
+        assert call_quantize(p, **{k: FAKE + off}) == ttq.TTQ_EALIGN, k
+    assert call_qmatmul(None) == ttq.TTQ_ENULL
+    for k in ("codes", "scales", "mins", "dhi", "X", "Y"):
+        assert call_qmatmul(p, **{k: None}) == ttq.TTQ_ENULL, k
+    for k, off in (("codes", 8), ("scales", 2), ("mins", 2), ("dhi", 4),
+                   ("X", 2), ("Y", 2), ("ws", 128)):
+        assert call_qmatmul(p, **{k: FAKE + off}) == ttq.TTQ_EALIGN, k
+    pr = prm(rank=8)
+    assert call_qmatmul(pr) == ttq.TTQ_ENULL
+    assert call_qmatmul(pr, Bm=FAKE, A=None) == ttq.TTQ_ENULL
+    assert call_qmatmul(pr, Bm=FAKE + 8, A=FAKE) == ttq.TTQ_EALIGN
+
+
+def test_packed_calls_workspace():
+    p = prm(T=1, rank=8)
+    need = ttq.ttq_qmatmul_workspace_bytes(p)
+    assert need > 0
+    assert call_qmatmul(p, Bm=FAKE, A=FAKE, ws_bytes=need - 1) == ttq.TTQ_EWORKSPACE
+    # the dequantize route of T > 1 holds the bf16 weights
+    big = ttq.ttq_qmatmul_workspace_bytes(prm(T=64))
+    assert big >= 64 * 256 * 2
+    assert ttq.ttq_qmatmul_workspace_bytes(prm(T=1)) == 0
+    q = prm(T=2048)
+    qneed = ttq.ttq_quantize_workspace_bytes(q)
+    assert qneed >= 256 * 4
+    assert call_quantize(q, ws_bytes=qneed - 1) == ttq.TTQ_EWORKSPACE
+
+
+def test_packed_calls_report_injected_hip_error(monkeypatch):
+    monkeypatch.setenv("TTQ_INJECT_HIP_ERROR", "1")
+    assert call_quantize(prm()) == ttq.TTQ_EHIP
+    assert call_qmatmul(prm()) == ttq.TTQ_EHIP
