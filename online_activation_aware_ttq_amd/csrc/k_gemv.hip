@@ -22,10 +22,14 @@
 // a group's statistics live in lanes {l, l^16, l^32, l^48}.  Each of the 16
 // waves owns a contiguous run of groups (contiguous weight bytes per row),
 // derives the statistics of its own channels while its first weights are in
-// flight, and walks its groups with two weight register sets (one group in
-// flight while the other is processed).  Weights are read with bounded
-// buffer loads: prefetches past the last group return zeros without memory
-// traffic, so the ring needs no branches.
+// flight, and then requests each next group as soon as the current one has
+// been processed.  The whole matrix is in flight across the chip either way;
+// measured on MI355X, a second group in flight per wave (requested before
+// the current one is processed, or before the statistics) makes the call
+// slower, not faster.  The statistics and every weight request run at raised
+// wave priority, so requests are not held behind other waves' arithmetic.
+// Weights are read with bounded buffer loads: a request past the last group
+// returns zeros without memory traffic, so the loop needs no branches.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -61,10 +65,6 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     GemvArgs a) {
   constexpr int VW = gemv_waves<GS, EXPORT>();
   constexpr int NKS = GS / 32;
-  // weight register sets in the ring: one group in flight while one is
-  // processed (measured on MI355X: requesting a wave's next groups up front,
-  // all at once, is slower than issuing each when the previous one starts)
-  constexpr int NR = 2;
   extern __shared__ __attribute__((aligned(16))) float lds[];
   // LDS: dh[d] | xp[d] | sxp[G] | red[VW][16]
   const int64_t d = a.d;
@@ -81,6 +81,8 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
   const int req = (int)(jb % a.R);
   if (rb >= a.rowblocks) return;
 
+  // the statistics prologue and the weight requests go first (see above)
+  __builtin_amdgcn_s_setprio(2);
   const int tid = threadIdx.x, l = tid & 63;
   // wave index as a scalar: the group loop below is then wave-uniform control
   // flow (a per-lane counter would make every loop exit a divergent branch)
@@ -128,10 +130,9 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     xv[p] = *(const u32x2*)(x + (c < c_end ? c : 0));
   }
   __builtin_amdgcn_sched_barrier(0);
-  u32x4 ring[NR][NKS];
+  u32x4 wv[NKS];
   int g = g_begin;
-#pragma unroll
-  for (int r = 0; r + 1 < NR; ++r) load_w(ring[r], g + r < g_end ? g + r : G);
+  load_w(wv, g < g_end ? g : G);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int lpg4 = GS / 4;  // lanes per group
 #pragma unroll
@@ -230,18 +231,16 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     if (qd == 0) acc = fmaf(mn, sx_s[gg], acc);
   };
 
-  // ring of NR weight register sets: NR - 1 groups in flight while one is
-  // processed (indices are compile-time after unrolling)
+  // one group at a time: process it, then request the next one (past the
+  // run: an empty request) at raised priority
+  __builtin_amdgcn_s_setprio(0);
   while (g < g_end) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int gn = g + NR - 1;
-      load_w(ring[(r + NR - 1) % NR], gn < g_end ? gn : G);
-      __builtin_amdgcn_sched_barrier(0);
-      process(ring[r], g);
-      g += 1;
-      if (g >= g_end) break;
-    }
+    process(wv, g);
+    g += 1;
+    __builtin_amdgcn_s_setprio(2);
+    load_w(wv, g < g_end ? g : G);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // static low-rank term: + B[row, :] . z, z = A x precomputed
