@@ -106,6 +106,25 @@ def test_batched_requests(T, flags):
     assert not np.array_equal(gpu["dh"][0], gpu["dh"][1])
 
 
+@pytest.mark.parametrize("R", [1, 3])
+def test_gemm_more_tiles_than_cus(R):
+    """Large-tile GEMM with more output tiles than the chip has CUs (a second,
+    partly filled round): R = 1, 9 x 32 tiles of 256 x 128 = 288; R = 3, the
+    same tile count over three requests' products, each with its own W_hat;
+    the low-rank segment is part of every tile's K range."""
+    T = 2304 if R == 1 else 768
+    prob = make_problem(f"tail_R{R}", d=1024, d_out=4096, T=T, R=R, bits=4,
+                        group=128, rank=32, x_kind="logu10_100", n_outliers=10,
+                        seed=60 + R)
+    rows = np.unique(np.concatenate([
+        np.arange(16), np.arange(3072, 3100), np.arange(4096 - 16, 4096),
+        np.random.default_rng(R).choice(4096, 32, replace=False)]))
+    print(f"[case] two GEMM rounds R={R} T={T} rows={len(rows)}", flush=True)
+    gpu = run_gpu(prob, flags=TWO, rows=rows)
+    rep = check_problem(prob, gpu, rows=rows)
+    _say(f"tail_R{R}", rep)
+
+
 def test_batched_matches_single_calls():
     prob = make_problem("bs", d=512, d_out=160, T=4, R=3, bits=4, group=128,
                         rank=16, seed=31)
