@@ -178,9 +178,11 @@ int ttq_quantize(const ttq_params* prm, const void* W, const void* X,
  * (same d, d_out, bits, group).  B, A as in ttq_linear (rank = prm->rank).
  * codes 16-byte aligned, dhalf_inv 16-byte aligned, the rest as in
  * ttq_linear.  p, lambda, alpha and TTQ_FLAG_FORCE_FUSED are not used;
- * TTQ_FLAG_FORCE_TWO_PHASE takes the dequantize + GEMM route also for
- * T = 1 (otherwise taken for T > 1, or where x D^{-1/2} of one token does
- * not fit 128 KiB of LDS: d above about 30000). */
+ * Routes: T = 1, a single kernel over the codes (unless x D^{-1/2} of the
+ * token does not fit 128 KiB of LDS: d above about 30000); T <= 128, the
+ * codes on the matrix cores; otherwise the codes are expanded to bf16
+ * weights and multiplied on the matrix cores.  TTQ_FLAG_FORCE_TWO_PHASE
+ * takes that last route at any T. */
 int ttq_qmatmul(const ttq_params* prm, const uint8_t* codes,
                 const float* scales, const float* mins, const float* dhalf_inv,
                 const void* X, const void* B, const void* A, float* Y,

@@ -32,6 +32,7 @@ SOURCES = [
     "k_lowrank.hip",
     "k_gemv.hip",
     "k_qgemv.hip",
+    "k_qfused.hip",
     "ttq_api.cpp",
 ]
 

@@ -19,10 +19,10 @@
 // output of a token, so a single bf16 rounding of its x' would be shared by
 // all of them; there x' is carried as a bf16 pair hi + lo (~16 significant
 // bits) and both halves are contracted.  For T > 16 x' is rounded once to
-// bf16 and the rounding errors average over the tokens; it is stored in MFMA
+// bf16 and the rounding errors average over the tokens.  It is stored in MFMA
 // fragment order so that every activation load is a contiguous 1 KiB per
-// wave, and the weights are streamed with non-temporal loads so that they do
-// not evict x' (re-read by every workgroup) from L2.
+// wave; for T > 16 the weights are streamed with non-temporal loads so that
+// they do not evict x' (re-read by every workgroup) from L2.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 with A = x' (16 tokens x 32 channels) and
 // B = codes (32 channels x 16 weight rows).  Lane l holds weight row l & 15
@@ -68,9 +68,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const int Tp = NTB * 16;
 
   const float* dhg = a.dh + (int64_t)req * d;
-  const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 * T : Tp) * d;
+  const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 : 1) * Tp * d;
   const float* sx = a.sx + (int64_t)req * G * Tp;
-  const bf16_t* xs_lo = xs + T * d;
+  const bf16_t* xs_lo = xs + (int64_t)Tp * d;
   // the workgroup's weight rows as one bounded buffer: rows past d_out and
   // groups past the end read as zeros without memory traffic
   const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
@@ -94,18 +94,14 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
       wv[k] = HILO ? buf_load16(wr, lane_off + k * 64, soff)
                    : buf_load16_nt(wr, lane_off + k * 64, soff);
   };
-  // lanes whose token is past T read a small zero buffer instead of
-  // branching (no divergent load paths for the wait-count logic)
-  const bool tok_ok = lr < T;
+  // fragment-ordered x' (zero past T): each load is 1 KiB per wave
   auto load_x = [&](int g) {
     if (NTB == 1) {
-      const int64_t colg = (int64_t)g * GS + qd * 8;
-      const bf16_t* ph = tok_ok ? xs + lr * d + colg : a.zeros + qd * 8;
-      const bf16_t* pl = tok_ok ? xs_lo + lr * d + colg : a.zeros + qd * 8;
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
-        xh[k] = *(const u32x4*)(ph + k * 32);
-        xl[k] = *(const u32x4*)(pl + k * 32);
+        const int64_t fi = 8 * xs_frag_index(g, 0, k, l, 1, GS);
+        xh[k] = *(const u32x4*)(xs + fi);
+        xl[k] = *(const u32x4*)(xs_lo + fi);
       }
       sxv0 = *(const f32x4*)(sx + (int64_t)g * Tp + qd * 4);
     }

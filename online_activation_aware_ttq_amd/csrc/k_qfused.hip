@@ -1,0 +1,287 @@
+// Contraction of a few later tokens (2..128) with stored packed codes on the
+// gfx950 matrix cores: the quantize-once counterpart of the fused one-pass
+// kernel ("TTQ: Activation-Aware Test-Time Quantization ...", nl summary,
+// Sec. 2-3; zh summary, Sec. 3-4: the codes, (s, min) and D^{-1/2} are kept
+// from the prompt, and moving low-bit weights is what makes it fast).
+//
+//   Y[t,i] = sum_g  s_ig * sum_{j in g} q_ij x'_tj  +  m_ig * sum_{j in g} x'_tj
+//
+// with x' = x D^{-1/2} from the stored D^{-1/2}.  The statistics kernel, in
+// its stored-D^{-1/2} mode, writes x' (a bf16 hi + lo pair for T <= 16, one
+// bf16 plane above; MFMA fragment order) and the per-token group sums, in
+// the layout the one-pass kernel reads; this kernel streams the codes instead
+// of bf16 weights.  Layout and work split are those of the one-pass kernel:
+// 8 or 16 waves own 16 weight rows and stride over the groups, each with
+// the codes and x' of its next group in flight; lane l holds row
+// l & 15 and channels 8*(l >> 4) .. +8 of each 32-channel step, i.e. CB bytes
+// of packed codes per step.
+//
+// Codes become the bf16 B operand exactly: for containers of up to 4 bits
+// the value 128 + q (bf16 bits 0x4300 | q, one byte permute per pair), whose
+// extra 128 * sum(x') is taken out with the minimum term:
+//   s * sum (128 + q) x' + (m - 128 s) * sum x';
+// for 8-bit containers q itself (converted through float32).
+#include "ttq_internal.h"
+
+namespace ttq {
+
+namespace {
+
+// waves per workgroup: 16 where the registers allow (more groups in flight
+// per CU; the work per group is small), else 8
+template <int NTB, int GS>
+constexpr int qf_waves() {
+  return (NTB <= 2 && GS <= 128) ? 16 : 8;
+}
+
+// 8 codes of CB bits, low bits first in `raw` -> 4 bf16 pairs (see above)
+template <int CB>
+__device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
+  if (CB == 8) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (float)((raw.x >> (8 * i)) & 0xFFu);
+      f[4 + i] = (float)((raw.y >> (8 * i)) & 0xFFu);
+    }
+    // the high halves of the floats (exact: at most 8 significant bits)
+    return u32x4{__builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u),
+                 __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u),
+                 __builtin_amdgcn_perm(__float_as_uint(f[5]), __float_as_uint(f[4]), 0x07060302u),
+                 __builtin_amdgcn_perm(__float_as_uint(f[7]), __float_as_uint(f[6]), 0x07060302u)};
+  } else if (CB == 4) {
+    // even codes in the bytes of lo, odd codes in the bytes of hi; pair k =
+    // bytes {lo.k, 0, hi.k, 0} (selector 0x0c: zero byte), then | 0x4300
+    const unsigned lo = raw.x & 0x0F0F0F0Fu, hi = (raw.x >> 4) & 0x0F0F0F0Fu;
+    return u32x4{__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u,
+                 __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u,
+                 __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u,
+                 __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u};
+  } else {
+    constexpr unsigned M = (1u << CB) - 1u;
+    unsigned p[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned q0 = (raw.x >> (2 * k * CB)) & M;
+      const unsigned q1 = (raw.x >> ((2 * k + 1) * CB)) & M;
+      p[k] = (q0 | (q1 << 16)) | 0x43004300u;
+    }
+    return u32x4{p[0], p[1], p[2], p[3]};
+  }
+}
+
+// CB bytes of codes at byte offset voff (+ soff) of the bounded row buffer
+template <int CB>
+__device__ __forceinline__ u32x2 load_codes(__amdgpu_buffer_rsrc_t r,
+                                            uint32_t voff, uint32_t soff) {
+  if (CB == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return u32x2{v[0], v[1]};
+  } else if (CB == 4) {
+    return u32x2{__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0), 0u};
+  } else if (CB == 2) {
+    return u32x2{(unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0), 0u};
+  } else {
+    return u32x2{(unsigned)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0), 0u};
+  }
+}
+
+template <int CB, int NTB, int GS>
+__global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArgs a) {
+  constexpr int QF_W = qf_waves<NTB, GS>();
+  constexpr int NKS = GS / 32;
+  constexpr bool HILO = (NTB == 1);
+  constexpr float BIAS = CB == 8 ? 0.f : 128.f;
+  __shared__ float red[QF_W][NTB * 4][64];
+
+  const int64_t rb = blockIdx.x;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = l & 15, qd = l >> 4;
+  const int64_t row = rb * 16 + lr;
+  const bool row_ok = row < a.d_out;
+  const int64_t T = a.T, d = a.d;
+  const int G = a.G;
+  const int Tp = NTB * 16;
+  const int64_t srow = (row_ok ? row : 0) * G;
+
+  // the workgroup's rows of codes as one bounded buffer (rows past d_out and
+  // groups past the end read as zeros, with no memory traffic)
+  const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(a.packed + rb * 16 * a.row_bytes, (uint32_t)(rows_here * a.row_bytes));
+  const uint32_t lane_off = (uint32_t)(lr * a.row_bytes + qd * CB);
+
+  auto load_g = [&](u32x2 (&cv)[NKS], int g) {
+    const uint32_t soff = g < G ? (uint32_t)((int64_t)g * GS * CB / 8) : kOutOfRange;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) cv[k] = load_codes<CB>(cr, lane_off + k * 4 * CB, soff);
+  };
+
+  f32x4 acc[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16_t* xs_lo = a.xs + (int64_t)Tp * d;  // T <= 16: the lo plane
+
+  // T <= 16: the group's x' (hi, lo) and group sums, fetched with its codes
+  // one group ahead (a group past the end fetches the last one again)
+  struct XHL {
+    u32x4 h[NKS], l[NKS];
+    f32x4 sx;
+  };
+  auto load_x = [&](XHL& x, int g) {
+    if (!HILO) return;
+    const int gg = g < G ? g : G - 1;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+      const int64_t fi = 8 * xs_frag_index(gg, 0, k, l, 1, GS);
+      x.h[k] = *(const u32x4*)(a.xs + fi);
+      x.l[k] = *(const u32x4*)(xs_lo + fi);
+    }
+    x.sx = *(const f32x4*)(a.sx + (int64_t)gg * Tp + qd * 4);
+  };
+
+  auto process = [&](const u32x2 (&cv)[NKS], const XHL& x, int g) {
+    const float s = a.s[srow + g];
+    const float mb = a.m[srow + g] - BIAS * s;
+    u32x4 qv[NKS];
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB>(cv[k]);
+    if (HILO) {
+      f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const bf16x8 q = __builtin_bit_cast(bf16x8, qv[k]);
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.h[k]), q, P, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.l[k]), q, P, 0, 0, 0);
+      }
+      const f32x4 sxv = x.sx;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[0][i] = fmaf(s, P[i], fmaf(mb, sxv[i], acc[0][i]));
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        u32x4 xv[NKS];
+#pragma unroll
+        for (int k = 0; k < NKS; ++k)
+          xv[k] = *(const u32x4*)(a.xs + 8 * xs_frag_index(g, tb, k, l, NTB, GS));
+        const f32x4 sxv = *(const f32x4*)(a.sx + (int64_t)g * Tp + tb * 16 + qd * 4);
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NKS; ++k)
+          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, xv[k]), __builtin_bit_cast(bf16x8, qv[k]), P, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[tb][i] = fmaf(s, P[i], fmaf(mb, sxv[i], acc[tb][i]));
+      }
+    }
+  };
+
+  // two register sets in ping-pong (a code request past the last group
+  // reads nothing)
+  u32x2 ca[NKS], cb[NKS];
+  XHL xa, xb;
+  int g = w;
+  load_g(ca, g);
+  load_x(xa, g);
+  while (g < G) {
+    load_g(cb, g + QF_W);
+    load_x(xb, g + QF_W);
+    __builtin_amdgcn_sched_barrier(0);
+    process(ca, xa, g);
+    g += QF_W;
+    if (g >= G) break;
+    load_g(ca, g + QF_W);
+    load_x(xa, g + QF_W);
+    __builtin_amdgcn_sched_barrier(0);
+    process(cb, xb, g);
+    g += QF_W;
+  }
+
+  // static low-rank term B (A X): one more MFMA chain on Z = A X
+  if (a.rank > 0) {
+    const int nk = a.rp / 32;
+    for (int kk = w; kk < nk; kk += QF_W) {
+      const int c8 = kk * 32 + qd * 8;
+      const u32x4 bv = (row_ok && c8 < a.rank)
+                           ? *(const u32x4*)(a.Blr + row * a.rank + c8)
+                           : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const int64_t tok = tb * 16 + lr;
+        const u32x4 zv = tok < T ? *(const u32x4*)(a.Z + tok * a.rp + c8)
+                                 : u32x4{0u, 0u, 0u, 0u};
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, bv), acc[tb], 0, 0, 0);
+      }
+    }
+  }
+
+  // combine the waves in a fixed order; C of a 16x16 tile: lane l holds row
+  // l & 15 and tokens 4 * (l >> 4) + i
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w][tb * 4 + i][l] = acc[tb][i];
+  __syncthreads();
+  for (int e = tid; e < NTB * 256; e += QF_W * 64) {
+    const int ti = e >> 6, ll = e & 63;
+    const int64_t tok = (ti >> 2) * 16 + (ll >> 4) * 4 + (ti & 3);
+    const int64_t rowx = rb * 16 + (ll & 15);
+    if (tok < T && rowx < a.d_out) {
+      float v = red[0][ti][ll];
+#pragma unroll
+      for (int ww = 1; ww < QF_W; ++ww) v += red[ww][ti][ll];
+      a.Y[tok * a.d_out + rowx] = v;
+    }
+  }
+}
+
+template <int CB, int NTB>
+hipError_t launch_qf_ntb(const QFusedArgs& a, int group, dim3 grid,
+                         const Launch& L) {
+#define TTQ_QF_CASE(GSV)                                                     \
+  case GSV:                                                                  \
+    return ext_launch(k_qfused<CB, NTB, GSV>, grid,                          \
+                      dim3(qf_waves<NTB, GSV>() * 64), 0, L, a);
+  switch (group) {
+    TTQ_QF_CASE(32)
+    TTQ_QF_CASE(64)
+    TTQ_QF_CASE(128)
+    TTQ_QF_CASE(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef TTQ_QF_CASE
+}
+
+template <int CB>
+hipError_t launch_qf_cb(const QFusedArgs& a, int ntb, int group, dim3 grid,
+                        const Launch& L) {
+  switch (ntb) {
+    case 1: return launch_qf_ntb<CB, 1>(a, group, grid, L);
+    case 2: return launch_qf_ntb<CB, 2>(a, group, grid, L);
+    case 4: return launch_qf_ntb<CB, 4>(a, group, grid, L);
+    case 8: return launch_qf_ntb<CB, 8>(a, group, grid, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qfused(const QFusedArgs& a, int ntb, int group, int cb,
+                         const Launch& L) {
+  const int64_t nblk = (a.d_out + 15) / 16;
+  if (nblk == 0 || a.T == 0) return hipSuccess;
+  if (a.T > 16 * ntb || (ntb == 1 && a.T > 16)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nblk);
+  switch (cb) {
+    case 1: return launch_qf_cb<1>(a, ntb, group, grid, L);
+    case 2: return launch_qf_cb<2>(a, ntb, group, grid, L);
+    case 4: return launch_qf_cb<4>(a, ntb, group, grid, L);
+    case 8: return launch_qf_cb<8>(a, ntb, group, grid, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ttq

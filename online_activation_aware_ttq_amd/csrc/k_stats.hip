@@ -72,9 +72,9 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 // (hi = bf16(x'), lo = bf16(x' - hi)), about 16 significant bits: with few
 // tokens one outlier channel can dominate every output and a single bf16
 // rounding of it would be shared by all of them.  For larger T a single bf16
-// plane is written, in MFMA fragment order (xs_frag_index) and zero-padded to
-// whole 16-token blocks.  The group sums are of exactly the values written,
-// zero past T up to the padded token count.
+// plane is written.  Planes are in MFMA fragment order (xs_frag_index) and
+// zero-padded to whole 16-token blocks.  The group sums are of exactly the
+// values written, zero past T up to the padded token count.
 // ---------------------------------------------------------------------------
 template <int PM, int BC>
 __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
@@ -92,10 +92,6 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
   const bool live = c0 < a.d;
   const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
 
-  if (a.zeros && blockIdx.x == 0 && blockIdx.z == 0 &&
-      tid < (int)(kZeroBytes / 4))
-    ((unsigned*)a.zeros)[tid] = 0u;
-
   u32x4 v[NTK];
 #pragma unroll
   for (int i = 0; i < NTK; ++i) {
@@ -103,7 +99,13 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
     v[i] = (live && t < a.T) ? *(const u32x4*)(X + t * a.d + c0)
                              : u32x4{0u, 0u, 0u, 0u};
   }
-  {
+  if (a.dhi_in) {
+    // stored D^{-1/2}: no statistics
+    if (tid < BC) {
+      const int64_t c = (int64_t)blockIdx.x * BC + tid;
+      dhi_l[tid] = c < a.d ? a.dhi_in[(int64_t)r * a.d + c] : 1.f;
+    }
+  } else {  // statistics (uniform branch)
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NTK; ++i)
@@ -115,21 +117,21 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
       for (int off = NCH; off < 64; off <<= 1) acc[j] += __shfl_xor(acc[j], off);
       if (tl % TPW == 0) red[wv][cq * 8 + j] = acc[j];
     }
-  }
-  __syncthreads();
-  if (tid < BC) {
-    const int64_t c = (int64_t)blockIdx.x * BC + tid;
-    double S = 0.0;
+    __syncthreads();
+    if (tid < BC) {
+      const int64_t c = (int64_t)blockIdx.x * BC + tid;
+      double S = 0.0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) S += red[k][tid];
-    float dh = 1.f, dhi = 1.f;
-    if (c < a.d) {
-      diag_half(finish_norm(S, PM, a.p), a.lam, a.alpha, dh, dhi);
-      a.dh[(int64_t)r * a.d + c] = dh;
-      a.dhi[(int64_t)r * a.d + c] = dhi;
-      if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
+      for (int k = 0; k < 16; ++k) S += red[k][tid];
+      float dh = 1.f, dhi = 1.f;
+      if (c < a.d) {
+        diag_half(finish_norm(S, PM, a.p), a.lam, a.alpha, dh, dhi);
+        a.dh[(int64_t)r * a.d + c] = dh;
+        a.dhi[(int64_t)r * a.d + c] = dhi;
+        if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
+      }
+      dhi_l[tid] = dhi;
     }
-    dhi_l[tid] = dhi;
   }
   if (!a.xs) return;
   __syncthreads();
@@ -138,8 +140,8 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
   const int ntb = a.Tp / 16;
   const int G = (int)(a.d / a.group);
   const int lpg = a.group >> 3;  // chunk lanes per quantization group
-  bf16_t* xs = a.xs + (int64_t)r * (tiled ? (int64_t)a.Tp : 2 * a.T) * a.d;
-  bf16_t* xs_lo = xs + a.T * a.d;
+  bf16_t* xs = a.xs + (int64_t)r * (tiled ? 1 : 2) * a.Tp * a.d;
+  bf16_t* xs_lo = xs + (int64_t)a.Tp * a.d;
   float* sx = a.sx + (int64_t)r * G * a.Tp;
   float sc[8];
 #pragma unroll
@@ -171,13 +173,10 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
                  bl[4] | (bl[5] << 16), bl[6] | (bl[7] << 16)};
     }
     if (live) {
-      if (tiled) {
-        const int lane = lane_q + (int)(t & 15);
-        *(u32x4*)(xs + 8 * xs_frag_index(g, t >> 4, k, lane, ntb, a.group)) = o;
-      } else if (t < a.T) {
-        *(u32x4*)(xs + t * a.d + c0) = o;
-        *(u32x4*)(xs_lo + t * a.d + c0) = ol;
-      }
+      const int lane = lane_q + (int)(t & 15);
+      const int64_t fi = 8 * xs_frag_index(g, t >> 4, k, lane, ntb, a.group);
+      *(u32x4*)(xs + fi) = o;
+      if (!tiled) *(u32x4*)(xs_lo + fi) = ol;
     }
     // the chunk lanes of one group are adjacent within a token row
     for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);

@@ -46,7 +46,7 @@ struct Plan {
   int zsplit = 1;        // two-phase: K splits of Z = X A^T
   int64_t zksplit = 0;   // channels per split
   size_t off_dh = 0, off_dhi = 0, off_xs = 0, off_sx = 0, off_z = 0,
-         off_statp = 0, off_what = 0, off_zeros = 0, off_zpart = 0;
+         off_statp = 0, off_what = 0, off_zpart = 0;
   size_t total = 0;
 };
 
@@ -137,10 +137,8 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     while (P.ntb * 16 < T) P.ntb *= 2;
     P.rowblocks = (dout + 15) / 16;
     P.planes = T <= 16 ? 2 : 1;
-    P.off_xs = take(sizeof(uint16_t) * P.planes * R *
-                    (P.planes == 2 ? T : 16 * P.ntb) * d);
+    P.off_xs = take(sizeof(uint16_t) * P.planes * R * 16 * P.ntb * d);
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
-    P.off_zeros = take(kZeroBytes);
   } else {
     plan_stats_split(P, R, T, d, take);
     // W_hat of up to rchunk requests at a time (at most kMaxWhatBytes)
@@ -172,7 +170,7 @@ TimingState g_timing;
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
-    "qgemv", "dequant"};
+    "qgemv", "dequant", "qfused"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -313,7 +311,6 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     sa.group = prm->group;
     sa.planes = P.planes;
     sa.Tp = 16 * P.ntb;
-    sa.zeros = need_quant ? reinterpret_cast<bf16_t*>(ws + P.off_zeros) : nullptr;
     st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, (int)R, L); });
     if (st != TTQ_OK) return st;
     if (!need_quant) return TTQ_OK;
@@ -326,7 +323,6 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     fa.W = Wb; fa.d = d; fa.d_out = dout; fa.T = T; fa.G = P.G; fa.Nf = Nf;
     fa.dh = dh; fa.xs = sa.xs; fa.sx = sa.sx;
     fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
-    fa.zeros = sa.zeros;
     fa.Y = Y;
     fa.rowblocks = P.rowblocks;
     fa.R = (int)R;
@@ -436,7 +432,9 @@ Plan make_quantize_plan(const ttq_params& q) {
   return P;
 }
 
-// path 2: one-token contraction of the codes; 1: dequantize + MFMA GEMM
+// path 2: one-token contraction of the codes; 0: x' from the stored
+// D^{-1/2}, then the codes on the matrix cores (T <= 128); 1: dequantize +
+// MFMA GEMM
 Plan make_qmatmul_plan(const ttq_params& q, int cb) {
   Plan P;
   const int64_t d = q.d, T = q.T;
@@ -450,7 +448,15 @@ Plan make_qmatmul_plan(const ttq_params& q, int cb) {
   };
   if (P.rp > 0) P.off_z = take(sizeof(uint16_t) * T * P.rp);
   const bool fits = qgemv_lds_bytes(d, cb, q.group) <= kGemvLdsMax;
-  P.path = (T == 1 && fits && !(q.flags & TTQ_FLAG_FORCE_TWO_PHASE)) ? 2 : 1;
+  const bool forced = (q.flags & TTQ_FLAG_FORCE_TWO_PHASE) != 0;
+  P.path = (T == 1 && fits && !forced) ? 2 : (T <= kFusedMaxT && !forced ? 0 : 1);
+  if (P.path == 0 && T > 0 && q.d_out > 0) {
+    P.ntb = 1;
+    while (P.ntb * 16 < T) P.ntb *= 2;
+    P.planes = T <= 16 ? 2 : 1;
+    P.off_xs = take(sizeof(uint16_t) * P.planes * 16 * P.ntb * d);
+    P.off_sx = take(sizeof(float) * P.G * 16 * P.ntb);
+  }
   if (P.path == 1 && T > 0 && q.d_out > 0) {
     P.off_what = take(sizeof(uint16_t) * q.d_out * d);
     if (P.rp > 0) plan_z_split(P, T, d, take);
@@ -558,6 +564,30 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     ga.dhi = dhalf_inv; ga.X = Xb; ga.d = d; ga.d_out = dout; ga.G = P.G;
     ga.Z = Zb; ga.Blr = Bb; ga.rank = (int)rank; ga.Y = Y;
     return run(K_QGEMV, s, [&](const Launch& L) { return launch_qgemv(ga, q.group, cb, L); });
+  }
+  if (P.path == 0) {
+    StatsSmallArgs sa{};
+    sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = 2; sa.p = 2.0;
+    sa.dhi_in = dhalf_inv;
+    sa.xs = reinterpret_cast<bf16_t*>(ws + P.off_xs);
+    sa.sx = reinterpret_cast<float*>(ws + P.off_sx);
+    sa.group = q.group;
+    sa.planes = P.planes;
+    sa.Tp = 16 * P.ntb;
+    st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
+    if (st != TTQ_OK) return st;
+    if (P.rp > 0) {
+      LowRankZArgs za{Xb, Ab, T, d, (int)rank, (int)P.rp, Zb};
+      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      if (st != TTQ_OK) return st;
+    }
+    QFusedArgs fa{};
+    fa.packed = codes; fa.row_bytes = rb; fa.s = scales; fa.m = mins;
+    fa.xs = sa.xs; fa.sx = sa.sx;
+    fa.d = d; fa.d_out = dout; fa.T = T; fa.G = P.G;
+    fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
+    fa.Y = Y;
+    return run(K_QFUSED, s, [&](const Launch& L) { return launch_qfused(fa, P.ntb, q.group, cb, L); });
   }
   bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
   DequantArgs da{};

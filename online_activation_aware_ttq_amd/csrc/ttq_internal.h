@@ -28,6 +28,7 @@ enum KernelKind {
   K_SPLITK_REDUCE,     // split-K partial sums of Z -> bf16
   K_QGEMV,             // stored packed codes x one token
   K_DEQUANT,           // stored packed codes -> W_hat
+  K_QFUSED,            // stored packed codes x 2..128 tokens
   K_NUM_KINDS
 };
 
@@ -80,14 +81,14 @@ __device__ __forceinline__ void wait_vmem_all() {
 // offsets of a weight tile stay far below 2^30)
 constexpr uint32_t kOutOfRange = 0x40000000u;
 
-// Scaled activations x' = x D^{-1/2} as the fused kernel's MFMA operand.
-//   T <= 16: two planes (bf16 hi, lo), each token-major [T][d].
-//   T  > 16: one plane in MFMA fragment order, Tp = 16 * ceil(T / 16) tokens
-//     (zeros past T): the 16-byte fragment of lane l for group g, 16-token
-//     block tb and 32-channel step k holds tokens tb*16 + (l & 15), channels
-//     g*GS + k*32 + 8*(l >> 4) .. +8, at fragment index
-//     ((g * NTB + tb) * (GS / 32) + k) * 64 + l, so that one wave load of a
-//     fragment is 1 KiB contiguous.
+// Scaled activations x' = x D^{-1/2} as the fused kernel's MFMA operand, in
+// MFMA fragment order over Tp = 16 * ceil(T / 16) tokens (zeros past T): the
+// 16-byte fragment of lane l for group g, 16-token block tb and 32-channel
+// step k holds tokens tb*16 + (l & 15), channels g*GS + k*32 + 8*(l >> 4)
+// .. +8, at fragment index ((g * NTB + tb) * (GS / 32) + k) * 64 + l, so that
+// one wave load of a fragment is 1 KiB contiguous.
+//   T <= 16: two such planes of Tp * d values (bf16 hi, then lo).
+//   T  > 16: one plane.
 __host__ __device__ inline int64_t xs_frag_index(int64_t g, int64_t tb,
                                                  int64_t k, int l, int ntb,
                                                  int gs) {
@@ -123,7 +124,9 @@ struct StatsSmallArgs {
   int group;
   int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16
   int Tp;               // 16 * ceil(T / 16): tokens of the fragment layout
-  bf16_t* zeros;        // optional kZeroBytes to clear
+  // optional [R][d] stored D^{-1/2}: no statistics are taken, x' and the
+  // group sums are formed with these values (dh, dhi are not written)
+  const float* dhi_in;
 };
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
                               const Launch& L);
@@ -155,7 +158,6 @@ struct FusedArgs {
   const bf16_t* Z;      // [R][T][rp] or null
   const bf16_t* Blr;    // [d_out][rank] or null
   int rank, rp;
-  const bf16_t* zeros;  // kZeroBytes of zeros (cleared by the stats kernel)
   float* Y;             // [R][T][d_out]
   int64_t rowblocks;    // ceil(d_out / 16)
   int R;
@@ -163,7 +165,6 @@ struct FusedArgs {
   float* s_out;         // [R][d_out][G]
   float* m_out;         // [R][d_out][G]
 };
-constexpr size_t kZeroBytes = 1024;
 // D^{1/2} is staged in LDS when it fits in this many bytes.
 constexpr size_t kFusedDhLdsMax = 64 * 1024;
 hipError_t launch_fused(const FusedArgs& a, int ntb, int group,
@@ -245,6 +246,26 @@ struct DequantArgs {
 };
 hipError_t launch_dequant(const DequantArgs& a, int group, int cb,
                           const Launch& L);
+
+// Contraction of 2..128 later tokens with stored packed codes on the matrix
+// cores (same x' operand and group sums as the fused one-pass kernel, written
+// by the statistics kernel from the stored D^{-1/2}).
+struct QFusedArgs {
+  const uint8_t* packed;  // [d_out][row_bytes]
+  int64_t row_bytes;
+  const float* s;         // [d_out][G]
+  const float* m;         // [d_out][G]
+  const bf16_t* xs;       // x' as written by the statistics kernel
+  const float* sx;        // [G][Tp] group sums of xs
+  int64_t d, d_out, T;
+  int G;
+  const bf16_t* Z;        // [T][rp] or null
+  const bf16_t* Blr;      // [d_out][rank] or null
+  int rank, rp;
+  float* Y;               // [T][d_out]
+};
+hipError_t launch_qfused(const QFusedArgs& a, int ntb, int group, int cb,
+                         const Launch& L);
 
 // C[M][N] (+)= A1[M][K1] B1[N][K1]^T + A2[M][K2] B2[N][K2]^T, fp32 accumulate.
 struct GemmArgs {

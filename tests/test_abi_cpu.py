@@ -298,9 +298,11 @@ def test_packed_calls_workspace():
     need = ttq.ttq_qmatmul_workspace_bytes(p)
     assert need > 0
     assert call_qmatmul(p, Bm=FAKE, A=FAKE, ws_bytes=need - 1) == ttq.TTQ_EWORKSPACE
-    # the dequantize route of T > 1 holds the bf16 weights
-    big = ttq.ttq_qmatmul_workspace_bytes(prm(T=64))
-    assert big >= 64 * 256 * 2
+    # T <= 128: x' of the step (one bf16 plane of 64 tokens here)
+    assert ttq.ttq_qmatmul_workspace_bytes(prm(T=64)) >= 64 * 256 * 2
+    # larger T (or the forced route) holds the expanded bf16 weights
+    assert ttq.ttq_qmatmul_workspace_bytes(prm(T=200)) >= 64 * 256 * 2
+    assert ttq.ttq_qmatmul_workspace_bytes(prm(T=8, flags=2)) >= 64 * 256 * 2
     assert ttq.ttq_qmatmul_workspace_bytes(prm(T=1)) == 0
     q = prm(T=2048)
     qneed = ttq.ttq_quantize_workspace_bytes(q)

@@ -14,7 +14,8 @@ Three checks per case:
     decode (Y bars).
 Shapes span several row blocks with ragged tails, every container width,
 every group size, both statistics routes of ttq_quantize (T <= 128 and
-larger) and both routes of ttq_qmatmul (one token, dequantize + GEMM).
+larger) and the three routes of ttq_qmatmul (one token; up to 128 tokens on
+the codes; dequantize + GEMM, also forced at small T).
 """
 import numpy as np
 import pytest
@@ -145,7 +146,7 @@ def test_quantize_then_decode(name, kw, steps):
         Y_or = oracle.ttq_qmatmul(qz["packed"], qz["s"], qz["m"], qz["dhi32"],
                                   Xs, bits=prob.bits, group=prob.group,
                                   B_bits=prob.B, A_bits=prob.A)
-        for flags in ((0, TWO) if Ts == 1 else (0,)):
+        for flags in (0, TWO):
             # decode kernel alone, on the oracle's stored values
             Y1 = _gpu_qmatmul(stored_oracle, Xs, prob, flags)
             check_y(Y1, Y_or, rep, f"decode_T{Ts}_f{flags}")
