@@ -17,8 +17,8 @@
 // and power, one rounding to float32), so the codes are decided from the
 // same float32 values as on the other paths.
 //
-// Lane layout as in the fused kernel: lane l holds weight row l & 15 and
-// channels 8*(l >> 4) .. +8 of each 32-channel step (one 16-byte load of W);
+// Lane layout: lane l holds weight row l & 15 and channels 8*(l >> 4) .. +8
+// of each 32-channel step (one 16-byte load of W);
 // a group's statistics live in lanes {l, l^16, l^32, l^48}.  Each of the 16
 // waves owns a contiguous run of groups (contiguous weight bytes per row),
 // derives the statistics of its own channels while its first weights are in

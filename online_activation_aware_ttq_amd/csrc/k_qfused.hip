@@ -10,11 +10,12 @@
 // its stored-D^{-1/2} mode, writes x' (a bf16 hi + lo pair for T <= 16, one
 // bf16 plane above; MFMA fragment order) and the per-token group sums, in
 // the layout the one-pass kernel reads; this kernel streams the codes instead
-// of bf16 weights.  Layout and work split are those of the one-pass kernel:
-// 8 or 16 waves own 16 weight rows and stride over the groups, each with
-// the codes and x' of its next group in flight; lane l holds row
-// l & 15 and channels 8*(l >> 4) .. +8 of each 32-channel step, i.e. CB bytes
-// of packed codes per step.
+// of bf16 weights.  The work split is that of the one-pass kernel: 8 or 16
+// waves own 16 weight rows and stride over the groups, each with the codes
+// and x' of its next group in flight.  Lane l holds row l & 15 and lane
+// quarter l >> 4 a contiguous quarter of each group (8 channels per MFMA
+// step; x' in the quarter fragment order), i.e. GS/32 * CB contiguous bytes
+// of the packed row per group: one wide load.
 //
 // Codes become the bf16 B operand exactly: for containers of up to 4 bits
 // the value 128 + q (bf16 bits 0x4300 | q, one byte permute per pair), whose
@@ -70,20 +71,45 @@ __device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
   }
 }
 
-// CB bytes of codes at byte offset voff (+ soff) of the bounded row buffer
-template <int CB>
-__device__ __forceinline__ u32x2 load_codes(__amdgpu_buffer_rsrc_t r,
-                                            uint32_t voff, uint32_t soff) {
-  if (CB == 8) {
+// A lane's codes of one group: its contiguous quarter of the group, NB =
+// GS/32 * CB bytes, fetched with the widest loads that tile it.
+template <int CB, int GS>
+struct GroupCodes {
+  static constexpr int NB = GS / 32 * CB;
+  unsigned w[NB >= 4 ? NB / 4 : 1];
+};
+
+template <int CB, int GS>
+__device__ __forceinline__ void load_codes(GroupCodes<CB, GS>& c,
+                                           __amdgpu_buffer_rsrc_t r,
+                                           uint32_t voff, uint32_t soff) {
+  constexpr int NB = GroupCodes<CB, GS>::NB;
+  if constexpr (NB >= 16) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const u32x4 v = buf_load16(r, voff + i * 16, soff);
+      c.w[4 * i] = v.x; c.w[4 * i + 1] = v.y; c.w[4 * i + 2] = v.z; c.w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NB == 8) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    return u32x2{v[0], v[1]};
-  } else if (CB == 4) {
-    return u32x2{__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0), 0u};
-  } else if (CB == 2) {
-    return u32x2{(unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0), 0u};
+    c.w[0] = v[0];
+    c.w[1] = v[1];
+  } else if constexpr (NB == 4) {
+    c.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  } else if constexpr (NB == 2) {
+    c.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   } else {
-    return u32x2{(unsigned)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0), 0u};
+    c.w[0] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
   }
+}
+
+// the 8 codes (CB bytes) of MFMA step k, low bits first
+template <int CB, int GS>
+__device__ __forceinline__ u32x2 step_codes(const GroupCodes<CB, GS>& c, int k) {
+  if (CB == 8) return u32x2{c.w[2 * k], c.w[2 * k + 1]};
+  if (CB == 4) return u32x2{c.w[k], 0u};
+  if (CB == 2) return u32x2{(c.w[k / 2] >> (16 * (k % 2))) & 0xFFFFu, 0u};
+  return u32x2{(c.w[k / 4] >> (8 * (k % 4))) & 0xFFu, 0u};
 }
 
 template <int CB, int NTB, int GS>
@@ -110,12 +136,13 @@ __global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArg
   const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
   const __amdgpu_buffer_rsrc_t cr =
       make_rsrc(a.packed + rb * 16 * a.row_bytes, (uint32_t)(rows_here * a.row_bytes));
-  const uint32_t lane_off = (uint32_t)(lr * a.row_bytes + qd * CB);
+  // lane quarter qd owns channels qd*GS/4 .. +GS/4 of each group
+  const uint32_t lane_off =
+      (uint32_t)(lr * a.row_bytes + qd * GroupCodes<CB, GS>::NB);
 
-  auto load_g = [&](u32x2 (&cv)[NKS], int g) {
+  auto load_g = [&](GroupCodes<CB, GS>& cv, int g) {
     const uint32_t soff = g < G ? (uint32_t)((int64_t)g * GS * CB / 8) : kOutOfRange;
-#pragma unroll
-    for (int k = 0; k < NKS; ++k) cv[k] = load_codes<CB>(cr, lane_off + k * 4 * CB, soff);
+    load_codes<CB, GS>(cv, cr, lane_off, soff);
   };
 
   f32x4 acc[NTB];
@@ -142,12 +169,12 @@ __global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArg
     x.sx = *(const f32x4*)(a.sx + (int64_t)gg * Tp + qd * 4);
   };
 
-  auto process = [&](const u32x2 (&cv)[NKS], const XHL& x, int g) {
+  auto process = [&](const GroupCodes<CB, GS>& cv, const XHL& x, int g) {
     const float s = a.s[srow + g];
     const float mb = a.m[srow + g] - BIAS * s;
     u32x4 qv[NKS];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB>(cv[k]);
+    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB>(step_codes<CB, GS>(cv, k));
     if (HILO) {
       f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -180,7 +207,7 @@ __global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArg
 
   // two register sets in ping-pong (a code request past the last group
   // reads nothing)
-  u32x2 ca[NKS], cb[NKS];
+  GroupCodes<CB, GS> ca, cb;
   XHL xa, xb;
   int g = w;
   load_g(ca, g);

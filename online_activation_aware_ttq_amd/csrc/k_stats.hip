@@ -146,8 +146,11 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
   float sc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) sc[j] = dhi_l[cq * 8 + j];
-  const int64_t g = c0 / a.group, k = (c0 % a.group) / 32;
-  const int lane_q = (int)((c0 % 32) / 8) * 16;
+  // fragment of these 8 channels (see xs_frag_index): MFMA step and lane
+  // quarter, in step-major or quarter order
+  const int64_t g = c0 / a.group, cig = c0 % a.group;
+  const int64_t k = a.quarter ? (cig % (a.group / 4)) / 8 : cig / 32;
+  const int lane_q = (int)(a.quarter ? cig / (a.group / 4) : (cig % 32) / 8) * 16;
 #pragma unroll
   for (int i = 0; i < NTK; ++i) {
     const int64_t t = tl + i * TLN;

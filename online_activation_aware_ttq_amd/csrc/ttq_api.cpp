@@ -569,6 +569,7 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     StatsSmallArgs sa{};
     sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = 2; sa.p = 2.0;
     sa.dhi_in = dhalf_inv;
+    sa.quarter = 1;
     sa.xs = reinterpret_cast<bf16_t*>(ws + P.off_xs);
     sa.sx = reinterpret_cast<float*>(ws + P.off_sx);
     sa.group = q.group;

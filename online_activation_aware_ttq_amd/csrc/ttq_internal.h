@@ -81,12 +81,17 @@ __device__ __forceinline__ void wait_vmem_all() {
 // offsets of a weight tile stay far below 2^30)
 constexpr uint32_t kOutOfRange = 0x40000000u;
 
-// Scaled activations x' = x D^{-1/2} as the fused kernel's MFMA operand, in
+// Scaled activations x' = x D^{-1/2} as the fused kernels' MFMA operand, in
 // MFMA fragment order over Tp = 16 * ceil(T / 16) tokens (zeros past T): the
-// 16-byte fragment of lane l for group g, 16-token block tb and 32-channel
-// step k holds tokens tb*16 + (l & 15), channels g*GS + k*32 + 8*(l >> 4)
-// .. +8, at fragment index ((g * NTB + tb) * (GS / 32) + k) * 64 + l, so that
-// one wave load of a fragment is 1 KiB contiguous.
+// 16-byte fragment of lane l for group g, 16-token block tb and MFMA step k
+// (k < GS / 32) holds tokens tb*16 + (l & 15) and 8 channels from
+//   step-major order:  g*GS + 32k + 8*(l >> 4)        (the one-pass kernel:
+//                      each wave load of weights covers 64 contiguous bytes
+//                      of each of 16 rows), or
+//   quarter order:     g*GS + (l >> 4) * GS/4 + 8k    (the packed-code kernel:
+//                      a lane's codes of one group are one contiguous run),
+// at fragment index ((g * NTB + tb) * (GS / 32) + k) * 64 + l, so that one
+// wave load of a fragment is 1 KiB contiguous.
 //   T <= 16: two such planes of Tp * d values (bf16 hi, then lo).
 //   T  > 16: one plane.
 __host__ __device__ inline int64_t xs_frag_index(int64_t g, int64_t tb,
@@ -124,6 +129,7 @@ struct StatsSmallArgs {
   int group;
   int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16
   int Tp;               // 16 * ceil(T / 16): tokens of the fragment layout
+  int quarter;          // 1: quarter order of the fragments, 0: step-major
   // optional [R][d] stored D^{-1/2}: no statistics are taken, x' and the
   // group sums are formed with these values (dh, dhi are not written)
   const float* dhi_in;
