@@ -60,13 +60,15 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 // ---------------------------------------------------------------------------
 // Small T (T <= 128, fused path and statistics-only calls): a workgroup of
 // 1024 threads owns BC channels (128, or 256 for groups of 256: always whole
-// quantization groups) and every token.  Thread (token lane tl, channel chunk
-// cq) loads the tokens tl + i * TLN of 8 consecutive channels; the float64
-// partial powers are summed over the token lanes of a wave (fixed butterfly),
-// then over the waves in LDS in order, one thread per channel finishes
-// D^{+-1/2} and publishes it.  Then every thread writes x' = x * D^{-1/2} for
-// its tokens (the fused kernel's MFMA operand) and the group sums of x' per
-// token.  X is read once.
+// quantization groups) and every token for the statistics, and writes x' for
+// one 32-token slice (the slices' workgroups repeat the statistics: X is
+// small, and the chip has more CUs than there are channel blocks).  Thread
+// (token lane tl, channel chunk cq) loads the tokens tl + i * TLN of 8
+// consecutive channels; the float64 partial powers are summed over the token
+// lanes of a wave (fixed butterfly), then over the waves in LDS in order, one
+// thread per channel finishes D^{+-1/2}.  Then the threads holding the
+// slice's tokens write x' = x * D^{-1/2} (the fused kernels' MFMA operand)
+// and the group sums of x' per token.
 //
 // For T <= 16 x' is carried as an unevaluated pair of bf16 numbers hi + lo
 // (hi = bf16(x'), lo = bf16(x' - hi)), about 16 significant bits: with few
@@ -126,9 +128,11 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
       float dh = 1.f, dhi = 1.f;
       if (c < a.d) {
         diag_half(finish_norm(S, PM, a.p), a.lam, a.alpha, dh, dhi);
-        a.dh[(int64_t)r * a.d + c] = dh;
-        a.dhi[(int64_t)r * a.d + c] = dhi;
-        if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
+        if (blockIdx.y == 0) {  // one of the token slices publishes
+          a.dh[(int64_t)r * a.d + c] = dh;
+          a.dhi[(int64_t)r * a.d + c] = dhi;
+          if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
+        }
       }
       dhi_l[tid] = dhi;
     }
@@ -155,6 +159,7 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
   for (int i = 0; i < NTK; ++i) {
     const int64_t t = tl + i * TLN;
     if (t >= a.Tp) break;  // uniform across the chunk lanes of a token
+    if ((t >> 5) != (int64_t)blockIdx.y) continue;  // another slice's token
     float ps = 0.f;
     u32x4 o = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
     if (live && t < a.T) {
@@ -189,14 +194,17 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
 
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
   if (a.T > 128) return hipErrorInvalidValue;
+  // x' of 32-token slices in separate workgroups (each takes the statistics
+  // of all tokens itself; one of them publishes D^{+-1/2})
+  const unsigned nsl = a.xs ? (unsigned)((a.Tp + 31) / 32) : 1u;
   const dim3 blk(1024);
   if (a.group == 256) {
-    const dim3 grid((unsigned)((a.d + 255) / 256), 1u, (unsigned)R);
+    const dim3 grid((unsigned)((a.d + 255) / 256), nsl, (unsigned)R);
     if (a.pmode == 2) return ext_launch(k_stats_small<2, 256>, grid, blk, 0, L, a);
     if (a.pmode == 1) return ext_launch(k_stats_small<1, 256>, grid, blk, 0, L, a);
     return ext_launch(k_stats_small<0, 256>, grid, blk, 0, L, a);
   }
-  const dim3 grid((unsigned)((a.d + 127) / 128), 1u, (unsigned)R);
+  const dim3 grid((unsigned)((a.d + 127) / 128), nsl, (unsigned)R);
   if (a.pmode == 2) return ext_launch(k_stats_small<2, 128>, grid, blk, 0, L, a);
   if (a.pmode == 1) return ext_launch(k_stats_small<1, 128>, grid, blk, 0, L, a);
   return ext_launch(k_stats_small<0, 128>, grid, blk, 0, L, a);
