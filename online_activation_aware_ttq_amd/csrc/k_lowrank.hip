@@ -3,67 +3,144 @@
 // ("TTQ: Activation-Aware Test-Time Quantization ...", gist.science zh
 // summary, Sec. 2.2: W ~ W_q + B A with static B, A).  Stored as bf16 with the
 // rank padded to a multiple of 32 (zeros), the operand layout the fused
-// kernel's MFMA tail reads.  A workgroup computes one rank index for up to 16
-// tokens: lanes stride over the channels with 16-byte loads, the partial
-// dot products are reduced across the workgroup in a fixed order.
+// kernels' MFMA tail reads.
+//
+// With few tokens the work is a long, thin reduction over the channels, so it
+// is cut along the channels: a workgroup of 4 waves takes 16 tokens, 64 rank
+// columns and one channel slice; each wave runs v_mfma_f32_16x16x32_bf16 over
+// a quarter of the slice (A operand: 16 tokens x 32 channels of X, one 16-byte
+// load per lane; B operand: 32 channels x 16 rank rows of A, likewise), the
+// waves are added in LDS in a fixed order and the slice's fp32 partial tile
+// is stored.  A second kernel adds the slices in slice order and rounds once
+// to bf16, so the result does not depend on scheduling.
 #include "ttq_internal.h"
 
 namespace ttq {
 
-__global__ __launch_bounds__(256) void k_lowrank_z(LowRankZArgs a) {
-  constexpr int TM = 16;
-  const int k = blockIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.y * TM;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int mcount = (int)min((int64_t)TM, a.M - m0);
-  if (k >= a.rank) {
-    if (tid < mcount) a.Z[(m0 + tid) * a.rp + k] = 0;
-    return;
+namespace {
+
+constexpr int ZW = 4;        // waves per workgroup
+constexpr int ZTILES = 4;    // 16-column rank tiles per workgroup
+
+__global__ __launch_bounds__(ZW * 64) void k_lowrank_zpart(LowRankZArgs a,
+                                                           int64_t kslice) {
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int n0 = blockIdx.y * 16 * ZTILES;
+  const int z = blockIdx.z;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt = min(ZTILES, (a.rp - n0) / 16);
+  const int tr = l & 15, kq = l >> 4;
+  const int64_t kbeg = (int64_t)z * kslice;
+  const int64_t kend = min(a.d, kbeg + kslice);
+  const int64_t wsl = kslice / ZW;
+  const int64_t k0 = kbeg + w * wsl, k1 = min(kend, k0 + wsl);
+  const int64_t m = m0 + tr;
+  const bf16_t* xr = a.X + (m < a.M ? m : 0) * a.d;
+
+  f32x4 acc[ZTILES];
+#pragma unroll
+  for (int t = 0; t < ZTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operands of one 32-channel step (zero past the slice, past M, past rank)
+  auto load = [&](int64_t kc, u32x4& xf, u32x4 (&af)[ZTILES]) {
+    const int64_t c = kc + 8 * kq;
+    const bool cin = c < k1;
+    xf = (cin && m < a.M) ? *(const u32x4*)(xr + c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < ZTILES; ++t) {
+      const int r = n0 + 16 * t + tr;
+      af[t] = (t < nt && cin && r < a.rank) ? *(const u32x4*)(a.A + (int64_t)r * a.d + c)
+                                             : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 xa, xb, aa[ZTILES], ab[ZTILES];
+  int64_t kc = k0;
+  load(kc, xa, aa);
+  while (kc < k1) {
+    load(kc + 32, xb, ab);
+#pragma unroll
+    for (int t = 0; t < ZTILES; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, xa), __builtin_bit_cast(bf16x8, aa[t]), acc[t], 0, 0, 0);
+    kc += 32;
+    if (kc >= k1) break;
+    load(kc + 32, xa, aa);
+#pragma unroll
+    for (int t = 0; t < ZTILES; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, xb), __builtin_bit_cast(bf16x8, ab[t]), acc[t], 0, 0, 0);
+    kc += 32;
   }
-  float acc[TM];
+
+  // waves in a fixed order; C of a 16x16 tile: lane l holds rank column
+  // l & 15 and tokens 4 * (l >> 4) + i
+  __shared__ float red[ZW][ZTILES * 4][64];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i] = 0.f;
-  const bf16_t* Ak = a.A + (int64_t)k * a.d;
-  for (int64_t c = (int64_t)tid * 8; c < a.d; c += 2048) {
-    const u32x4 av = *(const u32x4*)(Ak + c);
-    const float af[8] = {bf16lo(av.x), bf16hi(av.x), bf16lo(av.y),
-                         bf16hi(av.y), bf16lo(av.z), bf16hi(av.z),
-                         bf16lo(av.w), bf16hi(av.w)};
+  for (int t = 0; t < ZTILES; ++t)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (i < mcount) {
-        const u32x4 xv = *(const u32x4*)(a.X + (m0 + i) * a.d + c);
-        float s = acc[i];
-        s = fmaf(bf16lo(xv.x), af[0], s);
-        s = fmaf(bf16hi(xv.x), af[1], s);
-        s = fmaf(bf16lo(xv.y), af[2], s);
-        s = fmaf(bf16hi(xv.y), af[3], s);
-        s = fmaf(bf16lo(xv.z), af[4], s);
-        s = fmaf(bf16hi(xv.z), af[5], s);
-        s = fmaf(bf16lo(xv.w), af[6], s);
-        s = fmaf(bf16hi(xv.w), af[7], s);
-        acc[i] = s;
-      }
+    for (int i = 0; i < 4; ++i) red[w][t * 4 + i][l] = acc[t][i];
+  __syncthreads();
+  for (int e = tid; e < ZTILES * 4 * 64; e += ZW * 64) {
+    const int ti = e >> 6, ll = e & 63;
+    const int t = ti >> 2, i = ti & 3;
+    const int64_t tok = m0 + 4 * (ll >> 4) + i;
+    const int col = n0 + 16 * t + (ll & 15);
+    if (t < nt && tok < a.M && col < a.rp) {
+      const float v = ((red[0][ti][ll] + red[1][ti][ll]) + red[2][ti][ll]) + red[3][ti][ll];
+      a.part[((int64_t)z * a.M + tok) * a.rp + col] = v;
     }
   }
-  __shared__ float red[4][TM];
+}
+
+__global__ __launch_bounds__(256) void k_lowrank_zsum(LowRankZArgs a, int nsplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = a.M * a.rp;
+  if (i >= n) return;
+  // slice order; the loads of 16 slices are in flight together
+  float v = a.part[i];
+  int z = 1;
+  for (; z + 16 <= nsplit; z += 16) {
+    float t[16];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    float v = acc[i];
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if (l == 0) red[w][i] = v;
+    for (int j = 0; j < 16; ++j) t[j] = a.part[(int64_t)(z + j) * n + i];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v += t[j];
   }
-  __syncthreads();
-  if (tid < mcount) {
-    const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    a.Z[(m0 + tid) * a.rp + k] = (bf16_t)f2bf(v);
-  }
+  for (; z < nsplit; ++z) v += a.part[(int64_t)z * n + i];
+  a.Z[i] = (bf16_t)f2bf(v);
+}
+
+}  // namespace
+
+// channel slices: about 128 workgroups, each over at least 256 channels
+// (the slices are summed by a second kernel; few of them keep it short)
+int lowrank_z_splits(int64_t M, int64_t d, int rp) {
+  const int64_t blocks = ((M + 15) / 16) * ((rp + 16 * ZTILES - 1) / (16 * ZTILES));
+  int64_t s = (128 + blocks - 1) / blocks;
+  const int64_t smax = (d + 255) / 256;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
 hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L) {
   if (a.M == 0) return hipSuccess;
-  dim3 grid((unsigned)a.rp, (unsigned)((a.M + 15) / 16));
-  return ext_launch(k_lowrank_z, grid, dim3(256), 0, L, a);
+  if (!a.part || a.rp % 32 != 0) return hipErrorInvalidValue;
+  const int s = lowrank_z_splits(a.M, a.d, a.rp);
+  // slice length: a multiple of 128 channels (32 per wave)
+  const int64_t kslice = ((a.d + s - 1) / s + 127) / 128 * 128;
+  const dim3 grid((unsigned)((a.M + 15) / 16),
+                  (unsigned)((a.rp + 16 * ZTILES - 1) / (16 * ZTILES)), (unsigned)s);
+  return ext_launch(k_lowrank_zpart, grid, dim3(ZW * 64), 0, L, a, kslice);
+}
+
+hipError_t launch_lowrank_z_sum(const LowRankZArgs& a, const Launch& L) {
+  const int64_t n = a.M * a.rp;
+  if (n == 0) return hipSuccess;
+  const int s = lowrank_z_splits(a.M, a.d, a.rp);
+  return ext_launch(k_lowrank_zsum, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                    0, L, a, s);
 }
 
 }  // namespace ttq

@@ -47,6 +47,7 @@ struct Plan {
   int64_t zksplit = 0;   // channels per split
   size_t off_dh = 0, off_dhi = 0, off_xs = 0, off_sx = 0, off_z = 0,
          off_statp = 0, off_what = 0, off_zpart = 0;
+  size_t off_zsmall = 0;  // fp32 partials of the small-M Z kernel
   size_t total = 0;
 };
 
@@ -129,6 +130,8 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
   P.off_dh = take(sizeof(float) * R * d);
   P.off_dhi = take(sizeof(float) * R * d);
   if (P.rp > 0) P.off_z = take(sizeof(uint16_t) * R * T * P.rp);
+  if (P.rp > 0 && T > 0 && (P.path == 2 || fused))
+    P.off_zsmall = take(lowrank_z_part_bytes(R * T, d, (int)P.rp));
 
   if (P.path == 2) {
     P.rowblocks = (dout + 15) / 16;
@@ -170,7 +173,7 @@ TimingState g_timing;
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
-    "qgemv", "dequant", "qfused"};
+    "qgemv", "dequant", "qfused", "lowrank_zsum"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -242,6 +245,18 @@ int enqueue_z_gemm(const Plan& P, char* ws, const bf16_t* Xb,
   return run(K_SPLITK_REDUCE, s, [&](const Launch& L) { return launch_splitk_reduce(ra, L); });
 }
 
+// Z = X A^T for small M (one-token, fused and packed-code routes): channel
+// slices on the matrix cores, then their ordered sum.
+int enqueue_z_small(const Plan& P, char* ws, const bf16_t* Xb,
+                    const bf16_t* Ab, int64_t M, int64_t d, int64_t rank,
+                    bf16_t* Zb, hipStream_t s) {
+  LowRankZArgs za{Xb, Ab, M, d, (int)rank, (int)P.rp, Zb,
+                  reinterpret_cast<float*>(ws + P.off_zsmall)};
+  int st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+  if (st != TTQ_OK) return st;
+  return run(K_LOWRANK_ZSUM, s, [&](const Launch& L) { return launch_lowrank_z_sum(za, L); });
+}
+
 int linear_impl(const ttq_params* prm, int64_t R, const void* W,
                 const void* X, const void* B, const void* A, float* Y,
                 uint8_t* codes_out, float* scales_out, float* mins_out,
@@ -281,8 +296,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
 
   if (P.path == 2) {
     if (P.rp > 0) {
-      LowRankZArgs za{Xb, Ab, R, d, (int)rank, (int)P.rp, Zb};
-      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      st = enqueue_z_small(P, ws, Xb, Ab, R, d, rank, Zb, s);
       if (st != TTQ_OK) return st;
     }
     GemvArgs va{};
@@ -315,8 +329,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     if (st != TTQ_OK) return st;
     if (!need_quant) return TTQ_OK;
     if (P.rp > 0 && T > 0) {
-      LowRankZArgs za{Xb, Ab, R * T, d, (int)rank, (int)P.rp, Zb};
-      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      st = enqueue_z_small(P, ws, Xb, Ab, R * T, d, rank, Zb, s);
       if (st != TTQ_OK) return st;
     }
     FusedArgs fa{};
@@ -450,6 +463,8 @@ Plan make_qmatmul_plan(const ttq_params& q, int cb) {
   const bool fits = qgemv_lds_bytes(d, cb, q.group) <= kGemvLdsMax;
   const bool forced = (q.flags & TTQ_FLAG_FORCE_TWO_PHASE) != 0;
   P.path = (T == 1 && fits && !forced) ? 2 : (T <= kFusedMaxT && !forced ? 0 : 1);
+  if (P.rp > 0 && T > 0 && P.path != 1)
+    P.off_zsmall = take(lowrank_z_part_bytes(T, d, (int)P.rp));
   if (P.path == 0 && T > 0 && q.d_out > 0) {
     P.ntb = 1;
     while (P.ntb * 16 < T) P.ntb *= 2;
@@ -555,8 +570,7 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
   const bf16_t* Ab = static_cast<const bf16_t*>(A);
   if (P.path == 2) {
     if (P.rp > 0) {
-      LowRankZArgs za{Xb, Ab, 1, d, (int)rank, (int)P.rp, Zb};
-      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      st = enqueue_z_small(P, ws, Xb, Ab, 1, d, rank, Zb, s);
       if (st != TTQ_OK) return st;
     }
     QGemvArgs ga{};
@@ -578,8 +592,7 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
     if (st != TTQ_OK) return st;
     if (P.rp > 0) {
-      LowRankZArgs za{Xb, Ab, T, d, (int)rank, (int)P.rp, Zb};
-      st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+      st = enqueue_z_small(P, ws, Xb, Ab, T, d, rank, Zb, s);
       if (st != TTQ_OK) return st;
     }
     QFusedArgs fa{};

@@ -29,6 +29,7 @@ enum KernelKind {
   K_QGEMV,             // stored packed codes x one token
   K_DEQUANT,           // stored packed codes -> W_hat
   K_QFUSED,            // stored packed codes x 2..128 tokens
+  K_LOWRANK_ZSUM,      // ordered sum of the small-M low-rank partials
   K_NUM_KINDS
 };
 
@@ -108,10 +109,10 @@ struct Launch {
   hipEvent_t e0, e1;
 };
 
-template <typename A>
-inline hipError_t ext_launch(void (*kernel)(A), dim3 grid, dim3 block,
-                             uint32_t lds, const Launch& L, const A& args) {
-  void* argv[] = {const_cast<A*>(&args)};
+template <typename... A>
+inline hipError_t ext_launch(void (*kernel)(A...), dim3 grid, dim3 block,
+                             uint32_t lds, const Launch& L, const A&... args) {
+  void* argv[] = {const_cast<A*>(&args)...};
   return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
                             argv, lds, L.s, L.e0, L.e1, 0);
 }
@@ -317,7 +318,16 @@ struct LowRankZArgs {
   int64_t M, d;
   int rank, rp;
   bf16_t* Z;            // [M][rp]
+  float* part;          // [nsplit][M][rp] fp32 partial sums (workspace)
 };
+// Z = X A^T for small M: channel slices on the matrix cores (partials), then
+// their sum in slice order.  Two launches; lowrank_z_parts gives the slice
+// count and the bytes of `part`.
 hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L);
+hipError_t launch_lowrank_z_sum(const LowRankZArgs& a, const Launch& L);
+int lowrank_z_splits(int64_t M, int64_t d, int rp);
+inline size_t lowrank_z_part_bytes(int64_t M, int64_t d, int rp) {
+  return (size_t)lowrank_z_splits(M, d, rp) * M * rp * sizeof(float);
+}
 
 }  // namespace ttq
