@@ -132,7 +132,11 @@ int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
 /* Which path a call with these parameters takes: 0 = fused single pass over
  * W (statistics kernel + one fused quantize/MFMA kernel), 1 = two phase
  * (statistics, quantize pass writing W_hat, MFMA GEMM), 2 = single launch
- * for one token (T = 1, d <= 12288, no path flag).  Negative = status. */
+ * for one token (T = 1, d <= 12288, no path flag), 3 = two phase with the
+ * weight tiles quantized inside the MFMA GEMM (129 <= T <= 256, d a
+ * multiple of 128, group <= 128, no path flag; a call that asks for codes or
+ * scales takes path 1).  Paths 1 and 3 give bit-identical Y.
+ * Negative = status. */
 int ttq_path(const ttq_params* prm, int64_t n_requests);
 
 /* ---- quantize once per prompt, decode from the stored codes -------------

@@ -33,6 +33,7 @@ SOURCES = [
     "k_gemv.hip",
     "k_qgemv.hip",
     "k_qfused.hip",
+    "k_gemm_q.hip",
     "ttq_api.cpp",
 ]
 

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) issue(p, p);
   wait_vm<(NS - 2) * NL>();
-  __syncthreads();
+  lds_barrier();
   read_frags(0, 0, fa[0], fb[0]);
   issue(NS - 1, NS - 1);
 
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
       constexpr int cur = (BK / 16 - 1) & 1;
       // tile kt+1 landed (NS-2 younger tiles may still be in flight)
       wait_vm<(NS - 2) * NL>();
-      __syncthreads();   // ... for every wave; all reads of stage kt done
+      lds_barrier();   // ... for every wave; all reads of stage kt done
       read_frags(nstage, 0, fa[cur ^ 1], fb[cur ^ 1]);
       issue(kt + NS, stage);
       mfmas(fa[cur], fb[cur]);

@@ -25,6 +25,10 @@ constexpr int64_t kMaxElems = int64_t(1) << 34;
 // two-phase path: workspace for the dequantized weights of several requests
 constexpr int64_t kMaxWhatBytes = int64_t(4) << 30;
 constexpr int kFusedMaxT = 128;
+// one token tile per weight tile: the GEMM quantizes its weight tiles itself
+// instead of a quantize pass writing W_hat (with two token tiles the tile
+// would be quantized twice, which costs as much as the pass it replaces)
+constexpr int64_t kGemmQMaxT = 256;
 
 constexpr size_t kGemvLdsMax = 128 * 1024;
 
@@ -35,7 +39,8 @@ constexpr uint32_t known_flags() {
 }
 
 struct Plan {
-  int path = 0;          // 0 fused, 1 two-phase, 2 single launch (T = 1)
+  int path = 0;          // 0 fused, 1 two-phase, 2 single launch (T = 1),
+                         // 3 two-phase with quantization inside the GEMM
   int ntb = 1;           // fused: 16-token blocks (power of two)
   int G = 0;             // groups per row
   int planes = 1;        // fused: activation planes (2 = bf16 hi + lo)
@@ -151,6 +156,11 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     if (P.rchunk > R) P.rchunk = R;
     P.off_what = take((size_t)(per * P.rchunk));
     if (P.rp > 0 && T > 0) plan_z_split(P, R * T, d, take);
+    // (W_hat stays in the plan: a call that asks for the codes takes the
+    // quantize pass)
+    if (T <= kGemmQMaxT && gemm_q_supported(d, prm->group) &&
+        !(prm->flags & TTQ_FLAG_FORCE_TWO_PHASE))
+      P.path = 3;
   }
   P.total = off;
   return P;
@@ -173,7 +183,7 @@ TimingState g_timing;
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
-    "qgemv", "dequant", "qfused", "lowrank_zsum"};
+    "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -358,6 +368,19 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
   if (P.rp > 0) {
     st = enqueue_z_gemm(P, ws, Xb, Ab, R * T, d, rank, Zb, s);
     if (st != TTQ_OK) return st;
+  }
+  if (P.path == 3 && !codes_out && !scales_out) {
+    // every request in one launch, each with its own statistics
+    GemmQArgs qa{};
+    qa.X = Xb; qa.ldx = d; qa.W = Wb; qa.ldw = d;
+    qa.dh = dh; qa.dhi = dhi; qa.Nf = Nf; qa.K1 = d;
+    if (P.rp > 0) {
+      qa.A2 = Zb; qa.lda2 = P.rp; qa.B2 = Bb; qa.ldb2 = rank; qa.K2 = rank;
+    }
+    qa.M = T; qa.N = dout; qa.C = Y; qa.ldc = dout;
+    qa.batch = (int)R;
+    qa.sX = T * d; qa.sA2 = T * P.rp; qa.sC = T * dout;
+    return run(K_GEMM_Q, s, [&](const Launch& L) { return launch_gemm_q(qa, prm->group, L); });
   }
   // requests in chunks of P.rchunk: one quantize pass (each request its own
   // W_hat), then one batched GEMM launch per chunk

@@ -30,6 +30,7 @@ enum KernelKind {
   K_DEQUANT,           // stored packed codes -> W_hat
   K_QFUSED,            // stored packed codes x 2..128 tokens
   K_LOWRANK_ZSUM,      // ordered sum of the small-M low-rank partials
+  K_GEMM_Q,            // projection GEMM quantizing the weight tiles itself
   K_NUM_KINDS
 };
 
@@ -40,14 +41,17 @@ __device__ __forceinline__ float bf16lo(unsigned v) {
 __device__ __forceinline__ float bf16hi(unsigned v) {
   return __uint_as_float(v & 0xffff0000u);
 }
-// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ unsigned f2bf(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN), with the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).  Every kernel rounds
+// through these two, so equal float32 values give equal bf16 bits on every
+// path.
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2){lo, hi}, b2));
+}
+__device__ __forceinline__ unsigned f2bf(float f) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 // Raw buffer loads: a resource descriptor bounds the addressable range, and a
@@ -76,6 +80,15 @@ __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r,
 // Used to order a small dependent read ahead of a large batch of loads.
 __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Workgroup barrier for kernels that fill LDS with buffer_load ... lds:
+// this wave's LDS accesses are complete (lgkmcnt 0), then s_barrier.  The
+// direct-to-LDS loads are waited for explicitly through vmcnt, stage by
+// stage; __syncthreads() would also wait for every such load in flight
+// (vmcnt 0), which leaves a multi-stage load pipeline one stage deep.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // scalar offset that puts a load out of range (no wrap-around: the lane
@@ -302,6 +315,31 @@ hipError_t launch_gemm(const GemmArgs& a, const Launch& L);
 // 1 = 256 x 128 tiles.
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L);
 int gemm_lds_config(int64_t M, int64_t N, int64_t batch);
+
+// Projection GEMM with the weight operand quantized in the kernel:
+//   C[M][N] = X[M][K1] * W_hat[N][K1]^T  +  A2[M][K2] * B2[N][K2]^T
+// where W_hat = bf16((m + s q) D^{-1/2}) is formed from the bf16 weights W and
+// the product's D^{+-1/2} tile by tile, with the same float32 decisions as
+// the quantize pass (the results are identical to quantize pass + GEMM).
+// Products of a batch share W and have their own X, D^{+-1/2}, A2 and C.
+struct GemmQArgs {
+  const bf16_t* X; int64_t ldx;
+  const bf16_t* W; int64_t ldw;
+  const float* dh;      // [batch][K1]
+  const float* dhi;     // [batch][K1]
+  float Nf;             // 2^bits - 1
+  int64_t K1;
+  const bf16_t* A2; int64_t lda2;   // optional low-rank segment
+  const bf16_t* B2; int64_t ldb2;
+  int64_t K2;
+  int64_t M, N;
+  float* C; int64_t ldc;
+  int batch;
+  int64_t sX, sA2, sC;  // per-product strides (elements); D^{+-1/2}: K1
+};
+hipError_t launch_gemm_q(const GemmQArgs& a, int group, const Launch& L);
+// K1 a multiple of 128 and groups of 32, 64 or 128 channels
+bool gemm_q_supported(int64_t K1, int group);
 
 // out[i] = bf16(sum_{z<nsplit} part[z*n + i]) in split order, n % 4 == 0
 struct SplitReduceArgs {

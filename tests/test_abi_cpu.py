@@ -176,7 +176,12 @@ def test_path_selection():
     assert ttq.ttq_path(prm(T=1, flags=ttq.TTQ_FLAG_FORCE_FUSED)) == 0
     assert ttq.ttq_path(prm(T=2)) == 0
     assert ttq.ttq_path(prm(T=128)) == 0
-    assert ttq.ttq_path(prm(T=129)) == 1
+    assert ttq.ttq_path(prm(T=129)) == 3
+    assert ttq.ttq_path(prm(T=256)) == 3
+    assert ttq.ttq_path(prm(T=257)) == 1
+    assert ttq.ttq_path(prm(T=129, group=256)) == 1
+    assert ttq.ttq_path(prm(T=129, d=192, group=64)) == 1
+    assert ttq.ttq_path(prm(T=129, flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE)) == 1
     assert ttq.ttq_path(prm(T=2048)) == 1
     assert ttq.ttq_path(prm(T=2048, flags=ttq.TTQ_FLAG_FORCE_FUSED & 0)) == 1
     assert ttq.ttq_path(prm(T=64, flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE)) == 1

@@ -125,6 +125,48 @@ def test_gemm_more_tiles_than_cus(R):
     _say(f"tail_R{R}", rep)
 
 
+GEMM_Q_CASES = [
+    # the GEMM that quantizes its own weight tiles (129 <= T <= 256): every
+    # group size, ragged token / row tiles, low-rank segments of one, two and
+    # four k-tiles (ragged rank), the shortest channel range (one chunk), an
+    # odd number of chunks, batched requests
+    ("gq_g128", dict(d=1024, d_out=1040, T=200, bits=4, group=128,
+                     x_kind="logu10_100", n_outliers=10, seed=41)),
+    ("gq_g64_r128_p1", dict(d=1024, d_out=896, T=256, bits=2, group=64,
+                            rank=128, p=1.0, lam=1e-2, x_kind="t3_logu30_100",
+                            n_outliers=5, seed=42)),
+    ("gq_g32_r72", dict(d=384, d_out=200, T=129, bits=3, group=32, rank=72,
+                        seed=43)),
+    ("gq_d128_r200", dict(d=128, d_out=130, T=250, bits=5, group=64,
+                          rank=200, seed=44)),
+    ("gq_b8_r8", dict(d=640, d_out=136, T=200, bits=8, group=128, rank=8,
+                      seed=45)),
+    ("gq_b1_g32", dict(d=256, d_out=64, T=140, bits=1, group=32, seed=46)),
+    ("gq_R3_r32", dict(d=512, d_out=272, T=256, R=3, bits=4, group=128,
+                       rank=32, x_kind="logu10_100", n_outliers=5, seed=47)),
+]
+
+
+@pytest.mark.parametrize("name,kw", GEMM_Q_CASES, ids=[c[0] for c in GEMM_Q_CASES])
+def test_gemm_quant_path(name, kw):
+    """Y of the in-GEMM quantization equals that of the quantize pass + GEMM
+    bit for bit (same float32 decisions, same bf16 rounding, same MFMA
+    accumulation order) and meets the oracle's bars."""
+    import online_activation_aware_ttq_amd as ttq
+    prob = make_problem(name, **kw)
+    prm = ttq.make_params(d=prob.d, d_out=prob.d_out, T=prob.T, rank=prob.rank,
+                          bits=prob.bits, group=prob.group, p=prob.p,
+                          lam=prob.lam, alpha=prob.alpha)
+    assert ttq.ttq_path(prm, prob.R) == 3
+    print(f"[case] {name} gemm_quant vs two-phase", flush=True)
+    g3 = run_gpu(prob, flags=0, exports=False)
+    g1 = run_gpu(prob, flags=TWO, exports=False)
+    diff = g3["Y"] != g1["Y"]
+    assert not diff.any(), f"{int(diff.sum())} outputs differ from the two-phase path"
+    rep = check_problem(prob, g3, check_codes=False)
+    _say(name, rep)
+
+
 def test_batched_matches_single_calls():
     prob = make_problem("bs", d=512, d_out=160, T=4, R=3, bits=4, group=128,
                         rank=16, seed=31)
