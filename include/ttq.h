@@ -129,6 +129,40 @@ int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
                        float* scales_out, float* mins_out, float* dhalf_out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- continuous batching: requests of different lengths in one X --------
+ * n_segments requests packed one after another: request i owns the token
+ * rows seg_offsets[i] .. seg_offsets[i+1]-1 of X [T][d] and Y [T][d_out],
+ * where prm->T is the total token count.  The pages leave open how scales
+ * are derived when one batch mixes requests ("Test-time quantization:
+ * quantising on the fly with no calibration dataset", lo0 blog, section "What
+ * we have not covered"); here every request keeps its own statistics D, as
+ * in ttq_linear_batched, and its codes, scales and Y rows equal those of
+ * ttq_linear on that request alone, bit for bit (with a low-rank term, up to
+ * 64 MiB of low-rank partial sums per batch).
+ *   seg_offsets  host array of n_segments + 1 non-decreasing token offsets,
+ *                seg_offsets[0] = 0, seg_offsets[n_segments] = prm->T;
+ *                empty requests (equal offsets) are allowed
+ *   optional outputs gain a leading [n_segments] dimension, as in
+ *   ttq_linear_batched; all other arguments as for ttq_linear.
+ * The requests of one length class (1; 2..16; 17..32; 33..64; 65..128
+ * tokens; up to 64 at a time) are computed as one batch, shorter ones padded
+ * with zero tokens (which leave the norms unchanged) through workspace copies
+ * unless the batch is a run of consecutive requests of one length; when codes,
+ * scales or D^{1/2} are asked for, a batch takes only consecutive requests.
+ * Longer requests, or any request when a path flag is set, run alone.
+ * n_segments = 0 is a no-op.
+ * Errors: TTQ_ENULL for a NULL seg_offsets (n_segments > 0); TTQ_EINVAL for
+ * offsets that do not start at 0, end at prm->T or decrease, and for the
+ * conditions of ttq_linear_batched. */
+int ttq_segmented_workspace_bytes(const ttq_params* prm, int64_t n_segments,
+                                  const int64_t* seg_offsets, size_t* bytes);
+int ttq_linear_segmented(const ttq_params* prm, int64_t n_segments,
+                         const int64_t* seg_offsets, const void* W,
+                         const void* X, const void* B, const void* A, float* Y,
+                         uint8_t* codes_out, float* scales_out, float* mins_out,
+                         float* dhalf_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Which path a call with these parameters takes: 0 = fused single pass over
  * W (statistics kernel + one fused quantize/MFMA kernel), 1 = two phase
  * (statistics, quantize pass writing W_hat, MFMA GEMM), 2 = single launch

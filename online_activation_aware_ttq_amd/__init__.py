@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     timing_reset,
     ttq_linear,
     ttq_linear_batched,
+    ttq_linear_segmented,
+    ttq_segmented_workspace_bytes,
     ttq_params,
     ttq_packed_row_bytes,
     ttq_path,

@@ -36,6 +36,11 @@ EXPORTS = {
                                       _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
                                       _vp]),
     "ttq_path": (_c.c_int, [_vp, _c.c_int64]),
+    "ttq_segmented_workspace_bytes": (_c.c_int, [_vp, _c.c_int64, _vp,
+                                                 _c.POINTER(_c.c_size_t)]),
+    "ttq_linear_segmented": (_c.c_int, [_vp, _c.c_int64, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _c.c_size_t, _vp]),
     "ttq_packed_row_bytes": (_c.c_int, [_vp, _c.POINTER(_c.c_int64)]),
     "ttq_quantize_workspace_bytes": (_c.c_int, [_vp, _c.POINTER(_c.c_size_t)]),
     "ttq_qmatmul_workspace_bytes": (_c.c_int, [_vp, _c.POINTER(_c.c_size_t)]),
@@ -226,6 +231,68 @@ def ttq_linear_batched(W, X, B=None, A=None, *, p: float, lam: float,
                  group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
                  mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
                  stream=stream, flags=flags)
+
+
+def _offsets(seg_offsets):
+    arr = (ctypes.c_int64 * len(seg_offsets))(*[int(v) for v in seg_offsets])
+    return arr, len(seg_offsets) - 1
+
+
+def ttq_segmented_workspace_bytes(prm: ttq_params, seg_offsets) -> int:
+    arr, n = _offsets(seg_offsets)
+    out = ctypes.c_size_t(0)
+    st = load_library().ttq_segmented_workspace_bytes(
+        ctypes.byref(prm), n, ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(out))
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_segmented_workspace_bytes")
+    return int(out.value)
+
+
+def ttq_linear_segmented(W, X, B=None, A=None, *, seg_offsets, p: float,
+                         lam: float, alpha: float, bits: int, group: int,
+                         Y=None, codes_out=None, scales_out=None, mins_out=None,
+                         dhalf_out=None, workspace=None, stream=None,
+                         flags: int = 0):
+    """Requests of different lengths packed in X [T, d]: request i owns rows
+    seg_offsets[i] .. seg_offsets[i+1]-1 and has its own statistics."""
+    import torch
+    T, d = X.shape
+    d_out = W.shape[0]
+    rank = 0 if A is None else A.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("W must be a GPU tensor")
+    n = len(seg_offsets) - 1
+    G = d // group if group > 0 and d % group == 0 else 0
+    _check(W, "W", torch.bfloat16, (d_out, d), dev)
+    _check(X, "X", torch.bfloat16, (T, d), dev)
+    _check(B, "B", torch.bfloat16, (d_out, rank), dev)
+    _check(A, "A", torch.bfloat16, (rank, d), dev)
+    if (A is None) != (B is None):
+        raise ValueError("pass both B and A or neither")
+    prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
+                      group=group, p=p, lam=lam, alpha=alpha, flags=flags)
+    need = ttq_segmented_workspace_bytes(prm, seg_offsets)
+    if Y is None:
+        Y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
+    _check(Y, "Y", torch.float32, (T, d_out), dev)
+    _check(codes_out, "codes_out", torch.uint8, (n, d_out, d), dev)
+    _check(scales_out, "scales_out", torch.float32, (n, d_out, G), dev)
+    _check(mins_out, "mins_out", torch.float32, (n, d_out, G), dev)
+    _check(dhalf_out, "dhalf_out", torch.float32, (n, d), dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    arr, _ = _offsets(seg_offsets)
+    st = load_library().ttq_linear_segmented(
+        ctypes.byref(prm), n, ctypes.cast(arr, ctypes.c_void_p), _ptr(W),
+        _ptr(X), _ptr(B), _ptr(A), _ptr(Y), _ptr(codes_out), _ptr(scales_out),
+        _ptr(mins_out), _ptr(dhalf_out), _ptr(workspace), workspace.numel(),
+        stream)
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_linear_segmented")
+    return Y
 
 
 # ------------------------------------------- quantize once, decode from codes

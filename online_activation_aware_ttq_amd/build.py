@@ -34,6 +34,7 @@ SOURCES = [
     "k_qgemv.hip",
     "k_qfused.hip",
     "k_gemm_q.hip",
+    "k_segment.hip",
     "ttq_api.cpp",
 ]
 

@@ -115,13 +115,16 @@ __global__ __launch_bounds__(256) void k_lowrank_zsum(LowRankZArgs a, int nsplit
 
 // channel slices: about 128 workgroups, each over at least 256 channels
 // (the slices are summed by a second kernel; few of them keep it short)
+// Channel slices of about 256 channels, fixed by d alone as long as the fp32
+// partials fit in 64 MiB: the slices and the order of their sum, hence every
+// bit of a token's Z, then do not depend on how many tokens or requests
+// share the launch.
 int lowrank_z_splits(int64_t M, int64_t d, int rp) {
-  const int64_t blocks = ((M + 15) / 16) * ((rp + 16 * ZTILES - 1) / (16 * ZTILES));
-  int64_t s = (128 + blocks - 1) / blocks;
-  const int64_t smax = (d + 255) / 256;
-  if (s > smax) s = smax;
-  if (s < 1) s = 1;
-  return (int)s;
+  int64_t s = (d + 255) / 256;
+  const int64_t per = (M > 0 ? M : 1) * (rp > 0 ? rp : 1) * (int64_t)sizeof(float);
+  const int64_t cap = (int64_t(64) << 20) / per;
+  if (s > cap) s = cap;
+  return (int)(s < 1 ? 1 : s);
 }
 
 hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L) {

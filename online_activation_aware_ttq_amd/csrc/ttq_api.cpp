@@ -3,6 +3,7 @@
 // plain host code; the arithmetic of the method runs in the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -183,7 +184,7 @@ TimingState g_timing;
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
-    "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant"};
+    "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant", "seg_copy"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -648,6 +649,183 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
   return run(K_GEMM, s, [&](const Launch& L) { return launch_gemm_lds(ga, L); });
 }
 
+// ------------------------------------------------- continuous batching
+// Requests of different lengths packed in one X [sum T_r][d] (see
+// k_segment.hip).  Requests of one length class are computed as one batched
+// call: a class groups the lengths that run the same kernels with the same
+// per-token arithmetic (1; 2..16; 17..32; 33..64; 65..128), padded with zero
+// tokens to the longest request of the batch; longer requests run alone at
+// their own length.  Each request's D, codes and Y rows are then those of the
+// request alone.  Without exports a batch takes every request of its class;
+// with exports (written in request order) only runs of consecutive requests.
+int64_t seg_class(int64_t T) {
+  if (T <= 1) return T;
+  if (T <= 16) return 16;
+  if (T <= kFusedMaxT) {
+    int64_t c = 32;
+    while (c < T) c *= 2;
+    return c;
+  }
+  return -1;  // alone, at its own length
+}
+
+struct SegBatch {
+  std::vector<int64_t> seg;  // requests, in request order
+  int64_t Tpad = 0;
+  bool direct = false;       // consecutive requests of length Tpad: no copies
+  size_t ws = 0;             // workspace of the batched call
+  size_t xpad = 0, ypad = 0;
+};
+
+int check_offsets(const ttq_params* prm, int64_t n_seg, const int64_t* off) {
+  if (n_seg < 0 || n_seg > kMaxR * 64) return TTQ_EINVAL;
+  if (n_seg > 0 && !off) return TTQ_ENULL;
+  const int st = validate_params(prm, 1);
+  if (st != TTQ_OK) return st;
+  if (n_seg > 0 && (off[0] != 0 || off[n_seg] != prm->T)) return TTQ_EINVAL;
+  for (int64_t i = 0; i < n_seg; ++i)
+    if (off[i + 1] < off[i]) return TTQ_EINVAL;
+  return TTQ_OK;
+}
+
+int plan_segments(const ttq_params* prm, int64_t n_seg, const int64_t* off,
+                  bool by_class, std::vector<SegBatch>* out, size_t* total) {
+  // a path flag: every request alone (the flag fixes its kernels)
+  const bool alone = (prm->flags & known_flags()) != 0;
+  auto len = [&](int64_t i) { return off[i + 1] - off[i]; };
+  auto cls = [&](int64_t i) { return alone ? -1 : seg_class(len(i)); };
+  std::vector<SegBatch> batches;
+  std::vector<bool> taken((size_t)n_seg, false);
+  for (int64_t i = 0; i < n_seg; ++i) {
+    if (taken[(size_t)i]) continue;
+    const int64_t c = cls(i);
+    SegBatch b;
+    b.seg.push_back(i);
+    taken[(size_t)i] = true;
+    if (c > 0) {
+      for (int64_t k = i + 1; k < n_seg && (int64_t)b.seg.size() < kSegMax; ++k) {
+        if (taken[(size_t)k]) continue;
+        if (cls(k) != c) {
+          if (by_class) continue;
+          break;
+        }
+        b.seg.push_back(k);
+        taken[(size_t)k] = true;
+      }
+    }
+    batches.push_back(std::move(b));
+  }
+  size_t need = 0;
+  for (SegBatch& b : batches) {
+    const int64_t n = (int64_t)b.seg.size();
+    b.Tpad = 0;
+    for (int64_t k : b.seg) b.Tpad = std::max(b.Tpad, len(k));
+    b.direct = true;
+    for (int64_t j = 0; j < n; ++j)
+      if (b.seg[(size_t)j] != b.seg[0] + j || len(b.seg[(size_t)j]) != b.Tpad)
+        b.direct = false;
+    ttq_params q = *prm;
+    q.T = b.Tpad;
+    const int st = validate_params(&q, n);
+    if (st != TTQ_OK) return st;
+    b.ws = make_plan(&q, n).total;
+    if (!b.direct) {
+      b.xpad = align_up(sizeof(uint16_t) * n * b.Tpad * prm->d, 256);
+      b.ypad = align_up(sizeof(float) * n * b.Tpad * prm->d_out, 256);
+    }
+    need = std::max(need, align_up(b.ws, 256) + b.xpad + b.ypad);
+  }
+  if (out) *out = std::move(batches);
+  *total = need;
+  return TTQ_OK;
+}
+
+// workspace for either kind of call (with or without exports)
+int segmented_workspace(const ttq_params* prm, int64_t n_seg,
+                        const int64_t* off, size_t* total) {
+  int st = check_offsets(prm, n_seg, off);
+  if (st != TTQ_OK) return st;
+  size_t a = 0, b = 0;
+  st = plan_segments(prm, n_seg, off, true, nullptr, &a);
+  if (st != TTQ_OK) return st;
+  st = plan_segments(prm, n_seg, off, false, nullptr, &b);
+  if (st != TTQ_OK) return st;
+  *total = std::max(a, b);
+  return TTQ_OK;
+}
+
+int segmented_impl(const ttq_params* prm, int64_t n_seg, const int64_t* off,
+                   const void* W, const void* X, const void* B, const void* A,
+                   float* Y, uint8_t* codes_out, float* scales_out,
+                   float* mins_out, float* dhalf_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  int st = segmented_workspace(prm, n_seg, off, &need);
+  if (st != TTQ_OK) return st;
+  if (n_seg == 0) return TTQ_OK;
+  const int64_t d = prm->d, dout = prm->d_out, G = d / prm->group;
+  if (dout > 0 && !W) return TTQ_ENULL;
+  if (prm->T > 0 && !X) return TTQ_ENULL;
+  if (prm->T > 0 && dout > 0 && !Y) return TTQ_ENULL;
+  if ((scales_out == nullptr) != (mins_out == nullptr)) return TTQ_EINVAL;
+  if (misaligned(workspace, 256)) return TTQ_EALIGN;
+  if (need > 0 && !workspace) return TTQ_ENULL;
+  if (workspace_bytes < need) return TTQ_EWORKSPACE;
+  const bool exports = codes_out || scales_out || mins_out || dhalf_out;
+  std::vector<SegBatch> batches;
+  size_t unused = 0;
+  st = plan_segments(prm, n_seg, off, !exports, &batches, &unused);
+  if (st != TTQ_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bf16_t* Xb = static_cast<const bf16_t*>(X);
+  for (const SegBatch& b : batches) {
+    const int64_t n = (int64_t)b.seg.size(), s0 = b.seg[0];
+    if (b.Tpad == 0 && !exports) continue;  // empty requests, nothing asked
+    ttq_params q = *prm;
+    q.T = b.Tpad;
+    // exports only with runs of consecutive requests: slots s0 .. s0 + n - 1
+    uint8_t* co = codes_out ? codes_out + s0 * dout * d : nullptr;
+    float* so = scales_out ? scales_out + s0 * dout * G : nullptr;
+    float* mo = mins_out ? mins_out + s0 * dout * G : nullptr;
+    float* dho = dhalf_out ? dhalf_out + s0 * d : nullptr;
+    void* bws = b.ws > 0 ? ws : nullptr;
+    if (b.direct) {
+      st = linear_impl(&q, n, W, b.Tpad > 0 ? Xb + off[s0] * d : nullptr, B, A,
+                       Y ? Y + off[s0] * dout : nullptr, co, so, mo, dho, bws,
+                       b.ws, stream);
+      if (st != TTQ_OK) return st;
+      continue;
+    }
+    const size_t inner = align_up(b.ws, 256);
+    bf16_t* xpad = reinterpret_cast<bf16_t*>(ws + inner);
+    float* ypad = reinterpret_cast<float*>(ws + inner + b.xpad);
+    SegCopyArgs ca{};
+    ca.n = (int)n;
+    ca.Tpad = b.Tpad;
+    for (int64_t k = 0; k < n; ++k) {
+      ca.off[k] = off[b.seg[(size_t)k]];
+      ca.len[k] = off[b.seg[(size_t)k] + 1] - off[b.seg[(size_t)k]];
+    }
+    ca.src = Xb;
+    ca.dst = xpad;
+    ca.row_bytes = d * (int64_t)sizeof(uint16_t);
+    ca.scatter = 0;
+    st = run(K_SEG_COPY, s, [&](const Launch& L) { return launch_seg_copy(ca, L); });
+    if (st != TTQ_OK) return st;
+    st = linear_impl(&q, n, W, xpad, B, A, ypad, co, so, mo, dho, bws, b.ws, stream);
+    if (st != TTQ_OK) return st;
+    if (dout == 0) continue;
+    ca.src = ypad;
+    ca.dst = Y;
+    ca.row_bytes = dout * (int64_t)sizeof(float);
+    ca.scatter = 1;
+    st = run(K_SEG_COPY, s, [&](const Launch& L) { return launch_seg_copy(ca, L); });
+    if (st != TTQ_OK) return st;
+  }
+  return TTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -676,6 +854,23 @@ int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
                        void* workspace, size_t workspace_bytes, void* stream) {
   return linear_impl(prm, n_requests, W, X, B, A, Y, codes_out, scales_out,
                      mins_out, dhalf_out, workspace, workspace_bytes, stream);
+}
+
+int ttq_segmented_workspace_bytes(const ttq_params* prm, int64_t n_segments,
+                                  const int64_t* seg_offsets, size_t* bytes) {
+  if (!bytes) return TTQ_ENULL;
+  return segmented_workspace(prm, n_segments, seg_offsets, bytes);
+}
+
+int ttq_linear_segmented(const ttq_params* prm, int64_t n_segments,
+                         const int64_t* seg_offsets, const void* W,
+                         const void* X, const void* B, const void* A, float* Y,
+                         uint8_t* codes_out, float* scales_out, float* mins_out,
+                         float* dhalf_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return segmented_impl(prm, n_segments, seg_offsets, W, X, B, A, Y, codes_out,
+                        scales_out, mins_out, dhalf_out, workspace,
+                        workspace_bytes, stream);
 }
 
 int ttq_path(const ttq_params* prm, int64_t n_requests) {

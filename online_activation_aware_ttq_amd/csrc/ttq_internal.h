@@ -31,6 +31,7 @@ enum KernelKind {
   K_QFUSED,            // stored packed codes x 2..128 tokens
   K_LOWRANK_ZSUM,      // ordered sum of the small-M low-rank partials
   K_GEMM_Q,            // projection GEMM quantizing the weight tiles itself
+  K_SEG_COPY,          // row copies for requests of different lengths
   K_NUM_KINDS
 };
 
@@ -340,6 +341,21 @@ struct GemmQArgs {
 hipError_t launch_gemm_q(const GemmQArgs& a, int group, const Launch& L);
 // K1 a multiple of 128 and groups of 32, 64 or 128 channels
 bool gemm_q_supported(int64_t K1, int group);
+
+// Row copies between a packed multi-request array and a padded batch (see
+// k_segment.hip).  Rows are row_bytes long (a multiple of 4).
+constexpr int kSegMax = 64;  // requests per copy launch
+struct SegCopyArgs {
+  const void* src;
+  void* dst;
+  int64_t row_bytes;
+  int64_t Tpad;             // rows per request in the padded batch
+  int n;                    // requests in this launch
+  int scatter;              // 0: packed -> padded (zero fill), 1: padded -> packed
+  int64_t off[kSegMax];     // first row of request r in the packed array
+  int64_t len[kSegMax];     // rows of request r
+};
+hipError_t launch_seg_copy(const SegCopyArgs& a, const Launch& L);
 
 // out[i] = bf16(sum_{z<nsplit} part[z*n + i]) in split order, n % 4 == 0
 struct SplitReduceArgs {

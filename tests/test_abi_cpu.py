@@ -319,3 +319,64 @@ def test_packed_calls_report_injected_hip_error(monkeypatch):
     monkeypatch.setenv("TTQ_INJECT_HIP_ERROR", "1")
     assert call_quantize(prm()) == ttq.TTQ_EHIP
     assert call_qmatmul(prm()) == ttq.TTQ_EHIP
+
+
+# ---------------------------------------------- requests of different lengths
+def _offs(*v):
+    arr = (ctypes.c_int64 * len(v))(*v)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def seg_ws(p, offsets):
+    ptr, _keep = _offs(*offsets)
+    out = ctypes.c_size_t(0)
+    st = lib().ttq_segmented_workspace_bytes(ctypes.byref(p), len(offsets) - 1,
+                                             ptr, ctypes.byref(out))
+    return st, out.value
+
+
+def call_segmented(p, offsets, ws_bytes=1 << 40, n=None, Y=FAKE, ws=FAKE):
+    ptr, _keep = _offs(*offsets) if offsets is not None else (None, None)
+    n = len(offsets) - 1 if n is None else n
+    return lib().ttq_linear_segmented(ctypes.byref(p), n, ptr, FAKE, FAKE,
+                                      None, None, Y, None, None, None, None,
+                                      ws, ws_bytes, None)
+
+
+def test_segmented_offsets_validated():
+    p = prm(T=7)
+    assert seg_ws(p, [0, 3, 7])[0] == ttq.TTQ_OK
+    assert seg_ws(p, [1, 3, 7])[0] == ttq.TTQ_EINVAL       # does not start at 0
+    assert seg_ws(p, [0, 3, 6])[0] == ttq.TTQ_EINVAL       # does not end at T
+    assert seg_ws(p, [0, 5, 3, 7])[0] == ttq.TTQ_EINVAL    # decreasing
+    assert call_segmented(p, None, n=2) == ttq.TTQ_ENULL
+    assert call_segmented(p, [0, 5, 3, 7]) == ttq.TTQ_EINVAL
+    assert call_segmented(prm(T=7, bits=0), [0, 3, 7]) == ttq.TTQ_EINVAL
+
+
+def test_segmented_no_requests_is_a_no_op():
+    p = prm(T=0)
+    assert seg_ws(p, [0]) == (ttq.TTQ_OK, 0)
+    assert call_segmented(p, [0], ws=None, ws_bytes=0) == ttq.TTQ_OK
+
+
+def test_segmented_workspace_plan():
+    # equal lengths, consecutive: one batched call, no copies
+    p = prm(T=3)
+    st, need = seg_ws(p, [0, 1, 2, 3])
+    assert st == ttq.TTQ_OK and need == ttq.ttq_workspace_bytes(prm(T=1), 3)
+    # 1 token, then 5 and 16 tokens (one run, padded to 16 through copies)
+    p = prm(T=22)
+    st, need = seg_ws(p, [0, 1, 6, 22])
+    batch = ttq.ttq_workspace_bytes(prm(T=16), 2)
+    assert st == ttq.TTQ_OK and need > batch
+    # a path flag: every request alone at its own length
+    p = prm(T=22, flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE)
+    st, need = seg_ws(p, [0, 1, 6, 22])
+    alone = max(ttq.ttq_workspace_bytes(prm(T=t, flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE), 1)
+                for t in (1, 5, 16))
+    assert st == ttq.TTQ_OK and need == alone
+    # the call checks the workspace against the plan before any launch
+    st, need = seg_ws(prm(T=22), [0, 1, 6, 22])
+    assert call_segmented(prm(T=22), [0, 1, 6, 22], ws_bytes=need - 1) == ttq.TTQ_EWORKSPACE
+    assert call_segmented(prm(T=22), [0, 1, 6, 22], Y=None) == ttq.TTQ_ENULL
