@@ -218,9 +218,10 @@ int ttq_quantize(const ttq_params* prm, const void* W, const void* X,
  * ttq_linear.  p, lambda, alpha and TTQ_FLAG_FORCE_FUSED are not used;
  * Routes: T = 1, a single kernel over the codes (unless x D^{-1/2} of the
  * token does not fit 128 KiB of LDS: d above about 30000); T <= 128, the
- * codes on the matrix cores; otherwise the codes are expanded to bf16
- * weights and multiplied on the matrix cores.  TTQ_FLAG_FORCE_TWO_PHASE
- * takes that last route at any T. */
+ * codes on the matrix cores; otherwise a GEMM that expands the codes to
+ * bf16 weights tile by tile in LDS (d a multiple of 128), else a pass that
+ * writes the expanded weights followed by a GEMM.  TTQ_FLAG_FORCE_TWO_PHASE
+ * takes that last route at any T; both expansions give the same Y bits. */
 int ttq_qmatmul(const ttq_params* prm, const uint8_t* codes,
                 const float* scales, const float* mins, const float* dhalf_inv,
                 const void* X, const void* B, const void* A, float* Y,

@@ -171,7 +171,53 @@ __device__ __forceinline__ void quant_job(const u32x4 (&wv)[2],
   store_what(chunk, 1, r, p, J.dequant(1, dhi, Nf));
 }
 
-template <int GS>
+// Inputs of one job of a lane, one ring slot: bf16 weights (CB = 0) or
+// codes of CB-bit containers with their group's scale and minimum (CB > 0),
+// for the two k-tile halves.
+template <int CB>
+struct JobIn {
+  u32x4 w[2];
+  unsigned c[2][CB == 8 ? 2 : 1];
+  float s[2], m[2];
+  f32x4 s4, m4;  // groups of 32: the four groups of the chunk row
+};
+
+// Stored codes -> W_hat of half h: bf16((m + s q) D^{-1/2}), the expansion
+// of the quantize-once storage ("TTQ: Activation-Aware Test-Time
+// Quantization ...", nl summary, Sec. 2: statistics per prompt, weights
+// stored quantized), with the float32 operations of the dequantize pass.
+template <int CB, int GS>
+__device__ __forceinline__ u32x4 dequant_half(const JobIn<CB>& J, int h,
+                                              const f32x4 (&dhi)[4], int p) {
+  float sg, mg;
+  if constexpr (GS == 32) {  // group 2h + p/4 of the chunk row
+    const bool odd = p & 4;
+    sg = odd ? J.s4[2 * h + 1] : J.s4[2 * h];
+    mg = odd ? J.m4[2 * h + 1] : J.m4[2 * h];
+  } else {
+    sg = J.s[h];
+    mg = J.m[h];
+  }
+  float wq[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    unsigned code;
+    if constexpr (CB == 8) code = (J.c[h][e >> 2] >> ((e & 3) * 8)) & 0xffu;
+    else code = __builtin_amdgcn_ubfe(J.c[h][0], e * CB, CB);
+    const f32x4 di = dhi[2 * h + (e >> 2)];
+    wq[e] = fmaf(sg, (float)code, mg) * di[e & 3];
+  }
+  u32x4 o;
+  o.x = pack_bf16(wq[0], wq[1]);
+  o.y = pack_bf16(wq[2], wq[3]);
+  o.z = pack_bf16(wq[4], wq[5]);
+  o.w = pack_bf16(wq[6], wq[7]);
+  return o;
+}
+
+// CB = 0: quantize bf16 weights with the request's D (path of ttq_linear);
+// CB = 1, 2, 4, 8: expand stored codes (path of ttq_qmatmul).
+template <int GS, int CB>
 __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
   if (blockIdx.y > 0) {  // product z of a batch
     const int64_t z = blockIdx.y;
@@ -218,7 +264,7 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
   const auto rx = make_rsrc(a.X + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
   const auto ra2 = make_rsrc(a.A2 ? a.A2 + m0 * a.lda2 : a.X,
                              a.A2 ? (uint32_t)(mrows * a.lda2 * 2) : 0u);
-  const auto rb2 = make_rsrc(a.B2 ? a.B2 + n0 * a.ldb2 : a.W,
+  const auto rb2 = make_rsrc(a.B2 ? a.B2 + n0 * a.ldb2 : a.X,
                              a.B2 ? (uint32_t)(nrows * a.ldb2 * 2) : 0u);
   // activation tile kt < nk1 (nothing at or past nk1) into stage st; the
   // tile's part of the offset is a scalar, so that no control flow splits
@@ -264,23 +310,74 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
           (uint32_t)(j * 8 * QNW * ld * 2), 0, 0);
   };
 
-  // ---- quantization jobs: job q covers row (q & 1)*64 + w*8 + l/8 of chunk
-  // q/2, channels 8p..8p+7 of both k-tile halves
+  // ---- weight jobs: job q covers row (q & 1)*64 + w*8 + l/8 of chunk q/2,
+  // channels 8p..8p+7 of both k-tile halves
   const int p = l & 7;
   const int jrow = w * 8 + (l >> 3);
-  const auto rw = make_rsrc(a.W + n0 * a.ldw, (uint32_t)(nrows * a.ldw * 2));
-  const auto rdh = make_rsrc(a.dh, (uint32_t)(a.K1 * 4));
+  const auto rdh = make_rsrc(a.dh, CB == 0 ? (uint32_t)(a.K1 * 4) : 0u);
   const auto rdhi = make_rsrc(a.dhi, (uint32_t)(a.K1 * 4));
-  const int ldw = __builtin_amdgcn_readfirstlane((int)a.ldw);
   // lane parts of the offsets; the job's part is a scalar (out of range past
   // the weights, so that every k-tile issues the same number of loads)
-  const uint32_t woff = (uint32_t)((jrow * ldw + p * 8) * 2);
   const uint32_t doff = (uint32_t)(p * 32);
-  auto load_w = [&](int q, u32x4 (&wv)[2]) {
-    const uint32_t so = q < nk1 ? (uint32_t)(((q & 1) * 64 * ldw + (q >> 1) * 128) * 2)
-                                : kOutOfRange;
+  auto load_job = [&](int q, JobIn<CB>& J) {
+    const bool in = q < nk1;
+    if constexpr (CB == 0) {
+      const auto rw = make_rsrc(a.W + n0 * a.ldw, (uint32_t)(nrows * a.ldw * 2));
+      const int ldw = __builtin_amdgcn_readfirstlane((int)a.ldw);
+      const uint32_t woff = (uint32_t)((jrow * ldw + p * 8) * 2);
+      const uint32_t so = in ? (uint32_t)(((q & 1) * 64 * ldw + (q >> 1) * 128) * 2)
+                             : kOutOfRange;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) wv[h] = buf_load16(rw, woff + so + h * 128, 0);
+      for (int h = 0; h < 2; ++h) J.w[h] = buf_load16(rw, woff + so + h * 128, 0);
+    } else {
+      const int rb = __builtin_amdgcn_readfirstlane((int)a.row_bytes);
+      const int G = __builtin_amdgcn_readfirstlane((int)a.G);
+      const auto rc = make_rsrc(a.packed + n0 * a.row_bytes, (uint32_t)(nrows * a.row_bytes));
+      const auto rs = make_rsrc(a.s + n0 * a.G, (uint32_t)(nrows * a.G * 4));
+      const auto rm = make_rsrc(a.m + n0 * a.G, (uint32_t)(nrows * a.G * 4));
+      // codes: channel c of row r at byte r * row_bytes + c * CB / 8
+      const uint32_t so = in ? (uint32_t)((q & 1) * 64 * rb + (q >> 1) * 16 * CB) : kOutOfRange;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = (uint32_t)(jrow * rb + p * CB + h * 8 * CB) + so;
+        if constexpr (CB == 8) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+          J.c[h][0] = v[0];
+          J.c[h][1] = v[1];
+        } else if constexpr (CB == 4) {
+          J.c[h][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0);
+        } else if constexpr (CB == 2) {
+          J.c[h][0] = __builtin_amdgcn_raw_buffer_load_b16(rc, off, 0, 0);
+        } else {
+          J.c[h][0] = __builtin_amdgcn_raw_buffer_load_b8(rc, off, 0, 0);
+        }
+      }
+      // group of channel (q/2)*128 + 64h + 8p: one group for both halves
+      // (GS >= 128), two adjacent ones (64: one 8-byte load), or groups
+      // 2h + p/4 of four (32)
+      const int gq = GS >= 128 ? (q >> 1) * 128 / GS : (q >> 1) * (128 / GS);
+      const uint32_t sso = in ? (uint32_t)(((q & 1) * 64 * G + gq) * 4) : kOutOfRange;
+      if constexpr (GS >= 128) {
+        const uint32_t off = (uint32_t)(jrow * G * 4) + sso;
+        J.s[0] = J.s[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        J.m[0] = J.m[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, off, 0, 0));
+      } else if constexpr (GS == 64) {
+        const uint32_t off = (uint32_t)(jrow * G * 4) + sso;
+        // (the whole vector is reinterpreted: a bit_cast of one lane of the
+        // loaded vector was compiled into a one-dword load of lane 0)
+        typedef __attribute__((ext_vector_type(2))) float f32x2;
+        const f32x2 sv = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        const f32x2 mv = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off, 0, 0));
+        J.s[0] = sv.x;
+        J.s[1] = sv.y;
+        J.m[0] = mv.x;
+        J.m[1] = mv.y;
+      } else {
+        const uint32_t off = (uint32_t)(jrow * G * 4) + sso;
+        J.s4 = __builtin_bit_cast(f32x4, buf_load16(rs, off, 0));
+        J.m4 = __builtin_bit_cast(f32x4, buf_load16(rm, off, 0));
+      }
+    }
   };
   auto load_dh = [&](int c, f32x4 (&dv)[4], f32x4 (&iv)[4]) {
     const uint32_t so = 2 * c < nk1 ? (uint32_t)(c * 512) : kOutOfRange;
@@ -289,10 +386,15 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint32_t off = doff + (uint32_t)(h * 256 + i * 16) + so;
-        dv[2 * h + i] = __builtin_bit_cast(f32x4, buf_load16(rdh, off, 0));
+        if constexpr (CB == 0)
+          dv[2 * h + i] = __builtin_bit_cast(f32x4, buf_load16(rdh, off, 0));
         iv[2 * h + i] = __builtin_bit_cast(f32x4, buf_load16(rdhi, off, 0));
       }
   };
+  // loads per k-tile: activation tile, scales of a chunk (even k-tiles), job
+  constexpr int NA = QBM / (8 * QNW);
+  constexpr int ND = CB == 0 ? 8 : 4;
+  constexpr int NJ = CB == 0 ? 2 : 4;
 
   // ---- MFMA part: wave (wm, wn) owns 64 tokens x 64 weight rows
   const int wm = w >> 1, wn = w & 1;
@@ -335,17 +437,27 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
     }
   };
 
-  // ---- prologue: chunk 0 quantized, activation tiles 0, 1 and the loads of
+  // ---- prologue: chunk 0 ready, activation tiles 0, 1 and the loads of
   // jobs 2..4 and of the scales of chunk 1 in flight
-  u32x4 wring[4][2];
+  JobIn<CB> ring[4];
   f32x4 dhv[2][4], dhiv[2][4];
+  // one job into the chunk buffer
+  auto job = [&](const JobIn<CB>& J, int ds, int r) {
+    unsigned char* chunk = sB + ds * QC_BYTES;
+    if constexpr (CB == 0) {
+      quant_job<GS>(J.w, dhv[ds], dhiv[ds], Nf, p, r, chunk);
+    } else {
+      store_what(chunk, 0, r, p, dequant_half<CB, GS>(J, 0, dhiv[ds], p));
+      store_what(chunk, 1, r, p, dequant_half<CB, GS>(J, 1, dhiv[ds], p));
+    }
+  };
   // (issue order fixed: the first wait below counts on it, and the weights
   // of jobs 2 and 3 are as old as those of later jobs at their use)
   load_dh(0, dhv[0], dhiv[0]);
-  load_w(0, wring[0]);
-  load_w(1, wring[1]);
-  load_w(2, wring[2]);
-  load_w(3, wring[3]);
+  load_job(0, ring[0]);
+  load_job(1, ring[1]);
+  load_job(2, ring[2]);
+  load_job(3, ring[3]);
   __builtin_amdgcn_sched_barrier(0);
   load_dh(1, dhv[1], dhiv[1]);
   __builtin_amdgcn_sched_barrier(0);
@@ -353,74 +465,94 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   issue_x(1, 1);
   __builtin_amdgcn_sched_barrier(0);
-  quant_job<GS>(wring[0], dhv[0], dhiv[0], Nf, p, jrow, sB);
-  quant_job<GS>(wring[1], dhv[0], dhiv[0], Nf, p, 64 + jrow, sB);
+  job(ring[0], 0, jrow);
+  job(ring[1], 0, 64 + jrow);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(4, wring[0]);
+  load_job(4, ring[0]);
 
   int sta = 0;  // activation stage of k-tile kt
-  // k-tile kt < nk1: wait for its activation tile, issue the loads two
-  // (activations) and three (weights) k-tiles ahead, run its MFMAs and the
-  // quantization job kt + 2 (chunk kt/2 + 1; the jobs nk1, nk1 + 1 past the
-  // weights quantize zeros into a chunk that the main loop does not read).
-  // POS = kt % 4 fixes the register sets: weights of job q in ring slot
-  // q % 4, scales of chunk c in set c % 2.
-  // k-tile kt < nk1: wait for its activation tile, run its MFMAs and the
-  // quantization job kt + 2 (chunk kt/2 + 1; the jobs nk1, nk1 + 1 past the
-  // weights quantize zeros into a chunk that the main loop does not read),
-  // then issue the loads two (activations) and three (weights) k-tiles
-  // ahead.  POS = kt % 4 fixes the register sets: weights of job q in ring
-  // slot q % 4, scales of chunk c in set c % 2.
+  // k-tile kt < nk1: wait for its activation tile, run its MFMAs and the job
+  // kt + 2 (chunk kt/2 + 1; the jobs nk1, nk1 + 1 past the weights write
+  // zeros into a chunk that the main loop does not read), then issue the
+  // loads two (activations) and three (weights) k-tiles ahead.  POS = kt % 4
+  // fixes the register sets: job q in ring slot q % 4, scales of chunk c in
+  // set c % 2.
   auto step = [&](int kt, auto pos_c) {
     constexpr int POS = decltype(pos_c)::value;
     constexpr int QS = (POS + 2) & 3;          // ring slot of job kt + 2
     constexpr int DS = (QS >> 1) & 1;          // its scale set and chunk
-    // Loads of k-tile kt in issue order: [activation tile: 4] then, in any
-    // order, [scales of a chunk: 8, even kt] [weights: 2].  The activation
-    // tile of kt (issued in k-tile kt - 2) is followed by at least 16 loads
-    // (6 in the prologue for tile 0).
-    if (kt == 0) wait_vm<6>();
-    else wait_vm<16>();
+    // Loads of k-tile kt in issue order: [activation tile: NA] then, in any
+    // order, [scales of a chunk: ND, even kt] [job: NJ].  The activation tile
+    // of kt (issued in k-tile kt - 2) is followed by at least NA + ND + 2 NJ
+    // loads (NA + NJ in the prologue for tile 0).
+    if (kt == 0) wait_vm<NA + NJ>();
+    else wait_vm<NA + ND + 2 * NJ>();
     lds_barrier();
     const unsigned char* sa = sA + sta * QA_BYTES;
     const unsigned char* sb =
         sB + ((POS >> 1) & 1) * QC_BYTES + (POS & 1) * QH_BYTES;
     // The four MFMA steps with the job's parts between them; fragment reads
-    // one step ahead.  LDS writes (quantized weights, direct loads) come after
-    // the last fragment read.
-    QuantJob<GS> J;
+    // one step ahead.  LDS writes (weights, direct loads) come after the last
+    // fragment read.
     u32x4 fa[2][2], fb[2][2];
-    read_frags(sa, sb, 0, fa[0], fb[0]);
-    J.scale(wring[QS], dhv[DS]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sa, sb, 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-    J.divide(Nf, p);
+    u32x4 o0, o1;
+    if constexpr (CB == 0) {
+      QuantJob<GS> J;
+      read_frags(sa, sb, 0, fa[0], fb[0]);
+      J.scale(ring[QS].w, dhv[DS]);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 1, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      J.divide(Nf, p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 9, 1);  // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sa, sb, 2, fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
-    const u32x4 o0 = J.dequant(0, dhiv[DS], Nf);
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 9, 1);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 2, fa[0], fb[0]);
+      mfmas(fa[1], fb[1]);
+      o0 = J.dequant(0, dhiv[DS], Nf);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 13, 2);  // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sa, sb, 3, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-    const u32x4 o1 = J.dequant(1, dhiv[DS], Nf);
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 13, 2);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 3, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      o1 = J.dequant(1, dhiv[DS], Nf);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 13, 3);  // VALU
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 13, 3);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fa[1], fb[1]);
+    } else {
+      read_frags(sa, sb, 0, fa[0], fb[0]);
+      read_frags(sa, sb, 1, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      o0 = dequant_half<CB, GS>(ring[QS], 0, dhiv[DS], p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 2, fa[0], fb[0]);
+      mfmas(fa[1], fb[1]);
+      o1 = dequant_half<CB, GS>(ring[QS], 1, dhiv[DS], p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 2);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 3, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      mfmas(fa[1], fb[1]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa[1], fb[1]);
     unsigned char* chunk = sB + DS * QC_BYTES;
     const int r = (QS & 1) * 64 + jrow;
     store_what(chunk, 0, r, p, o0);
@@ -429,7 +561,7 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
     issue_x(kt + 2, st2);
     __builtin_amdgcn_sched_barrier(0);
     if (POS % 2 == 0) load_dh(kt / 2 + 2, dhv[(POS / 2) & 1], dhiv[(POS / 2) & 1]);
-    load_w(kt + 5, wring[(POS + 1) & 3]);
+    load_job(kt + 5, ring[(POS + 1) & 3]);
     sta = sta == QNS - 1 ? 0 : sta + 1;
   };
   int kt = 0;
@@ -477,34 +609,57 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
 
 }  // namespace
 
-bool gemm_q_supported(int64_t K1, int group) {
-  return K1 > 0 && K1 % 128 == 0 && (group == 32 || group == 64 || group == 128);
+bool gemm_q_supported(int64_t K1, int group, int cb) {
+  if (K1 <= 0 || K1 % 128 != 0) return false;
+  if (group == 32 || group == 64 || group == 128) return true;
+  return cb > 0 && group == 256;  // no group reduction when expanding codes
 }
 
-hipError_t launch_gemm_q(const GemmQArgs& a, int group, const Launch& L) {
+namespace {
+
+template <int GS, int CB>
+hipError_t launch_gq(const GemmQArgs& a, dim3 grid, const Launch& L) {
+  static hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_gemm_q<GS, CB>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, QLDS);
+  if (attr != hipSuccess) return attr;
+  return ext_launch(k_gemm_q<GS, CB>, grid, dim3(QNW * 64), QLDS, L, a);
+}
+
+template <int CB>
+hipError_t launch_gq_cb(const GemmQArgs& a, int group, dim3 grid, const Launch& L) {
+  switch (group) {
+    case 32: return launch_gq<32, CB>(a, grid, L);
+    case 64: return launch_gq<64, CB>(a, grid, L);
+    case 128: return launch_gq<128, CB>(a, grid, L);
+    case 256:
+      if constexpr (CB > 0) return launch_gq<256, CB>(a, grid, L);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q(const GemmQArgs& a, int group, int cb, const Launch& L) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!gemm_q_supported(a.K1, group) || !a.C) return hipErrorInvalidValue;
+  if (!gemm_q_supported(a.K1, group, cb) || !a.C) return hipErrorInvalidValue;
+  if (cb > 0 && (!a.packed || !a.s || !a.m || a.row_bytes * 8 != a.K1 * cb))
+    return hipErrorInvalidValue;
   const int64_t mtiles = (a.M + QBM - 1) / QBM;
   const int64_t ntiles = (a.N + QBN - 1) / QBN;
   const int64_t nblk =
       ntiles >= 8 ? ((ntiles + 7) / 8) * 8 * mtiles : ntiles * mtiles;
   const unsigned nb = a.batch > 1 ? (unsigned)a.batch : 1u;
-#define TTQ_GEMM_Q(GSV)                                                       \
-  case GSV: {                                                                 \
-    static hipError_t attr = hipFuncSetAttribute(                             \
-        reinterpret_cast<const void*>(k_gemm_q<GSV>),                         \
-        hipFuncAttributeMaxDynamicSharedMemorySize, QLDS);                    \
-    if (attr != hipSuccess) return attr;                                      \
-    return ext_launch(k_gemm_q<GSV>, dim3((unsigned)nblk, nb), dim3(QNW * 64), \
-                      QLDS, L, a);                                            \
-  }
-  switch (group) {
-    TTQ_GEMM_Q(32)
-    TTQ_GEMM_Q(64)
-    TTQ_GEMM_Q(128)
+  const dim3 grid((unsigned)nblk, nb);
+  switch (cb) {
+    case 0: return launch_gq_cb<0>(a, group, grid, L);
+    case 1: return launch_gq_cb<1>(a, group, grid, L);
+    case 2: return launch_gq_cb<2>(a, group, grid, L);
+    case 4: return launch_gq_cb<4>(a, group, grid, L);
+    case 8: return launch_gq_cb<8>(a, group, grid, L);
     default: return hipErrorInvalidValue;
   }
-#undef TTQ_GEMM_Q
 }
 
 }  // namespace ttq

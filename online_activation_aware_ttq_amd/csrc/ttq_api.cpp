@@ -159,7 +159,7 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     if (P.rp > 0 && T > 0) plan_z_split(P, R * T, d, take);
     // (W_hat stays in the plan: a call that asks for the codes takes the
     // quantize pass)
-    if (T <= kGemmQMaxT && gemm_q_supported(d, prm->group) &&
+    if (T <= kGemmQMaxT && gemm_q_supported(d, prm->group, 0) &&
         !(prm->flags & TTQ_FLAG_FORCE_TWO_PHASE))
       P.path = 3;
   }
@@ -381,7 +381,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     qa.M = T; qa.N = dout; qa.C = Y; qa.ldc = dout;
     qa.batch = (int)R;
     qa.sX = T * d; qa.sA2 = T * P.rp; qa.sC = T * dout;
-    return run(K_GEMM_Q, s, [&](const Launch& L) { return launch_gemm_q(qa, prm->group, L); });
+    return run(K_GEMM_Q, s, [&](const Launch& L) { return launch_gemm_q(qa, prm->group, 0, L); });
   }
   // requests in chunks of P.rchunk: one quantize pass (each request its own
   // W_hat), then one batched GEMM launch per chunk
@@ -487,7 +487,9 @@ Plan make_qmatmul_plan(const ttq_params& q, int cb) {
   const bool fits = qgemv_lds_bytes(d, cb, q.group) <= kGemvLdsMax;
   const bool forced = (q.flags & TTQ_FLAG_FORCE_TWO_PHASE) != 0;
   P.path = (T == 1 && fits && !forced) ? 2 : (T <= kFusedMaxT && !forced ? 0 : 1);
-  if (P.rp > 0 && T > 0 && P.path != 1)
+  // more tokens: the GEMM expands the codes itself (no W_hat in HBM)
+  if (P.path == 1 && !forced && gemm_q_supported(d, q.group, cb)) P.path = 3;
+  if (P.rp > 0 && T > 0 && (P.path == 0 || P.path == 2))
     P.off_zsmall = take(lowrank_z_part_bytes(T, d, (int)P.rp));
   if (P.path == 0 && T > 0 && q.d_out > 0) {
     P.ntb = 1;
@@ -496,8 +498,8 @@ Plan make_qmatmul_plan(const ttq_params& q, int cb) {
     P.off_xs = take(sizeof(uint16_t) * P.planes * 16 * P.ntb * d);
     P.off_sx = take(sizeof(float) * P.G * 16 * P.ntb);
   }
-  if (P.path == 1 && T > 0 && q.d_out > 0) {
-    P.off_what = take(sizeof(uint16_t) * q.d_out * d);
+  if ((P.path == 1 || P.path == 3) && T > 0 && q.d_out > 0) {
+    if (P.path == 1) P.off_what = take(sizeof(uint16_t) * q.d_out * d);
     if (P.rp > 0) plan_z_split(P, T, d, take);
   }
   P.total = off;
@@ -626,6 +628,22 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
     fa.Y = Y;
     return run(K_QFUSED, s, [&](const Launch& L) { return launch_qfused(fa, P.ntb, q.group, cb, L); });
+  }
+  if (P.path == 3) {
+    if (P.rp > 0) {
+      st = enqueue_z_gemm(P, ws, Xb, Ab, T, d, rank, Zb, s);
+      if (st != TTQ_OK) return st;
+    }
+    GemmQArgs qa{};
+    qa.X = Xb; qa.ldx = d;
+    qa.packed = codes; qa.row_bytes = rb; qa.s = scales; qa.m = mins; qa.G = P.G;
+    qa.dhi = dhalf_inv; qa.K1 = d;
+    if (P.rp > 0) {
+      qa.A2 = Zb; qa.lda2 = P.rp; qa.B2 = Bb; qa.ldb2 = rank; qa.K2 = rank;
+    }
+    qa.M = T; qa.N = dout; qa.C = Y; qa.ldc = dout;
+    qa.batch = 1;
+    return run(K_GEMM_Q, s, [&](const Launch& L) { return launch_gemm_q(qa, q.group, cb, L); });
   }
   bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
   DequantArgs da{};

@@ -323,10 +323,14 @@ int gemm_lds_config(int64_t M, int64_t N, int64_t batch);
 // the product's D^{+-1/2} tile by tile, with the same float32 decisions as
 // the quantize pass (the results are identical to quantize pass + GEMM).
 // Products of a batch share W and have their own X, D^{+-1/2}, A2 and C.
+// With stored codes instead of W (cb > 0), W_hat = bf16((m + s q) D^{-1/2})
+// from the codes' CB-bit containers and the per-group s, m (one product).
 struct GemmQArgs {
   const bf16_t* X; int64_t ldx;
   const bf16_t* W; int64_t ldw;
-  const float* dh;      // [batch][K1]
+  const uint8_t* packed; int64_t row_bytes;   // codes (cb > 0)
+  const float* s; const float* m; int64_t G;  // [N][G] (cb > 0)
+  const float* dh;      // [batch][K1] (cb = 0)
   const float* dhi;     // [batch][K1]
   float Nf;             // 2^bits - 1
   int64_t K1;
@@ -338,9 +342,10 @@ struct GemmQArgs {
   int batch;
   int64_t sX, sA2, sC;  // per-product strides (elements); D^{+-1/2}: K1
 };
-hipError_t launch_gemm_q(const GemmQArgs& a, int group, const Launch& L);
-// K1 a multiple of 128 and groups of 32, 64 or 128 channels
-bool gemm_q_supported(int64_t K1, int group);
+hipError_t launch_gemm_q(const GemmQArgs& a, int group, int cb, const Launch& L);
+// K1 a multiple of 128; groups of 32, 64 or 128 channels (also 256 when
+// expanding codes, cb > 0)
+bool gemm_q_supported(int64_t K1, int group, int cb);
 
 // Row copies between a packed multi-request array and a padded batch (see
 // k_segment.hip).  Rows are row_bytes long (a multiple of 4).

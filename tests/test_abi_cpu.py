@@ -305,8 +305,11 @@ def test_packed_calls_workspace():
     assert call_qmatmul(p, Bm=FAKE, A=FAKE, ws_bytes=need - 1) == ttq.TTQ_EWORKSPACE
     # T <= 128: x' of the step (one bf16 plane of 64 tokens here)
     assert ttq.ttq_qmatmul_workspace_bytes(prm(T=64)) >= 64 * 256 * 2
-    # larger T (or the forced route) holds the expanded bf16 weights
-    assert ttq.ttq_qmatmul_workspace_bytes(prm(T=200)) >= 64 * 256 * 2
+    # larger T expands the codes inside the GEMM (no workspace without the
+    # low-rank term); the forced route holds the expanded bf16 weights
+    assert ttq.ttq_qmatmul_workspace_bytes(prm(T=200)) == 0
+    assert ttq.ttq_qmatmul_workspace_bytes(
+        prm(T=200, flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE)) >= 64 * 256 * 2
     assert ttq.ttq_qmatmul_workspace_bytes(prm(T=8, flags=2)) >= 64 * 256 * 2
     assert ttq.ttq_qmatmul_workspace_bytes(prm(T=1)) == 0
     q = prm(T=2048)

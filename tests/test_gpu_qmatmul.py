@@ -251,3 +251,42 @@ def test_full_size_decode_q_proj():
     rep = {"code_mismatch": nb}
     check_y(Y, Y_or, rep, "decode_T1")
     print(f"[parity] full-size decode: {rep}", flush=True)
+
+
+PREFILL_CASES = [
+    # the GEMM that expands the stored codes itself (T > 128): every container
+    # width, every group size, ragged token / row tiles, low-rank segments
+    ("p_b4_g128_r32", dict(d=1024, d_out=520, T=16, bits=4, group=128, rank=32,
+                           x_kind="logu10_100", n_outliers=10, seed=61), (300,)),
+    ("p_b3_g32_r64", dict(d=512, d_out=300, T=64, bits=3, group=32, rank=64,
+                          seed=62), (130, 257)),
+    ("p_b2_g64_r8", dict(d=1024, d_out=200, T=8, bits=2, group=64, rank=8,
+                         seed=63), (129,)),
+    ("p_b1_g256", dict(d=1024, d_out=77, T=16, bits=1, group=256, seed=64), (200,)),
+    ("p_b8_g64", dict(d=2048, d_out=96, T=1, bits=8, group=64, seed=65), (160,)),
+    ("p_b5_g32", dict(d=256, d_out=50, T=4, bits=5, group=32, seed=66), (140,)),
+]
+
+
+@pytest.mark.parametrize("name,kw,steps", PREFILL_CASES,
+                         ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_decode_expands_codes_in_the_gemm(name, kw, steps):
+    """Y of the GEMM that expands the codes tile by tile equals the forced
+    expand-to-HBM + GEMM route bit for bit (same float32 expansion, same
+    rounding, same MFMA order), and meets the oracle's bars."""
+    prob = make_problem(name, **kw)
+    g = _gpu_quantize(prob)
+    rep = {}
+    for Ts in steps:
+        print(f"[case] {name} prefill decode T={Ts}", flush=True)
+        Xs = _step_x(prob, Ts)
+        Y3 = _gpu_qmatmul(g["dev"], Xs, prob, 0)
+        Y1 = _gpu_qmatmul(g["dev"], Xs, prob, TWO)
+        diff = Y3.view(np.uint32) != Y1.view(np.uint32)
+        assert not diff.any(), f"T={Ts}: {int(diff.sum())} outputs differ"
+        Y_or = oracle.ttq_qmatmul(g["packed"], g["s"], g["m"], g["dhi"], Xs,
+                                  bits=prob.bits, group=prob.group,
+                                  B_bits=prob.B, A_bits=prob.A)
+        check_y(Y3, Y_or, rep, f"T{Ts}")
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.3g}" for k, v in rep.items()),
+          flush=True)
