@@ -71,6 +71,19 @@ __all__ = [
     "unpack_codes",
     "ttq_quantize",
     "ttq_qmatmul",
+    "QFORMATS",
+    "e4m3_decode",
+    "e4m3_round",
+    "e4m3_encode",
+    "encode_sym_fp32",
+    "encode_intzp_fp32",
+    "encode_fp8_fp32",
+    "quantize_format",
+    "reconstruct_format",
+    "format_offsets",
+    "format_levels",
+    "pre_rounding_format_fp64",
+    "band_excused_levels",
 ]
 
 
@@ -185,7 +198,7 @@ def ttq_linear(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
                A_bits: Optional[np.ndarray] = None,
                rows: Optional[np.ndarray] = None,
                dh32_override: Optional[np.ndarray] = None,
-               want_t: bool = False) -> dict:
+               want_t: bool = False, qformat: str = "asym") -> dict:
     """One TTQ linear call for one request.
 
     ``W_bits`` uint16 ``[d_out, d]``, ``X_bits`` uint16 ``[T, d]``, optional
@@ -195,9 +208,14 @@ def ttq_linear(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
     ``dh32_override`` replaces the float32 D^{1/2} fed to the code decision
     (used to check a kernel's codes against its own exported statistics).
 
+    ``qformat`` picks the quantizer (``QFORMATS``; default the asymmetric
+    one of reading 1).
+
     Returns a dict with ``n, dh, dhi`` (float64 [d]), ``dh32`` (float32
-    [d]), ``q`` (uint8 [rows, d]), ``s, m`` (float32 [rows, G]), ``Y``
-    (float64 [T, rows]) and, if ``want_t``, the float64 pre-rounding values.
+    [d]), ``q`` (uint8 [rows, d], the stored codes), ``s, m`` (float32
+    [rows, G]; for formats other than asym ``m`` is ``format_offsets``),
+    ``Y`` (float64 [T, rows]) and, if ``want_t``, the float64 pre-rounding
+    values (``t64`` in level units for formats other than asym).
     """
     X = bf16_to_f64(X_bits)
     T, d = X.shape
@@ -212,18 +230,32 @@ def ttq_linear(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
     dh32 = dh.astype(np.float32) if dh32_override is None else \
         np.asarray(dh32_override, dtype=np.float32)
 
-    q, s, m = encode_groups_fp32(bf16_to_f32(Wsel), dh32, bits, group)
-    W_hat = dequantize(q, s, m, dhi, group)
+    if qformat == "asym":
+        q, s, m = encode_groups_fp32(bf16_to_f32(Wsel), dh32, bits, group)
+        W_hat = dequantize(q, s, m, dhi, group)
+        extra = {}
+    else:
+        f = quantize_format(bf16_to_f32(Wsel), dh32, bits, group, qformat)
+        q, s = f["codes"], f["s"]
+        m = format_offsets(s, bits, qformat, z=f.get("z"))
+        W_hat = reconstruct_format(q, s, bits, group, qformat, z=f.get("z")) \
+            * dhi[None, :]
+        extra = {"z": f["z"]} if "z" in f else {}
     Y = X @ W_hat.T
     if B_bits is not None and A_bits is not None and np.asarray(A_bits).size:
         A = bf16_to_f64(A_bits)
         Bm = bf16_to_f64(np.asarray(B_bits)[sel])
         Z = X @ A.T                       # (A X) stored token-major [T, r]
         Y = Y + Z @ Bm.T                  # + B (A X)   ([ZH] Sec. 2.2)
-    out = dict(n=n, dh=dh, dhi=dhi, dh32=dh32, q=q, s=s, m=m, Y=Y, rows=sel)
+    out = dict(n=n, dh=dh, dhi=dhi, dh32=dh32, q=q, s=s, m=m, Y=Y, rows=sel,
+               qformat=qformat, **extra)
     if want_t:
-        t, u, mm, ss = pre_rounding_fp64(bf16_to_f64(Wsel), dh, bits, group)
-        out.update(t64=t, u64=u, m64=mm, s64=ss)
+        if qformat == "asym":
+            t, u, mm, ss = pre_rounding_fp64(bf16_to_f64(Wsel), dh, bits, group)
+            out.update(t64=t, u64=u, m64=mm, s64=ss)
+        else:
+            out.update(t64=pre_rounding_format_fp64(bf16_to_f64(Wsel), dh, bits,
+                                                    group, qformat))
     return out
 
 
@@ -288,7 +320,8 @@ def unpack_codes(packed: np.ndarray, bits: int, d: int) -> np.ndarray:
 def ttq_quantize(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
                  group: int, p: float, lam: float, alpha: float,
                  rows: Optional[np.ndarray] = None,
-                 dh32_override: Optional[np.ndarray] = None) -> dict:
+                 dh32_override: Optional[np.ndarray] = None,
+                 qformat: str = "asym") -> dict:
     """Statistics of one prompt X and the quantized weights to keep.
 
     Same steps as ``ttq_linear`` up to the codes; returns ``q`` (uint8),
@@ -304,21 +337,39 @@ def ttq_quantize(W_bits: np.ndarray, X_bits: np.ndarray, *, bits: int,
     dh, dhi = diag_scales(n, lam, alpha)
     dh32 = dh.astype(np.float32) if dh32_override is None else \
         np.asarray(dh32_override, dtype=np.float32)
-    q, s, m = encode_groups_fp32(bf16_to_f32(Wsel), dh32, bits, group)
+    f = quantize_format(bf16_to_f32(Wsel), dh32, bits, group, qformat)
+    q, s = f["codes"], f["s"]
+    m = f["m"] if qformat == "asym" else format_offsets(s, bits, qformat,
+                                                        z=f.get("z"))
     return dict(q=q, packed=pack_codes(q, bits), s=s, m=m, dh=dh, dhi=dhi,
-                dh32=dh32, dhi32=dhi.astype(np.float32), rows=sel)
+                dh32=dh32, dhi32=dhi.astype(np.float32), rows=sel,
+                qformat=qformat)
 
 
 def ttq_qmatmul(packed: np.ndarray, s: np.ndarray, m: np.ndarray,
                 dhi32: np.ndarray, X_bits: np.ndarray, *, bits: int,
                 group: int, B_bits: Optional[np.ndarray] = None,
-                A_bits: Optional[np.ndarray] = None) -> np.ndarray:
+                A_bits: Optional[np.ndarray] = None,
+                qformat: str = "asym") -> np.ndarray:
     """Y [T, rows] = X ((min + s q) D^{-1/2})^T + (X A^T) B^T, float64, from
-    the stored codes, (s, min) and D^{-1/2} of an earlier prompt."""
+    the stored codes, (s, min) and D^{-1/2} of an earlier prompt.
+
+    For the other formats the group term ``m`` is the stored offset of
+    ``format_offsets``; the reconstruction follows the format's definition
+    (the intzp zero point is z = rint(m / s), exact for |z| <= 255)."""
     X = bf16_to_f64(X_bits)
     d = X.shape[1]
     q = unpack_codes(packed, bits, d)
-    W_hat = dequantize(q, s, m, np.asarray(dhi32, dtype=np.float64), group)
+    dhi64 = np.asarray(dhi32, dtype=np.float64)
+    if qformat == "asym":
+        W_hat = dequantize(q, s, m, dhi64, group)
+    else:
+        z = None
+        if qformat == "intzp":
+            s32 = np.asarray(s, dtype=np.float64)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                z = np.where(s32 > 0, np.rint(np.asarray(m, dtype=np.float64) / s32), 0.0)
+        W_hat = reconstruct_format(q, s, bits, group, qformat, z=z) * dhi64[None, :]
     Y = X @ W_hat.T
     if B_bits is not None and A_bits is not None and np.asarray(A_bits).size:
         Y = Y + (X @ bf16_to_f64(A_bits).T) @ bf16_to_f64(B_bits).T
@@ -375,6 +426,260 @@ def symmetric_quantize(x: np.ndarray, bits: int):
         return np.zeros_like(x, dtype=np.int64), 0.0, np.zeros_like(x)
     q = np.clip(np.rint(x / s), -L, L).astype(np.int64)
     return q, s, s * q
+
+
+# --------------------------------------------------------------------------
+# format variants of Q: the pages call TTQ orthogonal to the code format
+# ([BLOG-EN] section "What TTQ is NOT": the scale source is what defines the
+# method, so the same D-scaled groups can feed an INT4 or an FP8 quantizer;
+# its table names E4M3 and E5M2 as the FP8 formats).
+# Each variant below decides its codes in float32 by a fixed sequence, like
+# reading 7, and reconstructs by its own definition in float64.
+#
+#   "asym"   min-anchored real zero point (reading 1; encode_groups_fp32)
+#   "sym"    symmetric b-bit ([BLOG-EN] maths): s = max|u| / Z, Z = 2^{b-1}-1,
+#            level k = clamp(round(u / s), -Z, Z), u_hat = s k;
+#            stored code k + Z in [0, 2Z]
+#   "intzp"  the affine form of [BLOG-EN] maths with an integer zero point z:
+#            code q = round(u / s) - z in [0, N], u_hat = s (q + z).  Reading:
+#            the range is widened to contain 0 (zero is then exactly
+#            representable, the usual convention for integer zero points),
+#            s = (hi - lo) / N with lo = min(min u, 0), hi = max(max u, 0),
+#            z = round(lo / s)
+#   "fp8"    FP8 E4M3 codes (OCP 8-bit float: 1 sign, 4 exponent bits with
+#            bias 7, 3 mantissa bits, largest finite 448, no infinities) with
+#            one float32 scale per group from the D-scaled weights
+#            (TTQ over FP8, [BLOG-EN] "What TTQ is NOT"): s = max|u| / 448,
+#            value v = E4M3 rounding (nearest, ties to even mantissa) of u / s,
+#            u_hat = s v; stored code = the E4M3 bit pattern (a zero is
+#            stored as +0)
+# --------------------------------------------------------------------------
+QFORMATS = ("asym", "sym", "intzp", "fp8")
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """float64 value of E4M3 bit patterns (codes 0x7f / 0xff are NaN)."""
+    c = np.asarray(code).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    mnt = (c & 7).astype(np.float64)
+    val = np.where(e == 0, mnt * 2.0 ** -9,
+                   (1.0 + mnt / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((c & 0x7f) == 0x7f, np.nan, val)
+    return sign * val
+
+
+def _e4m3_nonneg_grid():
+    """All finite non-negative E4M3 values, ascending, with their codes."""
+    codes = np.arange(0x7f)                       # 0x00 .. 0x7e
+    return e4m3_decode(codes), codes
+
+
+def e4m3_round(t: np.ndarray) -> np.ndarray:
+    """Round each finite |t| <= 448 to the nearest E4M3 value; a tie goes to
+    the neighbour with the even mantissa (its code is even).  float64 out."""
+    t = np.asarray(t, dtype=np.float64)
+    if np.any(np.abs(t) > E4M3_MAX):
+        raise ValueError("outside the E4M3 range")
+    vals, codes = _e4m3_nonneg_grid()
+    a = np.abs(t)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    dlo = a - vals[lo]
+    dhi = vals[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
+    r = np.where(pick_hi, vals[hi], vals[lo])
+    return np.where(t < 0, -r, r)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Bit pattern of exact E4M3 values; the sign bit is set only for v < 0."""
+    v = np.asarray(v, dtype=np.float64)
+    vals, codes = _e4m3_nonneg_grid()
+    a = np.abs(v)
+    idx = np.searchsorted(vals, a)
+    if np.any(idx >= len(vals)) or np.any(vals[np.minimum(idx, len(vals) - 1)] != a):
+        raise ValueError("not an E4M3 value")
+    return (codes[idx] | np.where(v < 0, 0x80, 0)).astype(np.uint8)
+
+
+def _grouped_u32(W32, dh32, group):
+    W32 = np.asarray(W32, dtype=np.float32)
+    dh32 = np.asarray(dh32, dtype=np.float32)
+    rows, d = W32.shape
+    return (W32 * dh32[None, :]).reshape(rows, d // group, group), rows, d
+
+
+def _inv32(s):
+    inv = np.zeros_like(s)
+    pos = s > np.float32(0)
+    inv[pos] = np.float32(1.0) / s[pos]                      # fl(1/s)
+    return inv
+
+
+def encode_sym_fp32(W32, dh32, bits: int, group: int):
+    """Symmetric codes: A = max|u|; s = fl(A / Z); inv = fl(1/s) (0 if s = 0);
+    k = clamp(rint(fl(u * inv)), -Z, Z).  Returns (k int16 [rows, d], s)."""
+    if bits < 2:
+        raise ValueError("the symmetric quantizer needs bits >= 2")
+    u, rows, d = _grouped_u32(W32, dh32, group)
+    Z = np.float32(2 ** (bits - 1) - 1)
+    s = np.abs(u).max(axis=2) / Z
+    inv = _inv32(s)
+    k = np.clip(np.rint(u * inv[:, :, None]), -Z, Z)
+    return k.astype(np.int16).reshape(rows, d), s
+
+
+def encode_intzp_fp32(W32, dh32, bits: int, group: int):
+    """Integer zero point: lo = min(min u, 0), hi = max(max u, 0);
+    s = fl(fl(hi - lo) / N); inv = fl(1/s) (0 if s = 0); z = rint(fl(lo * inv));
+    q = clamp(rint(fl(u * inv)) - z, 0, N).  Returns (q uint8, s, z int16)."""
+    u, rows, d = _grouped_u32(W32, dh32, group)
+    N = np.float32(2 ** bits - 1)
+    lo = np.minimum(u.min(axis=2), np.float32(0))
+    hi = np.maximum(u.max(axis=2), np.float32(0))
+    s = (hi - lo) / N
+    inv = _inv32(s)
+    z = np.rint(lo * inv)
+    q = np.clip(np.rint(u * inv[:, :, None]) - z[:, :, None], np.float32(0), N)
+    return q.astype(np.uint8).reshape(rows, d), s, z.astype(np.int16)
+
+
+def encode_fp8_fp32(W32, dh32, group: int):
+    """FP8 E4M3 codes: A = max|u|; s = fl(A / 448); inv = fl(1/s) (0 if s = 0);
+    t = fl(u * inv) clamped to [-448, 448]; v = E4M3 rounding of t.
+    Returns (v float64 E4M3 values [rows, d], s)."""
+    u, rows, d = _grouped_u32(W32, dh32, group)
+    s = np.abs(u).max(axis=2) / np.float32(E4M3_MAX)
+    inv = _inv32(s)
+    t = np.clip(u * inv[:, :, None], np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_round(t.astype(np.float64)).reshape(rows, d), s
+
+
+def quantize_format(W32, dh32, bits: int, group: int, fmt: str) -> dict:
+    """Codes of W D^{1/2} in format ``fmt``.  Returns ``codes`` (uint8, the
+    stored code), ``s`` (float32 [rows, G]) and the format's own group term:
+    ``m`` (asym minimum), ``z`` (intzp zero point), else nothing."""
+    if fmt == "asym":
+        q, s, m = encode_groups_fp32(W32, dh32, bits, group)
+        return dict(codes=q, s=s, m=m)
+    if fmt == "sym":
+        k, s = encode_sym_fp32(W32, dh32, bits, group)
+        return dict(codes=(k + (2 ** (bits - 1) - 1)).astype(np.uint8), s=s)
+    if fmt == "intzp":
+        q, s, z = encode_intzp_fp32(W32, dh32, bits, group)
+        return dict(codes=q, s=s, z=z)
+    if fmt == "fp8":
+        if bits != 8:
+            raise ValueError("fp8 codes are 8 bits wide")
+        v, s = encode_fp8_fp32(W32, dh32, group)
+        return dict(codes=e4m3_encode(v), s=s)
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+def reconstruct_format(codes, s, bits: int, group: int, fmt: str, m=None,
+                       z=None) -> np.ndarray:
+    """u_hat (before D^{-1/2}) from stored codes, float64, by each format's
+    definition."""
+    codes = np.asarray(codes)
+    rows, d = codes.shape
+    G = d // group
+    s64 = np.asarray(s, dtype=np.float64)[:, :, None]
+    c = codes.reshape(rows, G, group)
+    if fmt == "asym":
+        v = np.asarray(m, dtype=np.float64)[:, :, None] + s64 * c.astype(np.float64)
+    elif fmt == "sym":
+        v = s64 * (c.astype(np.float64) - (2 ** (bits - 1) - 1))
+    elif fmt == "intzp":
+        v = s64 * (c.astype(np.float64) + np.asarray(z, dtype=np.float64)[:, :, None])
+    elif fmt == "fp8":
+        v = s64 * e4m3_decode(c)
+    else:
+        raise ValueError(f"unknown format {fmt!r}")
+    return v.reshape(rows, d)
+
+
+def format_offsets(s, bits: int, fmt: str, m=None, z=None) -> np.ndarray:
+    """The float32 per-group offset o with u_hat = o + s code for the integer
+    formats (asym: the minimum; sym: -fl(Z s); intzp: fl(z s)); 0 for fp8.
+    This is the group term the library exports and stores beside the scales."""
+    s = np.asarray(s, dtype=np.float32)
+    if fmt == "asym":
+        return np.asarray(m, dtype=np.float32)
+    if fmt == "sym":
+        return -(np.float32(2 ** (bits - 1) - 1) * s)
+    if fmt == "intzp":
+        return np.asarray(z).astype(np.float32) * s
+    if fmt == "fp8":
+        return np.zeros_like(s)
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+def format_levels(codes, bits: int, fmt: str, z=None, group: int = 1):
+    """Signed levels in units of s (the value the rounding decided):
+    asym code; sym code - Z; intzp code + z; fp8 the E4M3 value."""
+    c = np.asarray(codes)
+    if fmt == "asym":
+        return c.astype(np.float64)
+    if fmt == "sym":
+        return c.astype(np.float64) - (2 ** (bits - 1) - 1)
+    if fmt == "intzp":
+        zz = np.repeat(np.asarray(z, dtype=np.float64), group, axis=1)
+        return c.astype(np.float64) + zz
+    return e4m3_decode(c)
+
+
+def pre_rounding_format_fp64(W64, dh64, bits: int, group: int, fmt: str):
+    """float64 pre-rounding value in level units for each format (u/s for the
+    formats without a real minimum, (u - min)/s for asym).  Returns t [rows, d]."""
+    if fmt == "asym":
+        return pre_rounding_fp64(W64, dh64, bits, group)[0]
+    W64 = np.asarray(W64, dtype=np.float64)
+    rows, d = W64.shape
+    G = d // group
+    u = (W64 * np.asarray(dh64)[None, :]).reshape(rows, G, group)
+    if fmt == "sym":
+        s = np.abs(u).max(axis=2) / (2 ** (bits - 1) - 1)
+    elif fmt == "intzp":
+        lo = np.minimum(u.min(axis=2), 0.0)
+        hi = np.maximum(u.max(axis=2), 0.0)
+        s = (hi - lo) / (2 ** bits - 1)
+    elif fmt == "fp8":
+        s = np.abs(u).max(axis=2) / E4M3_MAX
+    else:
+        raise ValueError(f"unknown format {fmt!r}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s[:, :, None] > 0, u / s[:, :, None], 0.0)
+    return t.reshape(rows, d)
+
+
+def band_excused_levels(lv_gpu, lv_ref, t64, rel: float = 1e-6):
+    """Band rule in level units for any format: a mismatch is excused iff the
+    two levels are neighbours on the format's grid (no level between them:
+    distance 1 for the integer formats, adjacent E4M3 values for fp8) and
+    the float64 pre-rounding value lies within ``rel * max(|t*|, 1)`` of
+    their midpoint.  Returns ``(n_mismatch, n_excused)``."""
+    a = np.asarray(lv_gpu, dtype=np.float64)
+    b = np.asarray(lv_ref, dtype=np.float64)
+    bad = a != b
+    nb = int(bad.sum())
+    if nb == 0:
+        return 0, 0
+    lo = np.minimum(a, b)
+    hi = np.maximum(a, b)
+    vals, _ = _e4m3_nonneg_grid()
+    grid = np.concatenate([-vals[:0:-1], vals])
+    ilo = np.searchsorted(grid, lo)
+    ihi = np.searchsorted(grid, hi)
+    on_grid = (np.take(grid, np.minimum(ilo, len(grid) - 1)) == lo) & \
+        (np.take(grid, np.minimum(ihi, len(grid) - 1)) == hi)
+    integer = (lo == np.rint(lo)) & (hi == np.rint(hi))
+    neighbours = (integer & (hi - lo == 1)) | (on_grid & (ihi - ilo == 1))
+    mid = 0.5 * (lo + hi)
+    t = np.asarray(t64, dtype=np.float64)
+    near = np.abs(t - mid) <= rel * np.maximum(np.abs(t), 1.0)
+    return nb, int((bad & neighbours & near).sum())
 
 
 def overhead_ratio(d_out: int, T: int) -> float:

@@ -45,6 +45,8 @@ def run_gpu(prob, flags: int = 0, exports: bool = True, rows=None):
     out = {}
     kw = dict(p=prob.p, lam=prob.lam, alpha=prob.alpha, bits=prob.bits,
               group=prob.group, flags=flags)
+    if prob.qformat != "asym":
+        kw["qformat"] = prob.qformat
     if exports:
         kw.update(
             codes_out=torch.empty(lead + (prob.d_out, prob.d), dtype=torch.uint8, device=dev),
@@ -98,10 +100,11 @@ def check_problem(prob, gpu: dict, rows=None, report: dict = None,
     sel = np.arange(prob.d_out) if rows is None else np.asarray(rows)
     W32 = oracle.bf16_to_f32(np.asarray(prob.W)[sel])
     for r in range(prob.R):
+        fmt = prob.qformat
         ref = oracle.ttq_linear(
             prob.W, prob.X[r], bits=prob.bits, group=prob.group, p=prob.p,
             lam=prob.lam, alpha=prob.alpha, B_bits=prob.B, A_bits=prob.A,
-            rows=sel, want_t=check_codes)
+            rows=sel, want_t=check_codes, qformat=fmt)
         if check_codes and "dh" in gpu:
             dh_gpu = gpu["dh"][r]
             mis = dh_gpu.view(np.uint32) != ref["dh32"].view(np.uint32)
@@ -111,17 +114,35 @@ def check_problem(prob, gpu: dict, rows=None, report: dict = None,
                               - ref["dh32"].view(np.int32).astype(np.int64))
                 assert ulps.max() <= 1, ulps.max()
             # strict: the oracle's float32 decision with the kernel's D^{1/2}
-            q_s, s_s, m_s = oracle.encode_groups_fp32(W32, dh_gpu, prob.bits,
-                                                     prob.group)
+            if fmt == "asym":
+                q_s, s_s, m_s = oracle.encode_groups_fp32(W32, dh_gpu, prob.bits,
+                                                         prob.group)
+            else:
+                f = oracle.quantize_format(W32, dh_gpu, prob.bits, prob.group, fmt)
+                q_s, s_s = f["codes"], f["s"]
+                m_s = oracle.format_offsets(s_s, prob.bits, fmt, z=f.get("z"))
             n_strict = int((q_s != gpu["q"][r]).sum())
             rep["strict_mismatch"] += n_strict
             assert n_strict == 0, f"request {r}: {n_strict} code mismatches (strict)"
             np.testing.assert_array_equal(s_s.view(np.uint32), gpu["s"][r].view(np.uint32))
             np.testing.assert_array_equal(m_s.view(np.uint32), gpu["m"][r].view(np.uint32))
             # contract: against the oracle's own statistics, band rule
-            nb, ne, nl = oracle.band_excused(
-                gpu["q"][r], ref["q"], ref["t64"], ref["u64"], ref["m64"],
-                ref["s64"], prob.group, BAND_REL)
+            if fmt == "asym":
+                nb, ne, nl = oracle.band_excused(
+                    gpu["q"][r], ref["q"], ref["t64"], ref["u64"], ref["m64"],
+                    ref["s64"], prob.group, BAND_REL)
+            else:
+                z_gpu = None
+                if fmt == "intzp":
+                    with np.errstate(divide="ignore", invalid="ignore"):
+                        z_gpu = np.where(s_s > 0, np.rint(gpu["m"][r].astype(np.float64)
+                                                          / s_s), 0.0)
+                lv_gpu = oracle.format_levels(gpu["q"][r], prob.bits, fmt, z=z_gpu,
+                                              group=prob.group)
+                lv_ref = oracle.format_levels(ref["q"], prob.bits, fmt,
+                                              z=ref.get("z"), group=prob.group)
+                nb, ne = oracle.band_excused_levels(lv_gpu, lv_ref, ref["t64"], BAND_REL)
+                nl = 0
             rep["contract_mismatch"] += nb
             rep["contract_excused"] += ne
             rep["literal_band"] += nl

@@ -80,6 +80,7 @@ class Problem:
     B: Optional[np.ndarray] = None  # uint16 [d_out, rank]
     A: Optional[np.ndarray] = None  # uint16 [rank, d]
     meta: dict = dataclasses.field(default_factory=dict)
+    qformat: str = "asym"  # quantizer format: asym, sym, intzp, fp8
 
     @property
     def params(self) -> dict:
@@ -164,7 +165,7 @@ def make_problem(name: str, *, d: int, d_out: int, T: int, R: int = 1,
                  lam: float = 1e-3, alpha: float = 0.5, seed: int = 0,
                  x_kind: str = "x50", n_outliers: int = 4,
                  w_sigma: float = 0.02, lr_sigma: float = 0.01,
-                 call: int = 0) -> Problem:
+                 call: int = 0, qformat: str = "asym") -> Problem:
     """Generic seeded problem; the standard workloads call this."""
     W = _normal_bits(_rng(seed, _S_W), (d_out, d), w_sigma)
     B = A = None
@@ -176,7 +177,8 @@ def make_problem(name: str, *, d: int, d_out: int, T: int, R: int = 1,
                    group=group, rank=rank, p=p, lam=lam, alpha=alpha,
                    W=W, X=X, B=B, A=A,
                    meta=dict(seed=seed, x_kind=x_kind, n_outliers=n_outliers,
-                             w_sigma=w_sigma, lr_sigma=lr_sigma, call=call))
+                             w_sigma=w_sigma, lr_sigma=lr_sigma, call=call),
+                   qformat=qformat)
 
 
 def make_c1(**kw) -> Problem:
