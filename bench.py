@@ -34,6 +34,8 @@ METRIC = ("TTQ-linear tokens/s per projection + % HBM/MFMA roofline; "
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 640 * 2 ** 20
+FORMAT_NAMES = {"asym": "asymmetric", "sym": "symmetric",
+                "intzp": "integer zero point", "fp8": "FP8 E4M3"}
 KERNEL_SOURCES = {"gemv_t1": "k_gemv.hip", "fused_qdq_mfma": "k_fused.hip",
                   "stats_small": "k_stats.hip", "gemm_mfma": "k_gemm.hip",
                   "quant_what": "k_quant.hip"}
@@ -45,6 +47,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--T", type=int, default=1)
+    ap.add_argument("--qformat", default="asym",
+                    choices=("asym", "sym", "intzp", "fp8"),
+                    help="quantizer format of the timed step (fp8: 8-bit "
+                         "E4M3 codes; the others 4-bit)")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -85,13 +91,18 @@ def alg_flops(d, d_out, T, rank=0):
     return 2 * d_out * d * T + 2 * rank * T * (d + d_out)
 
 
+def format_bits(qformat: str) -> int:
+    return 8 if qformat == "fp8" else 4
+
+
 def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
-            want_gemm: bool):
+            want_gemm: bool, qformat: str = "asym"):
     import numpy as np
     from workloads import configs as wc
 
     d = d_out = 4096
     prob = wc.make_c2(T=T)
+    prob.bits = format_bits(qformat)
     w_bytes = 2 * d * d_out
     n_w = max(2, -(-ROTATE_BYTES // w_bytes))
     Ws = [dev_bf16(prob.W, torch)]
@@ -104,10 +115,10 @@ def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
     Ys = [torch.empty(T, d_out, dtype=torch.float32, device="cuda")
           for _ in range(n_y)]
     kw = dict(p=prob.p, lam=prob.lam, alpha=prob.alpha, bits=prob.bits,
-              group=prob.group)
+              group=prob.group, qformat=qformat)
     prm = ttq.make_params(d=d, d_out=d_out, T=T, bits=prob.bits,
                           group=prob.group, p=prob.p, lam=prob.lam,
-                          alpha=prob.alpha)
+                          alpha=prob.alpha, qformat=qformat)
     ws = torch.empty(ttq.ttq_workspace_bytes(prm), dtype=torch.uint8,
                      device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -183,7 +194,7 @@ def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
     return out
 
 
-def cpu_baseline(T: int, seconds: float):
+def cpu_baseline(T: int, seconds: float, qformat: str = "asym"):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import numpy as np
     import oracle
@@ -194,12 +205,14 @@ def cpu_baseline(T: int, seconds: float):
     except Exception:  # pragma: no cover
         threads = 1
     prob = wc.make_c2(T=T)
+    prob.bits = format_bits(qformat)
     calls = 0
     t0 = time.perf_counter()
     while True:
         X = wc.draw_x(1, 5000 + calls, 1, T, prob.d, "logu10_100", 41)[0]
         oracle.ttq_linear(prob.W, X, bits=prob.bits, group=prob.group,
-                          p=prob.p, lam=prob.lam, alpha=prob.alpha)
+                          p=prob.p, lam=prob.lam, alpha=prob.alpha,
+                          qformat=qformat)
         calls += 1
         el = time.perf_counter() - t0
         if (el >= seconds and calls >= 3) or el >= 3 * seconds:
@@ -327,13 +340,28 @@ def main():
 
     torch.cuda.init()
     main_m = measure(a.T, a.steps, a.warmup, torch, ttq,
-                     want_graph=not a.only_ttq, want_gemm=not a.only_ttq)
+                     want_graph=not a.only_ttq, want_gemm=not a.only_ttq,
+                     qformat=a.qformat)
     if a.copy_calib_mb:
         copy_calibration(a.copy_calib_mb, torch)
     sec = None
     if not a.only_ttq and a.T != 128:
         sec = measure(128, max(100, a.steps // 4), a.warmup, torch, ttq,
-                      want_graph=False, want_gemm=True)
+                      want_graph=False, want_gemm=True, qformat=a.qformat)
+    # the other quantizer formats on the same step (context lines)
+    fmts = {}
+    if not a.only_ttq:
+        for f in ("asym", "sym", "intzp", "fp8"):
+            if f == a.qformat:
+                continue
+            m = measure(a.T, max(200, a.steps // 4), a.warmup, torch, ttq,
+                        want_graph=False, want_gemm=False, qformat=f)
+            kms = max(m["kernels_ms_avg"].values())
+            fmts[f] = {"bits": format_bits(f), "ms_per_step": m["ms_per_step"],
+                       "tokens_per_s": a.T / (m["ms_per_step"] * 1e-3),
+                       "dominant_kernel_ms": kms,
+                       "hbm_frac_kernel": alg_bytes(4096, 4096, a.T) / (kms * 1e-3)
+                       / 1e9 / HBM_PEAK_GBS}
 
     d = d_out = 4096
     T = a.T
@@ -373,10 +401,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"attention q_proj d=d'=4096 T={T}, 4-bit g128 "
-                        "asymmetric, p=2, lambda=1e-3, alpha=0.5, 1% outlier "
-                        "channels x10-100 redrawn per call",
-            "d": d, "d_out": d_out, "T": T, "bits": 4, "group": 128,
+            "workload": f"attention q_proj d=d'=4096 T={T}, "
+                        f"{format_bits(a.qformat)}-bit g128 "
+                        f"{FORMAT_NAMES[a.qformat]}, p=2, lambda=1e-3, "
+                        "alpha=0.5, 1% outlier channels x10-100 redrawn per call",
+            "d": d, "d_out": d_out, "T": T, "bits": format_bits(a.qformat),
+            "group": 128, "qformat": a.qformat,
             "rank": 0, "parallelism": "single GPU",
             "weights": f"{main_m['rotating_w_copies']} rotating copies "
                        f"({main_m['rotating_bytes'] / 1e6:.0f} MB, above the "
@@ -408,8 +438,10 @@ def main():
             "rho_pages": 1.0 / d_out + 3.0 / 128,
             "kernels_ms_avg": sec["kernels_ms_avg"],
         }
+    if fmts:
+        line["other_formats"] = fmts
     if not a.no_cpu and not a.only_ttq:
-        line["cpu_baseline"] = cpu_baseline(T, a.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(T, a.cpu_seconds, a.qformat)
     print(json.dumps(line), flush=True)
 
 

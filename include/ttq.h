@@ -69,18 +69,47 @@ enum {
 #define TTQ_FLAG_FORCE_FUSED 1u    /* use the single-pass fused path (T <= 128) */
 #define TTQ_FLAG_FORCE_TWO_PHASE 2u /* quantize pass + GEMM, at any T            */
 
+/* Quantizer formats (ttq_params.qformat).  The method derives the scale from
+ * the activations and leaves the code format open (lo0 blog "Test-time
+ * quantization: quantising on the fly with no calibration dataset", section
+ * "What TTQ is NOT": orthogonal to INT4 or FP8; section "The maths that
+ * matter" for the symmetric scale and the affine form with a zero point).
+ * For one group of u = w D^{1/2} (float32, no fused operations, inv = 1/s or
+ * 0 when s = 0, rint = round half to even):
+ *   TTQ_QF_ASYM   s = (max - min)/N, q = clamp(rint((u - min) inv), 0, N),
+ *                 u_hat = min + s q                 (N = 2^b - 1; default)
+ *   TTQ_QF_SYM    s = max|u| / Z (Z = 2^{b-1} - 1, b >= 2),
+ *                 k = clamp(rint(u inv), -Z, Z), u_hat = s k, code q = k + Z
+ *   TTQ_QF_INTZP  lo = min(min u, 0), hi = max(max u, 0), s = (hi - lo)/N,
+ *                 z = rint(lo inv), q = clamp(rint(u inv) - z, 0, N),
+ *                 u_hat = s (q + z)   (integer zero point; zero is exact)
+ *   TTQ_QF_FP8    b = 8: s = max|u| / 448, code = the OCP FP8 E4M3 pattern
+ *                 of the nearest E4M3 value v (ties to even) of
+ *                 clamp(u inv, -448, 448), u_hat = s v (the sign bit is
+ *                 that of u inv, also when v is zero)
+ * The per-group term stored beside the scales (mins_out, and the `mins` of
+ * ttq_quantize / ttq_qmatmul) is the offset m with u_hat = m + s q for the
+ * integer formats: the minimum (ASYM), -(Z s) (SYM), z s (INTZP), each
+ * rounded once to float32; it is 0 for FP8, whose codes decode to E4M3
+ * values.  Codes are decided exactly as stated; Y uses these stored terms. */
+#define TTQ_QF_ASYM 0u
+#define TTQ_QF_SYM 1u
+#define TTQ_QF_INTZP 2u
+#define TTQ_QF_FP8 3u
+
 /* One projection's shape and the method's constants.
  *   d      input channels; >= 1 and a multiple of `group`
  *   d_out  output channels; >= 0
  *   T      tokens per request; >= 0 (T = 0: Y is empty, codes/scales are
  *          still produced from zero statistics)
  *   rank   low-rank r; 0 = no low-rank term; otherwise a multiple of 8, <= 1024
- *   bits   code width b in 1..8
+ *   bits   code width b in 1..8 (2..8 for TTQ_QF_SYM, 8 for TTQ_QF_FP8)
  *   group  group size along d: 32, 64, 128 or 256
  *   p      norm order, finite and > 0 (1 and 2 are exact; others use pow)
  *   lambda damping, finite and >= 0
  *   alpha  exponent, finite and >= 0 (0 gives D = I, i.e. plain RTN)
- *   flags  0, or one TTQ_FLAG_* path override                                */
+ *   flags  0, or one TTQ_FLAG_* path override
+ *   qformat one of TTQ_QF_* (0 = the asymmetric quantizer)                   */
 typedef struct ttq_params {
   int64_t d;
   int64_t d_out;
@@ -92,7 +121,7 @@ typedef struct ttq_params {
   double lambda;
   double alpha;
   uint32_t flags;
-  uint32_t reserved;
+  uint32_t qformat;
 } ttq_params;
 
 /* Device workspace, in bytes, that ttq_linear (n_requests = 1) or
@@ -107,7 +136,8 @@ int ttq_workspace_bytes(const ttq_params* prm, int64_t n_requests,
  *   Y                [T][d_out] float32; required iff T*d_out > 0; 4-byte aligned
  *   codes_out        optional [d_out][d] uint8 codes q
  *   scales_out       optional [d_out][d/group] float32 scales s
- *   mins_out         optional [d_out][d/group] float32 group minima (zero points)
+ *   mins_out         optional [d_out][d/group] float32 group offsets m (the
+ *                    minima for TTQ_QF_ASYM; see TTQ_QF_*)
  *   dhalf_out        optional [d] float32 D^{1/2} as fed to the code decision
  *   workspace        device scratch of at least ttq_workspace_bytes(prm, 1);
  *                    256-byte aligned; contents need not be initialized and
@@ -200,7 +230,8 @@ int ttq_qmatmul_workspace_bytes(const ttq_params* prm, size_t* bytes);
  * D from zero statistics, as in ttq_linear).
  *   codes       [d_out][row_bytes] packed codes, 16-byte aligned, required
  *   scales      [d_out][d/group] float32 s, required
- *   mins        [d_out][d/group] float32 group minima, required
+ *   mins        [d_out][d/group] float32 group offsets m (minima for
+ *               TTQ_QF_ASYM; see TTQ_QF_*), required
  *   dhalf_inv   [d] float32 D^{-1/2} = float32(1 / D^{1/2}), required
  *   dhalf_out   optional [d] float32 D^{1/2} as fed to the code decision
  * rank and the path flags are not read (the low-rank factors are used as

@@ -7,6 +7,7 @@ thin Python binding over it.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
+    QFORMATS,
     LIB_PATH,
     TTQ_EALIGN,
     TTQ_EHIP,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     container_bits,
     load_library,
     make_params,
+    qformat_code,
     timing_enable,
     timing_query,
     timing_reset,

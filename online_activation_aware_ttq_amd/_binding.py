@@ -72,8 +72,21 @@ class ttq_params(ctypes.Structure):
         ("lambda_", ctypes.c_double),
         ("alpha", ctypes.c_double),
         ("flags", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("qformat", ctypes.c_uint32),
     ]
+
+
+# quantizer formats (TTQ_QF_* of include/ttq.h)
+QFORMATS = {"asym": 0, "sym": 1, "intzp": 2, "fp8": 3}
+
+
+def qformat_code(qformat) -> int:
+    """TTQ_QF_* value of a format name ("asym", "sym", "intzp", "fp8") or int."""
+    if isinstance(qformat, str):
+        if qformat not in QFORMATS:
+            raise ValueError(f"unknown quantizer format {qformat!r}")
+        return QFORMATS[qformat]
+    return int(qformat)
 
 
 class TTQError(RuntimeError):
@@ -107,10 +120,10 @@ def load_library() -> ctypes.CDLL:
 
 def make_params(*, d: int, d_out: int, T: int, rank: int = 0, bits: int,
                 group: int, p: float, lam: float, alpha: float,
-                flags: int = 0) -> ttq_params:
+                flags: int = 0, qformat="asym") -> ttq_params:
     return ttq_params(int(d), int(d_out), int(T), int(rank), int(bits),
                       int(group), float(p), float(lam), float(alpha),
-                      int(flags), 0)
+                      int(flags), qformat_code(qformat))
 
 
 def ttq_status_string(status: int) -> str:
@@ -160,7 +173,7 @@ def _check(t, name, dtype, shape, device):
 
 def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
           codes_out, scales_out, mins_out, dhalf_out, workspace, stream,
-          flags):
+          flags, qformat):
     import torch
     lib = load_library()
     if batched:
@@ -181,7 +194,8 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
     prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
-                      group=group, p=p, lam=lam, alpha=alpha, flags=flags)
+                      group=group, p=p, lam=lam, alpha=alpha, flags=flags,
+                      qformat=qformat)
     need = ttq_workspace_bytes(prm, R)
     if Y is None:
         Y = torch.empty(lead + (T, d_out), dtype=torch.float32, device=dev)
@@ -209,7 +223,7 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
 def ttq_linear(W, X, B=None, A=None, *, p: float, lam: float, alpha: float,
                bits: int, group: int, Y=None, codes_out=None, scales_out=None,
                mins_out=None, dhalf_out=None, workspace=None, stream=None,
-               flags: int = 0):
+               flags: int = 0, qformat="asym"):
     """Y[T, d_out] = Q_D[W] X + B (A X) for one request (see include/ttq.h).
 
     W [d_out, d], X [T, d], B [d_out, r], A [r, d] are bfloat16 GPU tensors;
@@ -218,19 +232,19 @@ def ttq_linear(W, X, B=None, A=None, *, p: float, lam: float, alpha: float,
     return _call(False, W, X, B, A, p=p, lam=lam, alpha=alpha, bits=bits,
                  group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
                  mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
-                 stream=stream, flags=flags)
+                 stream=stream, flags=flags, qformat=qformat)
 
 
 def ttq_linear_batched(W, X, B=None, A=None, *, p: float, lam: float,
                        alpha: float, bits: int, group: int, Y=None,
                        codes_out=None, scales_out=None, mins_out=None,
                        dhalf_out=None, workspace=None, stream=None,
-                       flags: int = 0):
+                       flags: int = 0, qformat="asym"):
     """R requests with their own statistics on a shared W: X [R, T, d]."""
     return _call(True, W, X, B, A, p=p, lam=lam, alpha=alpha, bits=bits,
                  group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
                  mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
-                 stream=stream, flags=flags)
+                 stream=stream, flags=flags, qformat=qformat)
 
 
 def _offsets(seg_offsets):
@@ -252,7 +266,7 @@ def ttq_linear_segmented(W, X, B=None, A=None, *, seg_offsets, p: float,
                          lam: float, alpha: float, bits: int, group: int,
                          Y=None, codes_out=None, scales_out=None, mins_out=None,
                          dhalf_out=None, workspace=None, stream=None,
-                         flags: int = 0):
+                         flags: int = 0, qformat="asym"):
     """Requests of different lengths packed in X [T, d]: request i owns rows
     seg_offsets[i] .. seg_offsets[i+1]-1 and has its own statistics."""
     import torch
@@ -271,7 +285,8 @@ def ttq_linear_segmented(W, X, B=None, A=None, *, seg_offsets, p: float,
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
     prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
-                      group=group, p=p, lam=lam, alpha=alpha, flags=flags)
+                      group=group, p=p, lam=lam, alpha=alpha, flags=flags,
+                      qformat=qformat)
     need = ttq_segmented_workspace_bytes(prm, seg_offsets)
     if Y is None:
         Y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
@@ -329,7 +344,8 @@ def ttq_qmatmul_workspace_bytes(prm: ttq_params) -> int:
 
 def ttq_quantize(W, X, *, p: float, lam: float, alpha: float, bits: int,
                  group: int, codes=None, scales=None, mins=None,
-                 dhalf_inv=None, dhalf_out=None, workspace=None, stream=None):
+                 dhalf_inv=None, dhalf_out=None, workspace=None, stream=None,
+                 qformat="asym"):
     """Quantize W once for the prompt X (see include/ttq.h).
 
     Returns (codes [d_out, row_bytes] uint8, scales [d_out, G] float32,
@@ -343,7 +359,7 @@ def ttq_quantize(W, X, *, p: float, lam: float, alpha: float, bits: int,
     if dev.type != "cuda":
         raise ValueError("W must be a GPU tensor")
     prm = make_params(d=d, d_out=d_out, T=T, bits=bits, group=group, p=p,
-                      lam=lam, alpha=alpha)
+                      lam=lam, alpha=alpha, qformat=qformat)
     rb = ttq_packed_row_bytes(prm)
     need = ttq_quantize_workspace_bytes(prm)
     G = d // group
@@ -377,9 +393,10 @@ def ttq_quantize(W, X, *, p: float, lam: float, alpha: float, bits: int,
 
 def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
                 bits: int, group: int, Y=None, workspace=None, stream=None,
-                flags: int = 0):
+                flags: int = 0, qformat="asym"):
     """Y[T, d_out] = X ((min + s q) D^{-1/2})^T + (X A^T) B^T from the codes
-    stored by ttq_quantize (see include/ttq.h)."""
+    stored by ttq_quantize (see include/ttq.h; ``qformat`` as given to it:
+    E4M3 codes decode as FP8 values)."""
     import torch
     lib = load_library()
     T, d = X.shape
@@ -391,7 +408,8 @@ def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
     prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
-                      group=group, p=1.0, lam=0.0, alpha=0.0, flags=flags)
+                      group=group, p=1.0, lam=0.0, alpha=0.0, flags=flags,
+                      qformat=qformat)
     rb = ttq_packed_row_bytes(prm)
     need = ttq_qmatmul_workspace_bytes(prm)
     G = d // group

@@ -7,7 +7,9 @@
 //
 //   Y[t,i] = sum_k  s_ik * sum_{j in k} q_ij x'_tj  +  m_ik * sum_{j in k} x'_tj
 //
-// where x' = x D^{-1/2} and (s_ik, m_ik) are the group scale and minimum.
+// where x' = x D^{-1/2} and (s_ik, m_ik) are the group scale and minimum
+// (for the formats without a real minimum q is the signed level, exact in
+// bf16 like the codes, and the m term is absent).
 // This is the dequantized product (m + s q) D^{-1/2} X of "TTQ:
 // Activation-Aware Test-Time Quantization ..." (gist.science zh summary,
 // Sec. 2.1) regrouped so that the integer codes -- exact in bf16 -- are the
@@ -43,7 +45,7 @@ namespace ttq {
 
 constexpr int FW = 8;  // waves per workgroup
 
-template <int NTB, int GS, bool DH_LDS, bool EXPORT>
+template <int NTB, int GS, bool DH_LDS, bool EXPORT, int QF>
 __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   constexpr int NKS = GS / 32;
   constexpr bool HILO = (NTB == 1);
@@ -142,8 +144,10 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 
     // s = fl(fl(M - m) / N), inv = fl(1 / s); IEEE division, no contraction
-    const float s = (mx - mn) / Nf;
-    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    // (other formats: see QFmt)
+    const QGroup gq = qgroup<QF>(mn, mx, Nf);
+    const float s = gq.s;
+    const float inv = gq.inv;
 
     // codes q = rint(fl(fl(u - m) * inv)), packed as bf16 pairs.  The clamp to
     // [0, N] of the definition is a no-op here: 0 <= u - m <= M - m, and the
@@ -153,9 +157,12 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
 #pragma unroll
     for (int k = 0; k < NKS; ++k) {
       float q[8];
+      if constexpr (QF == QF_ASYM) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        q[j] = __builtin_rintf((u[k][j] - mn) * inv);
+        for (int j = 0; j < 8; ++j) q[j] = __builtin_rintf((u[k][j] - mn) * inv);
+      } else {
+        qlevels8<QF>(gq, u[k], q);
+      }
       qv[k].x = __builtin_amdgcn_perm(__float_as_uint(q[1]),
                                       __float_as_uint(q[0]), 0x07060302u);
       qv[k].y = __builtin_amdgcn_perm(__float_as_uint(q[3]),
@@ -166,10 +173,10 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
                                       __float_as_uint(q[6]), 0x07060302u);
       if (EXPORT && a.codes_out && row_ok) {
         u32x2 c;
-        c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
-              ((unsigned)q[3] << 24);
-        c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
-              ((unsigned)q[7] << 24);
+        c.x = qcode<QF>(gq, q[0]) | (qcode<QF>(gq, q[1]) << 8) |
+              (qcode<QF>(gq, q[2]) << 16) | (qcode<QF>(gq, q[3]) << 24);
+        c.y = qcode<QF>(gq, q[4]) | (qcode<QF>(gq, q[5]) << 8) |
+              (qcode<QF>(gq, q[6]) << 16) | (qcode<QF>(gq, q[7]) << 24);
         *(u32x2*)(a.codes_out + ((int64_t)req * a.d_out + row) * d + colg +
                   k * 32) = c;
       }
@@ -177,8 +184,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     if (EXPORT && a.s_out && row_ok && qd == 0) {
       const int64_t o = ((int64_t)req * a.d_out + row) * G + g;
       a.s_out[o] = s;
-      a.m_out[o] = mn;
+      a.m_out[o] = gq.off;
     }
+    const float mc = QF == QF_ASYM ? mn : 0.f;
 
     // contraction on the matrix cores + per-group affine epilogue
     if (NTB == 1) {
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[0][i] = fmaf(s, P[i], fmaf(mn, sxv0[i], acc[0][i]));
+        acc[0][i] = fmaf(s, P[i], fmaf(mc, sxv0[i], acc[0][i]));
     } else {
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
               __builtin_bit_cast(bf16x8, qv[k]), P, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc[tb][i] = fmaf(s, P[i], fmaf(mn, sxv[i], acc[tb][i]));
+          acc[tb][i] = fmaf(s, P[i], fmaf(mc, sxv[i], acc[tb][i]));
       }
     }
   };
@@ -297,17 +305,19 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   }
 }
 
-template <int NTB, bool DHL>
+template <int NTB, bool DHL, int QF>
 static hipError_t launch_fused_ntb(const FusedArgs& a, int group, dim3 grid,
                                    uint32_t lds, const Launch& L) {
   const dim3 blk(FW * 64);
   // the exports are a separate instantiation: conditional stores in the loop
   // would make the compiler's memory wait counts conservative
   const bool exp = a.codes_out || a.s_out;
-#define TTQ_FUSED_CASE(GSV)                                                  \
-  case GSV:                                                                  \
-    return exp ? ext_launch(k_fused<NTB, GSV, DHL, true>, grid, blk, lds, L, a) \
-               : ext_launch(k_fused<NTB, GSV, DHL, false>, grid, blk, lds, L, a);
+#define TTQ_FUSED_CASE(GSV)                                                    \
+  case GSV:                                                                    \
+    return exp ? ext_launch(k_fused<NTB, GSV, DHL, true, QF>, grid, blk, lds, L, \
+                            a)                                                 \
+               : ext_launch(k_fused<NTB, GSV, DHL, false, QF>, grid, blk, lds, \
+                            L, a);
   switch (group) {
     TTQ_FUSED_CASE(32)
     TTQ_FUSED_CASE(64)
@@ -318,14 +328,26 @@ static hipError_t launch_fused_ntb(const FusedArgs& a, int group, dim3 grid,
 #undef TTQ_FUSED_CASE
 }
 
+template <bool DHL, int QF>
+static hipError_t launch_fused_qf(const FusedArgs& a, int ntb, int group,
+                                  dim3 grid, uint32_t lds, const Launch& L) {
+  switch (ntb) {
+    case 1: return launch_fused_ntb<1, DHL, QF>(a, group, grid, lds, L);
+    case 2: return launch_fused_ntb<2, DHL, QF>(a, group, grid, lds, L);
+    case 4: return launch_fused_ntb<4, DHL, QF>(a, group, grid, lds, L);
+    case 8: return launch_fused_ntb<8, DHL, QF>(a, group, grid, lds, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <bool DHL>
 static hipError_t launch_fused_dhl(const FusedArgs& a, int ntb, int group,
                                    dim3 grid, uint32_t lds, const Launch& L) {
-  switch (ntb) {
-    case 1: return launch_fused_ntb<1, DHL>(a, group, grid, lds, L);
-    case 2: return launch_fused_ntb<2, DHL>(a, group, grid, lds, L);
-    case 4: return launch_fused_ntb<4, DHL>(a, group, grid, lds, L);
-    case 8: return launch_fused_ntb<8, DHL>(a, group, grid, lds, L);
+  switch (a.qf) {
+    case QF_ASYM: return launch_fused_qf<DHL, QF_ASYM>(a, ntb, group, grid, lds, L);
+    case QF_SYM: return launch_fused_qf<DHL, QF_SYM>(a, ntb, group, grid, lds, L);
+    case QF_INTZP: return launch_fused_qf<DHL, QF_INTZP>(a, ntb, group, grid, lds, L);
+    case QF_FP8: return launch_fused_qf<DHL, QF_FP8>(a, ntb, group, grid, lds, L);
     default: return hipErrorInvalidValue;
   }
 }

@@ -86,7 +86,7 @@ __device__ __forceinline__ void reduce_minmax(float& mn, float& mx) {
 // dhi[2h + i] for channel quarter i).  In three parts, so that the k-tile's
 // MFMAs can be spread between them: scaling and local extrema, the group
 // reduction and division, then the codes and W_hat of one half.
-template <int GS>
+template <int GS, int QF>
 struct QuantJob {
   float u[2][8];
   float mn[2], mx[2], s[2], inv[2];
@@ -116,7 +116,7 @@ struct QuantJob {
       mx[0] = fmaxf(mx[0], mx[1]);
       reduce_minmax<true>(mn[0], mx[0]);
       mn[1] = mn[0];
-      s[0] = (mx[0] - mn[0]) / Nf;
+      s[0] = qscale<QF>(mn[0], mx[0], Nf);
       inv[0] = s[0] > 0.f ? 1.0f / s[0] : 0.f;
       s[1] = s[0];
       inv[1] = inv[0];
@@ -127,7 +127,7 @@ struct QuantJob {
       const bool second = p & 1;
       const float mnc = second ? mn[1] : mn[0];
       const float mxc = second ? mx[1] : mx[0];
-      const float sc = (mxc - mnc) / Nf;
+      const float sc = qscale<QF>(mnc, mxc, Nf);
       const float ic = sc > 0.f ? 1.0f / sc : 0.f;
       s[0] = dpp<dpp_bcast(0)>(sc); inv[0] = dpp<dpp_bcast(0)>(ic);
       s[1] = dpp<dpp_bcast(1)>(sc); inv[1] = dpp<dpp_bcast(1)>(ic);
@@ -136,13 +136,13 @@ struct QuantJob {
 
   // W_hat of half h, 8 bf16
   __device__ __forceinline__ u32x4 dequant(int h, const f32x4 (&dhi)[4], float Nf) const {
-    float wq[8];
+    const QGroup g = qgroup_si<QF>(mn[h], s[h], inv[h], Nf);
+    float q[8], wq[8];
+    qlevels8<QF>(g, u[h], q);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float q = __builtin_amdgcn_fmed3f(
-          __builtin_rintf((u[h][e] - mn[h]) * inv[h]), 0.f, Nf);
       const f32x4 di = dhi[2 * h + (e >> 2)];
-      wq[e] = fmaf(s[h], q, mn[h]) * di[e & 3];
+      wq[e] = fmaf(s[h], q[e], g.c) * di[e & 3];
     }
     u32x4 o;
     o.x = pack_bf16(wq[0], wq[1]);
@@ -159,12 +159,12 @@ __device__ __forceinline__ void store_what(unsigned char* chunk, int h, int r, i
   *(u32x4*)(chunk + h * QH_BYTES + r * 128 + ((p ^ swz(r)) << 4)) = o;
 }
 
-template <int GS>
+template <int GS, int QF>
 __device__ __forceinline__ void quant_job(const u32x4 (&wv)[2],
                                           const f32x4 (&dh)[4],
                                           const f32x4 (&dhi)[4], float Nf,
                                           int p, int r, unsigned char* chunk) {
-  QuantJob<GS> J;
+  QuantJob<GS, QF> J;
   J.scale(wv, dh);
   J.divide(Nf, p);
   store_what(chunk, 0, r, p, J.dequant(0, dhi, Nf));
@@ -186,7 +186,7 @@ struct JobIn {
 // of the quantize-once storage ("TTQ: Activation-Aware Test-Time
 // Quantization ...", nl summary, Sec. 2: statistics per prompt, weights
 // stored quantized), with the float32 operations of the dequantize pass.
-template <int CB, int GS>
+template <int CB, int GS, bool F8>
 __device__ __forceinline__ u32x4 dequant_half(const JobIn<CB>& J, int h,
                                               const f32x4 (&dhi)[4], int p) {
   float sg, mg;
@@ -201,11 +201,12 @@ __device__ __forceinline__ u32x4 dequant_half(const JobIn<CB>& J, int h,
   float wq[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    unsigned code;
-    if constexpr (CB == 8) code = (J.c[h][e >> 2] >> ((e & 3) * 8)) & 0xffu;
-    else code = __builtin_amdgcn_ubfe(J.c[h][0], e * CB, CB);
+    float qv;
+    if constexpr (F8) qv = e4m3_byte(J.c[h][e >> 2], e & 3);
+    else if constexpr (CB == 8) qv = (float)((J.c[h][e >> 2] >> ((e & 3) * 8)) & 0xffu);
+    else qv = (float)__builtin_amdgcn_ubfe(J.c[h][0], e * CB, CB);
     const f32x4 di = dhi[2 * h + (e >> 2)];
-    wq[e] = fmaf(sg, (float)code, mg) * di[e & 3];
+    wq[e] = fmaf(sg, qv, mg) * di[e & 3];
   }
   u32x4 o;
   o.x = pack_bf16(wq[0], wq[1]);
@@ -215,9 +216,10 @@ __device__ __forceinline__ u32x4 dequant_half(const JobIn<CB>& J, int h,
   return o;
 }
 
-// CB = 0: quantize bf16 weights with the request's D (path of ttq_linear);
-// CB = 1, 2, 4, 8: expand stored codes (path of ttq_qmatmul).
-template <int GS, int CB>
+// CB = 0: quantize bf16 weights with the request's D (path of ttq_linear) in
+// format QF; CB = 1, 2, 4, 8: expand stored codes (path of ttq_qmatmul),
+// decoded as E4M3 values for QF == QF_FP8 (CB = 8) and as integers otherwise.
+template <int GS, int CB, int QF>
 __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
   if (blockIdx.y > 0) {  // product z of a batch
     const int64_t z = blockIdx.y;
@@ -445,10 +447,10 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
   auto job = [&](const JobIn<CB>& J, int ds, int r) {
     unsigned char* chunk = sB + ds * QC_BYTES;
     if constexpr (CB == 0) {
-      quant_job<GS>(J.w, dhv[ds], dhiv[ds], Nf, p, r, chunk);
+      quant_job<GS, QF>(J.w, dhv[ds], dhiv[ds], Nf, p, r, chunk);
     } else {
-      store_what(chunk, 0, r, p, dequant_half<CB, GS>(J, 0, dhiv[ds], p));
-      store_what(chunk, 1, r, p, dequant_half<CB, GS>(J, 1, dhiv[ds], p));
+      store_what(chunk, 0, r, p, dequant_half<CB, GS, QF == QF_FP8>(J, 0, dhiv[ds], p));
+      store_what(chunk, 1, r, p, dequant_half<CB, GS, QF == QF_FP8>(J, 1, dhiv[ds], p));
     }
   };
   // (issue order fixed: the first wait below counts on it, and the weights
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
     u32x4 fa[2][2], fb[2][2];
     u32x4 o0, o1;
     if constexpr (CB == 0) {
-      QuantJob<GS> J;
+      QuantJob<GS, QF> J;
       read_frags(sa, sb, 0, fa[0], fb[0]);
       J.scale(ring[QS].w, dhv[DS]);
       __builtin_amdgcn_sched_barrier(0);
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
       read_frags(sa, sb, 0, fa[0], fb[0]);
       read_frags(sa, sb, 1, fa[1], fb[1]);
       mfmas(fa[0], fb[0]);
-      o0 = dequant_half<CB, GS>(ring[QS], 0, dhiv[DS], p);
+      o0 = dequant_half<CB, GS, QF == QF_FP8>(ring[QS], 0, dhiv[DS], p);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(QNW * 64, 1) void k_gemm_q(GemmQArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       read_frags(sa, sb, 2, fa[0], fb[0]);
       mfmas(fa[1], fb[1]);
-      o1 = dequant_half<CB, GS>(ring[QS], 1, dhiv[DS], p);
+      o1 = dequant_half<CB, GS, QF == QF_FP8>(ring[QS], 1, dhiv[DS], p);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
@@ -617,23 +619,23 @@ bool gemm_q_supported(int64_t K1, int group, int cb) {
 
 namespace {
 
-template <int GS, int CB>
+template <int GS, int CB, int QF>
 hipError_t launch_gq(const GemmQArgs& a, dim3 grid, const Launch& L) {
   static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(k_gemm_q<GS, CB>),
+      reinterpret_cast<const void*>(k_gemm_q<GS, CB, QF>),
       hipFuncAttributeMaxDynamicSharedMemorySize, QLDS);
   if (attr != hipSuccess) return attr;
-  return ext_launch(k_gemm_q<GS, CB>, grid, dim3(QNW * 64), QLDS, L, a);
+  return ext_launch(k_gemm_q<GS, CB, QF>, grid, dim3(QNW * 64), QLDS, L, a);
 }
 
-template <int CB>
+template <int CB, int QF>
 hipError_t launch_gq_cb(const GemmQArgs& a, int group, dim3 grid, const Launch& L) {
   switch (group) {
-    case 32: return launch_gq<32, CB>(a, grid, L);
-    case 64: return launch_gq<64, CB>(a, grid, L);
-    case 128: return launch_gq<128, CB>(a, grid, L);
+    case 32: return launch_gq<32, CB, QF>(a, grid, L);
+    case 64: return launch_gq<64, CB, QF>(a, grid, L);
+    case 128: return launch_gq<128, CB, QF>(a, grid, L);
     case 256:
-      if constexpr (CB > 0) return launch_gq<256, CB>(a, grid, L);
+      if constexpr (CB > 0) return launch_gq<256, CB, QF>(a, grid, L);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -652,12 +654,24 @@ hipError_t launch_gemm_q(const GemmQArgs& a, int group, int cb, const Launch& L)
       ntiles >= 8 ? ((ntiles + 7) / 8) * 8 * mtiles : ntiles * mtiles;
   const unsigned nb = a.batch > 1 ? (unsigned)a.batch : 1u;
   const dim3 grid((unsigned)nblk, nb);
+  if (cb == 0) {
+    switch (a.qf) {
+      case QF_ASYM: return launch_gq_cb<0, QF_ASYM>(a, group, grid, L);
+      case QF_SYM: return launch_gq_cb<0, QF_SYM>(a, group, grid, L);
+      case QF_INTZP: return launch_gq_cb<0, QF_INTZP>(a, group, grid, L);
+      case QF_FP8: return launch_gq_cb<0, QF_FP8>(a, group, grid, L);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // stored codes: the integer formats share one decoding (u_hat = m + s q
+  // with the stored offset m); E4M3 codes are 8-bit
+  if (a.qf == QF_FP8)
+    return cb == 8 ? launch_gq_cb<8, QF_FP8>(a, group, grid, L) : hipErrorInvalidValue;
   switch (cb) {
-    case 0: return launch_gq_cb<0>(a, group, grid, L);
-    case 1: return launch_gq_cb<1>(a, group, grid, L);
-    case 2: return launch_gq_cb<2>(a, group, grid, L);
-    case 4: return launch_gq_cb<4>(a, group, grid, L);
-    case 8: return launch_gq_cb<8>(a, group, grid, L);
+    case 1: return launch_gq_cb<1, QF_ASYM>(a, group, grid, L);
+    case 2: return launch_gq_cb<2, QF_ASYM>(a, group, grid, L);
+    case 4: return launch_gq_cb<4, QF_ASYM>(a, group, grid, L);
+    case 8: return launch_gq_cb<8, QF_ASYM>(a, group, grid, L);
     default: return hipErrorInvalidValue;
   }
 }

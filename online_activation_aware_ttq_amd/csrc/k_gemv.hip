@@ -9,7 +9,8 @@
 //
 // the dequantized product (m + s q) D^{-1/2} x of "TTQ: Activation-Aware
 // Test-Time Quantization ..." (gist.science zh summary, Sec. 2.1), with the
-// per-group affine terms applied once per group.  x' stays in float32 and
+// per-group affine terms applied once per group (for the formats without a
+// real minimum, q is the signed level and the m term is absent).  x' stays in float32 and
 // the dot products run on the VALU (a 16x16 MFMA tile would be 1/16 used),
 // so the activation operand is never rounded to bf16.
 //
@@ -60,7 +61,7 @@ constexpr int gemv_waves() {
   return (GS <= 128 && !EXPORT) ? 16 : 8;
 }
 
-template <int GS, bool FAST, bool EXPORT>
+template <int GS, bool FAST, bool EXPORT, int QF>
 __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     GemvArgs a) {
   constexpr int VW = gemv_waves<GS, EXPORT>();
@@ -196,8 +197,10 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     mn = fminf(mn, __shfl_xor(mn, 32));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // s = fl(fl(M - m) / N), inv = fl(1 / s); IEEE division, no contraction
-    const float s = (mx - mn) / Nf;
-    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    // (other formats: see QFmt)
+    const QGroup gq = qgroup<QF>(mn, mx, Nf);
+    const float s = gq.s;
+    const float inv = gq.inv;
     // q = rint(fl(fl(u - m) * inv)) (the clamp to [0, N] is a no-op, see the
     // fused kernel); P = sum q x' over this lane's 32 channels
     float P = 0.f;
@@ -207,17 +210,20 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
       const f32x4 x1 = *(const f32x4*)(xp_s + colg + k * 32 + 4);
       const float xq[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       float q[8];
+      if constexpr (QF == QF_ASYM) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        q[j] = __builtin_rintf((u[k][j] - mn) * inv);
-        P = fmaf(q[j], xq[j], P);
+        for (int j = 0; j < 8; ++j) q[j] = __builtin_rintf((u[k][j] - mn) * inv);
+      } else {
+        qlevels8<QF>(gq, u[k], q);
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) P = fmaf(q[j], xq[j], P);
       if (EXPORT && a.codes_out && row_ok) {
         u32x2 c;
-        c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
-              ((unsigned)q[3] << 24);
-        c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
-              ((unsigned)q[7] << 24);
+        c.x = qcode<QF>(gq, q[0]) | (qcode<QF>(gq, q[1]) << 8) |
+              (qcode<QF>(gq, q[2]) << 16) | (qcode<QF>(gq, q[3]) << 24);
+        c.y = qcode<QF>(gq, q[4]) | (qcode<QF>(gq, q[5]) << 8) |
+              (qcode<QF>(gq, q[6]) << 16) | (qcode<QF>(gq, q[7]) << 24);
         *(u32x2*)(a.codes_out + ((int64_t)req * a.d_out + row) * d + colg +
                   k * 32) = c;
       }
@@ -225,10 +231,10 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     if (EXPORT && a.s_out && row_ok && qd == 0) {
       const int64_t o = ((int64_t)req * a.d_out + row) * G + gg;
       a.s_out[o] = s;
-      a.m_out[o] = mn;
+      a.m_out[o] = gq.off;
     }
     acc = fmaf(s, P, acc);
-    if (qd == 0) acc = fmaf(mn, sx_s[gg], acc);
+    if (QF == QF_ASYM && qd == 0) acc = fmaf(mn, sx_s[gg], acc);
   };
 
   // one group at a time: process it, then request the next one (past the
@@ -291,15 +297,24 @@ hipError_t launch_gemv(const GemvArgs& a, int group, const Launch& L) {
   // instantiation: conditional stores in the loop would make the compiler's
   // memory wait counts conservative on the timed path
   const bool exp = a.codes_out || a.s_out || a.dh_export;
-#define TTQ_GEMV_LAUNCH(GSV, F, E) \
-  ext_launch(k_gemv<GSV, F, E>, grid, dim3(gemv_waves<GSV, E>() * 64), lds, L, a)
-#define TTQ_GEMV_CASE(GSV)                                               \
-  case GSV:                                                              \
-    if (exp)                                                             \
-      return fast ? TTQ_GEMV_LAUNCH(GSV, true, true)                     \
-                  : TTQ_GEMV_LAUNCH(GSV, false, true);                   \
-    return fast ? TTQ_GEMV_LAUNCH(GSV, true, false)                      \
-                : TTQ_GEMV_LAUNCH(GSV, false, false);
+#define TTQ_GEMV_LAUNCH(GSV, F, E, QF)                                        \
+  ext_launch(k_gemv<GSV, F, E, QF>, grid, dim3(gemv_waves<GSV, E>() * 64), lds, \
+             L, a)
+#define TTQ_GEMV_FE(GSV, QF)                                                  \
+  if (exp)                                                                    \
+    return fast ? TTQ_GEMV_LAUNCH(GSV, true, true, QF)                        \
+                : TTQ_GEMV_LAUNCH(GSV, false, true, QF);                      \
+  return fast ? TTQ_GEMV_LAUNCH(GSV, true, false, QF)                         \
+              : TTQ_GEMV_LAUNCH(GSV, false, false, QF);
+#define TTQ_GEMV_CASE(GSV)                                                    \
+  case GSV:                                                                   \
+    switch (a.qf) {                                                           \
+      case QF_ASYM: TTQ_GEMV_FE(GSV, QF_ASYM)                                 \
+      case QF_SYM: TTQ_GEMV_FE(GSV, QF_SYM)                                   \
+      case QF_INTZP: TTQ_GEMV_FE(GSV, QF_INTZP)                               \
+      case QF_FP8: TTQ_GEMV_FE(GSV, QF_FP8)                                   \
+      default: return hipErrorInvalidValue;                                   \
+    }
   switch (group) {
     TTQ_GEMV_CASE(32)
     TTQ_GEMV_CASE(64)
@@ -308,6 +323,7 @@ hipError_t launch_gemv(const GemvArgs& a, int group, const Launch& L) {
     default: return hipErrorInvalidValue;
   }
 #undef TTQ_GEMV_CASE
+#undef TTQ_GEMV_FE
 #undef TTQ_GEMV_LAUNCH
 }
 

@@ -29,23 +29,31 @@ namespace ttq {
 namespace {
 
 // waves per workgroup: 16 where the registers allow (more groups in flight
-// per CU; the work per group is small), else 8
-template <int NTB, int GS>
+// per CU; the work per group is small), else 8 (also for the E4M3 decoding,
+// which needs more registers per code)
+template <int NTB, int GS, bool F8>
 constexpr int qf_waves() {
-  return (NTB <= 2 && GS <= 128) ? 16 : 8;
+  return (NTB <= 2 && GS <= 128 && !F8) ? 16 : 8;
 }
 
 // 8 codes of CB bits, low bits first in `raw` -> 4 bf16 pairs (see above)
-template <int CB>
+template <int CB, bool F8>
 __device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
+  static_assert(!F8 || CB == 8, "E4M3 codes are 8 bits wide");
   if (CB == 8) {
     float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[i] = (float)((raw.x >> (8 * i)) & 0xFFu);
-      f[4 + i] = (float)((raw.y >> (8 * i)) & 0xFFu);
+      if constexpr (F8) {
+        f[i] = e4m3_byte(raw.x, i);
+        f[4 + i] = e4m3_byte(raw.y, i);
+      } else {
+        f[i] = (float)((raw.x >> (8 * i)) & 0xFFu);
+        f[4 + i] = (float)((raw.y >> (8 * i)) & 0xFFu);
+      }
     }
-    // the high halves of the floats (exact: at most 8 significant bits)
+    // the high halves of the floats (exact: at most 8 significant bits, or
+    // the 4 of an E4M3 value)
     return u32x4{__builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u),
                  __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u),
                  __builtin_amdgcn_perm(__float_as_uint(f[5]), __float_as_uint(f[4]), 0x07060302u),
@@ -112,9 +120,9 @@ __device__ __forceinline__ u32x2 step_codes(const GroupCodes<CB, GS>& c, int k) 
   return u32x2{(c.w[k / 4] >> (8 * (k % 4))) & 0xFFu, 0u};
 }
 
-template <int CB, int NTB, int GS>
-__global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArgs a) {
-  constexpr int QF_W = qf_waves<NTB, GS>();
+template <int CB, int NTB, int GS, bool F8>
+__global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFusedArgs a) {
+  constexpr int QF_W = qf_waves<NTB, GS, F8>();
   constexpr int NKS = GS / 32;
   constexpr bool HILO = (NTB == 1);
   constexpr float BIAS = CB == 8 ? 0.f : 128.f;
@@ -174,7 +182,7 @@ __global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArg
     const float mb = a.m[srow + g] - BIAS * s;
     u32x4 qv[NKS];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB>(step_codes<CB, GS>(cv, k));
+    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB, F8>(step_codes<CB, GS>(cv, k));
     if (HILO) {
       f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -265,13 +273,13 @@ __global__ __launch_bounds__((qf_waves<NTB, GS>() * 64)) void k_qfused(QFusedArg
   }
 }
 
-template <int CB, int NTB>
+template <int CB, int NTB, bool F8>
 hipError_t launch_qf_ntb(const QFusedArgs& a, int group, dim3 grid,
                          const Launch& L) {
 #define TTQ_QF_CASE(GSV)                                                     \
   case GSV:                                                                  \
-    return ext_launch(k_qfused<CB, NTB, GSV>, grid,                          \
-                      dim3(qf_waves<NTB, GSV>() * 64), 0, L, a);
+    return ext_launch(k_qfused<CB, NTB, GSV, F8>, grid,                      \
+                      dim3(qf_waves<NTB, GSV, F8>() * 64), 0, L, a);
   switch (group) {
     TTQ_QF_CASE(32)
     TTQ_QF_CASE(64)
@@ -282,14 +290,14 @@ hipError_t launch_qf_ntb(const QFusedArgs& a, int group, dim3 grid,
 #undef TTQ_QF_CASE
 }
 
-template <int CB>
+template <int CB, bool F8 = false>
 hipError_t launch_qf_cb(const QFusedArgs& a, int ntb, int group, dim3 grid,
                         const Launch& L) {
   switch (ntb) {
-    case 1: return launch_qf_ntb<CB, 1>(a, group, grid, L);
-    case 2: return launch_qf_ntb<CB, 2>(a, group, grid, L);
-    case 4: return launch_qf_ntb<CB, 4>(a, group, grid, L);
-    case 8: return launch_qf_ntb<CB, 8>(a, group, grid, L);
+    case 1: return launch_qf_ntb<CB, 1, F8>(a, group, grid, L);
+    case 2: return launch_qf_ntb<CB, 2, F8>(a, group, grid, L);
+    case 4: return launch_qf_ntb<CB, 4, F8>(a, group, grid, L);
+    case 8: return launch_qf_ntb<CB, 8, F8>(a, group, grid, L);
     default: return hipErrorInvalidValue;
   }
 }
@@ -302,6 +310,8 @@ hipError_t launch_qfused(const QFusedArgs& a, int ntb, int group, int cb,
   if (nblk == 0 || a.T == 0) return hipSuccess;
   if (a.T > 16 * ntb || (ntb == 1 && a.T > 16)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nblk);
+  if (a.qf == QF_FP8)
+    return cb == 8 ? launch_qf_cb<8, true>(a, ntb, group, grid, L) : hipErrorInvalidValue;
   switch (cb) {
     case 1: return launch_qf_cb<1>(a, ntb, group, grid, L);
     case 2: return launch_qf_cb<2>(a, ntb, group, grid, L);

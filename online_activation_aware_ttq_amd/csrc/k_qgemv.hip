@@ -33,18 +33,21 @@ constexpr int QW = 8;    // waves per workgroup
 constexpr int QRPW = 2;  // rows per wave
 constexpr int QNB = 4;   // 1 KiB loads in flight per row
 
-// float value of code j (0 .. 128/CB - 1) of a 16-byte piece
-template <int CB>
+// float value of code j (0 .. 128/CB - 1) of a 16-byte piece (F8: E4M3
+// codes, CB = 8)
+template <int CB, bool F8>
 __device__ __forceinline__ float code_at(const u32x4& v, int j) {
+  static_assert(!F8 || CB == 8, "E4M3 codes are 8 bits wide");
   constexpr int PER = 32 / CB;  // codes per 32-bit word
   const unsigned w = j / PER < 2 ? (j / PER == 0 ? v.x : v.y)
                                  : (j / PER == 2 ? v.z : v.w);
   const int sh = (j % PER) * CB;
+  if constexpr (F8) return e4m3_byte(w, j % PER);
   if (CB == 8) return (float)((w >> sh) & 0xffu);
   return (float)__builtin_amdgcn_ubfe(w, sh, CB);
 }
 
-template <int CB, int GS>
+template <int CB, int GS, bool F8>
 __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
   constexpr int VPL = 128 / CB;                 // codes per lane per load
   constexpr int SUB = VPL < GS ? VPL : GS;      // channels per slice
@@ -164,10 +167,10 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
           for (int i = 0; i < SUB; i += 4) {
             const f32x4 xq = *(const f32x4*)(
                 xp + ((k * (VPL / 4) + (sb * SUB + i) / 4) * 64 + l) * 4);
-            P0 = fmaf(code_at<CB>(v[rr][j], sb * SUB + i + 0), xq.x, P0);
-            P1 = fmaf(code_at<CB>(v[rr][j], sb * SUB + i + 1), xq.y, P1);
-            P2 = fmaf(code_at<CB>(v[rr][j], sb * SUB + i + 2), xq.z, P2);
-            P3 = fmaf(code_at<CB>(v[rr][j], sb * SUB + i + 3), xq.w, P3);
+            P0 = fmaf(code_at<CB, F8>(v[rr][j], sb * SUB + i + 0), xq.x, P0);
+            P1 = fmaf(code_at<CB, F8>(v[rr][j], sb * SUB + i + 1), xq.y, P1);
+            P2 = fmaf(code_at<CB, F8>(v[rr][j], sb * SUB + i + 2), xq.z, P2);
+            P3 = fmaf(code_at<CB, F8>(v[rr][j], sb * SUB + i + 3), xq.w, P3);
           }
           const float P = (P0 + P1) + (P2 + P3);
           acc = fmaf(sg[rr][j][sb], P,
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
   }
 }
 
-template <int CB, int GS>
+template <int CB, int GS, bool F8>
 __global__ __launch_bounds__(256) void k_dequant(DequantArgs a) {
   constexpr int VPL = 128 / CB;
   const int64_t lanes_per_row = a.row_bytes / 16;
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(256) void k_dequant(DequantArgs a) {
     const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
     float wv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wv[i] = fmaf(sg, code_at<CB>(v, j + i), mg) * hv[i];
+    for (int i = 0; i < 8; ++i) wv[i] = fmaf(sg, code_at<CB, F8>(v, j + i), mg) * hv[i];
     *(u32x4*)(out + j) = u32x4{pack_bf16(wv[0], wv[1]), pack_bf16(wv[2], wv[3]),
                                pack_bf16(wv[4], wv[5]), pack_bf16(wv[6], wv[7])};
   }
@@ -229,19 +232,23 @@ hipError_t launch_qgemv(const QGemvArgs& a, int group, int cb,
   if (a.row_bytes % 16 != 0) return hipErrorInvalidValue;
   const uint32_t lds = (uint32_t)qgemv_lds_bytes(a.d, cb, group);
   const dim3 grid((unsigned)nblk), blk(QW * 64);
-#define TTQ_QGEMV_GS(CBV)                                                     \
+#define TTQ_QGEMV_GS(CBV, F8)                                                 \
   switch (group) {                                                            \
-    case 32: return ext_launch(k_qgemv<CBV, 32>, grid, blk, lds, L, a);       \
-    case 64: return ext_launch(k_qgemv<CBV, 64>, grid, blk, lds, L, a);       \
-    case 128: return ext_launch(k_qgemv<CBV, 128>, grid, blk, lds, L, a);     \
-    case 256: return ext_launch(k_qgemv<CBV, 256>, grid, blk, lds, L, a);     \
+    case 32: return ext_launch(k_qgemv<CBV, 32, F8>, grid, blk, lds, L, a);   \
+    case 64: return ext_launch(k_qgemv<CBV, 64, F8>, grid, blk, lds, L, a);   \
+    case 128: return ext_launch(k_qgemv<CBV, 128, F8>, grid, blk, lds, L, a); \
+    case 256: return ext_launch(k_qgemv<CBV, 256, F8>, grid, blk, lds, L, a); \
     default: return hipErrorInvalidValue;                                     \
   }
+  if (a.qf == QF_FP8) {
+    if (cb != 8) return hipErrorInvalidValue;
+    TTQ_QGEMV_GS(8, true)
+  }
   switch (cb) {
-    case 1: TTQ_QGEMV_GS(1)
-    case 2: TTQ_QGEMV_GS(2)
-    case 4: TTQ_QGEMV_GS(4)
-    case 8: TTQ_QGEMV_GS(8)
+    case 1: TTQ_QGEMV_GS(1, false)
+    case 2: TTQ_QGEMV_GS(2, false)
+    case 4: TTQ_QGEMV_GS(4, false)
+    case 8: TTQ_QGEMV_GS(8, false)
     default: return hipErrorInvalidValue;
   }
 #undef TTQ_QGEMV_GS
@@ -253,19 +260,23 @@ hipError_t launch_dequant(const DequantArgs& a, int group, int cb,
   const int64_t threads = a.d_out * (a.row_bytes / 16);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
-#define TTQ_DEQ_GS(CBV)                                                       \
+#define TTQ_DEQ_GS(CBV, F8)                                                   \
   switch (group) {                                                            \
-    case 32: return ext_launch(k_dequant<CBV, 32>, grid, blk, 0, L, a);       \
-    case 64: return ext_launch(k_dequant<CBV, 64>, grid, blk, 0, L, a);       \
-    case 128: return ext_launch(k_dequant<CBV, 128>, grid, blk, 0, L, a);     \
-    case 256: return ext_launch(k_dequant<CBV, 256>, grid, blk, 0, L, a);     \
+    case 32: return ext_launch(k_dequant<CBV, 32, F8>, grid, blk, 0, L, a);   \
+    case 64: return ext_launch(k_dequant<CBV, 64, F8>, grid, blk, 0, L, a);   \
+    case 128: return ext_launch(k_dequant<CBV, 128, F8>, grid, blk, 0, L, a); \
+    case 256: return ext_launch(k_dequant<CBV, 256, F8>, grid, blk, 0, L, a); \
     default: return hipErrorInvalidValue;                                     \
   }
+  if (a.qf == QF_FP8) {
+    if (cb != 8) return hipErrorInvalidValue;
+    TTQ_DEQ_GS(8, true)
+  }
   switch (cb) {
-    case 1: TTQ_DEQ_GS(1)
-    case 2: TTQ_DEQ_GS(2)
-    case 4: TTQ_DEQ_GS(4)
-    case 8: TTQ_DEQ_GS(8)
+    case 1: TTQ_DEQ_GS(1, false)
+    case 2: TTQ_DEQ_GS(2, false)
+    case 4: TTQ_DEQ_GS(4, false)
+    case 8: TTQ_DEQ_GS(8, false)
     default: return hipErrorInvalidValue;
   }
 #undef TTQ_DEQ_GS

@@ -16,10 +16,11 @@ namespace ttq {
 
 constexpr int QROWS = 8;  // weight rows per wave (D^{+-1/2} reused across them)
 
-// CB = 0: write W_hat (and optional byte codes, scales, minima);
+// CB = 0: write W_hat (and optional byte codes, scales, group offsets);
 // CB = 1, 2, 4, 8: write the codes packed in CB-bit containers instead of
 // W_hat (channel j of a row at bit (j*CB) % 8 of byte (j*CB) / 8).
-template <int GS, int CB>
+// QF: the quantizer format (QFmt; W_hat = bf16((c + s L) D^{-1/2})).
+template <int GS, int CB, int QF>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   constexpr int LPG = GS / 8;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -89,13 +90,13 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
       mn = fminf(mn, __shfl_xor(mn, off));
       mx = fmaxf(mx, __shfl_xor(mx, off));
     }
-    const float s = (mx - mn) / Nf;
-    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    const QGroup gq = qgroup<QF>(mn, mx, Nf);
+    const float s = gq.s;
     float q[8];
+    unsigned qc[8];
+    qlevels8<QF>(gq, u, q);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      q[j] = __builtin_amdgcn_fmed3f(__builtin_rintf((u[j] - mn) * inv), 0.f,
-                                     Nf);
+    for (int j = 0; j < 8; ++j) qc[j] = qcode<QF>(gq, q[j]);
     if (!live || row >= a.d_out) continue;
     if (CB > 0) {
       // 8 codes of this lane -> 8*CB bits, one aligned store
@@ -103,15 +104,13 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
                      row * a.row_bytes + c0 * CB / 8;
       if (CB == 8) {
         u32x2 c;
-        c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
-              ((unsigned)q[3] << 24);
-        c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
-              ((unsigned)q[7] << 24);
+        c.x = qc[0] | (qc[1] << 8) | (qc[2] << 16) | (qc[3] << 24);
+        c.y = qc[4] | (qc[5] << 8) | (qc[6] << 16) | (qc[7] << 24);
         *(u32x2*)dst = c;
       } else {
         unsigned c = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c |= (unsigned)q[j] << (j * CB);
+        for (int j = 0; j < 8; ++j) c |= qc[j] << (j * CB);
         if (CB == 4) *(unsigned*)dst = c;
         else if (CB == 2) *(uint16_t*)dst = (uint16_t)c;
         else *dst = (uint8_t)c;
@@ -119,28 +118,27 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
       if (s_out && (l % LPG) == 0) {
         const int64_t o2 = row * a.G + c0 / GS;
         s_out[o2] = s;
-        m_out[o2] = mn;
+        m_out[o2] = gq.off;
       }
       continue;
     }
+    const float c = gq.c;
     u32x4 o;
-    o.x = pack_bf16(fmaf(s, q[0], mn) * dhi[0], fmaf(s, q[1], mn) * dhi[1]);
-    o.y = pack_bf16(fmaf(s, q[2], mn) * dhi[2], fmaf(s, q[3], mn) * dhi[3]);
-    o.z = pack_bf16(fmaf(s, q[4], mn) * dhi[4], fmaf(s, q[5], mn) * dhi[5]);
-    o.w = pack_bf16(fmaf(s, q[6], mn) * dhi[6], fmaf(s, q[7], mn) * dhi[7]);
+    o.x = pack_bf16(fmaf(s, q[0], c) * dhi[0], fmaf(s, q[1], c) * dhi[1]);
+    o.y = pack_bf16(fmaf(s, q[2], c) * dhi[2], fmaf(s, q[3], c) * dhi[3]);
+    o.z = pack_bf16(fmaf(s, q[4], c) * dhi[4], fmaf(s, q[5], c) * dhi[5]);
+    o.w = pack_bf16(fmaf(s, q[6], c) * dhi[6], fmaf(s, q[7], c) * dhi[7]);
     *(u32x4*)(What + row * a.d + c0) = o;
     if (codes_out) {
-      u32x2 c;
-      c.x = (unsigned)q[0] | ((unsigned)q[1] << 8) | ((unsigned)q[2] << 16) |
-            ((unsigned)q[3] << 24);
-      c.y = (unsigned)q[4] | ((unsigned)q[5] << 8) | ((unsigned)q[6] << 16) |
-            ((unsigned)q[7] << 24);
-      *(u32x2*)(codes_out + row * a.d + c0) = c;
+      u32x2 cc;
+      cc.x = qc[0] | (qc[1] << 8) | (qc[2] << 16) | (qc[3] << 24);
+      cc.y = qc[4] | (qc[5] << 8) | (qc[6] << 16) | (qc[7] << 24);
+      *(u32x2*)(codes_out + row * a.d + c0) = cc;
     }
     if (s_out && (l % LPG) == 0) {
       const int64_t o2 = row * a.G + c0 / GS;
       s_out[o2] = s;
-      m_out[o2] = mn;
+      m_out[o2] = gq.off;
     }
   }
 }
@@ -151,23 +149,32 @@ hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L) {
   const int64_t nblk1 = (waves + 3) / 4;
   if (nblk1 == 0 || a.R == 0) return hipSuccess;
   const dim3 grid((unsigned)(((nblk1 + 7) / 8) * 8 * a.R)), blk(256);
-#define TTQ_QUANT_CB(GSV)                                                   \
-  case GSV:                                                                 \
-    switch (a.packed ? a.cb : 0) {                                          \
-      case 0: return ext_launch(k_quant<GSV, 0>, grid, blk, 0, L, a);       \
-      case 1: return ext_launch(k_quant<GSV, 1>, grid, blk, 0, L, a);       \
-      case 2: return ext_launch(k_quant<GSV, 2>, grid, blk, 0, L, a);       \
-      case 4: return ext_launch(k_quant<GSV, 4>, grid, blk, 0, L, a);       \
-      case 8: return ext_launch(k_quant<GSV, 8>, grid, blk, 0, L, a);       \
-      default: return hipErrorInvalidValue;                                 \
+#define TTQ_QUANT_CB(GSV, QF)                                                  \
+  switch (a.packed ? a.cb : 0) {                                               \
+    case 0: return ext_launch(k_quant<GSV, 0, QF>, grid, blk, 0, L, a);        \
+    case 1: return ext_launch(k_quant<GSV, 1, QF>, grid, blk, 0, L, a);        \
+    case 2: return ext_launch(k_quant<GSV, 2, QF>, grid, blk, 0, L, a);        \
+    case 4: return ext_launch(k_quant<GSV, 4, QF>, grid, blk, 0, L, a);        \
+    case 8: return ext_launch(k_quant<GSV, 8, QF>, grid, blk, 0, L, a);        \
+    default: return hipErrorInvalidValue;                                      \
+  }
+#define TTQ_QUANT_GS(GSV)                                                      \
+  case GSV:                                                                    \
+    switch (a.qf) {                                                            \
+      case QF_ASYM: TTQ_QUANT_CB(GSV, QF_ASYM)                                 \
+      case QF_SYM: TTQ_QUANT_CB(GSV, QF_SYM)                                   \
+      case QF_INTZP: TTQ_QUANT_CB(GSV, QF_INTZP)                               \
+      case QF_FP8: TTQ_QUANT_CB(GSV, QF_FP8)                                   \
+      default: return hipErrorInvalidValue;                                    \
     }
   switch (group) {
-    TTQ_QUANT_CB(32)
-    TTQ_QUANT_CB(64)
-    TTQ_QUANT_CB(128)
-    TTQ_QUANT_CB(256)
+    TTQ_QUANT_GS(32)
+    TTQ_QUANT_GS(64)
+    TTQ_QUANT_GS(128)
+    TTQ_QUANT_GS(256)
     default: return hipErrorInvalidValue;
   }
+#undef TTQ_QUANT_GS
 #undef TTQ_QUANT_CB
 }
 

@@ -67,6 +67,9 @@ int validate_params(const ttq_params* prm, int64_t R) {
   if (prm->T < 0 || prm->T > kMaxT) return TTQ_EINVAL;
   if (prm->rank < 0) return TTQ_EINVAL;
   if (prm->bits < 1 || prm->bits > 8) return TTQ_EINVAL;
+  if (prm->qformat > TTQ_QF_FP8) return TTQ_EINVAL;
+  if (prm->qformat == TTQ_QF_SYM && prm->bits < 2) return TTQ_EINVAL;
+  if (prm->qformat == TTQ_QF_FP8 && prm->bits != 8) return TTQ_EINVAL;
   if (prm->group <= 0 || prm->d % prm->group != 0) return TTQ_EINVAL;
   if (!(std::isfinite(prm->p) && prm->p > 0.0)) return TTQ_EINVAL;
   if (!finite_nonneg(prm->lambda) || !finite_nonneg(prm->alpha))
@@ -317,6 +320,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     va.Y = Y; va.rowblocks = P.rowblocks; va.R = (int)R;
     va.codes_out = codes_out; va.s_out = scales_out; va.m_out = mins_out;
     va.dh_export = dhalf_out;
+    va.qf = (int)prm->qformat;
     if (dout == 0) {  // statistics only: the gemv kernel needs a row block
       StatsSmallArgs sa{};
       sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = pmode;
@@ -351,6 +355,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     fa.rowblocks = P.rowblocks;
     fa.R = (int)R;
     fa.codes_out = codes_out; fa.s_out = scales_out; fa.m_out = mins_out;
+    fa.qf = (int)prm->qformat;
     return run(K_FUSED, s, [&](const Launch& L) { return launch_fused(fa, P.ntb, prm->group, L); });
   }
 
@@ -381,6 +386,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     qa.M = T; qa.N = dout; qa.C = Y; qa.ldc = dout;
     qa.batch = (int)R;
     qa.sX = T * d; qa.sA2 = T * P.rp; qa.sC = T * dout;
+    qa.qf = (int)prm->qformat;
     return run(K_GEMM_Q, s, [&](const Launch& L) { return launch_gemm_q(qa, prm->group, 0, L); });
   }
   // requests in chunks of P.rchunk: one quantize pass (each request its own
@@ -394,6 +400,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     qa.codes_out = codes_out ? codes_out + r0 * dout * d : nullptr;
     qa.s_out = scales_out ? scales_out + r0 * dout * P.G : nullptr;
     qa.m_out = mins_out ? mins_out + r0 * dout * P.G : nullptr;
+    qa.qf = (int)prm->qformat;
     st = run(K_QUANT, s, [&](const Launch& L) { return launch_quant(qa, prm->group, L); });
     if (st != TTQ_OK) return st;
     GemmArgs ga{};
@@ -558,6 +565,7 @@ int quantize_impl(const ttq_params* prm, const void* W, const void* X,
   qa.dh = dh; qa.dhi = dhalf_inv;
   qa.s_out = scales; qa.m_out = mins;
   qa.packed = codes; qa.cb = container_bits(q.bits); qa.row_bytes = rb;
+  qa.qf = (int)q.qformat;
   return run(K_QUANT, s, [&](const Launch& L) { return launch_quant(qa, q.group, L); });
 }
 
@@ -603,6 +611,7 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     ga.packed = codes; ga.row_bytes = rb; ga.s = scales; ga.m = mins;
     ga.dhi = dhalf_inv; ga.X = Xb; ga.d = d; ga.d_out = dout; ga.G = P.G;
     ga.Z = Zb; ga.Blr = Bb; ga.rank = (int)rank; ga.Y = Y;
+    ga.qf = (int)q.qformat;
     return run(K_QGEMV, s, [&](const Launch& L) { return launch_qgemv(ga, q.group, cb, L); });
   }
   if (P.path == 0) {
@@ -627,6 +636,7 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     fa.d = d; fa.d_out = dout; fa.T = T; fa.G = P.G;
     fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
     fa.Y = Y;
+    fa.qf = (int)q.qformat;
     return run(K_QFUSED, s, [&](const Launch& L) { return launch_qfused(fa, P.ntb, q.group, cb, L); });
   }
   if (P.path == 3) {
@@ -643,12 +653,14 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     }
     qa.M = T; qa.N = dout; qa.C = Y; qa.ldc = dout;
     qa.batch = 1;
+    qa.qf = (int)q.qformat;
     return run(K_GEMM_Q, s, [&](const Launch& L) { return launch_gemm_q(qa, q.group, cb, L); });
   }
   bf16_t* What = reinterpret_cast<bf16_t*>(ws + P.off_what);
   DequantArgs da{};
   da.packed = codes; da.row_bytes = rb; da.s = scales; da.m = mins;
   da.dhi = dhalf_inv; da.d = d; da.d_out = dout; da.G = P.G; da.What = What;
+  da.qf = (int)q.qformat;
   st = run(K_DEQUANT, s, [&](const Launch& L) { return launch_dequant(da, q.group, cb, L); });
   if (st != TTQ_OK) return st;
   if (P.rp > 0) {

@@ -96,6 +96,144 @@ __device__ __forceinline__ void lds_barrier() {
 // offsets of a weight tile stay far below 2^30)
 constexpr uint32_t kOutOfRange = 0x40000000u;
 
+// ---------------------------------------------------------------- formats
+// Quantizer formats Q (the method leaves the code format open: the
+// lo0 blog "Test-time quantization: quantising on the fly with no
+// calibration dataset", section "What TTQ is NOT", calls it orthogonal to
+// INT4 or FP8 codes).  For a group of u = w D^{1/2} with minimum mn and
+// maximum mx every format decides a level L per element in float32 and
+// reconstructs u_hat = s L + c:
+//   QF_ASYM   s = (mx - mn) / N, c = mn, L = rint((u - mn) inv) in [0, N],
+//             code L                                  (the default)
+//   QF_SYM    s = max(-mn, mx) / Z, Z = 2^{b-1} - 1, c = 0,
+//             L = clamp(rint(u inv), -Z, Z), code L + Z
+//   QF_INTZP  lo = min(mn, 0), hi = max(mx, 0), s = (hi - lo) / N, c = 0,
+//             z = rint(lo inv), L = clamp(rint(u inv), z, z + N), code L - z
+//             (the affine form with an integer zero point: zero is exact)
+//   QF_FP8    s = max(-mn, mx) / 448, c = 0, L = E4M3 rounding of
+//             clamp(u inv, -448, 448) (nearest, ties to even), code = the
+//             E4M3 bit pattern (OCP FP8, bias 7, no infinities; the sign
+//             bit is that of u inv, also when L is zero)
+// with inv = 1/s (0 when s = 0) and no fused operations.  Every level is
+// exact in bf16 (integers of at most 9 bits, or 4 significant bits), so it
+// can be an MFMA operand.  Beside the scales the library stores a per-group
+// offset `off` with u_hat = off + s code for the integer formats (QF_SYM:
+// -(Z s), QF_INTZP: z s; both one float32 rounding away from the exact
+// reconstruction); it is 0 for QF_FP8, whose codes decode to E4M3 values.
+enum QFmt : int { QF_ASYM = 0, QF_SYM = 1, QF_INTZP = 2, QF_FP8 = 3 };
+
+struct QGroup {
+  float s, inv;
+  float c;       // subtracted before the scaling, added back in u_hat
+  float lo, hi;  // level range
+  float off;     // stored offset
+};
+
+// the group scale s of a format
+template <int QF>
+__device__ __forceinline__ float qscale(float mn, float mx, float Nf) {
+  if constexpr (QF == QF_ASYM) return (mx - mn) / Nf;
+  else if constexpr (QF == QF_INTZP) return (fmaxf(mx, 0.f) - fminf(mn, 0.f)) / Nf;
+  else if constexpr (QF == QF_SYM) return fmaxf(-mn, mx) / ((Nf - 1.f) * 0.5f);
+  else return fmaxf(-mn, mx) / 448.f;
+}
+
+// the rest of the group's constants, given s and inv = 1/s (0 if s = 0)
+template <int QF>
+__device__ __forceinline__ QGroup qgroup_si(float mn, float s, float inv,
+                                            float Nf) {
+  QGroup g;
+  g.s = s;
+  g.inv = inv;
+  g.c = QF == QF_ASYM ? mn : 0.f;
+  if constexpr (QF == QF_ASYM) {
+    g.lo = 0.f;
+    g.hi = Nf;
+    g.off = mn;
+  } else if constexpr (QF == QF_INTZP) {
+    g.lo = __builtin_rintf(fminf(mn, 0.f) * inv);
+    g.hi = g.lo + Nf;
+    g.off = g.lo * s;
+  } else if constexpr (QF == QF_SYM) {
+    g.hi = (Nf - 1.f) * 0.5f;
+    g.lo = -g.hi;
+    g.off = -(g.hi * s);
+  } else {
+    g.lo = -448.f;
+    g.hi = 448.f;
+    g.off = 0.f;
+  }
+  return g;
+}
+
+template <int QF>
+__device__ __forceinline__ QGroup qgroup(float mn, float mx, float Nf) {
+  const float s = qscale<QF>(mn, mx, Nf);
+  return qgroup_si<QF>(mn, s, s > 0.f ? 1.0f / s : 0.f, Nf);
+}
+
+// E4M3 on the gfx950 conversion unit: v_cvt_pk_fp8_f32 rounds to the
+// nearest E4M3 value (ties to even, the sign kept, also for a zero result)
+// and writes its bit pattern; v_cvt_f32_fp8 decodes a pattern.  On |t| <=
+// 448 they agree bit for bit with the E4M3 definition (checked on MI355X over
+// every float32 input of that range and every code).
+__device__ __forceinline__ unsigned e4m3_code(float t) {
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xffu;
+}
+__device__ __forceinline__ float e4m3_value(unsigned c) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+}
+// value of byte b (0..3, a compile-time constant after unrolling) of w
+__device__ __forceinline__ float e4m3_byte(unsigned w, int b) {
+  switch (b & 3) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+
+template <int QF>
+__device__ __forceinline__ float qlevel(const QGroup& g, float u) {
+  if constexpr (QF == QF_ASYM)
+    return __builtin_amdgcn_fmed3f(__builtin_rintf((u - g.c) * g.inv), 0.f, g.hi);
+  else if constexpr (QF == QF_FP8)
+    return e4m3_value(e4m3_code(__builtin_amdgcn_fmed3f(u * g.inv, g.lo, g.hi)));
+  else
+    return __builtin_amdgcn_fmed3f(__builtin_rintf(u * g.inv), g.lo, g.hi);
+}
+
+// levels of 8 elements; QF_FP8 converts pairs (one instruction each way per
+// two elements)
+template <int QF>
+__device__ __forceinline__ void qlevels8(const QGroup& g, const float (&u)[8],
+                                         float (&L)[8]) {
+  if constexpr (QF == QF_FP8) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const int c = __builtin_amdgcn_cvt_pk_fp8_f32(
+          __builtin_amdgcn_fmed3f(u[j] * g.inv, g.lo, g.hi),
+          __builtin_amdgcn_fmed3f(u[j + 1] * g.inv, g.lo, g.hi), 0, false);
+      const f2 v = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+      L[j] = v.x;
+      L[j + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) L[j] = qlevel<QF>(g, u[j]);
+  }
+}
+
+template <int QF>
+__device__ __forceinline__ unsigned qcode(const QGroup& g, float L) {
+  if constexpr (QF == QF_SYM) return (unsigned)(L + g.hi);
+  else if constexpr (QF == QF_INTZP) return (unsigned)(L - g.lo);
+  else if constexpr (QF == QF_FP8) return e4m3_code(L);
+  else return (unsigned)L;
+}
+
+
 // Scaled activations x' = x D^{-1/2} as the fused kernels' MFMA operand, in
 // MFMA fragment order over Tp = 16 * ceil(T / 16) tokens (zeros past T): the
 // 16-byte fragment of lane l for group g, 16-token block tb and MFMA step k
@@ -185,6 +323,7 @@ struct FusedArgs {
   uint8_t* codes_out;   // [R][d_out][d]
   float* s_out;         // [R][d_out][G]
   float* m_out;         // [R][d_out][G]
+  int qf;               // quantizer format (QFmt)
 };
 // D^{1/2} is staged in LDS when it fits in this many bytes.
 constexpr size_t kFusedDhLdsMax = 64 * 1024;
@@ -209,6 +348,7 @@ struct GemvArgs {
   float* s_out;         // [R][d_out][G]
   float* m_out;
   float* dh_export;     // [R][d]
+  int qf;               // quantizer format (QFmt)
 };
 // the single-launch T = 1 kernel holds all of D^{1/2} and x' in LDS
 constexpr int64_t kGemvMaxD = 12288;
@@ -231,6 +371,7 @@ struct QuantArgs {
   uint8_t* packed;      // [R][d_out][row_bytes]
   int cb;               // container bits 1, 2, 4, 8
   int64_t row_bytes;    // d * cb / 8
+  int qf;               // quantizer format (QFmt)
 };
 hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L);
 
@@ -250,6 +391,7 @@ struct QGemvArgs {
   const bf16_t* Blr;      // [d_out][rank] or null
   int rank;
   float* Y;               // [d_out]
+  int qf;                 // QF_FP8: E4M3 codes; any other format: integer codes
 };
 hipError_t launch_qgemv(const QGemvArgs& a, int group, int cb, const Launch& L);
 size_t qgemv_lds_bytes(int64_t d, int cb, int group);
@@ -264,6 +406,7 @@ struct DequantArgs {
   int64_t d, d_out;
   int G;
   bf16_t* What;           // [d_out][d]
+  int qf;                 // QF_FP8: E4M3 codes; any other format: integer codes
 };
 hipError_t launch_dequant(const DequantArgs& a, int group, int cb,
                           const Launch& L);
@@ -284,6 +427,7 @@ struct QFusedArgs {
   const bf16_t* Blr;      // [d_out][rank] or null
   int rank, rp;
   float* Y;               // [T][d_out]
+  int qf;                 // QF_FP8: E4M3 codes; any other format: integer codes
 };
 hipError_t launch_qfused(const QFusedArgs& a, int ntb, int group, int cb,
                          const Launch& L);
@@ -341,6 +485,8 @@ struct GemmQArgs {
   float* C; int64_t ldc;
   int batch;
   int64_t sX, sA2, sC;  // per-product strides (elements); D^{+-1/2}: K1
+  int qf;               // quantizer format (QFmt); with codes: QF_FP8 decodes
+                        // E4M3 codes, every other value integer codes
 };
 hipError_t launch_gemm_q(const GemmQArgs& a, int group, int cb, const Launch& L);
 // K1 a multiple of 128; groups of 32, 64 or 128 channels (also 256 when

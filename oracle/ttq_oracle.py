@@ -451,8 +451,9 @@ def symmetric_quantize(x: np.ndarray, bits: int):
 #            one float32 scale per group from the D-scaled weights
 #            (TTQ over FP8, [BLOG-EN] "What TTQ is NOT"): s = max|u| / 448,
 #            value v = E4M3 rounding (nearest, ties to even mantissa) of u / s,
-#            u_hat = s v; stored code = the E4M3 bit pattern (a zero is
-#            stored as +0)
+#            u_hat = s v; stored code = the E4M3 bit pattern of v, whose sign
+#            bit is the sign of u / s (a conversion to a floating-point format
+#            keeps the sign, also of a result that rounds to zero)
 # --------------------------------------------------------------------------
 QFORMATS = ("asym", "sym", "intzp", "fp8")
 E4M3_MAX = 448.0
@@ -478,7 +479,8 @@ def _e4m3_nonneg_grid():
 
 def e4m3_round(t: np.ndarray) -> np.ndarray:
     """Round each finite |t| <= 448 to the nearest E4M3 value; a tie goes to
-    the neighbour with the even mantissa (its code is even).  float64 out."""
+    the neighbour with the even mantissa (its code is even); the sign of t
+    is kept (also for a zero result).  float64 out."""
     t = np.asarray(t, dtype=np.float64)
     if np.any(np.abs(t) > E4M3_MAX):
         raise ValueError("outside the E4M3 range")
@@ -490,18 +492,19 @@ def e4m3_round(t: np.ndarray) -> np.ndarray:
     dhi = vals[hi] - a
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
     r = np.where(pick_hi, vals[hi], vals[lo])
-    return np.where(t < 0, -r, r)
+    return np.where(np.signbit(t), -r, r)
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
-    """Bit pattern of exact E4M3 values; the sign bit is set only for v < 0."""
+    """Bit pattern of exact E4M3 values; the sign bit is the sign bit of v
+    (a negative zero is 0x80)."""
     v = np.asarray(v, dtype=np.float64)
     vals, codes = _e4m3_nonneg_grid()
     a = np.abs(v)
     idx = np.searchsorted(vals, a)
     if np.any(idx >= len(vals)) or np.any(vals[np.minimum(idx, len(vals) - 1)] != a):
         raise ValueError("not an E4M3 value")
-    return (codes[idx] | np.where(v < 0, 0x80, 0)).astype(np.uint8)
+    return (codes[idx] | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
 
 
 def _grouped_u32(W32, dh32, group):

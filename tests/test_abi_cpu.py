@@ -94,6 +94,9 @@ def test_status_strings_and_version():
     (dict(flags=3), ttq.TTQ_EINVAL),
     (dict(flags=4), ttq.TTQ_EINVAL),
     (dict(T=129, flags=1), ttq.TTQ_EUNSUPPORTED),
+    (dict(qformat=4), ttq.TTQ_EINVAL),
+    (dict(qformat=1, bits=1), ttq.TTQ_EINVAL),  # symmetric needs b >= 2
+    (dict(qformat=3, bits=4), ttq.TTQ_EINVAL),  # E4M3 codes are 8 bits
 ])
 def test_invalid_params_rejected_everywhere(kw, status):
     p = prm(**kw)
@@ -109,8 +112,17 @@ def test_valid_edge_params_accepted():
     for kw in (dict(bits=1), dict(bits=8), dict(group=32, d=32), dict(d_out=0),
                dict(T=0), dict(rank=8), dict(rank=1024), dict(alpha=0.0),
                dict(lam=0.0), dict(p=0.37), dict(group=256, d=512),
-               dict(T=128, flags=1), dict(T=1, flags=2)):
+               dict(T=128, flags=1), dict(T=1, flags=2), dict(qformat=1, bits=2),
+               dict(qformat=2, bits=1), dict(qformat=3, bits=8)):
         assert ttq.ttq_workspace_bytes(prm(**kw)) >= 0, kw
+
+
+def test_format_names_map_to_the_header_values():
+    assert ttq.QFORMATS == {"asym": 0, "sym": 1, "intzp": 2, "fp8": 3}
+    assert ttq.make_params(d=128, d_out=1, T=1, bits=8, group=128, p=2.0,
+                           lam=0.0, alpha=0.5, qformat="fp8").qformat == 3
+    with pytest.raises(ValueError):
+        ttq.qformat_code("int3")
 
 
 def test_null_pointers():

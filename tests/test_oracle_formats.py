@@ -63,8 +63,12 @@ def test_e4m3_encode_round_trip():
                      dtype=np.uint8)
     np.testing.assert_array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)),
                                   codes)
-    # a zero, also a negative one, is stored as +0
-    assert oracle.e4m3_encode(np.array([-0.0]))[0] == 0
+    # the sign is kept, also for a zero: as torch's float8_e4m3fn cast does
+    t = np.array([-0.0, 0.0, -1e-5, 1e-5, -2.0 ** -11], dtype=np.float32)
+    ours = oracle.e4m3_encode(oracle.e4m3_round(t.astype(np.float64)))
+    ref = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(ours, [0x80, 0x00, 0x80, 0x00, 0x80])
 
 
 # ---------------------------------------------------------------- symmetric
@@ -207,10 +211,7 @@ def test_fp8_group_matches_torch_cast_of_scaled_values():
     # the group maximum lands on +-448 exactly
     assert np.all(np.abs(v).reshape(6, 2, 128).max(axis=2) == 448.0)
     f = oracle.quantize_format(W, dh, 8, 128, "fp8")
-    np.testing.assert_array_equal(f["codes"].view(np.uint8),
-                                  ref.view(torch.uint8).numpy().reshape(6, 256) & 0xff
-                                  & ~np.where(ref.float().numpy().reshape(6, 256) == 0,
-                                              0x80, 0).astype(np.uint8))
+    np.testing.assert_array_equal(f["codes"], ref.view(torch.uint8).numpy().reshape(6, 256))
     with pytest.raises(ValueError):
         oracle.quantize_format(W, dh, 4, 128, "fp8")
 
