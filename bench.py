@@ -73,8 +73,13 @@ def kernel_src_sha(kernel: str) -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def traffic_file(kernel: str, T: int) -> str:
-    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_q_proj4096_T{T}.json")
+def fmt_suffix(qformat: str) -> str:
+    return "" if qformat == "asym" else f"_{qformat}"
+
+
+def traffic_file(kernel: str, T: int, qformat: str = "asym") -> str:
+    return os.path.join(ROOT, "profiles",
+                        f"traffic_{kernel}_q_proj4096_T{T}{fmt_suffix(qformat)}.json")
 
 
 def dev_bf16(bits, torch):
@@ -270,7 +275,9 @@ def summarize(a):
     traffic = f_kib * 1024 * sf + w_kib * 1024 * sw
     d = d_out = 4096
     ab = alg_bytes(d, d_out, T)
+    fs = fmt_suffix(a.qformat)
     rec = {"kernel": kname, "workload": f"q_proj 4096x4096 T={T}",
+           "qformat": a.qformat,
            "kernel_src_sha": kernel_src_sha(kname),
            "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
            "copy_calib_bytes": calib_bytes,
@@ -280,8 +287,9 @@ def summarize(a):
            "traffic_over_alg": traffic / ab,
            "launches_counted": [len(k_f), len(k_w)]}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    json.dump(rec, open(traffic_file(kname, T), "w"), indent=1)
-    lines = [f"# {kname}: 4096x4096 q_proj, T={T} (4-bit g128, p=2)", "",
+    json.dump(rec, open(traffic_file(kname, T, a.qformat), "w"), indent=1)
+    lines = [f"# {kname}: 4096x4096 q_proj, T={T} ({format_bits(a.qformat)}-bit "
+             f"g128 {FORMAT_NAMES[a.qformat]}, p=2)", "",
              "Commands (from the repository root):", "", "```"]
     lines += [c for c in a.profile_cmd.split(";;") if c] + ["```", "",
               "## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
@@ -298,16 +306,16 @@ def summarize(a):
               f"factors {sf:.4f} (fetch) and {sw:.4f} (write)",
               f"- traffic = {traffic / 1e6:.3f} MB/launch against "
               f"{ab / 1e6:.3f} MB algorithmic (ratio {traffic / ab:.3f})", ""]
-    md = os.path.join(ROOT, "profiles", f"{kname}_q_proj4096_T{T}.md")
+    md = os.path.join(ROOT, "profiles", f"{kname}_q_proj4096_T{T}{fs}.md")
     open(md, "w").write("\n".join(lines))
     print(json.dumps(rec))
 
 
-def traffic_entry(kernel: str, T: int):
+def traffic_entry(kernel: str, T: int, qformat: str = "asym"):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source has changed since it was taken."""
     try:
-        rec = json.load(open(traffic_file(kernel, T)))
+        rec = json.load(open(traffic_file(kernel, T, qformat)))
     except Exception:
         return None
     if rec.get("kernel_src_sha") != kernel_src_sha(kernel):
@@ -384,7 +392,7 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved,
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["traffic"] = traffic_entry(kname, T)
+    roof["traffic"] = traffic_entry(kname, T, a.qformat)
     roof.update(kernel=kname, kernel_ms=k_ms, alg_bytes=ab, alg_flops=af)
 
     line = {
