@@ -84,6 +84,10 @@ __all__ = [
     "format_levels",
     "pre_rounding_format_fp64",
     "band_excused_levels",
+    "orthonormalize",
+    "subspace_iteration",
+    "lowrank_pca",
+    "pca_exact",
 ]
 
 
@@ -683,6 +687,67 @@ def band_excused_levels(lv_gpu, lv_ref, t64, rel: float = 1e-6):
     t = np.asarray(t64, dtype=np.float64)
     near = np.abs(t - mid) <= rel * np.maximum(np.abs(t), 1.0)
     return nb, int((bad & neighbours & near).sum())
+
+
+# --------------------------------------------------------------------------
+# low-rank factors by PCA: [NL] Sec. 2 (static factors initialised by PCA,
+# dynamic adaptation supported), [IT] Sec. 2 (B, A static or adapted online by
+# PCA), [ZH] Sec. 2.2 (B, A statically initialised, e.g. by PCA).  The pages
+# give no algorithm.  Readings (listed in the design doc):
+#   * the principal subspace is that of the output rows: B (d' x r) is an
+#     orthonormal basis of the top-r left singular subspace of M, and
+#     A = B^T W, so B A = B B^T W is the rank-r PCA projection of W;
+#   * M = W for the static initialisation; online, M = W D^{1/2} with D from
+#     the current activations (the activation-aware principal directions);
+#   * the residual W - B A is what the quantizer sees (reading 6);
+#   * the subspace is found by randomized subspace iteration (Halko,
+#     Martinsson and Tropp, "Finding structure with randomness", 2011: range
+#     finder with q power iterations), the Gaussian test matrix Omega (d x r)
+#     given by the caller; every orthonormalisation is a QR factorisation with
+#     a positive diagonal of R (so Q is unique for full-rank input).
+# --------------------------------------------------------------------------
+def orthonormalize(Y: np.ndarray) -> np.ndarray:
+    """Q of the QR factorisation Y = Q R with diag(R) > 0, float64."""
+    Q, R = np.linalg.qr(np.asarray(Y, dtype=np.float64))
+    sgn = np.sign(np.diag(R))
+    sgn[sgn == 0] = 1.0
+    return Q * sgn[None, :]
+
+
+def subspace_iteration(M: np.ndarray, Omega: np.ndarray, iters: int) -> np.ndarray:
+    """Orthonormal basis (d' x r) of the range of M after ``iters`` power
+    iterations from Y = M Omega: Q = orth(M Omega); then ``iters`` times
+    Z = orth(M^T Q), Q = orth(M Z)."""
+    M = np.asarray(M, dtype=np.float64)
+    Q = orthonormalize(M @ np.asarray(Omega, dtype=np.float64))
+    for _ in range(iters):
+        Z = orthonormalize(M.T @ Q)
+        Q = orthonormalize(M @ Z)
+    return Q
+
+
+def lowrank_pca(W_bits: np.ndarray, Omega: np.ndarray, iters: int, *,
+                X_bits: Optional[np.ndarray] = None, p: float = 2.0,
+                lam: float = 0.0, alpha: float = 0.0) -> dict:
+    """Low-rank factors of W by PCA.  Returns ``B`` (d' x r), ``A`` (r x d),
+    ``R`` = W - B A (all float64) and ``M`` (the matrix whose principal
+    subspace was taken).  With ``X_bits`` ([T, d] bf16) the online variant:
+    M = W D^{1/2}, D from X with (p, lam, alpha) as in ``ttq_linear``."""
+    W = bf16_to_f64(W_bits)
+    M = W
+    if X_bits is not None:
+        n = channel_norms(bf16_to_f64(X_bits), p)
+        dh, _ = diag_scales(n, lam, alpha)
+        M = W * dh[None, :]
+    B = subspace_iteration(M, Omega, iters)
+    A = B.T @ W
+    return dict(B=B, A=A, R=W - B @ A, M=M)
+
+
+def pca_exact(M: np.ndarray, r: int) -> np.ndarray:
+    """Exact top-r left singular vectors of M (numpy SVD), float64."""
+    U, _, _ = np.linalg.svd(np.asarray(M, dtype=np.float64), full_matrices=False)
+    return U[:, :r]
 
 
 def overhead_ratio(d_out: int, T: int) -> float:
