@@ -279,6 +279,37 @@ int ttq_kernel_count(void);
 const char* ttq_kernel_name(int kernel);
 int ttq_timing_query(int kernel, double* total_ms, int64_t* launches);
 
+/* ---- low-rank factors by PCA
+ * The static low-rank factors of the projection are initialised by PCA, and
+ * may be adapted online ("TTQ: Activation-Aware Test-Time Quantization ...",
+ * nl summary, Sec. 2; it summary, Sec. 2; zh summary, Sec. 2.2); the pages
+ * give no algorithm.  This call computes
+ *   B  [d_out][rank] bf16: an orthonormal basis of the top-rank left
+ *      principal subspace of M = W (T = 0), or of M = W D^{1/2} with D from
+ *      the activations X (T > 0; p, lambda, alpha as in ttq_linear);
+ *   A  [rank][d] bf16 = B^T W;
+ *   Wres optional [d_out][d] bf16 = bf16(W - B A), computed from the bf16
+ *      B and A, so that ttq_linear(Wres, X, B, A) projects with
+ *      W ~ Q_D[Wres] + B A;
+ * by randomized subspace iteration (Halko, Martinsson and Tropp, 2011):
+ * Q = orth(M Omega), then `iters` times Z = orth(M^T Q), Q = orth(M Z), with
+ * orth = CholeskyQR2 (float32 panels, float64 Cholesky), B = Q.
+ *   prm     d, d_out >= 1; rank in {8, 16, 32, 64, 128}, <= min(d, d_out);
+ *           T >= 0 (T > 0 needs d % 8 == 0); bits, group, flags and qformat
+ *           are not read
+ *   iters   power iterations, 0..16
+ *   W       [d_out][d] bf16; X [T][d] bf16 (T > 0; NULL otherwise)
+ *   Omega   [d][rank] float32, the caller's Gaussian test matrix
+ *   workspace at least ttq_lowrank_pca_workspace_bytes, 256-byte aligned
+ * All pointers 16-byte aligned device memory.  Same error rules as
+ * ttq_linear; the result is deterministic for given inputs. */
+int ttq_lowrank_pca_workspace_bytes(const ttq_params* prm, int32_t iters,
+                                    size_t* bytes);
+int ttq_lowrank_pca(const ttq_params* prm, int32_t iters, const void* W,
+                    const void* X, const float* Omega, void* B_out,
+                    void* A_out, void* Wres_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

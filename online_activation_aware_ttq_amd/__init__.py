@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     ttq_linear,
     ttq_linear_batched,
     ttq_linear_segmented,
+    ttq_lowrank_pca,
+    ttq_lowrank_pca_workspace_bytes,
     ttq_segmented_workspace_bytes,
     ttq_params,
     ttq_packed_row_bytes,

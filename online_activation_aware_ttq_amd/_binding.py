@@ -48,6 +48,10 @@ EXPORTS = {
                                 _c.c_size_t, _vp]),
     "ttq_qmatmul": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _c.c_size_t, _vp]),
+    "ttq_lowrank_pca_workspace_bytes": (_c.c_int, [_vp, _c.c_int32,
+                                                   _c.POINTER(_c.c_size_t)]),
+    "ttq_lowrank_pca": (_c.c_int, [_vp, _c.c_int32, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _c.c_size_t, _vp]),
     "ttq_status_string": (_c.c_char_p, [_c.c_int]),
     "ttq_last_hip_error": (_c.c_int, []),
     "ttq_version": (_c.c_char_p, []),
@@ -433,6 +437,53 @@ def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
     if st != TTQ_OK:
         raise TTQError(st, "ttq_qmatmul")
     return Y
+
+
+# ------------------------------------------------- low-rank factors by PCA
+def ttq_lowrank_pca_workspace_bytes(prm: ttq_params, iters: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().ttq_lowrank_pca_workspace_bytes(
+        ctypes.byref(prm), int(iters), ctypes.byref(out))
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_lowrank_pca_workspace_bytes")
+    return int(out.value)
+
+
+def ttq_lowrank_pca(W, Omega, *, iters: int, X=None, p: float = 2.0,
+                    lam: float = 0.0, alpha: float = 0.0, want_residual=True,
+                    workspace=None, stream=None):
+    """Low-rank factors by PCA (see include/ttq.h): returns (B [d_out, r],
+    A [r, d], Wres [d_out, d] or None), bf16 GPU tensors.  ``Omega`` is the
+    float32 [d, r] Gaussian test matrix; with ``X`` ([T, d] bf16) the
+    principal subspace is that of W D^{1/2}."""
+    import torch
+    d_out, d = W.shape
+    r = Omega.shape[1]
+    T = 0 if X is None else X.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("W must be a GPU tensor")
+    _check(W, "W", torch.bfloat16, (d_out, d), dev)
+    _check(Omega, "Omega", torch.float32, (d, r), dev)
+    if X is not None:
+        _check(X, "X", torch.bfloat16, (T, d), dev)
+    prm = make_params(d=d, d_out=d_out, T=T, rank=r, bits=4, group=32, p=p,
+                      lam=lam, alpha=alpha)
+    need = ttq_lowrank_pca_workspace_bytes(prm, iters)
+    B = torch.empty((d_out, r), dtype=torch.bfloat16, device=dev)
+    A = torch.empty((r, d), dtype=torch.bfloat16, device=dev)
+    Wres = torch.empty((d_out, d), dtype=torch.bfloat16, device=dev) \
+        if want_residual else None
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load_library().ttq_lowrank_pca(
+        ctypes.byref(prm), int(iters), _ptr(W), _ptr(X), _ptr(Omega), _ptr(B),
+        _ptr(A), _ptr(Wres), _ptr(workspace), workspace.numel(), stream)
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_lowrank_pca")
+    return B, A, Wres
 
 
 # ------------------------------------------------------------------ timing

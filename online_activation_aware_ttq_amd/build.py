@@ -35,6 +35,7 @@ SOURCES = [
     "k_qfused.hip",
     "k_gemm_q.hip",
     "k_segment.hip",
+    "k_pca.hip",
     "ttq_api.cpp",
 ]
 

@@ -1,0 +1,306 @@
+// Low-rank factors by PCA ("TTQ: Activation-Aware Test-Time Quantization
+// ...": nl summary, Sec. 2, static factors initialised by PCA with dynamic
+// adaptation supported; it summary, Sec. 2, B and A static or adapted online
+// by PCA; zh summary, Sec. 2.2).  B (d' x r) is an orthonormal basis of the
+// top-r left principal subspace of M = W (or M = W D^{1/2}, D from the
+// current activations), A = B^T W, and the residual W - B A is what the
+// quantizer sees.  The subspace comes from randomized subspace iteration
+// (Halko, Martinsson and Tropp, 2011): Q = orth(M Omega), then per power
+// iteration Z = orth(M^T Q), Q = orth(M Z); orth is CholeskyQR2 (Gram
+// matrix, Cholesky in float64, Q = Y R^{-1} by substitution, twice).
+//
+// Kernels (all float32 accumulation on the VALU: the products are skinny,
+// r <= 128 columns, and the factors must be accurate to float32 before the
+// final bf16 rounding):
+//   k_skinny        one 64-row tile of C = A_s Bm over a K slice (split-K
+//                   partials); A is W (bf16) or a float32 panel, read either
+//                   row-wise (C = A Bm) or column-wise (C = A^T Bm); its
+//                   columns may be scaled by D^{1/2} as they are staged
+//   k_psum          ordered sum of the partials -> float32, and optionally
+//                   bf16 (as is, or transposed)
+//   k_chol          one workgroup: G = R^T R (Cholesky in float64)
+//   k_trsm          Q = Y R^{-1}, one row per lane (forward substitution)
+//   k_lr_residual   W_res = bf16(W - B A) from the bf16 factors
+#include "ttq_internal.h"
+
+namespace ttq {
+
+namespace {
+
+constexpr int SK_T = 64;  // rows of a C tile, and channels of a K tile
+
+template <int NC, bool TN, typename TA>
+__global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
+  constexpr int N = 4 * NC;  // columns of C
+  __shared__ float tA[SK_T][SK_T + 1];  // [k][row]
+  __shared__ __attribute__((aligned(16))) float tB[SK_T][N];
+  const int t = threadIdx.x;
+  const int r = t & 63, cg = t >> 6;  // row of the tile, column group (per wave)
+  const int64_t r0 = (int64_t)blockIdx.x * SK_T;
+  const int64_t k0 = (int64_t)blockIdx.y * a.kc;
+  const int64_t k1 = min(a.K, k0 + a.kc);
+  const TA* A = static_cast<const TA*>(a.A);
+  float acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+  for (int64_t kt = k0; kt < k1; kt += SK_T) {
+    // stage the A tile as [k][row]; element (row, k) is A[row][k] (C = A Bm)
+    // or A[k][row] (C = A^T Bm); the index along the memory row is the one
+    // the column scale applies to
+    for (int e = t; e < SK_T * SK_T; e += 256) {
+      int kk, rr;
+      if (TN) { rr = e & 63; kk = e >> 6; }
+      else { kk = e & 63; rr = e >> 6; }
+      const int64_t row = r0 + rr, k = kt + kk;
+      float v = 0.f;
+      if (row < a.rows && k < k1) {
+        const int64_t col = TN ? row : k;
+        const int64_t off = TN ? k * a.lda + row : row * a.lda + k;
+        if constexpr (sizeof(TA) == 2)
+          v = __uint_as_float((unsigned)reinterpret_cast<const uint16_t*>(A)[off] << 16);
+        else
+          v = A[off];
+        if (a.scale) v = v * a.scale[col];
+      }
+      tA[kk][rr] = v;
+    }
+    for (int e = t; e < SK_T * N; e += 256) {
+      const int kk = e / N, c = e % N;
+      const int64_t k = kt + kk;
+      tB[kk][c] = k < k1 ? a.Bm[k * a.ldb + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < SK_T; ++kk) {
+      const float av = tA[kk][r];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = fmaf(av, tB[kk][cg * NC + c], acc[c]);
+    }
+    __syncthreads();
+  }
+  const int64_t row = r0 + r;
+  if (row < a.rows) {
+    float* out = a.part + ((int64_t)blockIdx.y * a.rows + row) * N + cg * NC;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) out[c] = acc[c];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_psum(PsumArgs a) {
+  const int64_t total = a.rows * a.n;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    float v = 0.f;
+    for (int z = 0; z < a.nsplit; ++z) v += a.part[(int64_t)z * total + e];
+    if (a.out) a.out[e] = v;
+    const int64_t i = e / a.n, c = e % a.n;
+    if (a.out_bf16) a.out_bf16[e] = (bf16_t)f2bf(v);
+    if (a.out_bf16_t) a.out_bf16_t[c * a.rows + i] = (bf16_t)f2bf(v);
+  }
+}
+
+// G (n x n, float32, symmetric up to rounding) -> R with G = R^T R, R upper
+// triangular with a positive diagonal, Cholesky in float64 (right-looking,
+// one barrier per step: row k is kept unscaled while the trailing matrix is
+// updated with L[k][i] L[k][j] / pivot, and every row is scaled by 1/sqrt of
+// its pivot at the end).  A pivot below 1e-14 of the largest diagonal entry
+// is raised to that floor (a rank-deficient panel: the second CholeskyQR
+// pass then re-normalises).  LDS rows have an odd stride n + 1.
+__global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
+  extern __shared__ double L[];  // n rows of n + 1, then the n pivots
+  const int ld = n + 1;
+  double* piv = L + n * ld;
+  __shared__ double dmax;
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  for (int e = t; e < n * n; e += 256) {
+    const int i = e / n, j = e % n;
+    L[i * ld + j] = 0.5 * ((double)G[i * n + j] + (double)G[j * n + i]);
+  }
+  __syncthreads();
+  if (t == 0) {
+    double m = 0.0;
+    for (int i = 0; i < n; ++i) m = fmax(m, L[i * ld + i]);
+    dmax = m > 0.0 ? m : 1.0;
+  }
+  __syncthreads();
+  const double floor = 1e-14 * dmax;
+  for (int k = 0; k < n; ++k) {
+    const double pk = fmax(L[k * ld + k], floor);
+    if (t == 0) piv[k] = pk;
+    const double inv = 1.0 / pk;
+    for (int i = k + 1 + ty; i < n; i += 16) {
+      const double lki = L[k * ld + i] * inv;
+      for (int j = k + 1 + tx; j < n; j += 16)
+        if (j >= i) L[i * ld + j] -= lki * L[k * ld + j];
+    }
+    __syncthreads();
+  }
+  for (int e = t; e < n * n; e += 256) {
+    const int i = e / n, j = e % n;
+    R[e] = i < j ? (float)(L[i * ld + j] / sqrt(piv[i]))
+                 : (i == j ? (float)sqrt(piv[i]) : 0.f);
+  }
+}
+
+// Q = Y R^{-1} in place, one row of Y per thread by forward substitution:
+//   q_c = (y_c - sum_{m<c} q_m R[m][c]) / R[c][c]
+// R is staged transposed (row c holds column c of R, its diagonal entry
+// replaced by the reciprocal), so the terms of one q_c are contiguous and
+// every lane reads the same addresses (broadcast).
+template <int N>
+__global__ __launch_bounds__(64) void k_trsm(float* Y, const float* R, int64_t m) {
+  __shared__ __attribute__((aligned(16))) float sRt[N][N];
+  const int t = threadIdx.x;
+  for (int e = t; e < N * N; e += 64) {
+    const int c = e / N, k = e % N;  // sRt[c][k] = R[k][c]
+    sRt[c][k] = c == k ? 1.0f / R[k * N + c] : (k < c ? R[k * N + c] : 0.f);
+  }
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 64 + t;
+  if (i >= m) return;
+  float q[N];
+  float* row = Y + i * N;
+#pragma unroll
+  for (int c = 0; c < N; c += 4) {
+    const f32x4 v = *(const f32x4*)(row + c);
+    q[c] = v.x; q[c + 1] = v.y; q[c + 2] = v.z; q[c + 3] = v.w;
+  }
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    float v = q[c];
+#pragma unroll
+    for (int k = 0; k < c; ++k) v = fmaf(-q[k], sRt[c][k], v);
+    q[c] = v * sRt[c][c];
+  }
+#pragma unroll
+  for (int c = 0; c < N; c += 4) *(f32x4*)(row + c) = f32x4{q[c], q[c + 1], q[c + 2], q[c + 3]};
+}
+
+// W_res[i][j] = bf16(W[i][j] - sum_c B[i][c] A[c][j]), a tile of 64 rows
+// (32 for r = 128) x 64 columns per workgroup, float32 sums in c order
+template <int N>
+constexpr int lr_rows() { return N >= 128 ? 32 : 64; }  // 64 KiB of static LDS
+
+template <int N>
+__global__ __launch_bounds__(256) void k_lr_residual(LrResidualArgs a) {
+  constexpr int RT = lr_rows<N>();
+  __shared__ float sB[RT][N + 1];    // [row][c]
+  __shared__ float sA[N][SK_T + 1];  // [c][col]
+  const int t = threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.y * RT, j0 = (int64_t)blockIdx.x * SK_T;
+  for (int e = t; e < RT * N; e += 256) {
+    const int rr = e / N, c = e % N;
+    const int64_t i = i0 + rr;
+    sB[rr][c] = i < a.d_out ? bf16lo(a.B[i * N + c]) : 0.f;
+  }
+  for (int e = t; e < N * SK_T; e += 256) {
+    const int c = e / SK_T, jj = e % SK_T;
+    const int64_t j = j0 + jj;
+    sA[c][jj] = j < a.d ? bf16lo(a.A[(int64_t)c * a.d + j]) : 0.f;
+  }
+  __syncthreads();
+  const int jj = t & 63, rq = t >> 6;  // column, quarter of the rows
+  const int64_t j = j0 + jj;
+  if (j >= a.d) return;
+  for (int rr = rq * (RT / 4); rr < (rq + 1) * (RT / 4); ++rr) {
+    const int64_t i = i0 + rr;
+    if (i >= a.d_out) break;
+    float s = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < N; ++c) s = fmaf(sB[rr][c], sA[c][jj], s);
+    const float w = bf16lo(a.W[i * a.d + j]);
+    a.Wres[i * a.d + j] = (bf16_t)f2bf(w - s);
+  }
+}
+
+template <bool TN, typename TA>
+hipError_t launch_skinny_t(const SkinnyArgs& a, dim3 grid, const Launch& L) {
+  switch (a.n) {
+    case 8: return ext_launch(k_skinny<2, TN, TA>, grid, dim3(256), 0, L, a);
+    case 16: return ext_launch(k_skinny<4, TN, TA>, grid, dim3(256), 0, L, a);
+    case 32: return ext_launch(k_skinny<8, TN, TA>, grid, dim3(256), 0, L, a);
+    case 64: return ext_launch(k_skinny<16, TN, TA>, grid, dim3(256), 0, L, a);
+    case 128: return ext_launch(k_skinny<32, TN, TA>, grid, dim3(256), 0, L, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int skinny_splits(int64_t rows, int64_t K) {
+  const int64_t tiles = (rows + SK_T - 1) / SK_T;
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t smax = (K + 255) / 256;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  // whole K tiles per split
+  const int64_t kc = ((K + s - 1) / s + SK_T - 1) / SK_T * SK_T;
+  return (int)((K + kc - 1) / kc);
+}
+
+int64_t skinny_kc(int64_t K, int splits) {
+  return ((K + splits - 1) / splits + SK_T - 1) / SK_T * SK_T;
+}
+
+hipError_t launch_skinny(const SkinnyArgs& a, bool tn, bool a_bf16, const Launch& L) {
+  if (a.rows <= 0 || a.K <= 0) return hipSuccess;
+  if (a.kc <= 0 || a.kc % SK_T != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.rows + SK_T - 1) / SK_T), (unsigned)((a.K + a.kc - 1) / a.kc));
+  if (tn) return a_bf16 ? launch_skinny_t<true, bf16_t>(a, grid, L)
+                        : launch_skinny_t<true, float>(a, grid, L);
+  return a_bf16 ? launch_skinny_t<false, bf16_t>(a, grid, L)
+                : launch_skinny_t<false, float>(a, grid, L);
+}
+
+hipError_t launch_psum(const PsumArgs& a, const Launch& L) {
+  const int64_t total = a.rows * a.n;
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  return ext_launch(k_psum, dim3((unsigned)blocks), dim3(256), 0, L, a);
+}
+
+hipError_t launch_chol(const float* G, float* R, int n, const Launch& L) {
+  if (n <= 0 || n > 128) return hipErrorInvalidValue;
+  const uint32_t lds = (uint32_t)((n * (n + 1) + n) * sizeof(double));
+  static hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_chol),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)((128 * 129 + 128) * sizeof(double)));
+  if (attr != hipSuccess) return attr;
+  return ext_launch(k_chol, dim3(1), dim3(256), lds, L, G, R, n);
+}
+
+hipError_t launch_trsm(float* Y, const float* R, int64_t m, int n, const Launch& L) {
+  if (m <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((m + 63) / 64));
+  switch (n) {
+    case 8: return ext_launch(k_trsm<8>, grid, dim3(64), 0, L, Y, R, m);
+    case 16: return ext_launch(k_trsm<16>, grid, dim3(64), 0, L, Y, R, m);
+    case 32: return ext_launch(k_trsm<32>, grid, dim3(64), 0, L, Y, R, m);
+    case 64: return ext_launch(k_trsm<64>, grid, dim3(64), 0, L, Y, R, m);
+    case 128: return ext_launch(k_trsm<128>, grid, dim3(64), 0, L, Y, R, m);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_lr_residual(const LrResidualArgs& a, int n, const Launch& L) {
+  if (a.d_out <= 0 || a.d <= 0) return hipSuccess;
+  const unsigned gx = (unsigned)((a.d + SK_T - 1) / SK_T);
+#define TTQ_LR_CASE(NV)                                                        \
+  case NV:                                                                     \
+    return ext_launch(k_lr_residual<NV>,                                       \
+                      dim3(gx, (unsigned)((a.d_out + lr_rows<NV>() - 1) /      \
+                                          lr_rows<NV>())),                     \
+                      dim3(256), 0, L, a);
+  switch (n) {
+    TTQ_LR_CASE(8)
+    TTQ_LR_CASE(16)
+    TTQ_LR_CASE(32)
+    TTQ_LR_CASE(64)
+    TTQ_LR_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef TTQ_LR_CASE
+}
+
+}  // namespace ttq

@@ -187,7 +187,8 @@ TimingState g_timing;
 const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
-    "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant", "seg_copy"};
+    "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant", "seg_copy",
+    "pca_skinny", "pca_psum", "pca_chol", "pca_trsm", "pca_residual"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -856,6 +857,187 @@ int segmented_impl(const ttq_params* prm, int64_t n_seg, const int64_t* off,
   return TTQ_OK;
 }
 
+// ------------------------------------------------- low-rank factors by PCA
+// (k_pca.hip).  Reads d, d_out, rank (the r of B and A), T (0: the principal
+// subspace of W; > 0: of W D^{1/2}, D from X with p, lambda, alpha); bits,
+// group, flags and qformat are not read.
+int validate_pca(const ttq_params* prm, int32_t iters) {
+  if (!prm) return TTQ_ENULL;
+  if (prm->d < 1 || prm->d > kMaxD) return TTQ_EINVAL;
+  if (prm->d_out < 1 || prm->d_out > kMaxDout) return TTQ_EINVAL;
+  if (prm->T < 0 || prm->T > kMaxT) return TTQ_EINVAL;
+  if (prm->d * prm->d_out > kMaxElems || prm->T * prm->d > kMaxElems) return TTQ_EINVAL;
+  if (iters < 0 || iters > 16) return TTQ_EINVAL;
+  const int64_t r = prm->rank;
+  if (r < 1 || r > prm->d || r > prm->d_out) return TTQ_EINVAL;
+  if (r != 8 && r != 16 && r != 32 && r != 64 && r != 128) return TTQ_EUNSUPPORTED;
+  if (prm->T > 0) {
+    if (prm->d % 8 != 0) return TTQ_EUNSUPPORTED;  // 16-byte token loads
+    if (!(std::isfinite(prm->p) && prm->p > 0.0)) return TTQ_EINVAL;
+    if (!finite_nonneg(prm->lambda) || !finite_nonneg(prm->alpha)) return TTQ_EINVAL;
+  }
+  return TTQ_OK;
+}
+
+struct PcaPlan {
+  int sp_nt = 1, sp_tn = 1, sp_gy = 1, sp_gz = 1;  // splits of the products
+  size_t off_dh = 0, off_dhi = 0, off_statp = 0, off_y = 0, off_z = 0,
+         off_part = 0, off_g = 0, off_r = 0;
+  Plan stats;  // token slices of the norm partials (T > kFusedMaxT)
+  size_t total = 0;
+};
+
+PcaPlan make_pca_plan(const ttq_params* prm) {
+  PcaPlan P;
+  const int64_t d = prm->d, dout = prm->d_out, n = prm->rank, T = prm->T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  if (T > 0) {
+    P.off_dh = take(sizeof(float) * d);
+    P.off_dhi = take(sizeof(float) * d);
+    if (T > kFusedMaxT) {
+      plan_stats_split(P.stats, 1, T, d, take);
+      P.off_statp = P.stats.off_statp;
+    }
+  }
+  P.off_y = take(sizeof(float) * dout * n);
+  P.off_z = take(sizeof(float) * d * n);
+  P.sp_nt = skinny_splits(dout, d);   // Y = M Z        (rows d', K d)
+  P.sp_tn = skinny_splits(d, dout);   // Z = M^T Q      (rows d, K d')
+  P.sp_gy = skinny_splits(n, dout);   // Gram of Y
+  P.sp_gz = skinny_splits(n, d);      // Gram of Z
+  size_t part = 0;
+  auto need = [&](int sp, int64_t rows) {
+    const size_t b = sizeof(float) * sp * rows * n;
+    if (b > part) part = b;
+  };
+  need(P.sp_nt, dout);
+  need(P.sp_tn, d);
+  need(P.sp_gy, n);
+  need(P.sp_gz, n);
+  P.off_part = take(part);
+  P.off_g = take(sizeof(float) * n * n);
+  P.off_r = take(sizeof(float) * n * n);
+  P.total = off;
+  return P;
+}
+
+int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
+             const void* X, const float* Omega, void* B_out, void* A_out,
+             void* Wres_out, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  int st = validate_pca(prm, iters);
+  if (st != TTQ_OK) return st;
+  const int64_t d = prm->d, dout = prm->d_out, n = prm->rank, T = prm->T;
+  if (!W || !Omega || !B_out || !A_out) return TTQ_ENULL;
+  if (T > 0 && !X) return TTQ_ENULL;
+  if (misaligned(W, 16) || misaligned(X, 16) || misaligned(Omega, 16) ||
+      misaligned(B_out, 16) || misaligned(A_out, 16) ||
+      misaligned(Wres_out, 16) || misaligned(workspace, 256))
+    return TTQ_EALIGN;
+  const PcaPlan P = make_pca_plan(prm);
+  if (!workspace) return TTQ_ENULL;
+  if (workspace_bytes < P.total) return TTQ_EWORKSPACE;
+  if (inject_hip_error()) return TTQ_EHIP;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bf16_t* Wb = static_cast<const bf16_t*>(W);
+  float* Y = reinterpret_cast<float*>(ws + P.off_y);
+  float* Z = reinterpret_cast<float*>(ws + P.off_z);
+  float* part = reinterpret_cast<float*>(ws + P.off_part);
+  float* G = reinterpret_cast<float*>(ws + P.off_g);
+  float* Rf = reinterpret_cast<float*>(ws + P.off_r);
+  const float* dh = nullptr;
+
+  if (T > 0) {  // D of the current activations, as in ttq_linear
+    const bf16_t* Xb = static_cast<const bf16_t*>(X);
+    float* dhw = reinterpret_cast<float*>(ws + P.off_dh);
+    float* dhiw = reinterpret_cast<float*>(ws + P.off_dhi);
+    const int pmode = prm->p == 2.0 ? 2 : (prm->p == 1.0 ? 1 : 0);
+    if (T <= kFusedMaxT) {
+      StatsSmallArgs sa{};
+      sa.X = Xb; sa.T = T; sa.d = d; sa.pmode = pmode;
+      sa.p = prm->p; sa.lam = prm->lambda; sa.alpha = prm->alpha;
+      sa.dh = dhw; sa.dhi = dhiw; sa.group = 32;
+      st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
+    } else {
+      StatsSplitArgs ta{};
+      ta.X = Xb; ta.T = T; ta.d = d; ta.pmode = pmode;
+      ta.p = prm->p; ta.lam = prm->lambda; ta.alpha = prm->alpha;
+      ta.tchunk = P.stats.tchunk; ta.nsplit = P.stats.nsplit;
+      ta.partial = reinterpret_cast<double*>(ws + P.off_statp);
+      ta.dh = dhw; ta.dhi = dhiw;
+      st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_partial(ta, 1, L); });
+      if (st == TTQ_OK)
+        st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(ta, 1, L); });
+    }
+    if (st != TTQ_OK) return st;
+    dh = dhw;
+  }
+
+  // C[rows][n] = (A_s or A_s^T) Bm through the split partials
+  auto product = [&](bool tn, bool a_bf16, const void* A, int64_t lda,
+                     const float* scale, int64_t rows, int64_t K,
+                     const float* Bm, int splits, float* out, bf16_t* out_b,
+                     bf16_t* out_bt) -> int {
+    SkinnyArgs ka{};
+    ka.A = A; ka.lda = lda; ka.scale = scale; ka.Bm = Bm; ka.ldb = n;
+    ka.rows = rows; ka.K = K; ka.n = (int)n; ka.kc = skinny_kc(K, splits);
+    ka.part = part;
+    int r = run(K_SKINNY, s, [&](const Launch& L) { return launch_skinny(ka, tn, a_bf16, L); });
+    if (r != TTQ_OK) return r;
+    PsumArgs pa{};
+    pa.part = part; pa.nsplit = (int)((K + ka.kc - 1) / ka.kc);
+    pa.rows = rows; pa.n = n; pa.out = out; pa.out_bf16 = out_b; pa.out_bf16_t = out_bt;
+    return run(K_PSUM, s, [&](const Launch& L) { return launch_psum(pa, L); });
+  };
+  // CholeskyQR2 of the float32 panel V [m][n], in place
+  auto orth = [&](float* V, int64_t m, int sp_gram) -> int {
+    for (int pass = 0; pass < 2; ++pass) {
+      int r = product(true, false, V, n, nullptr, n, m, V, sp_gram, G, nullptr, nullptr);
+      if (r != TTQ_OK) return r;
+      r = run(K_CHOL, s, [&](const Launch& L) { return launch_chol(G, Rf, (int)n, L); });
+      if (r != TTQ_OK) return r;
+      r = run(K_TRSM, s, [&](const Launch& L) { return launch_trsm(V, Rf, m, (int)n, L); });
+      if (r != TTQ_OK) return r;
+    }
+    return TTQ_OK;
+  };
+
+  // Q = orth(M Omega)
+  st = product(false, true, Wb, d, dh, dout, d, Omega, P.sp_nt, Y, nullptr, nullptr);
+  if (st == TTQ_OK) st = orth(Y, dout, P.sp_gy);
+  for (int it = 0; it < iters && st == TTQ_OK; ++it) {
+    // Z = orth(M^T Q) = orth(D^{1/2} W^T Q);  Q = orth(M Z)
+    st = product(true, true, Wb, d, dh, d, dout, Y, P.sp_tn, Z, nullptr, nullptr);
+    if (st == TTQ_OK) st = orth(Z, d, P.sp_gz);
+    if (st == TTQ_OK)
+      st = product(false, true, Wb, d, dh, dout, d, Z, P.sp_nt, Y, nullptr, nullptr);
+    if (st == TTQ_OK) st = orth(Y, dout, P.sp_gy);
+  }
+  if (st != TTQ_OK) return st;
+  // B = bf16(Q); A = bf16(Q^T W), written transposed from W^T Q
+  bf16_t* Bb = static_cast<bf16_t*>(B_out);
+  bf16_t* Ab = static_cast<bf16_t*>(A_out);
+  {
+    PsumArgs pa{};
+    pa.part = Y; pa.nsplit = 1; pa.rows = dout; pa.n = n; pa.out_bf16 = Bb;
+    st = run(K_PSUM, s, [&](const Launch& L) { return launch_psum(pa, L); });
+    if (st != TTQ_OK) return st;
+  }
+  st = product(true, true, Wb, d, nullptr, d, dout, Y, P.sp_tn, Z, nullptr, Ab);
+  if (st != TTQ_OK || !Wres_out) return st;
+  LrResidualArgs ra{};
+  ra.W = Wb; ra.B = Bb; ra.A = Ab; ra.Wres = static_cast<bf16_t*>(Wres_out);
+  ra.d = d; ra.d_out = dout;
+  return run(K_LR_RESIDUAL, s, [&](const Launch& L) { return launch_lr_residual(ra, (int)n, L); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -949,6 +1131,23 @@ int ttq_qmatmul(const ttq_params* prm, const uint8_t* codes,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return qmatmul_impl(prm, codes, scales, mins, dhalf_inv, X, B, A, Y,
                       workspace, workspace_bytes, stream);
+}
+
+int ttq_lowrank_pca_workspace_bytes(const ttq_params* prm, int32_t iters,
+                                    size_t* bytes) {
+  if (!bytes) return TTQ_ENULL;
+  const int st = validate_pca(prm, iters);
+  if (st != TTQ_OK) return st;
+  *bytes = make_pca_plan(prm).total;
+  return TTQ_OK;
+}
+
+int ttq_lowrank_pca(const ttq_params* prm, int32_t iters, const void* W,
+                    const void* X, const float* Omega, void* B_out,
+                    void* A_out, void* Wres_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return pca_impl(prm, iters, W, X, Omega, B_out, A_out, Wres_out, workspace,
+                  workspace_bytes, stream);
 }
 
 const char* ttq_status_string(int status) {

@@ -32,6 +32,11 @@ enum KernelKind {
   K_LOWRANK_ZSUM,      // ordered sum of the small-M low-rank partials
   K_GEMM_Q,            // projection GEMM quantizing the weight tiles itself
   K_SEG_COPY,          // row copies for requests of different lengths
+  K_SKINNY,            // PCA: skinny products with W and the panels
+  K_PSUM,              // PCA: ordered sum of the split partials
+  K_CHOL,              // PCA: Cholesky factor of a Gram matrix
+  K_TRSM,              // PCA: panel times the inverse Cholesky factor
+  K_LR_RESIDUAL,       // PCA: W - B A in bf16
   K_NUM_KINDS
 };
 
@@ -507,6 +512,47 @@ struct SegCopyArgs {
   int64_t len[kSegMax];     // rows of request r
 };
 hipError_t launch_seg_copy(const SegCopyArgs& a, const Launch& L);
+
+// ---- low-rank factors by PCA (k_pca.hip)
+// one skinny product C[rows][n] = A_s Bm (A read row-wise: A[row][k]) or
+// A_s^T Bm (A read column-wise: A[k][row]), over K, as split-K partials
+// part[split][rows][n]; A is bf16 or float32, its columns (the index along a
+// memory row) optionally scaled by `scale`
+struct SkinnyArgs {
+  const void* A; int64_t lda;
+  const float* scale;     // optional, per column of A in memory
+  const float* Bm; int64_t ldb;   // [K][ldb] float32
+  int64_t rows, K;
+  int n;                  // 8, 16, 32, 64 or 128
+  int64_t kc;             // channels per split, a multiple of 64
+  float* part;            // [ceil(K / kc)][rows][n]
+};
+hipError_t launch_skinny(const SkinnyArgs& a, bool tn, bool a_bf16, const Launch& L);
+int skinny_splits(int64_t rows, int64_t K);
+int64_t skinny_kc(int64_t K, int splits);
+// out = sum of the nsplit partials in order (float32 [rows][n]), optionally
+// also as bf16 [rows][n] and / or bf16 transposed [n][rows]
+struct PsumArgs {
+  const float* part;
+  int nsplit;
+  int64_t rows, n;
+  float* out;
+  bf16_t* out_bf16;
+  bf16_t* out_bf16_t;
+};
+hipError_t launch_psum(const PsumArgs& a, const Launch& L);
+// Cholesky factor R (upper, G = R^T R) of an n x n Gram matrix (n <= 128),
+// and Y[m][n] <- Y R^{-1} in place
+hipError_t launch_chol(const float* G, float* R, int n, const Launch& L);
+hipError_t launch_trsm(float* Y, const float* R, int64_t m, int n, const Launch& L);
+struct LrResidualArgs {
+  const bf16_t* W;        // [d_out][d]
+  const bf16_t* B;        // [d_out][n]
+  const bf16_t* A;        // [n][d]
+  bf16_t* Wres;           // [d_out][d]
+  int64_t d, d_out;
+};
+hipError_t launch_lr_residual(const LrResidualArgs& a, int n, const Launch& L);
 
 // out[i] = bf16(sum_{z<nsplit} part[z*n + i]) in split order, n % 4 == 0
 struct SplitReduceArgs {

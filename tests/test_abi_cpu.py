@@ -395,3 +395,56 @@ def test_segmented_workspace_plan():
     st, need = seg_ws(prm(T=22), [0, 1, 6, 22])
     assert call_segmented(prm(T=22), [0, 1, 6, 22], ws_bytes=need - 1) == ttq.TTQ_EWORKSPACE
     assert call_segmented(prm(T=22), [0, 1, 6, 22], Y=None) == ttq.TTQ_ENULL
+
+
+# ---------------------------------------------------------------- PCA factors
+def _pca_prm(**kw):
+    base = dict(d=256, d_out=128, T=0, rank=16, bits=4, group=32, p=2.0,
+                lam=1e-3, alpha=0.5)
+    base.update(kw)
+    return ttq.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,iters,status", [
+    (dict(rank=12), 2, ttq.TTQ_EUNSUPPORTED),
+    (dict(rank=256, d=512, d_out=512), 2, ttq.TTQ_EUNSUPPORTED),
+    (dict(rank=0), 2, ttq.TTQ_EINVAL),
+    (dict(rank=16, d_out=8), 2, ttq.TTQ_EINVAL),       # rank > d_out
+    (dict(rank=16), -1, ttq.TTQ_EINVAL),
+    (dict(rank=16), 17, ttq.TTQ_EINVAL),
+    (dict(d_out=0), 2, ttq.TTQ_EINVAL),
+    (dict(T=-1), 2, ttq.TTQ_EINVAL),
+    (dict(T=4, d=260), 2, ttq.TTQ_EUNSUPPORTED),       # token rows of 16 bytes
+    (dict(T=4, p=0.0), 2, ttq.TTQ_EINVAL),
+    (dict(T=4, alpha=-1.0), 2, ttq.TTQ_EINVAL),
+])
+def test_pca_validation(kw, iters, status):
+    p = _pca_prm(**kw)
+    out = ctypes.c_size_t(5)
+    assert lib().ttq_lowrank_pca_workspace_bytes(ctypes.byref(p), iters,
+                                                 ctypes.byref(out)) == status
+    assert out.value == 5
+    assert lib().ttq_lowrank_pca(ctypes.byref(p), iters, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None, FAKE, 1 << 40, None) == status
+
+
+def test_pca_pointers_and_workspace():
+    p = _pca_prm()
+    need = ttq.ttq_lowrank_pca_workspace_bytes(p, 2)
+    assert need > 0
+    # bits / group / flags / qformat are not read; T = 0 needs no X
+    assert ttq.ttq_lowrank_pca_workspace_bytes(_pca_prm(bits=1, group=7), 2) == need
+    call = lambda **k: lib().ttq_lowrank_pca(
+        ctypes.byref(k.get("p", p)), 2, k.get("W", FAKE), k.get("X", None),
+        k.get("Om", FAKE), k.get("B", FAKE), k.get("A", FAKE), None,
+        k.get("ws", FAKE), k.get("wsb", need), None)
+    assert call(W=None) == ttq.TTQ_ENULL
+    assert call(Om=None) == ttq.TTQ_ENULL
+    assert call(B=None) == ttq.TTQ_ENULL
+    assert call(A=None) == ttq.TTQ_ENULL
+    assert call(ws=None) == ttq.TTQ_ENULL
+    assert call(p=_pca_prm(T=4)) == ttq.TTQ_ENULL       # T > 0 needs X
+    assert call(wsb=need - 1) == ttq.TTQ_EWORKSPACE
+    assert call(W=FAKE + 8) == ttq.TTQ_EALIGN
+    # online statistics need their own workspace
+    assert ttq.ttq_lowrank_pca_workspace_bytes(_pca_prm(T=300), 2) > need

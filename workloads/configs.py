@@ -46,6 +46,8 @@ __all__ = [
     "make_c5",
     "C5_PROJECTIONS",
     "draw_x",
+    "draw_omega",
+    "draw_lowrank_w",
 ]
 
 # (name, d_in, d_out) of the seven projections of a 7B-class decoder layer.
@@ -126,7 +128,7 @@ def _normal_bits(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 
 
 # Stream indices under each problem seed.
-_S_W, _S_B, _S_A, _S_X = 0, 1, 2, 3
+_S_W, _S_B, _S_A, _S_X, _S_OMEGA, _S_LR = 0, 1, 2, 3, 4, 5
 
 
 def draw_x(seed: int, call: int, R: int, T: int, d: int, kind: str,
@@ -227,3 +229,24 @@ def make_c5(T: int, proj: str = "q_proj", R: int = 8, **kw) -> Problem:
                 x_kind="logu10_100", n_outliers=max(1, round(0.01 * d)))
     args.update(kw)
     return make_problem(f"c5_{proj}_T{T}", **args)
+
+
+def draw_omega(seed: int, d: int, r: int) -> np.ndarray:
+    """Gaussian test matrix [d, r] (float32) for the PCA range finder."""
+    return _rng(seed, _S_OMEGA).standard_normal((d, r)).astype(np.float32)
+
+
+def draw_lowrank_w(seed: int, d_out: int, d: int, r: int, gap: float = 30.0,
+                   sigma: float = 0.02) -> np.ndarray:
+    """bf16 weights with a planted rank-r part: W = U S V^T + E with the
+    planted singular values (2 .. 1) x sigma sqrt(d) and a Gaussian E whose
+    singular values sit about ``gap`` times lower (a clear spectral gap at r,
+    as the PCA tests need).  U, V are Gaussian (not orthonormalised: the
+    planted part is then only approximately of singular values S)."""
+    rng = _rng(seed, _S_LR)
+    U = rng.standard_normal((d_out, r)) / np.sqrt(d_out)
+    V = rng.standard_normal((d, r)) / np.sqrt(d)
+    S = np.linspace(2.0, 1.0, r) * sigma * np.sqrt(d)
+    E = rng.standard_normal((d_out, d)) * (sigma / gap) / np.sqrt(max(d_out, d)) \
+        * np.sqrt(d) / 2.0
+    return bf16_round_bits(((U * S) @ V.T + E).astype(np.float32))
