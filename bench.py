@@ -199,6 +199,53 @@ def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
     return out
 
 
+FP32_PEAK_TFLOPS = 157.3
+
+
+def measure_pca(torch, ttq, reps: int = 10):
+    """Low-rank factors by PCA on the same 4096 x 4096 weights shape: r = 64,
+    two power iterations, static (context for the low-rank row; not the
+    timed step)."""
+    import numpy as np
+    from workloads.configs import draw_lowrank_w, draw_omega
+    d = d_out = 4096
+    r, iters = 64, 2
+    W = dev_bf16(draw_lowrank_w(1, d_out, d, r), torch)
+    Om = torch.from_numpy(draw_omega(2, d, r)).cuda()
+    prm = ttq.make_params(d=d, d_out=d_out, T=0, rank=r, bits=4, group=32,
+                          p=2.0, lam=0.0, alpha=0.0)
+    ws = torch.empty(ttq.ttq_lowrank_pca_workspace_bytes(prm, iters),
+                     dtype=torch.uint8, device="cuda")
+    f = lambda: ttq.ttq_lowrank_pca(W, Om, iters=iters, workspace=ws)
+    for _ in range(2):
+        f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ttq.timing_reset()
+    ttq.timing_enable(True)
+    for _ in range(reps):
+        f()
+    torch.cuda.synchronize()
+    kt = {k: v[0] / reps for k, v in ttq.timing_query().items() if v[1]}
+    ttq.timing_enable(False)
+    ttq.timing_reset()
+    # products with W: M Omega, 2 per power iteration, W^T Q for A (+ Gram
+    # and substitution work on the d x r panels, not counted)
+    flops_w = (2 + 2 * iters) * 2.0 * d_out * d * r
+    sk = kt.get("pca_skinny", float("nan"))
+    return {"shape": f"{d_out}x{d}, r={r}, {iters} power iterations",
+            "ms": ms, "kernels_ms": kt,
+            "skinny_tflops_w_products": flops_w / (sk * 1e-3) / 1e12,
+            "skinny_frac_fp32_peak": flops_w / (sk * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
+
+
 def cpu_baseline(T: int, seconds: float, qformat: str = "asym"):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import numpy as np
@@ -448,6 +495,8 @@ def main():
         }
     if fmts:
         line["other_formats"] = fmts
+    if not a.only_ttq:
+        line["lowrank_pca"] = measure_pca(torch, ttq)
     if not a.no_cpu and not a.only_ttq:
         line["cpu_baseline"] = cpu_baseline(T, a.cpu_seconds, a.qformat)
     print(json.dumps(line), flush=True)
