@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only-pca", action="store_true",
+                    help="time only the PCA low-rank factorisation "
+                         "(4096 x 4096, r = 64) and print its JSON")
     ap.add_argument("--only-ttq", action="store_true",
                     help="time only the TTQ step (for profiler runs)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -394,6 +397,10 @@ def main():
     import online_activation_aware_ttq_amd as ttq
 
     torch.cuda.init()
+    if a.only_pca:
+        print(json.dumps({"lowrank_pca": measure_pca(torch, ttq, reps=a.steps)}),
+              flush=True)
+        return
     main_m = measure(a.T, a.steps, a.warmup, torch, ttq,
                      want_graph=not a.only_ttq, want_gemm=not a.only_ttq,
                      qformat=a.qformat)

@@ -18,8 +18,11 @@
 //                   columns may be scaled by D^{1/2} as they are staged
 //   k_psum          ordered sum of the partials -> float32, and optionally
 //                   bf16 (as is, or transposed)
-//   k_chol          one workgroup: G = R^T R (Cholesky in float64)
-//   k_trsm          Q = Y R^{-1}, one row per lane (forward substitution)
+//   k_cholinv_wave  r <= 64: R^{-1} of the Gram matrix's Cholesky factor in
+//                   one wave (float64 registers); Q = Y R^{-1} is then one
+//                   more skinny product
+//   k_chol, k_trsm  r = 128: Cholesky in one workgroup (float64 in LDS) and
+//                   Q = Y R^{-1} by forward substitution, one row per lane
 //   k_lr_residual   W_res = bf16(W - B A) from the bf16 factors
 #include "ttq_internal.h"
 
@@ -29,20 +32,33 @@ namespace {
 
 constexpr int SK_T = 64;  // rows of a C tile, and channels of a K tile
 
-template <int NC, bool TN, typename TA>
+// a lane owns RW rows x CW columns of the 64 x N tile: (64 / RW) row groups
+// times (N / CW) column groups = 256 lanes; within a wave the A values are a
+// few contiguous LDS addresses and the Bm values a few broadcast ones
+template <int N>
+struct SkinnyShape {
+  static constexpr int RW = N >= 16 ? 4 : 2;
+  static constexpr int CW = N * RW >= 64 ? N * RW / 64 : 1;
+};
+
+template <int N, bool TN, typename TA>
 __global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
-  constexpr int N = 4 * NC;  // columns of C
-  __shared__ float tA[SK_T][SK_T + 1];  // [k][row]
+  constexpr int RW = SkinnyShape<N>::RW, CW = SkinnyShape<N>::CW;
+  constexpr int NRG = SK_T / RW;
+  static_assert(NRG * (N / CW) == 256, "lane layout");
+  __shared__ __attribute__((aligned(16))) float tA[SK_T][SK_T + 4];  // [k][row]
   __shared__ __attribute__((aligned(16))) float tB[SK_T][N];
   const int t = threadIdx.x;
-  const int r = t & 63, cg = t >> 6;  // row of the tile, column group (per wave)
+  const int rg = t % NRG, cg = t / NRG;
   const int64_t r0 = (int64_t)blockIdx.x * SK_T;
   const int64_t k0 = (int64_t)blockIdx.y * a.kc;
   const int64_t k1 = min(a.K, k0 + a.kc);
   const TA* A = static_cast<const TA*>(a.A);
-  float acc[NC];
+  float acc[RW][CW];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[i][c] = 0.f;
   for (int64_t kt = k0; kt < k1; kt += SK_T) {
     // stage the A tile as [k][row]; element (row, k) is A[row][k] (C = A Bm)
     // or A[k][row] (C = A^T Bm); the index along the memory row is the one
@@ -70,19 +86,28 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
       tB[kk][c] = k < k1 ? a.Bm[k * a.ldb + c] : 0.f;
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 2
     for (int kk = 0; kk < SK_T; ++kk) {
-      const float av = tA[kk][r];
+      float av[RW], bv[CW];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = fmaf(av, tB[kk][cg * NC + c], acc[c]);
+      for (int i = 0; i < RW; ++i) av[i] = tA[kk][rg * RW + i];
+#pragma unroll
+      for (int c = 0; c < CW; ++c) bv[c] = tB[kk][cg * CW + c];
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[i][c] = fmaf(av[i], bv[c], acc[i][c]);
     }
     __syncthreads();
   }
-  const int64_t row = r0 + r;
-  if (row < a.rows) {
-    float* out = a.part + ((int64_t)blockIdx.y * a.rows + row) * N + cg * NC;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) out[c] = acc[c];
+  for (int i = 0; i < RW; ++i) {
+    const int64_t row = r0 + rg * RW + i;
+    if (row < a.rows) {
+      float* out = a.part + ((int64_t)blockIdx.y * a.rows + row) * N + cg * CW;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) out[c] = acc[i][c];
+    }
   }
 }
 
@@ -91,6 +116,7 @@ __global__ __launch_bounds__(256) void k_psum(PsumArgs a) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
     float v = 0.f;
+#pragma unroll 8
     for (int z = 0; z < a.nsplit; ++z) v += a.part[(int64_t)z * total + e];
     if (a.out) a.out[e] = v;
     const int64_t i = e / a.n, c = e % a.n;
@@ -139,6 +165,75 @@ __global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
     const int i = e / n, j = e % n;
     R[e] = i < j ? (float)(L[i * ld + j] / sqrt(piv[i]))
                  : (i == j ? (float)sqrt(piv[i]) : 0.f);
+  }
+}
+
+// n <= 64: Cholesky and inverse in one wave, the rows in float64 registers.
+// Lane i holds row i of G.  Step k (unrolled): the pivot comes from lane k
+// (readlane), every lane writes its L[i][k] to LDS and reads the column back
+// as broadcasts, and updates its own row:
+//   L[i][k] = g_i[k] / sqrt(p_k),  g_i[j] -= L[i][k] L[j][k]  (j > k)
+// Then every lane writes its row of L to LDS and lane j solves column j of
+// L^{-1} down the rows (row i of L read as broadcasts):
+//   z_i = (delta_ij - sum_{m<i} L[i][m] z_m) / L[i][i]
+// and writes row j of R^{-1} = (L^{-1})^T: Rinv[j][i] = z_i.
+__device__ __forceinline__ double bcast(double v, int lane) {
+  const unsigned long long b = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)b, lane);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(b >> 32), lane);
+  return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
+
+// LDS writes of this wave visible to its later LDS reads
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int N>
+__global__ __launch_bounds__(64) void k_cholinv_wave(const float* G, float* Rinv) {
+  __shared__ double col[64];
+  __shared__ double Ls[N][N + 1];
+  const int l = threadIdx.x;
+  const bool live = l < N;
+  double g[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    g[j] = live ? 0.5 * ((double)G[l * N + j] + (double)G[j * N + l]) : 0.0;
+  // pivot floor: 1e-14 of the largest diagonal entry
+  double dmax = live ? (double)G[l * N + l] : 0.0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, off));
+  const double floor = 1e-14 * (dmax > 0.0 ? dmax : 1.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const double pk = fmax(bcast(g[k], k), floor);
+    const double rk = sqrt(pk);
+    const double lik = (l == k) ? rk : g[k] / rk;
+    g[k] = lik;  // L[l][k] (meaningful for l >= k)
+    col[l] = lik;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = k + 1; j < N; ++j) g[j] = fma(-lik, col[j], g[j]);
+    wave_lds_sync();
+  }
+  if (live) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) Ls[l][m] = g[m];
+  }
+  wave_lds_sync();
+  double z[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    double acc = (i == l) ? 1.0 : 0.0;
+#pragma unroll
+    for (int m = 0; m < i; ++m) acc = fma(-Ls[i][m], z[m], acc);
+    z[i] = acc / Ls[i][i];
+  }
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) Rinv[l * N + i] = (float)z[i];
   }
 }
 
@@ -216,11 +311,11 @@ __global__ __launch_bounds__(256) void k_lr_residual(LrResidualArgs a) {
 template <bool TN, typename TA>
 hipError_t launch_skinny_t(const SkinnyArgs& a, dim3 grid, const Launch& L) {
   switch (a.n) {
-    case 8: return ext_launch(k_skinny<2, TN, TA>, grid, dim3(256), 0, L, a);
-    case 16: return ext_launch(k_skinny<4, TN, TA>, grid, dim3(256), 0, L, a);
-    case 32: return ext_launch(k_skinny<8, TN, TA>, grid, dim3(256), 0, L, a);
-    case 64: return ext_launch(k_skinny<16, TN, TA>, grid, dim3(256), 0, L, a);
-    case 128: return ext_launch(k_skinny<32, TN, TA>, grid, dim3(256), 0, L, a);
+    case 8: return ext_launch(k_skinny<8, TN, TA>, grid, dim3(256), 0, L, a);
+    case 16: return ext_launch(k_skinny<16, TN, TA>, grid, dim3(256), 0, L, a);
+    case 32: return ext_launch(k_skinny<32, TN, TA>, grid, dim3(256), 0, L, a);
+    case 64: return ext_launch(k_skinny<64, TN, TA>, grid, dim3(256), 0, L, a);
+    case 128: return ext_launch(k_skinny<128, TN, TA>, grid, dim3(256), 0, L, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -228,9 +323,13 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, dim3 grid, const Launch& L) {
 }  // namespace
 
 int skinny_splits(int64_t rows, int64_t K) {
+  // about 1536 workgroups (six per CU) so that the loads of one hide behind
+  // the arithmetic of the others
   const int64_t tiles = (rows + SK_T - 1) / SK_T;
-  int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t smax = (K + 255) / 256;
+  int64_t s = (1536 + tiles - 1) / tiles;
+  // at least 256 channels a split, but one K tile for the small products
+  // (the r x r Gram matrices: one or two row tiles)
+  const int64_t smax = tiles <= 2 ? (K + SK_T - 1) / SK_T : (K + 255) / 256;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
   // whole K tiles per split
@@ -268,6 +367,16 @@ hipError_t launch_chol(const float* G, float* R, int n, const Launch& L) {
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)((128 * 129 + 128) * sizeof(double)));
   if (attr != hipSuccess) return attr;
   return ext_launch(k_chol, dim3(1), dim3(256), lds, L, G, R, n);
+}
+
+hipError_t launch_cholinv_wave(const float* G, float* Rinv, int n, const Launch& L) {
+  switch (n) {
+    case 8: return ext_launch(k_cholinv_wave<8>, dim3(1), dim3(64), 0, L, G, Rinv);
+    case 16: return ext_launch(k_cholinv_wave<16>, dim3(1), dim3(64), 0, L, G, Rinv);
+    case 32: return ext_launch(k_cholinv_wave<32>, dim3(1), dim3(64), 0, L, G, Rinv);
+    case 64: return ext_launch(k_cholinv_wave<64>, dim3(1), dim3(64), 0, L, G, Rinv);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_trsm(float* Y, const float* R, int64_t m, int n, const Launch& L) {

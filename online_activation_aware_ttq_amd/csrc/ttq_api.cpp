@@ -919,6 +919,8 @@ PcaPlan make_pca_plan(const ttq_params* prm) {
   need(P.sp_tn, d);
   need(P.sp_gy, n);
   need(P.sp_gz, n);
+  need(1, dout);  // Y R^{-1} (r <= 64)
+  need(1, d);
   P.off_part = take(part);
   P.off_g = take(sizeof(float) * n * n);
   P.off_r = take(sizeof(float) * n * n);
@@ -996,14 +998,22 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
     pa.rows = rows; pa.n = n; pa.out = out; pa.out_bf16 = out_b; pa.out_bf16_t = out_bt;
     return run(K_PSUM, s, [&](const Launch& L) { return launch_psum(pa, L); });
   };
-  // CholeskyQR2 of the float32 panel V [m][n], in place
-  auto orth = [&](float* V, int64_t m, int sp_gram) -> int {
-    for (int pass = 0; pass < 2; ++pass) {
+  // CholeskyQR of the float32 panel V [m][n], in place: two passes for the
+  // final basis (CholeskyQR2), one for the intermediate panels of the power
+  // iteration, which only carry the subspace to the next product
+  auto orth = [&](float* V, int64_t m, int sp_gram, int passes) -> int {
+    for (int pass = 0; pass < passes; ++pass) {
       int r = product(true, false, V, n, nullptr, n, m, V, sp_gram, G, nullptr, nullptr);
       if (r != TTQ_OK) return r;
-      r = run(K_CHOL, s, [&](const Launch& L) { return launch_chol(G, Rf, (int)n, L); });
-      if (r != TTQ_OK) return r;
-      r = run(K_TRSM, s, [&](const Launch& L) { return launch_trsm(V, Rf, m, (int)n, L); });
+      if (n <= 64) {  // R^{-1} in one wave, then V R^{-1} as a product
+        r = run(K_CHOL, s, [&](const Launch& L) { return launch_cholinv_wave(G, Rf, (int)n, L); });
+        if (r != TTQ_OK) return r;
+        r = product(false, false, V, n, nullptr, m, n, Rf, 1, V, nullptr, nullptr);
+      } else {
+        r = run(K_CHOL, s, [&](const Launch& L) { return launch_chol(G, Rf, (int)n, L); });
+        if (r != TTQ_OK) return r;
+        r = run(K_TRSM, s, [&](const Launch& L) { return launch_trsm(V, Rf, m, (int)n, L); });
+      }
       if (r != TTQ_OK) return r;
     }
     return TTQ_OK;
@@ -1011,14 +1021,14 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
 
   // Q = orth(M Omega)
   st = product(false, true, Wb, d, dh, dout, d, Omega, P.sp_nt, Y, nullptr, nullptr);
-  if (st == TTQ_OK) st = orth(Y, dout, P.sp_gy);
+  if (st == TTQ_OK) st = orth(Y, dout, P.sp_gy, iters == 0 ? 2 : 1);
   for (int it = 0; it < iters && st == TTQ_OK; ++it) {
     // Z = orth(M^T Q) = orth(D^{1/2} W^T Q);  Q = orth(M Z)
     st = product(true, true, Wb, d, dh, d, dout, Y, P.sp_tn, Z, nullptr, nullptr);
-    if (st == TTQ_OK) st = orth(Z, d, P.sp_gz);
+    if (st == TTQ_OK) st = orth(Z, d, P.sp_gz, 1);
     if (st == TTQ_OK)
       st = product(false, true, Wb, d, dh, dout, d, Z, P.sp_nt, Y, nullptr, nullptr);
-    if (st == TTQ_OK) st = orth(Y, dout, P.sp_gy);
+    if (st == TTQ_OK) st = orth(Y, dout, P.sp_gy, it + 1 == iters ? 2 : 1);
   }
   if (st != TTQ_OK) return st;
   // B = bf16(Q); A = bf16(Q^T W), written transposed from W^T Q
