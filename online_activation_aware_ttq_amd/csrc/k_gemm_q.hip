@@ -191,9 +191,13 @@ __device__ __forceinline__ u32x4 dequant_half(const JobIn<CB>& J, int h,
                                               const f32x4 (&dhi)[4], int p) {
   float sg, mg;
   if constexpr (GS == 32) {  // group 2h + p/4 of the chunk row
+    // (the four values as scalars first: a select between two elements of
+    // the ring's vectors made the compiler keep the whole ring in scratch)
     const bool odd = p & 4;
-    sg = odd ? J.s4[2 * h + 1] : J.s4[2 * h];
-    mg = odd ? J.m4[2 * h + 1] : J.m4[2 * h];
+    const float s0 = h ? J.s4.z : J.s4.x, s1 = h ? J.s4.w : J.s4.y;
+    const float m0 = h ? J.m4.z : J.m4.x, m1 = h ? J.m4.w : J.m4.y;
+    sg = odd ? s1 : s0;
+    mg = odd ? m1 : m0;
   } else {
     sg = J.s[h];
     mg = J.m[h];
