@@ -146,3 +146,22 @@ def test_pca_is_deterministic():
     b = _gpu_pca(Wb, Om, 2)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+def test_degenerate_inputs():
+    """An all-zero W (a singular Gram matrix at every step: the pivot floor)
+    gives zero factors and a zero residual, no NaN; a square W of full rank
+    r = d_out is reproduced by its factors (residual at the rounding level)."""
+    Z = np.zeros((64, 128), dtype=np.uint16)
+    Om = draw_omega(41, 128, 16)
+    Bg, Ag, Rg = _gpu_pca(Z, Om, 2)
+    for x in (Bg, Ag, Rg):
+        v = oracle.bf16_to_f64(x)
+        assert np.all(np.isfinite(v)) and not np.any(v)
+    from workloads.configs import bf16_round_bits
+    rng = np.random.default_rng(42)
+    Wb = bf16_round_bits((rng.standard_normal((32, 96)) * 0.05).astype(np.float32))
+    Bg, Ag, Rg = _gpu_pca(Wb, draw_omega(43, 96, 32), 1)
+    W = oracle.bf16_to_f64(Wb)
+    R = oracle.bf16_to_f64(Rg)
+    assert np.linalg.norm(R) <= 1e-2 * np.linalg.norm(W)
