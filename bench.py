@@ -249,6 +249,52 @@ def measure_pca(torch, ttq, reps: int = 10):
             "skinny_frac_fp32_peak": flops_w / (sk * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
 
 
+def measure_decode(torch, ttq, steps: int = 1000):
+    """One token against codes stored by ttq_quantize (the same 4096 x 4096
+    weights, 4-bit g128): 20 rotating stored copies, as for the main step."""
+    from workloads import configs as wc
+    d = d_out = 4096
+    prob = wc.make_c2(T=16)
+    W0 = dev_bf16(prob.W, torch)
+    X0 = dev_bf16(prob.X[0], torch)
+    kw = dict(bits=4, group=128)
+    st = [ttq.ttq_quantize(W0, X0, p=prob.p, lam=prob.lam, alpha=prob.alpha, **kw)
+          for _ in range(20)]
+    Xs = [dev_bf16(wc.draw_x(1, 3000 + c, 1, 1, d, "logu10_100", 41)[0], torch)
+          for c in range(64)]
+    Y = torch.empty(1, d_out, dtype=torch.float32, device="cuda")
+    prm = ttq.make_params(d=d, d_out=d_out, T=1, bits=4, group=128, p=1.0,
+                          lam=0.0, alpha=0.0)
+    ws = torch.empty(max(256, ttq.ttq_qmatmul_workspace_bytes(prm)),
+                     dtype=torch.uint8, device="cuda")
+    f = lambda i: ttq.ttq_qmatmul(*st[i % 20], Xs[i % 64], Y=Y, workspace=ws, **kw)
+    for i in range(50):
+        f(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        f(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ttq.timing_reset()
+    ttq.timing_enable(True)
+    for i in range(steps):
+        f(i)
+    torch.cuda.synchronize()
+    kt = {k: v[0] / v[1] for k, v in ttq.timing_query().items() if v[1]}
+    ttq.timing_enable(False)
+    ttq.timing_reset()
+    G = d // 128
+    alg = d_out * d // 2 + 8 * d_out * G + 2 * d + 4 * d + 4 * d_out
+    k = kt.get("qgemv", float("nan"))
+    return {"workload": "4096x4096, 4-bit g128 codes, one token", "ms_per_step": ms,
+            "tokens_per_s": 1.0 / (ms * 1e-3), "kernel": "qgemv", "kernel_ms": k,
+            "alg_bytes": alg, "hbm_frac_kernel": alg / (k * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(T: int, seconds: float, qformat: str = "asym"):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import numpy as np
@@ -503,6 +549,7 @@ def main():
     if fmts:
         line["other_formats"] = fmts
     if not a.only_ttq:
+        line["decode_from_codes"] = measure_decode(torch, ttq)
         line["lowrank_pca"] = measure_pca(torch, ttq)
     if not a.no_cpu and not a.only_ttq:
         line["cpu_baseline"] = cpu_baseline(T, a.cpu_seconds, a.qformat)

@@ -130,6 +130,24 @@ def make_params(*, d: int, d_out: int, T: int, rank: int = 0, bits: int,
                       int(flags), qformat_code(qformat))
 
 
+# The calls below build the same parameter block for every call of one shape;
+# the library only reads it, so one block per shape is kept (bounded).
+_PARAMS = {}
+
+
+def _params(d, d_out, T, rank, bits, group, p, lam, alpha, flags, qformat):
+    key = (d, d_out, T, rank, bits, group, p, lam, alpha, flags, qformat)
+    prm = _PARAMS.get(key)
+    if prm is None:
+        if len(_PARAMS) > 4096:
+            _PARAMS.clear()
+        prm = _PARAMS[key] = make_params(d=d, d_out=d_out, T=T, rank=rank,
+                                         bits=bits, group=group, p=p, lam=lam,
+                                         alpha=alpha, flags=flags,
+                                         qformat=qformat)
+    return prm
+
+
 def ttq_status_string(status: int) -> str:
     return load_library().ttq_status_string(int(status)).decode()
 
@@ -160,14 +178,12 @@ def _ptr(t) -> Optional[int]:
 
 
 def _check(t, name, dtype, shape, device):
-    import torch
     if t is None:
         return
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if getattr(t, "dtype", None) is not dtype:
+        raise TypeError(f"{name} must be a torch.Tensor of {dtype}, got "
+                        f"{getattr(t, 'dtype', type(t))}")
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -197,10 +213,7 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
     _check(A, "A", torch.bfloat16, (rank, d), dev)
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
-    prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
-                      group=group, p=p, lam=lam, alpha=alpha, flags=flags,
-                      qformat=qformat)
-    need = ttq_workspace_bytes(prm, R)
+    prm = _params(d, d_out, T, rank, bits, group, p, lam, alpha, flags, qformat)
     if Y is None:
         Y = torch.empty(lead + (T, d_out), dtype=torch.float32, device=dev)
     _check(Y, "Y", torch.float32, lead + (T, d_out), dev)
@@ -208,7 +221,8 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
     _check(scales_out, "scales_out", torch.float32, lead + (d_out, G), dev)
     _check(mins_out, "mins_out", torch.float32, lead + (d_out, G), dev)
     _check(dhalf_out, "dhalf_out", torch.float32, lead + (d,), dev)
-    if workspace is None:
+    if workspace is None:  # (a given workspace is checked by the library)
+        need = ttq_workspace_bytes(prm, R)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -328,6 +342,20 @@ def ttq_packed_row_bytes(prm: ttq_params) -> int:
     return int(out.value)
 
 
+_ROW_BYTES = {}
+
+
+def _row_bytes(d: int, bits: int, group: int) -> int:
+    """Packed row bytes for the shape checks of the calls below (the calls
+    themselves validate every parameter)."""
+    key = (d, bits, group)
+    if key not in _ROW_BYTES:
+        _ROW_BYTES[key] = ttq_packed_row_bytes(
+            make_params(d=d, d_out=1, T=0, bits=bits, group=group, p=1.0,
+                        lam=0.0, alpha=0.0))
+    return _ROW_BYTES[key]
+
+
 def ttq_quantize_workspace_bytes(prm: ttq_params) -> int:
     out = ctypes.c_size_t(0)
     st = load_library().ttq_quantize_workspace_bytes(ctypes.byref(prm),
@@ -411,11 +439,8 @@ def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
         raise ValueError("X must be a GPU tensor")
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
-    prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
-                      group=group, p=1.0, lam=0.0, alpha=0.0, flags=flags,
-                      qformat=qformat)
-    rb = ttq_packed_row_bytes(prm)
-    need = ttq_qmatmul_workspace_bytes(prm)
+    prm = _params(d, d_out, T, rank, bits, group, 1.0, 0.0, 0.0, flags, qformat)
+    rb = _row_bytes(d, bits, group)
     G = d // group
     _check(codes, "codes", torch.uint8, (d_out, rb), dev)
     _check(scales, "scales", torch.float32, (d_out, G), dev)
@@ -427,7 +452,8 @@ def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
     if Y is None:
         Y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
     _check(Y, "Y", torch.float32, (T, d_out), dev)
-    if workspace is None:
+    if workspace is None:  # (a given workspace is checked by the library)
+        need = ttq_qmatmul_workspace_bytes(prm)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
