@@ -293,7 +293,8 @@ int ttq_timing_query(int kernel, double* total_ms, int64_t* launches);
  *      W ~ Q_D[Wres] + B A;
  * by randomized subspace iteration (Halko, Martinsson and Tropp, 2011):
  * Q = orth(M Omega), then `iters` times Z = orth(M^T Q), Q = orth(M Z), with
- * orth = CholeskyQR2 (float32 panels, float64 Cholesky), B = Q.
+ * orth = CholeskyQR (float32 panels, float64 Cholesky; two passes for the
+ * final basis, one for the intermediate panels), B = Q.
  *   prm     d, d_out >= 1; rank in {8, 16, 32, 64, 128}, <= min(d, d_out);
  *           T >= 0 (T > 0 needs d % 8 == 0); bits, group, flags and qformat
  *           are not read

@@ -6,8 +6,8 @@
 // current activations), A = B^T W, and the residual W - B A is what the
 // quantizer sees.  The subspace comes from randomized subspace iteration
 // (Halko, Martinsson and Tropp, 2011): Q = orth(M Omega), then per power
-// iteration Z = orth(M^T Q), Q = orth(M Z); orth is CholeskyQR2 (Gram
-// matrix, Cholesky in float64, Q = Y R^{-1} by substitution, twice).
+// iteration Z = orth(M^T Q), Q = orth(M Z); orth is CholeskyQR (Gram
+// matrix, Cholesky in float64, Q = Y R^{-1}), twice for the final basis.
 //
 // Kernels (all float32 accumulation on the VALU: the products are skinny,
 // r <= 128 columns, and the factors must be accurate to float32 before the
