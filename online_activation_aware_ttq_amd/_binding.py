@@ -141,11 +141,46 @@ def _params(d, d_out, T, rank, bits, group, p, lam, alpha, flags, qformat):
     if prm is None:
         if len(_PARAMS) > 4096:
             _PARAMS.clear()
+            _NEED.clear()
         prm = _PARAMS[key] = make_params(d=d, d_out=d_out, T=T, rank=rank,
                                          bits=bits, group=group, p=p, lam=lam,
                                          alpha=alpha, flags=flags,
                                          qformat=qformat)
-    return prm
+    return prm, key
+
+
+def _current_stream(dev) -> int:
+    """Raw handle of torch's current stream on `dev` (the cheap accessor when
+    this torch build has it)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+# Workspace for calls that bring none: one buffer per (device, stream), kept
+# between calls.  Calls on one stream run in order, so they can share it;
+# calls on different streams get different buffers.  When a buffer has to
+# grow, the stream is drained before the old one is released.
+_NEED = {}
+_SCRATCH = {}
+
+
+def _workspace(dev, stream, need_key, query):
+    import torch
+    need = _NEED.get(need_key) if need_key is not None else None
+    if need is None:
+        need = max(int(query()), 256)
+        if need_key is not None:
+            _NEED[need_key] = need
+    key = (dev.index, stream)
+    buf = _SCRATCH.get(key)
+    if buf is None or buf.numel() < need:
+        if buf is not None:
+            torch.cuda.synchronize(dev)
+        buf = _SCRATCH[key] = torch.empty(need, dtype=torch.uint8, device=dev)
+    return buf
 
 
 def ttq_status_string(status: int) -> str:
@@ -213,7 +248,8 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
     _check(A, "A", torch.bfloat16, (rank, d), dev)
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
-    prm = _params(d, d_out, T, rank, bits, group, p, lam, alpha, flags, qformat)
+    prm, key = _params(d, d_out, T, rank, bits, group, p, lam, alpha, flags,
+                       qformat)
     if Y is None:
         Y = torch.empty(lead + (T, d_out), dtype=torch.float32, device=dev)
     _check(Y, "Y", torch.float32, lead + (T, d_out), dev)
@@ -221,11 +257,11 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
     _check(scales_out, "scales_out", torch.float32, lead + (d_out, G), dev)
     _check(mins_out, "mins_out", torch.float32, lead + (d_out, G), dev)
     _check(dhalf_out, "dhalf_out", torch.float32, lead + (d,), dev)
-    if workspace is None:  # (a given workspace is checked by the library)
-        need = ttq_workspace_bytes(prm, R)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _current_stream(dev)
+    if workspace is None:  # (a given workspace is checked by the library)
+        workspace = _workspace(dev, stream, ("linear", key, R),
+                               lambda: ttq_workspace_bytes(prm, R))
     args = [_ptr(W), _ptr(X), _ptr(B), _ptr(A), _ptr(Y), _ptr(codes_out),
             _ptr(scales_out), _ptr(mins_out), _ptr(dhalf_out),
             _ptr(workspace), workspace.numel(), stream]
@@ -305,7 +341,6 @@ def ttq_linear_segmented(W, X, B=None, A=None, *, seg_offsets, p: float,
     prm = make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
                       group=group, p=p, lam=lam, alpha=alpha, flags=flags,
                       qformat=qformat)
-    need = ttq_segmented_workspace_bytes(prm, seg_offsets)
     if Y is None:
         Y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
     _check(Y, "Y", torch.float32, (T, d_out), dev)
@@ -313,10 +348,11 @@ def ttq_linear_segmented(W, X, B=None, A=None, *, seg_offsets, p: float,
     _check(scales_out, "scales_out", torch.float32, (n, d_out, G), dev)
     _check(mins_out, "mins_out", torch.float32, (n, d_out, G), dev)
     _check(dhalf_out, "dhalf_out", torch.float32, (n, d), dev)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, stream, None,
+                               lambda: ttq_segmented_workspace_bytes(prm, seg_offsets))
     arr, _ = _offsets(seg_offsets)
     st = load_library().ttq_linear_segmented(
         ctypes.byref(prm), n, ctypes.cast(arr, ctypes.c_void_p), _ptr(W),
@@ -393,7 +429,6 @@ def ttq_quantize(W, X, *, p: float, lam: float, alpha: float, bits: int,
     prm = make_params(d=d, d_out=d_out, T=T, bits=bits, group=group, p=p,
                       lam=lam, alpha=alpha, qformat=qformat)
     rb = ttq_packed_row_bytes(prm)
-    need = ttq_quantize_workspace_bytes(prm)
     G = d // group
     _check(W, "W", torch.bfloat16, (d_out, d), dev)
     _check(X, "X", torch.bfloat16, (T, d), dev)
@@ -410,10 +445,11 @@ def ttq_quantize(W, X, *, p: float, lam: float, alpha: float, bits: int,
     _check(mins, "mins", torch.float32, (d_out, G), dev)
     _check(dhalf_inv, "dhalf_inv", torch.float32, (d,), dev)
     _check(dhalf_out, "dhalf_out", torch.float32, (d,), dev)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, stream, None,
+                               lambda: ttq_quantize_workspace_bytes(prm))
     st = lib.ttq_quantize(ctypes.byref(prm), _ptr(W), _ptr(X), _ptr(codes),
                           _ptr(scales), _ptr(mins), _ptr(dhalf_inv),
                           _ptr(dhalf_out), _ptr(workspace), workspace.numel(),
@@ -439,7 +475,8 @@ def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
         raise ValueError("X must be a GPU tensor")
     if (A is None) != (B is None):
         raise ValueError("pass both B and A or neither")
-    prm = _params(d, d_out, T, rank, bits, group, 1.0, 0.0, 0.0, flags, qformat)
+    prm, key = _params(d, d_out, T, rank, bits, group, 1.0, 0.0, 0.0, flags,
+                       qformat)
     rb = _row_bytes(d, bits, group)
     G = d // group
     _check(codes, "codes", torch.uint8, (d_out, rb), dev)
@@ -452,11 +489,11 @@ def ttq_qmatmul(codes, scales, mins, dhalf_inv, X, B=None, A=None, *,
     if Y is None:
         Y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
     _check(Y, "Y", torch.float32, (T, d_out), dev)
-    if workspace is None:  # (a given workspace is checked by the library)
-        need = ttq_qmatmul_workspace_bytes(prm)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _current_stream(dev)
+    if workspace is None:  # (a given workspace is checked by the library)
+        workspace = _workspace(dev, stream, ("qmatmul", key),
+                               lambda: ttq_qmatmul_workspace_bytes(prm))
     st = lib.ttq_qmatmul(ctypes.byref(prm), _ptr(codes), _ptr(scales),
                          _ptr(mins), _ptr(dhalf_inv), _ptr(X), _ptr(B), _ptr(A),
                          _ptr(Y), _ptr(workspace), workspace.numel(), stream)
@@ -495,15 +532,15 @@ def ttq_lowrank_pca(W, Omega, *, iters: int, X=None, p: float = 2.0,
         _check(X, "X", torch.bfloat16, (T, d), dev)
     prm = make_params(d=d, d_out=d_out, T=T, rank=r, bits=4, group=32, p=p,
                       lam=lam, alpha=alpha)
-    need = ttq_lowrank_pca_workspace_bytes(prm, iters)
     B = torch.empty((d_out, r), dtype=torch.bfloat16, device=dev)
     A = torch.empty((r, d), dtype=torch.bfloat16, device=dev)
     Wres = torch.empty((d_out, d), dtype=torch.bfloat16, device=dev) \
         if want_residual else None
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, stream, None,
+                               lambda: ttq_lowrank_pca_workspace_bytes(prm, iters))
     st = load_library().ttq_lowrank_pca(
         ctypes.byref(prm), int(iters), _ptr(W), _ptr(X), _ptr(Omega), _ptr(B),
         _ptr(A), _ptr(Wres), _ptr(workspace), workspace.numel(), stream)
