@@ -216,3 +216,39 @@ def test_segmented_with_a_format_equals_single_calls():
                                       y1.cpu().numpy().view(np.uint32))
     prob = dataclasses.replace(base, T=40, X=xs[3][None])
     check_problem(prob, {"Y": Y[offs[3]:offs[4]][None]}, check_codes=False)
+
+
+@pytest.mark.parametrize("fmt,bits", [("sym", 3), ("fp8", 8)])
+def test_formats_segmented_with_exports_and_group_256(fmt, bits):
+    """Formats through continuous batching with exports (consecutive runs),
+    and group 256 on the fused path at 65..128 tokens."""
+    import torch
+    import online_activation_aware_ttq_amd as ttq
+    lengths = [3, 3, 70, 1]
+    base = make_problem("segx", d=512, d_out=160, T=1, bits=bits, group=256,
+                        rank=0, seed=97, qformat=fmt)
+    xs = [draw_x(400 + i, 0, 1, t, 512, "logu10_100", 5)[0]
+          for i, t in enumerate(lengths)]
+    offs = np.concatenate([[0], np.cumsum(lengths)]).tolist()
+    W = to_dev(base.W)
+    n = len(xs)
+    G = 2
+    kw = dict(p=base.p, lam=base.lam, alpha=base.alpha, bits=bits, group=256,
+              qformat=fmt)
+    ex = dict(codes_out=torch.empty((n, 160, 512), dtype=torch.uint8, device="cuda"),
+              scales_out=torch.empty((n, 160, G), dtype=torch.float32, device="cuda"),
+              mins_out=torch.empty((n, 160, G), dtype=torch.float32, device="cuda"),
+              dhalf_out=torch.empty((n, 512), dtype=torch.float32, device="cuda"))
+    Y = ttq.ttq_linear_segmented(W, to_dev(np.concatenate(xs)), seg_offsets=offs,
+                                 **kw, **ex)
+    torch.cuda.synchronize()
+    Yh = Y.cpu().numpy()
+    for i, x in enumerate(xs):
+        prob = dataclasses.replace(base, T=x.shape[0], X=x[None])
+        gpu = {"Y": Yh[offs[i]:offs[i + 1]][None],
+               "q": ex["codes_out"][i].cpu().numpy()[None],
+               "s": ex["scales_out"][i].cpu().numpy()[None],
+               "m": ex["mins_out"][i].cpu().numpy()[None],
+               "dh": ex["dhalf_out"][i].cpu().numpy()[None]}
+        rep = check_problem(prob, gpu)
+        _say(f"seg_{fmt}_g256_req{i}_T{x.shape[0]}", rep)

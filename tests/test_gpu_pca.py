@@ -69,6 +69,7 @@ def _check_factors(Wb, Bg, Ag, Rg, ref, rep):
     (520, 1024, 64, 1),
     (72, 200, 8, 3),      # ragged tiles, d not a multiple of 64
     (200, 384, 128, 2),   # the largest rank
+    (600, 256, 32, 2),    # more output rows than input channels
 ])
 def test_static_pca_matches_oracle(d_out, d, r, iters):
     Wb = draw_lowrank_w(d_out + d, d_out, d, r)
