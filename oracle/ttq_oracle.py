@@ -26,7 +26,7 @@ Notation: X has d input channels and T tokens.  Arrays here store it
 token-major, ``X[t, j]`` = channel j of token t, as a linear layer receives
 it.  W is ``[d_out, d]``; Y = W_hat X is stored ``[T, d_out]``.
 
-Readings taken where the pages leave a step open (all listed in the design doc):
+Readings taken where the pages leave a step open:
 
 1. Quantizer Q: asymmetric b-bit, groups of ``group`` consecutive input
    channels of one output row, min-anchored with a real zero point:
@@ -274,9 +274,9 @@ def ttq_linear_batched(W_bits, X_bits, **kw) -> list:
 # The statistics are computed per input prompt ([NL] Sec. 2, methodology),
 # and the speed-up of the deployed model comes from integer-matmul kernels
 # over stored low-bit weights ([NL] Sec. 3, efficiency; [ZH] Sec. 3) because
-# moving the weights is the bottleneck at scale ([ZH] Sec. 4).  Reading
-# (listed in the design doc): the deployed form keeps the codes, the per-group
-# (s, min) and D^{-1/2} of the prompt, and every later step computes
+# moving the weights is the bottleneck at scale ([ZH] Sec. 4).  Reading:
+# the deployed form keeps the codes, the per-group (s, min) and D^{-1/2} of
+# the prompt, and every later step computes
 # Y = ((min + s q) D^{-1/2}) X + B (A X) with those stored values.
 #
 # Storage of the codes: each code takes the smallest of 1, 2, 4, 8 bits that
@@ -693,7 +693,7 @@ def band_excused_levels(lv_gpu, lv_ref, t64, rel: float = 1e-6):
 # low-rank factors by PCA: [NL] Sec. 2 (static factors initialised by PCA,
 # dynamic adaptation supported), [IT] Sec. 2 (B, A static or adapted online by
 # PCA), [ZH] Sec. 2.2 (B, A statically initialised, e.g. by PCA).  The pages
-# give no algorithm.  Readings (listed in the design doc):
+# give no algorithm.  Readings:
 #   * the principal subspace is that of the output rows: B (d' x r) is an
 #     orthonormal basis of the top-r left singular subspace of M, and
 #     A = B^T W, so B A = B B^T W is the rank-r PCA projection of W;
