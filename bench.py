@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time only the one-token decode from stored codes")
+    ap.add_argument("--only-segmented", action="store_true",
+                    help="time only the continuous-batching call")
     ap.add_argument("--only-pca", action="store_true",
                     help="time only the PCA low-rank factorisation "
                          "(4096 x 4096, r = 64) and print its JSON")
@@ -321,6 +325,55 @@ def measure_decode(torch, ttq, steps: int = 1000):
             "hbm_frac_kernel": alg / (k * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def measure_segmented(torch, ttq, reps: int = 50):
+    """Continuous batching on the same 4096 x 4096 weights (4-bit g128,
+    r = 32): 22 requests of mixed lengths (16 single tokens, 4 of 3..16,
+    one of 100, one of 200; 354 tokens) in one packed X, each with its own
+    statistics -- one ttq_linear_segmented call against one ttq_linear call
+    per request."""
+    import numpy as np
+    from workloads import configs as wc
+    d = d_out = 4096
+    prob = wc.make_problem("seg", d=d, d_out=d_out, T=1, bits=4, group=128,
+                           rank=32, seed=11)
+    lengths = [1] * 16 + [3, 7, 12, 16, 100, 200]
+    rng = np.random.default_rng(12)
+    lengths = [int(x) for x in rng.permutation(lengths)]
+    xs = [wc.draw_x(500 + i, 0, 1, t, d, "logu10_100", 41)[0]
+          for i, t in enumerate(lengths)]
+    offs = [0] + [int(x) for x in np.cumsum(lengths)]
+    W = dev_bf16(prob.W, torch)
+    Bm, A = dev_bf16(prob.B, torch), dev_bf16(prob.A, torch)
+    X = dev_bf16(np.concatenate(xs), torch)
+    Xr = [dev_bf16(x, torch) for x in xs]
+    kw = dict(p=prob.p, lam=prob.lam, alpha=prob.alpha, bits=4, group=128)
+    Y = torch.empty(offs[-1], d_out, dtype=torch.float32, device="cuda")
+
+    def seg():
+        ttq.ttq_linear_segmented(W, X, Bm, A, seg_offsets=offs, Y=Y, **kw)
+
+    def single():
+        for i, x in enumerate(Xr):
+            ttq.ttq_linear(W, x, Bm, A, Y=Y[offs[i]:offs[i + 1]], **kw)
+
+    out = {"workload": f"4096x4096 4-bit g128 r=32, {len(lengths)} requests, "
+                       f"{offs[-1]} tokens (16 x 1, 3, 7, 12, 16, 100, 200)"}
+    for name, f in (("segmented", seg), ("one_call_per_request", single)):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": ms, "tokens_per_s": offs[-1] / (ms * 1e-3)}
+    return out
+
+
 def cpu_baseline(T: int, seconds: float, qformat: str = "asym"):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import numpy as np
@@ -473,6 +526,16 @@ def main():
         print(json.dumps({"lowrank_pca": measure_pca(torch, ttq, reps=a.steps)}),
               flush=True)
         return
+    if a.only_decode:
+        r = measure_decode(torch, ttq, a.steps)
+        if a.copy_calib_mb:
+            copy_calibration(a.copy_calib_mb, torch)
+        print(json.dumps({"decode_from_codes": r}), flush=True)
+        return
+    if a.only_segmented:
+        print(json.dumps({"continuous_batching": measure_segmented(torch, ttq, a.steps)}),
+              flush=True)
+        return
     main_m = measure(a.T, a.steps, a.warmup, torch, ttq,
                      want_graph=not a.only_ttq, want_gemm=not a.only_ttq,
                      qformat=a.qformat)
@@ -576,6 +639,7 @@ def main():
         line["other_formats"] = fmts
     if not a.only_ttq:
         line["decode_from_codes"] = measure_decode(torch, ttq)
+        line["continuous_batching"] = measure_segmented(torch, ttq)
         line["lowrank_pca"] = measure_pca(torch, ttq)
     if not a.no_cpu and not a.only_ttq:
         line["cpu_baseline"] = cpu_baseline(T, a.cpu_seconds, a.qformat)
