@@ -59,7 +59,7 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 
 // ---------------------------------------------------------------------------
 // Small T (T <= 128, fused path and statistics-only calls): a workgroup of
-// 1024 threads owns BC channels (128, or 256 for groups of 256: always whole
+// NT = 512 threads owns BC channels (128, or 256 for groups of 256: always whole
 // quantization groups) and every token for the statistics, and writes x' for
 // one 32-token slice (the slices' workgroups repeat the statistics: X is
 // small, and the chip has more CUs than there are channel blocks).  Thread
@@ -78,13 +78,19 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 // zero-padded to whole 16-token blocks.  The group sums are of exactly the
 // values written, zero past T up to the padded token count.
 // ---------------------------------------------------------------------------
-template <int PM, int BC>
-__global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
+// (512 threads: measured on MI355X, one or two 16-token steps take about
+// 1 us less than with 1024, whose extra token lanes sit idle for small T and
+// add a deeper cross-wave reduction)
+constexpr int kStatsThreads = 512;
+
+template <int PM, int BC, int NT>
+__global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
   constexpr int NCH = BC / 8;          // channel chunks
-  constexpr int TLN = 1024 / NCH;      // token lanes
+  constexpr int TLN = NT / NCH;        // token lanes
   constexpr int TPW = 64 / NCH;        // token lanes per wave
   constexpr int NTK = 128 / TLN;       // tokens per thread (T <= 128)
-  __shared__ double red[16][BC];
+  constexpr int NWV = NT / 64;         // waves
+  __shared__ double red[NWV][BC];
   __shared__ float dhi_l[BC];
   const int tid = threadIdx.x;
   const int cq = tid % NCH, tl = tid / NCH;
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(1024) void k_stats_small(StatsSmallArgs a) {
       const int64_t c = (int64_t)blockIdx.x * BC + tid;
       double S = 0.0;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) S += red[k][tid];
+      for (int k = 0; k < NWV; ++k) S += red[k][tid];
       float dh = 1.f, dhi = 1.f;
       if (c < a.d) {
         diag_half(finish_norm(S, PM, a.p), a.lam, a.alpha, dh, dhi);
@@ -197,17 +203,17 @@ hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
   // x' of 32-token slices in separate workgroups (each takes the statistics
   // of all tokens itself; one of them publishes D^{+-1/2})
   const unsigned nsl = a.xs ? (unsigned)((a.Tp + 31) / 32) : 1u;
-  const dim3 blk(1024);
+  const dim3 blk(kStatsThreads);
   if (a.group == 256) {
     const dim3 grid((unsigned)((a.d + 255) / 256), nsl, (unsigned)R);
-    if (a.pmode == 2) return ext_launch(k_stats_small<2, 256>, grid, blk, 0, L, a);
-    if (a.pmode == 1) return ext_launch(k_stats_small<1, 256>, grid, blk, 0, L, a);
-    return ext_launch(k_stats_small<0, 256>, grid, blk, 0, L, a);
+    if (a.pmode == 2) return ext_launch(k_stats_small<2, 256, kStatsThreads>, grid, blk, 0, L, a);
+    if (a.pmode == 1) return ext_launch(k_stats_small<1, 256, kStatsThreads>, grid, blk, 0, L, a);
+    return ext_launch(k_stats_small<0, 256, kStatsThreads>, grid, blk, 0, L, a);
   }
   const dim3 grid((unsigned)((a.d + 127) / 128), nsl, (unsigned)R);
-  if (a.pmode == 2) return ext_launch(k_stats_small<2, 128>, grid, blk, 0, L, a);
-  if (a.pmode == 1) return ext_launch(k_stats_small<1, 128>, grid, blk, 0, L, a);
-  return ext_launch(k_stats_small<0, 128>, grid, blk, 0, L, a);
+  if (a.pmode == 2) return ext_launch(k_stats_small<2, 128, kStatsThreads>, grid, blk, 0, L, a);
+  if (a.pmode == 1) return ext_launch(k_stats_small<1, 128, kStatsThreads>, grid, blk, 0, L, a);
+  return ext_launch(k_stats_small<0, 128, kStatsThreads>, grid, blk, 0, L, a);
 }
 
 // ---------------------------------------------------------------------------
