@@ -244,7 +244,9 @@ int ttq_quantize(const ttq_params* prm, const void* W, const void* X,
 
 /* Y [T][d_out] float32 for the step activations X ([T][d] bf16, T =
  * prm->T) from the stored codes, scales, mins and dhalf_inv of ttq_quantize
- * (same d, d_out, bits, group).  B, A as in ttq_linear (rank = prm->rank).
+ * (same d, d_out, bits, group and qformat: TTQ_QF_FP8 codes decode as E4M3
+ * values, every other format as integers with the stored offsets, u_hat =
+ * mins + scales * code).  B, A as in ttq_linear (rank = prm->rank).
  * codes 16-byte aligned, dhalf_inv 16-byte aligned, the rest as in
  * ttq_linear.  p, lambda, alpha and TTQ_FLAG_FORCE_FUSED are not used;
  * Routes: T = 1, a single kernel over the codes (unless x D^{-1/2} of the
