@@ -60,11 +60,11 @@ def test_linear_formats(fmt, bits, T, flags):
 
 @pytest.mark.parametrize("fmt,bits", [("sym", 4), ("fp8", 8)])
 def test_formats_batched_and_group_sizes(fmt, bits):
-    for group in (32, 64, 256):
-        prob = make_problem(f"{fmt}_g{group}", d=768, d_out=150, T=5, R=3,
+    for group, T in ((32, 5), (64, 5), (256, 5), (128, 1), (64, 1)):
+        prob = make_problem(f"{fmt}_g{group}", d=768, d_out=150, T=T, R=3,
                             bits=bits, group=group, rank=16, seed=70 + group,
                             x_kind="logu10_100", n_outliers=6, qformat=fmt)
-        print(f"[case] {fmt} batched g={group}", flush=True)
+        print(f"[case] {fmt} batched g={group} T={T}", flush=True)
         for flags in (0, TWO):
             rep = check_problem(prob, run_gpu(prob, flags=flags))
             _say(f"{fmt}_g{group}_R3_f{flags}", rep)
@@ -149,7 +149,8 @@ def _check_y(Y, ref, rep, key):
 
 @pytest.mark.parametrize("fmt,bits,group", [("sym", 4, 128), ("intzp", 2, 64),
                                             ("fp8", 8, 128), ("fp8", 8, 32),
-                                            ("sym", 8, 256)])
+                                            ("sym", 8, 256), ("fp8", 8, 256),
+                                            ("intzp", 4, 32)])
 def test_quantize_then_decode_formats(fmt, bits, group):
     prob = make_problem(f"q_{fmt}", d=1024, d_out=300, T=40, bits=bits,
                         group=group, rank=32, x_kind="logu10_100",
