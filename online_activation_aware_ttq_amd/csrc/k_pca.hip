@@ -272,21 +272,24 @@ __global__ __launch_bounds__(64) void k_trsm(float* Y, const float* R, int64_t m
 }
 
 // W_res[i][j] = bf16(W[i][j] - sum_c B[i][c] A[c][j]), a tile of 64 rows
-// (32 for r = 128) x 64 columns per workgroup, float32 sums in c order
+// (32 for r = 128) x 64 columns per workgroup, float32 sums in c order.  A
+// lane owns RT/16 rows x 4 columns; B is staged transposed so that a lane's
+// rows and columns are each one contiguous LDS read per c.
 template <int N>
 constexpr int lr_rows() { return N >= 128 ? 32 : 64; }  // 64 KiB of static LDS
 
 template <int N>
 __global__ __launch_bounds__(256) void k_lr_residual(LrResidualArgs a) {
   constexpr int RT = lr_rows<N>();
-  __shared__ float sB[RT][N + 1];    // [row][c]
-  __shared__ float sA[N][SK_T + 1];  // [c][col]
+  constexpr int RPT = RT / 16;  // rows per lane
+  __shared__ __attribute__((aligned(16))) float sBt[N][RT];    // [c][row]
+  __shared__ __attribute__((aligned(16))) float sA[N][SK_T];   // [c][col]
   const int t = threadIdx.x;
   const int64_t i0 = (int64_t)blockIdx.y * RT, j0 = (int64_t)blockIdx.x * SK_T;
   for (int e = t; e < RT * N; e += 256) {
     const int rr = e / N, c = e % N;
     const int64_t i = i0 + rr;
-    sB[rr][c] = i < a.d_out ? bf16lo(a.B[i * N + c]) : 0.f;
+    sBt[c][rr] = i < a.d_out ? bf16lo(a.B[i * N + c]) : 0.f;
   }
   for (int e = t; e < N * SK_T; e += 256) {
     const int c = e / SK_T, jj = e % SK_T;
@@ -294,17 +297,38 @@ __global__ __launch_bounds__(256) void k_lr_residual(LrResidualArgs a) {
     sA[c][jj] = j < a.d ? bf16lo(a.A[(int64_t)c * a.d + j]) : 0.f;
   }
   __syncthreads();
-  const int jj = t & 63, rq = t >> 6;  // column, quarter of the rows
-  const int64_t j = j0 + jj;
-  if (j >= a.d) return;
-  for (int rr = rq * (RT / 4); rr < (rq + 1) * (RT / 4); ++rr) {
-    const int64_t i = i0 + rr;
+  const int rq = t / 16, cq = t % 16;
+  float acc[RPT][4];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < N; ++c) {
+    float bv[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) bv[r] = sBt[c][rq * RPT + r];
+    const f32x4 av = *(const f32x4*)&sA[c][cq * 4];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      acc[r][0] = fmaf(bv[r], av.x, acc[r][0]);
+      acc[r][1] = fmaf(bv[r], av.y, acc[r][1]);
+      acc[r][2] = fmaf(bv[r], av.z, acc[r][2]);
+      acc[r][3] = fmaf(bv[r], av.w, acc[r][3]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int64_t i = i0 + rq * RPT + r;
     if (i >= a.d_out) break;
-    float s = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < N; ++c) s = fmaf(sB[rr][c], sA[c][jj], s);
-    const float w = bf16lo(a.W[i * a.d + j]);
-    a.Wres[i * a.d + j] = (bf16_t)f2bf(w - s);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t j = j0 + cq * 4 + q;
+      if (j < a.d) {
+        const float w = bf16lo(a.W[i * a.d + j]);
+        a.Wres[i * a.d + j] = (bf16_t)f2bf(w - acc[r][q]);
+      }
+    }
   }
 }
 
