@@ -173,15 +173,28 @@ __global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
 // (readlane), every lane writes its L[i][k] to LDS and reads the column back
 // as broadcasts, and updates its own row:
 //   L[i][k] = g_i[k] / sqrt(p_k),  g_i[j] -= L[i][k] L[j][k]  (j > k)
-// Then every lane writes its row of L to LDS and lane j solves column j of
-// L^{-1} down the rows (row i of L read as broadcasts):
-//   z_i = (delta_ij - sum_{m<i} L[i][m] z_m) / L[i][i]
-// and writes row j of R^{-1} = (L^{-1})^T: Rinv[j][i] = z_i.
+// with 1/sqrt(p_k) from a Newton-refined estimate.
+// Then every lane writes its row of L to LDS as a column of L^T, and lane j
+// solves column j of L^{-1} in column order (column i of L read as
+// broadcasts), starting from z = e_j:
+//   z_i *= 1 / L[i][i],  z_m -= L[m][i] z_i  (m > i)
+// so the updates of one step are independent of each other, and writes row
+// j of R^{-1} = (L^{-1})^T: Rinv[j][i] = z_i.
 __device__ __forceinline__ double bcast(double v, int lane) {
   const unsigned long long b = __double_as_longlong(v);
   const unsigned lo = __builtin_amdgcn_readlane((unsigned)b, lane);
   const unsigned hi = __builtin_amdgcn_readlane((unsigned)(b >> 32), lane);
   return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
+
+// 1/sqrt(p) for p > 0: the hardware estimate refined by two Newton steps
+// y <- y (3/2 - (p/2) y^2), each of which roughly doubles the correct bits
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  const double h = 0.5 * p;
+  double y = __builtin_amdgcn_rsq(p);
+  y = y * fma(-h * y, y, 1.5);
+  y = y * fma(-h * y, y, 1.5);
+  return y;
 }
 
 // LDS writes of this wave visible to its later LDS reads
@@ -193,8 +206,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int N>
 __global__ __launch_bounds__(64) void k_cholinv_wave(const float* G, float* Rinv) {
-  __shared__ double col[64];
-  __shared__ double Ls[N][N + 1];
+  __shared__ double col[2][64];    // step k broadcasts through col[k & 1]
+  __shared__ double Lt[N][N + 2];  // Lt[i][m] = L[m][i]
+  __shared__ double dinv[N];
   const int l = threadIdx.x;
   const bool live = l < N;
   double g[N];
@@ -209,27 +223,30 @@ __global__ __launch_bounds__(64) void k_cholinv_wave(const float* G, float* Rinv
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const double pk = fmax(bcast(g[k], k), floor);
-    const double rk = sqrt(pk);
-    const double lik = (l == k) ? rk : g[k] / rk;
+    const double ir = rsqrt_f64(pk);
+    const double lik = (l == k) ? pk * ir : g[k] * ir;
     g[k] = lik;  // L[l][k] (meaningful for l >= k)
-    col[l] = lik;
+    col[k & 1][l] = lik;
+    if (l == 0) dinv[k] = ir;
+    // the wait also retires step k - 1's reads of the other buffer before
+    // step k + 1 overwrites it
     wave_lds_sync();
 #pragma unroll
-    for (int j = k + 1; j < N; ++j) g[j] = fma(-lik, col[j], g[j]);
-    wave_lds_sync();
+    for (int j = k + 1; j < N; ++j) g[j] = fma(-lik, col[k & 1][j], g[j]);
   }
   if (live) {
 #pragma unroll
-    for (int m = 0; m < N; ++m) Ls[l][m] = g[m];
+    for (int m = 0; m < N; ++m) Lt[m][l] = g[m];
   }
   wave_lds_sync();
   double z[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    double acc = (i == l) ? 1.0 : 0.0;
+  for (int i = 0; i < N; ++i) z[i] = (i == l) ? 1.0 : 0.0;
 #pragma unroll
-    for (int m = 0; m < i; ++m) acc = fma(-Ls[i][m], z[m], acc);
-    z[i] = acc / Ls[i][i];
+  for (int i = 0; i < N; ++i) {
+    z[i] *= dinv[i];
+#pragma unroll
+    for (int m = i + 1; m < N; ++m) z[m] = fma(-Lt[i][m], z[i], z[m]);
   }
   if (live) {
 #pragma unroll
