@@ -154,10 +154,28 @@ __global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
     const double pk = fmax(L[k * ld + k], floor);
     if (t == 0) piv[k] = pk;
     const double inv = 1.0 / pk;
+    // row k does not change in step k: this lane's entries of it go to
+    // registers, and each row's reads are issued before its writes (n - k - 1
+    // <= 127 columns: 8 per lane cover them)
+    double uk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = k + 1 + tx + 16 * q;
+      uk[q] = j < n ? L[k * ld + j] : 0.0;
+    }
     for (int i = k + 1 + ty; i < n; i += 16) {
       const double lki = L[k * ld + i] * inv;
-      for (int j = k + 1 + tx; j < n; j += 16)
-        if (j >= i) L[i * ld + j] -= lki * L[k * ld + j];
+      double v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = k + 1 + tx + 16 * q;
+        v[q] = (j < n && j >= i) ? L[i * ld + j] : 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = k + 1 + tx + 16 * q;
+        if (j < n && j >= i) L[i * ld + j] = v[q] - lki * uk[q];
+      }
     }
     __syncthreads();
   }
