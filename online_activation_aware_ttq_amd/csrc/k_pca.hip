@@ -54,7 +54,15 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
   const int64_t k0 = (int64_t)blockIdx.y * a.kc;
   const int64_t k1 = min(a.K, k0 + a.kc);
   const TA* A = static_cast<const TA*>(a.A);
+  // N >= 16: float32 matrix instructions, wave w owning rows 16w..16w+15 of
+  // the tile and all N / 16 column blocks; N = 8: VALU FMAs, RW x CW per lane
+  constexpr bool MF = N >= 16;
+  constexpr int NCB = MF ? N / 16 : 1;
+  const int lane = t & 63, wv = t >> 6;
+  f32x4 macc[NCB];
   float acc[RW][CW];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) macc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RW; ++i)
 #pragma unroll
@@ -63,6 +71,42 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
     // stage the A tile as [k][row]; element (row, k) is A[row][k] (C = A Bm)
     // or A[k][row] (C = A^T Bm); the index along the memory row is the one
     // the column scale applies to
+    // a full tile with 16-byte aligned lines is read in 16-byte vectors along
+    // the memory row; any other tile element by element
+    const bool vec_a = kt + SK_T <= k1 && r0 + SK_T <= a.rows &&
+                       a.lda % (int64_t)(16 / sizeof(TA)) == 0 &&
+                       (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+    if (vec_a) {
+      constexpr int VE = 16 / sizeof(TA), VPL = SK_T / VE;
+#pragma unroll
+      for (int p = 0; p < SK_T * VPL / 256; ++p) {
+        const int vi = t + 256 * p;
+        const int ln = vi / VPL, o = (vi % VPL) * VE;  // line, offset along it
+        const int64_t off = TN ? (kt + ln) * a.lda + r0 + o : (r0 + ln) * a.lda + kt + o;
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(A + off);
+        float v[VE];
+        if constexpr (sizeof(TA) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(raw[e] << 16);
+            v[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(raw[e]);
+        }
+        if (a.scale) {
+          const int64_t c0 = TN ? r0 + o : kt + o;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) v[e] = v[e] * a.scale[c0 + e];
+        }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          if (TN) tA[ln][o + e] = v[e];
+          else tA[o + e][ln] = v[e];
+        }
+      }
+    } else
     for (int e = t; e < SK_T * SK_T; e += 256) {
       int kk, rr;
       if (TN) { rr = e & 63; kk = e >> 6; }
@@ -80,12 +124,34 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
       }
       tA[kk][rr] = v;
     }
+    if (kt + SK_T <= k1 && a.ldb % 4 == 0 && (reinterpret_cast<uintptr_t>(a.Bm) & 15) == 0) {
+      for (int vi = t; vi < SK_T * N / 4; vi += 256) {
+        const int kk = vi / (N / 4), c0 = (vi % (N / 4)) * 4;
+        *reinterpret_cast<f32x4*>(&tB[kk][c0]) =
+            *reinterpret_cast<const f32x4*>(a.Bm + (kt + kk) * a.ldb + c0);
+      }
+    } else
     for (int e = t; e < SK_T * N; e += 256) {
       const int kk = e / N, c = e % N;
       const int64_t k = kt + kk;
       tB[kk][c] = k < k1 ? a.Bm[k * a.ldb + c] : 0.f;
     }
     __syncthreads();
+    if constexpr (MF) {
+      // 16x16x4 operands: lane (i, q) = (lane % 16, lane / 16) supplies
+      // A[row i][k q] and Bm[k q][column i]
+      const int i = lane & 15, q = lane >> 4;
+#pragma unroll 4
+      for (int k4 = 0; k4 < SK_T; k4 += 4) {
+        const float af = tA[k4 + q][wv * 16 + i];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+          macc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(af, tB[k4 + q][c * 16 + i],
+                                                         macc[c], 0, 0, 0);
+      }
+      __syncthreads();
+      continue;
+    }
 #pragma unroll 2
     for (int kk = 0; kk < SK_T; ++kk) {
       float av[RW], bv[CW];
@@ -99,6 +165,19 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyArgs a) {
         for (int c = 0; c < CW; ++c) acc[i][c] = fmaf(av[i], bv[c], acc[i][c]);
     }
     __syncthreads();
+  }
+  if constexpr (MF) {
+    // result element (4 (lane / 16) + v, lane % 16) of each 16 x 16 block
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = r0 + wv * 16 + 4 * (lane >> 4) + v;
+      if (row < a.rows) {
+        float* out = a.part + ((int64_t)blockIdx.y * a.rows + row) * N + (lane & 15);
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) out[c * 16] = macc[c][v];
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
