@@ -206,7 +206,7 @@ def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
     return out
 
 
-FP32_PEAK_TFLOPS = 157.3
+FP32_PEAK_TFLOPS = 157.3  # float32 peak, the vector units and the matrix instruction alike
 
 
 def measure_pca(torch, ttq, reps: int = 10):

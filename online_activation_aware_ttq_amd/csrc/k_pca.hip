@@ -18,9 +18,9 @@
 //                   columns may be scaled by D^{1/2} as they are staged
 //   k_psum          ordered sum of the partials -> float32, and optionally
 //                   bf16 (as is, or transposed)
-//   k_cholinv_wave  r <= 64: R^{-1} of the Gram matrix's Cholesky factor in
-//                   one wave (float64 registers); Q = Y R^{-1} is then one
-//                   more skinny product
+//   k_cholinv       r <= 64: R^{-1} of the Gram matrix's Cholesky factor in
+//                   one workgroup (float64 registers); Q = Y R^{-1} is then
+//                   one more skinny product
 //   k_chol, k_trsm  r = 128: Cholesky in one workgroup (float64 in LDS) and
 //                   Q = Y R^{-1} by forward substitution, one row per lane
 //   k_lr_residual   W_res = bf16(W - B A) from the bf16 factors
@@ -265,18 +265,21 @@ __global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
   }
 }
 
-// n <= 64: Cholesky and inverse in one wave, the rows in float64 registers.
-// Lane i holds row i of G.  Step k (unrolled): the pivot comes from lane k
-// (readlane), every lane writes its L[i][k] to LDS and reads the column back
-// as broadcasts, and updates its own row:
+// n <= 64: Cholesky and inverse in one workgroup of four waves, the rows in
+// float64 registers.  Lane i of wave w holds the entries j = w (mod 4) of row
+// i of G.  Step k (unrolled): in the wave holding column k the pivot comes
+// from lane k (readlane) and every lane writes its L[i][k] to LDS; after one
+// barrier every lane reads the column back as broadcasts and updates its
+// entries of its row:
 //   L[i][k] = g_i[k] / sqrt(p_k),  g_i[j] -= L[i][k] L[j][k]  (j > k)
 // with 1/sqrt(p_k) from a Newton-refined estimate.
-// Then every lane writes its row of L to LDS as a column of L^T, and lane j
-// solves column j of L^{-1} in column order (column i of L read as
-// broadcasts), starting from z = e_j:
+// Then every lane writes its entries of L to LDS as columns of L^T, and lane
+// j of the first wave solves column j of L^{-1} in column order (column i of
+// L read as broadcasts), starting from z = e_j:
 //   z_i *= 1 / L[i][i],  z_m -= L[m][i] z_i  (m > i)
 // so the updates of one step are independent of each other, and writes row
-// j of R^{-1} = (L^{-1})^T: Rinv[j][i] = z_i.
+// j of R^{-1} = (L^{-1})^T: Rinv[j][i] = z_i.  (Splitting this solve over
+// the four waves as well, with one barrier per step, measured no faster.)
 __device__ __forceinline__ double bcast(double v, int lane) {
   const unsigned long long b = __double_as_longlong(v);
   const unsigned lo = __builtin_amdgcn_readlane((unsigned)b, lane);
@@ -294,24 +297,20 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
-// LDS writes of this wave visible to its later LDS reads
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int N>
-__global__ __launch_bounds__(64) void k_cholinv_wave(const float* G, float* Rinv) {
+__global__ __launch_bounds__(256) void k_cholinv(const float* G, float* Rinv) {
+  constexpr int NQ = N / 4;
   __shared__ double col[2][64];    // step k broadcasts through col[k & 1]
   __shared__ double Lt[N][N + 2];  // Lt[i][m] = L[m][i]
   __shared__ double dinv[N];
-  const int l = threadIdx.x;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const bool live = l < N;
-  double g[N];
+  double g[NQ];  // g[q] = G[l][w + 4 q], then L[l][w + 4 q]
 #pragma unroll
-  for (int j = 0; j < N; ++j)
-    g[j] = live ? 0.5 * ((double)G[l * N + j] + (double)G[j * N + l]) : 0.0;
+  for (int q = 0; q < NQ; ++q) {
+    const int j = w + 4 * q;
+    g[q] = live ? 0.5 * ((double)G[l * N + j] + (double)G[j * N + l]) : 0.0;
+  }
   // pivot floor: 1e-14 of the largest diagonal entry
   double dmax = live ? (double)G[l * N + l] : 0.0;
 #pragma unroll
@@ -319,23 +318,28 @@ __global__ __launch_bounds__(64) void k_cholinv_wave(const float* G, float* Rinv
   const double floor = 1e-14 * (dmax > 0.0 ? dmax : 1.0);
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    const double pk = fmax(bcast(g[k], k), floor);
-    const double ir = rsqrt_f64(pk);
-    const double lik = (l == k) ? pk * ir : g[k] * ir;
-    g[k] = lik;  // L[l][k] (meaningful for l >= k)
-    col[k & 1][l] = lik;
-    if (l == 0) dinv[k] = ir;
-    // the wait also retires step k - 1's reads of the other buffer before
-    // step k + 1 overwrites it
-    wave_lds_sync();
+    if (w == (k & 3)) {  // the wave holding column k
+      const double pk = fmax(bcast(g[k >> 2], k), floor);
+      const double ir = rsqrt_f64(pk);
+      const double lik = (l == k) ? pk * ir : g[k >> 2] * ir;
+      g[k >> 2] = lik;  // L[l][k] (meaningful for l >= k)
+      col[k & 1][l] = lik;
+      if (l == 0) dinv[k] = ir;
+    }
+    // the barrier also retires step k - 1's reads of the other buffer
+    // before step k + 1 overwrites it
+    __syncthreads();
+    const double lik = col[k & 1][l];
 #pragma unroll
-    for (int j = k + 1; j < N; ++j) g[j] = fma(-lik, col[k & 1][j], g[j]);
+    for (int q = 0; q < NQ; ++q)
+      if (w + 4 * q > k) g[q] = fma(-lik, col[k & 1][w + 4 * q], g[q]);
   }
   if (live) {
 #pragma unroll
-    for (int m = 0; m < N; ++m) Lt[m][l] = g[m];
+    for (int q = 0; q < NQ; ++q) Lt[w + 4 * q][l] = g[q];
   }
-  wave_lds_sync();
+  __syncthreads();
+  if (w != 0) return;
   double z[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) z[i] = (i == l) ? 1.0 : 0.0;
@@ -507,12 +511,12 @@ hipError_t launch_chol(const float* G, float* R, int n, const Launch& L) {
   return ext_launch(k_chol, dim3(1), dim3(256), lds, L, G, R, n);
 }
 
-hipError_t launch_cholinv_wave(const float* G, float* Rinv, int n, const Launch& L) {
+hipError_t launch_cholinv(const float* G, float* Rinv, int n, const Launch& L) {
   switch (n) {
-    case 8: return ext_launch(k_cholinv_wave<8>, dim3(1), dim3(64), 0, L, G, Rinv);
-    case 16: return ext_launch(k_cholinv_wave<16>, dim3(1), dim3(64), 0, L, G, Rinv);
-    case 32: return ext_launch(k_cholinv_wave<32>, dim3(1), dim3(64), 0, L, G, Rinv);
-    case 64: return ext_launch(k_cholinv_wave<64>, dim3(1), dim3(64), 0, L, G, Rinv);
+    case 8: return ext_launch(k_cholinv<8>, dim3(1), dim3(256), 0, L, G, Rinv);
+    case 16: return ext_launch(k_cholinv<16>, dim3(1), dim3(256), 0, L, G, Rinv);
+    case 32: return ext_launch(k_cholinv<32>, dim3(1), dim3(256), 0, L, G, Rinv);
+    case 64: return ext_launch(k_cholinv<64>, dim3(1), dim3(256), 0, L, G, Rinv);
     default: return hipErrorInvalidValue;
   }
 }

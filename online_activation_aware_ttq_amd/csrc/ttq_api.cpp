@@ -1006,7 +1006,7 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
       int r = product(true, false, V, n, nullptr, n, m, V, sp_gram, G, nullptr, nullptr);
       if (r != TTQ_OK) return r;
       if (n <= 64) {  // R^{-1} in one wave, then V R^{-1} as a product
-        r = run(K_CHOL, s, [&](const Launch& L) { return launch_cholinv_wave(G, Rf, (int)n, L); });
+        r = run(K_CHOL, s, [&](const Launch& L) { return launch_cholinv(G, Rf, (int)n, L); });
         if (r != TTQ_OK) return r;
         r = product(false, false, V, n, nullptr, m, n, Rf, 1, V, nullptr, nullptr);
       } else {

@@ -546,7 +546,7 @@ hipError_t launch_psum(const PsumArgs& a, const Launch& L);
 hipError_t launch_chol(const float* G, float* R, int n, const Launch& L);
 hipError_t launch_trsm(float* Y, const float* R, int64_t m, int n, const Launch& L);
 // n <= 64: R^{-1} of the Cholesky factor in one wave (float64 registers)
-hipError_t launch_cholinv_wave(const float* G, float* Rinv, int n, const Launch& L);
+hipError_t launch_cholinv(const float* G, float* Rinv, int n, const Launch& L);
 struct LrResidualArgs {
   const bf16_t* W;        // [d_out][d]
   const bf16_t* B;        // [d_out][n]
