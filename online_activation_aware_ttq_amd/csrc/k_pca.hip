@@ -435,10 +435,25 @@ __global__ __launch_bounds__(256) void k_lr_residual(LrResidualArgs a) {
       acc[r][3] = fmaf(bv[r], av.w, acc[r][3]);
     }
   }
+  // a lane's 4 columns as one 8-byte load of W and store of W_res where the
+  // row is aligned for it, element by element otherwise
+  const int64_t jv = j0 + cq * 4;
+  const bool vec = jv + 4 <= a.d && (a.d & 3) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.W) | reinterpret_cast<uintptr_t>(a.Wres)) & 7) == 0;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int64_t i = i0 + rq * RPT + r;
     if (i >= a.d_out) break;
+    if (vec) {
+      const u32x2 wv = *reinterpret_cast<const u32x2*>(a.W + i * a.d + jv);
+      const float w0 = __uint_as_float(wv.x << 16), w1 = __uint_as_float(wv.x & 0xffff0000u);
+      const float w2 = __uint_as_float(wv.y << 16), w3 = __uint_as_float(wv.y & 0xffff0000u);
+      u32x2 o;
+      o.x = (f2bf(w0 - acc[r][0]) & 0xffffu) | (f2bf(w1 - acc[r][1]) << 16);
+      o.y = (f2bf(w2 - acc[r][2]) & 0xffffu) | (f2bf(w3 - acc[r][3]) << 16);
+      *reinterpret_cast<u32x2*>(a.Wres + i * a.d + jv) = o;
+      continue;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t j = j0 + cq * 4 + q;
