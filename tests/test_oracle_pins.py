@@ -357,3 +357,56 @@ def test_band_rule_classification():
     q_gpu = np.array([[2, 3, 1]])
     nb, ne, nl = oracle.band_excused(q_gpu, q_ref, t, u, m, s, 3)
     assert (nb, ne, nl) == (2, 1, 1)
+
+
+# ------------------------------------------------ float64 pre-rounding value
+def test_pre_rounding_fp64_matches_e1_golden_t(golden_dir):
+    g = _load(golden_dir, "e1_rtn_tie.json")
+    t, u, m, s = oracle.pre_rounding_fp64(np.array([g["w"]]), np.ones(4),
+                                          g["bits"], g["group"])
+    np.testing.assert_array_equal(t[0], g["t"])
+    np.testing.assert_array_equal(u[0], g["w"])
+    assert m[0, 0] == g["min"] and s[0, 0] == g["scale"]
+
+
+def test_pre_rounding_fp64_matches_e2_handworked_t(golden_dir):
+    g = _load(golden_dir, "e2_ttq_handworked.json")
+    Xtok = np.array(g["X_channel_major"]).T
+    r = _run(np.array(g["W"]), Xtok, bits=g["bits"], group=g["group"],
+             p=g["p"], lam=g["lambda"], alpha=g["alpha"], want_t=True)
+    np.testing.assert_allclose(r["t64"], g["t"], rtol=1e-15, atol=1e-15)
+    np.testing.assert_array_equal(r["u64"], g["u"])
+    np.testing.assert_array_equal(r["m64"][:, 0], g["min"])
+    np.testing.assert_array_equal(r["m64"][:, 0] + r["s64"][:, 0] * 3, g["max"])
+
+
+def test_pre_rounding_fp64_uses_float64_statistics_closed_form():
+    # p = 1, lambda = 0, alpha = 1: channel norms [1, 2, 1, 1] give
+    # D^{1/2} = [1, sqrt 2, 1, 1], which float32 cannot hold.  Row [1, 1, 0, 0]
+    # has u = [1, sqrt 2, 0, 0], s = sqrt(2)/3, t = [3/sqrt 2, 3, 0, 0]; row
+    # [0.5, -1, 1, 0] has u = [0.5, -sqrt 2, 1, 0], s = (1 + sqrt 2)/3,
+    # t = [4.5 - 1.5 sqrt 2, 0, 3, 6 - 3 sqrt 2].  A t taken from the float32
+    # D^{1/2} or a float32 scale is off by about 1e-8 relative.
+    Xtok = np.array([[1.0, 1.0, 0.0, 1.0], [0.0, 1.0, 1.0, 0.0]])
+    W = np.array([[1.0, 1.0, 0.0, 0.0], [0.5, -1.0, 1.0, 0.0]])
+    r = _run(W, Xtok, bits=2, group=4, p=1.0, lam=0.0, alpha=1.0, want_t=True)
+    r2 = np.sqrt(2.0)
+    exact = np.array([[3 / r2, 3.0, 0.0, 0.0],
+                      [4.5 - 1.5 * r2, 0.0, 3.0, 6 - 3 * r2]])
+    np.testing.assert_allclose(r["t64"], exact, rtol=4e-16, atol=1e-15)
+    assert np.abs(np.float32(r2) - r2) / r2 > 1e-8   # the slip would show
+    np.testing.assert_allclose(r["s64"][:, 0], [r2 / 3, (1 + r2) / 3], rtol=4e-16)
+    # the float32 code decision agrees with rint(t) here (no value near a tie)
+    assert r["q"].tolist() == [[2, 3, 0, 0], [2, 0, 3, 2]]
+
+
+def test_pre_rounding_fp64_agrees_with_fp32_codes_outside_the_band():
+    rng = np.random.default_rng(7)
+    W = _bits(rng.standard_normal((32, 512)) * 0.02)
+    X = _bits(rng.standard_normal((8, 512)))
+    r = oracle.ttq_linear(W, X, bits=4, group=128, p=2.0, lam=1e-3, alpha=0.5,
+                          want_t=True)
+    q_ref = np.clip(np.rint(r["t64"]), 0, 15)
+    nb, ne, _ = oracle.band_excused(r["q"], q_ref, r["t64"], r["u64"],
+                                    r["m64"], r["s64"], 128)
+    assert nb == ne   # every disagreement sits on a rounding boundary
