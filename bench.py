@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Throughput of the TTQ linear projection on one MI355X.
 
-One step = one full TTQ projection call (activation statistics, on-the-fly
-group quantize-dequantize of W D^{1/2}, contraction with X on the matrix
-cores) on the 4096 x 4096 attention-projection workload at decode, T = 1:
-4-bit, group 128, p = 2, lambda = 1e-3, alpha = 0.5, activations with 1 % of
-channels scaled log-uniformly by 10-100x and a new outlier set every call.
+Headline step: one full 7B-class decoder layer of TTQ projections -- q, k, v,
+o (4096 -> 4096), gate, up (4096 -> 11008) and down (11008 -> 4096) -- for
+R = 8 independent requests of T = 4096 tokens each, every request with its
+own activation statistics and its own outlier channels (multitenant), 4-bit
+groups of 128, p = 2, lambda = 1e-3, alpha = 0.5, static low rank r = 32 on
+all seven projections.  One step = the seven batched calls; ``value`` is the
+layer's throughput in tokens/s (R T / step time), inputs resident in HBM.
 
-Inputs are resident in HBM before the timed region; the weight matrix
-rotates over enough distinct copies (> 512 MB) that it is read from HBM, not
-from the 256 MB Infinity Cache, as in a real model where every layer has
-its own weights.  The JSON line also carries: the roofline of the dominant
-kernel (event-timed launches), the oracle timed on the host cores
-(cpu_baseline), a plain bf16 GEMM of the same shape (hipBLASLt via torch) for
-the pages' overhead ratio rho = 1/d' + 3/T, the same step under a HIP graph,
-and the T = 128 case of the same workload.
+The JSON line also carries, as keys of their own: the same layer at T = 1,
+16 and 256; the 70B-class up projection (8192 -> 28672, T = 512, 2-bit g64,
+r = 128) at p = 2 and p = 1; the MLP gate/up and down projections at
+T = 2048 (3-bit, r = 64); the 4096 x 4096 projection at T = 1 and T = 128;
+for each a plain bf16 GEMM of the same shape (torch -> hipBLASLt) and the
+measured overhead ratio against the pages' 1/d' + 3/T.  Then the roofline of
+the dominant kernel (event-timed launches on the library's stream; HBM
+traffic from committed rocprofv3 counter summaries), two measured ceilings
+(a device copy for HBM, a large bf16 GEMM for the matrix cores) and the CPU
+oracle on the host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -33,229 +37,470 @@ METRIC = ("TTQ-linear tokens/s per projection + % HBM/MFMA roofline; "
           "overhead vs bf16 GEMM")
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
 ROTATE_BYTES = 640 * 2 ** 20
 FORMAT_NAMES = {"asym": "asymmetric", "sym": "symmetric",
                 "intzp": "integer zero point", "fp8": "FP8 E4M3"}
+# timing-kind name -> kernel source (for the counter summaries' freshness)
 KERNEL_SOURCES = {"gemv_t1": "k_gemv.hip", "fused_qdq_mfma": "k_fused.hip",
-                  "stats_small": "k_stats.hip", "gemm_mfma": "k_gemm.hip",
-                  "quant_what": "k_quant.hip"}
+                  "stats_small": "k_stats.hip", "gemm_mfma": "k_gemm_lds.hip",
+                  "quant_what": "k_quant.hip", "gemm_quant": "k_gemm_q.hip",
+                  "qgemv": "k_qgemv.hip"}
+# timing-kind name -> substring of the HIP kernel symbol in rocprofv3 output
+KERNEL_SYMBOLS = {"gemv_t1": "k_gemv", "fused_qdq_mfma": "k_fused",
+                  "gemm_mfma": "k_gemm_lds", "quant_what": "k_quant",
+                  "gemm_quant": "k_gemm_q", "qgemv": "k_qgemv",
+                  "stats_small": "k_stats_small"}
+C5_PROJ = (("q_proj", 4096, 4096), ("k_proj", 4096, 4096),
+           ("v_proj", 4096, 4096), ("o_proj", 4096, 4096),
+           ("gate_proj", 4096, 11008), ("up_proj", 4096, 11008),
+           ("down_proj", 11008, 4096))
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--T", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10,
+                    help="timed steps of the headline layer")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--leg", default="all",
+                    choices=("all", "c5", "c4", "c3", "c2", "decode",
+                             "segmented", "pca", "ceilings"),
+                    help="run one workload only (profiler runs); 'all' is "
+                         "the full line")
+    ap.add_argument("--T", type=int, default=0,
+                    help="token count of the c5 / c2 leg (default 4096 / 1)")
+    ap.add_argument("--p", type=float, default=2.0, help="p of the c4 leg")
+    ap.add_argument("--which", default="gate_up", choices=("gate_up", "down"),
+                    help="projection of the c3 leg")
     ap.add_argument("--qformat", default="asym",
                     choices=("asym", "sym", "intzp", "fp8"),
-                    help="quantizer format of the timed step (fp8: 8-bit "
-                         "E4M3 codes; the others 4-bit)")
+                    help="quantizer format of the c2 leg")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only-decode", action="store_true",
-                    help="time only the one-token decode from stored codes")
-    ap.add_argument("--only-segmented", action="store_true",
-                    help="time only the continuous-batching call")
-    ap.add_argument("--only-pca", action="store_true",
-                    help="time only the PCA low-rank factorisation "
-                         "(4096 x 4096, r = 64) and print its JSON")
-    ap.add_argument("--only-ttq", action="store_true",
-                    help="time only the TTQ step (for profiler runs)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after the timed work, run 5 device-to-device copies "
                          "of this many MiB (counter calibration)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
                     help="write profiles/ summaries from rocprofv3 output "
-                         "directories (kernel trace, FETCH_SIZE, WRITE_SIZE)")
+                         "directories (kernel trace, FETCH_SIZE, WRITE_SIZE) "
+                         "for --kernel on the workload named by --leg")
+    ap.add_argument("--kernel", default="",
+                    help="timing-kind name of the summarized kernel")
     ap.add_argument("--profile-cmd", default="",
-                    help="command lines recorded in the summary")
+                    help="command lines recorded in the summary (';;' apart)")
     return ap.parse_args()
 
 
-def kernel_src_sha(kernel: str) -> str:
-    p = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
-                     KERNEL_SOURCES.get(kernel, "k_fused.hip"))
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
-
-
-def fmt_suffix(qformat: str) -> str:
-    return "" if qformat == "asym" else f"_{qformat}"
-
-
-def traffic_file(kernel: str, T: int, qformat: str = "asym") -> str:
-    return os.path.join(ROOT, "profiles",
-                        f"traffic_{kernel}_q_proj4096_T{T}{fmt_suffix(qformat)}.json")
-
-
+# ------------------------------------------------------------------ helpers
 def dev_bf16(bits, torch):
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(
         "cuda").view(torch.bfloat16)
 
 
-def alg_bytes(d, d_out, T, rank=0):
-    return 2 * d_out * d + 2 * T * d + 4 * T * d_out + 2 * rank * (d + d_out)
+def draw_x_gpu(torch, seed: int, R: int, T: int, d: int, kind: str,
+               n_out: int):
+    """Seeded activations [R, T, d] bf16, drawn on the GPU (input generation
+    only), a new outlier channel set per request, rounded to bf16 to nearest
+    even.  kind ``n``: N(0,1) with ``n_out`` channels multiplied
+    log-uniformly by 10-100x; ``x50``: N(0,1) with ``n_out`` channels x50;
+    ``t3``: Student-t(3) with ``n_out`` channels x30-100 log-uniform."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    X = torch.empty(R, T, d, dtype=torch.bfloat16, device="cuda")
+    for r in range(R):
+        if kind == "t3":
+            # Student-t(3) = N / sqrt(chi2_3 / 3)
+            z = torch.randn(T, d, generator=g, device="cuda")
+            c = torch.randn(3, T, d, generator=g, device="cuda").pow_(2).sum(0)
+            x = z / torch.sqrt(c / 3.0)
+            lo = 1.4771212547196624   # log10 30
+        else:
+            x = torch.randn(T, d, generator=g, device="cuda")
+            lo = 1.0
+        ch = torch.randperm(d, generator=g, device="cuda")[:n_out]
+        if kind == "x50":
+            mult = torch.full((n_out,), 50.0, device="cuda")
+        else:
+            mult = torch.pow(10.0, lo + (2.0 - lo) * torch.rand(
+                n_out, generator=g, device="cuda"))
+        x[:, ch] *= mult
+        X[r] = x.to(torch.bfloat16)
+        del x
+    return X
 
 
-def alg_flops(d, d_out, T, rank=0):
-    return 2 * d_out * d * T + 2 * rank * T * (d + d_out)
+def timed_wall(torch, fn, n: int, w: int) -> float:
+    """ms per call: w untimed calls, then n calls bracketed by device
+    synchronisations (host wall clock)."""
+    for i in range(w):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / n
 
 
-def format_bits(qformat: str) -> int:
-    return 8 if qformat == "fp8" else 4
-
-
-def measure(T: int, steps: int, warmup: int, torch, ttq, want_graph: bool,
-            want_gemm: bool, qformat: str = "asym"):
-    import numpy as np
-    from workloads import configs as wc
-
-    d = d_out = 4096
-    prob = wc.make_c2(T=T)
-    prob.bits = format_bits(qformat)
-    w_bytes = 2 * d * d_out
-    n_w = max(2, -(-ROTATE_BYTES // w_bytes))
-    Ws = [dev_bf16(prob.W, torch)]
-    for i in range(1, n_w):  # distinct copies of the same seeded W
-        Ws.append(Ws[0].clone())
-    n_x = 64
-    Xs = [dev_bf16(wc.draw_x(1, 1000 + c, 1, T, d, "logu10_100", 41)[0], torch)
-          for c in range(n_x)]
-    n_y = 8
-    Ys = [torch.empty(T, d_out, dtype=torch.float32, device="cuda")
-          for _ in range(n_y)]
-    kw = dict(p=prob.p, lam=prob.lam, alpha=prob.alpha, bits=prob.bits,
-              group=prob.group, qformat=qformat)
-    prm = ttq.make_params(d=d, d_out=d_out, T=T, bits=prob.bits,
-                          group=prob.group, p=prob.p, lam=prob.lam,
-                          alpha=prob.alpha, qformat=qformat)
-    ws = torch.empty(ttq.ttq_workspace_bytes(prm), dtype=torch.uint8,
-                     device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
-
-    def step(i):
-        ttq.ttq_linear(Ws[i % n_w], Xs[i % n_x], Y=Ys[i % n_y], workspace=ws,
-                       stream=stream, **kw)
-
-    def timed(fn, n, w):
-        for i in range(w):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n  # ms per step
-
-    out = {"T": T, "rotating_w_copies": n_w,
-           "rotating_bytes": n_w * w_bytes}
-    ms = timed(step, steps, warmup)
-    out["ms_per_step"] = ms
-
-    # per-kernel event timing over the same kind of steps
+def kernel_times(torch, ttq, fn, n: int) -> dict:
+    """{timing kind: (avg ms per launch, launches per call)} over n calls, from
+    the events the runtime stamps around each kernel of the library."""
     ttq.timing_reset()
     ttq.timing_enable(True)
-    for i in range(steps):
-        step(i)
+    for i in range(n):
+        fn(i)
     torch.cuda.synchronize()
     kt = ttq.timing_query()
     ttq.timing_enable(False)
     ttq.timing_reset()
-    out["kernels_ms_avg"] = {k: v[0] / v[1] for k, v in kt.items() if v[1]}
-    out["kernels_launches"] = {k: v[1] for k, v in kt.items() if v[1]}
+    return {k: (v[0] / v[1], v[1] / n) for k, v in kt.items() if v[1]}
 
-    # hot-cache figure (same W every call) for context
-    def step_hot(i):
-        ttq.ttq_linear(Ws[0], Xs[i % n_x], Y=Ys[i % n_y], workspace=ws,
+
+def gemm_ms(torch, Ws, Xs, n: int, w: int) -> float:
+    """Plain bf16 GEMM(s) of the same shapes (torch.nn.functional.linear ->
+    hipBLASLt), one per (weight, request) like the TTQ call."""
+    import torch.nn.functional as F
+
+    def f(i):
+        for W, X in zip(Ws, Xs):
+            for r in range(X.shape[0]):
+                F.linear(X[r], W)
+    return timed_wall(torch, f, n, w)
+
+
+def alg(d, d_out, T, R=1, rank=0):
+    """Algorithmic bytes (W once, X, Y fp32, B and A) and matrix flops of
+    one call: R requests of T tokens on one shared W."""
+    by = 2 * d_out * d + R * (2 * T * d + 4 * T * d_out) + 2 * rank * (d + d_out)
+    fl = R * (2 * d_out * d * T + 2 * rank * T * (d + d_out))
+    return by, fl
+
+
+def kernel_units(kind: str, d, d_out, T, R, rank):
+    """Algorithmic (bytes, flops) of one launch of a kernel kind for one
+    call of the shape.  The projection GEMMs do the main contraction and the
+    low-rank segment Z B^T; the quantize pass reads W once and writes one
+    bf16 W_hat per request; the one-pass kernels stream W once."""
+    if kind in ("gemm_mfma", "gemm_quant"):
+        by = R * (2 * T * d + 4 * T * d_out + 2 * T * rank) + 2 * d_out * rank
+        by += 2 * d_out * d * (R if kind == "gemm_mfma" else 1)
+        return by, R * 2 * T * d_out * (d + rank)
+    if kind == "quant_what":
+        return 2 * d_out * d * (1 + R), 0
+    if kind in ("gemv_t1", "fused_qdq_mfma"):
+        by = 2 * d_out * d + R * (2 * T * d + 4 * T * d_out) + 2 * d_out * rank
+        return by, R * 2 * T * d_out * d
+    return 0, 0
+
+
+def roofline(kind: str, ms_per_launch: float, bytes_per_launch: float,
+             flops_per_launch: float, traffic=None) -> dict:
+    t_hbm = bytes_per_launch / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_per_launch / (BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        a = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
+    else:
+        a = flops_per_launch / (ms_per_launch * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": a, "peak": BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": a / BF16_PEAK_TFLOPS}
+    r["traffic"] = traffic
+    r.update(kernel=kind, kernel_ms=ms_per_launch,
+             alg_bytes_per_launch=bytes_per_launch,
+             alg_flops_per_launch=flops_per_launch)
+    return r
+
+
+def kernel_src_sha(kind: str) -> str:
+    p = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
+                     KERNEL_SOURCES.get(kind, "k_fused.hip"))
+    h = hashlib.sha256(open(p, "rb").read())
+    # the shared header changes every kernel
+    h.update(open(os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
+                               "ttq_internal.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kind: str, leg: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kind}_{leg}.json")
+
+
+def traffic_entry(kind: str, leg: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source has changed since it was taken."""
+    try:
+        rec = json.load(open(traffic_file(kind, leg)))
+    except Exception:
+        return None
+    if rec.get("kernel_src_sha") != kernel_src_sha(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------- legs
+def leg_c5(torch, ttq, T: int, steps: int, warmup: int, want_gemm: bool,
+           per_projection: bool = True) -> dict:
+    """The seven projections of a 7B-class layer for R = 8 requests of T
+    tokens each; one step = seven batched calls."""
+    from workloads import configs as wc
+    R, bits, group, rank = 8, 4, 128, 32
+    kw = dict(p=2.0, lam=1e-3, alpha=0.5, bits=bits, group=group)
+    projs = []
+    for i, (name, d, d_out) in enumerate(C5_PROJ):
+        prob = wc.make_c5(T=1, proj=name, R=1)   # W, B, A (seeded per projection)
+        projs.append(dict(
+            name=name, d=d, d_out=d_out,
+            W=dev_bf16(prob.W, torch), B=dev_bf16(prob.B, torch),
+            A=dev_bf16(prob.A, torch),
+            X=draw_x_gpu(torch, 4000 + 7 * T + i, R, T, d, "n",
+                         max(1, round(0.01 * d))),
+            Y=torch.empty(R, T, d_out, dtype=torch.float32, device="cuda")))
+    ws_bytes = max(ttq.ttq_workspace_bytes(
+        ttq.make_params(d=p["d"], d_out=p["d_out"], T=T, rank=rank, bits=bits,
+                        group=group, p=2.0, lam=1e-3, alpha=0.5), R)
+        for p in projs)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call(p):
+        ttq.ttq_linear_batched(p["W"], p["X"], p["B"], p["A"], Y=p["Y"],
+                               workspace=ws, stream=stream, **kw)
+
+    def step(i):
+        for p in projs:
+            call(p)
+
+    reps = steps if T >= 256 else max(steps, 50)
+    ms = timed_wall(torch, step, reps, warmup)
+    kt = kernel_times(torch, ttq, step, max(2, min(reps, 20)))
+    out = {"workload": f"7B-class layer, 7 projections, R={R} requests x "
+                       f"T={T} tokens, 4-bit g128 asymmetric, p=2, "
+                       "lambda=1e-3, alpha=0.5, r=32, own outlier set per "
+                       "request", "T": T, "R": R, "steps": reps,
+           "warmup": warmup, "ms_per_step": ms,
+           "tokens_per_s": R * T / (ms * 1e-3),
+           "kernels": {k: {"ms_per_launch": v[0], "launches_per_step": v[1]}
+                       for k, v in kt.items()},
+           "path": ttq.ttq_path(ttq.make_params(
+               d=4096, d_out=4096, T=T, rank=rank, bits=bits, group=group,
+               p=2.0, lam=1e-3, alpha=0.5), R)}
+    by = fl = 0
+    for p in projs:
+        b_, f_ = alg(p["d"], p["d_out"], T, R, rank)
+        by += b_
+        fl += f_
+    out["alg_bytes_per_step"] = by
+    out["alg_flops_per_step"] = fl
+    out["hbm_frac_step"] = by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    out["mfma_frac_step"] = fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    # dominant kernel: the largest share of the step's kernel time
+    dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
+    ub = uf = 0
+    for p in projs:
+        b_, f_ = kernel_units(dom, p["d"], p["d_out"], T, R, rank)
+        ub += b_
+        uf += f_
+    n_l = kt[dom][1]
+    out["roofline"] = roofline(dom, kt[dom][0], ub / n_l, uf / n_l,
+                               traffic_entry(dom, f"c5_T{T}"))
+    if per_projection:
+        pp = {}
+        for p in projs:
+            pm = timed_wall(torch, lambda i: call(p), max(3, reps // 2), 1)
+            e = {"ms": pm, "tokens_per_s": R * T / (pm * 1e-3)}
+            b_, f_ = alg(p["d"], p["d_out"], T, R, rank)
+            e["mfma_frac"] = f_ / (pm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+            e["hbm_frac"] = b_ / (pm * 1e-3) / 1e9 / HBM_PEAK_GBS
+            if want_gemm:
+                g = gemm_ms(torch, [p["W"]], [p["X"]], max(3, reps // 2), 1)
+                e["gemm_bf16_ms"] = g
+                e["rho_measured"] = pm / g - 1.0
+                e["rho_pages"] = 1.0 / p["d_out"] + 3.0 / T
+            pp[p["name"]] = e
+        out["per_projection"] = pp
+        if want_gemm:
+            gl = sum(e["gemm_bf16_ms"] for e in pp.values())
+            out["gemm_bf16_layer_ms"] = gl
+            out["rho_measured_layer"] = ms / gl - 1.0
+    del projs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def leg_single(torch, ttq, leg: str, name: str, prob_fn, T: int, d: int,
+               d_out: int,
+               bits: int, group: int, rank: int, p: float, lam: float,
+               x_kind: str, n_out: int, steps: int, seed: int,
+               want_gemm: bool = True) -> dict:
+    """One projection (R = 1) with its weights rotated over enough copies to
+    exceed the 256 MB Infinity Cache; a new activation draw per call."""
+    prob = prob_fn()
+    w_bytes = 2 * d * d_out
+    n_w = max(1, -(-ROTATE_BYTES // (w_bytes + 2 * T * d + 4 * T * d_out)))
+    W0 = dev_bf16(prob.W, torch)
+    Ws = [W0] + [W0.clone() for _ in range(n_w - 1)]
+    B = dev_bf16(prob.B, torch) if rank else None
+    A = dev_bf16(prob.A, torch) if rank else None
+    n_x = max(2, n_w)
+    Xs = [draw_x_gpu(torch, seed + c, 1, T, d, x_kind, n_out)[0]
+          for c in range(n_x)]
+    Ys = [torch.empty(T, d_out, dtype=torch.float32, device="cuda")
+          for _ in range(n_x)]
+    prm = ttq.make_params(d=d, d_out=d_out, T=T, rank=rank, bits=bits,
+                          group=group, p=p, lam=lam, alpha=0.5)
+    ws = torch.empty(max(256, ttq.ttq_workspace_bytes(prm)), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    kw = dict(p=p, lam=lam, alpha=0.5, bits=bits, group=group)
+
+    def step(i):
+        ttq.ttq_linear(Ws[i % n_w], Xs[i % n_x], B, A, Y=Ys[i % n_x],
+                       workspace=ws, stream=stream, **kw)
+
+    ms = timed_wall(torch, step, steps, 2)
+    kt = kernel_times(torch, ttq, step, min(steps, 20))
+    by, fl = alg(d, d_out, T, 1, rank)
+    out = {"workload": name, "d": d, "d_out": d_out, "T": T, "bits": bits,
+           "group": group, "rank": rank, "p": p, "lambda": lam,
+           "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+           "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+           "path": ttq.ttq_path(prm, 1),
+           "rotating_w_copies": n_w,
+           "kernels": {k: {"ms_per_launch": v[0], "launches_per_call": v[1]}
+                       for k, v in kt.items()}}
+    dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
+    ub, uf = kernel_units(dom, d, d_out, T, 1, rank)
+    out["roofline"] = roofline(dom, kt[dom][0], ub, uf,
+                               traffic_entry(dom, leg))
+    if want_gemm:
+        g = gemm_ms(torch, [Ws[0]], [Xs[0][None]], steps, 2)
+        out["gemm_bf16_ms"] = g
+        out["rho_measured"] = ms / g - 1.0
+        out["rho_pages"] = 1.0 / d_out + 3.0 / T
+    del Ws, Xs, Ys, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def leg_c4(torch, ttq, p: float, steps: int) -> dict:
+    from workloads import configs as wc
+    return leg_single(torch, ttq, f"c4_p{int(p)}", f"c4 up_proj 8192->28672 T=512 2-bit g64 "
+                      f"r=128 p={p:g} lambda=1e-2",
+                      lambda: wc.make_c4(p=p, T=1), 512, 8192, 28672, 2, 64,
+                      128, p, 1e-2, "t3", 41, steps, 7000 + int(p))
+
+
+def leg_c3(torch, ttq, which: str, steps: int) -> dict:
+    from workloads import configs as wc
+    d, d_out = (4096, 11008) if which == "gate_up" else (11008, 4096)
+    return leg_single(torch, ttq, f"c3_{which}", f"c3 {which} {d}->{d_out} "
+                      "T=2048 3-bit g128 r=64, 4 outlier channels x50",
+                      lambda: wc.make_c3(which, T=1), 2048, d, d_out, 3, 128,
+                      64, 2.0, 1e-3, "x50", 4, steps,
+                      8000 + (0 if which == "gate_up" else 50))
+
+
+def leg_c2(torch, ttq, T: int, steps: int, warmup: int, qformat: str,
+           want_graph: bool, want_gemm: bool) -> dict:
+    """The 4096 x 4096 projection at T tokens, W rotated over 20 copies."""
+    from workloads import configs as wc
+    d = d_out = 4096
+    bits = 8 if qformat == "fp8" else 4
+    prob = wc.make_c2(T=T)
+    n_w = max(2, -(-ROTATE_BYTES // (2 * d * d_out)))
+    W0 = dev_bf16(prob.W, torch)
+    Ws = [W0] + [W0.clone() for _ in range(n_w - 1)]
+    n_x = 64
+    Xall = draw_x_gpu(torch, 1000 + T, n_x, T, d, "n", 41)
+    Ys = [torch.empty(T, d_out, dtype=torch.float32, device="cuda")
+          for _ in range(8)]
+    kw = dict(p=2.0, lam=1e-3, alpha=0.5, bits=bits, group=128, qformat=qformat)
+    prm = ttq.make_params(d=d, d_out=d_out, T=T, bits=bits, group=128, p=2.0,
+                          lam=1e-3, alpha=0.5, qformat=qformat)
+    ws = torch.empty(max(256, ttq.ttq_workspace_bytes(prm)), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        ttq.ttq_linear(Ws[i % n_w], Xall[i % n_x], Y=Ys[i % 8], workspace=ws,
                        stream=stream, **kw)
-    if want_graph:
-        out["ms_per_step_hot_w"] = timed(step_hot, max(50, steps // 4), warmup)
 
+    ms = timed_wall(torch, step, steps, warmup)
+    kt = kernel_times(torch, ttq, step, min(steps, 1000))
+    by, fl = alg(d, d_out, T)
+    out = {"workload": f"q_proj 4096x4096 T={T}, {bits}-bit g128 "
+                       f"{FORMAT_NAMES[qformat]}, p=2, lambda=1e-3, alpha=0.5",
+           "T": T, "qformat": qformat, "ms": ms,
+           "tokens_per_s": T / (ms * 1e-3),
+           "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "rotating_w_copies": n_w,
+           "kernels": {k: {"ms_per_launch": v[0], "launches_per_call": v[1]}
+                       for k, v in kt.items()}}
+    dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
+    ub, uf = kernel_units(dom, d, d_out, T, 1, 0)
+    sfx = "" if qformat == "asym" else f"_{qformat}"
+    out["roofline"] = roofline(dom, kt[dom][0], ub, uf,
+                               traffic_entry(dom, f"c2_T{T}{sfx}"))
     if want_graph:
-        # one graph holding n_w calls (one per W copy), replayed
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for i in range(n_w):  # warm-up on the capture stream
-                ttq.ttq_linear(Ws[i], Xs[i % n_x], Y=Ys[i % n_y], workspace=ws,
+            for i in range(n_w):
+                ttq.ttq_linear(Ws[i], Xall[i], Y=Ys[i % 8], workspace=ws,
                                stream=s.cuda_stream, **kw)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream().cuda_stream
             for i in range(n_w):
-                ttq.ttq_linear(Ws[i], Xs[i % n_x], Y=Ys[i % n_y], workspace=ws,
+                ttq.ttq_linear(Ws[i], Xall[i], Y=Ys[i % 8], workspace=ws,
                                stream=cs, **kw)
         reps = max(1, steps // n_w)
-        gms = timed(lambda i: g.replay(), reps, 3) / n_w
-        out["ms_per_step_graph"] = gms
-
+        out["ms_graph"] = timed_wall(torch, lambda i: g.replay(), reps, 3) / n_w
     if want_gemm:
-        # plain bf16 GEMM of the same shape and cache policy (hipBLASLt)
-        def gemm(i):
-            torch.matmul(Xs[i % n_x], Ws[i % n_w].t())
-        out["gemm_bf16_ms"] = timed(gemm, steps, warmup)
-    del Ws, Xs, Ys, ws
+        gm = gemm_ms(torch, [Ws[0]], [Xall[0][None]], steps, warmup)
+        out["gemm_bf16_ms"] = gm
+        out["rho_measured"] = ms / gm - 1.0
+        out["rho_pages"] = 1.0 / d_out + 3.0 / T
+    del Ws, Xall, Ys, ws
     torch.cuda.empty_cache()
     return out
 
 
-FP32_PEAK_TFLOPS = 157.3  # float32 peak, the vector units and the matrix instruction alike
+def leg_ceilings(torch) -> dict:
+    """Measured ceilings on this machine: HBM from a device-to-device copy of
+    2 GiB (read + write bytes over time), matrix cores from a large bf16
+    GEMM (torch -> hipBLASLt, 8192^3)."""
+    n = 2 * 2 ** 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed_wall(torch, lambda i: dst.copy_(src), 20, 3)
+    copy = {"bytes_moved": 2 * n, "ms": ms,
+            "GB_s": 2 * n / (ms * 1e-3) / 1e9,
+            "frac_of_peak": 2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del src, dst
+    M = 8192
+    a = torch.randn(M, M, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(M, M, dtype=torch.bfloat16, device="cuda")
+    ms2 = timed_wall(torch, lambda i: torch.matmul(a, b), 20, 3)
+    fl = 2.0 * M ** 3
+    gemm = {"shape": "8192x8192x8192 bf16", "ms": ms2,
+            "TFLOP_s": fl / (ms2 * 1e-3) / 1e12,
+            "frac_of_peak": fl / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy": copy, "bf16_gemm": gemm}
 
 
-def measure_pca(torch, ttq, reps: int = 10):
-    """Low-rank factors by PCA on the same 4096 x 4096 weights shape: r = 64,
-    two power iterations, static (context for the low-rank row; not the
-    timed step)."""
-    import numpy as np
-    from workloads.configs import draw_lowrank_w, draw_omega
-    d = d_out = 4096
-    r, iters = 64, 2
-    W = dev_bf16(draw_lowrank_w(1, d_out, d, r), torch)
-    Om = torch.from_numpy(draw_omega(2, d, r)).cuda()
-    prm = ttq.make_params(d=d, d_out=d_out, T=0, rank=r, bits=4, group=32,
-                          p=2.0, lam=0.0, alpha=0.0)
-    ws = torch.empty(ttq.ttq_lowrank_pca_workspace_bytes(prm, iters),
-                     dtype=torch.uint8, device="cuda")
-    f = lambda: ttq.ttq_lowrank_pca(W, Om, iters=iters, workspace=ws)
-    for _ in range(2):
-        f()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        f()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    ttq.timing_reset()
-    ttq.timing_enable(True)
-    for _ in range(reps):
-        f()
-    torch.cuda.synchronize()
-    kt = {k: v[0] / reps for k, v in ttq.timing_query().items() if v[1]}
-    ttq.timing_enable(False)
-    ttq.timing_reset()
-    # products with W: M Omega, 2 per power iteration, W^T Q for A (+ Gram
-    # and substitution work on the d x r panels, not counted)
-    flops_w = (2 + 2 * iters) * 2.0 * d_out * d * r
-    sk = kt.get("pca_skinny", float("nan"))
-    return {"shape": f"{d_out}x{d}, r={r}, {iters} power iterations",
-            "ms": ms, "kernels_ms": kt,
-            "skinny_tflops_w_products": flops_w / (sk * 1e-3) / 1e12,
-            "skinny_frac_fp32_peak": flops_w / (sk * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
-
-
-def measure_decode(torch, ttq, steps: int = 1000):
-    """One token against codes stored by ttq_quantize (the same 4096 x 4096
-    weights, 4-bit g128): 20 rotating stored copies, as for the main step."""
+def leg_decode(torch, ttq, steps: int = 1000) -> dict:
+    """One token against codes stored by ttq_quantize (4096 x 4096, 4-bit
+    g128): 20 rotating stored copies."""
     from workloads import configs as wc
     d = d_out = 4096
     prob = wc.make_c2(T=16)
@@ -264,34 +509,15 @@ def measure_decode(torch, ttq, steps: int = 1000):
     kw = dict(bits=4, group=128)
     st = [ttq.ttq_quantize(W0, X0, p=prob.p, lam=prob.lam, alpha=prob.alpha, **kw)
           for _ in range(20)]
-    Xs = [dev_bf16(wc.draw_x(1, 3000 + c, 1, 1, d, "logu10_100", 41)[0], torch)
-          for c in range(64)]
+    Xs = draw_x_gpu(torch, 3000, 64, 1, d, "n", 41)
     Y = torch.empty(1, d_out, dtype=torch.float32, device="cuda")
     prm = ttq.make_params(d=d, d_out=d_out, T=1, bits=4, group=128, p=1.0,
                           lam=0.0, alpha=0.0)
     ws = torch.empty(max(256, ttq.ttq_qmatmul_workspace_bytes(prm)),
                      dtype=torch.uint8, device="cuda")
     f = lambda i: ttq.ttq_qmatmul(*st[i % 20], Xs[i % 64], Y=Y, workspace=ws, **kw)
-    for i in range(50):
-        f(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        f(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    ttq.timing_reset()
-    ttq.timing_enable(True)
-    for i in range(steps):
-        f(i)
-    torch.cuda.synchronize()
-    kt = {k: v[0] / v[1] for k, v in ttq.timing_query().items() if v[1]}
-    ttq.timing_enable(False)
-    ttq.timing_reset()
-    # the same calls replayed from a HIP graph (no host work per call)
+    ms = timed_wall(torch, f, steps, 50)
+    kt = kernel_times(torch, ttq, f, steps)
     g = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
     cs.wait_stream(torch.cuda.current_stream())
@@ -305,32 +531,23 @@ def measure_decode(torch, ttq, steps: int = 1000):
         s = torch.cuda.current_stream().cuda_stream
         for i in range(20):
             ttq.ttq_qmatmul(*st[i], Xs[i], Y=Y, workspace=ws, stream=s, **kw)
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, steps // 20)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    gms = e0.elapsed_time(e1) / (reps * 20)
+    gms = timed_wall(torch, lambda i: g.replay(), max(1, steps // 20), 3) / 20
     G = d // 128
-    alg = d_out * d // 2 + 8 * d_out * G + 2 * d + 4 * d + 4 * d_out
-    k = kt.get("qgemv", float("nan"))
-    return {"workload": "4096x4096, 4-bit g128 codes, one token", "ms_per_step": ms,
-            "tokens_per_s": 1.0 / (ms * 1e-3), "ms_per_step_graph": gms,
+    ab = d_out * d // 2 + 8 * d_out * G + 2 * d + 4 * d + 4 * d_out
+    k = kt.get("qgemv", (float("nan"), 0))[0]
+    return {"workload": "4096x4096, 4-bit g128 codes, one token",
+            "ms": ms, "tokens_per_s": 1.0 / (ms * 1e-3), "ms_graph": gms,
             "tokens_per_s_graph": 1.0 / (gms * 1e-3), "kernel": "qgemv",
-            "kernel_ms": k, "alg_bytes": alg,
-            "hbm_frac_kernel": alg / (k * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "kernel_ms": k, "alg_bytes": ab,
+            "hbm_frac_kernel": ab / (k * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": traffic_entry("qgemv", "decode_int4")}
 
 
-def measure_segmented(torch, ttq, reps: int = 50):
-    """Continuous batching on the same 4096 x 4096 weights (4-bit g128,
-    r = 32): 22 requests of mixed lengths (16 single tokens, 4 of 3..16,
-    one of 100, one of 200; 354 tokens) in one packed X, each with its own
-    statistics -- one ttq_linear_segmented call against one ttq_linear call
-    per request."""
+def leg_segmented(torch, ttq, reps: int = 50) -> dict:
+    """Continuous batching on the 4096 x 4096 weights (4-bit g128, r = 32):
+    22 requests of mixed lengths (16 single tokens, 3, 7, 12, 16, 100, 200;
+    354 tokens) in one packed X, each with its own statistics -- one
+    ttq_linear_segmented call against one ttq_linear call per request."""
     import numpy as np
     from workloads import configs as wc
     d = d_out = 4096
@@ -339,71 +556,108 @@ def measure_segmented(torch, ttq, reps: int = 50):
     lengths = [1] * 16 + [3, 7, 12, 16, 100, 200]
     rng = np.random.default_rng(12)
     lengths = [int(x) for x in rng.permutation(lengths)]
-    xs = [wc.draw_x(500 + i, 0, 1, t, d, "logu10_100", 41)[0]
+    xs = [draw_x_gpu(torch, 500 + i, 1, t, d, "n", 41)[0]
           for i, t in enumerate(lengths)]
     offs = [0] + [int(x) for x in np.cumsum(lengths)]
     W = dev_bf16(prob.W, torch)
     Bm, A = dev_bf16(prob.B, torch), dev_bf16(prob.A, torch)
-    X = dev_bf16(np.concatenate(xs), torch)
-    Xr = [dev_bf16(x, torch) for x in xs]
+    X = torch.cat(xs)
     kw = dict(p=prob.p, lam=prob.lam, alpha=prob.alpha, bits=4, group=128)
     Y = torch.empty(offs[-1], d_out, dtype=torch.float32, device="cuda")
 
-    def seg():
+    def seg(i):
         ttq.ttq_linear_segmented(W, X, Bm, A, seg_offsets=offs, Y=Y, **kw)
 
-    def single():
-        for i, x in enumerate(Xr):
-            ttq.ttq_linear(W, x, Bm, A, Y=Y[offs[i]:offs[i + 1]], **kw)
+    def single(i):
+        for j, x in enumerate(xs):
+            ttq.ttq_linear(W, x, Bm, A, Y=Y[offs[j]:offs[j + 1]], **kw)
 
     out = {"workload": f"4096x4096 4-bit g128 r=32, {len(lengths)} requests, "
                        f"{offs[-1]} tokens (16 x 1, 3, 7, 12, 16, 100, 200)"}
     for name, f in (("segmented", seg), ("one_call_per_request", single)):
-        for _ in range(3):
-            f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            f()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = timed_wall(torch, f, reps, 3)
         out[name] = {"ms": ms, "tokens_per_s": offs[-1] / (ms * 1e-3)}
     return out
 
 
-def cpu_baseline(T: int, seconds: float, qformat: str = "asym"):
-    """The oracle as it stands, on the host cores, on a bounded sample."""
+def leg_pca(torch, ttq, reps: int = 10) -> dict:
+    """Low-rank factors by PCA (4096 x 4096, r = 64, two power iterations,
+    static): a per-model initialisation, context for the low-rank row."""
+    from workloads.configs import draw_lowrank_w, draw_omega
+    d = d_out = 4096
+    r, iters = 64, 2
+    W = dev_bf16(draw_lowrank_w(1, d_out, d, r), torch)
+    Om = torch.from_numpy(draw_omega(2, d, r)).cuda()
+    prm = ttq.make_params(d=d, d_out=d_out, T=0, rank=r, bits=4, group=32,
+                          p=2.0, lam=0.0, alpha=0.0)
+    ws = torch.empty(ttq.ttq_lowrank_pca_workspace_bytes(prm, iters),
+                     dtype=torch.uint8, device="cuda")
+    f = lambda i: ttq.ttq_lowrank_pca(W, Om, iters=iters, workspace=ws)
+    ms = timed_wall(torch, f, reps, 2)
+    kt = kernel_times(torch, ttq, f, reps)
+    flops_w = (2 + 2 * iters) * 2.0 * d_out * d * r
+    sk = kt.get("pca_skinny", (float("nan"), 1))
+    sk_ms = sk[0] * sk[1]
+    return {"shape": f"{d_out}x{d}, r={r}, {iters} power iterations",
+            "ms": ms, "kernels_ms_per_call": {k: v[0] * v[1] for k, v in kt.items()},
+            "skinny_tflops_w_products": flops_w / (sk_ms * 1e-3) / 1e12,
+            "skinny_frac_fp32_peak": flops_w / (sk_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
+
+
+# ------------------------------------------------------------ cpu baseline
+def _threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline_c5(T: int, seconds: float) -> dict:
+    """The oracle as it stands on the host cores, on a bounded sample of the
+    headline workload: for each of the seven projections, one request's call
+    (statistics over all T tokens, then quantization and contraction) on two
+    subsets of output rows; the time is extrapolated linearly in the row
+    count to all d' rows (rows are independent once D is fixed) and
+    multiplied by the R = 8 requests."""
     import numpy as np
     import oracle
     from workloads import configs as wc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    prob = wc.make_c2(T=T)
-    prob.bits = format_bits(qformat)
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        X = wc.draw_x(1, 5000 + calls, 1, T, prob.d, "logu10_100", 41)[0]
-        oracle.ttq_linear(prob.W, X, bits=prob.bits, group=prob.group,
-                          p=prob.p, lam=prob.lam, alpha=prob.alpha,
-                          qformat=qformat)
-        calls += 1
-        el = time.perf_counter() - t0
-        if (el >= seconds and calls >= 3) or el >= 3 * seconds:
-            break
-    return {"value": calls * T / el, "unit": "tokens/s", "cores": threads,
+    R = 8
+    t_layer = 0.0
+    measured = 0.0
+    t_start = time.perf_counter()
+    rows_a, rows_b = 8, 24
+    scale = max(1.0, min(4.0, seconds / 12.0))
+    rows_a, rows_b = int(rows_a * scale), int(rows_b * scale)
+    for i, (name, d, d_out) in enumerate(C5_PROJ):
+        prob = wc.make_c5(T=1, proj=name, R=1)
+        X = wc.draw_x(4000 + i, 0, 1, T, d, "logu10_100",
+                      max(1, round(0.01 * d)))[0]
+        ts = []
+        for nr in (rows_a, rows_b):
+            rows = np.arange(nr)
+            t0 = time.perf_counter()
+            oracle.ttq_linear(prob.W, X, bits=4, group=128, p=2.0, lam=1e-3,
+                              alpha=0.5, B_bits=prob.B, A_bits=prob.A,
+                              rows=rows)
+            ts.append(time.perf_counter() - t0)
+        measured += sum(ts)
+        per_row = max(0.0, (ts[1] - ts[0]) / (rows_b - rows_a))
+        fixed = max(0.0, ts[0] - per_row * rows_a)
+        t_layer += R * (fixed + per_row * d_out)
+    wall = time.perf_counter() - t_start
+    return {"value": R * T / t_layer, "unit": "tokens/s", "cores": _threads(),
             "kind": "oracle",
-            "sample": f"{calls} full calls of the same workload (T={T}, "
-                      f"d=d'=4096), X redrawn per call, {el:.1f} s wall, "
-                      f"host cpu_count={os.cpu_count()}"}
+            "sample": f"extrapolated x{t_layer / measured:.0f}: one request of "
+                      f"each of the 7 projections at T={T}, rows {rows_a} and "
+                      f"{rows_b} of d' (statistics over all T tokens), "
+                      f"{measured:.1f} s of oracle time ({wall:.1f} s wall "
+                      "with input generation), extrapolated linearly in d' "
+                      f"and times R=8; host cpu_count={os.cpu_count()}"}
 
 
+# ---------------------------------------------------------------- profiles
 def _read_csv(d, suffix):
     import csv
     import glob
@@ -414,26 +668,36 @@ def _read_csv(d, suffix):
     return rows
 
 
+def leg_name(a) -> str:
+    if a.leg == "c5":
+        return f"c5_T{a.T or 4096}"
+    if a.leg == "c4":
+        return f"c4_p{int(a.p)}"
+    if a.leg == "c3":
+        return f"c3_{a.which}"
+    if a.leg == "c2":
+        sfx = "" if a.qformat == "asym" else f"_{a.qformat}"
+        return f"c2_T{a.T or 1}{sfx}"
+    if a.leg == "decode":
+        return "decode_int4"
+    return a.leg
+
+
 def summarize(a):
-    """profiles/: kernel-trace summary of the dominant kernel and the HBM
-    traffic per launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
-    same counter reads for a device-to-device copy of known size."""
+    """profiles/: kernel-trace summary of one kernel on one workload and its
+    HBM traffic per launch from FETCH_SIZE / WRITE_SIZE, each scaled by what
+    the same counter reads for a device-to-device copy of known size."""
     trace, fetch, write = a.summarize
+    kind = a.kernel
+    key = KERNEL_SYMBOLS[kind]
     stats = _read_csv(trace, "kernel_stats.csv")
-    T = a.T
-    key = {1: "gemv", 128: "k_fused"}.get(T, "k_fused")
-    kname = {1: "gemv_t1"}.get(T, "fused_qdq_mfma")
     calib_bytes = a.copy_calib_mb * 2 ** 20
-
-    def per_dispatch(rows, counter, match):
-        vals = [float(r["Counter_Value"]) for r in rows
-                if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
-        return vals
-
     fr = _read_csv(fetch, "counter_collection.csv")
     wr = _read_csv(write, "counter_collection.csv")
-    k_f = per_dispatch(fr, "FETCH_SIZE", lambda n: key in n)
-    k_w = per_dispatch(wr, "WRITE_SIZE", lambda n: key in n)
+
+    def per_dispatch(rows, counter):
+        return [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and key in r["Kernel_Name"]]
 
     def calib(rows, counter):
         cp = [r for r in rows if r["Counter_Name"] == counter
@@ -442,60 +706,42 @@ def summarize(a):
         vals = [float(r["Counter_Value"]) for r in cp[-5:]]
         return sum(vals) / len(vals) if vals else float("nan")
 
+    k_f, k_w = per_dispatch(fr, "FETCH_SIZE"), per_dispatch(wr, "WRITE_SIZE")
     c_f, c_w = calib(fr, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
     sf = calib_bytes / (c_f * 1024) if c_f == c_f and c_f > 0 else float("nan")
     sw = calib_bytes / (c_w * 1024) if c_w == c_w and c_w > 0 else float("nan")
-    f_kib = sum(k_f) / len(k_f)
-    w_kib = sum(k_w) / len(k_w)
+    f_kib = sum(k_f) / max(1, len(k_f))
+    w_kib = sum(k_w) / max(1, len(k_w))
     traffic = f_kib * 1024 * sf + w_kib * 1024 * sw
-    d = d_out = 4096
-    ab = alg_bytes(d, d_out, T)
-    fs = fmt_suffix(a.qformat)
-    rec = {"kernel": kname, "workload": f"q_proj 4096x4096 T={T}",
-           "qformat": a.qformat,
-           "kernel_src_sha": kernel_src_sha(kname),
+    leg = leg_name(a)
+    rec = {"kernel": kind, "workload": leg, "kernel_src_sha": kernel_src_sha(kind),
            "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
-           "copy_calib_bytes": calib_bytes,
-           "copy_fetch_kib": c_f, "copy_write_kib": c_w,
-           "fetch_scale": sf, "write_scale": sw,
-           "bytes_per_launch": traffic, "alg_bytes_per_launch": ab,
-           "traffic_over_alg": traffic / ab,
-           "launches_counted": [len(k_f), len(k_w)]}
+           "copy_calib_bytes": calib_bytes, "copy_fetch_kib": c_f,
+           "copy_write_kib": c_w, "fetch_scale": sf, "write_scale": sw,
+           "bytes_per_launch": traffic, "launches_counted": [len(k_f), len(k_w)]}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    json.dump(rec, open(traffic_file(kname, T, a.qformat), "w"), indent=1)
-    lines = [f"# {kname}: 4096x4096 q_proj, T={T} ({format_bits(a.qformat)}-bit "
-             f"g128 {FORMAT_NAMES[a.qformat]}, p=2)", "",
-             "Commands (from the repository root):", "", "```"]
-    lines += [c for c in a.profile_cmd.split(";;") if c] + ["```", "",
-              "## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
-              "| kernel | calls | avg ns | min ns | max ns |",
-              "|---|---|---|---|---|"]
+    json.dump(rec, open(traffic_file(kind, leg), "w"), indent=1)
+    lines = [f"# {kind} on {leg}", "", "Commands (from the repository root):",
+             "", "```"]
+    lines += [c for c in a.profile_cmd.split(";;") if c] + [
+        "```", "", "## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
+        "| kernel | calls | avg ns | min ns | max ns | share % |",
+        "|---|---|---|---|---|---|"]
     for r in stats:
-        lines.append(f"| {r['Name'][:70]} | {r['Calls']} | "
-                     f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | "
+                     f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r.get('Percentage', 0) or 0):.1f} |")
     lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-              f"- kernel FETCH_SIZE {f_kib:.0f} KiB/launch, WRITE_SIZE {w_kib:.1f} KiB/launch"
-              f" (averaged over {len(k_f)} / {len(k_w)} launches)",
+              f"- {kind}: FETCH_SIZE {f_kib:.0f} KiB/launch, WRITE_SIZE "
+              f"{w_kib:.1f} KiB/launch (averaged over {len(k_f)} / {len(k_w)} "
+              "launches)",
               f"- calibration: device-to-device copy of {calib_bytes} bytes reads "
               f"FETCH_SIZE {c_f:.0f} KiB and WRITE_SIZE {c_w:.0f} KiB; scale "
               f"factors {sf:.4f} (fetch) and {sw:.4f} (write)",
-              f"- traffic = {traffic / 1e6:.3f} MB/launch against "
-              f"{ab / 1e6:.3f} MB algorithmic (ratio {traffic / ab:.3f})", ""]
-    md = os.path.join(ROOT, "profiles", f"{kname}_q_proj4096_T{T}{fs}.md")
-    open(md, "w").write("\n".join(lines))
+              f"- traffic = {traffic / 1e6:.3f} MB per launch", ""]
+    open(os.path.join(ROOT, "profiles", f"{kind}_{leg}.md"), "w").write(
+        "\n".join(lines))
     print(json.dumps(rec))
-
-
-def traffic_entry(kernel: str, T: int, qformat: str = "asym"):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel source has changed since it was taken."""
-    try:
-        rec = json.load(open(traffic_file(kernel, T, qformat)))
-    except Exception:
-        return None
-    if rec.get("kernel_src_sha") != kernel_src_sha(kernel):
-        return None
-    return rec.get("bytes_per_launch")
 
 
 def copy_calibration(mb: int, torch):
@@ -508,6 +754,7 @@ def copy_calibration(mb: int, torch):
     torch.cuda.synchronize()
 
 
+# -------------------------------------------------------------------- main
 def main():
     a = parse()
     if a.summarize:
@@ -522,74 +769,77 @@ def main():
     import online_activation_aware_ttq_amd as ttq
 
     torch.cuda.init()
-    if a.only_pca:
-        print(json.dumps({"lowrank_pca": measure_pca(torch, ttq, reps=a.steps)}),
-              flush=True)
-        return
-    if a.only_decode:
-        r = measure_decode(torch, ttq, a.steps)
+    ttq.load_library()
+
+    def emit(obj):
+        print(json.dumps(obj), flush=True)
+
+    if a.leg != "all":
+        if a.leg == "c5":
+            r = leg_c5(torch, ttq, a.T or 4096, a.steps, a.warmup,
+                       want_gemm=False, per_projection=False)
+        elif a.leg == "c4":
+            r = leg_c4(torch, ttq, a.p, a.steps)
+        elif a.leg == "c3":
+            r = leg_c3(torch, ttq, a.which, a.steps)
+        elif a.leg == "c2":
+            r = leg_c2(torch, ttq, a.T or 1, a.steps, a.warmup, a.qformat,
+                       False, False)
+        elif a.leg == "decode":
+            r = leg_decode(torch, ttq, a.steps)
+        elif a.leg == "segmented":
+            r = leg_segmented(torch, ttq, a.steps)
+        elif a.leg == "pca":
+            r = leg_pca(torch, ttq, a.steps)
+        else:
+            r = leg_ceilings(torch)
         if a.copy_calib_mb:
             copy_calibration(a.copy_calib_mb, torch)
-        print(json.dumps({"decode_from_codes": r}), flush=True)
+        emit({a.leg: r})
         return
-    if a.only_segmented:
-        print(json.dumps({"continuous_batching": measure_segmented(torch, ttq, a.steps)}),
-              flush=True)
-        return
-    main_m = measure(a.T, a.steps, a.warmup, torch, ttq,
-                     want_graph=not a.only_ttq, want_gemm=not a.only_ttq,
-                     qformat=a.qformat)
-    if a.copy_calib_mb:
-        copy_calibration(a.copy_calib_mb, torch)
-    sec = None
-    if not a.only_ttq and a.T != 128:
-        sec = measure(128, max(100, a.steps // 4), a.warmup, torch, ttq,
-                      want_graph=False, want_gemm=True, qformat=a.qformat)
-    # the other quantizer formats on the same step (context lines)
+
+    T = 4096
+    head = leg_c5(torch, ttq, T, a.steps, a.warmup, want_gemm=True)
+    print(f"# c5 T={T}: {head['ms_per_step']:.2f} ms/step", file=sys.stderr,
+          flush=True)
+    legs = {}
+    for t in (1, 16, 256):
+        legs[f"c5_T{t}"] = leg_c5(torch, ttq, t, 20, 3, want_gemm=True)
+        print(f"# c5 T={t} done", file=sys.stderr, flush=True)
+    legs["c4_p2"] = leg_c4(torch, ttq, 2.0, 10)
+    legs["c4_p1"] = leg_c4(torch, ttq, 1.0, 10)
+    legs["c3_gate_up"] = leg_c3(torch, ttq, "gate_up", 10)
+    legs["c3_down"] = leg_c3(torch, ttq, "down", 10)
+    print("# c4, c3 done", file=sys.stderr, flush=True)
+    legs["c2_T1"] = leg_c2(torch, ttq, 1, 2000, 50, "asym", True, True)
+    legs["c2_T128"] = leg_c2(torch, ttq, 128, 500, 20, "asym", False, True)
     fmts = {}
-    if not a.only_ttq:
-        for f in ("asym", "sym", "intzp", "fp8"):
-            if f == a.qformat:
-                continue
-            m = measure(a.T, max(200, a.steps // 4), a.warmup, torch, ttq,
-                        want_graph=False, want_gemm=False, qformat=f)
-            kms = max(m["kernels_ms_avg"].values())
-            fmts[f] = {"bits": format_bits(f), "ms_per_step": m["ms_per_step"],
-                       "tokens_per_s": a.T / (m["ms_per_step"] * 1e-3),
-                       "dominant_kernel_ms": kms,
-                       "hbm_frac_kernel": alg_bytes(4096, 4096, a.T) / (kms * 1e-3)
-                       / 1e9 / HBM_PEAK_GBS}
+    for f in ("sym", "intzp", "fp8"):
+        m = leg_c2(torch, ttq, 1, 500, 20, f, False, False)
+        fmts[f] = {k: m[k] for k in ("ms", "tokens_per_s", "hbm_frac")}
+        fmts[f]["dominant_kernel_ms"] = m["roofline"]["kernel_ms"]
+    legs["c2_T1_other_formats"] = fmts
+    legs["decode_from_codes"] = leg_decode(torch, ttq)
+    legs["continuous_batching"] = leg_segmented(torch, ttq)
+    legs["lowrank_pca"] = leg_pca(torch, ttq)
+    ceil = leg_ceilings(torch)
+    print("# context legs done", file=sys.stderr, flush=True)
 
-    d = d_out = 4096
-    T = a.T
-    ms = main_m["ms_per_step"]
-    value = T / (ms * 1e-3)
-    # dominant kernel: the largest share of the step's kernel time
-    kt = main_m["kernels_ms_avg"]
-    launches = main_m["kernels_launches"]
-    kname = max(kt, key=lambda k: kt[k] * launches[k])
-    k_ms = kt[kname]
-    ab = alg_bytes(d, d_out, T)
-    af = alg_flops(d, d_out, T)
-    hbm_bound = ab / HBM_PEAK_GBS > af / (BF16_PEAK_TFLOPS * 1e3)
-    if hbm_bound:
-        achieved = ab / (k_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS}
+    ms = head["ms_per_step"]
+    roof = dict(head["roofline"])
+    # the same kernel against the measured ceilings (context for frac)
+    if roof["bound"] == "mfma":
+        roof["frac_of_measured_gemm_ceiling"] = (
+            roof["achieved"] / ceil["bf16_gemm"]["TFLOP_s"])
     else:
-        achieved = af / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved,
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["traffic"] = traffic_entry(kname, T, a.qformat)
-    roof.update(kernel=kname, kernel_ms=k_ms, alg_bytes=ab, alg_flops=af)
-
+        roof["frac_of_measured_copy_ceiling"] = (
+            roof["achieved"] / ceil["hbm_copy"]["GB_s"])
     line = {
         "metric": METRIC,
-        "value": value,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": a.steps,
+        "steps": head["steps"],
         "warmup": a.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -598,51 +848,22 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"attention q_proj d=d'=4096 T={T}, "
-                        f"{format_bits(a.qformat)}-bit g128 "
-                        f"{FORMAT_NAMES[a.qformat]}, p=2, lambda=1e-3, "
-                        "alpha=0.5, 1% outlier channels x10-100 redrawn per call",
-            "d": d, "d_out": d_out, "T": T, "bits": format_bits(a.qformat),
-            "group": 128, "qformat": a.qformat,
-            "rank": 0, "parallelism": "single GPU",
-            "weights": f"{main_m['rotating_w_copies']} rotating copies "
-                       f"({main_m['rotating_bytes'] / 1e6:.0f} MB, above the "
-                       "256 MB Infinity Cache)",
+            "workload": "7B-class decoder layer: q/k/v/o 4096->4096, gate/up "
+                        "4096->11008, down 11008->4096; 8 requests x 4096 "
+                        "tokens, per-request TTQ statistics and outlier "
+                        "channels (1% of channels x10-100 log-uniform); 4-bit "
+                        "g128 asymmetric, p=2, lambda=1e-3, alpha=0.5, "
+                        "static low rank r=32 on all seven",
+            "requests": 8, "T": T, "bits": 4, "group": 128, "rank": 32,
+            "global_batch": 8 * T, "parallelism": "single GPU",
         },
         "roofline": roof,
-        "step_all_kernels_ms": main_m["kernels_ms_avg"],
-        "hbm_frac_whole_step": ab / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "ms_per_step_hot_w": main_m.get("ms_per_step_hot_w"),
-        "ms_per_step_graph": main_m.get("ms_per_step_graph"),
+        "step": head,
+        "ceilings": ceil,
+        **legs,
     }
-    if "gemm_bf16_ms" in main_m:
-        g = main_m["gemm_bf16_ms"]
-        line["gemm_bf16"] = {"ms": g, "tokens_per_s": T / (g * 1e-3),
-                             "impl": "torch.matmul (hipBLASLt), same shape "
-                                     "and cache rotation"}
-        line["rho_measured"] = ms / g - 1.0
-        line["rho_pages"] = 1.0 / d_out + 3.0 / T
-    if sec is not None:
-        s_ms = sec["ms_per_step"]
-        k2 = max(sec["kernels_ms_avg"].values())
-        line["secondary_T128"] = {
-            "tokens_per_s": 128 / (s_ms * 1e-3), "ms_per_step": s_ms,
-            "fused_kernel_ms": k2,
-            "hbm_frac_kernel": alg_bytes(d, d_out, 128) / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_frac_kernel": alg_flops(d, d_out, 128) / (k2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "gemm_bf16_ms": sec.get("gemm_bf16_ms"),
-            "rho_measured": s_ms / sec["gemm_bf16_ms"] - 1.0 if sec.get("gemm_bf16_ms") else None,
-            "rho_pages": 1.0 / d_out + 3.0 / 128,
-            "kernels_ms_avg": sec["kernels_ms_avg"],
-        }
-    if fmts:
-        line["other_formats"] = fmts
-    if not a.only_ttq:
-        line["decode_from_codes"] = measure_decode(torch, ttq)
-        line["continuous_batching"] = measure_segmented(torch, ttq)
-        line["lowrank_pca"] = measure_pca(torch, ttq)
-    if not a.no_cpu and not a.only_ttq:
-        line["cpu_baseline"] = cpu_baseline(T, a.cpu_seconds, a.qformat)
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_c5(T, a.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -199,7 +199,8 @@ int ttq_linear_segmented(const ttq_params* prm, int64_t n_segments,
  * for one token (T = 1, d <= 12288, no path flag), 3 = two phase with the
  * weight tiles quantized inside the MFMA GEMM (129 <= T <= 256, d a
  * multiple of 128, group <= 128, no path flag; a call that asks for codes or
- * scales takes path 1).  Paths 1 and 3 give bit-identical Y.
+ * scales adds a pass over W that writes only them).  Paths 1 and 3 give
+ * bit-identical Y.
  * Negative = status. */
 int ttq_path(const ttq_params* prm, int64_t n_requests);
 

@@ -16,7 +16,8 @@ namespace ttq {
 
 constexpr int QROWS = 8;  // weight rows per wave (D^{+-1/2} reused across them)
 
-// CB = 0: write W_hat (and optional byte codes, scales, group offsets);
+// CB = 0: write W_hat (and optional byte codes, scales, group offsets; with
+// a null W_hat only those exports);
 // CB = 1, 2, 4, 8: write the codes packed in CB-bit containers instead of
 // W_hat (channel j of a row at bit (j*CB) % 8 of byte (j*CB) / 8).
 // QF: the quantizer format (QFmt; W_hat = bf16((c + s L) D^{-1/2})).
@@ -44,7 +45,8 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   const float Nf = a.Nf;
   const float* dhr = a.dh + (int64_t)r * a.d;
   const float* dhir = a.dhi + (int64_t)r * a.d;
-  bf16_t* What = a.What + (int64_t)r * a.d_out * a.d;
+  // What == null: the codes, scales and offsets only (no W_hat is written)
+  bf16_t* What = a.What ? a.What + (int64_t)r * a.d_out * a.d : nullptr;
   uint8_t* codes_out = a.codes_out ? a.codes_out + (int64_t)r * a.d_out * a.d : nullptr;
   float* s_out = a.s_out ? a.s_out + (int64_t)r * a.d_out * a.G : nullptr;
   float* m_out = a.m_out ? a.m_out + (int64_t)r * a.d_out * a.G : nullptr;
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     o.y = pack_bf16(fmaf(s, q[2], c) * dhi[2], fmaf(s, q[3], c) * dhi[3]);
     o.z = pack_bf16(fmaf(s, q[4], c) * dhi[4], fmaf(s, q[5], c) * dhi[5]);
     o.w = pack_bf16(fmaf(s, q[6], c) * dhi[6], fmaf(s, q[7], c) * dhi[7]);
-    *(u32x4*)(What + row * a.d + c0) = o;
+    if (What) *(u32x4*)(What + row * a.d + c0) = o;
     if (codes_out) {
       u32x2 cc;
       cc.x = qc[0] | (qc[1] << 8) | (qc[2] << 16) | (qc[3] << 24);

@@ -153,18 +153,20 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
   } else {
     plan_stats_split(P, R, T, d, take);
-    // W_hat of up to rchunk requests at a time (at most kMaxWhatBytes)
-    const int64_t per = (int64_t)sizeof(uint16_t) * dout * d;
-    P.rchunk = per > 0 ? kMaxWhatBytes / per : R;
-    if (P.rchunk < 1) P.rchunk = 1;
-    if (P.rchunk > R) P.rchunk = R;
-    P.off_what = take((size_t)(per * P.rchunk));
     if (P.rp > 0 && T > 0) plan_z_split(P, R * T, d, take);
-    // (W_hat stays in the plan: a call that asks for the codes takes the
-    // quantize pass)
     if (T <= kGemmQMaxT && gemm_q_supported(d, prm->group, 0) &&
-        !(prm->flags & TTQ_FLAG_FORCE_TWO_PHASE))
+        !(prm->flags & TTQ_FLAG_FORCE_TWO_PHASE)) {
+      // no W_hat: the GEMM quantizes its weight tiles itself (exports, when
+      // asked for, come from a quantize pass that writes only them)
       P.path = 3;
+    } else {
+      // W_hat of up to rchunk requests at a time (at most kMaxWhatBytes)
+      const int64_t per = (int64_t)sizeof(uint16_t) * dout * d;
+      P.rchunk = per > 0 ? kMaxWhatBytes / per : R;
+      if (P.rchunk < 1) P.rchunk = 1;
+      if (P.rchunk > R) P.rchunk = R;
+      P.off_what = take((size_t)(per * P.rchunk));
+    }
   }
   P.total = off;
   return P;
@@ -376,7 +378,17 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     st = enqueue_z_gemm(P, ws, Xb, Ab, R * T, d, rank, Zb, s);
     if (st != TTQ_OK) return st;
   }
-  if (P.path == 3 && !codes_out && !scales_out) {
+  if (P.path == 3) {
+    if (codes_out || scales_out) {
+      // the exports of every request, without W_hat
+      QuantArgs ea{};
+      ea.W = Wb; ea.d = d; ea.d_out = dout; ea.G = P.G; ea.R = (int)R; ea.Nf = Nf;
+      ea.dh = dh; ea.dhi = dhi; ea.What = nullptr;
+      ea.codes_out = codes_out; ea.s_out = scales_out; ea.m_out = mins_out;
+      ea.qf = (int)prm->qformat;
+      st = run(K_QUANT, s, [&](const Launch& L) { return launch_quant(ea, prm->group, L); });
+      if (st != TTQ_OK) return st;
+    }
     // every request in one launch, each with its own statistics
     GemmQArgs qa{};
     qa.X = Xb; qa.ldx = d; qa.W = Wb; qa.ldw = d;

@@ -208,6 +208,20 @@ def test_workspace_grows_with_shape():
     assert big >= 11008 * 256 * 2
 
 
+def test_gemm_quantizing_path_reserves_no_dequantized_weights():
+    # 8 requests of 256 tokens on an 8192 -> 28672 projection: the path that
+    # quantizes inside the GEMM needs statistics, Z and partial sums only,
+    # far less than one request's bf16 W_hat (470 MB)
+    p3 = prm(d=8192, d_out=28672, T=256, rank=128, group=64, bits=2)
+    assert ttq.ttq_path(p3, 8) == 3
+    ws = ttq.ttq_workspace_bytes(p3, 8)
+    assert ws < 28672 * 8192 * 2 // 8
+    # forcing the quantize pass brings W_hat back
+    p1 = prm(d=8192, d_out=28672, T=256, rank=128, group=64, bits=2,
+             flags=ttq.TTQ_FLAG_FORCE_TWO_PHASE)
+    assert ttq.ttq_workspace_bytes(p1, 8) >= ws + 28672 * 8192 * 2
+
+
 def test_timing_api_without_launches():
     L = lib()
     n = L.ttq_kernel_count()
