@@ -297,7 +297,12 @@ int ttq_timing_query(int kernel, double* total_ms, int64_t* launches);
  * by randomized subspace iteration (Halko, Martinsson and Tropp, 2011):
  * Q = orth(M Omega), then `iters` times Z = orth(M^T Q), Q = orth(M Z), with
  * orth = CholeskyQR (float32 panels, float64 Cholesky; two passes for the
- * final basis, one for the intermediate panels), B = Q.
+ * final basis, one for the intermediate panels), B = Q.  When M has rank
+ * below `rank` (e.g. W = 0) the columns past the rank are not determined by
+ * M: a column whose Gram pivot is at the float32 noise level (1e-5 of the
+ * largest) is dropped, and in the first pass of the final basis replaced by
+ * a pseudo-random column before the second pass,
+ * so B is orthonormal in every case (A and Wres do not depend on the choice).
  *   prm     d, d_out >= 1; rank in {8, 16, 32, 64, 128}, <= min(d, d_out);
  *           T >= 0 (T > 0 needs d % 8 == 0); bits, group, flags and qformat
  *           are not read

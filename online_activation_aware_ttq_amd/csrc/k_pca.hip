@@ -204,14 +204,26 @@ __global__ __launch_bounds__(256) void k_psum(PsumArgs a) {
   }
 }
 
+// A Gram pivot at or below this fraction of the largest diagonal entry is
+// numerical noise (G is summed in float32: its relative rounding is about
+// 1e-5 for the longest panels): the column carries no direction of its own.
+// It is dropped -- its column of L, and its row and column of R^{-1}, are
+// zero, so that column of Q = Y R^{-1} is zero and no other column depends on
+// it -- and flagged, so that the final basis can be completed.  (Eliminating
+// with such a pivot would amplify rounding noise by 1/sqrt(pivot) and can
+// overflow.)
+constexpr double kPivotDropTol = 1e-5;
+
 // G (n x n, float32, symmetric up to rounding) -> R with G = R^T R, R upper
 // triangular with a positive diagonal, Cholesky in float64 (right-looking,
 // one barrier per step: row k is kept unscaled while the trailing matrix is
 // updated with L[k][i] L[k][j] / pivot, and every row is scaled by 1/sqrt of
-// its pivot at the end).  A pivot below 1e-14 of the largest diagonal entry
-// is raised to that floor (a rank-deficient panel: the second CholeskyQR
-// pass then re-normalises).  LDS rows have an odd stride n + 1.
-__global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
+// its pivot at the end).  A pivot at or below kPivotDropTol of the largest
+// diagonal entry drops its column (row k of R and R[k][k] are zero) and,
+// when `defic` is given, is flagged there (1 for a dropped column, else 0).
+// LDS rows have an odd stride n + 1.
+__global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n,
+                                              int* defic) {
   extern __shared__ double L[];  // n rows of n + 1, then the n pivots
   const int ld = n + 1;
   double* piv = L + n * ld;
@@ -228,11 +240,15 @@ __global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
     dmax = m > 0.0 ? m : 1.0;
   }
   __syncthreads();
-  const double floor = 1e-14 * dmax;
+  const double tol = kPivotDropTol * dmax;
   for (int k = 0; k < n; ++k) {
-    const double pk = fmax(L[k * ld + k], floor);
-    if (t == 0) piv[k] = pk;
-    const double inv = 1.0 / pk;
+    const double raw = L[k * ld + k];
+    const bool drop = !(raw > tol);
+    if (t == 0) {
+      piv[k] = drop ? 0.0 : raw;
+      if (defic) defic[k] = drop ? 1 : 0;
+    }
+    const double inv = drop ? 0.0 : 1.0 / raw;
     // row k does not change in step k: this lane's entries of it go to
     // registers, and each row's reads are issued before its writes (n - k - 1
     // <= 127 columns: 8 per lane cover them)
@@ -260,8 +276,9 @@ __global__ __launch_bounds__(256) void k_chol(const float* G, float* R, int n) {
   }
   for (int e = t; e < n * n; e += 256) {
     const int i = e / n, j = e % n;
-    R[e] = i < j ? (float)(L[i * ld + j] / sqrt(piv[i]))
-                 : (i == j ? (float)sqrt(piv[i]) : 0.f);
+    R[e] = piv[i] > 0.0 && i <= j
+               ? (i < j ? (float)(L[i * ld + j] / sqrt(piv[i])) : (float)sqrt(piv[i]))
+               : 0.f;
   }
 }
 
@@ -298,7 +315,8 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 }
 
 template <int N>
-__global__ __launch_bounds__(256) void k_cholinv(const float* G, float* Rinv) {
+__global__ __launch_bounds__(256) void k_cholinv(const float* G, float* Rinv,
+                                                 int* defic) {
   constexpr int NQ = N / 4;
   __shared__ double col[2][64];    // step k broadcasts through col[k & 1]
   __shared__ double Lt[N][N + 2];  // Lt[i][m] = L[m][i]
@@ -311,17 +329,20 @@ __global__ __launch_bounds__(256) void k_cholinv(const float* G, float* Rinv) {
     const int j = w + 4 * q;
     g[q] = live ? 0.5 * ((double)G[l * N + j] + (double)G[j * N + l]) : 0.0;
   }
-  // pivot floor: 1e-14 of the largest diagonal entry
+  // pivots at or below kPivotDropTol of the largest diagonal entry drop
+  // their column
   double dmax = live ? (double)G[l * N + l] : 0.0;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, off));
-  const double floor = 1e-14 * (dmax > 0.0 ? dmax : 1.0);
+  const double tol = kPivotDropTol * (dmax > 0.0 ? dmax : 1.0);
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     if (w == (k & 3)) {  // the wave holding column k
-      const double pk = fmax(bcast(g[k >> 2], k), floor);
-      const double ir = rsqrt_f64(pk);
-      const double lik = (l == k) ? pk * ir : g[k >> 2] * ir;
+      const double raw = bcast(g[k >> 2], k);
+      const bool drop = !(raw > tol);
+      if (defic && l == 0) defic[k] = drop ? 1 : 0;
+      const double ir = drop ? 0.0 : rsqrt_f64(raw);
+      const double lik = (l == k) ? raw * ir : g[k >> 2] * ir;
       g[k >> 2] = lik;  // L[l][k] (meaningful for l >= k)
       col[k & 1][l] = lik;
       if (l == 0) dinv[k] = ir;
@@ -355,6 +376,33 @@ __global__ __launch_bounds__(256) void k_cholinv(const float* G, float* Rinv) {
   }
 }
 
+// Completion of a basis whose Gram matrix had dropped pivots (a panel of
+// rank below n, e.g. from an all-zero M): each flagged column k of V
+// [m][n] is replaced by a pseudo-random column of entries +-1/sqrt(m) (signs
+// from a counter-based hash of (row, k)), which the next CholeskyQR pass
+// orthonormalises against the others.  Unflagged columns are not touched, so
+// a full-rank panel passes through unchanged.
+__device__ __forceinline__ uint32_t hash_rc(uint32_t i, uint32_t k) {
+  uint32_t h = i * 0x9E3779B1u ^ (k + 0x7F4A7C15u) * 0x85EBCA77u;
+  h ^= h >> 16; h *= 0x7FEB352Du;
+  h ^= h >> 15; h *= 0x846CA68Bu;
+  h ^= h >> 16;
+  return h;
+}
+__global__ __launch_bounds__(256) void k_pca_complete(float* V, int64_t m, int n,
+                                                      const int* defic) {
+  __shared__ int flag[128];
+  const int t = threadIdx.x;
+  const int f = t < n ? defic[t] : 0;
+  if (t < n) flag[t] = f;
+  if (!__syncthreads_or(f)) return;   // full-rank panel: nothing to do
+  const int64_t i = (int64_t)blockIdx.x * 256 + t;
+  if (i >= m) return;
+  const float sc = 1.0f / sqrtf((float)m);
+  for (int k = 0; k < n; ++k)
+    if (flag[k]) V[i * n + k] = (hash_rc((uint32_t)i, (uint32_t)k) & 1u) ? sc : -sc;
+}
+
 // Q = Y R^{-1} in place, one row of Y per thread by forward substitution:
 //   q_c = (y_c - sum_{m<c} q_m R[m][c]) / R[c][c]
 // R is staged transposed (row c holds column c of R, its diagonal entry
@@ -366,7 +414,9 @@ __global__ __launch_bounds__(64) void k_trsm(float* Y, const float* R, int64_t m
   const int t = threadIdx.x;
   for (int e = t; e < N * N; e += 64) {
     const int c = e / N, k = e % N;  // sRt[c][k] = R[k][c]
-    sRt[c][k] = c == k ? 1.0f / R[k * N + c] : (k < c ? R[k * N + c] : 0.f);
+    // a dropped column has R[c][c] = 0: its q_c is zero
+    const float rd = R[k * N + c];
+    sRt[c][k] = c == k ? (rd > 0.f ? 1.0f / rd : 0.f) : (k < c ? rd : 0.f);
   }
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * 64 + t;
@@ -516,22 +566,31 @@ hipError_t launch_psum(const PsumArgs& a, const Launch& L) {
   return ext_launch(k_psum, dim3((unsigned)blocks), dim3(256), 0, L, a);
 }
 
-hipError_t launch_chol(const float* G, float* R, int n, const Launch& L) {
+hipError_t launch_pca_complete(float* V, int64_t m, int n, const int* defic,
+                               const Launch& L) {
+  if (m <= 0 || n <= 0 || n > 128) return m <= 0 ? hipSuccess : hipErrorInvalidValue;
+  return ext_launch(k_pca_complete, dim3((unsigned)((m + 255) / 256)), dim3(256), 0,
+                    L, V, m, n, defic);
+}
+
+hipError_t launch_chol(const float* G, float* R, int n, int* defic,
+                       const Launch& L) {
   if (n <= 0 || n > 128) return hipErrorInvalidValue;
   const uint32_t lds = (uint32_t)((n * (n + 1) + n) * sizeof(double));
   static hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k_chol),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)((128 * 129 + 128) * sizeof(double)));
   if (attr != hipSuccess) return attr;
-  return ext_launch(k_chol, dim3(1), dim3(256), lds, L, G, R, n);
+  return ext_launch(k_chol, dim3(1), dim3(256), lds, L, G, R, n, defic);
 }
 
-hipError_t launch_cholinv(const float* G, float* Rinv, int n, const Launch& L) {
+hipError_t launch_cholinv(const float* G, float* Rinv, int n, int* defic,
+                          const Launch& L) {
   switch (n) {
-    case 8: return ext_launch(k_cholinv<8>, dim3(1), dim3(256), 0, L, G, Rinv);
-    case 16: return ext_launch(k_cholinv<16>, dim3(1), dim3(256), 0, L, G, Rinv);
-    case 32: return ext_launch(k_cholinv<32>, dim3(1), dim3(256), 0, L, G, Rinv);
-    case 64: return ext_launch(k_cholinv<64>, dim3(1), dim3(256), 0, L, G, Rinv);
+    case 8: return ext_launch(k_cholinv<8>, dim3(1), dim3(256), 0, L, G, Rinv, defic);
+    case 16: return ext_launch(k_cholinv<16>, dim3(1), dim3(256), 0, L, G, Rinv, defic);
+    case 32: return ext_launch(k_cholinv<32>, dim3(1), dim3(256), 0, L, G, Rinv, defic);
+    case 64: return ext_launch(k_cholinv<64>, dim3(1), dim3(256), 0, L, G, Rinv, defic);
     default: return hipErrorInvalidValue;
   }
 }

@@ -190,7 +190,8 @@ const char* kKernelNames[K_NUM_KINDS] = {
     "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
     "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant", "seg_copy",
-    "pca_skinny", "pca_psum", "pca_chol", "pca_trsm", "pca_residual"};
+    "pca_skinny", "pca_psum", "pca_chol", "pca_trsm", "pca_residual",
+    "pca_complete"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -894,7 +895,7 @@ int validate_pca(const ttq_params* prm, int32_t iters) {
 struct PcaPlan {
   int sp_nt = 1, sp_tn = 1, sp_gy = 1, sp_gz = 1;  // splits of the products
   size_t off_dh = 0, off_dhi = 0, off_statp = 0, off_y = 0, off_z = 0,
-         off_part = 0, off_g = 0, off_r = 0;
+         off_part = 0, off_g = 0, off_r = 0, off_def = 0;
   Plan stats;  // token slices of the norm partials (T > kFusedMaxT)
   size_t total = 0;
 };
@@ -936,6 +937,7 @@ PcaPlan make_pca_plan(const ttq_params* prm) {
   P.off_part = take(part);
   P.off_g = take(sizeof(float) * n * n);
   P.off_r = take(sizeof(float) * n * n);
+  P.off_def = take(sizeof(int) * n);
   P.total = off;
   return P;
 }
@@ -966,6 +968,7 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
   float* part = reinterpret_cast<float*>(ws + P.off_part);
   float* G = reinterpret_cast<float*>(ws + P.off_g);
   float* Rf = reinterpret_cast<float*>(ws + P.off_r);
+  int* defic = reinterpret_cast<int*>(ws + P.off_def);
   const float* dh = nullptr;
 
   if (T > 0) {  // D of the current activations, as in ttq_linear
@@ -1012,20 +1015,27 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
   };
   // CholeskyQR of the float32 panel V [m][n], in place: two passes for the
   // final basis (CholeskyQR2), one for the intermediate panels of the power
-  // iteration, which only carry the subspace to the next product
+  // iteration, which only carry the subspace to the next product.  Between
+  // the two passes of the final basis, columns whose pivot was dropped (a
+  // panel of rank below n) are replaced by pseudo-random columns, so the
+  // second pass returns n orthonormal columns in every case.
   auto orth = [&](float* V, int64_t m, int sp_gram, int passes) -> int {
     for (int pass = 0; pass < passes; ++pass) {
+      int* df = passes == 2 && pass == 0 ? defic : nullptr;
       int r = product(true, false, V, n, nullptr, n, m, V, sp_gram, G, nullptr, nullptr);
       if (r != TTQ_OK) return r;
       if (n <= 64) {  // R^{-1} in one wave, then V R^{-1} as a product
-        r = run(K_CHOL, s, [&](const Launch& L) { return launch_cholinv(G, Rf, (int)n, L); });
+        r = run(K_CHOL, s, [&](const Launch& L) { return launch_cholinv(G, Rf, (int)n, df, L); });
         if (r != TTQ_OK) return r;
         r = product(false, false, V, n, nullptr, m, n, Rf, 1, V, nullptr, nullptr);
       } else {
-        r = run(K_CHOL, s, [&](const Launch& L) { return launch_chol(G, Rf, (int)n, L); });
+        r = run(K_CHOL, s, [&](const Launch& L) { return launch_chol(G, Rf, (int)n, df, L); });
         if (r != TTQ_OK) return r;
         r = run(K_TRSM, s, [&](const Launch& L) { return launch_trsm(V, Rf, m, (int)n, L); });
       }
+      if (r != TTQ_OK) return r;
+      if (df)
+        r = run(K_PCA_COMPLETE, s, [&](const Launch& L) { return launch_pca_complete(V, m, (int)n, df, L); });
       if (r != TTQ_OK) return r;
     }
     return TTQ_OK;

@@ -37,6 +37,7 @@ enum KernelKind {
   K_CHOL,              // PCA: Cholesky factor of a Gram matrix
   K_TRSM,              // PCA: panel times the inverse Cholesky factor
   K_LR_RESIDUAL,       // PCA: W - B A in bf16
+  K_PCA_COMPLETE,      // PCA: completion of a rank-deficient basis
   K_NUM_KINDS
 };
 
@@ -543,10 +544,16 @@ struct PsumArgs {
 hipError_t launch_psum(const PsumArgs& a, const Launch& L);
 // Cholesky factor R (upper, G = R^T R) of an n x n Gram matrix (n <= 128),
 // and Y[m][n] <- Y R^{-1} in place
-hipError_t launch_chol(const float* G, float* R, int n, const Launch& L);
+// (defic, optional: n flags, 1 where the pivot was raised to the floor)
+hipError_t launch_chol(const float* G, float* R, int n, int* defic,
+                       const Launch& L);
 hipError_t launch_trsm(float* Y, const float* R, int64_t m, int n, const Launch& L);
 // n <= 64: R^{-1} of the Cholesky factor in one wave (float64 registers)
-hipError_t launch_cholinv(const float* G, float* Rinv, int n, const Launch& L);
+hipError_t launch_cholinv(const float* G, float* Rinv, int n, int* defic,
+                          const Launch& L);
+// flagged columns of V [m][n] <- pseudo-random +-1/sqrt(m) columns (n <= 128)
+hipError_t launch_pca_complete(float* V, int64_t m, int n, const int* defic,
+                               const Launch& L);
 struct LrResidualArgs {
   const bf16_t* W;        // [d_out][d]
   const bf16_t* B;        // [d_out][n]

@@ -150,15 +150,50 @@ def test_pca_is_deterministic():
 
 
 def test_degenerate_inputs():
-    """An all-zero W (a singular Gram matrix at every step: the pivot floor)
-    gives zero factors and a zero residual, no NaN; a square W of full rank
-    r = d_out is reproduced by its factors (residual at the rounding level)."""
+    """Rank-deficient inputs.  With an all-zero W every Gram pivot hits the
+    floor; B is then completed to an orthonormal basis (any orthonormal B is
+    a valid principal basis of a zero matrix, so B itself is checked for
+    orthonormality only), and A = B^T W and the residual are compared with
+    the oracle's (both exactly zero).  A W of exact rank 4 with r = 16: the
+    rank-4 principal subspace is unique and both B's must contain it; the
+    other 12 columns are arbitrary but must stay orthonormal; A and the
+    residual (zero up to the bf16 rounding of the factors) match the
+    oracle's.  A square W of full rank r = d_out is reproduced by its
+    factors."""
     Z = np.zeros((64, 128), dtype=np.uint16)
     Om = draw_omega(41, 128, 16)
     Bg, Ag, Rg = _gpu_pca(Z, Om, 2)
-    for x in (Bg, Ag, Rg):
-        v = oracle.bf16_to_f64(x)
-        assert np.all(np.isfinite(v)) and not np.any(v)
+    ref = oracle.lowrank_pca(Z, Om, 2)
+    B = oracle.bf16_to_f64(Bg)
+    assert np.all(np.isfinite(B))
+    np.testing.assert_allclose(B.T @ B, np.eye(16), atol=2e-2)
+    np.testing.assert_allclose(ref["B"].T @ ref["B"], np.eye(16), atol=1e-12)
+    np.testing.assert_array_equal(oracle.bf16_to_f64(Ag), ref["A"])
+    np.testing.assert_array_equal(oracle.bf16_to_f64(Rg), ref["R"])
+    # exact rank 4 (small integers: W is exact in bf16)
+    rng = np.random.default_rng(7)
+    U = rng.integers(-3, 4, (96, 4)).astype(np.float32)
+    V = rng.integers(-3, 4, (4, 128)).astype(np.float32)
+    from workloads.configs import bf16_round_bits
+    W4b = bf16_round_bits(U @ V)
+    assert np.array_equal(oracle.bf16_to_f64(W4b), U @ V)
+    Om4 = draw_omega(44, 128, 16)
+    Bg, Ag, Rg = _gpu_pca(W4b, Om4, 1)
+    ref = oracle.lowrank_pca(W4b, Om4, 1)
+    W4 = U.astype(np.float64) @ V
+    B = oracle.bf16_to_f64(Bg)
+    np.testing.assert_allclose(B.T @ B, np.eye(16), atol=2e-2)
+    scale = np.linalg.norm(W4)
+    for Bx in (B, ref["B"]):   # both contain the unique rank-4 subspace
+        assert np.linalg.norm(W4 - Bx @ (Bx.T @ W4)) <= 1e-2 * scale
+    # the first 4 columns orthonormalise the same 4 independent columns of
+    # M Z (positive R diagonal): unique, equal up to rounding
+    np.testing.assert_allclose(B[:, :4], ref["B"][:, :4], atol=2e-2)
+    np.testing.assert_allclose(oracle.bf16_to_f64(Ag)[:4], ref["A"][:4],
+                               atol=2e-2 * np.abs(ref["A"][:4]).max())
+    # residual: zero up to the bf16 rounding of the factors (oracle: exact)
+    assert np.linalg.norm(ref["R"]) <= 1e-9 * scale
+    assert np.linalg.norm(oracle.bf16_to_f64(Rg) - ref["R"]) <= 1e-2 * scale
     from workloads.configs import bf16_round_bits
     rng = np.random.default_rng(42)
     Wb = bf16_round_bits((rng.standard_normal((32, 96)) * 0.05).astype(np.float32))
