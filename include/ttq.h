@@ -159,6 +159,29 @@ int ttq_linear_batched(const ttq_params* prm, int64_t n_requests,
                        float* scales_out, float* mins_out, float* dhalf_out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- allocation-free variant ----------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as ttq_linear_batched (n_requests = 1 is ttq_linear),
+ * minus the workspace: the library takes it from a static device array of
+ * TTQ_NOALLOC_SCRATCH_BYTES that every GPU it runs on holds until the process
+ * ends (its address is looked up on the first call on each device, with that
+ * device current).  The call allocates nothing, frees nothing and calls no
+ * allocating routine.  All calls on one GPU share that GPU's array, which
+ * keeps the last call's contents (no kernel needs it cleared): calls that
+ * overlap on one GPU -- concurrent streams or threads -- race and must be
+ * serialised by the caller.
+ * Errors: as ttq_linear_batched, plus TTQ_EWORKSPACE when the call needs more
+ * scratch than TTQ_NOALLOC_SCRATCH_BYTES (ttq_workspace_bytes gives the need;
+ * checked on the host, nothing is enqueued), and TTQ_EHIP when the array's
+ * address cannot be obtained. */
+#define TTQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ttq_linear_noalloc(const ttq_params* prm, int64_t n_requests,
+                       const void* W, const void* X, const void* B,
+                       const void* A, float* Y, uint8_t* codes_out,
+                       float* scales_out, float* mins_out, float* dhalf_out,
+                       void* stream);
+
 /* ---- continuous batching: requests of different lengths in one X --------
  * n_segments requests packed one after another: request i owns the token
  * rows seg_offsets[i] .. seg_offsets[i+1]-1 of X [T][d] and Y [T][d_out],

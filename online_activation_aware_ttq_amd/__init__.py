@@ -28,6 +28,8 @@ from ._binding import (  # noqa: F401
     timing_reset,
     ttq_linear,
     ttq_linear_batched,
+    ttq_linear_noalloc,
+    TTQ_NOALLOC_SCRATCH_BYTES,
     ttq_linear_segmented,
     ttq_lowrank_pca,
     ttq_lowrank_pca_workspace_bytes,

@@ -35,6 +35,8 @@ EXPORTS = {
     "ttq_linear_batched": (_c.c_int, [_vp, _c.c_int64, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
                                       _vp]),
+    "ttq_linear_noalloc": (_c.c_int, [_vp, _c.c_int64, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp]),
     "ttq_path": (_c.c_int, [_vp, _c.c_int64]),
     "ttq_segmented_workspace_bytes": (_c.c_int, [_vp, _c.c_int64, _vp,
                                                  _c.POINTER(_c.c_size_t)]),
@@ -228,7 +230,7 @@ def _check(t, name, dtype, shape, device):
 
 def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
           codes_out, scales_out, mins_out, dhalf_out, workspace, stream,
-          flags, qformat):
+          flags, qformat, noalloc=False):
     import torch
     lib = load_library()
     if batched:
@@ -259,6 +261,13 @@ def _call(batched: bool, W, X, B, A, *, p, lam, alpha, bits, group, Y,
     _check(dhalf_out, "dhalf_out", torch.float32, lead + (d,), dev)
     if stream is None:
         stream = _current_stream(dev)
+    if noalloc:
+        args = [_ptr(W), _ptr(X), _ptr(B), _ptr(A), _ptr(Y), _ptr(codes_out),
+                _ptr(scales_out), _ptr(mins_out), _ptr(dhalf_out), stream]
+        st = lib.ttq_linear_noalloc(ctypes.byref(prm), R, *args)
+        if st != TTQ_OK:
+            raise TTQError(st, "ttq_linear_noalloc")
+        return Y
     if workspace is None:  # (a given workspace is checked by the library)
         workspace = _workspace(dev, stream, ("linear", key, R),
                                lambda: ttq_workspace_bytes(prm, R))
@@ -299,6 +308,24 @@ def ttq_linear_batched(W, X, B=None, A=None, *, p: float, lam: float,
                  group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
                  mins_out=mins_out, dhalf_out=dhalf_out, workspace=workspace,
                  stream=stream, flags=flags, qformat=qformat)
+
+
+def ttq_linear_noalloc(W, X, B=None, A=None, *, p: float, lam: float,
+                       alpha: float, bits: int, group: int, Y,
+                       codes_out=None, scales_out=None, mins_out=None,
+                       dhalf_out=None, stream=None, flags: int = 0,
+                       qformat="asym"):
+    """ttq_linear_batched (X [R, T, d]) on the library's static scratch: no
+    workspace and no allocation; Y must be given (see include/ttq.h)."""
+    if Y is None:
+        raise ValueError("ttq_linear_noalloc needs a preallocated Y")
+    return _call(True, W, X, B, A, p=p, lam=lam, alpha=alpha, bits=bits,
+                 group=group, Y=Y, codes_out=codes_out, scales_out=scales_out,
+                 mins_out=mins_out, dhalf_out=dhalf_out, workspace=None,
+                 stream=stream, flags=flags, qformat=qformat, noalloc=True)
+
+
+TTQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def _offsets(seg_offsets):

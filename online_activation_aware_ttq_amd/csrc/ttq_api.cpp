@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -1070,9 +1071,63 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
   return run(K_LR_RESIDUAL, s, [&](const Launch& L) { return launch_lr_residual(ra, (int)n, L); });
 }
 
+// ------------------------------------------- allocation-free entry point
+// Scratch for callers that cannot allocate: one array per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in symbol): its device address is looked up once
+// per device with that device current, and that pointer is what the kernels
+// receive.  Calls that overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = TTQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// device address of this device's scratch array (looked up on first use)
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return TTQ_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return TTQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return TTQ_EHIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ttq_linear_noalloc(const ttq_params* prm, int64_t n_requests,
+                       const void* W, const void* X, const void* B,
+                       const void* A, float* Y, uint8_t* codes_out,
+                       float* scales_out, float* mins_out, float* dhalf_out,
+                       void* stream) {
+  // the plan's size is checked on the host before anything touches HIP
+  int st = validate_params(prm, n_requests);
+  if (st != TTQ_OK) return st;
+  if (n_requests == 0) return TTQ_OK;
+  const size_t need = make_plan(prm, n_requests).total;
+  if (need > kScratchBytes) return TTQ_EWORKSPACE;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != TTQ_OK) return st;
+  return linear_impl(prm, n_requests, W, X, B, A, Y, codes_out, scales_out,
+                     mins_out, dhalf_out, ws, kScratchBytes, stream);
+}
 
 int ttq_workspace_bytes(const ttq_params* prm, int64_t n_requests,
                         size_t* bytes) {

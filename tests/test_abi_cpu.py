@@ -222,6 +222,21 @@ def test_gemm_quantizing_path_reserves_no_dequantized_weights():
     assert ttq.ttq_workspace_bytes(p1, 8) >= ws + 28672 * 8192 * 2
 
 
+def test_noalloc_checks_size_before_touching_the_device():
+    L = lib()
+    # validation as for the batched call
+    assert L.ttq_linear_noalloc(None, 1, *([None] * 9), None) == ttq.TTQ_ENULL
+    assert L.ttq_linear_noalloc(ctypes.byref(prm(bits=9)), 1, *([None] * 9),
+                                None) == ttq.TTQ_EINVAL
+    assert L.ttq_linear_noalloc(ctypes.byref(prm()), 0, *([None] * 9),
+                                None) == ttq.TTQ_OK
+    # a plan beyond the static scratch is refused on the host
+    big = prm(d=4096, d_out=11008, T=4096, rank=32)
+    assert ttq.ttq_workspace_bytes(big, 8) > ttq.TTQ_NOALLOC_SCRATCH_BYTES
+    assert L.ttq_linear_noalloc(ctypes.byref(big), 8, *([FAKE] * 5),
+                                None, None, None, None, None) == ttq.TTQ_EWORKSPACE
+
+
 def test_timing_api_without_launches():
     L = lib()
     n = L.ttq_kernel_count()
