@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libttq.so")
+# TTQ_LIBRARY selects another build of the same library (the CPU tests use
+# it for a host build with address and undefined-behaviour sanitizers)
+LIB_PATH = os.environ.get("TTQ_LIBRARY") or os.path.join(PKG_DIR, "libttq.so")
 
 TTQ_OK = 0
 TTQ_EINVAL = -1

@@ -94,5 +94,50 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
     return LIB_PATH
 
 
+def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """``libttq.so`` with the host layer (``ttq_api.cpp``: validation,
+    planning, workspace offsets) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the kernel objects of the regular
+    build (``build()`` first).  Loaded through ``TTQ_LIBRARY`` with the ASan
+    runtime preloaded (``asan_runtime()``); only host code is instrumented."""
+    objs = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s != "ttq_api.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"kernel objects missing ({missing[0]}): run build() first")
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = os.path.join(out_dir, "ttq_api_san.o")
+    flags = [f for f in COMMON_FLAGS if f != "-O3"] + ["-O1", "-g"]
+    cmd = [_hipcc(), "-x", "hip", *flags, *san, "-c",
+           os.path.join(CSRC, "ttq_api.cpp"), "-o", api_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        print(res.stdout + res.stderr, file=sys.stderr)
+        raise RuntimeError("hipcc failed on the sanitized ttq_api.cpp")
+    lib = os.path.join(out_dir, "libttq.so")
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", lib,
+           api_obj, *objs, *san[:4], "-shared-libsan"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        print(res.stdout + res.stderr, file=sys.stderr)
+        raise RuntimeError("linking the sanitized libttq.so failed")
+    return lib
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that a sanitized build needs preloaded."""
+    out = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True).stdout.strip()
+    if out and os.path.exists(out):
+        return out
+    import glob
+    cands = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    if not cands:
+        raise RuntimeError("the ASan runtime (libclang_rt.asan-x86_64.so) was not found")
+    return cands[0]
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
