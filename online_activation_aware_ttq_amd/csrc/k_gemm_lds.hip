@@ -23,10 +23,13 @@
 //    stalls the issuing wave; spread out they hide behind the matrix core);
 //  * fragment reads for the next 16-channel step are interleaved with the
 //    MFMAs of the current one (register double buffer).
-// Workgroups are ordered so that the M tiles of one weight tile run back to
-// back on the same XCD (shared through that XCD's L2); narrower outputs are
-// spread over all XCDs.  A batch of independent products (one per request,
-// each with its own W_hat) is the second grid dimension.
+// Tile order: the output tiles of all products of the batch are laid out in
+// strips of 8 N tiles (row by row inside a strip), and each of the 8 XCDs
+// (workgroups id, id + 8, ...) takes one contiguous eighth of that order, so
+// that the ~32 workgroups an XCD runs at once cover a patch of about 4 M x 8 N
+// tiles whose operand slices its L2 shares, and a partial last round is
+// spread evenly over the XCDs.  Operand loads carry the device-scope cache
+// bit (sc0; measured slightly faster than the default here).
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -43,17 +46,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// strip width of the tile order (N tiles)
+constexpr int kStripN = 8;
+
 // TM x TN MFMA tiles of 32 x 32 per wave, WGM x WGN waves, NS LDS stages.
 template <int TM, int TN, int WGM, int WGN, int NS>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
-  if (blockIdx.y > 0) {  // product z of a batch
-    const int64_t z = blockIdx.y;
-    a.A1 += z * a.sA1;
-    a.B1 += z * a.sB1;
-    if (a.A2) a.A2 += z * a.sA2;
-    if (a.B2) a.B2 += z * a.sB2;
-    a.C += z * a.sC;
-  }
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32, BK = 64;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
@@ -67,18 +65,26 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
 
   const int64_t mtiles = (a.M + BM - 1) / BM;
   const int64_t ntiles = (a.N_store + BN - 1) / BN;
-  const int64_t id = blockIdx.x;
-  int64_t ntile, mtile;
-  if (ntiles >= 8) {
-    const int xcd = (int)(id & 7);
-    const int64_t j = id >> 3;
-    ntile = (j / mtiles) * 8 + xcd;
-    mtile = j % mtiles;
-  } else {
-    ntile = id % ntiles;
-    mtile = id / ntiles;
+  const int64_t per_product = mtiles * ntiles;
+  const int64_t nprod = a.batch > 1 ? a.batch : 1;
+  const int64_t total = per_product * nprod;
+  // this XCD's contiguous share of the tile order, then the tile
+  const int64_t xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int64_t base = total >> 3, extra = total & 7;
+  if (j >= base + (xcd < extra ? 1 : 0)) return;
+  const int64_t t = xcd * base + min(xcd, extra) + j;
+  const int64_t z = t / per_product, tz = t % per_product;
+  const int64_t strip = tz / (kStripN * mtiles), in_strip = tz % (kStripN * mtiles);
+  const int64_t width = min((int64_t)kStripN, ntiles - strip * kStripN);
+  const int64_t mtile = in_strip / width;
+  const int64_t ntile = strip * kStripN + in_strip % width;
+  if (z > 0) {  // product z of a batch
+    a.A1 += z * a.sA1;
+    a.B1 += z * a.sB1;
+    if (a.A2) a.A2 += z * a.sA2;
+    if (a.B2) a.B2 += z * a.sB2;
+    a.C += z * a.sC;
   }
-  if (ntile >= ntiles || mtile >= mtiles) return;
   const int64_t m0 = mtile * BM, n0 = ntile * BN;
   const int64_t mrows = min((int64_t)BM, a.M - m0);
   const int64_t nrows = max((int64_t)0, min((int64_t)BN, a.N - n0));
@@ -119,12 +125,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
     for (int j = 0; j < NLA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void*)(sa + (w + j * NW) * 1024),
-          16, va, (uint32_t)(j * 8 * NW * lda * 2), 0, 0);
+          16, va, (uint32_t)(j * 8 * NW * lda * 2), 0, 1);
 #pragma unroll
     for (int j = 0; j < NLB; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb, (__attribute__((address_space(3))) void*)(sb + (w + j * NW) * 1024),
-          16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 0);
+          16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 1);
   };
 
   f32x16 acc[TM][TN];
@@ -229,27 +235,29 @@ hipError_t launch_t(const GemmArgs& a, const Launch& L) {
   static_assert(lds <= 160 * 1024, "LDS");
   const int64_t mtiles = (a.M + BM - 1) / BM;
   const int64_t ntiles = (a.N_store + BN - 1) / BN;
-  const int64_t nblk =
-      ntiles >= 8 ? ((ntiles + 7) / 8) * 8 * mtiles : ntiles * mtiles;
+  const int64_t total = mtiles * ntiles * (a.batch > 1 ? a.batch : 1);
+  const int64_t nblk = (total + 7) / 8 * 8;
   if (nblk == 0) return hipSuccess;
   // more than 64 KB of dynamic LDS must be allowed per kernel (idempotent)
   static hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k_gemm_lds<TM, TN, WGM, WGN, NS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  const unsigned nb = a.batch > 1 ? (unsigned)a.batch : 1u;
-  return ext_launch(k_gemm_lds<TM, TN, WGM, WGN, NS>, dim3((unsigned)nblk, nb),
+  return ext_launch(k_gemm_lds<TM, TN, WGM, WGN, NS>, dim3((unsigned)nblk),
                     dim3(WGM * WGN * 64), lds, L, a);
 }
 
 }  // namespace
 
 int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
-  // 256 x 256 tiles keep the most MFMA work per LDS byte; when they would
-  // leave a quarter of the 256 CUs idle in a single round, 256 x 128 tiles
-  // give twice as many workgroups
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256) * batch;
-  return big >= 192 ? 0 : 1;
+  // 256 x 256 tiles move the fewest operand bytes per flop; 256 x 128 tiles
+  // give twice as many workgroups, each costing about 0.57 of a big one
+  // (measured on the 7B-class shapes).  Take the one whose rounds of 256
+  // workgroups (one per CU) cost less: a partial last round costs a full one.
+  const int64_t mt = (M + 255) / 256;
+  const int64_t r256 = (mt * ((N + 255) / 256) * batch + 255) / 256;
+  const int64_t r128 = (mt * ((N + 127) / 128) * batch + 255) / 256;
+  return r128 * 57 < r256 * 100 ? 1 : 0;
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L) {

@@ -16,12 +16,50 @@ namespace ttq {
 
 constexpr int QROWS = 8;  // weight rows per wave (D^{+-1/2} reused across them)
 
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                      false));
+}
+
+// min and max over the LPG consecutive lanes of a group: DPP inside each row
+// of 16 lanes (quad xor 1 and 2, then the mirrors of 8 and of 16 lanes, each
+// of which pairs a lane with one in the other half), a shuffle across rows
+template <int LPG>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+  mn = fminf(mn, dpp<0xB1>(mn));   // quad_perm [1,0,3,2]
+  mx = fmaxf(mx, dpp<0xB1>(mx));
+  if constexpr (LPG >= 4) {
+    mn = fminf(mn, dpp<0x4E>(mn));   // quad_perm [2,3,0,1]
+    mx = fmaxf(mx, dpp<0x4E>(mx));
+  }
+  if constexpr (LPG >= 8) {
+    mn = fminf(mn, dpp<0x141>(mn));  // row_half_mirror
+    mx = fmaxf(mx, dpp<0x141>(mx));
+  }
+  if constexpr (LPG >= 16) {
+    mn = fminf(mn, dpp<0x140>(mn));  // row_mirror
+    mx = fmaxf(mx, dpp<0x140>(mx));
+  }
+  if constexpr (LPG >= 32) {
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+  }
+}
+
+}  // namespace
+
 // CB = 0: write W_hat (and optional byte codes, scales, group offsets; with
 // a null W_hat only those exports);
 // CB = 1, 2, 4, 8: write the codes packed in CB-bit containers instead of
 // W_hat (channel j of a row at bit (j*CB) % 8 of byte (j*CB) / 8).
 // QF: the quantizer format (QFmt; W_hat = bf16((c + s L) D^{-1/2})).
-template <int GS, int CB, int QF>
+// EXP (CB = 0): codes, scales and offsets are asked for; without them the
+// integer codes are not formed.
+template <int GS, int CB, int QF, bool EXP>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   constexpr int LPG = GS / 8;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -46,7 +84,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   const float* dhr = a.dh + (int64_t)r * a.d;
   const float* dhir = a.dhi + (int64_t)r * a.d;
   // What == null: the codes, scales and offsets only (no W_hat is written)
-  bf16_t* What = a.What ? a.What + (int64_t)r * a.d_out * a.d : nullptr;
+  bf16_t* What = a.What ? a.What + (int64_t)r * a.d_out * a.ldwh : nullptr;
   uint8_t* codes_out = a.codes_out ? a.codes_out + (int64_t)r * a.d_out * a.d : nullptr;
   float* s_out = a.s_out ? a.s_out + (int64_t)r * a.d_out * a.G : nullptr;
   float* m_out = a.m_out ? a.m_out + (int64_t)r * a.d_out * a.G : nullptr;
@@ -87,18 +125,16 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
       mn = fminf(mn, u[j]);
       mx = fmaxf(mx, u[j]);
     }
-#pragma unroll
-    for (int off = LPG / 2; off > 0; off >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off));
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-    }
+    group_minmax<LPG>(mn, mx);
     const QGroup gq = qgroup<QF>(mn, mx, Nf);
     const float s = gq.s;
     float q[8];
     unsigned qc[8];
     qlevels8<QF>(gq, u, q);
+    if constexpr (CB > 0 || EXP) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qc[j] = qcode<QF>(gq, q[j]);
+      for (int j = 0; j < 8; ++j) qc[j] = qcode<QF>(gq, q[j]);
+    }
     if (!live || row >= a.d_out) continue;
     if (CB > 0) {
       // 8 codes of this lane -> 8*CB bits, one aligned store
@@ -130,17 +166,19 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     o.y = pack_bf16(fmaf(s, q[2], c) * dhi[2], fmaf(s, q[3], c) * dhi[3]);
     o.z = pack_bf16(fmaf(s, q[4], c) * dhi[4], fmaf(s, q[5], c) * dhi[5]);
     o.w = pack_bf16(fmaf(s, q[6], c) * dhi[6], fmaf(s, q[7], c) * dhi[7]);
-    if (What) *(u32x4*)(What + row * a.d + c0) = o;
-    if (codes_out) {
-      u32x2 cc;
-      cc.x = qc[0] | (qc[1] << 8) | (qc[2] << 16) | (qc[3] << 24);
-      cc.y = qc[4] | (qc[5] << 8) | (qc[6] << 16) | (qc[7] << 24);
-      *(u32x2*)(codes_out + row * a.d + c0) = cc;
-    }
-    if (s_out && (l % LPG) == 0) {
-      const int64_t o2 = row * a.G + c0 / GS;
-      s_out[o2] = s;
-      m_out[o2] = gq.off;
+    if (What) *(u32x4*)(What + row * a.ldwh + c0) = o;
+    if constexpr (EXP) {
+      if (codes_out) {
+        u32x2 cc;
+        cc.x = qc[0] | (qc[1] << 8) | (qc[2] << 16) | (qc[3] << 24);
+        cc.y = qc[4] | (qc[5] << 8) | (qc[6] << 16) | (qc[7] << 24);
+        *(u32x2*)(codes_out + row * a.d + c0) = cc;
+      }
+      if (s_out && (l % LPG) == 0) {
+        const int64_t o2 = row * a.G + c0 / GS;
+        s_out[o2] = s;
+        m_out[o2] = gq.off;
+      }
     }
   }
 }
@@ -151,13 +189,16 @@ hipError_t launch_quant(const QuantArgs& a, int group, const Launch& L) {
   const int64_t nblk1 = (waves + 3) / 4;
   if (nblk1 == 0 || a.R == 0) return hipSuccess;
   const dim3 grid((unsigned)(((nblk1 + 7) / 8) * 8 * a.R)), blk(256);
+  const bool exp = a.codes_out != nullptr || a.s_out != nullptr;
 #define TTQ_QUANT_CB(GSV, QF)                                                  \
   switch (a.packed ? a.cb : 0) {                                               \
-    case 0: return ext_launch(k_quant<GSV, 0, QF>, grid, blk, 0, L, a);        \
-    case 1: return ext_launch(k_quant<GSV, 1, QF>, grid, blk, 0, L, a);        \
-    case 2: return ext_launch(k_quant<GSV, 2, QF>, grid, blk, 0, L, a);        \
-    case 4: return ext_launch(k_quant<GSV, 4, QF>, grid, blk, 0, L, a);        \
-    case 8: return ext_launch(k_quant<GSV, 8, QF>, grid, blk, 0, L, a);        \
+    case 0:                                                                    \
+      return exp ? ext_launch(k_quant<GSV, 0, QF, true>, grid, blk, 0, L, a)   \
+                 : ext_launch(k_quant<GSV, 0, QF, false>, grid, blk, 0, L, a); \
+    case 1: return ext_launch(k_quant<GSV, 1, QF, true>, grid, blk, 0, L, a);  \
+    case 2: return ext_launch(k_quant<GSV, 2, QF, true>, grid, blk, 0, L, a);  \
+    case 4: return ext_launch(k_quant<GSV, 4, QF, true>, grid, blk, 0, L, a);  \
+    case 8: return ext_launch(k_quant<GSV, 8, QF, true>, grid, blk, 0, L, a);  \
     default: return hipErrorInvalidValue;                                      \
   }
 #define TTQ_QUANT_GS(GSV)                                                      \

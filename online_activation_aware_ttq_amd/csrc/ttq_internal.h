@@ -369,7 +369,8 @@ struct QuantArgs {
   float Nf;
   const float* dh;      // [R][d]
   const float* dhi;     // [R][d]
-  bf16_t* What;         // [R][d_out][d]
+  bf16_t* What;         // [R][d_out][ldwh]
+  int64_t ldwh;         // row stride of W_hat (elements, >= d)
   uint8_t* codes_out;   // [R][d_out][d]
   float* s_out;         // [R][d_out][G]
   float* m_out;         // [R][d_out][G]
@@ -437,6 +438,13 @@ struct QFusedArgs {
 };
 hipError_t launch_qfused(const QFusedArgs& a, int ntb, int group, int cb,
                          const Launch& L);
+
+// Row stride of the W_hat written by the quantize pass for the GEMM: d plus
+// 64 elements, so that the rows of one 64-channel slice fall in different L2
+// channels (with d a multiple of a power of two the rows of a tile slice
+// would otherwise map to few channels; measured 6-11 % on the GEMM).
+constexpr int64_t kWhatPad = 64;
+inline int64_t what_ld(int64_t d) { return d + kWhatPad; }
 
 // C[M][N] (+)= A1[M][K1] B1[N][K1]^T + A2[M][K2] B2[N][K2]^T, fp32 accumulate.
 struct GemmArgs {
