@@ -683,14 +683,34 @@ def leg_name(a) -> str:
     return a.leg
 
 
+def _stats_table(stats) -> list:
+    lines = ["## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
+             "| kernel | calls | avg ns | min ns | max ns | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | "
+                     f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r.get('Percentage', 0) or 0):.1f} |")
+    return lines
+
+
 def summarize(a):
     """profiles/: kernel-trace summary of one kernel on one workload and its
     HBM traffic per launch from FETCH_SIZE / WRITE_SIZE, each scaled by what
     the same counter reads for a device-to-device copy of known size."""
     trace, fetch, write = a.summarize
-    kind = a.kernel
-    key = KERNEL_SYMBOLS[kind]
+    kind = a.kernel or a.leg
     stats = _read_csv(trace, "kernel_stats.csv")
+    leg = leg_name(a)
+    if fetch == "-" or write == "-":   # kernel trace only (no counters)
+        lines = [f"# kernel trace of the {leg} workload", "",
+                 "Commands (from the repository root):", "", "```"]
+        lines += [c for c in a.profile_cmd.split(";;") if c] + ["```", ""]
+        lines += _stats_table(stats)
+        open(os.path.join(ROOT, "profiles", f"trace_{leg}.md"), "w").write(
+            "\n".join(lines))
+        return
+    key = KERNEL_SYMBOLS[kind]
     calib_bytes = a.copy_calib_mb * 2 ** 20
     fr = _read_csv(fetch, "counter_collection.csv")
     wr = _read_csv(write, "counter_collection.csv")
@@ -713,7 +733,6 @@ def summarize(a):
     f_kib = sum(k_f) / max(1, len(k_f))
     w_kib = sum(k_w) / max(1, len(k_w))
     traffic = f_kib * 1024 * sf + w_kib * 1024 * sw
-    leg = leg_name(a)
     rec = {"kernel": kind, "workload": leg, "kernel_src_sha": kernel_src_sha(kind),
            "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
            "copy_calib_bytes": calib_bytes, "copy_fetch_kib": c_f,
@@ -723,14 +742,8 @@ def summarize(a):
     json.dump(rec, open(traffic_file(kind, leg), "w"), indent=1)
     lines = [f"# {kind} on {leg}", "", "Commands (from the repository root):",
              "", "```"]
-    lines += [c for c in a.profile_cmd.split(";;") if c] + [
-        "```", "", "## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
-        "| kernel | calls | avg ns | min ns | max ns | share % |",
-        "|---|---|---|---|---|---|"]
-    for r in stats:
-        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | "
-                     f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
-                     f"{float(r.get('Percentage', 0) or 0):.1f} |")
+    lines += [c for c in a.profile_cmd.split(";;") if c] + ["```", ""]
+    lines += _stats_table(stats)
     lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
               f"- {kind}: FETCH_SIZE {f_kib:.0f} KiB/launch, WRITE_SIZE "
               f"{w_kib:.1f} KiB/launch (averaged over {len(k_f)} / {len(k_w)} "
