@@ -49,8 +49,26 @@ __device__ __forceinline__ void wait_vm() {
 // strip width of the tile order (N tiles)
 constexpr int kStripN = 8;
 
+// Step schedules (SCHED):
+//  kDoubleBuf: fragments for the next 16-channel step are read while the
+//    current one is contracted (two register sets); the loads of tile kt+NS
+//    go out after the barrier in the last step of tile kt;
+//  kSingleBuf: one register set, each step reads its fragments and then
+//    contracts them; the loads of tile kt+NS-1 are spread over the MFMAs of
+//    the first step of tile kt, right after the barrier that retired the
+//    stage they overwrite;
+//  kSingleBufSplit: the same, with the A loads in the first step and the B
+//    loads in the second.
+// Every schedule runs the same MFMAs in the same order on every output, so
+// the result does not depend on it.  Measured (256 x 256 tiles): with many
+// rounds of workgroups per CU (7B-class layer, 8 requests x 4096 tokens)
+// kSingleBuf takes 6-9 % less time than kDoubleBuf; with one partial round
+// (70B-class up projection, T = 512) kSingleBuf is 15 % slower and
+// kSingleBufSplit 4 % faster.
+constexpr int kDoubleBuf = 0, kSingleBuf = 1, kSingleBufSplit = 2;
+
 // TM x TN MFMA tiles of 32 x 32 per wave, WGM x WGN waves, NS LDS stages.
-template <int TM, int TN, int WGM, int WGN, int NS>
+template <int TM, int TN, int WGM, int WGN, int NS, int SCHED>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32, BK = 64;
@@ -104,7 +122,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
 
   // Tiles at or past nk read nothing: both segments put every lane out of
   // range (zero fill into a stage that is not read again).
-  auto issue = [&](int kt, int stage) {
+  // part: 1 = A loads, 2 = B loads, 3 = both
+  auto issue = [&](int kt, int stage, int part) {
     const bool seg2 = kt >= nk1;
     const bf16_t* Ap = seg2 ? a.A2 : a.A1;
     const bf16_t* Bp = seg2 ? a.B2 : a.B1;
@@ -121,16 +140,20 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
         kin ? (uint32_t)(((w * 8 + lrow) * ldb + k0 + lch * 8) * 2) : kOutOfRange;
     unsigned char* sa = smem + stage * STAGE;
     unsigned char* sb = sa + ABYTES;
+    if (part & 1) {
 #pragma unroll
-    for (int j = 0; j < NLA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(sa + (w + j * NW) * 1024),
-          16, va, (uint32_t)(j * 8 * NW * lda * 2), 0, 1);
+      for (int j = 0; j < NLA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(sa + (w + j * NW) * 1024),
+            16, va, (uint32_t)(j * 8 * NW * lda * 2), 0, 1);
+    }
+    if (part & 2) {
 #pragma unroll
-    for (int j = 0; j < NLB; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(sb + (w + j * NW) * 1024),
-          16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 1);
+      for (int j = 0; j < NLB; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(sb + (w + j * NW) * 1024),
+            16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 1);
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -147,7 +170,6 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
   const int fh = l >> 5;
   const int arow = (wm * TM * 32 + (l & 31)) * 128;
   const int brow = (wn * TN * 32 + (l & 31)) * 128;
-  u32x4 fa[2][TM], fb[2][TN];
   auto read_frags = [&](int stage, int kk, u32x4* A_, u32x4* B_) {
     const unsigned char* sa = smem + stage * STAGE;
     const unsigned char* sb = sa + ABYTES;
@@ -167,47 +189,100 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
             acc[i][j], 0, 0, 0);
   };
 
-  // prologue: tiles 0 .. NS-2 in flight, wait for tile 0
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue(p, p);
-  wait_vm<(NS - 2) * NL>();
-  lds_barrier();
-  read_frags(0, 0, fa[0], fb[0]);
-  issue(NS - 1, NS - 1);
-
   constexpr int NMF = TM * TN;
-  constexpr int PR = (TM + TN + NMF - 1) / NMF;   // fragment reads per MFMA
-  constexpr int PL = (NL + NMF - 1) / NMF;        // tile loads per MFMA
-  int stage = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int nstage = stage + 1 == NS ? 0 : stage + 1;
+  if constexpr (SCHED == kDoubleBuf) {
+    u32x4 fa[2][TM], fb[2][TN];
+    // prologue: tiles 0 .. NS-2 in flight, wait for tile 0
 #pragma unroll
-    for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-      const int cur = kk & 1;
-      read_frags(stage, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      mfmas(fa[cur], fb[cur]);
+    for (int p = 0; p < NS - 1; ++p) issue(p, p, 3);
+    wait_vm<(NS - 2) * NL>();
+    lds_barrier();
+    read_frags(0, 0, fa[0], fb[0]);
+    issue(NS - 1, NS - 1, 3);
+
+    constexpr int PR = (TM + TN + NMF - 1) / NMF;   // fragment reads per MFMA
+    constexpr int PL = (NL + NMF - 1) / NMF;        // tile loads per MFMA
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int nstage = stage + 1 == NS ? 0 : stage + 1;
 #pragma unroll
-      for (int q = 0; q < NMF; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, PR, 0);  // DS read
+      for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+        const int cur = kk & 1;
+        read_frags(stage, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        mfmas(fa[cur], fb[cur]);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, PR, 0);  // DS read
+        }
       }
+      {
+        constexpr int cur = (BK / 16 - 1) & 1;
+        // tile kt+1 landed (NS-2 younger tiles may still be in flight)
+        wait_vm<(NS - 2) * NL>();
+        lds_barrier();   // ... for every wave; all reads of stage kt done
+        read_frags(nstage, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        issue(kt + NS, stage, 3);
+        mfmas(fa[cur], fb[cur]);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, PR, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x020, PL, 0);  // VMEM read
+        }
+      }
+      stage = nstage;
     }
-    {
-      constexpr int cur = (BK / 16 - 1) & 1;
-      // tile kt+1 landed (NS-2 younger tiles may still be in flight)
+  } else {
+    u32x4 fa[TM], fb[TN];
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) issue(p, p, 3);
+    wait_vm<(NS - 2) * NL>();
+    lds_barrier();
+    constexpr int PL = (NL + NMF - 1) / NMF;
+    constexpr int PA = (NLA + NMF - 1) / NMF, PB = (NLB + NMF - 1) / NMF;
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      // the stage tile kt-1 used was retired by the last barrier
+      const int pstage = stage == 0 ? NS - 1 : stage - 1;
+      if constexpr (SCHED == kSingleBuf) {
+        read_frags(stage, 0, fa, fb);
+        issue(kt + NS - 1, pstage, 3);
+        mfmas(fa, fb);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, PL, 0);  // VMEM read
+        }
+      } else {
+        read_frags(stage, 0, fa, fb);
+        issue(kt + NS - 1, pstage, 1);
+        mfmas(fa, fb);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, PA, 0);
+        }
+        read_frags(stage, 1, fa, fb);
+        issue(kt + NS - 1, pstage, 2);
+        mfmas(fa, fb);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, PB, 0);
+        }
+      }
+#pragma unroll
+      for (int kk = SCHED == kSingleBuf ? 1 : 2; kk < BK / 16; ++kk) {
+        read_frags(stage, kk, fa, fb);
+        mfmas(fa, fb);
+      }
+      // tile kt+1 landed (NS-2 younger tiles may still be in flight), and
+      // every wave is done with this stage
       wait_vm<(NS - 2) * NL>();
-      lds_barrier();   // ... for every wave; all reads of stage kt done
-      read_frags(nstage, 0, fa[cur ^ 1], fb[cur ^ 1]);
-      issue(kt + NS, stage);
-      mfmas(fa[cur], fb[cur]);
-#pragma unroll
-      for (int q = 0; q < NMF; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, PR, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x020, PL, 0);  // VMEM read
-      }
+      lds_barrier();
+      stage = stage + 1 == NS ? 0 : stage + 1;
     }
-    stage = nstage;
   }
   // the loads issued past the last tile read nothing, but they still write
   // LDS: let them retire before the workgroup ends
@@ -228,7 +303,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
       }
 }
 
-template <int TM, int TN, int WGM, int WGN, int NS>
+template <int TM, int TN, int WGM, int WGN, int NS, int SCHED>
 hipError_t launch_t(const GemmArgs& a, const Launch& L) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   constexpr int lds = NS * (BM + BN) * 64 * 2;
@@ -240,10 +315,10 @@ hipError_t launch_t(const GemmArgs& a, const Launch& L) {
   if (nblk == 0) return hipSuccess;
   // more than 64 KB of dynamic LDS must be allowed per kernel (idempotent)
   static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(k_gemm_lds<TM, TN, WGM, WGN, NS>),
+      reinterpret_cast<const void*>(k_gemm_lds<TM, TN, WGM, WGN, NS, SCHED>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  return ext_launch(k_gemm_lds<TM, TN, WGM, WGN, NS>, dim3((unsigned)nblk),
+  return ext_launch(k_gemm_lds<TM, TN, WGM, WGN, NS, SCHED>, dim3((unsigned)nblk),
                     dim3(WGM * WGN * 64), lds, L, a);
 }
 
@@ -254,18 +329,26 @@ int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
   // give twice as many workgroups, each costing about 0.57 of a big one
   // (measured on the 7B-class shapes).  Take the one whose rounds of 256
   // workgroups (one per CU) cost less: a partial last round costs a full one.
+  // 256 x 256 tiles use the single-buffered step schedule from four rounds
+  // on, its split-load form below that.
   const int64_t mt = (M + 255) / 256;
   const int64_t r256 = (mt * ((N + 255) / 256) * batch + 255) / 256;
   const int64_t r128 = (mt * ((N + 127) / 128) * batch + 255) / 256;
-  return r128 * 57 < r256 * 100 ? 1 : 0;
+  if (r128 * 57 < r256 * 100) return 1;
+  return r256 >= 4 ? 0 : 2;
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L) {
   if (a.M <= 0 || a.N_store <= 0) return hipSuccess;
   if (a.K1 <= 0 || !a.C || a.nsplit > 1) return hipErrorInvalidValue;
-  if (gemm_lds_config(a.M, a.N_store, a.batch > 1 ? a.batch : 1) == 0)
-    return launch_t<4, 2, 2, 4, 2>(a, L);   // 256 x 256, 8 waves, 2 stages
-  return launch_t<2, 2, 4, 2, 3>(a, L);     // 256 x 128, 8 waves, 3 stages
+  switch (gemm_lds_config(a.M, a.N_store, a.batch > 1 ? a.batch : 1)) {
+    case 0:  // 256 x 256, 8 waves, 2 stages
+      return launch_t<4, 2, 2, 4, 2, kSingleBuf>(a, L);
+    case 2:
+      return launch_t<4, 2, 2, 4, 2, kSingleBufSplit>(a, L);
+    default:  // 256 x 128, 8 waves, 3 stages
+      return launch_t<2, 2, 4, 2, 3, kDoubleBuf>(a, L);
+  }
 }
 
 }  // namespace ttq

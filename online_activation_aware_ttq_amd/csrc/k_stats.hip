@@ -222,6 +222,14 @@ hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
 // float64 partial per block; a finalize pass sums the block partials in
 // order (deterministic).
 // ---------------------------------------------------------------------------
+// The p mode is a template parameter: with the general-p branch in the loop
+// the kernel needs 160 VGPRs (3 waves per SIMD) and streamed X at about
+// 3.8 TB/s; the p = 2 instantiation (54 VGPRs) reads it at 5.8 TB/s, against
+// 7.2 TB/s for a plain read kernel (8 requests x 4096 tokens x 4096
+// channels).  Non-temporal loads read faster still (6.4 TB/s) but leave X
+// out of the last-level cache, and the low-rank product that reads X next
+// then took 104 instead of 66 us: the loads stay plain.
+template <int PM>
 __global__ __launch_bounds__(256) void k_stats_partial(StatsSplitArgs a) {
   __shared__ double red[4][512];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -239,14 +247,14 @@ __global__ __launch_bounds__(256) void k_stats_partial(StatsSplitArgs a) {
       u32x4 v1 = *(const u32x4*)(X + (t + 1) * a.d + c0);
       u32x4 v2 = *(const u32x4*)(X + (t + 2) * a.d + c0);
       u32x4 v3 = *(const u32x4*)(X + (t + 3) * a.d + c0);
-      accum8(acc, v0, a.pmode, a.p);
-      accum8(acc, v1, a.pmode, a.p);
-      accum8(acc, v2, a.pmode, a.p);
-      accum8(acc, v3, a.pmode, a.p);
+      accum8(acc, v0, PM, a.p);
+      accum8(acc, v1, PM, a.p);
+      accum8(acc, v2, PM, a.p);
+      accum8(acc, v3, PM, a.p);
     }
     for (; t < t1; ++t) {
       u32x4 v = *(const u32x4*)(X + t * a.d + c0);
-      accum8(acc, v, a.pmode, a.p);
+      accum8(acc, v, PM, a.p);
     }
   }
 #pragma unroll
@@ -292,7 +300,9 @@ hipError_t launch_stats_partial(const StatsSplitArgs& a, int R,
   if (a.nsplit == 0) return hipSuccess;
   dim3 grid((unsigned)((a.d + 511) / 512), (unsigned)((a.nsplit + 3) / 4),
             (unsigned)R);
-  return ext_launch(k_stats_partial, grid, dim3(256), 0, L, a);
+  if (a.pmode == 2) return ext_launch(k_stats_partial<2>, grid, dim3(256), 0, L, a);
+  if (a.pmode == 1) return ext_launch(k_stats_partial<1>, grid, dim3(256), 0, L, a);
+  return ext_launch(k_stats_partial<0>, grid, dim3(256), 0, L, a);
 }
 
 hipError_t launch_stats_final(const StatsSplitArgs& a, int R, const Launch& L) {
