@@ -64,7 +64,12 @@ def test_c4_up_proj(p):
     _check(wc.make_c4(p))
 
 
-@pytest.mark.parametrize("T,proj", [(1, "q_proj"), (16, "gate_proj"),
-                                    (256, "down_proj"), (4096, "o_proj")])
+# every projection shape at every token count of the layer at least once,
+# the three shapes of the headline token count (4096) all at full size
+@pytest.mark.parametrize("T,proj", [(1, "q_proj"), (1, "down_proj"),
+                                    (16, "gate_proj"), (16, "k_proj"),
+                                    (256, "down_proj"), (256, "up_proj"),
+                                    (256, "v_proj"), (4096, "o_proj"),
+                                    (4096, "gate_proj"), (4096, "down_proj")])
 def test_c5_layer_requests(T, proj):
     _check(wc.make_c5(T, proj))
