@@ -45,8 +45,14 @@ def _check(prob):
     full = run_gpu(prob, exports=True, rows=rows)
     rep = check_problem(prob, full, rows=rows)
     _say(prob.name + " (exports)", rep)
-    # the two launches compute the same Y
-    np.testing.assert_allclose(plain["Y"], full["Y"], rtol=1e-5, atol=1e-6)
+    # the two launches compute the same Y up to the fp32 summation order (the
+    # one-token kernel's export instantiation splits the contraction over 8
+    # instead of 16 waves): error per element relative to max(|Y|, RMS of the
+    # token's row), the scale of the Y bars
+    yp, yf = np.asarray(plain["Y"], np.float64), np.asarray(full["Y"], np.float64)
+    rms = np.sqrt(np.mean(yf * yf, axis=-1, keepdims=True))
+    e = np.abs(yp - yf) / np.maximum(np.maximum(np.abs(yf), rms), 1e-30)
+    assert e.max() <= 1e-4, e.max()
 
 
 @pytest.mark.parametrize("T", [1, 128])
