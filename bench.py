@@ -45,12 +45,12 @@ FORMAT_NAMES = {"asym": "asymmetric", "sym": "symmetric",
 KERNEL_SOURCES = {"gemv_t1": "k_gemv.hip", "fused_qdq_mfma": "k_fused.hip",
                   "stats_small": "k_stats.hip", "gemm_mfma": "k_gemm_lds.hip",
                   "quant_what": "k_quant.hip", "gemm_quant": "k_gemm_q.hip",
-                  "qgemv": "k_qgemv.hip", "stats_partial": "k_stats.hip"}
+                  "qgemv": "k_qgemv.hip", "stats_z": "k_stats.hip"}
 # timing-kind name -> substring of the HIP kernel symbol in rocprofv3 output
 KERNEL_SYMBOLS = {"gemv_t1": "k_gemv", "fused_qdq_mfma": "k_fused",
                   "gemm_mfma": "k_gemm_lds", "quant_what": "k_quant",
                   "gemm_quant": "k_gemm_q", "qgemv": "k_qgemv",
-                  "stats_small": "k_stats_small", "stats_partial": "k_stats_partial"}
+                  "stats_small": "k_stats_small", "stats_z": "k_stats_z"}
 C5_PROJ = (("q_proj", 4096, 4096), ("k_proj", 4096, 4096),
            ("v_proj", 4096, 4096), ("o_proj", 4096, 4096),
            ("gate_proj", 4096, 11008), ("up_proj", 4096, 11008),

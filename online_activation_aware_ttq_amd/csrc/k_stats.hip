@@ -217,66 +217,246 @@ hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {
 }
 
 // ---------------------------------------------------------------------------
-// Large T: each wave reduces one slice of tokens for 512 channels; the four
-// waves of a block add their slices in LDS in slice order and write one
-// float64 partial per block; a finalize pass sums the block partials in
-// order (deterministic).
+// Large T: one workgroup (8 waves) per 64-token block of a request and range
+// of channels.  X streams through LDS in chunks of 512 channels with
+// buffer_load ... lds (two 64 KiB stages, the GEMM's swizzled 128-byte rows,
+// channel block j of a chunk at j * 8 KiB), and every chunk is used twice:
+//  * statistics: wave w owns the 64 channels of block w, lane (o, g) the
+//    channels 8o .. 8o+7 of the tokens g, g+8, ..., g+56; float64 sums of
+//    |x|^p over those tokens, then over the eight token groups (DPP, fixed
+//    order), one float64 partial per channel and block;
+//  * low rank (optional): wave w contracts its channel block with the same
+//    channels of A on v_mfma_f32_32x32x16_bf16 (both 32-token halves of the
+//    block, rank tiles of 32), accumulating over all chunks; the eight waves'
+//    products are added in LDS in wave order and Z is rounded once to bf16
+//    (or stored as a float32 partial of the channel range).
+// So X is read once for both, and the token block's Z needs no partials
+// when one range covers all channels.  The result depends on d, T and the
+// channel ranges only: a request's statistics are the same in any batch.
 // ---------------------------------------------------------------------------
-// The p mode is a template parameter: with the general-p branch in the loop
-// the kernel needs 160 VGPRs (3 waves per SIMD) and streamed X at about
-// 3.8 TB/s; the p = 2 instantiation (54 VGPRs) reads it at 5.8 TB/s, against
-// 7.2 TB/s for a plain read kernel (8 requests x 4096 tokens x 4096
-// channels).  Non-temporal loads read faster still (6.4 TB/s) but leave X
-// out of the last-level cache, and the low-rank product that reads X next
-// then took 104 instead of 66 us: the loads stay plain.
-template <int PM>
-__global__ __launch_bounds__(256) void k_stats_partial(StatsSplitArgs a) {
-  __shared__ double red[4][512];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int split = blockIdx.y * 4 + w;
-  const int r = blockIdx.z;
-  const int64_t c0 = (int64_t)blockIdx.x * 512 + l * 8;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (split < a.nsplit && c0 < a.d) {
-    const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
-    const int64_t t0 = (int64_t)split * a.tchunk;
-    const int64_t t1 = min(a.T, t0 + a.tchunk);
-    int64_t t = t0;
-    for (; t + 4 <= t1; t += 4) {
-      u32x4 v0 = *(const u32x4*)(X + (t + 0) * a.d + c0);
-      u32x4 v1 = *(const u32x4*)(X + (t + 1) * a.d + c0);
-      u32x4 v2 = *(const u32x4*)(X + (t + 2) * a.d + c0);
-      u32x4 v3 = *(const u32x4*)(X + (t + 3) * a.d + c0);
-      accum8(acc, v0, PM, a.p);
-      accum8(acc, v1, PM, a.p);
-      accum8(acc, v2, PM, a.p);
-      accum8(acc, v3, PM, a.p);
-    }
-    for (; t < t1; ++t) {
-      u32x4 v = *(const u32x4*)(X + t * a.d + c0);
-      accum8(acc, v, PM, a.p);
-    }
-  }
+namespace {
+
+constexpr int kZTB = 64;                    // tokens per workgroup
+constexpr int kZCW = 512;                   // channels per chunk
+constexpr int kZStage = kZTB * kZCW * 2;    // 64 KiB
+
+__device__ __forceinline__ int zswz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+template <int N>
+__device__ __forceinline__ void zwait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+}  // namespace
+
+// PM: p mode (2, 1, 0 = general p); RT: rank tiles of 32 (0 = statistics only)
+template <int PM, int RT>
+__global__ __launch_bounds__(512, 1) void k_stats_z(StatsZArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t b = blockIdx.x;
+  const int split = (int)(b % a.csplit);
+  b /= a.csplit;
+  const int64_t tb = b % a.ntb, r = b / a.ntb;
+  const int64_t t0 = tb * kZTB;
+  const int64_t trows = min((int64_t)kZTB, a.T - t0);
+  const int64_t cbeg = (int64_t)split * a.cps * kZCW;
+  const int64_t cend = min(a.d, cbeg + (int64_t)a.cps * kZCW);
+  const int nck = (int)((cend - cbeg + kZCW - 1) / kZCW);
+  // rows past the block's tokens read as zeros (no traffic)
+  const auto rx = make_rsrc(a.X + (r * a.T + t0) * a.d, (uint32_t)(trows * a.d * 2));
+
+  // loads: wave w, instruction j fills rows 8w .. 8w+7 of channel block j;
+  // lane l writes row 8w + l/8, physical chunk l%8 = logical (l%8)^zswz(row)
+  const int lrow = w * 8 + (l >> 3);
+  const int lch = (l & 7) ^ zswz(lrow);
+  auto issue = [&](int kc, int stage) {
+    const int64_t cb0 = cbeg + (int64_t)kc * kZCW;
+    unsigned char* st = smem + stage * kZStage + w * 1024;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[w][l * 8 + j] = acc[j];
-  __syncthreads();
-  const int64_t nb = (a.nsplit + 3) / 4;
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int64_t c = (int64_t)blockIdx.x * 512 + i;
-    if (c < a.d) {
-      const double v = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
-      a.partial[((int64_t)r * nb + blockIdx.y) * a.d + c] = v;
+    for (int j = 0; j < 8; ++j) {
+      const int64_t c = cb0 + j * 64 + lch * 8;
+      const uint32_t vo =
+          (kc < nck && c < cend) ? (uint32_t)((lrow * a.d + c) * 2) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(st + j * 8192), 16, vo, 0, 0, 0);
     }
+  };
+
+  // statistics lanes: token group g, channel octet o of block w
+  const int g = l & 7, o = l >> 3;
+  // low-rank lanes: MFMA row l%32, 8-channel half l/32 of each 16-channel step
+  const auto ra = make_rsrc(a.A, (uint32_t)((int64_t)a.rank * a.d * 2));
+  constexpr int NZ = RT > 0 ? RT : 1;
+  f32x16 zacc[2][NZ];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int rt = 0; rt < NZ; ++rt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) zacc[tt][rt][q] = 0.f;
+
+  issue(0, 0);
+  for (int kc = 0; kc < nck; ++kc) {
+    const int stage = kc & 1;
+    const int64_t cb0 = cbeg + (int64_t)kc * kZCW;
+    // the rank rows' channels of this chunk (their latency hides behind the
+    // statistics work); channels past the range meet zero activations
+    u32x4 bfr[NZ][4];
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int64_t c = cb0 + w * 64 + kk * 16 + (l >> 5) * 8;
+          const int row = rt * 32 + (l & 31);
+          const uint32_t vo = c < cend ? (uint32_t)((row * a.d + c) * 2) : kOutOfRange;
+          bfr[rt][kk] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, vo, 0, 0));
+        }
+    }
+    // the next chunk into the other stage (retired by the last barrier)
+    issue(kc + 1, stage ^ 1);
+    // this chunk landed (the rank loads and the next chunk may be in flight)
+    zwait_vm<8 + 4 * RT>();
+    lds_barrier();
+    const unsigned char* st = smem + stage * kZStage + w * 8192;
+    if constexpr (PM >= 0) {
+      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = i * 8 + g;
+        const u32x4 v = *(const u32x4*)(st + row * 128 + ((o ^ zswz(row)) * 16));
+        accum8(acc, v, PM, a.p);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[j] = acc[j] + dpp64<0xB1>(acc[j]);    // quad_perm [1,0,3,2]
+        acc[j] = acc[j] + dpp64<0x4E>(acc[j]);    // quad_perm [2,3,0,1]
+        acc[j] = acc[j] + dpp64<0x141>(acc[j]);   // row_half_mirror
+      }
+      const int64_t c = cb0 + w * 64 + o * 8;
+      if (g == 0 && c < cend) {
+        double* P = a.partial + (r * a.ntb + tb) * a.d + c;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          typedef __attribute__((ext_vector_type(2))) double d2;
+          *(d2*)(P + j) = d2{acc[j], acc[j + 1]};
+        }
+      }
+    }
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 af[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int row = tt * 32 + (l & 31);
+          const int ch = ((kk << 1) | (l >> 5)) ^ zswz(row);
+          af[tt] = *(const u32x4*)(st + row * 128 + ch * 16);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            zacc[tt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, af[tt]), __builtin_bit_cast(bf16x8, bfr[rt][kk]),
+                zacc[tt][rt], 0, 0, 0);
+      }
+    }
+    lds_barrier();   // every wave is done with this stage
+  }
+  // the load issued past the last chunk still writes LDS
+  zwait_vm<0>();
+  lds_barrier();
+
+  if constexpr (RT > 0) {
+    // the eight waves' products, added in wave order
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        // C layout of a 32x32 tile: lane l holds column l%32 and rows
+        // 8*(q/4) + 4*(l/32) + q%4
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
+          red[w * 1024 + m * 32 + (l & 31)] = zacc[tt][rt][q];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int oi = tid + h * 512;
+          float v = red[oi];
+#pragma unroll
+          for (int ww = 1; ww < 8; ++ww) v += red[ww * 1024 + oi];
+          const int64_t tok = t0 + tt * 32 + (oi >> 5);
+          if (tok < a.T) {
+            const int64_t zi = (r * a.T + tok) * a.rp + rt * 32 + (oi & 31);
+            if (a.csplit == 1)
+              a.Z[zi] = (bf16_t)f2bf(v);
+            else
+              a.Zpart[(int64_t)split * a.zslice + zi] = v;
+          }
+        }
+        lds_barrier();
+      }
   }
 }
 
+size_t stats_z_lds_bytes() { return 2 * (size_t)kZStage; }
+
+namespace {
+template <int PM, int RT>
+hipError_t launch_sz(const StatsZArgs& a, unsigned nblk, const Launch& L) {
+  constexpr uint32_t lds = 2 * kZStage;
+  static hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_stats_z<PM, RT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  return ext_launch(k_stats_z<PM, RT>, dim3(nblk), dim3(512), lds, L, a);
+}
+template <int PM>
+hipError_t launch_sz_rt(const StatsZArgs& a, unsigned nblk, const Launch& L) {
+  switch (a.A ? a.rp / 32 : 0) {
+    case 0: return launch_sz<PM, 0>(a, nblk, L);
+    case 1: return launch_sz<PM, 1>(a, nblk, L);
+    case 2: return launch_sz<PM, 2>(a, nblk, L);
+    case 3: return launch_sz<PM, 3>(a, nblk, L);
+    case 4: return launch_sz<PM, 4>(a, nblk, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+hipError_t launch_stats_z(const StatsZArgs& a, int R, const Launch& L) {
+  const int64_t nblk = (int64_t)R * a.ntb * a.csplit;
+  if (nblk == 0) return hipSuccess;
+  if (a.A && (a.rp % 32 != 0 || a.rp > 128 || a.rank > a.rp)) return hipErrorInvalidValue;
+  if (a.d % 8 != 0 || (int64_t)kZTB * a.d * 2 >= (int64_t)kOutOfRange) return hipErrorInvalidValue;
+  if (a.pmode == 2) return launch_sz_rt<2>(a, (unsigned)nblk, L);
+  if (a.pmode == 1) return launch_sz_rt<1>(a, (unsigned)nblk, L);
+  return launch_sz_rt<0>(a, (unsigned)nblk, L);
+}
+
 // One thread per channel; the block partials are read 8 at a time (independent
-// loads in flight) and added in slice order.
-__global__ __launch_bounds__(64) void k_stats_final(StatsSplitArgs a) {
+// loads in flight) and added in block order.
+__global__ __launch_bounds__(64) void k_stats_final(StatsFinalArgs a) {
   const int r = blockIdx.y;
   const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (c >= a.d) return;
-  const int nb = (a.nsplit + 3) / 4;
+  const int nb = a.nb;
   const double* P = a.partial + (int64_t)r * nb * a.d + c;
   double S = 0.0;
   int k = 0;
@@ -295,17 +475,8 @@ __global__ __launch_bounds__(64) void k_stats_final(StatsSplitArgs a) {
   if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
 }
 
-hipError_t launch_stats_partial(const StatsSplitArgs& a, int R,
-                                const Launch& L) {
-  if (a.nsplit == 0) return hipSuccess;
-  dim3 grid((unsigned)((a.d + 511) / 512), (unsigned)((a.nsplit + 3) / 4),
-            (unsigned)R);
-  if (a.pmode == 2) return ext_launch(k_stats_partial<2>, grid, dim3(256), 0, L, a);
-  if (a.pmode == 1) return ext_launch(k_stats_partial<1>, grid, dim3(256), 0, L, a);
-  return ext_launch(k_stats_partial<0>, grid, dim3(256), 0, L, a);
-}
-
-hipError_t launch_stats_final(const StatsSplitArgs& a, int R, const Launch& L) {
+hipError_t launch_stats_final(const StatsFinalArgs& a, int R, const Launch& L) {
+  if (R == 0 || a.d == 0) return hipSuccess;
   dim3 grid((unsigned)((a.d + 63) / 64), (unsigned)R);
   return ext_launch(k_stats_final, grid, dim3(64), 0, L, a);
 }

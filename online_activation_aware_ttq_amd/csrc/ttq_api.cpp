@@ -47,7 +47,10 @@ struct Plan {
   int G = 0;             // groups per row
   int planes = 1;        // fused: activation planes (2 = bf16 hi + lo)
   int64_t rowblocks = 0;
-  int tchunk = 0, nsplit = 0;
+  int sz_ntb = 0;         // large T: 64-token blocks per request,
+  int sz_csplit = 1;      // channel ranges per block,
+  int sz_cps = 0;         // 512-channel chunks per range
+  bool z_fused = false;   // Z = X A^T computed by the statistics pass
   int64_t rp = 0;        // rank padded to a multiple of 32
   int64_t rchunk = 1;    // two-phase: requests quantized per pass
   int zsplit = 1;        // two-phase: K splits of Z = X A^T
@@ -93,17 +96,30 @@ int validate_params(const ttq_params* prm, int64_t R) {
 
 // Token slices for the norm partials of the large-T statistics: enough
 // workgroups to fill the chip (about 2048 waves), at least 8 tokens a slice.
+// Large T: one workgroup per 64-token block of a request; when that gives
+// fewer than 512 workgroups the channels are split into ranges of whole
+// 512-channel chunks as well (the low-rank product of each range is then a
+// float32 partial, summed in range order).
 template <class Take>
-void plan_stats_split(Plan& P, int64_t R, int64_t T, int64_t d, Take& take) {
-  const int64_t cchunks = (d + 511) / 512;
-  int64_t target = 2048 / (cchunks * R);
-  if (target < 1) target = 1;
-  int64_t tch = (T + target - 1) / target;
-  if (tch < 8) tch = 8;
-  P.tchunk = (int)tch;
-  P.nsplit = (int)((T + P.tchunk - 1) / P.tchunk);
-  P.off_statp = take(sizeof(double) * R * ((P.nsplit + 3) / 4) * d);
+void plan_stats_z(Plan& P, int64_t R, int64_t T, int64_t d, bool with_z,
+                  Take& take) {
+  P.sz_ntb = (int)((T + 63) / 64);
+  const int64_t nck = (d + 511) / 512;
+  const int64_t blocks = R * P.sz_ntb;
+  int64_t cs = blocks > 0 ? (512 + blocks - 1) / blocks : 1;
+  if (cs > nck) cs = nck;
+  if (cs < 1) cs = 1;
+  P.sz_cps = (int)((nck + cs - 1) / cs);
+  P.sz_csplit = P.sz_cps > 0 ? (int)((nck + P.sz_cps - 1) / P.sz_cps) : 1;
+  P.off_statp = take(sizeof(double) * R * P.sz_ntb * d);
+  P.z_fused = with_z;
+  if (with_z && P.sz_csplit > 1)
+    P.off_zpart = take(sizeof(float) * P.sz_csplit * R * T * P.rp);
 }
+
+// the statistics pass computes Z itself for ranks up to 96 with p in {1, 2}
+// (registers: larger ranks or the general-p power use the GEMM for Z)
+bool z_in_stats(int64_t rp, double p) { return rp > 0 && rp <= 96 && (p == 2.0 || p == 1.0); }
 
 // Z = X A^T has few output tiles (rank columns): split the channels so that
 // about 512 workgroups run, each over at least 256 channels.
@@ -153,8 +169,9 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.off_xs = take(sizeof(uint16_t) * P.planes * R * 16 * P.ntb * d);
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
   } else {
-    plan_stats_split(P, R, T, d, take);
-    if (P.rp > 0 && T > 0) plan_z_split(P, R * T, d, take);
+    const bool zf = T > 0 && z_in_stats(P.rp, prm->p);
+    plan_stats_z(P, R, T, d, zf, take);
+    if (P.rp > 0 && T > 0 && !zf) plan_z_split(P, R * T, d, take);
     if (T <= kGemmQMaxT && gemm_q_supported(d, prm->group, 0) &&
         !(prm->flags & TTQ_FLAG_FORCE_TWO_PHASE)) {
       // no W_hat: the GEMM quantizes its weight tiles itself (exports, when
@@ -188,7 +205,7 @@ struct TimingState {
 TimingState g_timing;
 
 const char* kKernelNames[K_NUM_KINDS] = {
-    "stats_small", "stats_partial", "stats_final", "fused_qdq_mfma",
+    "stats_small", "stats_z", "stats_final", "fused_qdq_mfma",
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
     "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant", "seg_copy",
     "pca_skinny", "pca_psum", "pca_chol", "pca_trsm", "pca_residual",
@@ -274,6 +291,37 @@ int enqueue_z_small(const Plan& P, char* ws, const bf16_t* Xb,
   int st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
   if (st != TTQ_OK) return st;
   return run(K_LOWRANK_ZSUM, s, [&](const Launch& L) { return launch_lowrank_z_sum(za, L); });
+}
+
+// Statistics of a large-T call (and Z = X A^T when the plan fuses it): the
+// block partials, then D^{+-1/2}; with several channel ranges Z is summed
+// from their float32 partials in range order.
+int enqueue_stats_z(const Plan& P, char* ws, const bf16_t* Xb,
+                    const bf16_t* Ab, int64_t R, int64_t T, int64_t d,
+                    int64_t rank, bf16_t* Zb, int pmode, double p, double lam,
+                    double alpha, float* dh, float* dhi, float* dh_export,
+                    hipStream_t s) {
+  const bool zf = P.z_fused && Ab && T > 0;
+  StatsZArgs za{};
+  za.X = Xb; za.T = T; za.d = d; za.pmode = pmode; za.p = p;
+  za.ntb = P.sz_ntb; za.csplit = P.sz_csplit; za.cps = P.sz_cps;
+  za.partial = reinterpret_cast<double*>(ws + P.off_statp);
+  if (zf) {
+    za.A = Ab; za.rank = (int)rank; za.rp = (int)P.rp;
+    za.Z = Zb;
+    za.Zpart = P.sz_csplit > 1 ? reinterpret_cast<float*>(ws + P.off_zpart) : nullptr;
+    za.zslice = R * T * P.rp;
+  }
+  int st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_z(za, (int)R, L); });
+  if (st != TTQ_OK) return st;
+  StatsFinalArgs fa{};
+  fa.partial = za.partial; fa.d = d; fa.nb = P.sz_ntb; fa.pmode = pmode;
+  fa.p = p; fa.lam = lam; fa.alpha = alpha;
+  fa.dh = dh; fa.dhi = dhi; fa.dh_export = dh_export;
+  st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(fa, (int)R, L); });
+  if (st != TTQ_OK || !zf || P.sz_csplit <= 1) return st;
+  SplitReduceArgs ra{za.Zpart, P.sz_csplit, za.zslice, Zb};
+  return run(K_SPLITK_REDUCE, s, [&](const Launch& L) { return launch_splitk_reduce(ra, L); });
 }
 
 int linear_impl(const ttq_params* prm, int64_t R, const void* W,
@@ -364,19 +412,13 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     return run(K_FUSED, s, [&](const Launch& L) { return launch_fused(fa, P.ntb, prm->group, L); });
   }
 
-  // two-phase path
-  StatsSplitArgs ta{};
-  ta.X = Xb; ta.T = T; ta.d = d; ta.pmode = pmode;
-  ta.p = prm->p; ta.lam = prm->lambda; ta.alpha = prm->alpha;
-  ta.tchunk = P.tchunk; ta.nsplit = P.nsplit;
-  ta.partial = reinterpret_cast<double*>(ws + P.off_statp);
-  ta.dh = dh; ta.dhi = dhi; ta.dh_export = dhalf_out;
-  st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_partial(ta, (int)R, L); });
-  if (st != TTQ_OK) return st;
-  st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(ta, (int)R, L); });
+  // two-phase path: statistics (and Z, when fused) in one pass over X
+  st = enqueue_stats_z(P, ws, Xb, need_quant ? Ab : nullptr, R, T, d, rank, Zb,
+                       pmode, prm->p, prm->lambda, prm->alpha, dh, dhi,
+                       dhalf_out, s);
   if (st != TTQ_OK) return st;
   if (!need_quant) return TTQ_OK;
-  if (P.rp > 0) {
+  if (P.rp > 0 && !P.z_fused) {
     st = enqueue_z_gemm(P, ws, Xb, Ab, R * T, d, rank, Zb, s);
     if (st != TTQ_OK) return st;
   }
@@ -488,7 +530,7 @@ Plan make_quantize_plan(const ttq_params& q) {
   };
   P.off_dh = take(sizeof(float) * q.d);
   P.path = q.T <= kFusedMaxT ? 0 : 1;
-  if (P.path == 1) plan_stats_split(P, 1, q.T, q.d, take);
+  if (P.path == 1) plan_stats_z(P, 1, q.T, q.d, false, take);
   P.total = off;
   return P;
 }
@@ -565,15 +607,8 @@ int quantize_impl(const ttq_params* prm, const void* W, const void* X,
     sa.dh = dh; sa.dhi = dhalf_inv; sa.dh_export = dhalf_out; sa.group = q.group;
     st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
   } else {
-    StatsSplitArgs ta{};
-    ta.X = Xb; ta.T = T; ta.d = d; ta.pmode = pmode;
-    ta.p = q.p; ta.lam = q.lambda; ta.alpha = q.alpha;
-    ta.tchunk = P.tchunk; ta.nsplit = P.nsplit;
-    ta.partial = reinterpret_cast<double*>(ws + P.off_statp);
-    ta.dh = dh; ta.dhi = dhalf_inv; ta.dh_export = dhalf_out;
-    st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_partial(ta, 1, L); });
-    if (st == TTQ_OK)
-      st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(ta, 1, L); });
+    st = enqueue_stats_z(P, ws, Xb, nullptr, 1, T, d, 0, nullptr, pmode, q.p,
+                         q.lambda, q.alpha, dh, dhalf_inv, dhalf_out, s);
   }
   if (st != TTQ_OK || dout == 0) return st;
   QuantArgs qa{};
@@ -916,7 +951,7 @@ PcaPlan make_pca_plan(const ttq_params* prm) {
     P.off_dh = take(sizeof(float) * d);
     P.off_dhi = take(sizeof(float) * d);
     if (T > kFusedMaxT) {
-      plan_stats_split(P.stats, 1, T, d, take);
+      plan_stats_z(P.stats, 1, T, d, false, take);
       P.off_statp = P.stats.off_statp;
     }
   }
@@ -986,15 +1021,10 @@ int pca_impl(const ttq_params* prm, int32_t iters, const void* W,
       sa.dh = dhw; sa.dhi = dhiw; sa.group = 32;
       st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
     } else {
-      StatsSplitArgs ta{};
-      ta.X = Xb; ta.T = T; ta.d = d; ta.pmode = pmode;
-      ta.p = prm->p; ta.lam = prm->lambda; ta.alpha = prm->alpha;
-      ta.tchunk = P.stats.tchunk; ta.nsplit = P.stats.nsplit;
-      ta.partial = reinterpret_cast<double*>(ws + P.off_statp);
-      ta.dh = dhw; ta.dhi = dhiw;
-      st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_partial(ta, 1, L); });
-      if (st == TTQ_OK)
-        st = run(K_STATS_FINAL, s, [&](const Launch& L) { return launch_stats_final(ta, 1, L); });
+      Plan sp = P.stats;
+      sp.off_statp = P.off_statp;
+      st = enqueue_stats_z(sp, ws, Xb, nullptr, 1, T, d, 0, nullptr, pmode,
+                           prm->p, prm->lambda, prm->alpha, dhw, dhiw, nullptr, s);
     }
     if (st != TTQ_OK) return st;
     dh = dhw;

@@ -18,7 +18,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 // Kernel kinds, for the optional event timing.
 enum KernelKind {
   K_STATS_SMALL = 0,   // norms + diag + scaled activations (T <= 128)
-  K_STATS_PARTIAL,     // norms, partial sums over a token slice
+  K_STATS_PARTIAL,     // norms, partial sums per 64-token block (+ Z = X A^T)
   K_STATS_FINAL,       // norms finalize + diag
   K_FUSED,             // fused quantize + MFMA contraction (single W pass)
   K_QUANT,             // quantize pass writing W_hat (two-phase path)
@@ -296,20 +296,39 @@ struct StatsSmallArgs {
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
                               const Launch& L);
 
-struct StatsSplitArgs {
+// Large T (two-phase paths, quantize-once and PCA statistics): one pass over
+// X per 64-token block that writes float64 partial powers per channel and,
+// when asked for, the low-rank product Z = X A^T of the block's tokens.
+struct StatsZArgs {
   const bf16_t* X;      // [R][T][d]
   int64_t T, d;
+  int pmode;            // 1: p == 1, 2: p == 2, 0: general p
+  double p;
+  int ntb;              // 64-token blocks per request (ceil(T / 64))
+  int csplit, cps;      // channel ranges per block, 512-channel chunks each
+  double* partial;      // [R][ntb][d] sums of |x|^p over each block's tokens
+  const bf16_t* A;      // [rank][d], or null: statistics only
+  int rank, rp;         // rp = rank rounded up to 32, at most 128
+  bf16_t* Z;            // csplit == 1: [R*T][rp] (columns past rank zero)
+  float* Zpart;         // csplit > 1: [csplit][R*T][rp] fp32 partials
+  int64_t zslice;       // R*T*rp: the stride of one channel range's partials
+};
+hipError_t launch_stats_z(const StatsZArgs& a, int R, const Launch& L);
+size_t stats_z_lds_bytes();
+
+// D^{+-1/2} from the block partials: nb partial rows per request, summed in
+// order, then the norm, lambda and the power.
+struct StatsFinalArgs {
+  const double* partial;  // [R][nb][d]
+  int64_t d;
+  int nb;
   int pmode;
   double p, lam, alpha;
-  int tchunk, nsplit;
-  double* partial;      // [R][ceil(nsplit/4)][d], one row per block of 4 slices
   float* dh;
   float* dhi;
   float* dh_export;
 };
-hipError_t launch_stats_partial(const StatsSplitArgs& a, int R,
-                                const Launch& L);
-hipError_t launch_stats_final(const StatsSplitArgs& a, int R, const Launch& L);
+hipError_t launch_stats_final(const StatsFinalArgs& a, int R, const Launch& L);
 
 struct FusedArgs {
   const bf16_t* W;      // [d_out][d]
