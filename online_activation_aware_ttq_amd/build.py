@@ -84,8 +84,10 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-           *objs]
+    # every symbol must resolve at link time (a kernel whose host stub the
+    # compiler did not emit would otherwise fail only when first launched)
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           "-Wl,--no-undefined", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         print(res.stdout + res.stderr, file=sys.stderr)

@@ -32,6 +32,8 @@
 // bit (sc0; measured slightly faster than the default here).
 #include "ttq_internal.h"
 
+#include <algorithm>
+
 namespace ttq {
 
 namespace {
@@ -62,9 +64,10 @@ constexpr int kStripN = 8;
 // Every schedule runs the same MFMAs in the same order on every output, so
 // the result does not depend on it.  Measured (256 x 256 tiles): with many
 // rounds of workgroups per CU (7B-class layer, 8 requests x 4096 tokens)
-// kSingleBuf takes 6-9 % less time than kDoubleBuf; with one partial round
+// kSingleBuf takes 6-9 % less time than kDoubleBuf, and in the persistent
+// kernel below kSingleBufSplit another 2-4 % less; with one partial round
 // (70B-class up projection, T = 512) kSingleBuf is 15 % slower and
-// kSingleBufSplit 4 % faster.
+// kSingleBufSplit 4 % faster than kDoubleBuf.
 constexpr int kDoubleBuf = 0, kSingleBuf = 1, kSingleBufSplit = 2;
 
 // TM x TN MFMA tiles of 32 x 32 per wave, WGM x WGN waves, NS LDS stages.
@@ -303,6 +306,249 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
       }
 }
 
+// Persistent form of the single-buffered schedules: one workgroup per CU
+// walks its XCD's share of the tile order (the same tiles, in the same
+// order, as the one-tile-per-workgroup launch).  Measured on the 7B-class
+// layer (8 requests x 4096 tokens), split-load schedule, alternating runs:
+// q 1205 -> 1034 us, gate 2981 -> 2742, down 2781 -> 2550; one partial
+// round (T = 512) gains nothing, so fewer than four rounds keep one tile
+// per workgroup.  At the end of a tile the
+// loads of the next tile's first k-tiles go out first, then C leaves through
+// LDS (32-row passes through the free stage, one 16-byte store per lane and
+// row piece, 1 KiB per wave instruction) and the next tile's k-loop starts
+// while those stores drain.  With one workgroup per CU (LDS) the C stores
+// of a tile otherwise stall the CU: every round of tiles ends in the same
+// store burst, bound by the write bandwidth (timing copy without the C
+// stores: 10-20 % faster on the 7B-class layer).  The MFMAs and their order
+// per output are those of k_gemm_lds: the results are bit-identical.
+template <int TM, int TN, int WGM, int WGN, int NS, int SCHED>
+__global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds_p(GemmArgs a) {
+  constexpr int NW = WGM * WGN, NT = NW * 64;
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32, BK = 64;
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
+  constexpr int STAGE = ABYTES + BBYTES;
+  constexpr int NLA = BM / (8 * NW), NLB = BN / (8 * NW);
+  constexpr int NL = NLA + NLB;
+  constexpr int CST = BN + 4;                    // staged C row (floats)
+  constexpr int NSTORE = BM * BN / 4 / NT;       // 16-byte stores per thread
+  static_assert(SCHED != kDoubleBuf, "single-buffered schedules only");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && NW % 2 == 0, "load split");
+  static_assert(NS == 2, "one k-tile of the next tile in flight during the C stores");
+  static_assert(NSTORE + (NS - 2) * NL < 64, "vmcnt range");
+  static_assert(32 * CST * 4 <= STAGE, "C pass fits a stage");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int64_t mtiles = (a.M + BM - 1) / BM;
+  const int64_t ntiles = (a.N_store + BN - 1) / BN;
+  const int64_t per_product = mtiles * ntiles;
+  const int64_t nprod = a.batch > 1 ? a.batch : 1;
+  const int64_t total = per_product * nprod;
+  // this XCD's contiguous share of the tile order; this workgroup takes its
+  // tiles jj, jj + nper, ... (blocks of one XCD are id, id + 8, ...)
+  const int64_t xcd = blockIdx.x & 7, jj = blockIdx.x >> 3, nper = gridDim.x >> 3;
+  const int64_t base = total >> 3, extra = total & 7;
+  const int64_t cnt = base + (xcd < extra ? 1 : 0);
+  const int64_t first = xcd * base + min(xcd, extra);
+  if (jj >= cnt) return;
+
+  // the current tile (plain locals: a local struct used inside the load
+  // lambda keeps the compiler from emitting this kernel's host stub)
+  const bf16_t *tA1 = nullptr, *tB1 = nullptr, *tA2 = nullptr, *tB2 = nullptr;
+  float* tC = nullptr;
+  int64_t tm0 = 0, tn0 = 0, tmrows = 0, tnrows = 0;
+  auto set_tile = [&](int64_t j) {
+    const int64_t t = first + j;
+    const int64_t z = t / per_product, tz = t % per_product;
+    const int64_t strip = tz / (kStripN * mtiles), in_strip = tz % (kStripN * mtiles);
+    const int64_t width = min((int64_t)kStripN, ntiles - strip * kStripN);
+    tm0 = (in_strip / width) * BM;
+    tn0 = (strip * kStripN + in_strip % width) * BN;
+    tA1 = a.A1 + z * a.sA1;
+    tB1 = a.B1 + z * a.sB1;
+    tA2 = a.A2 ? a.A2 + z * a.sA2 : nullptr;
+    tB2 = a.B2 ? a.B2 + z * a.sB2 : nullptr;
+    tC = a.C + z * a.sC;
+    tmrows = min((int64_t)BM, a.M - tm0);
+    tnrows = max((int64_t)0, min((int64_t)BN, a.N - tn0));
+  };
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WGN, wn = w % WGN;
+  const int lrow = l >> 3;
+  const int lch = (l & 7) ^ swz(w * 8 + lrow);
+  const int nk1 = (int)((a.K1 + BK - 1) / BK);
+  const int nk2 = a.K2 > 0 ? (int)((a.K2 + BK - 1) / BK) : 0;
+  const int nk = nk1 + nk2;
+
+  // loads of k-tile kt of the current tile (tiles at or past nk read
+  // nothing: zero fill into a stage not read again)
+  set_tile(jj);
+  auto issue = [&](int kt, int stage, int part) {
+    const bool seg2 = kt >= nk1;
+    const bf16_t* Ap = seg2 ? tA2 : tA1;
+    const bf16_t* Bp = seg2 ? tB2 : tB1;
+    const int lda = __builtin_amdgcn_readfirstlane((int)(seg2 ? a.lda2 : a.lda1));
+    const int ldb = __builtin_amdgcn_readfirstlane((int)(seg2 ? a.ldb2 : a.ldb1));
+    const int K = __builtin_amdgcn_readfirstlane((int)(seg2 ? a.K2 : a.K1));
+    const int k0 = __builtin_amdgcn_readfirstlane((seg2 ? kt - nk1 : kt) * BK);
+    const auto ra = make_rsrc(Ap + tm0 * lda, (uint32_t)(tmrows * lda * 2));
+    const auto rb = make_rsrc(Bp + tn0 * ldb, (uint32_t)(tnrows * ldb * 2));
+    const bool kin = k0 + lch * 8 < K;
+    const uint32_t va =
+        kin ? (uint32_t)(((w * 8 + lrow) * lda + k0 + lch * 8) * 2) : kOutOfRange;
+    const uint32_t vb =
+        kin ? (uint32_t)(((w * 8 + lrow) * ldb + k0 + lch * 8) * 2) : kOutOfRange;
+    unsigned char* sa = smem + stage * STAGE;
+    unsigned char* sb = sa + ABYTES;
+    if (part & 1) {
+#pragma unroll
+      for (int j = 0; j < NLA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(sa + (w + j * NW) * 1024),
+            16, va, (uint32_t)(j * 8 * NW * lda * 2), 0, 1);
+    }
+    if (part & 2) {
+#pragma unroll
+      for (int j = 0; j < NLB; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(sb + (w + j * NW) * 1024),
+            16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 1);
+    }
+  };
+
+  const int fs = swz(l & 15);
+  const int fh = l >> 5;
+  const int arow = (wm * TM * 32 + (l & 31)) * 128;
+  const int brow = (wn * TN * 32 + (l & 31)) * 128;
+  auto read_frags = [&](int stage, int kk, u32x4* A_, u32x4* B_) {
+    const unsigned char* sa = smem + stage * STAGE;
+    const unsigned char* sb = sa + ABYTES;
+    const int off = (((kk << 1) | fh) ^ fs) * 16;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) B_[j] = *(const u32x4*)(sb + brow + j * 4096 + off);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) A_[i] = *(const u32x4*)(sa + arow + i * 4096 + off);
+  };
+  f32x16 acc[TM][TN];
+  auto mfmas = [&](const u32x4* A_, const u32x4* B_) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, A_[i]), __builtin_bit_cast(bf16x8, B_[j]),
+            acc[i][j], 0, 0, 0);
+  };
+  constexpr int NMF = TM * TN;
+  constexpr int PL = (NL + NMF - 1) / NMF;
+  constexpr int PA = (NLA + NMF - 1) / NMF, PB = (NLB + NMF - 1) / NMF;
+  const bool cvec = (a.ldc % 4 == 0) && (a.sC % 4 == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0);
+
+  issue(0, 0, 3);
+  wait_vm<0>();
+  for (int64_t j = jj; j < cnt; j += nper) {
+    // k-tile 0 of this tile landed (the previous tile's C stores, issued
+    // after it, may still be in flight)
+    wait_vm<NSTORE>();
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jn][r] = 0.f;
+    u32x4 fa[TM], fb[TN];
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int pstage = stage == 0 ? NS - 1 : stage - 1;
+      if constexpr (SCHED == kSingleBuf) {
+        read_frags(stage, 0, fa, fb);
+        issue(kt + NS - 1, pstage, 3);
+        mfmas(fa, fb);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, PL, 0);  // VMEM read
+        }
+      } else {
+        read_frags(stage, 0, fa, fb);
+        issue(kt + NS - 1, pstage, 1);
+        mfmas(fa, fb);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, PA, 0);
+        }
+        read_frags(stage, 1, fa, fb);
+        issue(kt + NS - 1, pstage, 2);
+        mfmas(fa, fb);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, PB, 0);
+        }
+      }
+#pragma unroll
+      for (int kk = SCHED == kSingleBuf ? 1 : 2; kk < BK / 16; ++kk) {
+        read_frags(stage, kk, fa, fb);
+        mfmas(fa, fb);
+      }
+      wait_vm<(NS - 2) * NL>();
+      lds_barrier();
+      stage = stage + 1 == NS ? 0 : stage + 1;
+    }
+    // the loads issued past the last k-tile still write LDS
+    wait_vm<0>();
+    lds_barrier();
+    // the next tile's first k-tile goes out before the C stores
+    const int64_t om0 = tm0, on0 = tn0;
+    float* oC = tC;
+    if (j + nper < cnt) {
+      set_tile(j + nper);
+      issue(0, 0, 3);
+    }
+    // C through the second stage, 32 rows per pass: the waves holding those
+    // rows write their 32 x 32 fragments (lane l: column l%32, rows
+    // 8*(r/4) + 4*(l/32) + r%4), then every thread stores 16-byte pieces of
+    // whole rows
+    float* cs = reinterpret_cast<float*>(smem + (NS - 1) * STAGE);
+#pragma unroll
+    for (int p = 0; p < BM / 32; ++p) {
+      if (wm == p / TM) {
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+            cs[row * CST + wn * TN * 32 + jn * 32 + (l & 31)] = acc[p % TM][jn][r];
+          }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int e = 0; e < 32 * BN / 4 / NT; ++e) {
+        const int idx = tid + e * NT;
+        const int row = idx / (BN / 4), c4 = idx % (BN / 4);
+        const f32x4 v = *(const f32x4*)(cs + row * CST + c4 * 4);
+        const int64_t m = om0 + p * 32 + row, n = on0 + c4 * 4;
+        if (m < a.M) {
+          float* dst = oC + m * a.ldc + n;
+          if (cvec && n + 3 < a.N_store) {
+            *(f32x4*)dst = v;
+          } else {
+            if (n < a.N_store) dst[0] = v.x;
+            if (n + 1 < a.N_store) dst[1] = v.y;
+            if (n + 2 < a.N_store) dst[2] = v.z;
+            if (n + 3 < a.N_store) dst[3] = v.w;
+          }
+        }
+      }
+      lds_barrier();
+    }
+  }
+}
+
 template <int TM, int TN, int WGM, int WGN, int NS, int SCHED>
 hipError_t launch_t(const GemmArgs& a, const Launch& L) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
@@ -322,6 +568,34 @@ hipError_t launch_t(const GemmArgs& a, const Launch& L) {
                     dim3(WGM * WGN * 64), lds, L, a);
 }
 
+// persistent launch: one workgroup per CU (at most), a multiple of 8
+template <int TM, int TN, int WGM, int WGN, int NS, int SCHED>
+hipError_t launch_tp(const GemmArgs& a, const Launch& L) {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  constexpr int lds = NS * (BM + BN) * 64 * 2;
+  static_assert(lds <= 160 * 1024, "LDS");
+  const int64_t mtiles = (a.M + BM - 1) / BM;
+  const int64_t ntiles = (a.N_store + BN - 1) / BN;
+  const int64_t total = mtiles * ntiles * (a.batch > 1 ? a.batch : 1);
+  if (total == 0) return hipSuccess;
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus = n > 0 ? n : 256;
+  }
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t wg_xcd = std::min<int64_t>(per_xcd, std::max(1, cus / 8));
+  static hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_gemm_lds_p<TM, TN, WGM, WGN, NS, SCHED>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  return ext_launch(k_gemm_lds_p<TM, TN, WGM, WGN, NS, SCHED>,
+                    dim3((unsigned)(wg_xcd * 8)), dim3(WGM * WGN * 64), lds, L, a);
+}
+
 }  // namespace
 
 int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
@@ -329,8 +603,9 @@ int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
   // give twice as many workgroups, each costing about 0.57 of a big one
   // (measured on the 7B-class shapes).  Take the one whose rounds of 256
   // workgroups (one per CU) cost less: a partial last round costs a full one.
-  // 256 x 256 tiles use the single-buffered step schedule from four rounds
-  // on, its split-load form below that.
+  // From four rounds of 256 x 256 tiles on, one persistent workgroup per CU
+  // walks the tiles (its C stores overlap the next tile); below that each
+  // tile is a workgroup.  Both use the split-load single-buffered schedule.
   const int64_t mt = (M + 255) / 256;
   const int64_t r256 = (mt * ((N + 255) / 256) * batch + 255) / 256;
   const int64_t r128 = (mt * ((N + 127) / 128) * batch + 255) / 256;
@@ -342,8 +617,8 @@ hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L) {
   if (a.M <= 0 || a.N_store <= 0) return hipSuccess;
   if (a.K1 <= 0 || !a.C || a.nsplit > 1) return hipErrorInvalidValue;
   switch (gemm_lds_config(a.M, a.N_store, a.batch > 1 ? a.batch : 1)) {
-    case 0:  // 256 x 256, 8 waves, 2 stages
-      return launch_t<4, 2, 2, 4, 2, kSingleBuf>(a, L);
+    case 0:  // 256 x 256, 8 waves, 2 stages, persistent
+      return launch_tp<4, 2, 2, 4, 2, kSingleBufSplit>(a, L);
     case 2:
       return launch_t<4, 2, 2, 4, 2, kSingleBufSplit>(a, L);
     default:  // 256 x 128, 8 waves, 3 stages

@@ -489,9 +489,9 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, const Launch& L);
 // Large-tile variant for the projection GEMM (fp32 C, no split): operands
-// streamed into LDS by direct loads.  gemm_lds_config: 0 = 256 x 256 tiles
-// (single-buffered steps), 1 = 256 x 128 tiles, 2 = 256 x 256 tiles
-// (single-buffered steps, A and B loads in separate steps).
+// streamed into LDS by direct loads.  gemm_lds_config: 0 = 256 x 256 tiles,
+// persistent workgroups, 1 = 256 x 128 tiles, 2 = 256 x 256 tiles, one per
+// workgroup.
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L);
 int gemm_lds_config(int64_t M, int64_t N, int64_t batch);
 
