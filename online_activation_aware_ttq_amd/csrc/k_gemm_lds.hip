@@ -135,12 +135,22 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
     const int K = __builtin_amdgcn_readfirstlane((int)(seg2 ? a.K2 : a.K1));
     const int k0 = __builtin_amdgcn_readfirstlane((seg2 ? kt - nk1 : kt) * BK);
     const auto ra = make_rsrc(Ap + m0 * lda, (uint32_t)(mrows * lda * 2));
-    const auto rb = make_rsrc(Bp + n0 * ldb, (uint32_t)(nrows * ldb * 2));
     const bool kin = k0 + lch * 8 < K;
     const uint32_t va =
         kin ? (uint32_t)(((w * 8 + lrow) * lda + k0 + lch * 8) * 2) : kOutOfRange;
+    // B1 in the tiled W_hat layout: this tile's rows are rows n0 % 256 ..
+    // of 256-row block n0 / 256, whose k-tiles are contiguous 32 KiB tiles
+    const bool tiled = a.b1_tiled && !seg2;
+    const auto rb =
+        tiled ? make_rsrc(Bp + (n0 / kWtRows) * nk1 * (kWtRows * kWtCols),
+                          (uint32_t)(nk1 * (kWtRows * kWtCols) * 2))
+              : make_rsrc(Bp + n0 * ldb, (uint32_t)(nrows * ldb * 2));
     const uint32_t vb =
-        kin ? (uint32_t)(((w * 8 + lrow) * ldb + k0 + lch * 8) * 2) : kOutOfRange;
+        !kin ? kOutOfRange
+             : tiled ? (uint32_t)(((kt * kWtRows + n0 % kWtRows + w * 8 + lrow) * kWtCols +
+                                   lch * 8) * 2)
+                     : (uint32_t)(((w * 8 + lrow) * ldb + k0 + lch * 8) * 2);
+    const int ldbs = tiled ? (int)kWtCols : ldb;   // row step of the B loads
     unsigned char* sa = smem + stage * STAGE;
     unsigned char* sb = sa + ABYTES;
     if (part & 1) {
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
       for (int j = 0; j < NLB; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (__attribute__((address_space(3))) void*)(sb + (w + j * NW) * 1024),
-            16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 1);
+            16, vb, (uint32_t)(j * 8 * NW * ldbs * 2), 0, 1);
     }
   };
 
@@ -393,12 +403,21 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds_p(GemmArgs a) {
     const int K = __builtin_amdgcn_readfirstlane((int)(seg2 ? a.K2 : a.K1));
     const int k0 = __builtin_amdgcn_readfirstlane((seg2 ? kt - nk1 : kt) * BK);
     const auto ra = make_rsrc(Ap + tm0 * lda, (uint32_t)(tmrows * lda * 2));
-    const auto rb = make_rsrc(Bp + tn0 * ldb, (uint32_t)(tnrows * ldb * 2));
     const bool kin = k0 + lch * 8 < K;
     const uint32_t va =
         kin ? (uint32_t)(((w * 8 + lrow) * lda + k0 + lch * 8) * 2) : kOutOfRange;
+    // B1 in the tiled W_hat layout (see k_gemm_lds)
+    const bool tiled = a.b1_tiled && !seg2;
+    const auto rb =
+        tiled ? make_rsrc(Bp + (tn0 / kWtRows) * nk1 * (kWtRows * kWtCols),
+                          (uint32_t)(nk1 * (kWtRows * kWtCols) * 2))
+              : make_rsrc(Bp + tn0 * ldb, (uint32_t)(tnrows * ldb * 2));
     const uint32_t vb =
-        kin ? (uint32_t)(((w * 8 + lrow) * ldb + k0 + lch * 8) * 2) : kOutOfRange;
+        !kin ? kOutOfRange
+             : tiled ? (uint32_t)(((kt * kWtRows + tn0 % kWtRows + w * 8 + lrow) * kWtCols +
+                                   lch * 8) * 2)
+                     : (uint32_t)(((w * 8 + lrow) * ldb + k0 + lch * 8) * 2);
+    const int ldbs = tiled ? (int)kWtCols : ldb;   // row step of the B loads
     unsigned char* sa = smem + stage * STAGE;
     unsigned char* sb = sa + ABYTES;
     if (part & 1) {
@@ -413,7 +432,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds_p(GemmArgs a) {
       for (int j = 0; j < NLB; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (__attribute__((address_space(3))) void*)(sb + (w + j * NW) * 1024),
-            16, vb, (uint32_t)(j * 8 * NW * ldb * 2), 0, 1);
+            16, vb, (uint32_t)(j * 8 * NW * ldbs * 2), 0, 1);
     }
   };
 
@@ -616,6 +635,9 @@ int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L) {
   if (a.M <= 0 || a.N_store <= 0) return hipSuccess;
   if (a.K1 <= 0 || !a.C || a.nsplit > 1) return hipErrorInvalidValue;
+  // tiled B: 32-bit offsets inside one 256-row block of k-tiles
+  if (a.b1_tiled && (a.K1 + 63) / 64 * kWtRows * kWtCols * 2 >= (int64_t)kOutOfRange)
+    return hipErrorInvalidValue;
   switch (gemm_lds_config(a.M, a.N_store, a.batch > 1 ? a.batch : 1)) {
     case 0:  // 256 x 256, 8 waves, 2 stages, persistent
       return launch_tp<4, 2, 2, 4, 2, kSingleBufSplit>(a, L);

@@ -62,6 +62,11 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
 template <int GS, int CB, int QF, bool EXP>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   constexpr int LPG = GS / 8;
+  // W_hat leaves through LDS: lane l quantizes channels 8l .. 8l+7 of the
+  // wave's 8 rows, and each store instruction then writes one 64-channel
+  // tile slice of all 8 rows (1 KiB contiguous in the tiled layout) rather
+  // than 8 pieces of 128 bytes 32 KiB apart
+  __shared__ u32x4 tw[4][QROWS][64];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int64_t nchunk = (a.d + 511) / 512;
   const int64_t nblk1 = (((a.d_out + QROWS - 1) / QROWS) * nchunk + 3) / 4;
@@ -84,7 +89,8 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   const float* dhr = a.dh + (int64_t)r * a.d;
   const float* dhir = a.dhi + (int64_t)r * a.d;
   // What == null: the codes, scales and offsets only (no W_hat is written)
-  bf16_t* What = a.What ? a.What + (int64_t)r * a.d_out * a.ldwh : nullptr;
+  bf16_t* What = a.What ? a.What + (int64_t)r * what_tiled_elems(a.d_out, a.d) : nullptr;
+  const int64_t nkw = (a.d + kWtCols - 1) / kWtCols;
   uint8_t* codes_out = a.codes_out ? a.codes_out + (int64_t)r * a.d_out * a.d : nullptr;
   float* s_out = a.s_out ? a.s_out + (int64_t)r * a.d_out * a.G : nullptr;
   float* m_out = a.m_out ? a.m_out + (int64_t)r * a.d_out * a.G : nullptr;
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     o.y = pack_bf16(fmaf(s, q[2], c) * dhi[2], fmaf(s, q[3], c) * dhi[3]);
     o.z = pack_bf16(fmaf(s, q[4], c) * dhi[4], fmaf(s, q[5], c) * dhi[5]);
     o.w = pack_bf16(fmaf(s, q[6], c) * dhi[6], fmaf(s, q[7], c) * dhi[7]);
-    if (What) *(u32x4*)(What + row * a.ldwh + c0) = o;
+    if (What) tw[w][rr][l] = o;
     if constexpr (EXP) {
       if (codes_out) {
         u32x2 cc;
@@ -179,6 +185,16 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
         s_out[o2] = s;
         m_out[o2] = gq.off;
       }
+    }
+  }
+  if (What) {
+    const int rr = l >> 3, oc = l & 7;
+    const int64_t row = row0 + rr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t c = chunk * 512 + i * 64 + oc * 8;
+      if (row < a.d_out && c < a.d)
+        *(u32x4*)(What + what_tiled_index(row, c, nkw)) = tw[w][rr][i * 8 + oc];
     }
   }
 }

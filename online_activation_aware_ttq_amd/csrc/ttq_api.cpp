@@ -179,7 +179,7 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
       P.path = 3;
     } else {
       // W_hat of up to rchunk requests at a time (at most kMaxWhatBytes)
-      const int64_t per = (int64_t)sizeof(uint16_t) * dout * what_ld(d);
+      const int64_t per = (int64_t)sizeof(uint16_t) * what_tiled_elems(dout, d);
       P.rchunk = per > 0 ? kMaxWhatBytes / per : R;
       if (P.rchunk < 1) P.rchunk = 1;
       if (P.rchunk > R) P.rchunk = R;
@@ -454,7 +454,6 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     QuantArgs qa{};
     qa.W = Wb; qa.d = d; qa.d_out = dout; qa.G = P.G; qa.R = (int)rc; qa.Nf = Nf;
     qa.dh = dh + r0 * d; qa.dhi = dhi + r0 * d; qa.What = What;
-    qa.ldwh = what_ld(d);
     qa.codes_out = codes_out ? codes_out + r0 * dout * d : nullptr;
     qa.s_out = scales_out ? scales_out + r0 * dout * P.G : nullptr;
     qa.m_out = mins_out ? mins_out + r0 * dout * P.G : nullptr;
@@ -462,7 +461,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     st = run(K_QUANT, s, [&](const Launch& L) { return launch_quant(qa, prm->group, L); });
     if (st != TTQ_OK) return st;
     GemmArgs ga{};
-    ga.A1 = Xb + r0 * T * d; ga.lda1 = d; ga.B1 = What; ga.ldb1 = what_ld(d);
+    ga.A1 = Xb + r0 * T * d; ga.lda1 = d; ga.B1 = What; ga.ldb1 = d; ga.b1_tiled = 1;
     ga.K1 = d;
     if (P.rp > 0) {
       ga.A2 = Zb + r0 * T * P.rp; ga.lda2 = P.rp;
@@ -471,7 +470,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     ga.M = T; ga.N = dout; ga.N_store = dout;
     ga.C = Y + r0 * T * dout; ga.ldc = dout;
     ga.batch = (int)rc;
-    ga.sA1 = T * d; ga.sB1 = dout * what_ld(d); ga.sA2 = T * P.rp; ga.sB2 = 0;
+    ga.sA1 = T * d; ga.sB1 = what_tiled_elems(dout, d); ga.sA2 = T * P.rp; ga.sB2 = 0;
     ga.sC = T * dout;
     st = run(K_GEMM, s, [&](const Launch& L) { return launch_gemm_lds(ga, L); });
     if (st != TTQ_OK) return st;

@@ -388,8 +388,7 @@ struct QuantArgs {
   float Nf;
   const float* dh;      // [R][d]
   const float* dhi;     // [R][d]
-  bf16_t* What;         // [R][d_out][ldwh]
-  int64_t ldwh;         // row stride of W_hat (elements, >= d)
+  bf16_t* What;         // [R][what_tiled_elems(d_out, d)], tiled (see below)
   uint8_t* codes_out;   // [R][d_out][d]
   float* s_out;         // [R][d_out][G]
   float* m_out;         // [R][d_out][G]
@@ -458,18 +457,32 @@ struct QFusedArgs {
 hipError_t launch_qfused(const QFusedArgs& a, int ntb, int group, int cb,
                          const Launch& L);
 
-// Row stride of the W_hat written by the quantize pass for the GEMM: d plus
-// 64 elements, so that the rows of one 64-channel slice fall in different L2
-// channels (with d a multiple of a power of two the rows of a tile slice
-// would otherwise map to few channels; measured 6-11 % on the GEMM).
-constexpr int64_t kWhatPad = 64;
-inline int64_t what_ld(int64_t d) { return d + kWhatPad; }
+// Layout of the W_hat the quantize pass writes for the GEMM: tiles of 256
+// rows x 64 channels stored contiguously (32 KiB), the tiles of a 256-row
+// block in channel order, blocks in row order:
+//   element (n, k) at ((n / 256) * ceil(K / 64) + k / 64) * 16384
+//                     + (n % 256) * 64 + k % 64.
+// One direct-to-LDS load of the GEMM (8 rows x 64 channels) is then 1 KiB of
+// contiguous memory instead of 8 row pieces 2 d bytes apart (measured on the
+// 7B-class layer: 5-14 % less GEMM time than row-major rows padded to
+// d + 64, which were themselves 6-11 % faster than unpadded rows).  Rows
+// past d_out in the last block are never written; the GEMM reads them only
+// into output columns it does not store.  Channels past K are not read.
+constexpr int64_t kWtRows = 256, kWtCols = 64;
+__host__ __device__ inline int64_t what_tiled_elems(int64_t d_out, int64_t K) {
+  return (d_out + kWtRows - 1) / kWtRows * kWtRows * ((K + kWtCols - 1) / kWtCols) * kWtCols;
+}
+__host__ __device__ inline int64_t what_tiled_index(int64_t n, int64_t k, int64_t nk) {
+  return ((n / kWtRows) * nk + k / kWtCols) * (kWtRows * kWtCols) + (n % kWtRows) * kWtCols +
+         k % kWtCols;
+}
 
 // C[M][N] (+)= A1[M][K1] B1[N][K1]^T + A2[M][K2] B2[N][K2]^T, fp32 accumulate.
 struct GemmArgs {
   const bf16_t* A1; int64_t lda1;
   const bf16_t* B1; int64_t ldb1;
   int64_t K1;
+  int b1_tiled;                     // B1 in the tiled W_hat layout (ldb1 unused)
   const bf16_t* A2; int64_t lda2;   // optional second segment (low rank)
   const bf16_t* B2; int64_t ldb2;
   int64_t K2;
