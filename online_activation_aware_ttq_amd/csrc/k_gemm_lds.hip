@@ -24,11 +24,13 @@
 //  * fragment reads for the next 16-channel step are interleaved with the
 //    MFMAs of the current one (register double buffer).
 // Tile order: the output tiles of all products of the batch are laid out in
-// strips of 8 N tiles (row by row inside a strip), and each of the 8 XCDs
-// (workgroups id, id + 8, ...) takes one contiguous eighth of that order, so
-// that the ~32 workgroups an XCD runs at once cover a patch of about 4 M x 8 N
-// tiles whose operand slices its L2 shares, and a partial last round is
-// spread evenly over the XCDs.  Operand loads carry the device-scope cache
+// strips of 8 N tiles (row by row inside a strip).  With one tile per
+// workgroup (fewer than four rounds of tiles) each of the 8 XCDs (workgroups
+// id, id + 8, ...) takes one contiguous eighth of that order, so that the ~32
+// workgroups an XCD runs at once cover a patch of about 4 M x 8 N tiles whose
+// operand slices its L2 shares, and a partial last round is spread evenly
+// over the XCDs; the persistent kernel deals 32-tile patches round-robin to
+// the XCDs instead (see there).  Operand loads carry the device-scope cache
 // bit (sc0; measured slightly faster than the default here).
 #include "ttq_internal.h"
 
@@ -317,8 +319,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds(GemmArgs a) {
 }
 
 // Persistent form of the single-buffered schedules: one workgroup per CU
-// walks its XCD's share of the tile order (the same tiles, in the same
-// order, as the one-tile-per-workgroup launch).  Measured on the 7B-class
+// walks its XCD's share of the tile order.  Measured on the 7B-class
 // layer (8 requests x 4096 tokens), split-load schedule, alternating runs:
 // q 1205 -> 1034 us, gate 2981 -> 2742, down 2781 -> 2550; one partial
 // round (T = 512) gains nothing, so fewer than four rounds keep one tile
@@ -353,12 +354,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds_p(GemmArgs a) {
   const int64_t per_product = mtiles * ntiles;
   const int64_t nprod = a.batch > 1 ? a.batch : 1;
   const int64_t total = per_product * nprod;
-  // this XCD's contiguous share of the tile order; this workgroup takes its
-  // tiles jj, jj + nper, ... (blocks of one XCD are id, id + 8, ...)
+  // the tile order is cut in chunks of 32 consecutive tiles (a 4 x 8 patch of
+  // one product), dealt round-robin to the XCDs: XCD x takes chunks x, x + 8,
+  // ..., and its workgroup jj the tiles jj, jj + nper, ... of that list
+  // (blocks of one XCD are id, id + 8, ...).  With 32 CUs per XCD all XCDs
+  // then work on the same product at a time, so the last-level cache holds
+  // one product's operands instead of eight (measured on the 7B-class layer
+  // against contiguous eighths per XCD: q 1130 -> 1015 us, gate 2770 ->
+  // 2420, down 2620 -> 2355).
   const int64_t xcd = blockIdx.x & 7, jj = blockIdx.x >> 3, nper = gridDim.x >> 3;
-  const int64_t base = total >> 3, extra = total & 7;
-  const int64_t cnt = base + (xcd < extra ? 1 : 0);
-  const int64_t first = xcd * base + min(xcd, extra);
+  const int64_t full = total / 256, rem = total % 256;
+  const int64_t cnt = full * 32 + min((int64_t)32, max((int64_t)0, rem - xcd * 32));
   if (jj >= cnt) return;
 
   // the current tile (plain locals: a local struct used inside the load
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void k_gemm_lds_p(GemmArgs a) {
   float* tC = nullptr;
   int64_t tm0 = 0, tn0 = 0, tmrows = 0, tnrows = 0;
   auto set_tile = [&](int64_t j) {
-    const int64_t t = first + j;
+    const int64_t t = (xcd + 8 * (j / 32)) * 32 + (j % 32);
     const int64_t z = t / per_product, tz = t % per_product;
     const int64_t strip = tz / (kStripN * mtiles), in_strip = tz % (kStripN * mtiles);
     const int64_t width = min((int64_t)kStripN, ntiles - strip * kStripN);
