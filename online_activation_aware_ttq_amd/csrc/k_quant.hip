@@ -70,13 +70,16 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int64_t nchunk = (a.d + 511) / 512;
   const int64_t nblk1 = (((a.d_out + QROWS - 1) / QROWS) * nchunk + 3) / 4;
-  // the R requests of one weight tile run back to back on the same XCD and
-  // share it through that XCD's L2
+  // requests one after the other, the last one first: the GEMM that follows
+  // starts with request 0, whose W_hat is then the most recently written
+  // (still in the last-level cache); W itself is small enough to stay there
+  // between the requests
   const int64_t b = blockIdx.x;
   const int xcd = (int)(b & 7);
   const int64_t jb = b >> 3;
-  const int64_t bq = (jb / a.R) * 8 + xcd;
-  const int r = (int)(jb % a.R);
+  const int64_t nq = (nblk1 + 7) / 8;
+  const int64_t bq = (jb % nq) * 8 + xcd;
+  const int r = a.R - 1 - (int)(jb / nq);
   if (bq >= nblk1) return;
   const int64_t wid = bq * 4 + w;
   const int64_t rgrp = wid / nchunk;
