@@ -38,6 +38,10 @@ METRIC = ("TTQ-linear tokens/s per projection + % HBM/MFMA roofline; "
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
+# one vector-ALU lane operation per lane and clock without packed fp32 math:
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (157.3 TFLOP/s counts an FMA as 2
+# and a packed pair as 2 more)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 ROTATE_BYTES = 640 * 2 ** 20
 FORMAT_NAMES = {"asym": "asymmetric", "sym": "symmetric",
                 "intzp": "integer zero point", "fp8": "FP8 E4M3"}
@@ -196,11 +200,26 @@ def kernel_units(kind: str, d, d_out, T, R, rank):
     return 0, 0
 
 
+def alu_ops(kind: str, d, d_out, R) -> float:
+    """Vector-ALU operations of the quantization in one launch: per weight
+    element and request the scaling u = w D^{1/2}, the group minimum and
+    maximum, t = (u - m) / s as a subtraction and a product, the rounding,
+    and (one-token kernel only) the product with x' -- 7 and 6 operations."""
+    per = {"gemv_t1": 7, "fused_qdq_mfma": 6}.get(kind, 0)
+    return float(per) * R * d_out * d
+
+
 def roofline(kind: str, ms_per_launch: float, bytes_per_launch: float,
-             flops_per_launch: float, traffic=None) -> dict:
+             flops_per_launch: float, traffic=None, ops_per_launch: float = 0.0
+             ) -> dict:
     t_hbm = bytes_per_launch / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops_per_launch / (BF16_PEAK_TFLOPS * 1e12)
-    if t_hbm >= t_mfma:
+    t_alu = ops_per_launch / (VALU_PEAK_TOPS * 1e12)
+    if t_alu > max(t_hbm, t_mfma):
+        a = ops_per_launch / (ms_per_launch * 1e-3) / 1e12
+        r = {"bound": "alu", "achieved": a, "peak": VALU_PEAK_TOPS,
+             "unit": "Tops/s", "frac": a / VALU_PEAK_TOPS}
+    elif t_hbm >= t_mfma:
         a = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
         r = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
              "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
@@ -212,6 +231,8 @@ def roofline(kind: str, ms_per_launch: float, bytes_per_launch: float,
     r.update(kernel=kind, kernel_ms=ms_per_launch,
              alg_bytes_per_launch=bytes_per_launch,
              alg_flops_per_launch=flops_per_launch)
+    if ops_per_launch:
+        r["alg_alu_ops_per_launch"] = ops_per_launch
     return r
 
 
@@ -299,14 +320,15 @@ def leg_c5(torch, ttq, T: int, steps: int, warmup: int, want_gemm: bool,
     out["mfma_frac_step"] = fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
     # dominant kernel: the largest share of the step's kernel time
     dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
-    ub = uf = 0
+    ub = uf = uo = 0
     for p in projs:
         b_, f_ = kernel_units(dom, p["d"], p["d_out"], T, R, rank)
         ub += b_
         uf += f_
+        uo += alu_ops(dom, p["d"], p["d_out"], R)
     n_l = kt[dom][1]
     out["roofline"] = roofline(dom, kt[dom][0], ub / n_l, uf / n_l,
-                               traffic_entry(dom, f"c5_T{T}"))
+                               traffic_entry(dom, f"c5_T{T}"), uo / n_l)
     if per_projection:
         pp = {}
         for p in projs:
