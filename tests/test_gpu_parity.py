@@ -125,6 +125,42 @@ def test_gemm_more_tiles_than_cus(R):
     _say(f"tail_R{R}", rep)
 
 
+def test_persistent_gemm_ragged_tiles():
+    """Enough 256 x 256 tiles for the persistent GEMM (more than four rounds
+    of the chip's CUs) with every edge at once: ragged token tiles (T = 1000),
+    ragged weight-row tiles (d_out = 4000), a channel count that ends in half
+    a 64-channel k-tile (d = 544, groups of 32) in the tiled W_hat, a tile
+    count whose last round of 32-tile patches is partial (17 requests), and
+    a ragged low-rank segment (r = 40)."""
+    prob = make_problem("persist", d=544, d_out=4000, T=1000, R=17, bits=4,
+                        group=32, rank=40, x_kind="logu10_100", n_outliers=8,
+                        seed=71)
+    rows = np.unique(np.concatenate([
+        np.arange(8), np.arange(3832, 3848), np.arange(4000 - 8, 4000),
+        np.random.default_rng(7).choice(4000, 24, replace=False)]))
+    print(f"[case] persistent GEMM R=17 T=1000 d=544 d_out=4000 rows={len(rows)}",
+          flush=True)
+    gpu = run_gpu(prob, rows=rows, exports=False)
+    rep = check_problem(prob, gpu, rows=rows, check_codes=False)
+    _say("persist", rep)
+
+
+def test_split_schedule_gemm_ragged_tiles():
+    """One partial round of 256 x 256 tiles (one tile per workgroup, the
+    split-load schedule) with ragged token and weight-row tiles and a
+    channel count ending in half a k-tile of the tiled W_hat."""
+    prob = make_problem("split1", d=544, d_out=11000, T=600, bits=4, group=32,
+                        rank=24, x_kind="logu10_100", n_outliers=8, seed=72)
+    rows = np.unique(np.concatenate([
+        np.arange(8), np.arange(10744, 10760), np.arange(11000 - 8, 11000),
+        np.random.default_rng(8).choice(11000, 24, replace=False)]))
+    print(f"[case] split-schedule GEMM T=600 d=544 d_out=11000 rows={len(rows)}",
+          flush=True)
+    gpu = run_gpu(prob, rows=rows, exports=False)
+    rep = check_problem(prob, gpu, rows=rows, check_codes=False)
+    _say("split1", rep)
+
+
 GEMM_Q_CASES = [
     # the GEMM that quantizes its own weight tiles (129 <= T <= 256): every
     # group size, ragged token / row tiles, low-rank segments of one, two and
