@@ -45,7 +45,10 @@ namespace ttq {
 
 constexpr int FW = 8;  // waves per workgroup
 
-template <int NTB, int GS, bool DH_LDS, bool EXPORT, int QF>
+// RB: 16-row blocks per workgroup; they share every activation load, which
+// divides the activations' L2 -> CU traffic (the binding resource when every
+// workgroup re-reads x') by RB.
+template <int NTB, int GS, bool DH_LDS, bool EXPORT, int QF, int RB>
 __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   constexpr int NKS = GS / 32;
   constexpr bool HILO = (NTB == 1);
@@ -54,17 +57,15 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const int64_t b = blockIdx.x;
   const int xcd = (int)(b & 7);
   const int64_t jb = b >> 3;
-  const int64_t rb = (jb / a.R) * 8 + xcd;
   const int req = (int)(jb % a.R);
-  if (rb >= a.rowblocks) return;
+  const int64_t rb0 = ((jb / a.R) * 8 + xcd) * RB;
+  if (rb0 >= a.rowblocks) return;
 
   const int tid = threadIdx.x, l = tid & 63;
   // wave index as a scalar: the group loop below is then wave-uniform control
   // flow (a per-lane counter would make every loop exit a divergent branch)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = l & 15, qd = l >> 4;
-  const int64_t row = rb * 16 + lr;
-  const bool row_ok = row < a.d_out;
   const int64_t T = a.T, d = a.d;
   const int G = a.G;
   const int Tp = NTB * 16;
@@ -73,28 +74,35 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 : 1) * Tp * d;
   const float* sx = a.sx + (int64_t)req * G * Tp;
   const bf16_t* xs_lo = xs + (int64_t)Tp * d;
-  // the workgroup's weight rows as one bounded buffer: rows past d_out and
-  // groups past the end read as zeros without memory traffic
-  const int64_t rows_here = min((int64_t)16, a.d_out - rb * 16);
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(a.W + rb * 16 * d, (uint32_t)(rows_here * d * 2));
+  // each row block's weight rows as one bounded buffer: rows past d_out and
+  // groups past the end read as zeros without memory traffic (separate
+  // scalars rather than an array or structure: see the persistent GEMM)
+  const int64_t rh0 = min((int64_t)16, a.d_out - rb0 * 16);
+  const int64_t rh1 = RB > 1 ? max((int64_t)0, min((int64_t)16, a.d_out - (rb0 + 1) * 16)) : 0;
+  const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(a.W + rb0 * 16 * d, (uint32_t)(rh0 * d * 2));
+  const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(a.W + (rb0 + (RB > 1 ? 1 : 0)) * 16 * d,
+                                               (uint32_t)(rh1 * d * 2));
   const uint32_t lane_off = (uint32_t)((lr * d + qd * 8) * 2);
   const float Nf = a.Nf;
 
-  f32x4 acc[NTB];
+  f32x4 acc[RB][NTB];
 #pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // T <= 16: lane l holds token l & 15 of the activation operand
   u32x4 xh[NKS], xl[NKS];
   f32x4 sxv0;
 
-  auto load_w = [&](u32x4 (&wv)[NKS], int g) {
+  auto load_w = [&](u32x4 (&wv)[RB][NKS], int g) {
     const uint32_t soff = g < G ? (uint32_t)g * GS * 2 : kOutOfRange;
 #pragma unroll
-    for (int k = 0; k < NKS; ++k)
-      wv[k] = HILO ? buf_load16(wr, lane_off + k * 64, soff)
-                   : buf_load16_nt(wr, lane_off + k * 64, soff);
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int k = 0; k < NKS; ++k)
+        wv[r][k] = HILO ? buf_load16(r ? wr1 : wr0, lane_off + k * 64, soff)
+                        : buf_load16_nt(r ? wr1 : wr0, lane_off + k * 64, soff);
   };
   // fragment-ordered x' (zero past T): each load is 1 KiB per wave
   auto load_x = [&](int g) {
@@ -109,117 +117,131 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     }
   };
 
-  auto process = [&](const u32x4 (&wv)[NKS], int g) {
+  auto process = [&](const u32x4 (&wv)[RB][NKS], int g) {
     const int64_t colg = (int64_t)g * GS + qd * 8;
-    // u = fl(w * dh), group min / max
-    float u[NKS][8];
-    float mn = __builtin_inff(), mx = -__builtin_inff();
+    u32x4 qv[RB][NKS];
+    float sr[RB], mcr[RB];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) {
-      f32x4 d0, d1;
-      if (DH_LDS) {
-        d0 = *(const f32x4*)(lds + colg + k * 32);
-        d1 = *(const f32x4*)(lds + colg + k * 32 + 4);
-      } else {
-        d0 = *(const f32x4*)(dhg + colg + k * 32);
-        d1 = *(const f32x4*)(dhg + colg + k * 32 + 4);
-      }
-      u[k][0] = bf16lo(wv[k].x) * d0.x;
-      u[k][1] = bf16hi(wv[k].x) * d0.y;
-      u[k][2] = bf16lo(wv[k].y) * d0.z;
-      u[k][3] = bf16hi(wv[k].y) * d0.w;
-      u[k][4] = bf16lo(wv[k].z) * d1.x;
-      u[k][5] = bf16hi(wv[k].z) * d1.y;
-      u[k][6] = bf16lo(wv[k].w) * d1.z;
-      u[k][7] = bf16hi(wv[k].w) * d1.w;
+    for (int r = 0; r < RB; ++r) {
+      const int64_t row = (rb0 + r) * 16 + lr;
+      const bool row_ok = row < a.d_out;
+      // u = fl(w * dh), group min / max
+      float u[NKS][8];
+      float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        mn = fminf(mn, u[k][j]);
-        mx = fmaxf(mx, u[k][j]);
+      for (int k = 0; k < NKS; ++k) {
+        f32x4 d0, d1;
+        if (DH_LDS) {
+          d0 = *(const f32x4*)(lds + colg + k * 32);
+          d1 = *(const f32x4*)(lds + colg + k * 32 + 4);
+        } else {
+          d0 = *(const f32x4*)(dhg + colg + k * 32);
+          d1 = *(const f32x4*)(dhg + colg + k * 32 + 4);
+        }
+        u[k][0] = bf16lo(wv[r][k].x) * d0.x;
+        u[k][1] = bf16hi(wv[r][k].x) * d0.y;
+        u[k][2] = bf16lo(wv[r][k].y) * d0.z;
+        u[k][3] = bf16hi(wv[r][k].y) * d0.w;
+        u[k][4] = bf16lo(wv[r][k].z) * d1.x;
+        u[k][5] = bf16hi(wv[r][k].z) * d1.y;
+        u[k][6] = bf16lo(wv[r][k].w) * d1.z;
+        u[k][7] = bf16hi(wv[r][k].w) * d1.w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          mn = fminf(mn, u[k][j]);
+          mx = fmaxf(mx, u[k][j]);
+        }
       }
-    }
-    mn = fminf(mn, __shfl_xor(mn, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mn = fminf(mn, __shfl_xor(mn, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mn = fminf(mn, __shfl_xor(mn, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mn = fminf(mn, __shfl_xor(mn, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-    // s = fl(fl(M - m) / N), inv = fl(1 / s); IEEE division, no contraction
-    // (other formats: see QFmt)
-    const QGroup gq = qgroup<QF>(mn, mx, Nf);
-    const float s = gq.s;
-    const float inv = gq.inv;
+      // s = fl(fl(M - m) / N), inv = fl(1 / s); IEEE division, no
+      // contraction (other formats: see QFmt)
+      const QGroup gq = qgroup<QF>(mn, mx, Nf);
+      const float inv = gq.inv;
+      sr[r] = gq.s;
 
-    // codes q = rint(fl(fl(u - m) * inv)), packed as bf16 pairs.  The clamp to
-    // [0, N] of the definition is a no-op here: 0 <= u - m <= M - m, and the
-    // largest t is N (1 + e) with |e| < 4e-7 for the three roundings, so
-    // rint(t) stays in [0, N] for every finite input (NaN propagates to Y).
-    u32x4 qv[NKS];
+      // codes q = rint(fl(fl(u - m) * inv)), packed as bf16 pairs.  The clamp
+      // to [0, N] of the definition is a no-op here: 0 <= u - m <= M - m, and
+      // the largest t is N (1 + e) with |e| < 4e-7 for the three roundings,
+      // so rint(t) stays in [0, N] for every finite input (NaN propagates to
+      // Y).
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) {
-      float q[8];
-      if constexpr (QF == QF_ASYM) {
+      for (int k = 0; k < NKS; ++k) {
+        float q[8];
+        if constexpr (QF == QF_ASYM) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) q[j] = __builtin_rintf((u[k][j] - mn) * inv);
-      } else {
-        qlevels8<QF>(gq, u[k], q);
+          for (int j = 0; j < 8; ++j) q[j] = __builtin_rintf((u[k][j] - mn) * inv);
+        } else {
+          qlevels8<QF>(gq, u[k], q);
+        }
+        qv[r][k].x = __builtin_amdgcn_perm(__float_as_uint(q[1]),
+                                           __float_as_uint(q[0]), 0x07060302u);
+        qv[r][k].y = __builtin_amdgcn_perm(__float_as_uint(q[3]),
+                                           __float_as_uint(q[2]), 0x07060302u);
+        qv[r][k].z = __builtin_amdgcn_perm(__float_as_uint(q[5]),
+                                           __float_as_uint(q[4]), 0x07060302u);
+        qv[r][k].w = __builtin_amdgcn_perm(__float_as_uint(q[7]),
+                                           __float_as_uint(q[6]), 0x07060302u);
+        if (EXPORT && a.codes_out && row_ok) {
+          u32x2 c;
+          c.x = qcode<QF>(gq, q[0]) | (qcode<QF>(gq, q[1]) << 8) |
+                (qcode<QF>(gq, q[2]) << 16) | (qcode<QF>(gq, q[3]) << 24);
+          c.y = qcode<QF>(gq, q[4]) | (qcode<QF>(gq, q[5]) << 8) |
+                (qcode<QF>(gq, q[6]) << 16) | (qcode<QF>(gq, q[7]) << 24);
+          *(u32x2*)(a.codes_out + ((int64_t)req * a.d_out + row) * d + colg +
+                    k * 32) = c;
+        }
       }
-      qv[k].x = __builtin_amdgcn_perm(__float_as_uint(q[1]),
-                                      __float_as_uint(q[0]), 0x07060302u);
-      qv[k].y = __builtin_amdgcn_perm(__float_as_uint(q[3]),
-                                      __float_as_uint(q[2]), 0x07060302u);
-      qv[k].z = __builtin_amdgcn_perm(__float_as_uint(q[5]),
-                                      __float_as_uint(q[4]), 0x07060302u);
-      qv[k].w = __builtin_amdgcn_perm(__float_as_uint(q[7]),
-                                      __float_as_uint(q[6]), 0x07060302u);
-      if (EXPORT && a.codes_out && row_ok) {
-        u32x2 c;
-        c.x = qcode<QF>(gq, q[0]) | (qcode<QF>(gq, q[1]) << 8) |
-              (qcode<QF>(gq, q[2]) << 16) | (qcode<QF>(gq, q[3]) << 24);
-        c.y = qcode<QF>(gq, q[4]) | (qcode<QF>(gq, q[5]) << 8) |
-              (qcode<QF>(gq, q[6]) << 16) | (qcode<QF>(gq, q[7]) << 24);
-        *(u32x2*)(a.codes_out + ((int64_t)req * a.d_out + row) * d + colg +
-                  k * 32) = c;
+      if (EXPORT && a.s_out && row_ok && qd == 0) {
+        const int64_t o = ((int64_t)req * a.d_out + row) * G + g;
+        a.s_out[o] = gq.s;
+        a.m_out[o] = gq.off;
       }
+      mcr[r] = QF == QF_ASYM ? mn : 0.f;
     }
-    if (EXPORT && a.s_out && row_ok && qd == 0) {
-      const int64_t o = ((int64_t)req * a.d_out + row) * G + g;
-      a.s_out[o] = s;
-      a.m_out[o] = gq.off;
-    }
-    const float mc = QF == QF_ASYM ? mn : 0.f;
 
     // contraction on the matrix cores + per-group affine epilogue
     if (NTB == 1) {
-      f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < NKS; ++k) {
-        const bf16x8 q = __builtin_bit_cast(bf16x8, qv[k]);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xh[k]), q, P, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xl[k]), q, P, 0, 0, 0);
+      for (int r = 0; r < RB; ++r) {
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NKS; ++k) {
+          const bf16x8 q = __builtin_bit_cast(bf16x8, qv[r][k]);
+          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, xh[k]), q, P, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, xl[k]), q, P, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[r][0][i] = fmaf(sr[r], P[i], fmaf(mcr[r], sxv0[i], acc[r][0][i]));
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[0][i] = fmaf(s, P[i], fmaf(mc, sxv0[i], acc[0][i]));
     } else {
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        // fragment-ordered x' (zero past T): each load is 1 KiB per wave
+        // fragment-ordered x' (zero past T): each load is 1 KiB per wave,
+        // shared by the RB row blocks
         u32x4 xv[NKS];
 #pragma unroll
         for (int k = 0; k < NKS; ++k)
           xv[k] = *(const u32x4*)(xs + 8 * xs_frag_index(g, tb, k, l, NTB, GS));
         const f32x4 sxv = *(const f32x4*)(sx + (int64_t)g * Tp + tb * 16 + qd * 4);
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < NKS; ++k)
-          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, xv[k]),
-              __builtin_bit_cast(bf16x8, qv[k]), P, 0, 0, 0);
+        for (int r = 0; r < RB; ++r) {
+          f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[tb][i] = fmaf(s, P[i], fmaf(mc, sxv[i], acc[tb][i]));
+          for (int k = 0; k < NKS; ++k)
+            P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, xv[k]),
+                __builtin_bit_cast(bf16x8, qv[r][k]), P, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[r][tb][i] = fmaf(sr[r], P[i], fmaf(mcr[r], sxv[i], acc[r][tb][i]));
+        }
       }
     }
   };
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   // issued after this group's activation loads, so waiting for the latter
   // does not wait for the former, and no register copies are needed
   // (a prefetch past the last group is out of range: zeros, no traffic)
-  u32x4 wa[NKS], wb[NKS];
+  u32x4 wa[RB][NKS], wb[RB][NKS];
   int g = w;
   if (DH_LDS) {
     // D^{1/2} of this request into LDS before the first weight loads: once
@@ -267,45 +289,57 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     const int nk = a.rp / 32;
     for (int kk = w; kk < nk; kk += FW) {
       const int c8 = kk * 32 + qd * 8;
-      const u32x4 bv = (row_ok && c8 < a.rank)
-                           ? *(const u32x4*)(a.Blr + row * a.rank + c8)
-                           : u32x4{0u, 0u, 0u, 0u};
+      u32x4 bv[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int64_t row = (rb0 + r) * 16 + lr;
+        bv[r] = (row < a.d_out && c8 < a.rank)
+                    ? *(const u32x4*)(a.Blr + row * a.rank + c8)
+                    : u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         const int64_t tok = tb * 16 + lr;
         const u32x4 zv =
             tok < T ? *(const u32x4*)(a.Z + ((int64_t)req * T + tok) * a.rp + c8)
                     : u32x4{0u, 0u, 0u, 0u};
-        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, bv),
-            acc[tb], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+          acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, bv[r]),
+              acc[r][tb], 0, 0, 0);
       }
     }
   }
 
-  // combine the 8 waves in a fixed order (LDS reused after the main loop)
-  if (DH_LDS) __syncthreads();
+  // combine the 8 waves in a fixed order, one row block at a time (LDS reused
+  // after the main loop)
+  float* Y = a.Y + (int64_t)req * T * a.d_out;
   float* red = lds;  // [FW][NTB * 4][64]
 #pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
+  for (int r = 0; r < RB; ++r) {
+    if (DH_LDS || r > 0) __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(w * NTB * 4 + tb * 4 + i) * 64 + l] = acc[tb][i];
-  __syncthreads();
-  float* Y = a.Y + (int64_t)req * T * a.d_out;
-  for (int e = tid; e < NTB * 256; e += FW * 64) {
-    const int ti = e >> 6, ll = e & 63;
-    const int64_t tok = (ti >> 2) * 16 + (ll >> 4) * 4 + (ti & 3);
-    const int64_t rowx = rb * 16 + (ll & 15);
-    if (tok < T && rowx < a.d_out) {
-      float v = red[ti * 64 + ll];
+    for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-      for (int ww = 1; ww < FW; ++ww) v += red[(ww * NTB * 4 + ti) * 64 + ll];
-      Y[tok * a.d_out + rowx] = v;
+      for (int i = 0; i < 4; ++i)
+        red[(w * NTB * 4 + tb * 4 + i) * 64 + l] = acc[r][tb][i];
+    __syncthreads();
+    for (int e = tid; e < NTB * 256; e += FW * 64) {
+      const int ti = e >> 6, ll = e & 63;
+      const int64_t tok = (ti >> 2) * 16 + (ll >> 4) * 4 + (ti & 3);
+      const int64_t rowx = (rb0 + r) * 16 + (ll & 15);
+      if (tok < T && rowx < a.d_out) {
+        float v = red[ti * 64 + ll];
+#pragma unroll
+        for (int ww = 1; ww < FW; ++ww) v += red[(ww * NTB * 4 + ti) * 64 + ll];
+        Y[tok * a.d_out + rowx] = v;
+      }
     }
   }
 }
 
-template <int NTB, bool DHL, int QF>
+template <int NTB, bool DHL, int QF, int RB>
 static hipError_t launch_fused_ntb(const FusedArgs& a, int group, dim3 grid,
                                    uint32_t lds, const Launch& L) {
   const dim3 blk(FW * 64);
@@ -314,40 +348,59 @@ static hipError_t launch_fused_ntb(const FusedArgs& a, int group, dim3 grid,
   const bool exp = a.codes_out || a.s_out;
 #define TTQ_FUSED_CASE(GSV)                                                    \
   case GSV:                                                                    \
-    return exp ? ext_launch(k_fused<NTB, GSV, DHL, true, QF>, grid, blk, lds, L, \
-                            a)                                                 \
-               : ext_launch(k_fused<NTB, GSV, DHL, false, QF>, grid, blk, lds, \
-                            L, a);
+    return exp ? ext_launch(k_fused<NTB, GSV, DHL, true, QF, RB>, grid, blk,   \
+                            lds, L, a)                                         \
+               : ext_launch(k_fused<NTB, GSV, DHL, false, QF, RB>, grid, blk,  \
+                            lds, L, a);
   switch (group) {
     TTQ_FUSED_CASE(32)
     TTQ_FUSED_CASE(64)
     TTQ_FUSED_CASE(128)
-    TTQ_FUSED_CASE(256)
+    case 256:
+      // two row blocks of 256-channel groups would not fit in registers
+      if constexpr (RB == 1) {
+        return exp ? ext_launch(k_fused<NTB, 256, DHL, true, QF, 1>, grid, blk,
+                                lds, L, a)
+                   : ext_launch(k_fused<NTB, 256, DHL, false, QF, 1>, grid, blk,
+                                lds, L, a);
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 #undef TTQ_FUSED_CASE
 }
 
-template <bool DHL, int QF>
-static hipError_t launch_fused_qf(const FusedArgs& a, int ntb, int group,
+template <bool DHL, int QF, int RB>
+static hipError_t launch_fused_rb(const FusedArgs& a, int ntb, int group,
                                   dim3 grid, uint32_t lds, const Launch& L) {
   switch (ntb) {
-    case 1: return launch_fused_ntb<1, DHL, QF>(a, group, grid, lds, L);
-    case 2: return launch_fused_ntb<2, DHL, QF>(a, group, grid, lds, L);
-    case 4: return launch_fused_ntb<4, DHL, QF>(a, group, grid, lds, L);
-    case 8: return launch_fused_ntb<8, DHL, QF>(a, group, grid, lds, L);
+    case 1:
+      // (one token tile: the kernel is bound by its vector ALU work, and the
+      // host takes one row block)
+      if constexpr (RB == 1) return launch_fused_ntb<1, DHL, QF, 1>(a, group, grid, lds, L);
+      return hipErrorInvalidValue;
+    case 2: return launch_fused_ntb<2, DHL, QF, RB>(a, group, grid, lds, L);
+    case 4: return launch_fused_ntb<4, DHL, QF, RB>(a, group, grid, lds, L);
+    case 8: return launch_fused_ntb<8, DHL, QF, RB>(a, group, grid, lds, L);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <bool DHL, int QF>
+static hipError_t launch_fused_qf(const FusedArgs& a, int ntb, int group, int rb,
+                                  dim3 grid, uint32_t lds, const Launch& L) {
+  return rb == 2 ? launch_fused_rb<DHL, QF, 2>(a, ntb, group, grid, lds, L)
+                 : launch_fused_rb<DHL, QF, 1>(a, ntb, group, grid, lds, L);
+}
+
 template <bool DHL>
-static hipError_t launch_fused_dhl(const FusedArgs& a, int ntb, int group,
+static hipError_t launch_fused_dhl(const FusedArgs& a, int ntb, int group, int rb,
                                    dim3 grid, uint32_t lds, const Launch& L) {
   switch (a.qf) {
-    case QF_ASYM: return launch_fused_qf<DHL, QF_ASYM>(a, ntb, group, grid, lds, L);
-    case QF_SYM: return launch_fused_qf<DHL, QF_SYM>(a, ntb, group, grid, lds, L);
-    case QF_INTZP: return launch_fused_qf<DHL, QF_INTZP>(a, ntb, group, grid, lds, L);
-    case QF_FP8: return launch_fused_qf<DHL, QF_FP8>(a, ntb, group, grid, lds, L);
+    case QF_ASYM: return launch_fused_qf<DHL, QF_ASYM>(a, ntb, group, rb, grid, lds, L);
+    case QF_SYM: return launch_fused_qf<DHL, QF_SYM>(a, ntb, group, rb, grid, lds, L);
+    case QF_INTZP: return launch_fused_qf<DHL, QF_INTZP>(a, ntb, group, rb, grid, lds, L);
+    case QF_FP8: return launch_fused_qf<DHL, QF_FP8>(a, ntb, group, rb, grid, lds, L);
     default: return hipErrorInvalidValue;
   }
 }
@@ -359,15 +412,17 @@ size_t fused_lds_bytes(int64_t d, int ntb, bool* dh_in_lds) {
   return *dh_in_lds ? (dhb > red ? dhb : red) : red;
 }
 
-hipError_t launch_fused(const FusedArgs& a, int ntb, int group,
+hipError_t launch_fused(const FusedArgs& a, int ntb, int group, int rb,
                         const Launch& L) {
-  const int64_t nblk = ((a.rowblocks + 7) / 8) * 8 * a.R;
+  if (rb != 1 && rb != 2) return hipErrorInvalidValue;
+  const int64_t pairs = (a.rowblocks + rb - 1) / rb;
+  const int64_t nblk = ((pairs + 7) / 8) * 8 * a.R;
   if (nblk == 0) return hipSuccess;
   bool dh_in = false;
   const uint32_t lds = (uint32_t)fused_lds_bytes(a.d, ntb, &dh_in);
   dim3 grid((unsigned)nblk);
-  return dh_in ? launch_fused_dhl<true>(a, ntb, group, grid, lds, L)
-               : launch_fused_dhl<false>(a, ntb, group, grid, lds, L);
+  return dh_in ? launch_fused_dhl<true>(a, ntb, group, rb, grid, lds, L)
+               : launch_fused_dhl<false>(a, ntb, group, rb, grid, lds, L);
 }
 
 }  // namespace ttq

@@ -352,7 +352,9 @@ struct FusedArgs {
 };
 // D^{1/2} is staged in LDS when it fits in this many bytes.
 constexpr size_t kFusedDhLdsMax = 64 * 1024;
-hipError_t launch_fused(const FusedArgs& a, int ntb, int group,
+// rb: 16-row blocks per workgroup (1, or 2 for groups of up to 128 and
+// ntb >= 2)
+hipError_t launch_fused(const FusedArgs& a, int ntb, int group, int rb,
                         const Launch& L);
 
 struct GemvArgs {

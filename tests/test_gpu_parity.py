@@ -161,6 +161,45 @@ def test_split_schedule_gemm_ragged_tiles():
     _say("split1", rep)
 
 
+ROW_PAIR_CASES = [
+    # fused path with two 16-row blocks per workgroup (taken for T > 16 when
+    # that still leaves at least 256 workgroups): a ragged last pair (odd
+    # row-block count), ragged tokens in every token-tile count, group sizes
+    # 32 / 64 / 128 with an odd group count, low rank, p = 1, every quantizer
+    # format; T = 16 (one row block, hi + lo activations) beside them
+    ("rp_T100_g128", dict(d=512, d_out=2064, T=100, R=4, bits=4, group=128,
+                          rank=32, x_kind="logu10_100", n_outliers=5,
+                          seed=81)),
+    ("rp_T40_g64_G9", dict(d=576, d_out=1000, T=40, R=8, bits=3, group=64,
+                           rank=8, seed=82)),
+    ("rp_T128_g32_p1", dict(d=256, d_out=4080, T=128, R=2, bits=2, group=32,
+                            p=1.0, lam=1e-2, x_kind="t3_logu30_100",
+                            n_outliers=3, seed=83)),
+    ("rp_T16_hilo", dict(d=512, d_out=1040, T=16, R=8, bits=4, group=128,
+                         rank=32, x_kind="logu10_100", n_outliers=5, seed=84)),
+    ("rp_T17_g64", dict(d=384, d_out=1010, T=17, R=8, bits=4, group=64,
+                        seed=85)),
+    ("rp_T24_sym4", dict(d=256, d_out=1040, T=24, R=8, bits=4, group=128,
+                         qformat="sym", x_kind="logu10_100", n_outliers=3,
+                         seed=86)),
+    ("rp_T64_intzp3", dict(d=256, d_out=1040, T=64, R=8, bits=3, group=64,
+                           qformat="intzp", rank=16, seed=87)),
+    ("rp_T128_fp8", dict(d=256, d_out=1040, T=128, R=8, bits=8, group=128,
+                         qformat="fp8", x_kind="logu10_100", n_outliers=3,
+                         seed=88)),
+]
+
+
+@pytest.mark.parametrize("name,kw", ROW_PAIR_CASES,
+                         ids=[c[0] for c in ROW_PAIR_CASES])
+def test_fused_row_pairs(name, kw):
+    prob = make_problem(name, **kw)
+    _run_and_check(prob, 0, name)
+    # without exports (the other instantiation): the same bars
+    rep = check_problem(prob, run_gpu(prob, exports=False), check_codes=False)
+    _say(name + "_noexport", rep)
+
+
 GEMM_Q_CASES = [
     # the GEMM that quantizes its own weight tiles (129 <= T <= 256): every
     # group size, ragged token / row tiles, low-rank segments of one, two and
