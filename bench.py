@@ -240,9 +240,11 @@ def kernel_src_sha(kind: str) -> str:
     p = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
                      KERNEL_SOURCES.get(kind, "k_fused.hip"))
     h = hashlib.sha256(open(p, "rb").read())
-    # the shared header changes every kernel
-    h.update(open(os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
-                               "ttq_internal.h"), "rb").read())
+    # the shared headers change every kernel
+    cdir = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc")
+    for name in sorted(os.listdir(cdir)):
+        if name.endswith(".h"):
+            h.update(open(os.path.join(cdir, name), "rb").read())
     return h.hexdigest()[:16]
 
 

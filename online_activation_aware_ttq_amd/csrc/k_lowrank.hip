@@ -98,29 +98,29 @@ __global__ __launch_bounds__(256) void k_lowrank_zsum(LowRankZArgs a, int nsplit
   const int64_t n = a.M * a.rp;
   if (i >= n) return;
   // slice order; the loads of 16 slices are in flight together
-  float v = a.part[i];
-  int z = 1;
-  for (; z + 16 <= nsplit; z += 16) {
+  float v = 0.f;
+  for (int z0 = 0; z0 < nsplit; z0 += 16) {
     float t[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) t[j] = a.part[(int64_t)(z + j) * n + i];
+    for (int j = 0; j < 16; ++j)
+      t[j] = z0 + j < nsplit ? a.part[(int64_t)(z0 + j) * n + i] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v += t[j];
+    for (int j = 0; j < 16; ++j)
+      if (z0 + j < nsplit) v = (z0 + j == 0) ? t[j] : v + t[j];
   }
-  for (; z < nsplit; ++z) v += a.part[(int64_t)z * n + i];
   a.Z[i] = (bf16_t)f2bf(v);
 }
 
 }  // namespace
 
-// channel slices: about 128 workgroups, each over at least 256 channels
-// (the slices are summed by a second kernel; few of them keep it short)
-// Channel slices of about 256 channels, fixed by d alone as long as the fp32
-// partials fit in 64 MiB: the slices and the order of their sum, hence every
-// bit of a token's Z, then do not depend on how many tokens or requests
-// share the launch.
-int lowrank_z_splits(int64_t M, int64_t d, int rp) {
-  int64_t s = (d + 255) / 256;
+// Channel slices of `slice` channels (256 for this kernel: a workgroup of 4
+// waves x 64 channels; 128 for the partials the small-T statistics kernel
+// writes, one 32-channel step per wave), fixed by d alone as long as the
+// fp32 partials fit in 64 MiB: the slices and the order of their sum, hence
+// every bit of a token's Z, then do not depend on how many tokens or
+// requests share the launch.
+int lowrank_z_splits(int64_t M, int64_t d, int rp, int slice) {
+  int64_t s = (d + slice - 1) / slice;
   const int64_t per = (M > 0 ? M : 1) * (rp > 0 ? rp : 1) * (int64_t)sizeof(float);
   const int64_t cap = (int64_t(64) << 20) / per;
   if (s > cap) s = cap;
@@ -130,7 +130,7 @@ int lowrank_z_splits(int64_t M, int64_t d, int rp) {
 hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L) {
   if (a.M == 0) return hipSuccess;
   if (!a.part || a.rp % 32 != 0) return hipErrorInvalidValue;
-  const int s = lowrank_z_splits(a.M, a.d, a.rp);
+  const int s = lowrank_z_splits(a.M, a.d, a.rp, 256);
   // slice length: a multiple of 128 channels (32 per wave)
   const int64_t kslice = ((a.d + s - 1) / s + 127) / 128 * 128;
   const dim3 grid((unsigned)((a.M + 15) / 16),
@@ -138,12 +138,12 @@ hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L) {
   return ext_launch(k_lowrank_zpart, grid, dim3(ZW * 64), 0, L, a, kslice);
 }
 
-hipError_t launch_lowrank_z_sum(const LowRankZArgs& a, const Launch& L) {
+hipError_t launch_lowrank_z_sum(const LowRankZArgs& a, int nsplit, const Launch& L) {
   const int64_t n = a.M * a.rp;
   if (n == 0) return hipSuccess;
-  const int s = lowrank_z_splits(a.M, a.d, a.rp);
+  if (nsplit < 1) return hipErrorInvalidValue;
   return ext_launch(k_lowrank_zsum, dim3((unsigned)((n + 255) / 256)), dim3(256),
-                    0, L, a, s);
+                    0, L, a, nsplit);
 }
 
 }  // namespace ttq

@@ -196,6 +196,49 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
     for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
     if (live && (cq % lpg) == 0) sx[g * a.Tp + t] = ps;
   }
+
+  // Low-rank partials of this workgroup's 128-channel slice(s) and 32
+  // tokens (Z = X A^T, summed over the slices by k_lowrank_zsum): per 16
+  // tokens x 16 rank columns, one v_mfma_f32_16x16x32_bf16 from zero for
+  // each 32-channel quarter of the slice (zero-filled past d, T and the
+  // rank), added in quarter order.  A token's partials depend only on its
+  // row of X and on A.
+  if (a.zpart) {
+    constexpr int NSL = BC / 128;
+    const int l = tid & 63, tr = l & 15, kq = l >> 4;
+    const int ntr = a.zrp / 16;
+    const int64_t M = (int64_t)gridDim.z * a.T;
+    const int jobs = 2 * ntr * NSL;
+    for (int j = wv; j < jobs; j += NWV) {
+      const int tt = j & 1, rt = (j >> 1) % ntr, sl = (j >> 1) / ntr;
+      const int64_t t0 = (int64_t)blockIdx.y * 32 + tt * 16;
+      const int64_t zs = (int64_t)blockIdx.x * NSL + sl;
+      if (t0 >= a.T || zs * 128 >= a.d) continue;  // uniform per wave
+      const int64_t tk = t0 + tr;
+      const int rrow = rt * 16 + tr;
+      const bool tok = tk < a.T, rok = rrow < a.zrank;
+      f32x4 q[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int64_t c = zs * 128 + 32 * qq + 8 * kq;
+        const bool cin = c < a.d;
+        const u32x4 xf = (cin && tok) ? *(const u32x4*)(X + tk * a.d + c)
+                                      : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 af = (cin && rok) ? *(const u32x4*)(a.zA + (int64_t)rrow * a.d + c)
+                                      : u32x4{0u, 0u, 0u, 0u};
+        q[qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, xf), __builtin_bit_cast(bf16x8, af),
+            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 4 * (l >> 4) + i;
+        if (t < a.T)
+          a.zpart[(zs * M + (int64_t)r * a.T + t) * a.zrp + rt * 16 + (l & 15)] =
+              ((q[0][i] + q[1][i]) + q[2][i]) + q[3][i];
+      }
+    }
+  }
 }
 
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R, const Launch& L) {

@@ -153,6 +153,19 @@ void fused_shape(Plan& P, int64_t R, int group) {
     P.frb = 2;
 }
 
+// The small-T statistics kernel writes the low-rank partials itself (its
+// workgroups own 128-channel blocks) when 128-channel slices are not capped
+// by the partials' size; otherwise the small-M kernel writes 256-channel ones.
+bool z_parts_in_stats(int64_t rp, int64_t M, int64_t d) {
+  return rp > 0 && M > 0 && lowrank_z_splits(M, d, (int)rp, 128) == (d + 127) / 128;
+}
+
+size_t z_small_bytes(int64_t rp, int64_t M, int64_t d) {
+  const size_t b = lowrank_z_part_bytes(M, d, (int)rp, 256);
+  const size_t f = z_parts_in_stats(rp, M, d) ? lowrank_z_part_bytes(M, d, (int)rp, 128) : 0;
+  return b > f ? b : f;
+}
+
 Plan make_plan(const ttq_params* prm, int64_t R) {
   Plan P;
   const int64_t d = prm->d, dout = prm->d_out, T = prm->T;
@@ -175,7 +188,7 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
   P.off_dhi = take(sizeof(float) * R * d);
   if (P.rp > 0) P.off_z = take(sizeof(uint16_t) * R * T * P.rp);
   if (P.rp > 0 && T > 0 && (P.path == 2 || fused))
-    P.off_zsmall = take(lowrank_z_part_bytes(R * T, d, (int)P.rp));
+    P.off_zsmall = take(z_small_bytes(P.rp, R * T, d));
 
   if (P.path == 2) {
     P.rowblocks = (dout + 15) / 16;
@@ -304,12 +317,16 @@ int enqueue_z_gemm(const Plan& P, char* ws, const bf16_t* Xb,
 // slices on the matrix cores, then their ordered sum.
 int enqueue_z_small(const Plan& P, char* ws, const bf16_t* Xb,
                     const bf16_t* Ab, int64_t M, int64_t d, int64_t rank,
-                    bf16_t* Zb, hipStream_t s) {
+                    bf16_t* Zb, hipStream_t s, bool parts_written = false) {
   LowRankZArgs za{Xb, Ab, M, d, (int)rank, (int)P.rp, Zb,
                   reinterpret_cast<float*>(ws + P.off_zsmall)};
-  int st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
-  if (st != TTQ_OK) return st;
-  return run(K_LOWRANK_ZSUM, s, [&](const Launch& L) { return launch_lowrank_z_sum(za, L); });
+  if (!parts_written) {
+    const int st = run(K_LOWRANK_Z, s, [&](const Launch& L) { return launch_lowrank_z_small(za, L); });
+    if (st != TTQ_OK) return st;
+  }
+  const int ns = parts_written ? (int)((d + 127) / 128)
+                               : lowrank_z_splits(M, d, (int)P.rp, 256);
+  return run(K_LOWRANK_ZSUM, s, [&](const Launch& L) { return launch_lowrank_z_sum(za, ns, L); });
 }
 
 // Statistics of a large-T call (and Z = X A^T when the plan fuses it): the
@@ -412,11 +429,16 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     sa.group = prm->group;
     sa.planes = P.planes;
     sa.Tp = 16 * P.ntb;
+    const bool zin = need_quant && z_parts_in_stats(P.rp, R * T, d);
+    if (zin) {
+      sa.zA = Ab; sa.zrank = (int)rank; sa.zrp = (int)P.rp;
+      sa.zpart = reinterpret_cast<float*>(ws + P.off_zsmall);
+    }
     st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, (int)R, L); });
     if (st != TTQ_OK) return st;
     if (!need_quant) return TTQ_OK;
     if (P.rp > 0 && T > 0) {
-      st = enqueue_z_small(P, ws, Xb, Ab, R * T, d, rank, Zb, s);
+      st = enqueue_z_small(P, ws, Xb, Ab, R * T, d, rank, Zb, s, zin);
       if (st != TTQ_OK) return st;
     }
     FusedArgs fa{};
@@ -574,7 +596,7 @@ Plan make_qmatmul_plan(const ttq_params& q, int cb) {
   // more tokens: the GEMM expands the codes itself (no W_hat in HBM)
   if (P.path == 1 && !forced && gemm_q_supported(d, q.group, cb)) P.path = 3;
   if (P.rp > 0 && T > 0 && (P.path == 0 || P.path == 2))
-    P.off_zsmall = take(lowrank_z_part_bytes(T, d, (int)P.rp));
+    P.off_zsmall = take(z_small_bytes(P.rp, T, d));
   if (P.path == 0 && T > 0 && q.d_out > 0) {
     P.ntb = 1;
     while (P.ntb * 16 < T) P.ntb *= 2;
@@ -694,10 +716,15 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     sa.group = q.group;
     sa.planes = P.planes;
     sa.Tp = 16 * P.ntb;
+    const bool zin = z_parts_in_stats(P.rp, T, d);
+    if (zin) {
+      sa.zA = Ab; sa.zrank = (int)rank; sa.zrp = (int)P.rp;
+      sa.zpart = reinterpret_cast<float*>(ws + P.off_zsmall);
+    }
     st = run(K_STATS_SMALL, s, [&](const Launch& L) { return launch_stats_small(sa, 1, L); });
     if (st != TTQ_OK) return st;
     if (P.rp > 0) {
-      st = enqueue_z_small(P, ws, Xb, Ab, T, d, rank, Zb, s);
+      st = enqueue_z_small(P, ws, Xb, Ab, T, d, rank, Zb, s, zin);
       if (st != TTQ_OK) return st;
     }
     QFusedArgs fa{};

@@ -292,6 +292,12 @@ struct StatsSmallArgs {
   // optional [R][d] stored D^{-1/2}: no statistics are taken, x' and the
   // group sums are formed with these values (dh, dhi are not written)
   const float* dhi_in;
+  // optional (with xs): the float32 partials of Z = X A^T over each
+  // 128-channel slice, [ceil(d / 128)][R * T][zrp], in the layout of the
+  // small-M low-rank kernel's partials (its sum kernel finishes Z)
+  const bf16_t* zA;     // [zrank][d]
+  int zrank, zrp;
+  float* zpart;
 };
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
                               const Launch& L);
@@ -624,13 +630,14 @@ struct LowRankZArgs {
   float* part;          // [nsplit][M][rp] fp32 partial sums (workspace)
 };
 // Z = X A^T for small M: channel slices on the matrix cores (partials), then
-// their sum in slice order.  Two launches; lowrank_z_parts gives the slice
-// count and the bytes of `part`.
+// their sum in slice order.  Two launches; lowrank_z_splits gives the slice
+// count and lowrank_z_part_bytes the bytes of `part` (256-channel slices;
+// 128 where the small-T statistics kernel writes the partials).
 hipError_t launch_lowrank_z_small(const LowRankZArgs& a, const Launch& L);
-hipError_t launch_lowrank_z_sum(const LowRankZArgs& a, const Launch& L);
-int lowrank_z_splits(int64_t M, int64_t d, int rp);
-inline size_t lowrank_z_part_bytes(int64_t M, int64_t d, int rp) {
-  return (size_t)lowrank_z_splits(M, d, rp) * M * rp * sizeof(float);
+hipError_t launch_lowrank_z_sum(const LowRankZArgs& a, int nsplit, const Launch& L);
+int lowrank_z_splits(int64_t M, int64_t d, int rp, int slice);
+inline size_t lowrank_z_part_bytes(int64_t M, int64_t d, int rp, int slice) {
+  return (size_t)lowrank_z_splits(M, d, rp, slice) * M * rp * sizeof(float);
 }
 
 }  // namespace ttq

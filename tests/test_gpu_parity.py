@@ -84,6 +84,15 @@ CASES = [
                          seed=32)),
     ("T1_alpha1_p1", dict(d=384, d_out=50, T=1, bits=2, group=128, p=1.0,
                           alpha=1.0, lam=0.0, seed=33)),
+    # the small-token low-rank product Z = X A^T: several 32-column rank jobs
+    # per 16-token tile (rank 200, padded to 224), a ragged last token tile,
+    # channel runs of the 8 waves that end mid-run (d = 800); in the
+    # statistics launch (T = 100) and in its own launch (T = 1)
+    ("z_r200_T100", dict(d=800, d_out=130, T=100, R=3, bits=4, group=32,
+                         rank=200, x_kind="logu10_100", n_outliers=8,
+                         seed=34)),
+    ("z_r200_T1", dict(d=800, d_out=130, T=1, R=5, bits=4, group=32,
+                       rank=200, x_kind="logu10_100", n_outliers=8, seed=35)),
 ]
 
 
