@@ -496,21 +496,41 @@ hipError_t launch_stats_z(const StatsZArgs& a, int R, const Launch& L) {
 // One thread per channel; the block partials are read 8 at a time (independent
 // loads in flight) and added in block order.
 __global__ __launch_bounds__(64) void k_stats_final(StatsFinalArgs a) {
+  if ((int)blockIdx.y >= a.R) {
+    // the low-rank partial sum's workgroups (the split-K reduction of the
+    // statistics pass's Z ranges): 4 consecutive elements per thread
+    const int64_t i =
+        (((int64_t)(blockIdx.y - a.R) * gridDim.x + blockIdx.x) * 64 + threadIdx.x) * 4;
+    if (i >= a.zn) return;
+    f32x4 acc = *(const f32x4*)(a.zpart + i);
+    for (int z = 1; z < a.zsplit; ++z) {
+      const f32x4 v = *(const f32x4*)(a.zpart + (int64_t)z * a.zn + i);
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    u32x2 o;
+    o.x = pack_bf16(acc[0], acc[1]);
+    o.y = pack_bf16(acc[2], acc[3]);
+    *(u32x2*)(a.Z + i) = o;
+    return;
+  }
   const int r = blockIdx.y;
   const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (c >= a.d) return;
   const int nb = a.nb;
   const double* P = a.partial + (int64_t)r * nb * a.d + c;
+  // block order; the loads of 8 blocks are in flight together
   double S = 0.0;
-  int k = 0;
-  for (; k + 8 <= nb; k += 8) {
+  for (int k0 = 0; k0 < nb; k0 += 8) {
     double v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = P[(int64_t)(k + j) * a.d];
+    for (int j = 0; j < 8; ++j) v[j] = k0 + j < nb ? P[(int64_t)(k0 + j) * a.d] : 0.0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) S += v[j];
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < nb) S += v[j];
   }
-  for (; k < nb; ++k) S += P[(int64_t)k * a.d];
   float dh, dhi;
   diag_half(finish_norm(S, a.pmode, a.p), a.lam, a.alpha, dh, dhi);
   a.dh[(int64_t)r * a.d + c] = dh;
@@ -518,9 +538,18 @@ __global__ __launch_bounds__(64) void k_stats_final(StatsFinalArgs a) {
   if (a.dh_export) a.dh_export[(int64_t)r * a.d + c] = dh;
 }
 
-hipError_t launch_stats_final(const StatsFinalArgs& a, int R, const Launch& L) {
-  if (R == 0 || a.d == 0) return hipSuccess;
-  dim3 grid((unsigned)((a.d + 63) / 64), (unsigned)R);
+hipError_t launch_stats_final(const StatsFinalArgs& a0, int R, const Launch& L) {
+  StatsFinalArgs a = a0;
+  a.R = R;
+  const unsigned gx = (unsigned)((a.d + 63) / 64);
+  unsigned zrows = 0;
+  if (a.zpart && a.zn > 0) {
+    if (a.zn % 4 != 0 || a.zsplit < 1 || !a.Z) return hipErrorInvalidValue;
+    const int64_t wgs = (a.zn / 4 + 63) / 64;
+    zrows = (unsigned)((wgs + gx - 1) / gx);
+  }
+  if ((R == 0 || a.d == 0) && zrows == 0) return hipSuccess;
+  dim3 grid(gx > 0 ? gx : 1u, (unsigned)R + zrows);
   return ext_launch(k_stats_final, grid, dim3(64), 0, L, a);
 }
 

@@ -333,6 +333,13 @@ struct StatsFinalArgs {
   float* dh;
   float* dhi;
   float* dh_export;
+  // optional (zpart non-null): Z[i] = bf16(sum_{k<zsplit} zpart[k*zn + i])
+  // in range order, i < zn (zn % 4 == 0), by extra workgroups of the launch
+  const float* zpart;
+  int zsplit;
+  int64_t zn;
+  bf16_t* Z;
+  int R;                  // requests (set by the launcher)
 };
 hipError_t launch_stats_final(const StatsFinalArgs& a, int R, const Launch& L);
 
