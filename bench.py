@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -236,15 +237,23 @@ def roofline(kind: str, ms_per_launch: float, bytes_per_launch: float,
     return r
 
 
+def _code_only(path: str) -> bytes:
+    """Source text without comments and blank space (a comment edit does not
+    change what the counters measured)."""
+    txt = open(path, encoding="utf-8").read()
+    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+    txt = re.sub(r"//[^\n]*", " ", txt)
+    return " ".join(txt.split()).encode()
+
+
 def kernel_src_sha(kind: str) -> str:
-    p = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc",
-                     KERNEL_SOURCES.get(kind, "k_fused.hip"))
-    h = hashlib.sha256(open(p, "rb").read())
-    # the shared headers change every kernel
     cdir = os.path.join(ROOT, "online_activation_aware_ttq_amd", "csrc")
+    h = hashlib.sha256(_code_only(os.path.join(
+        cdir, KERNEL_SOURCES.get(kind, "k_fused.hip"))))
+    # the shared headers change every kernel
     for name in sorted(os.listdir(cdir)):
         if name.endswith(".h"):
-            h.update(open(os.path.join(cdir, name), "rb").read())
+            h.update(_code_only(os.path.join(cdir, name)))
     return h.hexdigest()[:16]
 
 

@@ -33,12 +33,14 @@
 // {l, l^16, l^32, l^48}, and the accumulators of row l & 15 land in the same
 // lane that owns its scale and minimum.
 //
-// Work split: a workgroup of 8 waves owns 16 weight rows and all of K; waves
-// stride over the groups and meet once in LDS at the end (fixed order, no
-// inter-workgroup traffic, deterministic).  D^{1/2} of the request is staged
-// in LDS once per workgroup (when it fits).  Workgroup indices are laid out so
-// that the R requests of one weight tile run back to back on the same XCD and
-// share the tile through its L2.
+// Work split: a workgroup of 8 waves owns 16 weight rows (or two blocks of
+// 16 that share every activation load, for T > 16 when that still leaves a
+// workgroup per CU) and all of K; waves stride over the groups and meet once
+// in LDS at the end (fixed order, no inter-workgroup traffic,
+// deterministic).  D^{1/2} of the request is staged in LDS once per
+// workgroup (when it fits).  Workgroup indices are laid out so that the R
+// requests of one weight tile run back to back on the same XCD and share the
+// tile through its L2.
 #include "ttq_internal.h"
 
 namespace ttq {
