@@ -752,6 +752,16 @@ def summarize(a):
         return [float(r["Counter_Value"]) for r in rows
                 if r["Counter_Name"] == counter and key in r["Kernel_Name"]]
 
+    def calls(rows, counter):
+        # one timed launch of a kind can be two dispatches (a GEMM's whole
+        # rounds of big tiles and its narrow tail): the launches are the
+        # dispatches of the most frequent matching kernel
+        n = {}
+        for r in rows:
+            if r["Counter_Name"] == counter and key in r["Kernel_Name"]:
+                n[r["Kernel_Name"]] = n.get(r["Kernel_Name"], 0) + 1
+        return max(n.values()) if n else 0
+
     def calib(rows, counter):
         cp = [r for r in rows if r["Counter_Name"] == counter
               and "copyBuffer" in r["Kernel_Name"]]
@@ -763,14 +773,16 @@ def summarize(a):
     c_f, c_w = calib(fr, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
     sf = calib_bytes / (c_f * 1024) if c_f == c_f and c_f > 0 else float("nan")
     sw = calib_bytes / (c_w * 1024) if c_w == c_w and c_w > 0 else float("nan")
-    f_kib = sum(k_f) / max(1, len(k_f))
-    w_kib = sum(k_w) / max(1, len(k_w))
+    n_f, n_w = calls(fr, "FETCH_SIZE"), calls(wr, "WRITE_SIZE")
+    f_kib = sum(k_f) / max(1, n_f)
+    w_kib = sum(k_w) / max(1, n_w)
     traffic = f_kib * 1024 * sf + w_kib * 1024 * sw
     rec = {"kernel": kind, "workload": leg, "kernel_src_sha": kernel_src_sha(kind),
            "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
            "copy_calib_bytes": calib_bytes, "copy_fetch_kib": c_f,
            "copy_write_kib": c_w, "fetch_scale": sf, "write_scale": sw,
-           "bytes_per_launch": traffic, "launches_counted": [len(k_f), len(k_w)]}
+           "bytes_per_launch": traffic, "launches_counted": [n_f, n_w],
+           "dispatches_counted": [len(k_f), len(k_w)]}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     json.dump(rec, open(traffic_file(kind, leg), "w"), indent=1)
     lines = [f"# {kind} on {leg}", "", "Commands (from the repository root):",
@@ -779,8 +791,8 @@ def summarize(a):
     lines += _stats_table(stats)
     lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
               f"- {kind}: FETCH_SIZE {f_kib:.0f} KiB/launch, WRITE_SIZE "
-              f"{w_kib:.1f} KiB/launch (averaged over {len(k_f)} / {len(k_w)} "
-              "launches)",
+              f"{w_kib:.1f} KiB/launch (summed over {len(k_f)} / {len(k_w)} "
+              f"dispatches, {n_f} / {n_w} launches)",
               f"- calibration: device-to-device copy of {calib_bytes} bytes reads "
               f"FETCH_SIZE {c_f:.0f} KiB and WRITE_SIZE {c_w:.0f} KiB; scale "
               f"factors {sf:.4f} (fetch) and {sw:.4f} (write)",

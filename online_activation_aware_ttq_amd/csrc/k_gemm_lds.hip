@@ -35,6 +35,7 @@
 #include "ttq_internal.h"
 
 #include <algorithm>
+#include <numeric>
 
 namespace ttq {
 
@@ -638,12 +639,54 @@ int gemm_lds_config(int64_t M, int64_t N, int64_t batch) {
   return r256 >= 4 ? 0 : 2;
 }
 
+// Columns [0, nm) as whole rounds of 256 x 256 tiles and the rest as 256 x
+// 128 tiles in a second launch, when that costs fewer rounds than either
+// tile size alone (a last round of big tiles that would run partly empty):
+// returns nm, or 0 for one launch.  Costs as in gemm_lds_config.  Not from
+// four rounds on, where the persistent kernel spreads a partial last round
+// over its workgroups (7B-class gate projection, 21.5 rounds: the split was
+// 0.6 % slower; 11008 x 4096 at T = 2048, 1.34 rounds: 238 -> 215 us).
+int64_t gemm_lds_split(int64_t M, int64_t N, int64_t batch) {
+  const int64_t per = ((M + 255) / 256) * batch;  // 256 x 256 tiles per column
+  const int64_t nt = (N + 255) / 256;
+  if ((per * nt + 255) / 256 >= 4) return 0;
+  const int64_t step = 256 / std::gcd(per, (int64_t)256);
+  const int64_t ntm = nt / step * step;
+  if (ntm == 0 || ntm == nt) return 0;
+  const int64_t r_main = per * ntm / 256;
+  const int64_t n_tail = N - ntm * 256;
+  const int64_t r_tail = (((M + 255) / 256) * ((n_tail + 127) / 128) * batch + 255) / 256;
+  const int64_t r256 = (per * nt + 255) / 256;
+  const int64_t r128 = (((M + 255) / 256) * ((N + 127) / 128) * batch + 255) / 256;
+  const int64_t best = std::min(r256 * 100, r128 * 57);
+  return r_main * 100 + r_tail * 57 < best ? ntm * 256 : 0;
+}
+
 hipError_t launch_gemm_lds(const GemmArgs& a, const Launch& L) {
   if (a.M <= 0 || a.N_store <= 0) return hipSuccess;
   if (a.K1 <= 0 || !a.C || a.nsplit > 1) return hipErrorInvalidValue;
   // tiled B: 32-bit offsets inside one 256-row block of k-tiles
   if (a.b1_tiled && (a.K1 + 63) / 64 * kWtRows * kWtCols * 2 >= (int64_t)kOutOfRange)
     return hipErrorInvalidValue;
+  const int64_t nm = gemm_lds_split(a.M, a.N_store, a.batch > 1 ? a.batch : 1);
+  if (nm > 0) {
+    // the same MFMAs in the same order per output with either tile size:
+    // the result does not depend on the split
+    GemmArgs m = a, t = a;
+    m.N_store = nm;
+    m.N = std::min(a.N, nm);
+    t.N_store = a.N_store - nm;
+    t.N = std::max((int64_t)0, a.N - nm);
+    t.C = a.C + nm;
+    t.B1 = a.b1_tiled ? a.B1 + (nm / kWtRows) * ((a.K1 + 63) / 64) * (kWtRows * kWtCols)
+                      : a.B1 + nm * a.ldb1;
+    if (a.B2) t.B2 = a.B2 + nm * a.ldb2;
+    // (timing events: the first launch's start, the second's end)
+    const Launch Lm{L.s, L.e0, nullptr}, Lt{L.s, nullptr, L.e1};
+    const hipError_t e = launch_gemm_lds(m, Lm);
+    if (e != hipSuccess) return e;
+    return launch_t<2, 2, 4, 2, 3, kDoubleBuf>(t, Lt);
+  }
   switch (gemm_lds_config(a.M, a.N_store, a.batch > 1 ? a.batch : 1)) {
     case 0:  // 256 x 256, 8 waves, 2 stages, persistent
       return launch_tp<4, 2, 2, 4, 2, kSingleBufSplit>(a, L);

@@ -170,6 +170,25 @@ def test_split_schedule_gemm_ragged_tiles():
     _say("split1", rep)
 
 
+def test_gemm_whole_rounds_and_narrow_tail():
+    """A column count whose last round of 256 x 256 tiles would run partly
+    empty: the first 8192 columns as whole rounds of 256 x 256 tiles, the
+    ragged rest (356 columns, three 128-wide tiles) in a second launch of
+    256 x 128 tiles, both with the ragged low-rank segment (r = 40) and
+    the tiled W_hat offset past the split."""
+    prob = make_problem("tail_split", d=256, d_out=8548, T=2048, bits=4,
+                        group=32, rank=40, x_kind="logu10_100", n_outliers=4,
+                        seed=73)
+    rows = np.unique(np.concatenate([
+        np.arange(8), np.arange(8184, 8200), np.arange(8548 - 12, 8548),
+        np.random.default_rng(9).choice(8548, 24, replace=False)]))
+    print(f"[case] whole rounds + tail T=2048 d=256 d_out=8548 rows={len(rows)}",
+          flush=True)
+    gpu = run_gpu(prob, rows=rows, exports=False)
+    rep = check_problem(prob, gpu, rows=rows, check_codes=False)
+    _say("tail_split", rep)
+
+
 ROW_PAIR_CASES = [
     # fused path with two 16-row blocks per workgroup (taken for T > 16 when
     # that still leaves at least 256 workgroups): a ragged last pair (odd
