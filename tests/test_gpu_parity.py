@@ -218,6 +218,21 @@ ROW_PAIR_CASES = [
 ]
 
 
+def test_fused_row_pairs_wide_d_without_lds_scales():
+    """Two row blocks per workgroup with D^{1/2} read from memory instead of
+    LDS (d = 16896 channels: 66 KiB of scales) and exports; sampled rows."""
+    prob = make_problem("rp_wide", d=16896, d_out=1040, T=64, R=8, bits=4,
+                        group=128, rank=16, x_kind="logu10_100",
+                        n_outliers=20, seed=89)
+    rows = np.unique(np.concatenate([
+        np.arange(8), np.arange(1024, 1040),
+        np.random.default_rng(10).choice(1040, 16, replace=False)]))
+    print(f"[case] row pairs, d=16896 T=64 R=8 rows={len(rows)}", flush=True)
+    gpu = run_gpu(prob, rows=rows)
+    rep = check_problem(prob, gpu, rows=rows)
+    _say("rp_wide", rep)
+
+
 @pytest.mark.parametrize("name,kw", ROW_PAIR_CASES,
                          ids=[c[0] for c in ROW_PAIR_CASES])
 def test_fused_row_pairs(name, kw):
