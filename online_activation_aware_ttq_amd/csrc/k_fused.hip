@@ -253,16 +253,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   // does not wait for the former, and no register copies are needed
   // (a prefetch past the last group is out of range: zeros, no traffic)
   u32x4 wa[RB][NKS], wb[RB][NKS];
-  // wave w takes groups w, w + FW, ...; with FusedArgs::rotate each
-  // workgroup starts that list at its own rotation, so that the CUs of an
-  // XCD do not all read the same x' slice from L2 at the same time (the
-  // workgroups of one XCD have consecutive row-block-group indices >> 3; the
-  // order of the group sums per output is fixed by the row block alone)
-  const int nw = w < G ? (G - w + FW - 1) / FW : 0;
-  const int rot = (a.rotate && nw > 0) ? (int)(((rb0 / RB) >> 3) % nw) : 0;
-  auto gof = [&](int j) { return j < nw ? w + FW * ((j + rot) % nw) : G; };
-  int gi = 0;
-  int g = gof(0);
+  int g = w;
   if (DH_LDS) {
     // D^{1/2} of this request into LDS before the first weight loads: once
     // every CU's weight requests are queued, these small reads would sit
@@ -279,21 +270,20 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   }
   // (scheduling barriers keep that issue order: the compiler would otherwise
   // hoist loads across the prefetch)
-  while (gi < nw) {
+  while (g < G) {
     load_x(g);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(wb, gof(gi + 1));
+    load_w(wb, g + FW);
     __builtin_amdgcn_sched_barrier(0);
     process(wa, g);
-    if (++gi >= nw) break;
-    g = gof(gi);
+    g += FW;
+    if (g >= G) break;
     load_x(g);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(wa, gof(gi + 1));
+    load_w(wa, g + FW);
     __builtin_amdgcn_sched_barrier(0);
     process(wb, g);
-    ++gi;
-    g = gof(gi);
+    g += FW;
   }
 
   // static low-rank term B (A X): one more MFMA chain on Z = A X

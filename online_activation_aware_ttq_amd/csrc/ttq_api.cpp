@@ -34,10 +34,6 @@ constexpr int64_t kGemmQMaxT = 256;
 
 constexpr size_t kGemvLdsMax = 128 * 1024;
 
-// the fused kernel's workgroups rotate their order of the groups when all
-// requests' x' together take at most this many bytes (half an XCD's L2)
-constexpr int64_t kFusedRotateBytes = int64_t(2) << 20;
-
 // the fused kernel takes two row blocks per workgroup from this many
 // workgroups on (the chip's compute units)
 constexpr int64_t kFusedPairWgs = 256;
@@ -457,11 +453,6 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     fa.R = (int)R;
     fa.codes_out = codes_out; fa.s_out = scales_out; fa.m_out = mins_out;
     fa.qf = (int)prm->qformat;
-    // the workgroups of an XCD read x' in different orders when every
-    // request's x' fits in half an XCD's L2 together; with more, the same
-    // order keeps one moving window of it in L2 (8 requests x 128 tokens
-    // x 4096 channels: 186 -> 273 us with rotated orders; 1-2 MiB: -2 to -3 %)
-    fa.rotate = (int64_t)P.planes * R * 16 * P.ntb * d * 2 <= kFusedRotateBytes;
     return run(K_FUSED, s, [&](const Launch& L) { return launch_fused(fa, P.ntb, prm->group, P.frb, L); });
   }
 

@@ -362,7 +362,6 @@ struct FusedArgs {
   float* s_out;         // [R][d_out][G]
   float* m_out;         // [R][d_out][G]
   int qf;               // quantizer format (QFmt)
-  int rotate;           // 1: each workgroup rotates its order of the groups
 };
 // D^{1/2} is staged in LDS when it fits in this many bytes.
 constexpr size_t kFusedDhLdsMax = 64 * 1024;
