@@ -299,6 +299,22 @@ def test_batched_matches_single_calls():
         np.testing.assert_array_equal(gs["Y"][0], gb["Y"][r])
 
 
+def test_row_pairs_match_single_calls_bit_for_bit():
+    """Eight requests take two row blocks per workgroup (8 x 33 pairs >= 256
+    workgroups), one request alone takes one: the same codes and the same Y
+    bits (each output's arithmetic does not depend on the row pairing)."""
+    kw = dict(d=512, d_out=1040, T=40, bits=4, group=128, rank=32,
+              x_kind="logu10_100", n_outliers=5, seed=36)
+    prob = make_problem("rpb", R=8, **kw)
+    gb = run_gpu(prob)
+    for r in (0, 5):
+        single = make_problem("rpb", R=1, **kw)
+        single.X = prob.X[r:r + 1]
+        gs = run_gpu(single)
+        np.testing.assert_array_equal(gs["q"][0], gb["q"][r])
+        np.testing.assert_array_equal(gs["Y"][0], gb["Y"][r])
+
+
 def test_degenerate_groups_and_zero_channels():
     # constant weight rows (max == min) and all-zero activation channels with
     # lambda = 0 (n + lambda = 0 -> neutral scale 1)
