@@ -350,7 +350,7 @@ int enqueue_stats_z(const Plan& P, char* ws, const bf16_t* Xb,
     za.Zpart = P.sz_csplit > 1 ? reinterpret_cast<float*>(ws + P.off_zpart) : nullptr;
     za.zslice = R * T * P.rp;
   }
-  int st = run(K_STATS_PARTIAL, s, [&](const Launch& L) { return launch_stats_z(za, (int)R, L); });
+  int st = run(K_STATS_Z, s, [&](const Launch& L) { return launch_stats_z(za, (int)R, L); });
   if (st != TTQ_OK) return st;
   StatsFinalArgs fa{};
   fa.partial = za.partial; fa.d = d; fa.nb = P.sz_ntb; fa.pmode = pmode;

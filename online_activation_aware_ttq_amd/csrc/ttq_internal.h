@@ -18,7 +18,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 // Kernel kinds, for the optional event timing.
 enum KernelKind {
   K_STATS_SMALL = 0,   // norms + diag + scaled activations (T <= 128)
-  K_STATS_PARTIAL,     // norms, partial sums per 64-token block (+ Z = X A^T)
+  K_STATS_Z,           // norms, partial sums per 64-token block (+ Z = X A^T)
   K_STATS_FINAL,       // norms finalize + diag
   K_FUSED,             // fused quantize + MFMA contraction (single W pass)
   K_QUANT,             // quantize pass writing W_hat (two-phase path)
