@@ -70,10 +70,12 @@ def test_c4_up_proj(p):
     _check(wc.make_c4(p))
 
 
-# every projection shape at every token count of the layer at least once,
-# the three shapes of the headline token count (4096) all at full size
-@pytest.mark.parametrize("T,proj", [(1, "q_proj"), (1, "down_proj"),
+# all three projection shapes (square, 4096 -> 11008, 11008 -> 4096) at
+# every token count of the layer
+@pytest.mark.parametrize("T,proj", [(1, "q_proj"), (1, "gate_proj"),
+                                    (1, "down_proj"),
                                     (16, "gate_proj"), (16, "k_proj"),
+                                    (16, "down_proj"),
                                     (256, "down_proj"), (256, "up_proj"),
                                     (256, "v_proj"), (4096, "o_proj"),
                                     (4096, "gate_proj"), (4096, "down_proj")])
