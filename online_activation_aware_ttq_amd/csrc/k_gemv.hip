@@ -42,11 +42,11 @@ namespace ttq {
 // pow: correctly rounded ones for alpha = 1 and, outside [1e-30, 1e30], for
 // alpha = 1/2; inside that range base^(1/4) is a float32 seed (two square
 // roots) refined by one Newton step in float64, z + z e / 4 with
-// e = (base - z^4) / z^4 (e below 2^-20, so the neglected terms are below
-// 2^-43 relative).  Every value is far closer to the exact one than the
-// single rounding to float32 can resolve except within ~2^-43 of a rounding
-// midpoint; the rounded float32 equals that of the float64 route for every
-// bf16 input at the lambdas checked.  The kernel's workgroups each derive
+// e = (base - z^4) / z^4 (e of order 2^-21; the neglected terms, about
+// 3 e^2 / 32, stay below 2^-40 relative even with a seed a few ulps off).
+// Such a value rounds to the same float32 as the float64 route unless it
+// lies within that distance of a rounding midpoint; for every bf16 input
+// at the lambdas checked the results are equal.  The kernel's workgroups each derive
 // the statistics of their token, so this is their prologue's main cost.
 template <bool FAST>
 __device__ __forceinline__ double gemv_diag(double ax, int pmode, double p,
