@@ -12,7 +12,9 @@
 // load per lane; B operand: 32 channels x 16 rank rows of A, likewise), the
 // waves are added in LDS in a fixed order and the slice's fp32 partial tile
 // is stored.  A second kernel adds the slices in slice order and rounds once
-// to bf16, so the result does not depend on scheduling.
+// to bf16, so the result does not depend on scheduling.  On the fused route
+// (2 to 128 tokens) the small-T statistics kernel writes such partials
+// itself, over 128-channel slices, and only the sum kernel runs.
 #include "ttq_internal.h"
 
 namespace ttq {
