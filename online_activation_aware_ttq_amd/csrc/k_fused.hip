@@ -23,8 +23,9 @@
 // bits) and both halves are contracted.  For T > 16 x' is rounded once to
 // bf16 and the rounding errors average over the tokens.  It is stored in MFMA
 // fragment order so that every activation load is a contiguous 1 KiB per
-// wave; for T > 16 the weights are streamed with non-temporal loads so that
-// they do not evict x' (re-read by every workgroup) from L2.
+// wave.  The weights are read with the default cache policy: non-temporal
+// loads (meant to keep x', re-read by every workgroup, in L2) made the
+// 8-request 7B-class layer 5-8 % slower at 32 and 128 tokens.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 with A = x' (16 tokens x 32 channels) and
 // B = codes (32 channels x 16 weight rows).  Lane l holds weight row l & 15
@@ -103,8 +104,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int k = 0; k < NKS; ++k)
-        wv[r][k] = HILO ? buf_load16(r ? wr1 : wr0, lane_off + k * 64, soff)
-                        : buf_load16_nt(r ? wr1 : wr0, lane_off + k * 64, soff);
+        wv[r][k] = buf_load16(r ? wr1 : wr0, lane_off + k * 64, soff);
   };
   // fragment-ordered x' (zero past T): each load is 1 KiB per wave
   auto load_x = [&](int g) {

@@ -37,23 +37,28 @@ __global__ __launch_bounds__(ZW * 64) void k_lowrank_zpart(LowRankZArgs a,
   const int64_t kend = min(a.d, kbeg + kslice);
   const int64_t wsl = kslice / ZW;
   const int64_t k0 = kbeg + w * wsl, k1 = min(kend, k0 + wsl);
-  const int64_t m = m0 + tr;
-  const bf16_t* xr = a.X + (m < a.M ? m : 0) * a.d;
 
   f32x4 acc[ZTILES];
 #pragma unroll
   for (int t = 0; t < ZTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // operands of one 32-channel step (zero past the slice, past M, past rank)
+  // operands of one 32-channel step (zero past the slice, past M, past
+  // rank), as bounded buffer loads with no branch, so that the compiler
+  // keeps both steps' loads in flight (guarded loads were waited for one by
+  // one)
+  constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(a.X + m0 * a.d, (uint32_t)(min((int64_t)16, a.M - m0) * a.d * 2));
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A, (uint32_t)((int64_t)a.rank * a.d * 2));
   auto load = [&](int64_t kc, u32x4& xf, u32x4 (&af)[ZTILES]) {
     const int64_t c = kc + 8 * kq;
     const bool cin = c < k1;
-    xf = (cin && m < a.M) ? *(const u32x4*)(xr + c) : u32x4{0u, 0u, 0u, 0u};
+    xf = buf_load16(xrs, cin ? (uint32_t)((tr * a.d + c) * 2) : kPastEnd, 0);
 #pragma unroll
     for (int t = 0; t < ZTILES; ++t) {
       const int r = n0 + 16 * t + tr;
-      af[t] = (t < nt && cin && r < a.rank) ? *(const u32x4*)(a.A + (int64_t)r * a.d + c)
-                                             : u32x4{0u, 0u, 0u, 0u};
+      af[t] = buf_load16(ars, (t < nt && cin && r < a.rank) ? (uint32_t)(((int64_t)r * a.d + c) * 2)
+                                                             : kPastEnd, 0);
     }
   };
   u32x4 xa, xb, aa[ZTILES], ab[ZTILES];

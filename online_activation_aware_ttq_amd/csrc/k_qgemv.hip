@@ -76,16 +76,17 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
   // as they return.
   constexpr int LPS = SUB / 4;                  // lanes per slice
   const int64_t nitem = dpad / 4;               // multiple of 256
+  // Bounded buffer loads: channels past d read zeros with no branch.  (A
+  // guarded load made the compiler wait for it before the code stream was
+  // requested, putting the two latencies in series.)
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)(d * 2));
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.dhi, (uint32_t)(d * 4));
   auto xload = [&](int64_t it, u32x2& xv, f32x4& h) {
     const int64_t q = it / LPS, i = (it % LPS) * 4;
     const int64_t ln = q & 63, ks = q >> 6;
     const int64_t c = (ks / NSB) * CPL + ln * VPL + (ks % NSB) * SUB + i;
-    xv = u32x2{0u, 0u};
-    h = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (c < d) {
-      xv = *(const u32x2*)(a.X + c);
-      h = *(const f32x4*)(a.dhi + c);
-    }
+    xv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xr, (uint32_t)(c * 2), 0, 0));
+    h = __builtin_bit_cast(f32x4, buf_load16(hr, (uint32_t)(c * 4), 0));
   };
   auto xstore = [&](int64_t it, const u32x2& xv, const f32x4& h) {
     const int64_t q = it / LPS, i = (it % LPS) * 4;
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
   u32x2 xv0, xv1;
   f32x4 h0, h1;
   const int64_t it0 = tid, it1 = tid + QW * 64;  // wave-uniform validity
-  if (it0 < nitem) xload(it0, xv0, h0);
-  if (it1 < nitem) xload(it1, xv1, h1);
+  xload(it0, xv0, h0);   // (items past the padded range read zeros)
+  xload(it1, xv1, h1);
   __builtin_amdgcn_sched_barrier(0);
 
   // A ring of QNB loads per row: load k of a row lives in slot k % QNB and
@@ -121,13 +122,17 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
                        rlive ? (uint32_t)a.row_bytes : 0u);
     srow[rr] = (rlive ? row : 0) * a.G;
   }
+  // Every fetch is issued, with no branch: a load past the row reads zeros
+  // and its scale index is clamped to a valid one.  With the loads in
+  // branches the compiler's wait counts at the joins became conservative
+  // (the x' prologue waited for the whole code stream).
   auto fetch = [&](int rr, int slot, int k) {
-    if (k >= nld) return;  // uniform
-    v[rr][slot] = buf_load16(cr[rr], (uint32_t)(l * 16), (uint32_t)k * 1024);
+    const bool live = k < nld;  // uniform
+    v[rr][slot] = buf_load16(cr[rr], (uint32_t)(l * 16), live ? (uint32_t)k * 1024 : kOutOfRange);
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       const int64_t cs = (int64_t)k * CPL + (int64_t)l * VPL + sb * SUB;
-      const int64_t gi = srow[rr] + (cs < d ? cs / GS : 0);
+      const int64_t gi = srow[rr] + (live && cs < d ? cs / GS : 0);
       sg[rr][slot][sb] = a.s[gi];
       mg[rr][slot][sb] = a.m[gi];
     }
@@ -160,8 +165,9 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
         if (k >= nld) break;  // uniform
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-          const int64_t cs = (int64_t)k * CPL + (int64_t)l * VPL + sb * SUB;
-          if (cs >= d) break;
+          // slices past d add nothing (a select, not a branch: padding
+          // bytes of a row need not hold finite codes)
+          const bool in_d = (int64_t)k * CPL + (int64_t)l * VPL + sb * SUB < d;
           float P0 = 0.f, P1 = 0.f, P2 = 0.f, P3 = 0.f;
 #pragma unroll
           for (int i = 0; i < SUB; i += 4) {
@@ -172,11 +178,11 @@ __global__ __launch_bounds__(QW * 64) void k_qgemv(QGemvArgs a) {
             P2 = fmaf(code_at<CB, F8>(v[rr][j], sb * SUB + i + 2), xq.z, P2);
             P3 = fmaf(code_at<CB, F8>(v[rr][j], sb * SUB + i + 3), xq.w, P3);
           }
-          const float P = (P0 + P1) + (P2 + P3);
+          const float P = in_d ? (P0 + P1) + (P2 + P3) : 0.f;
           acc = fmaf(sg[rr][j][sb], P,
                      fmaf(mg[rr][j][sb], sxs[(k * NSB + sb) * 64 + l], acc));
         }
-        if (k + QNB < nld) fetch(rr, j, k + QNB);
+        fetch(rr, j, k + QNB);
       }
     }
     // static low-rank term: + B[row, :] . z

@@ -100,12 +100,16 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
   const bool live = c0 < a.d;
   const bf16_t* X = a.X + (int64_t)r * a.T * a.d;
 
+  // Bounded buffer loads over the request's rows: tokens past T and chunks
+  // past d read zeros with no branch, so all NTK loads are in flight at
+  // once (guarded loads were waited for in pairs, one round trip each).
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(a.T * a.d * 2));
   u32x4 v[NTK];
 #pragma unroll
   for (int i = 0; i < NTK; ++i) {
     const int64_t t = tl + i * TLN;
-    v[i] = (live && t < a.T) ? *(const u32x4*)(X + t * a.d + c0)
-                             : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t off = live ? (uint32_t)((t * a.d + c0) * 2) : kOutOfRange;
+    v[i] = buf_load16(xr, off, 0);
   }
   if (a.dhi_in) {
     // stored D^{-1/2}: no statistics
@@ -205,6 +209,8 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
   // row of X and on A.
   if (a.zpart) {
     constexpr int NSL = BC / 128;
+    constexpr uint32_t kPastEnd = 0xFFFFFFF0u;   // past any row range below
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.zA, (uint32_t)((int64_t)a.zrank * a.d * 2));
     const int l = tid & 63, tr = l & 15, kq = l >> 4;
     const int ntr = a.zrp / 16;
     const int64_t M = (int64_t)gridDim.z * a.T;
@@ -217,19 +223,22 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
       const int64_t tk = t0 + tr;
       const int rrow = rt * 16 + tr;
       const bool tok = tk < a.T, rok = rrow < a.zrank;
-      f32x4 q[4];
+      // bounded loads (zeros past d, T and the rank, no branch: all eight
+      // in flight at once)
+      u32x4 xf[4], af[4];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int64_t c = zs * 128 + 32 * qq + 8 * kq;
         const bool cin = c < a.d;
-        const u32x4 xf = (cin && tok) ? *(const u32x4*)(X + tk * a.d + c)
-                                      : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 af = (cin && rok) ? *(const u32x4*)(a.zA + (int64_t)rrow * a.d + c)
-                                      : u32x4{0u, 0u, 0u, 0u};
-        q[qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, xf), __builtin_bit_cast(bf16x8, af),
-            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        xf[qq] = buf_load16(xr, cin && tok ? (uint32_t)((tk * a.d + c) * 2) : kPastEnd, 0);
+        af[qq] = buf_load16(ar, cin && rok ? (uint32_t)(((int64_t)rrow * a.d + c) * 2) : kPastEnd, 0);
       }
+      f32x4 q[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        q[qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, xf[qq]), __builtin_bit_cast(bf16x8, af[qq]),
+            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t t = t0 + 4 * (l >> 4) + i;
