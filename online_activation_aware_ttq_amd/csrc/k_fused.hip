@@ -252,6 +252,39 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   // issued after this group's activation loads, so waiting for the latter
   // does not wait for the former, and no register copies are needed
   // (a prefetch past the last group is out of range: zeros, no traffic)
+  // static low-rank term B (A X): one more MFMA chain on Z = A X, rank step
+  // kk (32 columns) per wave.  Bounded buffer loads: rows past d_out,
+  // columns past the rank and tokens past T read zeros with no branch.
+  constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+  const int nk = a.rank > 0 ? a.rp / 32 : 0;
+  const int64_t lr_rows = min((int64_t)16 * RB, a.d_out - rb0 * 16);
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(a.rank > 0 ? a.Blr + rb0 * 16 * a.rank : a.W,
+                a.rank > 0 ? (uint32_t)(lr_rows * a.rank * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t zrs =
+      make_rsrc(a.rank > 0 ? a.Z + (int64_t)req * T * a.rp : a.W,
+                a.rank > 0 ? (uint32_t)(T * a.rp * 2) : 0u);
+  auto lr_load = [&](int kk, u32x4 (&bv)[RB], u32x4 (&zv)[NTB]) {
+    const int c8 = kk * 32 + qd * 8;
+    const bool on = kk < nk && c8 < a.rank;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+      bv[r] = buf_load16(brs, on ? (uint32_t)(((r * 16 + lr) * a.rank + c8) * 2) : kPastEnd, 0);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+      zv[tb] = buf_load16(zrs, kk < nk ? (uint32_t)(((tb * 16 + lr) * a.rp + c8) * 2) : kPastEnd, 0);
+  };
+  auto lr_mfma = [&](const u32x4 (&bv)[RB], const u32x4 (&zv)[NTB]) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, zv[tb]), __builtin_bit_cast(bf16x8, bv[r]),
+            acc[r][tb], 0, 0, 0);
+  };
+  u32x4 lbv[RB], lzv[NTB];
+
   u32x4 wa[RB][NKS], wb[RB][NKS];
   int g = w;
   if (DH_LDS) {
@@ -286,32 +319,13 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
     g += FW;
   }
 
-  // static low-rank term B (A X): one more MFMA chain on Z = A X
-  if (a.rank > 0) {
-    const int nk = a.rp / 32;
-    for (int kk = w; kk < nk; kk += FW) {
-      const int c8 = kk * 32 + qd * 8;
-      u32x4 bv[RB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const int64_t row = (rb0 + r) * 16 + lr;
-        bv[r] = (row < a.d_out && c8 < a.rank)
-                    ? *(const u32x4*)(a.Blr + row * a.rank + c8)
-                    : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        const int64_t tok = tb * 16 + lr;
-        const u32x4 zv =
-            tok < T ? *(const u32x4*)(a.Z + ((int64_t)req * T + tok) * a.rp + c8)
-                    : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-          acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, bv[r]),
-              acc[r][tb], 0, 0, 0);
-      }
-    }
+  // the low-rank steps of this wave, in increasing kk (requesting the first
+  // step's operands with the first weights instead raised the register count
+  // at T <= 16 from 123 to 131 and cost a workgroup per CU: +29 % at 8 x 16
+  // tokens)
+  for (int kk = w; kk < nk; kk += FW) {
+    lr_load(kk, lbv, lzv);
+    lr_mfma(lbv, lzv);
   }
 
   // combine the 8 waves in a fixed order, one row block at a time (LDS reused

@@ -150,6 +150,34 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
   int g = g_begin;
   load_w(wv, g < g_end ? g : G);
   __builtin_amdgcn_sched_barrier(0);
+  // low-rank operands (bounded loads: rows past d_out and columns past the
+  // rank read zeros with no branch)
+  constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(a.rank > 0 ? a.Blr + rb * 16 * a.rank : a.W,
+                a.rank > 0 ? (uint32_t)(rows_here * a.rank * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t zrs =
+      make_rsrc(a.rank > 0 ? a.Z + (int64_t)req * a.rp : a.W,
+                a.rank > 0 ? (uint32_t)(a.rank * 2) : 0u);
+  const int lr_k0 = (w * 4 + qd) * 8;
+  auto lr_load = [&](int k, u32x4& bv, u32x4& zv) {
+    const bool on = k < a.rank;
+    bv = buf_load16(brs, on ? (uint32_t)((lr * a.rank + k) * 2) : kPastEnd, 0);
+    zv = buf_load16(zrs, on ? (uint32_t)(k * 2) : kPastEnd, 0);
+  };
+  auto lr_fma = [](float& acc_, const u32x4& bv, const u32x4& zv) {
+    acc_ = fmaf(bf16lo(bv.x), bf16lo(zv.x), acc_);
+    acc_ = fmaf(bf16hi(bv.x), bf16hi(zv.x), acc_);
+    acc_ = fmaf(bf16lo(bv.y), bf16lo(zv.y), acc_);
+    acc_ = fmaf(bf16hi(bv.y), bf16hi(zv.y), acc_);
+    acc_ = fmaf(bf16lo(bv.z), bf16lo(zv.z), acc_);
+    acc_ = fmaf(bf16hi(bv.z), bf16hi(zv.z), acc_);
+    acc_ = fmaf(bf16lo(bv.w), bf16lo(zv.w), acc_);
+    acc_ = fmaf(bf16hi(bv.w), bf16hi(zv.w), acc_);
+  };
+  u32x4 lbv = {0u, 0u, 0u, 0u}, lzv = {0u, 0u, 0u, 0u};
+  if (a.rank > 0) lr_load(lr_k0, lbv, lzv);   // (uniform)
+  __builtin_amdgcn_sched_barrier(0);
   constexpr int lpg4 = GS / 4;  // lanes per group
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -264,21 +292,16 @@ __global__ __launch_bounds__((gemv_waves<GS, EXPORT>() * 64)) void k_gemv(
     __builtin_amdgcn_s_setprio(0);
   }
 
-  // static low-rank term: + B[row, :] . z, z = A x precomputed
-  if (a.rank > 0 && w == 0 && qd == 0 && row_ok) {
-    const bf16_t* Br = a.Blr + row * a.rank;
-    const bf16_t* z = a.Z + (int64_t)req * a.rp;
-    for (int k = 0; k < a.rank; k += 8) {
-      const u32x4 bv = *(const u32x4*)(Br + k);
-      const u32x4 zv = *(const u32x4*)(z + k);
-      acc = fmaf(bf16lo(bv.x), bf16lo(zv.x), acc);
-      acc = fmaf(bf16hi(bv.x), bf16hi(zv.x), acc);
-      acc = fmaf(bf16lo(bv.y), bf16lo(zv.y), acc);
-      acc = fmaf(bf16hi(bv.y), bf16hi(zv.y), acc);
-      acc = fmaf(bf16lo(bv.z), bf16lo(zv.z), acc);
-      acc = fmaf(bf16hi(bv.z), bf16hi(zv.z), acc);
-      acc = fmaf(bf16lo(bv.w), bf16lo(zv.w), acc);
-      acc = fmaf(bf16hi(bv.w), bf16hi(zv.w), acc);
+  // static low-rank term: + B[row, :] . z, z = A x precomputed.  Lane
+  // quarter qd of wave w takes columns (4w + qd) * 8 + 512 j .. +8, so a
+  // rank of up to 512 is one step; the first step's operands were requested
+  // with the first weights
+  if (a.rank > 0) {
+    lr_fma(acc, lbv, lzv);
+    for (int k = lr_k0 + VW * 32; k < a.rank; k += VW * 32) {
+      u32x4 bv, zv;
+      lr_load(k, bv, zv);
+      lr_fma(acc, bv, zv);
     }
   }
 
