@@ -438,6 +438,25 @@ def leg_c3(torch, ttq, which: str, steps: int) -> dict:
                       8000 + (0 if which == "gate_up" else 50))
 
 
+def stream_read_ms(torch, Ws, n: int) -> float:
+    """A plain read of the same bytes: torch's float32 sum over one W copy
+    (rotating copies, so none is cache-resident), per-call events on the
+    current stream, median over n calls."""
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    for i in range(3):
+        torch.sum(Ws[i % len(Ws)].view(torch.float32), out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        torch.sum(Ws[i % len(Ws)].view(torch.float32), out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return t[len(t) // 2]
+
+
 def leg_c2(torch, ttq, T: int, steps: int, warmup: int, qformat: str,
            want_graph: bool, want_gemm: bool) -> dict:
     """The 4096 x 4096 projection at T tokens, W rotated over 20 copies."""
@@ -480,6 +499,15 @@ def leg_c2(torch, ttq, T: int, steps: int, warmup: int, qformat: str,
     out["roofline"] = roofline(dom, kt[dom][0], ub, uf,
                                traffic_entry(dom, f"c2_T{T}{sfx}"))
     if want_graph:
+        # the ceiling of a one-pass kernel over W: a plain read of the bytes
+        sr = stream_read_ms(torch, Ws, 200)
+        wb = 2 * d * d_out
+        out["stream_read"] = {
+            "what": "torch float32 sum over the same W bytes (rotating copies), "
+                    "event-timed median per call",
+            "bytes": wb, "ms": sr, "GB_s": wb / (sr * 1e-3) / 1e9,
+            "frac_of_peak": wb / (sr * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "dominant_kernel_vs_read": kt[dom][0] / sr}
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
