@@ -438,22 +438,21 @@ def leg_c3(torch, ttq, which: str, steps: int) -> dict:
                       8000 + (0 if which == "gate_up" else 50))
 
 
-def stream_read_ms(torch, Ws, n: int) -> float:
-    """A plain read of the same bytes: torch's float32 sum over one W copy
-    (rotating copies, so none is cache-resident), per-call events on the
-    current stream, median over n calls."""
-    for i in range(3):
-        Ws[i % len(Ws)].view(torch.float32).sum()
+def stream_read_ms(torch, ttq, Ws, n: int) -> float:
+    """Kernel time of a plain read of the same bytes (ttq_stream_read: the
+    one-token kernel's launch shape, rotating W copies so that none is
+    cache-resident), averaged over n launches from the library's events."""
+    sink = torch.empty(-(-Ws[0].numel() * 2 // (128 * 1024)), dtype=torch.int32,
+                       device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        ttq.stream_read(Ws[i % len(Ws)], sink=sink, stream=stream)
+
+    for i in range(5):
+        step(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    for i, (e0, e1) in enumerate(ev):
-        e0.record()
-        Ws[i % len(Ws)].view(torch.float32).sum()
-        e1.record()
-    torch.cuda.synchronize()
-    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
-    return t[len(t) // 2]
+    return kernel_times(torch, ttq, step, n)["stream_read"][0]
 
 
 def leg_c2(torch, ttq, T: int, steps: int, warmup: int, qformat: str,
@@ -502,10 +501,10 @@ def leg_c2(torch, ttq, T: int, steps: int, warmup: int, qformat: str,
         # (an auxiliary figure: a failure here is recorded, not fatal)
         wb = 2 * d * d_out
         try:
-            sr = stream_read_ms(torch, Ws, 200)
+            sr = stream_read_ms(torch, ttq, Ws, 200)
             out["stream_read"] = {
-                "what": "torch float32 sum over the same W bytes (rotating "
-                        "copies), event-timed median per call",
+                "what": "ttq_stream_read over the same W bytes in the one-token "
+                        "kernel's launch shape (rotating copies), kernel time",
                 "bytes": wb, "ms": sr, "GB_s": wb / (sr * 1e-3) / 1e9,
                 "frac_of_peak": wb / (sr * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "dominant_kernel_vs_read": kt[dom][0] / sr}

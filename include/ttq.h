@@ -305,6 +305,17 @@ int ttq_kernel_count(void);
 const char* ttq_kernel_name(int kernel);
 int ttq_timing_query(int kernel, double* total_ms, int64_t* launches);
 
+/* Plain streaming read, the measured ceiling of a one-pass kernel over W (not
+ * part of the method): reads `bytes` bytes of device memory at `src` once,
+ * in the launch shape of the one-token projection (one workgroup of 16
+ * waves per 128 KiB, 64 bytes per lane in flight), and writes the 32-bit XOR
+ * of each workgroup's words to sink[ceil(bytes / 131072)] (device memory)
+ * so that no load is elided.  Timed as the kernel kind "stream_read".
+ * `bytes` is a multiple of 16 (TTQ_EINVAL otherwise); `src` 16-byte and
+ * `sink` 4-byte aligned (TTQ_EALIGN); both non-NULL when bytes > 0
+ * (TTQ_ENULL).  Enqueued on `stream`. */
+int ttq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* ---- low-rank factors by PCA
  * The static low-rank factors of the projection are initialised by PCA, and
  * may be adapted online ("TTQ: Activation-Aware Test-Time Quantization ...",

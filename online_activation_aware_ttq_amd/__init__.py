@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     load_library,
     make_params,
     qformat_code,
+    stream_read,
     timing_enable,
     timing_query,
     timing_reset,

@@ -58,6 +58,7 @@ EXPORTS = {
                                    _vp, _vp, _c.c_size_t, _vp]),
     "ttq_status_string": (_c.c_char_p, [_c.c_int]),
     "ttq_last_hip_error": (_c.c_int, []),
+    "ttq_stream_read": (_c.c_int, [_vp, _c.c_int64, _vp, _vp]),
     "ttq_version": (_c.c_char_p, []),
     "ttq_timing_enable": (_c.c_int, [_c.c_int]),
     "ttq_timing_reset": (_c.c_int, []),
@@ -579,6 +580,25 @@ def ttq_lowrank_pca(W, Omega, *, iters: int, X=None, p: float = 2.0,
 
 
 # ------------------------------------------------------------------ timing
+def stream_read(src, sink=None, stream=None):
+    """Plain read of a device tensor's bytes (the ceiling of a one-pass
+    kernel over W; see ttq_stream_read).  Returns the per-workgroup XOR
+    words (uint32 stored in an int32 tensor)."""
+    import torch
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("stream_read: src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    nblk = -(-nbytes // (128 * 1024))
+    if sink is None:
+        sink = torch.empty(max(1, nblk), dtype=torch.int32, device=src.device)
+    if stream is None:
+        stream = _current_stream(src.device)
+    st = load_library().ttq_stream_read(_ptr(src), nbytes, _ptr(sink), stream)
+    if st != TTQ_OK:
+        raise TTQError(st, "ttq_stream_read")
+    return sink
+
+
 def timing_enable(on: bool = True) -> None:
     load_library().ttq_timing_enable(1 if on else 0)
 

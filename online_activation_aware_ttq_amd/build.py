@@ -36,6 +36,7 @@ SOURCES = [
     "k_gemm_q.hip",
     "k_segment.hip",
     "k_pca.hip",
+    "k_stream.hip",
     "ttq_api.cpp",
 ]
 

@@ -243,7 +243,7 @@ const char* kKernelNames[K_NUM_KINDS] = {
     "quant_what", "gemm_mfma", "lowrank_z", "gemv_t1", "splitk_reduce",
     "qgemv", "dequant", "qfused", "lowrank_zsum", "gemm_quant", "seg_copy",
     "pca_skinny", "pca_psum", "pca_chol", "pca_trsm", "pca_residual",
-    "pca_complete"};
+    "pca_complete", "stream_read"};
 
 hipEvent_t take_event() {
   if (!g_timing.pool.empty()) {
@@ -1333,6 +1333,16 @@ const char* ttq_status_string(int status) {
 int ttq_last_hip_error(void) { return g_last_hip_error; }
 
 const char* ttq_version(void) { return "ttq-gfx950 0.1.0"; }
+
+int ttq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return TTQ_EINVAL;
+  if (bytes == 0) return TTQ_OK;
+  if (!src || !sink) return TTQ_ENULL;
+  if (misaligned(src, 16) || misaligned(sink, 4)) return TTQ_EALIGN;
+  if (inject_hip_error()) return TTQ_EHIP;
+  return run(K_STREAM_READ, static_cast<hipStream_t>(stream),
+             [&](const Launch& L) { return launch_stream_read(src, bytes, sink, L); });
+}
 
 int ttq_timing_enable(int on) {
   g_timing.enabled = on != 0;

@@ -38,6 +38,7 @@ enum KernelKind {
   K_TRSM,              // PCA: panel times the inverse Cholesky factor
   K_LR_RESIDUAL,       // PCA: W - B A in bf16
   K_PCA_COMPLETE,      // PCA: completion of a rank-deficient basis
+  K_STREAM_READ,       // plain read of device memory (measurement ceiling)
   K_NUM_KINDS
 };
 
@@ -646,5 +647,11 @@ int lowrank_z_splits(int64_t M, int64_t d, int rp, int slice);
 inline size_t lowrank_z_part_bytes(int64_t M, int64_t d, int rp, int slice) {
   return (size_t)lowrank_z_splits(M, d, rp, slice) * M * rp * sizeof(float);
 }
+
+// Plain streaming read (measurement ceiling of the one-token projection):
+// one workgroup per kStreamReadBlockBytes, one XOR per workgroup to sink.
+constexpr int64_t kStreamReadBlockBytes = 128 * 1024;
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                              const Launch& L);
 
 }  // namespace ttq

@@ -477,3 +477,16 @@ def test_pca_pointers_and_workspace():
     assert call(W=FAKE + 8) == ttq.TTQ_EALIGN
     # online statistics need their own workspace
     assert ttq.ttq_lowrank_pca_workspace_bytes(_pca_prm(T=300), 2) > need
+
+
+def test_stream_read_validation():
+    # the measurement read validates on the host before anything is enqueued
+    L = lib()
+    sink = FAKE + 1024
+    assert L.ttq_stream_read(FAKE, 0, None, None) == ttq.TTQ_OK       # nothing to read
+    assert L.ttq_stream_read(FAKE, -16, sink, None) == ttq.TTQ_EINVAL
+    assert L.ttq_stream_read(FAKE, 24, sink, None) == ttq.TTQ_EINVAL  # not a multiple of 16
+    assert L.ttq_stream_read(None, 4096, sink, None) == ttq.TTQ_ENULL
+    assert L.ttq_stream_read(FAKE, 4096, None, None) == ttq.TTQ_ENULL
+    assert L.ttq_stream_read(FAKE + 8, 4096, sink, None) == ttq.TTQ_EALIGN
+    assert L.ttq_stream_read(FAKE, 4096, sink + 2, None) == ttq.TTQ_EALIGN
