@@ -19,9 +19,13 @@
 //
 // Activation operand: for T <= 16 one outlier channel can dominate every
 // output of a token, so a single bf16 rounding of its x' would be shared by
-// all of them; there x' is carried as a bf16 pair hi + lo (~16 significant
-// bits) and both halves are contracted.  For T > 16 x' is rounded once to
-// bf16 and the rounding errors average over the tokens.  It is stored in MFMA
+// all of them; there x' is carried in fp16 (11 significant bits) scaled by a
+// power of two per (group, token) so that any float32 magnitude fits, the
+// codes are the fp16 operand of v_mfma_f32_16x16x32_f16, and the scale is
+// undone in the group epilogue.  (A bf16 pair hi + lo, two MFMAs and twice
+// the activation bytes, was 20 % slower on the 8-request 7B-class layer at
+// 16 tokens.)  For T > 16 x' is rounded once to bf16 and the rounding errors
+// average over the tokens.  It is stored in MFMA
 // fragment order so that every activation load is a contiguous 1 KiB per
 // wave.  The weights are read with the default cache policy: non-temporal
 // loads (meant to keep x', re-read by every workgroup, in L2) made the
@@ -74,9 +78,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const int Tp = NTB * 16;
 
   const float* dhg = a.dh + (int64_t)req * d;
-  const bf16_t* xs = a.xs + (int64_t)req * (HILO ? 2 : 1) * Tp * d;
+  const bf16_t* xs = a.xs + (int64_t)req * Tp * d;
   const float* sx = a.sx + (int64_t)req * G * Tp;
-  const bf16_t* xs_lo = xs + (int64_t)Tp * d;
+  const float* xsc = HILO ? a.xsc + (int64_t)req * G * Tp : nullptr;
   // each row block's weight rows as one bounded buffer: rows past d_out and
   // groups past the end read as zeros without memory traffic (separate
   // scalars rather than an array or structure: see the persistent GEMM)
@@ -94,9 +98,10 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) acc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // T <= 16: lane l holds token l & 15 of the activation operand
-  u32x4 xh[NKS], xl[NKS];
-  f32x4 sxv0;
+  // T <= 16: lane l holds token l & 15 of the activation operand (scaled
+  // fp16), and the inverse scales of tokens 4 (l >> 4) .. +4
+  u32x4 xh[NKS];
+  f32x4 sxv0, scv0;
 
   auto load_w = [&](u32x4 (&wv)[RB][NKS], int g) {
     const uint32_t soff = g < G ? (uint32_t)g * GS * 2 : kOutOfRange;
@@ -113,9 +118,9 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
       for (int k = 0; k < NKS; ++k) {
         const int64_t fi = 8 * xs_frag_index(g, 0, k, l, 1, GS);
         xh[k] = *(const u32x4*)(xs + fi);
-        xl[k] = *(const u32x4*)(xs_lo + fi);
       }
       sxv0 = *(const f32x4*)(sx + (int64_t)g * Tp + qd * 4);
+      scv0 = *(const f32x4*)(xsc + (int64_t)g * Tp + qd * 4);
     }
   };
 
@@ -179,14 +184,22 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
         } else {
           qlevels8<QF>(gq, u[k], q);
         }
-        qv[r][k].x = __builtin_amdgcn_perm(__float_as_uint(q[1]),
-                                           __float_as_uint(q[0]), 0x07060302u);
-        qv[r][k].y = __builtin_amdgcn_perm(__float_as_uint(q[3]),
-                                           __float_as_uint(q[2]), 0x07060302u);
-        qv[r][k].z = __builtin_amdgcn_perm(__float_as_uint(q[5]),
-                                           __float_as_uint(q[4]), 0x07060302u);
-        qv[r][k].w = __builtin_amdgcn_perm(__float_as_uint(q[7]),
-                                           __float_as_uint(q[6]), 0x07060302u);
+        if constexpr (HILO) {
+          // fp16 operand (levels and E4M3 values are exact in fp16)
+          qv[r][k].x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(q[0], q[1]));
+          qv[r][k].y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(q[2], q[3]));
+          qv[r][k].z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(q[4], q[5]));
+          qv[r][k].w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(q[6], q[7]));
+        } else {
+          qv[r][k].x = __builtin_amdgcn_perm(__float_as_uint(q[1]),
+                                             __float_as_uint(q[0]), 0x07060302u);
+          qv[r][k].y = __builtin_amdgcn_perm(__float_as_uint(q[3]),
+                                             __float_as_uint(q[2]), 0x07060302u);
+          qv[r][k].z = __builtin_amdgcn_perm(__float_as_uint(q[5]),
+                                             __float_as_uint(q[4]), 0x07060302u);
+          qv[r][k].w = __builtin_amdgcn_perm(__float_as_uint(q[7]),
+                                             __float_as_uint(q[6]), 0x07060302u);
+        }
         if (EXPORT && a.codes_out && row_ok) {
           u32x2 c;
           c.x = qcode<QF>(gq, q[0]) | (qcode<QF>(gq, q[1]) << 8) |
@@ -211,16 +224,14 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
       for (int r = 0; r < RB; ++r) {
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < NKS; ++k) {
-          const bf16x8 q = __builtin_bit_cast(bf16x8, qv[r][k]);
-          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, xh[k]), q, P, 0, 0, 0);
-          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, xl[k]), q, P, 0, 0, 0);
-        }
+        for (int k = 0; k < NKS; ++k)
+          P = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, xh[k]), __builtin_bit_cast(f16x8, qv[r][k]), P,
+              0, 0, 0);
+        // undo the token's power-of-two scale (exact), then s P + m sum(x')
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc[r][0][i] = fmaf(sr[r], P[i], fmaf(mcr[r], sxv0[i], acc[r][0][i]));
+          acc[r][0][i] = fmaf(sr[r], P[i] * scv0[i], fmaf(mcr[r], sxv0[i], acc[r][0][i]));
       }
     } else {
 #pragma unroll

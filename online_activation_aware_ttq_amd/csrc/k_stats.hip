@@ -70,11 +70,14 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 // slice's tokens write x' = x * D^{-1/2} (the fused kernels' MFMA operand)
 // and the group sums of x' per token.
 //
-// For T <= 16 x' is carried as an unevaluated pair of bf16 numbers hi + lo
-// (hi = bf16(x'), lo = bf16(x' - hi)), about 16 significant bits: with few
-// tokens one outlier channel can dominate every output and a single bf16
-// rounding of it would be shared by all of them.  For larger T a single bf16
-// plane is written.  Planes are in MFMA fragment order (xs_frag_index) and
+// For T <= 16 one outlier channel can dominate every output of a token, and
+// a single bf16 rounding of its x' would be shared by all of them: the fused
+// projection takes x' in fp16 (11 significant bits) scaled by a power of two
+// per (group, token) so that any float32 magnitude fits, with the inverse
+// factors in their own array; the decode-from-codes kernel takes an
+// unevaluated pair of bf16 numbers hi + lo (hi = bf16(x'), lo = bf16(x' -
+// hi)), about 16 significant bits.  For larger T a single bf16 plane is
+// written.  Planes are in MFMA fragment order (xs_frag_index) and
 // zero-padded to whole 16-token blocks.  The group sums are of exactly the
 // values written, zero past T up to the padded token count.
 // ---------------------------------------------------------------------------
@@ -157,6 +160,12 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
   bf16_t* xs = a.xs + (int64_t)r * (tiled ? 1 : 2) * a.Tp * a.d;
   bf16_t* xs_lo = xs + (int64_t)a.Tp * a.d;
   float* sx = a.sx + (int64_t)r * G * a.Tp;
+  // scaled fp16 form (one plane): x' of a (group, token) is stored as
+  // fp16(x' 2^k), k chosen from the group's largest |x'| so that it lands in
+  // [2^14, 2^15); 2^-k goes to xsc.  The power of two is exact, so only the
+  // fp16 rounding remains (11 significant bits) at any float32 magnitude.
+  const bool f16s = a.xsc != nullptr;
+  float* xsc = f16s ? a.xsc + (int64_t)r * G * a.Tp : nullptr;
   float sc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) sc[j] = dhi_l[cq * 8 + j];
@@ -172,10 +181,37 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
     if ((t >> 5) != (int64_t)blockIdx.y) continue;  // another slice's token
     float ps = 0.f;
     u32x4 o = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
-    if (live && t < a.T) {
-      const float x[8] = {bf16lo(v[i].x), bf16hi(v[i].x), bf16lo(v[i].y),
-                          bf16hi(v[i].y), bf16lo(v[i].z), bf16hi(v[i].z),
-                          bf16lo(v[i].w), bf16hi(v[i].w)};
+    const bool have = live && t < a.T;
+    const float x[8] = {bf16lo(v[i].x), bf16hi(v[i].x), bf16lo(v[i].y),
+                        bf16hi(v[i].y), bf16lo(v[i].z), bf16hi(v[i].z),
+                        bf16lo(v[i].w), bf16hi(v[i].w)};
+    float inv_scale = 1.f;
+    if (f16s) {  // uniform
+      float xp[8], gm = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xp[j] = x[j] * sc[j];
+        gm = fmaxf(gm, fabsf(xp[j]));
+      }
+      if (!have) gm = 0.f;
+      // the group's largest |x'| over its adjacent chunk lanes
+      for (int off = lpg >> 1; off > 0; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      // gm in [2^(e-1), 2^e): scale by 2^k, k = 15 - e (at most 126)
+      const int k = gm > 0.f ? min(126, 15 - __builtin_amdgcn_frexp_expf(gm)) : 0;
+      const float scale = __builtin_amdgcn_ldexpf(1.f, k);
+      inv_scale = __builtin_amdgcn_ldexpf(1.f, -k);
+      if (have) {
+        unsigned hb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 h = (_Float16)(xp[j] * scale);
+          hb[j] = (unsigned)__builtin_bit_cast(unsigned short, h);
+          ps += (float)h * inv_scale;
+        }
+        o = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
+                  hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+      }
+    } else if (have) {
       unsigned bh[8], bl[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -198,7 +234,10 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
     }
     // the chunk lanes of one group are adjacent within a token row
     for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
-    if (live && (cq % lpg) == 0) sx[g * a.Tp + t] = ps;
+    if (live && (cq % lpg) == 0) {
+      sx[g * a.Tp + t] = ps;
+      if (f16s) xsc[g * a.Tp + t] = inv_scale;
+    }
   }
 
   // Low-rank partials of this workgroup's 128-channel slice(s) and 32

@@ -49,7 +49,7 @@ struct Plan {
                          // 3 two-phase with quantization inside the GEMM
   int ntb = 1;           // fused: 16-token blocks (power of two)
   int G = 0;             // groups per row
-  int planes = 1;        // fused: activation planes (2 = bf16 hi + lo)
+  int planes = 1;        // activation planes (2 = bf16 hi + lo, decode path)
   int frb = 1;           // fused: 16-row blocks per workgroup
   int64_t rowblocks = 0;
   int sz_ntb = 0;         // large T: 64-token blocks per request,
@@ -63,6 +63,7 @@ struct Plan {
   size_t off_dh = 0, off_dhi = 0, off_xs = 0, off_sx = 0, off_z = 0,
          off_statp = 0, off_what = 0, off_zpart = 0;
   size_t off_zsmall = 0;  // fp32 partials of the small-M Z kernel
+  size_t off_xsc = 0;     // fused, T <= 16: inverse fp16 scales of x'
   size_t total = 0;
 };
 
@@ -198,9 +199,12 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.ntb = 1;
     while (P.ntb * 16 < T) P.ntb *= 2;
     P.rowblocks = (dout + 15) / 16;
-    P.planes = T <= 16 ? 2 : 1;
-    P.off_xs = take(sizeof(uint16_t) * P.planes * R * 16 * P.ntb * d);
+    // one activation plane: bf16 for T > 16, scaled fp16 for T <= 16 (with
+    // an inverse scale per group and token)
+    P.planes = 1;
+    P.off_xs = take(sizeof(uint16_t) * R * 16 * P.ntb * d);
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
+    if (T <= 16) P.off_xsc = take(sizeof(float) * R * P.G * 16 * P.ntb);
     fused_shape(P, R, prm->group);
   } else {
     const bool zf = T > 0 && z_in_stats(P.rp, prm->p);
@@ -429,6 +433,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     sa.dh = dh; sa.dhi = dhi; sa.dh_export = dhalf_out;
     sa.xs = need_quant ? reinterpret_cast<bf16_t*>(ws + P.off_xs) : nullptr;
     sa.sx = need_quant ? reinterpret_cast<float*>(ws + P.off_sx) : nullptr;
+    sa.xsc = need_quant && P.ntb == 1 ? reinterpret_cast<float*>(ws + P.off_xsc) : nullptr;
     sa.group = prm->group;
     sa.planes = P.planes;
     sa.Tp = 16 * P.ntb;
@@ -446,7 +451,7 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     }
     FusedArgs fa{};
     fa.W = Wb; fa.d = d; fa.d_out = dout; fa.T = T; fa.G = P.G; fa.Nf = Nf;
-    fa.dh = dh; fa.xs = sa.xs; fa.sx = sa.sx;
+    fa.dh = dh; fa.xs = sa.xs; fa.sx = sa.sx; fa.xsc = sa.xsc;
     fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
     fa.Y = Y;
     fa.rowblocks = P.rowblocks;

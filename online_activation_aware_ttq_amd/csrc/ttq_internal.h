@@ -10,6 +10,7 @@ namespace ttq {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bit pattern
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -287,7 +288,8 @@ struct StatsSmallArgs {
   bf16_t* xs;           // optional x * D^{-1/2} in bf16, see xs_frag_index
   float* sx;            // with xs: [R][G][Tp] group sums of xs, zero past T
   int group;
-  int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16
+  int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16 (or,
+                        // with xsc, single scaled fp16)
   int Tp;               // 16 * ceil(T / 16): tokens of the fragment layout
   int quarter;          // 1: quarter order of the fragments, 0: step-major
   // optional [R][d] stored D^{-1/2}: no statistics are taken, x' and the
@@ -299,6 +301,9 @@ struct StatsSmallArgs {
   const bf16_t* zA;     // [zrank][d]
   int zrank, zrp;
   float* zpart;
+  // optional (with xs, planes 1): x' as fp16 scaled by a power of two per
+  // (group, token), the inverse factors [R][G][Tp] here
+  float* xsc;
 };
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
                               const Launch& L);
@@ -353,6 +358,7 @@ struct FusedArgs {
   const bf16_t* xs;     // x * D^{-1/2}, layout as written by the stats kernel
   const float* sx;      // [R][G][Tp] group sums of xs, Tp = 16 * ntb,
                         // zero past T
+  const float* xsc;     // ntb == 1: [R][G][Tp] inverse fp16 scales of xs
   const bf16_t* Z;      // [R][T][rp] or null
   const bf16_t* Blr;    // [d_out][rank] or null
   int rank, rp;

@@ -133,13 +133,20 @@ def test_all_requests_empty_or_one_token():
             one = _run_single(base, x, exports=False)
             np.testing.assert_array_equal(seg["Y"][offs[i]:offs[i + 1]].view(np.uint32),
                                           one["Y"].view(np.uint32))
-    # the plan: the run of three single tokens, each empty request alone (an
-    # empty request still needs its statistics workspace in case codes are
-    # asked for)
+    # the workspace covers both plans: with exports, runs of consecutive
+    # requests (the three single tokens, each empty request alone, the last
+    # token alone; an empty request still needs its statistics workspace in
+    # case codes are asked for); without, requests grouped by length (the
+    # four single tokens in one batch, gathered into padded X and Y copies)
     def ws(T, R):
         return ttq.ttq_workspace_bytes(
             ttq.make_params(d=512, d_out=272, T=T, bits=4, group=128, p=2.0,
                             lam=1e-3, alpha=0.5), R)
+
+    def up(n):
+        return -(-n // 256) * 256
     prm = ttq.make_params(d=512, d_out=272, T=4, bits=4, group=128, p=2.0,
                           lam=1e-3, alpha=0.5)
-    assert ttq.ttq_segmented_workspace_bytes(prm, offs) == max(ws(1, 3), ws(0, 1))
+    gathered = up(ws(1, 4)) + up(4 * 1 * 512 * 2) + up(4 * 1 * 272 * 4)
+    assert ttq.ttq_segmented_workspace_bytes(prm, offs) == max(ws(1, 3), ws(0, 1),
+                                                               ws(1, 1), gathered)
