@@ -598,12 +598,27 @@ def leg_decode(torch, ttq, steps: int = 1000) -> dict:
     G = d // 128
     ab = d_out * d // 2 + 8 * d_out * G + 2 * d + 4 * d + 4 * d_out
     k = kt.get("qgemv", (float("nan"), 0))[0]
+    # the same stored codes against 16 new tokens (statistics kernel in its
+    # stored-D^{-1/2} mode, then the packed-code MFMA kernel)
+    X16 = draw_x_gpu(torch, 3100, 16, 16, d, "n", 41)
+    Y16 = torch.empty(16, d_out, dtype=torch.float32, device="cuda")
+    prm16 = ttq.make_params(d=d, d_out=d_out, T=16, bits=4, group=128, p=1.0,
+                            lam=0.0, alpha=0.0)
+    ws16 = torch.empty(max(256, ttq.ttq_qmatmul_workspace_bytes(prm16)),
+                       dtype=torch.uint8, device="cuda")
+    f16 = lambda i: ttq.ttq_qmatmul(*st[i % 20], X16[i % 16], Y=Y16, workspace=ws16, **kw)
+    ms16 = timed_wall(torch, f16, steps // 2, 20)
+    kt16 = kernel_times(torch, ttq, f16, steps // 2)
     return {"workload": "4096x4096, 4-bit g128 codes, one token",
             "ms": ms, "tokens_per_s": 1.0 / (ms * 1e-3), "ms_graph": gms,
             "tokens_per_s_graph": 1.0 / (gms * 1e-3), "kernel": "qgemv",
             "kernel_ms": k, "alg_bytes": ab,
             "hbm_frac_kernel": ab / (k * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic_entry("qgemv", "decode_int4")}
+            "traffic": traffic_entry("qgemv", "decode_int4"),
+            "T16": {"workload": "the same codes, 16 tokens", "ms": ms16,
+                    "tokens_per_s": 16 / (ms16 * 1e-3),
+                    "kernels": {kk: {"ms_per_launch": v[0], "launches_per_call": v[1]}
+                                for kk, v in kt16.items()}}}
 
 
 def leg_segmented(torch, ttq, reps: int = 50) -> dict:

@@ -7,8 +7,10 @@
 //   Y[t,i] = sum_g  s_ig * sum_{j in g} q_ij x'_tj  +  m_ig * sum_{j in g} x'_tj
 //
 // with x' = x D^{-1/2} from the stored D^{-1/2}.  The statistics kernel, in
-// its stored-D^{-1/2} mode, writes x' (a bf16 hi + lo pair for T <= 16, one
-// bf16 plane above; MFMA fragment order) and the per-token group sums, in
+// its stored-D^{-1/2} mode, writes x' (for T <= 16 fp16 scaled by a power of
+// two per group and token, with the inverse factors, as for the one-pass
+// kernel; one bf16 plane above; MFMA fragment order) and the per-token group
+// sums, in
 // the layout the one-pass kernel reads; this kernel streams the codes instead
 // of bf16 weights.  The work split is that of the one-pass kernel: 8 or 16
 // waves own 16 weight rows and stride over the groups, each with the codes
@@ -17,10 +19,11 @@
 // step; x' in the quarter fragment order), i.e. GS/32 * CB contiguous bytes
 // of the packed row per group: one wide load.
 //
-// Codes become the bf16 B operand exactly: for containers of up to 4 bits
-// the value 128 + q (bf16 bits 0x4300 | q, one byte permute per pair), whose
-// extra 128 * sum(x') is taken out with the minimum term:
-//   s * sum (128 + q) x' + (m - 128 s) * sum x';
+// Codes become the B operand exactly: for containers of up to 4 bits the
+// value 128 + q (bf16 bits 0x4300 | q, one byte permute per pair; in fp16 at
+// T <= 16, 1024 + q, bits 0x6400 | q), whose extra bias * sum(x') is taken
+// out with the minimum term:
+//   s * sum (bias + q) x' + (m - bias s) * sum x';
 // for 8-bit containers q itself (converted through float32).
 #include "ttq_internal.h"
 
@@ -36,10 +39,13 @@ constexpr int qf_waves() {
   return (NTB <= 2 && GS <= 128 && !F8) ? 16 : 8;
 }
 
-// 8 codes of CB bits, low bits first in `raw` -> 4 bf16 pairs (see above)
-template <int CB, bool F8>
+// 8 codes of CB bits, low bits first in `raw` -> 4 bf16 pairs (see above),
+// or with H16 4 fp16 pairs: 1024 + q (fp16 bits 0x6400 | q) for containers
+// of up to 4 bits, q itself for 8-bit containers
+template <int CB, bool F8, bool H16 = false>
 __device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
   static_assert(!F8 || CB == 8, "E4M3 codes are 8 bits wide");
+  constexpr unsigned OR = H16 ? 0x64006400u : 0x43004300u;
   if (CB == 8) {
     float f[8];
 #pragma unroll
@@ -52,6 +58,12 @@ __device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
         f[4 + i] = (float)((raw.y >> (8 * i)) & 0xFFu);
       }
     }
+    if constexpr (H16) {  // exact in fp16 (integers up to 255, E4M3 values)
+      return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[0], f[1])),
+                   __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[2], f[3])),
+                   __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[4], f[5])),
+                   __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[6], f[7]))};
+    }
     // the high halves of the floats (exact: at most 8 significant bits, or
     // the 4 of an E4M3 value)
     return u32x4{__builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u),
@@ -62,10 +74,10 @@ __device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
     // even codes in the bytes of lo, odd codes in the bytes of hi; pair k =
     // bytes {lo.k, 0, hi.k, 0} (selector 0x0c: zero byte), then | 0x4300
     const unsigned lo = raw.x & 0x0F0F0F0Fu, hi = (raw.x >> 4) & 0x0F0F0F0Fu;
-    return u32x4{__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u,
-                 __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u,
-                 __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u,
-                 __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u};
+    return u32x4{__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | OR,
+                 __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | OR,
+                 __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | OR,
+                 __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | OR};
   } else {
     constexpr unsigned M = (1u << CB) - 1u;
     unsigned p[4];
@@ -73,7 +85,7 @@ __device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
     for (int k = 0; k < 4; ++k) {
       const unsigned q0 = (raw.x >> (2 * k * CB)) & M;
       const unsigned q1 = (raw.x >> ((2 * k + 1) * CB)) & M;
-      p[k] = (q0 | (q1 << 16)) | 0x43004300u;
+      p[k] = (q0 | (q1 << 16)) | OR;
     }
     return u32x4{p[0], p[1], p[2], p[3]};
   }
@@ -124,8 +136,8 @@ template <int CB, int NTB, int GS, bool F8>
 __global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFusedArgs a) {
   constexpr int QF_W = qf_waves<NTB, GS, F8>();
   constexpr int NKS = GS / 32;
-  constexpr bool HILO = (NTB == 1);
-  constexpr float BIAS = CB == 8 ? 0.f : 128.f;
+  constexpr bool HILO = (NTB == 1);   // T <= 16: scaled fp16 operands
+  constexpr float BIAS = CB == 8 ? 0.f : (HILO ? 1024.f : 128.f);
   __shared__ float red[QF_W][NTB * 4][64];
 
   const int64_t rb = blockIdx.x;
@@ -157,24 +169,21 @@ __global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFuse
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16_t* xs_lo = a.xs + (int64_t)Tp * d;  // T <= 16: the lo plane
-
-  // T <= 16: the group's x' (hi, lo) and group sums, fetched with its codes
-  // one group ahead (a group past the end fetches the last one again)
+  // T <= 16: the group's x' (fp16, scaled by a power of two per group and
+  // token), its group sums and inverse scales, fetched with its codes one
+  // group ahead (a group past the end fetches the last one again)
   struct XHL {
-    u32x4 h[NKS], l[NKS];
-    f32x4 sx;
+    u32x4 h[NKS];
+    f32x4 sx, sc;
   };
   auto load_x = [&](XHL& x, int g) {
     if (!HILO) return;
     const int gg = g < G ? g : G - 1;
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) {
-      const int64_t fi = 8 * xs_frag_index(gg, 0, k, l, 1, GS);
-      x.h[k] = *(const u32x4*)(a.xs + fi);
-      x.l[k] = *(const u32x4*)(xs_lo + fi);
-    }
+    for (int k = 0; k < NKS; ++k)
+      x.h[k] = *(const u32x4*)(a.xs + 8 * xs_frag_index(gg, 0, k, l, 1, GS));
     x.sx = *(const f32x4*)(a.sx + (int64_t)gg * Tp + qd * 4);
+    x.sc = *(const f32x4*)(a.xsc + (int64_t)gg * Tp + qd * 4);
   };
 
   auto process = [&](const GroupCodes<CB, GS>& cv, const XHL& x, int g) {
@@ -182,18 +191,17 @@ __global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFuse
     const float mb = a.m[srow + g] - BIAS * s;
     u32x4 qv[NKS];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB, F8>(step_codes<CB, GS>(cv, k));
+    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB, F8, HILO>(step_codes<CB, GS>(cv, k));
     if (HILO) {
       f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < NKS; ++k) {
-        const bf16x8 q = __builtin_bit_cast(bf16x8, qv[k]);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.h[k]), q, P, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.l[k]), q, P, 0, 0, 0);
-      }
-      const f32x4 sxv = x.sx;
+      for (int k = 0; k < NKS; ++k)
+        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.h[k]),
+                                                  __builtin_bit_cast(f16x8, qv[k]), P, 0, 0, 0);
+      // undo the token's power-of-two scale (exact), then s P + (m - BIAS s) sum(x')
+      const f32x4 sxv = x.sx, scv = x.sc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[0][i] = fmaf(s, P[i], fmaf(mb, sxv[i], acc[0][i]));
+      for (int i = 0; i < 4; ++i) acc[0][i] = fmaf(s, P[i] * scv[i], fmaf(mb, sxv[i], acc[0][i]));
     } else {
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {

@@ -71,14 +71,12 @@ __device__ __forceinline__ void accum8(double acc[8], u32x4 v, int pmode,
 // and the group sums of x' per token.
 //
 // For T <= 16 one outlier channel can dominate every output of a token, and
-// a single bf16 rounding of its x' would be shared by all of them: the fused
-// projection takes x' in fp16 (11 significant bits) scaled by a power of two
-// per (group, token) so that any float32 magnitude fits, with the inverse
-// factors in their own array; the decode-from-codes kernel takes an
-// unevaluated pair of bf16 numbers hi + lo (hi = bf16(x'), lo = bf16(x' -
-// hi)), about 16 significant bits.  For larger T a single bf16 plane is
-// written.  Planes are in MFMA fragment order (xs_frag_index) and
-// zero-padded to whole 16-token blocks.  The group sums are of exactly the
+// a single bf16 rounding of its x' would be shared by all of them: x' is
+// written in fp16 (11 significant bits) scaled by a power of two per (group,
+// token) so that any float32 magnitude fits, with the inverse factors in
+// their own array.  For larger T x' is written in bf16.  The plane is in
+// MFMA fragment order (xs_frag_index) and zero-padded to whole 16-token
+// blocks.  The group sums are of exactly the
 // values written, zero past T up to the padded token count.
 // ---------------------------------------------------------------------------
 // (512 threads: measured on MI355X, one or two 16-token steps take about
@@ -153,12 +151,10 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
   if (!a.xs) return;
   __syncthreads();
 
-  const bool tiled = a.planes == 1;
   const int ntb = a.Tp / 16;
   const int G = (int)(a.d / a.group);
   const int lpg = a.group >> 3;  // chunk lanes per quantization group
-  bf16_t* xs = a.xs + (int64_t)r * (tiled ? 1 : 2) * a.Tp * a.d;
-  bf16_t* xs_lo = xs + (int64_t)a.Tp * a.d;
+  bf16_t* xs = a.xs + (int64_t)r * a.Tp * a.d;
   float* sx = a.sx + (int64_t)r * G * a.Tp;
   // scaled fp16 form (one plane): x' of a (group, token) is stored as
   // fp16(x' 2^k), k chosen from the group's largest |x'| so that it lands in
@@ -180,7 +176,7 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
     if (t >= a.Tp) break;  // uniform across the chunk lanes of a token
     if ((t >> 5) != (int64_t)blockIdx.y) continue;  // another slice's token
     float ps = 0.f;
-    u32x4 o = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
+    u32x4 o = {0u, 0u, 0u, 0u};
     const bool have = live && t < a.T;
     const float x[8] = {bf16lo(v[i].x), bf16hi(v[i].x), bf16lo(v[i].y),
                         bf16hi(v[i].y), bf16lo(v[i].z), bf16hi(v[i].z),
@@ -212,25 +208,19 @@ __global__ __launch_bounds__(NT) void k_stats_small(StatsSmallArgs a) {
                   hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
       }
     } else if (have) {
-      unsigned bh[8], bl[8];
+      unsigned bh[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float xp = x[j] * sc[j];
-        bh[j] = f2bf(xp);
-        const float hi = __uint_as_float(bh[j] << 16);
-        bl[j] = f2bf(xp - hi);
-        ps += tiled ? hi : hi + __uint_as_float(bl[j] << 16);
+        bh[j] = f2bf(x[j] * sc[j]);
+        ps += __uint_as_float(bh[j] << 16);
       }
       o = u32x4{bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16),
                 bh[4] | (bh[5] << 16), bh[6] | (bh[7] << 16)};
-      ol = u32x4{bl[0] | (bl[1] << 16), bl[2] | (bl[3] << 16),
-                 bl[4] | (bl[5] << 16), bl[6] | (bl[7] << 16)};
     }
     if (live) {
       const int lane = lane_q + (int)(t & 15);
       const int64_t fi = 8 * xs_frag_index(g, t >> 4, k, lane, ntb, a.group);
       *(u32x4*)(xs + fi) = o;
-      if (!tiled) *(u32x4*)(xs_lo + fi) = ol;
     }
     // the chunk lanes of one group are adjacent within a token row
     for (int off = lpg >> 1; off > 0; off >>= 1) ps += __shfl_xor(ps, off);

@@ -49,7 +49,6 @@ struct Plan {
                          // 3 two-phase with quantization inside the GEMM
   int ntb = 1;           // fused: 16-token blocks (power of two)
   int G = 0;             // groups per row
-  int planes = 1;        // activation planes (2 = bf16 hi + lo, decode path)
   int frb = 1;           // fused: 16-row blocks per workgroup
   int64_t rowblocks = 0;
   int sz_ntb = 0;         // large T: 64-token blocks per request,
@@ -201,7 +200,6 @@ Plan make_plan(const ttq_params* prm, int64_t R) {
     P.rowblocks = (dout + 15) / 16;
     // one activation plane: bf16 for T > 16, scaled fp16 for T <= 16 (with
     // an inverse scale per group and token)
-    P.planes = 1;
     P.off_xs = take(sizeof(uint16_t) * R * 16 * P.ntb * d);
     P.off_sx = take(sizeof(float) * R * P.G * 16 * P.ntb);
     if (T <= 16) P.off_xsc = take(sizeof(float) * R * P.G * 16 * P.ntb);
@@ -435,7 +433,6 @@ int linear_impl(const ttq_params* prm, int64_t R, const void* W,
     sa.sx = need_quant ? reinterpret_cast<float*>(ws + P.off_sx) : nullptr;
     sa.xsc = need_quant && P.ntb == 1 ? reinterpret_cast<float*>(ws + P.off_xsc) : nullptr;
     sa.group = prm->group;
-    sa.planes = P.planes;
     sa.Tp = 16 * P.ntb;
     const bool zin = need_quant && z_parts_in_stats(P.rp, R * T, d);
     if (zin) {
@@ -608,9 +605,11 @@ Plan make_qmatmul_plan(const ttq_params& q, int cb) {
   if (P.path == 0 && T > 0 && q.d_out > 0) {
     P.ntb = 1;
     while (P.ntb * 16 < T) P.ntb *= 2;
-    P.planes = T <= 16 ? 2 : 1;
-    P.off_xs = take(sizeof(uint16_t) * P.planes * 16 * P.ntb * d);
+    // one activation plane: scaled fp16 for T <= 16 (with an inverse scale
+    // per group and token), bf16 above
+    P.off_xs = take(sizeof(uint16_t) * 16 * P.ntb * d);
     P.off_sx = take(sizeof(float) * P.G * 16 * P.ntb);
+    if (T <= 16) P.off_xsc = take(sizeof(float) * P.G * 16 * P.ntb);
   }
   if ((P.path == 1 || P.path == 3) && T > 0 && q.d_out > 0) {
     if (P.path == 1) P.off_what = take(sizeof(uint16_t) * q.d_out * d);
@@ -721,8 +720,8 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     sa.quarter = 1;
     sa.xs = reinterpret_cast<bf16_t*>(ws + P.off_xs);
     sa.sx = reinterpret_cast<float*>(ws + P.off_sx);
+    sa.xsc = P.ntb == 1 ? reinterpret_cast<float*>(ws + P.off_xsc) : nullptr;
     sa.group = q.group;
-    sa.planes = P.planes;
     sa.Tp = 16 * P.ntb;
     const bool zin = z_parts_in_stats(P.rp, T, d);
     if (zin) {
@@ -737,7 +736,7 @@ int qmatmul_impl(const ttq_params* prm, const uint8_t* codes,
     }
     QFusedArgs fa{};
     fa.packed = codes; fa.row_bytes = rb; fa.s = scales; fa.m = mins;
-    fa.xs = sa.xs; fa.sx = sa.sx;
+    fa.xs = sa.xs; fa.sx = sa.sx; fa.xsc = sa.xsc;
     fa.d = d; fa.d_out = dout; fa.T = T; fa.G = P.G;
     fa.Z = Zb; fa.Blr = Bb; fa.rank = (int)rank; fa.rp = (int)P.rp;
     fa.Y = Y;

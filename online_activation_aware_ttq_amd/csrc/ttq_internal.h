@@ -253,8 +253,8 @@ __device__ __forceinline__ unsigned qcode(const QGroup& g, float L) {
 //                      a lane's codes of one group are one contiguous run),
 // at fragment index ((g * NTB + tb) * (GS / 32) + k) * 64 + l, so that one
 // wave load of a fragment is 1 KiB contiguous.
-//   T <= 16: two such planes of Tp * d values (bf16 hi, then lo).
-//   T  > 16: one plane.
+// One plane of Tp * d values: fp16 scaled per (group, token) for T <= 16,
+// bf16 above.
 __host__ __device__ inline int64_t xs_frag_index(int64_t g, int64_t tb,
                                                  int64_t k, int l, int ntb,
                                                  int gs) {
@@ -288,8 +288,6 @@ struct StatsSmallArgs {
   bf16_t* xs;           // optional x * D^{-1/2} in bf16, see xs_frag_index
   float* sx;            // with xs: [R][G][Tp] group sums of xs, zero past T
   int group;
-  int planes;           // 2: hi + lo pair (T <= 16), 1: single bf16 (or,
-                        // with xsc, single scaled fp16)
   int Tp;               // 16 * ceil(T / 16): tokens of the fragment layout
   int quarter;          // 1: quarter order of the fragments, 0: step-major
   // optional [R][d] stored D^{-1/2}: no statistics are taken, x' and the
@@ -301,8 +299,8 @@ struct StatsSmallArgs {
   const bf16_t* zA;     // [zrank][d]
   int zrank, zrp;
   float* zpart;
-  // optional (with xs, planes 1): x' as fp16 scaled by a power of two per
-  // (group, token), the inverse factors [R][G][Tp] here
+  // optional (with xs): x' as fp16 scaled by a power of two per (group,
+  // token) instead of bf16, the inverse factors [R][G][Tp] here
   float* xsc;
 };
 hipError_t launch_stats_small(const StatsSmallArgs& a, int R,
@@ -468,6 +466,7 @@ struct QFusedArgs {
   const float* m;         // [d_out][G]
   const bf16_t* xs;       // x' as written by the statistics kernel
   const float* sx;        // [G][Tp] group sums of xs
+  const float* xsc;       // T <= 16: [G][16] inverse fp16 scales of xs
   int64_t d, d_out, T;
   int G;
   const bf16_t* Z;        // [T][rp] or null
