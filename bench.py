@@ -607,8 +607,9 @@ def leg_decode(torch, ttq, steps: int = 1000) -> dict:
     ws16 = torch.empty(max(256, ttq.ttq_qmatmul_workspace_bytes(prm16)),
                        dtype=torch.uint8, device="cuda")
     f16 = lambda i: ttq.ttq_qmatmul(*st[i % 20], X16[i % 16], Y=Y16, workspace=ws16, **kw)
-    ms16 = timed_wall(torch, f16, steps // 2, 20)
-    kt16 = kernel_times(torch, ttq, f16, steps // 2)
+    n16 = max(1, steps // 2)
+    ms16 = timed_wall(torch, f16, n16, 20)
+    kt16 = kernel_times(torch, ttq, f16, n16)
     return {"workload": "4096x4096, 4-bit g128 codes, one token",
             "ms": ms, "tokens_per_s": 1.0 / (ms * 1e-3), "ms_graph": gms,
             "tokens_per_s_graph": 1.0 / (gms * 1e-3), "kernel": "qgemv",

@@ -398,3 +398,29 @@ def test_deterministic_and_stateless():
     assert not np.array_equal(a["dh"], c["dh"])
     assert not np.array_equal(a["q"], c["q"])
     check_problem(p2, c)
+
+
+def _with_scaled_channels(prob, big, tiny):
+    """The problem with channel sets multiplied by 1e18 and 1e-18 (bf16 has
+    float32's exponent range, so such activations are valid inputs)."""
+    import dataclasses
+    x = oracle.bf16_to_f32(prob.X).astype(np.float64)
+    x[..., big] *= 1e18
+    x[..., tiny] *= 1e-18
+    b = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    return dataclasses.replace(prob, X=b)
+
+
+@pytest.mark.parametrize("T,alpha", [(1, 0.0), (5, 0.0), (16, 0.5), (3, 1.0)])
+def test_fp16_activations_any_magnitude(T, alpha):
+    """At T <= 16 the fused kernel takes x' in fp16 scaled by a power of two
+    per group and token: activations far beyond fp16's range (and far below)
+    must still meet the bars, in groups of their own and mixed with ordinary
+    channels of the same group."""
+    base = make_problem(f"range_T{T}", d=512, d_out=80, T=T, R=2, bits=4,
+                        group=128, alpha=alpha, seed=61 + T)
+    big = list(range(0, 8)) + [300]
+    tiny = list(range(128, 136)) + [301]
+    prob = _with_scaled_channels(base, big, tiny)
+    _run_and_check(prob, flags=FUSED, name=f"fp16_range_T{T}_a{alpha}")
