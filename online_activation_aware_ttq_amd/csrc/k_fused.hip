@@ -58,7 +58,7 @@ constexpr int FW = 8;  // waves per workgroup
 template <int NTB, int GS, bool DH_LDS, bool EXPORT, int QF, int RB>
 __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   constexpr int NKS = GS / 32;
-  constexpr bool HILO = (NTB == 1);
+  constexpr bool XF16 = (NTB == 1);  // T <= 16: x' in scaled fp16
   extern __shared__ __attribute__((aligned(16))) float lds[];
 
   const int64_t b = blockIdx.x;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
   const float* dhg = a.dh + (int64_t)req * d;
   const bf16_t* xs = a.xs + (int64_t)req * Tp * d;
   const float* sx = a.sx + (int64_t)req * G * Tp;
-  const float* xsc = HILO ? a.xsc + (int64_t)req * G * Tp : nullptr;
+  const float* xsc = XF16 ? a.xsc + (int64_t)req * G * Tp : nullptr;
   // each row block's weight rows as one bounded buffer: rows past d_out and
   // groups past the end read as zeros without memory traffic (separate
   // scalars rather than an array or structure: see the persistent GEMM)
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(FW * 64) void k_fused(FusedArgs a) {
         } else {
           qlevels8<QF>(gq, u[k], q);
         }
-        if constexpr (HILO) {
+        if constexpr (XF16) {
           // fp16 operand (levels and E4M3 values are exact in fp16)
           qv[r][k].x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(q[0], q[1]));
           qv[r][k].y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(q[2], q[3]));

@@ -43,7 +43,7 @@ constexpr int qf_waves() {
 // or with H16 4 fp16 pairs: 1024 + q (fp16 bits 0x6400 | q) for containers
 // of up to 4 bits, q itself for 8-bit containers
 template <int CB, bool F8, bool H16 = false>
-__device__ __forceinline__ u32x4 codes_bf16(u32x2 raw) {
+__device__ __forceinline__ u32x4 codes_operand(u32x2 raw) {
   static_assert(!F8 || CB == 8, "E4M3 codes are 8 bits wide");
   constexpr unsigned OR = H16 ? 0x64006400u : 0x43004300u;
   if (CB == 8) {
@@ -136,8 +136,8 @@ template <int CB, int NTB, int GS, bool F8>
 __global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFusedArgs a) {
   constexpr int QF_W = qf_waves<NTB, GS, F8>();
   constexpr int NKS = GS / 32;
-  constexpr bool HILO = (NTB == 1);   // T <= 16: scaled fp16 operands
-  constexpr float BIAS = CB == 8 ? 0.f : (HILO ? 1024.f : 128.f);
+  constexpr bool XF16 = (NTB == 1);   // T <= 16: scaled fp16 operands
+  constexpr float BIAS = CB == 8 ? 0.f : (XF16 ? 1024.f : 128.f);
   __shared__ float red[QF_W][NTB * 4][64];
 
   const int64_t rb = blockIdx.x;
@@ -177,7 +177,7 @@ __global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFuse
     f32x4 sx, sc;
   };
   auto load_x = [&](XHL& x, int g) {
-    if (!HILO) return;
+    if (!XF16) return;
     const int gg = g < G ? g : G - 1;
 #pragma unroll
     for (int k = 0; k < NKS; ++k)
@@ -191,8 +191,8 @@ __global__ __launch_bounds__((qf_waves<NTB, GS, F8>() * 64)) void k_qfused(QFuse
     const float mb = a.m[srow + g] - BIAS * s;
     u32x4 qv[NKS];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) qv[k] = codes_bf16<CB, F8, HILO>(step_codes<CB, GS>(cv, k));
-    if (HILO) {
+    for (int k = 0; k < NKS; ++k) qv[k] = codes_operand<CB, F8, XF16>(step_codes<CB, GS>(cv, k));
+    if (XF16) {
       f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NKS; ++k)
