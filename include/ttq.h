@@ -39,6 +39,12 @@
  * faults surface at the caller's next synchronization.  Results are
  * deterministic: identical inputs give bit-identical outputs.
  *
+ * Accuracy of Y: the contraction accumulates in float32.  Its activation
+ * operand x' = x D^{-1/2} is float32 for one token, fp16 scaled by a power
+ * of two per (group, token) for 2..16 tokens (any float32 magnitude), and
+ * bf16 above; above 128 tokens the dequantized weights are rounded once to
+ * bf16 and contracted with the bf16 X.
+ *
  * Errors: validation happens before anything is enqueued, so a negative
  * status means nothing was launched -- except TTQ_EHIP, which reports a
  * failed launch (some earlier kernels of the same call may have been
