@@ -706,21 +706,35 @@ def cpu_baseline_c5(T: int, seconds: float) -> dict:
     t_layer = 0.0
     measured = 0.0
     t_start = time.perf_counter()
-    rows_a, rows_b = 8, 24
-    scale = max(1.0, min(4.0, seconds / 12.0))
-    rows_a, rows_b = int(rows_a * scale), int(rows_b * scale)
-    for i, (name, d, d_out) in enumerate(C5_PROJ):
+
+    def run(prob, X, nr):
+        t0 = time.perf_counter()
+        oracle.ttq_linear(prob.W, X, bits=4, group=128, p=2.0, lam=1e-3,
+                          alpha=0.5, B_bits=prob.B, A_bits=prob.A,
+                          rows=np.arange(nr))
+        return time.perf_counter() - t0
+
+    def inputs(i):
+        name, d, d_out = C5_PROJ[i]
         prob = wc.make_c5(T=1, proj=name, R=1)
         X = wc.draw_x(4000 + i, 0, 1, T, d, "logu10_100",
                       max(1, round(0.01 * d)))[0]
-        ts = []
-        for nr in (rows_a, rows_b):
-            rows = np.arange(nr)
-            t0 = time.perf_counter()
-            oracle.ttq_linear(prob.W, X, bits=4, group=128, p=2.0, lam=1e-3,
-                              alpha=0.5, B_bits=prob.B, A_bits=prob.A,
-                              rows=rows)
-            ts.append(time.perf_counter() - t0)
+        return prob, X, d_out
+
+    # row counts sized from one short pass (rows 8 and 24 of the first
+    # projection: a fixed part and a cost per row) so that the seven pairs
+    # of calls take about `seconds` of oracle time
+    prob, X, _ = inputs(0)
+    c8, c24 = run(prob, X, 8), run(prob, X, 24)
+    per_row = max((c24 - c8) / 16, 1e-6)
+    fixed = max(0.0, c8 - 8 * per_row)
+    n = len(C5_PROJ)
+    rows_b = int((seconds / n - 2 * fixed) / (per_row * 4 / 3))
+    rows_b = max(24, min(min(d_out for _, _, d_out in C5_PROJ), rows_b))
+    rows_a = rows_b // 3
+    for i in range(len(C5_PROJ)):
+        prob, X, d_out = inputs(i)
+        ts = [run(prob, X, rows_a), run(prob, X, rows_b)]
         measured += sum(ts)
         per_row = max(0.0, (ts[1] - ts[0]) / (rows_b - rows_a))
         fixed = max(0.0, ts[0] - per_row * rows_a)
